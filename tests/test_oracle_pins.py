@@ -1,0 +1,410 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+Each test ties one oracle function to a closed form, a library routine on a
+special case, an invariant, a brute-force enumeration or a count the pages
+state.  They are chosen so that a plausible slip (a dropped normalisation, a
+wrong group / head / row index, a wrong sign, a transposed operand, an
+off-by-one in causality or in the window) fails at least one of them.
+
+Pin status per oracle function:
+  compress      -- pinned: library mean (uniform logits), selection (one-hot),
+                   closed-form weights 1:2:3:4, shift invariance, identity at m=1,
+                   convexity.
+  round_bf16    -- pinned: torch's float32->bfloat16 conversion, hand-checked ties.
+  n_visible     -- pinned: brute-force enumeration, the page's 1M-token counts.
+  index_scores  -- pinned: numpy matmul + ReLU at one head, linearity in w,
+                   head-permutation invariance, causal mask positions.
+  topk          -- pinned: brute-force full sort, tie-heavy inputs, k >= n_visible.
+  sparse_mqa /
+  dense_mqa     -- pinned: torch SDPA (causal MQA and banded window), scipy
+                   softmax / logsumexp on basis rows, two-row closed form,
+                   permutation invariance, CSA == HCA when k >= n_visible.
+The whole path against a trained model is parity unpinned: the pages print no
+numeric example and no weights exist.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+# --------------------------------------------------------------------------
+# compress
+# --------------------------------------------------------------------------
+def test_compress_uniform_logits_is_group_mean(orc):
+    r = rng(1)
+    B, G, m, d = 3, 5, 4, 16
+    raw = r.standard_normal((B, G * m, d)).astype(np.float32)
+    logits = np.full((B, G * m), 0.37, dtype=np.float32)
+    out = orc.compress(raw, logits, m)
+    ref = raw.astype(np.float64).reshape(B, G, m, d).mean(axis=2)
+    np.testing.assert_allclose(out, ref, rtol=1e-14, atol=1e-14)
+
+
+def test_compress_one_hot_logit_selects_token(orc):
+    r = rng(2)
+    B, G, m, d = 2, 6, 4, 8
+    raw = r.standard_normal((B, G * m, d)).astype(np.float32)
+    logits = np.zeros((B, G * m), dtype=np.float32)
+    pick = r.integers(0, m, size=(B, G))
+    for b in range(B):
+        for g in range(G):
+            logits[b, g * m + pick[b, g]] = 60.0
+    out = orc.compress(raw, logits, m)
+    for b in range(B):
+        for g in range(G):
+            np.testing.assert_allclose(out[b, g], raw[b, g * m + pick[b, g]], rtol=0, atol=1e-24)
+
+
+def test_compress_closed_form_weights(orc):
+    # logits log(1..4) give softmax weights exactly 0.1, 0.2, 0.3, 0.4
+    r = rng(3)
+    B, G, m, d = 1, 3, 4, 5
+    raw = r.standard_normal((B, G * m, d)).astype(np.float32)
+    logits = np.tile(np.log(np.arange(1, 5, dtype=np.float64)).astype(np.float32), G)[None]
+    out = orc.compress(raw, logits, m)
+    a = np.exp(logits.astype(np.float64).reshape(G, m))
+    a = a / a.sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(a, np.tile([0.1, 0.2, 0.3, 0.4], (G, 1)), rtol=1e-6)
+    ref = np.einsum("gi,gix->gx", a, raw[0].astype(np.float64).reshape(G, m, d))
+    np.testing.assert_allclose(out[0], ref, rtol=1e-13, atol=1e-14)
+
+
+def test_compress_shift_invariance_and_convexity(orc):
+    r = rng(4)
+    B, G, m, d = 2, 4, 128, 12
+    raw = r.standard_normal((B, G * m, d)).astype(np.float32)
+    logits = r.standard_normal((B, G * m)).astype(np.float32)
+    shift = np.repeat(r.uniform(-500, 500, size=(B, G)), m, axis=1).astype(np.float32)
+    a = orc.compress(raw, logits, m)
+    b = orc.compress(raw, (logits.astype(np.float64) + shift).astype(np.float32), m)
+    # the shifted logits are rounded to float32, so compare loosely; exact shift below
+    assert np.max(np.abs(a - b)) < 1e-3
+    big = orc.compress(raw, logits + np.float32(1000.0), m)  # exact in float32 for |z|<8? no: check finite
+    assert np.all(np.isfinite(big))
+    grp = raw.astype(np.float64).reshape(B, G, m, d)
+    assert np.all(a <= grp.max(axis=2) + 1e-12) and np.all(a >= grp.min(axis=2) - 1e-12)
+
+
+def test_compress_m1_identity(orc):
+    r = rng(5)
+    raw = r.standard_normal((2, 9, 7)).astype(np.float32)
+    logits = r.standard_normal((2, 9)).astype(np.float32)
+    np.testing.assert_array_equal(orc.compress(raw, logits, 1), raw.astype(np.float64))
+
+
+def test_compress_batches_and_groups_independent(orc):
+    r = rng(6)
+    B, G, m, d = 4, 3, 4, 6
+    raw = r.standard_normal((B, G * m, d)).astype(np.float32)
+    logits = r.standard_normal((B, G * m)).astype(np.float32)
+    full = orc.compress(raw, logits, m)
+    perm = [2, 0, 3, 1]
+    np.testing.assert_array_equal(orc.compress(raw[perm], logits[perm], m), full[perm])
+    gp = [1, 2, 0]
+    raw_g = raw.reshape(B, G, m, d)[:, gp].reshape(B, G * m, d)
+    log_g = logits.reshape(B, G, m)[:, gp].reshape(B, G * m)
+    np.testing.assert_array_equal(orc.compress(raw_g, log_g, m), full[:, gp])
+
+
+# --------------------------------------------------------------------------
+# bf16 rounding of the compressed cache
+# --------------------------------------------------------------------------
+def test_round_bf16_matches_torch_on_float32_values(orc):
+    r = rng(7)
+    x = np.concatenate([r.standard_normal(20000) * 10.0 ** r.integers(-30, 30, 20000),
+                        [0.0, -0.0, 1.0, -2.5, 3.0e38, 1e-39]]).astype(np.float32)
+    mine = orc.round_bf16(x.astype(np.float64))
+    ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    np.testing.assert_array_equal(mine, ref)
+
+
+def test_round_bf16_ties_to_even(orc):
+    u = 2.0 ** -7  # bf16 spacing in [1, 2)
+    x = np.array([1 + u / 2, 1 + 1.5 * u, 1 + u / 2 + 2 ** -40, -(1 + 1.5 * u)])
+    np.testing.assert_array_equal(orc.round_bf16(x), np.array([1.0, 1 + 2 * u, 1 + u, -(1 + 2 * u)],
+                                                              dtype=np.float32))
+
+
+# --------------------------------------------------------------------------
+# causal bookkeeping
+# --------------------------------------------------------------------------
+def test_n_visible_page_counts(orc):
+    with open(os.path.join(GOLDEN, "page_counts.json")) as f:
+        g = json.load(f)
+    for case in g["cases"]:
+        T, m = case["tokens"], case["m"]
+        n = orc.n_visible(T - 1, m, 1 << 40)
+        assert n == case["entries"]
+        lo, hi = case.get("page_range", [n, n])
+        assert lo <= n <= hi
+
+
+def test_n_visible_brute_force(orc):
+    for m in (1, 2, 3, 4, 128):
+        for N in (0, 1, 3, 1000):
+            for t in range(-2, 300):
+                brute = sum(1 for g in range(N) if g * m + m - 1 <= t)
+                assert orc.n_visible(t, m, N) == brute, (m, N, t)
+
+
+def test_window_start(orc):
+    for W in (1, 4, 64):
+        for t in range(0, 100):
+            brute = [p for p in range(0, t + 1) if t - p < W]
+            assert orc.window_start(t, W) == brute[0]
+
+
+# --------------------------------------------------------------------------
+# lightning indexer
+# --------------------------------------------------------------------------
+def _idx_inputs(seed, B, Tq, N, HI, dI):
+    r = rng(seed)
+    q = (r.standard_normal((B, Tq, HI, dI)) / np.sqrt(dI)).astype(np.float32)
+    w = r.uniform(0, 1, (B, Tq, HI)).astype(np.float32)
+    k = (r.standard_normal((B, N, dI)) / np.sqrt(dI)).astype(np.float32)
+    return q, w, k
+
+
+def test_index_single_head_is_relu_matmul(orc):
+    q, w, k = _idx_inputs(10, 2, 5, 40, 1, 16)
+    w[:] = 1.0
+    m, q_pos0 = 1, 100  # every entry visible
+    s = orc.index_scores(q, w, k, m, q_pos0)
+    for b in range(2):
+        ref = np.maximum(q[b, :, 0].astype(np.float64) @ k[b].astype(np.float64).T, 0.0)
+        np.testing.assert_allclose(s[b], ref, rtol=1e-13, atol=1e-15)
+
+
+def test_index_one_hot_head_weight(orc):
+    q, w, k = _idx_inputs(11, 1, 3, 30, 4, 8)
+    for h in range(4):
+        wh = np.zeros_like(w)
+        wh[..., h] = 1.0
+        s = orc.index_scores(q, wh, k, 1, 100)
+        ref = np.maximum(q[0, :, h].astype(np.float64) @ k[0].astype(np.float64).T, 0.0)
+        np.testing.assert_allclose(s[0], ref, rtol=1e-13, atol=1e-15)
+
+
+def test_index_linear_in_w_and_head_permutation(orc):
+    q, w, k = _idx_inputs(12, 2, 4, 50, 4, 32)
+    w2 = rng(13).uniform(-1, 1, w.shape).astype(np.float32)
+    s1 = orc.index_scores(q, w, k, 1, 100)
+    s2 = orc.index_scores(q, w2, k, 1, 100)
+    s12 = orc.index_scores(q, (w.astype(np.float64) + w2).astype(np.float32), k, 1, 100)
+    # w + w2 is rounded to float32; linearity holds up to that rounding
+    np.testing.assert_allclose(s12, s1 + s2, rtol=1e-6, atol=1e-6)
+    perm = [2, 0, 3, 1]
+    sp = orc.index_scores(q[:, :, perm], w[:, :, perm], k, 1, 100)
+    np.testing.assert_allclose(sp, s1, rtol=1e-13, atol=1e-15)
+    # scaling w by a positive constant scales the scores
+    np.testing.assert_allclose(orc.index_scores(q, w * np.float32(4.0), k, 1, 100), 4.0 * s1, rtol=1e-13)
+
+
+def test_index_relu_drops_negative_dots(orc):
+    dI = 4
+    q = np.array([[[[1, 0, 0, 0], [0, 1, 0, 0]]]], dtype=np.float32)  # B=1,Tq=1,HI=2
+    w = np.array([[[2.0, 3.0]]], dtype=np.float32)
+    k = np.array([[[1, 1, 0, 0], [-1, 1, 0, 0], [1, -1, 0, 0], [-1, -1, 0, 0]]], dtype=np.float32)
+    s = orc.index_scores(q, w, k, 1, 10)
+    np.testing.assert_array_equal(s[0, 0], [5.0, 3.0, 2.0, 0.0])
+
+
+def test_index_causal_mask(orc):
+    B, Tq, N, m = 1, 40, 20, 4
+    q, w, k = _idx_inputs(14, B, Tq, N, 2, 8)
+    q_pos0 = 3
+    s = orc.index_scores(q, w, k, m, q_pos0)
+    for ti in range(Tq):
+        t = q_pos0 + ti
+        nv = min(N, (t + 1) // m)
+        assert np.all(np.isfinite(s[0, ti, :nv])) and np.all(s[0, ti, nv:] == -np.inf), ti
+
+
+# --------------------------------------------------------------------------
+# top-k
+# --------------------------------------------------------------------------
+def _brute_topk(s, nv, k):
+    order = sorted(range(nv), key=lambda j: (-s[j], j))[:k]
+    out = sorted(order) + [-1] * (k - min(k, nv))
+    return out
+
+
+@pytest.mark.parametrize("kind", ["random", "ties"])
+def test_topk_equals_brute_force_sort(orc, kind):
+    r = rng(20)
+    B, Tq, N, m, k = 2, 30, 64, 2, 10
+    if kind == "random":
+        s = r.standard_normal((B, Tq, N))
+    else:
+        s = r.integers(0, 3, (B, Tq, N)).astype(np.float64)
+    q_pos0 = 0
+    for ti in range(Tq):
+        nv = min(N, (q_pos0 + ti + 1) // m)
+        s[:, ti, nv:] = -np.inf
+    idx = orc.topk(s, k, m, q_pos0)
+    for b in range(B):
+        for ti in range(Tq):
+            nv = min(N, (q_pos0 + ti + 1) // m)
+            assert list(idx[b, ti]) == _brute_topk(list(s[b, ti]), nv, k), (b, ti)
+
+
+def test_topk_k_at_least_visible_selects_all(orc):
+    s = rng(21).standard_normal((1, 3, 12))
+    idx = orc.topk(s, 16, 1, 5)  # n_visible = 6, 7, 8
+    for ti, nv in enumerate((6, 7, 8)):
+        assert list(idx[0, ti]) == list(range(nv)) + [-1] * (16 - nv)
+
+
+def test_topk_positive_scaling_invariance(orc):
+    q, w, k = _idx_inputs(22, 1, 6, 200, 4, 16)
+    s = orc.index_scores(q, w, k, 1, 500)
+    s3 = orc.index_scores(q, w * np.float32(0.125), k, 1, 500)
+    np.testing.assert_array_equal(orc.topk(s, 17, 1, 500), orc.topk(s3, 17, 1, 500))
+
+
+# --------------------------------------------------------------------------
+# attention
+# --------------------------------------------------------------------------
+def _sdpa_mqa(q, c, mask):
+    """torch SDPA in float64 on the CPU; K = V = c shared by every head."""
+    Tq, H, d = q.shape
+    qt = torch.from_numpy(q.astype(np.float64)).permute(1, 0, 2)  # [H, Tq, d]
+    kv = torch.from_numpy(c.astype(np.float64))[None].expand(H, -1, -1)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kv, kv, attn_mask=torch.from_numpy(mask))
+    return o.permute(1, 0, 2).numpy()
+
+
+def test_hca_m1_no_window_is_causal_mqa(orc):
+    r = rng(30)
+    T, H, d = 24, 3, 16
+    c = r.standard_normal((1, T, d)).astype(np.float32)
+    q = r.standard_normal((1, T, H, d)).astype(np.float32)
+    entries = orc.compress(c, r.standard_normal((1, T)).astype(np.float32), 1).astype(np.float32)
+    out, lse = orc.dense_mqa(q, entries, c, 0, 1, 0, 0)
+    mask = np.tril(np.ones((T, T), dtype=bool))
+    np.testing.assert_allclose(out[0], _sdpa_mqa(q[0], c[0], mask), rtol=1e-12, atol=1e-12)
+
+
+def test_csa_m1_k_ge_T_no_window_is_causal_mqa(orc):
+    r = rng(31)
+    T, H, d = 20, 2, 8
+    c = r.standard_normal((1, T, d)).astype(np.float32)
+    q = r.standard_normal((1, T, H, d)).astype(np.float32)
+    qi, wi, ki = _idx_inputs(32, 1, T, T, 2, 8)
+    s = orc.index_scores(qi, wi, ki, 1, 0)
+    idx = orc.topk(s, T + 3, 1, 0)
+    out, _ = orc.sparse_mqa(q, c, idx, c, 0, 0, 0)
+    mask = np.tril(np.ones((T, T), dtype=bool))
+    np.testing.assert_allclose(out[0], _sdpa_mqa(q[0], c[0], mask), rtol=1e-12, atol=1e-12)
+
+
+def test_window_only_is_banded_mqa(orc):
+    # t < m-1 for every query: no complete group, only the sliding window
+    r = rng(33)
+    T, H, d, W = 30, 2, 8, 5
+    c = r.standard_normal((1, T, d)).astype(np.float32)
+    q = r.standard_normal((1, T, H, d)).astype(np.float32)
+    idx = np.full((1, T, 4), -1, dtype=np.int32)
+    entries = np.zeros((1, 1, d), dtype=np.float32)
+    out, _ = orc.sparse_mqa(q, entries, idx, c, 0, W, 0)
+    i = np.arange(T)
+    mask = (i[None, :] <= i[:, None]) & (i[:, None] - i[None, :] < W)
+    np.testing.assert_allclose(out[0], _sdpa_mqa(q[0], c[0], mask), rtol=1e-12, atol=1e-12)
+    out2, _ = orc.dense_mqa(q, entries, c, 0, 128, W, 0)
+    np.testing.assert_allclose(out2, out, rtol=0, atol=0)
+
+
+def test_attention_basis_rows_give_softmax_and_lse(orc):
+    r = rng(34)
+    n, d, H = 6, 8, 3
+    entries = np.eye(d, dtype=np.float32)[None, :n]  # entry j = basis vector e_j
+    q = r.standard_normal((1, 1, H, d)).astype(np.float32) * 3
+    idx = np.array([[[0, 1, 2, 3, 4, 5, -1, -1]]], dtype=np.int32)
+    raw = np.zeros((1, 1, d), dtype=np.float32)
+    scale = 0.7
+    out, lse = orc.sparse_mqa(q, entries, idx, raw, 0, 0, 0, scale=scale)
+    logits = scale * q[0, 0, :, :n].astype(np.float64)
+    np.testing.assert_allclose(out[0, 0, :, :n], scipy.special.softmax(logits, axis=1), rtol=1e-13)
+    np.testing.assert_array_equal(out[0, 0, :, n:], 0.0)
+    np.testing.assert_allclose(out[0, 0].sum(axis=1), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(lse[0, 0], scipy.special.logsumexp(logits, axis=1), rtol=1e-14)
+
+
+def test_attention_two_row_closed_form(orc):
+    r = rng(35)
+    d, H = 5, 2
+    R = r.standard_normal((1, 2, d)).astype(np.float32)
+    q = r.standard_normal((1, 1, H, d)).astype(np.float32)
+    idx = np.array([[[1, -1, -1]]], dtype=np.int32)  # entry 1 selected
+    raw = R[:, :1]  # window of one raw row: position 0
+    entries = R
+    out, lse = orc.sparse_mqa(q, entries, idx, raw, 0, 1, 0, scale=1.0)
+    for h in range(H):
+        l1 = float(np.dot(q[0, 0, h].astype(np.float64), R[0, 1].astype(np.float64)))
+        l2 = float(np.dot(q[0, 0, h].astype(np.float64), R[0, 0].astype(np.float64)))
+        a1 = 1.0 / (1.0 + math.exp(l2 - l1))
+        ref = a1 * R[0, 1].astype(np.float64) + (1 - a1) * R[0, 0].astype(np.float64)
+        np.testing.assert_allclose(out[0, 0, h], ref, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lse[0, 0, h], np.logaddexp(l1, l2), rtol=1e-14)
+
+
+def test_attention_constant_rows_and_empty(orc):
+    r = rng(36)
+    d = 6
+    row = r.standard_normal(d).astype(np.float32)
+    entries = np.tile(row, (1, 10, 1))
+    raw = np.tile(row, (1, 4, 1))
+    q = r.standard_normal((1, 1, 2, d)).astype(np.float32)
+    idx = np.array([[[0, 3, 7, 9]]], dtype=np.int32)
+    out, _ = orc.sparse_mqa(q, entries, idx, raw, 0, 4, 3)
+    np.testing.assert_allclose(out[0, 0], np.tile(row.astype(np.float64), (2, 1)), rtol=1e-14)
+    empty = np.full((1, 1, 4), -1, dtype=np.int32)
+    out, lse = orc.sparse_mqa(q, entries, empty, raw, 0, 0, 3)
+    assert np.all(out == 0.0) and np.all(lse == -np.inf)
+
+
+def test_attention_permuting_selection_changes_nothing(orc):
+    r = rng(37)
+    B, N, d, H, k, W = 2, 40, 16, 4, 12, 3
+    entries = r.standard_normal((B, N, d)).astype(np.float32)
+    raw = r.standard_normal((B, 5, d)).astype(np.float32)
+    q = r.standard_normal((B, 1, H, d)).astype(np.float32)
+    idx = np.stack([np.sort(r.choice(N, k, replace=False)) for _ in range(B)])[:, None].astype(np.int32)
+    a, la = orc.sparse_mqa(q, entries, idx, raw, 100, W, 104)
+    pidx = idx[:, :, r.permutation(k)]
+    b, lb = orc.sparse_mqa(q, entries, pidx, raw, 100, W, 104)
+    np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(la, lb, rtol=1e-14)
+    # a window row added at the raw buffer's far end does not change a W-row window
+    raw2 = np.concatenate([r.standard_normal((B, 1, d)).astype(np.float32), raw], axis=1)
+    c, _ = orc.sparse_mqa(q, entries, idx, raw2, 99, W, 104)
+    np.testing.assert_allclose(c, a, rtol=1e-13, atol=1e-15)
+
+
+def test_csa_with_k_ge_visible_equals_hca(orc):
+    r = rng(38)
+    B, T, m, d, H, W = 2, 64, 4, 16, 4, 6
+    Tq = 9
+    q_pos0 = T - Tq
+    N = T // m
+    entries = r.standard_normal((B, N, d)).astype(np.float32)
+    raw = r.standard_normal((B, T, d)).astype(np.float32)
+    q = r.standard_normal((B, Tq, H, d)).astype(np.float32)
+    qi, wi, ki = _idx_inputs(39, B, Tq, N, 2, 8)
+    s = orc.index_scores(qi, wi, ki, m, q_pos0)
+    idx = orc.topk(s, N, m, q_pos0)
+    a, la = orc.sparse_mqa(q, entries, idx, raw, 0, W, q_pos0)
+    b, lb = orc.dense_mqa(q, entries, raw, 0, m, W, q_pos0)
+    np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(la, lb, rtol=1e-14)
