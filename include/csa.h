@@ -1,0 +1,174 @@
+/*
+ * csa.h -- C ABI of the MI355X (gfx950) compressed-attention library libcsa.so.
+ *
+ * The library computes one layer of DeepSeek-V4's hybrid compressed
+ * attention, as the DeepSeek-V4 overview page (gitcode.csdn.net) states it
+ * in section 2 ("hybrid attention architecture"):
+ *
+ *   csa_compress    -- section 2.2, CSA step 1 (and 2.3 for HCA): every m
+ *                      adjacent tokens' KV latents are pooled into one entry
+ *                      with weights from a softmax over learned logits.
+ *   csa_index_topk  -- section 2.2, step 2: a lightweight "lightning indexer"
+ *                      scores the query against every causally visible entry
+ *                      and only the top-k entries are kept.
+ *   csa_sparse_mqa  -- section 2.2, step 3: the kept entries serve as both key
+ *                      and value, shared by all query heads (multi-query
+ *                      attention), in one softmax with a window of recent raw
+ *                      tokens.
+ *   hca_dense_mqa   -- section 2.3: the same attention over every visible
+ *                      entry (no selection), for m=128 compression.
+ *
+ * Conventions common to every call
+ * --------------------------------
+ * Memory.   Every tensor argument is a DEVICE pointer to caller-owned memory.
+ *           The library never allocates, frees, synchronises or prints, and
+ *           keeps no state between calls except a per-thread error string.
+ * Streams.  `stream` is a hipStream_t passed as void*.  NULL is the default
+ *           stream.  Every call only enqueues work on that stream and returns;
+ *           a fault during execution surfaces at the caller's next
+ *           synchronisation on that stream.
+ * Types.    `dt` (csa_dtype_t) is the element type of raw latents, compressed
+ *           entries, queries and indexer keys/queries: CSA_F32 or CSA_BF16.
+ *           Pooling logits, indexer head weights, scores, outputs and lse are
+ *           always float32; selections are int32.  Arithmetic is float32
+ *           (bf16 products are exact in float32; sums accumulate in float32).
+ * Layout.   Row-major with the innermost dimension packed.  The batch stride of
+ *           raw / entries / indexer keys is an explicit argument in ELEMENTS,
+ *           so a cache may have capacity beyond N.  Every tensor pointer must
+ *           be 16-byte aligned and every batch stride a multiple of 8 elements.
+ * Position. A query's absolute position is t = q_pos0 + i for query row i.
+ *           Compressed entry g covers positions [g*m, g*m+m); it is visible to
+ *           t when g*m+m-1 <= t, so n_visible(t) = min(N, floor((t+1)/m)).
+ *           The window of t is positions max(0, t-W+1) .. t (W rows, t
+ *           included); raw row r of a batch holds position raw_pos0 + r.
+ * Errors.   Every call returns 0 (CSA_OK) or a negative csa_status_t.  On an
+ *           error nothing has been enqueued; csa_last_error_detail() (per
+ *           thread) says which argument was wrong.  CSA_EHIP reports a failed
+ *           kernel launch.
+ * Sizes.    d in {32, 64, 128, 256, 512}; d_I in {32, 64, 128}; H <= 64;
+ *           H_I <= 64; m in 1..128; 0 < k <= 2048.  Other values return
+ *           CSA_EUNSUPPORTED.
+ */
+#ifndef CSA_H_
+#define CSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CSA_OK = 0,
+    CSA_EINVAL = -1,       /* inconsistent sizes, positions or NULL pointers   */
+    CSA_EDTYPE = -2,       /* unknown element type                             */
+    CSA_EALIGN = -3,       /* pointer or stride not aligned as required        */
+    CSA_EWORKSPACE = -4,   /* workspace smaller than *_workspace_bytes() says  */
+    CSA_EHIP = -5,         /* a kernel launch failed                           */
+    CSA_EUNSUPPORTED = -6  /* size outside the supported set                   */
+} csa_status_t;
+
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype_t;
+
+/* Version of this ABI (incremented on any incompatible change). */
+int csa_abi_version(void);
+/* Static description of a status code. */
+const char *csa_status_string(int status);
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char *csa_last_error_detail(void);
+
+/*
+ * csa_compress -- group compression (overview page, section 2.2 step 1;
+ * section 2.3 for m=128).  For batch b and group g < G:
+ *     alpha_i = softmax_i(logits[b, g*m + i]),  i < m
+ *     out[b, g, :] = sum_i alpha_i * raw[b, g*m + i, :]
+ * rounded once to `dt` (round-to-nearest-even for bf16).
+ *   raw     [B, G*m, d]  dt,  batch stride raw_bstride elements
+ *   logits  [B, G*m]     f32, batch stride logit_bstride elements
+ *   out     [B, G, d]    dt,  batch stride out_bstride elements (may point
+ *                        into a cache at entry g0: out = cache + g0*d)
+ * `out` must not overlap `raw` or `logits`.
+ */
+int csa_compress(int dt, int B, int G, int m, int d,
+                 const void *raw, int64_t raw_bstride,
+                 const float *logits, int64_t logit_bstride,
+                 void *out, int64_t out_bstride, void *stream);
+
+/*
+ * csa_index_topk -- lightning indexer and per-query top-k (overview page,
+ * section 2.2 step 2; indexer form fixed as a sum over index heads of a
+ * head weight times ReLU of a query-key dot product).  For query row i of
+ * batch b at position t = q_pos0 + i and entry j < n_visible(t):
+ *     s[j] = sum_h w_idx[b,i,h] * max(0, q_idx[b,i,h,:] . k_idx[b,j,:])
+ * The k entries first in the order (s descending, j ascending) are kept; if
+ * n_visible(t) <= k all visible entries are kept.  topk_idx[b,i,:] holds
+ * the kept indices in ascending order followed by -1 padding.
+ *   q_idx     [B, Tq, H_I, d_I]  dt
+ *   w_idx     [B, Tq, H_I]       f32
+ *   k_idx     [B, N, d_I]        dt, batch stride k_bstride elements
+ *   topk_idx  [B, Tq, k]         int32 (output)
+ *   scores_out optional [B, Tq, N] f32 (output): s[j] for visible j, -inf
+ *             for j >= n_visible(t).  NULL: scores stay in the workspace.
+ *   workspace device scratch of at least
+ *             csa_index_topk_workspace_bytes(B, Tq, N, H_I, k) bytes.
+ * Scores must not be NaN (inputs must be finite).
+ */
+size_t csa_index_topk_workspace_bytes(int B, int Tq, int N, int H_I, int k);
+int csa_index_topk(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k,
+                   int64_t q_pos0,
+                   const void *q_idx, const float *w_idx,
+                   const void *k_idx, int64_t k_bstride,
+                   int32_t *topk_idx, float *scores_out,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * csa_sparse_mqa -- shared-KV multi-query attention over the selected
+ * entries plus the raw window, one softmax (overview page, section 2.2
+ * step 3: selected entries act as both key and value, all heads share them).
+ * For query row i (position t) the row set is
+ *     R = { entries[b, j] : j in topk_idx[b,i,:], 0 <= j < n_visible(t) }
+ *       + { raw[b, p - raw_pos0] : max(0, t-W+1) <= p <= t }
+ * (slots holding -1 or an index outside [0, n_visible(t)) are skipped), and
+ * for every head h
+ *     l_r = scale * q[b,i,h,:] . R_r,   o = sum_r softmax(l)_r R_r,
+ *     lse = log sum_r exp(l_r).
+ * An empty row set gives o = 0 and lse = -inf.
+ *   q         [B, Tq, H, d]    dt
+ *   entries   [B, N, d]        dt, batch stride e_bstride elements
+ *   topk_idx  [B, Tq, k]       int32
+ *   raw       [B, raw_len, d]  dt, batch stride raw_bstride elements;
+ *             must cover the window: raw_pos0 <= max(0, q_pos0-W+1) and
+ *             raw_pos0 + raw_len >= q_pos0 + Tq  (checked, CSA_EINVAL)
+ *   out       [B, Tq, H, d]    f32 (output)
+ *   lse       [B, Tq, H]       f32 (output, optional: NULL)
+ *   workspace at least csa_mqa_workspace_bytes(B, Tq, H, d, k + W) bytes.
+ */
+size_t csa_mqa_workspace_bytes(int B, int Tq, int H, int d, int n_rows_max);
+int csa_sparse_mqa(int dt, int B, int Tq, int H, int d, int N, int m, int k, int W,
+                   int64_t q_pos0, float scale,
+                   const void *q,
+                   const void *entries, int64_t e_bstride,
+                   const int32_t *topk_idx,
+                   const void *raw, int64_t raw_bstride, int64_t raw_pos0, int raw_len,
+                   float *out, float *lse,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * hca_dense_mqa -- HCA attention (overview page, section 2.3: no sparse
+ * selection, dense attention over all compressed entries).  Same as
+ * csa_sparse_mqa with the row set { entries[b, j] : j < n_visible(t) } plus
+ * the same raw window.  workspace: csa_mqa_workspace_bytes(B, Tq, H, d, N + W).
+ */
+int hca_dense_mqa(int dt, int B, int Tq, int H, int d, int N, int m, int W,
+                  int64_t q_pos0, float scale,
+                  const void *q,
+                  const void *entries, int64_t e_bstride,
+                  const void *raw, int64_t raw_bstride, int64_t raw_pos0, int raw_len,
+                  float *out, float *lse,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H_ */

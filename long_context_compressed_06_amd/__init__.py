@@ -1,0 +1,209 @@
+"""Python binding of libcsa.so: DeepSeek-V4 hybrid compressed attention on MI355X.
+
+Thin ctypes layer with the same names as the C ABI (``include/csa.h``).  Each
+function checks that the torch tensors it receives are contiguous CUDA (HIP)
+tensors of the expected dtype, then passes raw device pointers and the
+current stream to the library.  Every step of the path runs in the HIP
+kernels; PyTorch only provides device memory and the stream.  If libcsa.so
+is missing the import of the library fails loudly: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsa.so")
+
+CSA_F32, CSA_BF16 = 0, 1
+_STATUS = {0: "CSA_OK", -1: "CSA_EINVAL", -2: "CSA_EDTYPE", -3: "CSA_EALIGN", -4: "CSA_EWORKSPACE",
+           -5: "CSA_EHIP", -6: "CSA_EUNSUPPORTED"}
+EXPORTS = ("csa_abi_version", "csa_status_string", "csa_last_error_detail", "csa_compress",
+           "csa_index_topk_workspace_bytes", "csa_index_topk", "csa_mqa_workspace_bytes", "csa_sparse_mqa",
+           "hca_dense_mqa")
+
+
+class CsaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+_lib = None
+
+
+def lib():
+    """Load libcsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    L.csa_abi_version.restype = I
+    L.csa_status_string.argtypes = [I]
+    L.csa_status_string.restype = ctypes.c_char_p
+    L.csa_last_error_detail.restype = ctypes.c_char_p
+    L.csa_compress.argtypes = [I, I, I, I, I, P, I64, P, I64, P, I64, P]
+    L.csa_compress.restype = I
+    L.csa_index_topk_workspace_bytes.argtypes = [I, I, I, I, I]
+    L.csa_index_topk_workspace_bytes.restype = SZ
+    L.csa_index_topk.argtypes = [I, I, I, I, I, I, I, I, I64, P, P, P, I64, P, P, P, SZ, P]
+    L.csa_index_topk.restype = I
+    L.csa_mqa_workspace_bytes.argtypes = [I, I, I, I, I]
+    L.csa_mqa_workspace_bytes.restype = SZ
+    L.csa_sparse_mqa.argtypes = [I, I, I, I, I, I, I, I, I, I64, F, P, P, I64, P, P, I64, I64, I, P, P, P, SZ, P]
+    L.csa_sparse_mqa.restype = I
+    L.hca_dense_mqa.argtypes = [I, I, I, I, I, I, I, I, I64, F, P, P, I64, P, I64, I64, I, P, P, P, SZ, P]
+    L.hca_dense_mqa.restype = I
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise CsaError(status, lib().csa_last_error_detail().decode())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return CSA_F32
+    if t.dtype == torch.bfloat16:
+        return CSA_BF16
+    raise TypeError(f"element type {t.dtype} is neither float32 nor bfloat16")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, name, dtype=None, dims=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if dims is not None and t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dimensions, got {t.dim()}")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name} needs a packed innermost dimension")
+
+
+def _bstride(t):
+    return t.stride(0)
+
+
+def csa_compress(raw: torch.Tensor, logits: torch.Tensor, m: int, out: torch.Tensor) -> torch.Tensor:
+    """raw [B, G*m, d], logits [B, G*m] f32 -> out [B, G, d] (written in place, may be a cache view)."""
+    _need(raw, "raw", dims=3)
+    _need(logits, "logits", torch.float32, 2)
+    _need(out, "out", raw.dtype, 3)
+    B, Gm, d = raw.shape
+    if Gm % m:
+        raise ValueError("raw rows must be a multiple of m")
+    G = Gm // m
+    for t, n in ((raw, "raw"), (out, "out")):
+        if t.stride(1) != d:
+            raise ValueError(f"{n} rows must be packed")
+    if out.shape != (B, G, d) or logits.shape != (B, Gm) or logits.stride(1) != 1:
+        raise ValueError("shape mismatch between raw, logits and out")
+    _check(lib().csa_compress(_dt(raw), B, G, m, d, _p(raw), _bstride(raw), _p(logits), _bstride(logits), _p(out),
+                              _bstride(out), _stream(raw)))
+    return out
+
+
+def index_topk_workspace_bytes(B, Tq, N, H_I, k) -> int:
+    return int(lib().csa_index_topk_workspace_bytes(B, Tq, N, H_I, k))
+
+
+def csa_index_topk(q_idx, w_idx, k_idx, N: int, m: int, k: int, q_pos0: int, topk_idx=None, scores_out=None,
+                   workspace=None) -> torch.Tensor:
+    """q_idx [B,Tq,H_I,d_I], w_idx [B,Tq,H_I] f32, k_idx [B,cap,d_I] (first N rows used) -> topk_idx [B,Tq,k] int32."""
+    _need(q_idx, "q_idx", dims=4)
+    _need(w_idx, "w_idx", torch.float32, 3)
+    _need(k_idx, "k_idx", q_idx.dtype, 3)
+    B, Tq, HI, dI = q_idx.shape
+    if not q_idx.is_contiguous() or not w_idx.is_contiguous() or k_idx.stride(1) != dI or k_idx.shape[1] < N:
+        raise ValueError("q_idx/w_idx must be contiguous and k_idx rows packed with >= N rows")
+    if topk_idx is None:
+        topk_idx = torch.empty((B, Tq, k), dtype=torch.int32, device=q_idx.device)
+    _need(topk_idx, "topk_idx", torch.int32, 3)
+    if scores_out is not None:
+        _need(scores_out, "scores_out", torch.float32, 3)
+        if scores_out.shape != (B, Tq, N) or not scores_out.is_contiguous():
+            raise ValueError("scores_out must be a contiguous [B, Tq, N] tensor")
+    need = index_topk_workspace_bytes(B, Tq, N, HI, k)
+    if workspace is None and scores_out is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_idx.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().csa_index_topk(_dt(q_idx), B, Tq, N, HI, dI, m, k, q_pos0, _p(q_idx), _p(w_idx), _p(k_idx),
+                                _bstride(k_idx), _p(topk_idx), _p(scores_out), _p(workspace), ws_bytes,
+                                _stream(q_idx)))
+    return topk_idx
+
+
+def mqa_workspace_bytes(B, Tq, H, d, n_rows_max) -> int:
+    return int(lib().csa_mqa_workspace_bytes(B, Tq, H, d, n_rows_max))
+
+
+def _mqa_checks(q, entries, raw, out, lse):
+    _need(q, "q", dims=4)
+    _need(entries, "entries", q.dtype, 3)
+    _need(raw, "raw", q.dtype, 3)
+    B, Tq, H, d = q.shape
+    if not q.is_contiguous() or entries.stride(1) != d or raw.stride(1) != d:
+        raise ValueError("q must be contiguous and entries/raw rows packed")
+    if out is None:
+        out = torch.empty((B, Tq, H, d), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, 4)
+    if out.shape != (B, Tq, H, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, Tq, H, d] float32 tensor")
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 3)
+        if lse.shape != (B, Tq, H) or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous [B, Tq, H] float32 tensor")
+    return B, Tq, H, d, out
+
+
+def csa_sparse_mqa(q, entries, topk_idx, raw, N: int, m: int, W: int, q_pos0: int, raw_pos0: int,
+                   scale: float | None = None, out=None, lse=None, workspace=None):
+    """Sparse shared-KV MQA over topk_idx rows plus the raw window -> out [B,Tq,H,d] f32 (and lse if given)."""
+    B, Tq, H, d, out = _mqa_checks(q, entries, raw, out, lse)
+    _need(topk_idx, "topk_idx", torch.int32, 3)
+    if topk_idx.shape[:2] != (B, Tq) or not topk_idx.is_contiguous():
+        raise ValueError("topk_idx must be a contiguous [B, Tq, k] tensor")
+    k = topk_idx.shape[2]
+    scale = (1.0 / d ** 0.5) if scale is None else scale
+    need = mqa_workspace_bytes(B, Tq, H, d, k + W)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().csa_sparse_mqa(_dt(q), B, Tq, H, d, N, m, k, W, q_pos0, scale, _p(q), _p(entries),
+                                _bstride(entries), _p(topk_idx), _p(raw), _bstride(raw), raw_pos0, raw.shape[1],
+                                _p(out), _p(lse), _p(workspace), ws_bytes, _stream(q)))
+    return out
+
+
+def hca_dense_mqa(q, entries, raw, N: int, m: int, W: int, q_pos0: int, raw_pos0: int, scale: float | None = None,
+                  out=None, lse=None, workspace=None):
+    """Dense shared-KV MQA over all visible entries plus the raw window -> out [B,Tq,H,d] f32."""
+    B, Tq, H, d, out = _mqa_checks(q, entries, raw, out, lse)
+    scale = (1.0 / d ** 0.5) if scale is None else scale
+    need = mqa_workspace_bytes(B, Tq, H, d, N + W)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().hca_dense_mqa(_dt(q), B, Tq, H, d, N, m, W, q_pos0, scale, _p(q), _p(entries), _bstride(entries),
+                               _p(raw), _bstride(raw), raw_pos0, raw.shape[1], _p(out), _p(lse), _p(workspace),
+                               ws_bytes, _stream(q)))
+    return out
+
+
+from .step import AttentionStep  # noqa: E402  (uses the functions above)

@@ -1,0 +1,233 @@
+// extern "C" boundary of libcsa: argument checking, workspace sizing, status
+// strings and dispatch to the kernel launchers.  Nothing here allocates,
+// synchronises or throws; every error returns before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/csa.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_detail;
+
+int fail(int status, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_detail = buf;
+    return status;
+}
+
+int ok() {
+    g_detail.clear();
+    return CSA_OK;
+}
+
+bool d_supported(int d) { return d == 32 || d == 64 || d == 128 || d == 256 || d == 512; }
+bool dI_supported(int d) { return d == 32 || d == 64 || d == 128; }
+size_t esize(int dt) { return dt == CSA_F32 ? 4 : 2; }
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// byte range [lo, hi) of a batched tensor: B batches of `inner` elements, `bstride` apart
+struct Span {
+    uintptr_t lo, hi;
+};
+Span span(const void *p, int64_t B, int64_t bstride, int64_t inner, size_t es) {
+    Span s{(uintptr_t)p, (uintptr_t)p};
+    if (p && B > 0 && inner > 0) s.hi = s.lo + (size_t)((B - 1) * bstride + inner) * es;
+    return s;
+}
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int check_dt(int dt) {
+    if (dt != CSA_F32 && dt != CSA_BF16) return fail(CSA_EDTYPE, "dt=%d is neither CSA_F32 nor CSA_BF16", dt);
+    return CSA_OK;
+}
+
+int hip_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(CSA_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa_abi_version(void) { return 1; }
+
+const char *csa_status_string(int s) {
+    switch (s) {
+        case CSA_OK: return "ok";
+        case CSA_EINVAL: return "invalid argument";
+        case CSA_EDTYPE: return "unknown element type";
+        case CSA_EALIGN: return "misaligned pointer or stride";
+        case CSA_EWORKSPACE: return "workspace too small";
+        case CSA_EHIP: return "HIP launch failure";
+        case CSA_EUNSUPPORTED: return "unsupported size";
+        default: return "unknown status";
+    }
+}
+
+const char *csa_last_error_detail(void) { return g_detail.c_str(); }
+
+int csa_compress(int dt, int B, int G, int m, int d, const void *raw, int64_t raw_bstride, const float *logits,
+                 int64_t logit_bstride, void *out, int64_t out_bstride, void *stream) {
+    if (int s = check_dt(dt)) return s;
+    if (B < 0 || G < 0) return fail(CSA_EINVAL, "B=%d and G=%d must be >= 0", B, G);
+    if (m < 1 || m > 128) return fail(CSA_EUNSUPPORTED, "m=%d outside 1..128", m);
+    if (!d_supported(d)) return fail(CSA_EUNSUPPORTED, "d=%d not in {32,64,128,256,512}", d);
+    if ((int64_t)B * G == 0) return ok();
+    if (!raw || !logits || !out) return fail(CSA_EINVAL, "NULL tensor pointer");
+    if (raw_bstride < (int64_t)G * m * d || logit_bstride < (int64_t)G * m || out_bstride < (int64_t)G * d)
+        return fail(CSA_EINVAL, "a batch stride is smaller than one batch's extent");
+    if (!aligned(raw, 16) || !aligned(out, 16) || !aligned(logits, 4) || raw_bstride % 8 || out_bstride % 8)
+        return fail(CSA_EALIGN, "raw/out need 16-byte alignment and batch strides a multiple of 8 elements");
+    const size_t es = esize(dt);
+    const Span so = span(out, B, out_bstride, (int64_t)G * d, es);
+    if (overlap(so, span(raw, B, raw_bstride, (int64_t)G * m * d, es)) ||
+        overlap(so, span(logits, B, logit_bstride, (int64_t)G * m, 4)))
+        return fail(CSA_EINVAL, "out overlaps raw or logits");
+    return hip_status(csa::launch_compress(dt, B, G, m, d, raw, raw_bstride, logits, logit_bstride, out,
+                                           out_bstride, (hipStream_t)stream),
+                      "compress launch");
+}
+
+size_t csa_index_topk_workspace_bytes(int B, int Tq, int N, int H_I, int k) {
+    (void)H_I;
+    (void)k;
+    if (B <= 0 || Tq <= 0 || N <= 0) return 0;
+    const size_t scores = (size_t)B * Tq * N * sizeof(float);
+    return (scores + 255) / 256 * 256;
+}
+
+int csa_index_topk(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k, int64_t q_pos0, const void *q_idx,
+                   const float *w_idx, const void *k_idx, int64_t k_bstride, int32_t *topk_idx, float *scores_out,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+    if (int s = check_dt(dt)) return s;
+    if (B < 0 || Tq < 0 || N < 0) return fail(CSA_EINVAL, "B, Tq and N must be >= 0");
+    if (H_I < 1 || H_I > 64) return fail(CSA_EUNSUPPORTED, "H_I=%d outside 1..64", H_I);
+    if (!dI_supported(d_I)) return fail(CSA_EUNSUPPORTED, "d_I=%d not in {32,64,128}", d_I);
+    if (m < 1) return fail(CSA_EINVAL, "m=%d must be >= 1", m);
+    if (k < 1 || k > 2048) return fail(CSA_EUNSUPPORTED, "k=%d outside 1..2048", k);
+    if (q_pos0 < 0) return fail(CSA_EINVAL, "q_pos0 must be >= 0");
+    if ((int64_t)B * Tq == 0) return ok();
+    if (!q_idx || !w_idx || !topk_idx || (N > 0 && !k_idx)) return fail(CSA_EINVAL, "NULL tensor pointer");
+    if (N > 0 && k_bstride < (int64_t)N * d_I) return fail(CSA_EINVAL, "k_bstride smaller than N*d_I");
+    if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(w_idx, 4) || !aligned(topk_idx, 4) ||
+        !aligned(scores_out, 4) || k_bstride % 8)
+        return fail(CSA_EALIGN, "q_idx/k_idx need 16-byte alignment, k_bstride a multiple of 8 elements");
+    float *scores = scores_out;
+    if (!scores && N > 0) {
+        const size_t need = csa_index_topk_workspace_bytes(B, Tq, N, H_I, k);
+        if (!workspace || workspace_bytes < need)
+            return fail(CSA_EWORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+        if (!aligned(workspace, 16)) return fail(CSA_EALIGN, "workspace needs 16-byte alignment");
+        scores = (float *)workspace;
+    }
+    const size_t es = esize(dt);
+    const Span si = span(topk_idx, B, (int64_t)Tq * k, (int64_t)Tq * k, 4);
+    const Span ss = span(scores_out, B, (int64_t)Tq * N, (int64_t)Tq * N, 4);
+    const Span inputs[3] = {span(q_idx, B, (int64_t)Tq * H_I * d_I, (int64_t)Tq * H_I * d_I, es),
+                            span(w_idx, B, (int64_t)Tq * H_I, (int64_t)Tq * H_I, 4),
+                            span(k_idx, B, k_bstride, (int64_t)N * d_I, es)};
+    for (const Span &in : inputs)
+        if (overlap(si, in) || overlap(ss, in)) return fail(CSA_EINVAL, "an output overlaps an input");
+    if (overlap(si, ss)) return fail(CSA_EINVAL, "topk_idx overlaps scores_out");
+    hipStream_t st = (hipStream_t)stream;
+    if (N > 0) {
+        if (int s = hip_status(csa::launch_index_scores(dt, B, Tq, N, H_I, d_I, m, q_pos0, q_idx, w_idx, k_idx,
+                                                         k_bstride, scores, st),
+                               "indexer launch"))
+            return s;
+    }
+    return hip_status(csa::launch_topk(B, Tq, N, m, k, q_pos0, scores, topk_idx, st), "top-k launch");
+}
+
+size_t csa_mqa_workspace_bytes(int B, int Tq, int H, int d, int n_rows_max) {
+    if (B <= 0 || Tq <= 0 || H <= 0 || d <= 0) return 0;
+    int tps = 0;
+    const int64_t rows = (int64_t)B * Tq;
+    const int s = csa::mqa_choose_splits(rows, n_rows_max, &tps);
+    if (s <= 1) return 0;
+    const size_t bytes = (size_t)rows * s * H * (d + 2) * sizeof(float);
+    return (bytes + 255) / 256 * 256;
+}
+
+static int mqa_common(int dt, int B, int Tq, int H, int d, int N, int m, int k, int W, int64_t q_pos0, float scale,
+                      const void *q, const void *entries, int64_t e_bstride, const int32_t *idx, const void *raw,
+                      int64_t raw_bstride, int64_t raw_pos0, int raw_len, float *out, float *lse, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+    if (int s = check_dt(dt)) return s;
+    if (B < 0 || Tq < 0 || N < 0 || W < 0 || raw_len < 0) return fail(CSA_EINVAL, "B, Tq, N, W, raw_len must be >= 0");
+    if (H < 1 || H > 64) return fail(CSA_EUNSUPPORTED, "H=%d outside 1..64", H);
+    if (!d_supported(d)) return fail(CSA_EUNSUPPORTED, "d=%d not in {32,64,128,256,512}", d);
+    if (m < 1) return fail(CSA_EINVAL, "m=%d must be >= 1", m);
+    if (k < 0 || k > 2048) return fail(CSA_EUNSUPPORTED, "k=%d outside 1..2048", k);
+    if (!(scale > 0.f) || !std::isfinite(scale)) return fail(CSA_EINVAL, "scale must be finite and > 0");
+    if (q_pos0 < 0 || raw_pos0 < 0) return fail(CSA_EINVAL, "positions must be >= 0");
+    if ((int64_t)B * Tq == 0) return ok();
+    if (W > 0) {
+        const int64_t win0 = q_pos0 - W + 1 > 0 ? q_pos0 - W + 1 : 0;
+        if (raw_pos0 > win0 || raw_pos0 + raw_len < q_pos0 + Tq)
+            return fail(CSA_EINVAL, "raw rows [%lld, %lld) do not cover the window [%lld, %lld)", (long long)raw_pos0,
+                        (long long)(raw_pos0 + raw_len), (long long)win0, (long long)(q_pos0 + Tq));
+        if (!raw) return fail(CSA_EINVAL, "NULL raw with W > 0");
+        if (raw_bstride < (int64_t)raw_len * d) return fail(CSA_EINVAL, "raw_bstride smaller than raw_len*d");
+    }
+    if (!q || !out || (N > 0 && !entries) || (k > 0 && !idx)) return fail(CSA_EINVAL, "NULL tensor pointer");
+    if (N > 0 && e_bstride < (int64_t)N * d) return fail(CSA_EINVAL, "e_bstride smaller than N*d");
+    if (!aligned(q, 16) || !aligned(entries, 16) || !aligned(raw, 16) || !aligned(out, 16) || !aligned(idx, 4) ||
+        !aligned(lse, 4) || e_bstride % 8 || raw_bstride % 8)
+        return fail(CSA_EALIGN, "q/entries/raw/out need 16-byte alignment, strides a multiple of 8 elements");
+    const size_t es = esize(dt);
+    const Span so = span(out, B, (int64_t)Tq * H * d, (int64_t)Tq * H * d, 4);
+    const Span sl = span(lse, B, (int64_t)Tq * H, (int64_t)Tq * H, 4);
+    const Span inputs[4] = {span(q, B, (int64_t)Tq * H * d, (int64_t)Tq * H * d, es),
+                            span(entries, B, e_bstride, (int64_t)N * d, es),
+                            span(raw, B, raw_bstride, (int64_t)raw_len * d, es),
+                            span(idx, B, (int64_t)Tq * k, (int64_t)Tq * k, 4)};
+    for (const Span &in : inputs)
+        if (overlap(so, in) || overlap(sl, in)) return fail(CSA_EINVAL, "an output overlaps an input");
+    if (overlap(so, sl)) return fail(CSA_EINVAL, "out overlaps lse");
+    const int64_t rows = (int64_t)B * Tq;
+    const int64_t n_rows_max = (int64_t)(k > 0 ? k : N) + W;
+    int tps = 0;
+    const int splits = csa::mqa_choose_splits(rows, n_rows_max, &tps);
+    float *ws = nullptr;
+    if (splits > 1) {
+        const size_t need = csa_mqa_workspace_bytes(B, Tq, H, d, (int)n_rows_max);
+        if (!workspace || workspace_bytes < need)
+            return fail(CSA_EWORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+        if (!aligned(workspace, 16)) return fail(CSA_EALIGN, "workspace needs 16-byte alignment");
+        ws = (float *)workspace;
+    }
+    return hip_status(csa::launch_mqa(dt, B, Tq, H, d, N, m, k, W, q_pos0, scale, q, entries, e_bstride, idx, raw,
+                                      raw_bstride, raw_pos0, out, lse, ws, splits, tps, (hipStream_t)stream),
+                      "attention launch");
+}
+
+int csa_sparse_mqa(int dt, int B, int Tq, int H, int d, int N, int m, int k, int W, int64_t q_pos0, float scale,
+                   const void *q, const void *entries, int64_t e_bstride, const int32_t *topk_idx, const void *raw,
+                   int64_t raw_bstride, int64_t raw_pos0, int raw_len, float *out, float *lse, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+    if (k < 1 || k > 2048) return fail(CSA_EUNSUPPORTED, "k=%d outside 1..2048", k);
+    return mqa_common(dt, B, Tq, H, d, N, m, k, W, q_pos0, scale, q, entries, e_bstride, topk_idx, raw, raw_bstride,
+                      raw_pos0, raw_len, out, lse, workspace, workspace_bytes, stream);
+}
+
+int hca_dense_mqa(int dt, int B, int Tq, int H, int d, int N, int m, int W, int64_t q_pos0, float scale, const void *q,
+                  const void *entries, int64_t e_bstride, const void *raw, int64_t raw_bstride, int64_t raw_pos0,
+                  int raw_len, float *out, float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+    return mqa_common(dt, B, Tq, H, d, N, m, 0, W, q_pos0, scale, q, entries, e_bstride, nullptr, raw, raw_bstride,
+                      raw_pos0, raw_len, out, lse, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// Device-side building blocks shared by the gfx950 kernels of libcsa.
+//
+// Element types: `float` for the fp32 path and `bf16_t` (raw 16-bit storage)
+// for the bf16 path.  All arithmetic is float32.  Matrix products use the
+// CDNA MFMA instructions with 16x16 output tiles and 64-lane wavefronts:
+//   bf16: v_mfma_f32_16x16x32_bf16  (K = 32, 8 K-values per lane)
+//   fp32: v_mfma_f32_16x16x4_f32    (K = 4,  1 K-value per lane)
+// Operand layout (both instructions): lane l supplies A[l % 16][kgrp] and
+// B[kgrp][l % 16], where kgrp is the lane group g = l / 16's share of K; the
+// result tile lands with lane l holding D[4*g + e][l % 16] for e = 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa {
+
+typedef uint16_t bf16_t;
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+// round-to-nearest-even float32 -> bf16 (inputs are finite in this library)
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+template <typename T> struct Elem;
+
+template <> struct Elem<float> {
+    static constexpr int KPL = 1;    // K values held per lane by one MFMA operand
+    static constexpr int KSTEP = 4;  // K of one MFMA
+    typedef float frag;
+    static __device__ __forceinline__ float to_f32(float v) { return v; }
+    static __device__ __forceinline__ float from_f32(float v) { return v; }
+    static __device__ __forceinline__ floatx4 mma(frag a, frag b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    // load the KPL consecutive elements starting at p
+    static __device__ __forceinline__ frag load(const float *p) { return *p; }
+    static __device__ __forceinline__ frag zero() { return 0.f; }
+};
+
+template <> struct Elem<bf16_t> {
+    static constexpr int KPL = 8;
+    static constexpr int KSTEP = 32;
+    typedef bf16x8 frag;
+    static __device__ __forceinline__ float to_f32(bf16_t v) { return bf16_to_f32(v); }
+    static __device__ __forceinline__ bf16_t from_f32(float v) { return f32_to_bf16(v); }
+    static __device__ __forceinline__ floatx4 mma(frag a, frag b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ frag load(const bf16_t *p) { return *(const bf16x8 *)p; }
+    static __device__ __forceinline__ frag zero() {
+        frag z;
+        for (int i = 0; i < 8; ++i) z[i] = (__bf16)0.0f;
+        return z;
+    }
+};
+
+// Entries visible to a query at absolute position t: complete groups only.
+__device__ __forceinline__ int64_t n_visible(int64_t t, int m, int64_t N) {
+    if (t < 0) return 0;
+    int64_t n = (t + 1) / m;
+    return n < N ? n : N;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+}  // namespace csa

@@ -1,0 +1,131 @@
+// Lightning indexer (DeepSeek-V4 overview page, section 2.2 step 2):
+//     s[t, j] = sum_h w[t, h] * ReLU(qI[t, h, :] . kI[j, :])
+// for every entry j visible to query t; invisible entries get -inf.
+//
+// Mapping.  One wavefront owns one query and a contiguous chunk of entries.
+// The query's index heads sit in registers as the MFMA A operand (M = 16
+// heads per block, K = d_I); each 16-entry tile of index keys is streamed
+// from HBM straight into registers as the B operand (N = 16 entries), so
+// every key byte is read exactly once with 16-byte loads that cover whole
+// rows.  The 16x16 output tile holds four heads per lane for one entry: the
+// ReLU, the head weight and the head sum happen in registers, and two
+// cross-lane exchanges finish the sum over the four lane groups.  UNROLL
+// tiles of loads are issued before their MFMAs to keep HBM busy.
+#include "kernels.h"
+
+namespace csa {
+
+template <typename T, int DI, int MB>
+__global__ __launch_bounds__(256) void k_index_scores(int Tq, int N, int HI, int m, int64_t q_pos0, int64_t n_items,
+                                                       int chunks_per_row, int tiles_per_chunk,
+                                                       const T *__restrict__ qI, const float *__restrict__ w,
+                                                       const T *__restrict__ kI, int64_t k_bs,
+                                                       float *__restrict__ scores) {
+    using E = Elem<T>;
+    constexpr int KS = DI / E::KSTEP;
+    constexpr int UNROLL = 4;
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= n_items) return;
+    const int64_t row = item / chunks_per_row;
+    const int chunk = (int)(item % chunks_per_row);
+    const int64_t b = row / Tq, ti = row % Tq;
+    const int64_t nv = n_visible(q_pos0 + ti, m, N);
+    const int g = lane >> 4, c = lane & 15;
+
+    typename E::frag a[MB][KS];
+    float wv[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int head = mb * 16 + c;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            a[mb][ks] = head < HI ? E::load(qI + (row * HI + head) * DI + ks * E::KSTEP + g * E::KPL) : E::zero();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int hh = mb * 16 + 4 * g + e;
+            wv[mb][e] = hh < HI ? w[row * HI + hh] : 0.f;
+        }
+    }
+
+    const T *kb = kI + b * k_bs + g * E::KPL;
+    float *srow = scores + row * (int64_t)N;
+    const int64_t j_lo = (int64_t)chunk * tiles_per_chunk * 16;
+    const int64_t j_hi = min((int64_t)N, j_lo + (int64_t)tiles_per_chunk * 16);
+    for (int64_t j0 = j_lo; j0 < j_hi; j0 += 16 * UNROLL) {
+        typename E::frag bf[UNROLL][KS];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            int64_t jr = j0 + u * 16 + c;
+            jr = jr < nv ? jr : (nv > 0 ? nv - 1 : 0);  // clamp: masked lanes reread a valid row
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                bf[u][ks] = nv > 0 ? E::load(kb + jr * DI + ks * E::KSTEP) : E::zero();
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int64_t j = j0 + u * 16 + c;
+            floatx4 acc[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) acc[mb] = E::mma(a[mb][ks], bf[u][ks], acc[mb]);
+            float s = 0.f;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s += wv[mb][e] * fmaxf(acc[mb][e], 0.f);
+            s += __shfl_xor(s, 16);
+            s += __shfl_xor(s, 32);
+            if (g == 0 && j < j_hi) srow[j] = j < nv ? s : -INFINITY;
+        }
+    }
+}
+
+template <typename T, int DI, int MB>
+static hipError_t launch_t(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const void *qI, const float *w,
+                           const void *kI, int64_t k_bs, float *scores, hipStream_t st) {
+    const int64_t rows = (int64_t)B * Tq;
+    const int64_t tiles = (N + 15) / 16;
+    // aim for ~2048 wavefronts in flight (8 per CU) when there are few queries
+    int64_t chunks = (2048 + rows - 1) / rows;
+    if (chunks > tiles) chunks = tiles;
+    if (chunks < 1) chunks = 1;
+    int64_t tpc = (tiles + chunks - 1) / chunks;
+    tpc = (tpc + 3) / 4 * 4;
+    chunks = (tiles + tpc - 1) / tpc;
+    if (chunks < 1) chunks = 1;
+    const int64_t items = rows * chunks;
+    const int64_t blocks = (items + 3) / 4;
+    hipLaunchKernelGGL((k_index_scores<T, DI, MB>), dim3((unsigned)blocks), dim3(256), 0, st, Tq, N, HI, m, q_pos0,
+                       items, (int)chunks, (int)tpc, (const T *)qI, w, (const T *)kI, k_bs, scores);
+    return hipGetLastError();
+}
+
+template <typename T, int DI>
+static hipError_t launch_di(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const void *qI, const float *w,
+                            const void *kI, int64_t k_bs, float *scores, hipStream_t st) {
+    if (HI <= 16) return launch_t<T, DI, 1>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, st);
+    if (HI <= 32) return launch_t<T, DI, 2>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, st);
+    return launch_t<T, DI, 4>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, st);
+}
+
+template <typename T>
+static hipError_t launch_dt(int B, int Tq, int N, int HI, int dI, int m, int64_t q_pos0, const void *qI,
+                            const float *w, const void *kI, int64_t k_bs, float *scores, hipStream_t st) {
+    switch (dI) {
+        case 32: return launch_di<T, 32>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, st);
+        case 64: return launch_di<T, 64>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, st);
+        default: return launch_di<T, 128>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, st);
+    }
+}
+
+hipError_t launch_index_scores(int dt, int B, int Tq, int N, int HI, int dI, int m, int64_t q_pos0, const void *qI,
+                               const float *w, const void *kI, int64_t k_bs, float *scores, hipStream_t st) {
+    if (dt == 0) return launch_dt<float>(B, Tq, N, HI, dI, m, q_pos0, qI, w, kI, k_bs, scores, st);
+    return launch_dt<bf16_t>(B, Tq, N, HI, dI, m, q_pos0, qI, w, kI, k_bs, scores, st);
+}
+
+}  // namespace csa

@@ -1,0 +1,63 @@
+"""The oracle's view of one attention step (test infrastructure).
+
+Runs the CPU oracle on host copies of a workload's generated inputs, taken
+before any GPU work, so no oracle input comes from the HIP path.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle as orc
+
+
+def host_inputs(x: dict) -> dict:
+    """Exact float32 host copies of every tensor input (bf16 widens exactly)."""
+    out = {}
+    for k, v in x.items():
+        if hasattr(v, "detach"):
+            v = v.detach().cpu()
+            out[k] = v.numpy() if v.dtype.is_floating_point is False else v.float().numpy()
+        else:
+            out[k] = v
+    return out
+
+
+def oracle_step(wl, xh: dict, rows=None) -> dict:
+    """Oracle results for workload ``wl`` on host inputs ``xh``.
+
+    rows: query rows (0..Tq-1) to evaluate for the indexer / top-k /
+    attention; None evaluates every row.  Compression is always complete.
+    """
+    N, m, g0 = wl.N, wl.m, wl.g0
+    r0 = g0 * m - wl.raw_pos0
+    e = orc.compress(xh["raw"][:, r0:r0 + wl.G_new * m], xh["logits"], m) if wl.G_new > 0 else None
+    ent = np.array(xh["entries"][:, :N], dtype=np.float32, copy=True)
+    if e is not None:
+        ent[:, g0:N] = orc.round_bf16(e) if wl.dtype == "bf16" else e.astype(np.float32)
+    res = {"e": e, "entries": ent}
+    sel = list(range(wl.Tq)) if rows is None else list(rows)
+    if rows is None:
+        groups = [(0, wl.Tq)]
+    else:
+        groups = [(ti, ti + 1) for ti in sel]
+    outs, lses, idxs, scs = [], [], [], []
+    for a, b in groups:
+        qp = wl.q_pos0 + a
+        q = xh["q"][:, a:b]
+        if wl.mode == "csa":
+            s = orc.index_scores(xh["q_idx"][:, a:b], xh["w_idx"][:, a:b], xh["k_idx"][:, :N], m, qp)
+            idx = orc.topk(s, wl.k, m, qp)
+            o, l = orc.sparse_mqa(q, ent, idx, xh["raw"], wl.raw_pos0, wl.W, qp, wl.scale)
+            scs.append(s)
+            idxs.append(idx)
+        else:
+            o, l = orc.dense_mqa(q, ent, xh["raw"], wl.raw_pos0, m, wl.W, qp, wl.scale)
+        outs.append(o)
+        lses.append(l)
+    res["rows"] = sel
+    res["out"] = np.concatenate(outs, axis=1)
+    res["lse"] = np.concatenate(lses, axis=1)
+    if wl.mode == "csa":
+        res["scores"] = np.concatenate(scs, axis=1)
+        res["idx"] = np.concatenate(idxs, axis=1)
+    return res

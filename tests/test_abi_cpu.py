@@ -1,0 +1,124 @@
+"""Host-side checks of the C ABI: the library loads, exports what include/csa.h
+declares, and rejects bad arguments before launching anything.  No GPU is
+needed: every call here fails validation, so no device pointer is touched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import long_context_compressed_06_amd as csa
+
+    return csa.lib()
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "csa.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:csa|hca)_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    import long_context_compressed_06_amd as csa
+
+    names = header_functions()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(csa.EXPORTS) == names
+
+
+def test_version_and_status_strings(L):
+    assert L.csa_abi_version() == 1
+    for s in range(-6, 1):
+        assert L.csa_status_string(s)
+    assert L.csa_status_string(-99) == b"unknown status"
+
+
+P = 0x100000  # a 16-byte aligned fake device address, never dereferenced
+
+
+def compress(L, dt=1, B=2, G=3, m=4, d=128, raw=P, rbs=None, logits=P + 0x100000, lbs=None, out=P + 0x200000,
+             obs=None):
+    rbs = G * m * d if rbs is None else rbs
+    lbs = G * m if lbs is None else lbs
+    obs = G * d if obs is None else obs
+    return L.csa_compress(dt, B, G, m, d, raw, rbs, logits, lbs, out, obs, None)
+
+
+def test_compress_validation(L):
+    assert compress(L, dt=7) == -2
+    assert compress(L, d=100) == -6
+    assert compress(L, m=0) == -6 and compress(L, m=129) == -6
+    assert compress(L, B=-1) == -1
+    assert compress(L, B=0) == 0 and compress(L, G=0) == 0  # empty: nothing enqueued
+    assert compress(L, raw=0) == -1
+    assert compress(L, raw=P + 8) == -3
+    assert compress(L, rbs=3 * 4 * 128 + 4) == -3
+    assert compress(L, rbs=100) == -1
+    assert compress(L, out=P + 64) == -1  # overlaps raw
+    assert b"overlap" in L.csa_last_error_detail()
+
+
+def index(L, dt=1, B=1, Tq=1, N=1000, HI=64, dI=128, m=4, k=64, q_pos0=3999, ws=P + 0x4000000, wsb=1 << 30,
+          scores=None, kbs=None, q=P, w=P + 0x100000, kk=P + 0x200000, out=P + 0x3000000):
+    kbs = N * dI if kbs is None else kbs
+    return L.csa_index_topk(dt, B, Tq, N, HI, dI, m, k, q_pos0, q, w, kk, kbs, out, scores, ws, wsb, None)
+
+
+def test_index_topk_validation(L):
+    assert index(L, dt=2) == -2
+    assert index(L, HI=65) == -6 and index(L, dI=48) == -6
+    assert index(L, k=0) == -6 and index(L, k=4096) == -6
+    assert index(L, m=0) == -1 and index(L, q_pos0=-1) == -1
+    assert index(L, B=0) == 0 and index(L, Tq=0) == 0
+    assert index(L, ws=0, wsb=0) == -4
+    assert index(L, wsb=1000 * 4 - 1) == -4
+    assert index(L, kk=P + 4) == -3
+    assert index(L, kbs=10) == -1
+    assert index(L, out=P + 16) == -1  # topk_idx overlaps q_idx
+    need = L.csa_index_topk_workspace_bytes(2, 3, 1000, 64, 64)
+    assert need >= 2 * 3 * 1000 * 4 and need % 256 == 0
+
+
+def mqa(L, fn="sparse", dt=1, B=1, Tq=1, H=64, d=512, N=1000, m=4, k=64, W=128, q_pos0=4095, scale=0.04,
+        q=P, e=P + 0x100000, idx=P + 0x2000000, raw=P + 0x3000000, raw_pos0=3968, raw_len=128, out=P + 0x4000000,
+        lse=None, ws=P + 0x5000000, wsb=1 << 30, ebs=None, rbs=None):
+    ebs = N * d if ebs is None else ebs
+    rbs = raw_len * d if rbs is None else rbs
+    sc = ctypes.c_float(scale)
+    if fn == "sparse":
+        return L.csa_sparse_mqa(dt, B, Tq, H, d, N, m, k, W, q_pos0, sc, q, e, ebs, idx, raw, rbs, raw_pos0,
+                                raw_len, out, lse, ws, wsb, None)
+    return L.hca_dense_mqa(dt, B, Tq, H, d, N, m, W, q_pos0, sc, q, e, ebs, raw, rbs, raw_pos0, raw_len, out, lse,
+                           ws, wsb, None)
+
+
+@pytest.mark.parametrize("fn", ["sparse", "dense"])
+def test_mqa_validation(L, fn):
+    assert mqa(L, fn, dt=5) == -2
+    assert mqa(L, fn, H=0) == -6 and mqa(L, fn, H=65) == -6 and mqa(L, fn, d=96) == -6
+    assert mqa(L, fn, scale=0.0) == -1 and mqa(L, fn, scale=float("inf")) == -1
+    assert mqa(L, fn, raw_pos0=3969) == -1  # window start 3968 not covered
+    assert mqa(L, fn, raw_len=127) == -1    # last position not covered
+    assert mqa(L, fn, B=0) == 0
+    assert mqa(L, fn, q=P + 2) == -3
+    assert mqa(L, fn, out=P + 0x100000 + 512) == -1  # overlaps entries
+    assert mqa(L, fn, ebs=1000 * 512 - 8) == -1
+    assert mqa(L, fn, B=8, ws=0, wsb=0) == -4  # 8 queries use split-K partials
+    if fn == "sparse":
+        assert mqa(L, fn, k=0) == -6 and mqa(L, fn, k=5000) == -6
+
+
+def test_mqa_workspace_sizes(L):
+    # many queries: one split per query, no partials
+    assert L.csa_mqa_workspace_bytes(1, 4096, 64, 512, 1152) == 0
+    # decode at batch 32 over 1152 rows: split-K partials of (d + 2) floats per head
+    n = L.csa_mqa_workspace_bytes(32, 1, 64, 512, 1152)
+    assert n > 0 and n % 256 == 0 and n % (32 * 64 * 514 * 4) < 256

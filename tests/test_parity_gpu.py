@@ -1,0 +1,241 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every case prints its name, shape and seed before touching the GPU.  Inputs
+are seeded synthetic tensors drawn on the GPU; the oracle receives host copies
+taken before the step runs.  Rules (tests/helpers.py): bf16 max 2e-2 / mean
+2e-3 absolute, fp32 1e-5 normwise per row, top-k rule T, bookkeeping exact.
+Attention is compared twice: the GPU attention fed the oracle's own selection
+(so a legal near-tie swap cannot hide an attention error), and the full GPU
+chain on the rows whose selection matches the oracle's.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from chain import host_inputs, oracle_step
+from helpers import assert_close, check_topk, nvis_rows, to_np
+from workloads import CONFIGS, Workload, make_inputs, scaled
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def csa():
+    import long_context_compressed_06_amd as m
+
+    m.lib()
+    assert torch.cuda.is_available(), "no GPU visible"
+    return m
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def run_and_check(csa, wl: Workload, rows=None, entries_capacity=None):
+    say(wl)
+    x = make_inputs(wl, "cuda", entries_capacity=entries_capacity)
+    xh = host_inputs(x)
+    step = csa.AttentionStep.for_workload(wl)
+    out = step(x)
+    torch.cuda.synchronize()
+    ref = oracle_step(wl, xh, rows)
+    sel = ref["rows"]
+    # a1: compressed entries against the unrounded oracle value
+    if ref["e"] is not None:
+        assert_close(x["entries"][:, wl.g0:wl.N], ref["e"], wl.dtype, "entries")
+    if wl.mode == "csa":
+        gidx = to_np(step.topk_idx)[:, sel]
+        nv = nvis_rows(wl)[:, sel]
+        swapped = check_topk(gidx, ref["idx"], ref["scores"], nv, wl.k, "topk")
+        # attention on the oracle's selection
+        ridx = torch.from_numpy(np.ascontiguousarray(ref["idx"])).cuda()
+        qs = x["q"][:, sel].contiguous()
+        if rows is None:
+            o2 = csa.csa_sparse_mqa(qs, x["entries"], ridx, x["raw"], wl.N, wl.m, wl.W, wl.q_pos0, wl.raw_pos0,
+                                    scale=wl.scale, lse=torch.empty(qs.shape[:3], device="cuda"))
+            lse2 = None
+        else:
+            o2 = torch.empty_like(out[:, sel])
+            for i, ti in enumerate(sel):
+                csa.csa_sparse_mqa(qs[:, i:i + 1].contiguous(), x["entries"], ridx[:, i:i + 1].contiguous(), x["raw"],
+                                   wl.N, wl.m, wl.W, wl.q_pos0 + ti, wl.raw_pos0, scale=wl.scale,
+                                   out=o2[:, i:i + 1])
+            lse2 = None
+        torch.cuda.synchronize()
+        assert_close(o2, ref["out"], wl.dtype, "attention(oracle idx)", row_dims=1)
+        # full chain on rows with identical selection
+        same = np.all(gidx == ref["idx"], axis=2)
+        assert same.mean() >= 0.75, f"only {same.mean():.2%} of rows select the oracle's exact set"
+        o_g = to_np(out[:, sel])
+        assert_close(o_g[same], ref["out"][same], wl.dtype, "chain out")
+        assert_close(to_np(step.lse[:, sel])[same], ref["lse"][same], wl.dtype, "chain lse", row_dims=1)
+        say(f"top-k rows with a legal near-tie swap: {swapped} of {gidx.shape[0] * gidx.shape[1]}")
+        del lse2
+    else:
+        assert_close(out[:, sel], ref["out"], wl.dtype, "out")
+        assert_close(step.lse[:, sel], ref["lse"], wl.dtype, "lse", row_dims=1)
+    return x, step, ref
+
+
+# ---------------------------------------------------------------- full configs
+def test_c1_tiny_prefill_fp32(csa):
+    run_and_check(csa, CONFIGS["c1"])
+
+
+def test_c2_csa_decode_128k(csa):
+    run_and_check(csa, CONFIGS["c2"])
+
+
+def test_c3_hca_decode_1m(csa):
+    run_and_check(csa, CONFIGS["c3"])
+
+
+def test_c4_csa_prefill_chunk_sampled(csa):
+    wl = CONFIGS["c4"]
+    rows = [0, 1, 2, 3, 127, 128, 1000, 2047, 2048, 3071, 4093, 4094, 4095]
+    run_and_check(csa, wl, rows=rows)
+
+
+def test_c5_csa_decode_1m_stress(csa):
+    run_and_check(csa, CONFIGS["c5"])
+
+
+# ------------------------------------------------------- small and ragged shapes
+SMALL = [
+    # name, dtype, B, T, Tq, m, d, H, W, k, HI, dI
+    ("csa_bf16_ragged", "bf16", 2, 1003, 37, 4, 128, 64, 16, 50, 64, 128),
+    ("csa_bf16_k_ge_n", "bf16", 1, 300, 9, 4, 64, 16, 8, 2048, 16, 64),
+    ("csa_f32_m1", "f32", 2, 200, 11, 1, 32, 8, 5, 17, 4, 32),
+    ("csa_f32_d512", "f32", 1, 700, 3, 4, 512, 20, 33, 100, 17, 128),
+    ("csa_bf16_no_window", "bf16", 3, 500, 4, 4, 256, 64, 0, 64, 64, 128),
+    ("csa_bf16_w1_h1", "bf16", 2, 4097, 2, 4, 512, 1, 1, 1000, 1, 32),
+    ("csa_bf16_early_queries", "bf16", 1, 40, 40, 4, 128, 8, 3, 5, 4, 32),
+    ("csa_bf16_big_row", "bf16", 1, 4 * 40000, 1, 4, 128, 16, 128, 1024, 64, 128),
+    ("hca_bf16_ragged", "bf16", 2, 128 * 77 + 5, 3, 128, 512, 64, 128, 0, 0, 0),
+    ("hca_f32_m1_w0", "f32", 1, 150, 150, 1, 64, 4, 0, 0, 0, 0),
+    ("hca_bf16_window_only", "bf16", 1, 100, 100, 128, 128, 64, 16, 0, 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_shapes(csa, case):
+    name, dt, B, T, Tq, m, d, H, W, k, HI, dI = case
+    wl = Workload(name, dt, B=B, T=T, Tq=Tq, m=m, d=d, H=H, W=W, k=k, HI=HI, dI=dI,
+                  seed_base=90000 + 1000 * SMALL.index(case))
+    run_and_check(csa, wl, entries_capacity=wl.N + 40)
+
+
+# ----------------------------------------------------------------- exact ties
+def test_topk_exact_integer_scores(csa):
+    """Small-integer index keys and dyadic head weights make every score exact in
+    float32, with many ties: the selection must equal the oracle's bit for bit."""
+    wl = Workload("ties", "bf16", B=2, T=4 * 3000, Tq=3, m=4, d=128, H=16, W=4, k=700, HI=16, dI=32, seed_base=77000)
+    say(wl)
+    g = torch.Generator(device="cuda").manual_seed(77001)
+    x = make_inputs(wl, "cuda")
+    x["k_idx"] = torch.randint(-2, 3, x["k_idx"].shape, generator=g, device="cuda").to(torch.bfloat16)
+    x["q_idx"] = torch.randint(-2, 3, x["q_idx"].shape, generator=g, device="cuda").to(torch.bfloat16)
+    x["w_idx"] = torch.randint(0, 5, x["w_idx"].shape, generator=g, device="cuda").float() * 0.25
+    xh = host_inputs(x)
+    step = csa.AttentionStep.for_workload(wl)
+    step(x)
+    torch.cuda.synchronize()
+    ref = oracle_step(wl, xh)
+    assert np.array_equal(to_np(step.topk_idx), ref["idx"])
+
+
+def test_scores_out_and_masking(csa):
+    wl = Workload("scores", "bf16", B=2, T=4 * 700 + 3, Tq=5, m=4, d=128, H=16, W=4, k=64, HI=64, dI=128,
+                  seed_base=78000)
+    say(wl)
+    x = make_inputs(wl, "cuda")
+    xh = host_inputs(x)
+    sc = torch.empty((wl.B, wl.Tq, wl.N), device="cuda")
+    csa.csa_index_topk(x["q_idx"], x["w_idx"], x["k_idx"], wl.N, wl.m, wl.k, wl.q_pos0, scores_out=sc)
+    torch.cuda.synchronize()
+    ref = oracle_step(wl, xh)["scores"]
+    got = to_np(sc)
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+    fin = np.isfinite(ref)
+    rel = np.abs(got[fin] - ref[fin]).max() / np.abs(ref[fin]).max()
+    assert rel <= 1e-5, rel
+
+
+# ------------------------------------------------------ poison, empty, determinism
+def test_poisoned_memory_is_never_read(csa):
+    """Entries and index keys beyond N, and raw rows outside every window, are
+    filled with large finite values: outputs must not change by a single bit."""
+    wl = Workload("poison", "bf16", B=2, T=4 * 2000 + 2, Tq=4, m=4, d=256, H=64, W=32, k=300, HI=64, dI=128,
+                  seed_base=79000)
+    say(wl)
+    outs = []
+    for poison in (False, True):
+        x = make_inputs(wl, "cuda", entries_capacity=wl.N + 64)
+        if poison:
+            x["entries"][:, wl.N:] = 3e4
+            x["k_idx"][:, wl.N:] = 3e4
+        step = csa.AttentionStep.for_workload(wl)
+        step(x)
+        torch.cuda.synchronize()
+        outs.append((step.out.clone(), step.topk_idx.clone(), step.lse.clone()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_empty_and_invisible(csa):
+    say("empty batch / no visible rows")
+    q = torch.randn((1, 1, 16, 64), device="cuda").to(torch.bfloat16)
+    e = torch.randn((1, 8, 64), device="cuda").to(torch.bfloat16)
+    raw = torch.randn((1, 4, 64), device="cuda").to(torch.bfloat16)
+    # query at position 2 with m=4: no complete group, W=0: empty row set
+    lse = torch.empty((1, 1, 16), device="cuda")
+    out = csa.hca_dense_mqa(q, e, raw, 8, 4, 0, 2, 0, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+    # zero-sized batch enqueues nothing
+    q0 = torch.empty((0, 1, 16, 64), device="cuda", dtype=torch.bfloat16)
+    csa.hca_dense_mqa(q0, e[:0], raw[:0], 8, 4, 2, 2, 0)
+
+
+def test_determinism(csa):
+    wl = CONFIGS["c5"]
+    say(wl, "twice")
+    res = []
+    for _ in range(2):
+        x = make_inputs(wl, "cuda")
+        step = csa.AttentionStep.for_workload(wl)
+        step(x)
+        torch.cuda.synchronize()
+        res.append((step.out.clone(), step.topk_idx.clone()))
+        del x, step
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
+def test_graph_replay_matches_eager(csa):
+    wl = CONFIGS["c2"]
+    say(wl, "graph replay")
+    x = make_inputs(wl, "cuda")
+    step = csa.AttentionStep.for_workload(wl)
+    step(x)
+    torch.cuda.synchronize()
+    eager = (step.out.clone(), step.topk_idx.clone(), step.lse.clone())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(x)
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(x)
+    for i in range(4):
+        step.out.fill_(float("nan"))
+        step.topk_idx.fill_(-7)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(step.out, eager[0]) and torch.equal(step.topk_idx, eager[1]), i
+        assert torch.equal(step.lse, eager[2]), i
+        _ = (x["q"].float() * 2).sum().item()  # unrelated eager work between replays
