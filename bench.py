@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark of one compressed-attention layer step on one MI355X.
+
+Default workload: CSA decode, bf16, batch 32 at a 131072-token context
+(32768 compressed entries, m=4; 64 index heads x 128; top-1024; 64 query heads
+x 512 sharing the KV; window of 128 raw tokens; the new token's group is
+compressed in the step).  A step = csa_compress + csa_index_topk +
+csa_sparse_mqa through the C ABI, replayed from captured HIP graphs over R
+input replicas (>= 1 GiB touched in rotation, so the 256 MB Infinity Cache
+cannot serve repeats).  Inputs are resident in HBM before timing starts.
+
+Printed: ONE JSON line with tokens/s (= B*Tq / step time), the dominant
+kernel's roofline (the lightning indexer, HBM-bound: algorithmic bytes per
+launch over its HIP-event-timed average duration), the oracle timed on the
+host's cores, and the HCA 1M and CSA 1M decode workloads as secondary lines.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(wl) -> dict:
+    """Bytes the method must move once per step (overheads like scores and
+    split-K partials excluded), and the indexer kernel's share."""
+    es = 2 if wl.dtype == "bf16" else 4
+    step = idx_kernel = 0
+    for ti in range(wl.Tq):
+        t = wl.q_pos0 + ti
+        nv = min(wl.N, (t + 1) // wl.m)
+        n_win = min(wl.W, t + 1)
+        q = wl.H * wl.d * es
+        out = wl.H * wl.d * 4
+        if wl.mode == "csa":
+            ki = nv * wl.dI * es + wl.HI * wl.dI * es + wl.HI * 4
+            idx_kernel += ki
+            rows = (min(wl.k, nv) + n_win) * wl.d * es
+            step += ki + rows + q + out + 2 * wl.k * 4
+        else:
+            step += (nv + n_win) * wl.d * es + q + out
+    step *= wl.B
+    idx_kernel *= wl.B
+    # compression of the new groups: logits, raw rows outside the window, the entry write
+    step += wl.B * (wl.G_new * wl.m * 4 + wl.G_new * wl.d * es)
+    return {"step": step, "indexer": idx_kernel}
+
+
+def replicas_for(x: dict) -> int:
+    foot = sum(v.numel() * v.element_size() for v in x.values() if hasattr(v, "numel"))
+    return max(2, min(8, math.ceil((1 << 30) / max(foot, 1)) + 1))
+
+
+def clone_inputs(x):
+    return {k: (v.clone() if hasattr(v, "clone") else v) for k, v in x.items()}
+
+
+def capture(fn):
+    import torch
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def time_graphs(graphs, steps, warmup):
+    import torch
+
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    end.record()
+    end.synchronize()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms
+
+
+def bench_workload(wl, steps, warmup, with_kernel=True):
+    import torch
+
+    import long_context_compressed_06_amd as csa
+    from workloads import make_inputs
+
+    x0 = make_inputs(wl, "cuda")
+    R = replicas_for(x0)
+    xs = [x0] + [clone_inputs(x0) for _ in range(R - 1)]
+    steps_ = [csa.AttentionStep.for_workload(wl) for _ in xs]
+    for s, x in zip(steps_, xs):
+        s(x)
+    torch.cuda.synchronize()
+    graphs = [capture(lambda s=s, x=x: s(x)) for s, x in zip(steps_, xs)]
+    ms = time_graphs(graphs, steps, warmup)
+    res = {"ms_per_step": ms, "replicas": R}
+    if with_kernel and wl.mode == "csa":
+        # the lightning indexer alone, same launch configuration, timed with HIP
+        # events on the stream it runs on
+        sc = [torch.empty((wl.B, wl.Tq, wl.N), dtype=torch.float32, device="cuda") for _ in xs]
+        kg = [capture(lambda x=x, o=o: csa.csa_index_scores(x["q_idx"], x["w_idx"], x["k_idx"], wl.N, wl.m,
+                                                            wl.q_pos0, scores=o)) for x, o in zip(xs, sc)]
+        res["indexer_ms"] = time_graphs(kg, steps, warmup)
+        del sc, kg
+    del graphs, steps_, xs, x0
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(wl, min_seconds=10.0, max_reps=5):
+    """The oracle, as it stands, on the same workload's inputs (host copies)."""
+    import torch
+
+    import oracle
+    from workloads import make_inputs
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from chain import host_inputs, oracle_step
+
+    x = make_inputs(wl, "cuda")
+    xh = host_inputs(x)
+    del x
+    torch.cuda.empty_cache()
+    reps, t0 = 0, time.perf_counter()
+    while reps < max_reps:
+        oracle_step(wl, xh)
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": wl.B * wl.Tq * reps / el, "unit": "tokens/s", "cores": oracle.default_threads(),
+            "kind": "oracle",
+            "sample": f"whole step of the {wl.name} workload (all {wl.B} sequences: compression, indexer over "
+                      f"{wl.N} entries, top-{wl.k}, attention) repeated {reps}x in {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2", help="c2 (default), c3 or c5")
+    ap.add_argument("--also", default="c3,c5", help="secondary decode workloads ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        log("bench.py measures one GPU: this build has no multi-GPU path (one process, one MI355X). Use --gpus 1.")
+        sys.exit(2)
+
+    import torch
+
+    from workloads import CONFIGS
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = CONFIGS[args.workload]
+    log(f"[bench] {wl}")
+    r = bench_workload(wl, args.steps, args.warmup)
+    ab = algorithmic_bytes(wl)
+    toks = wl.B * wl.Tq / (r["ms_per_step"] * 1e-3)
+    line = {
+        "metric": "compressed-attn decode tokens/s + % HBM roofline at 128K and 1M ctx",
+        "value": toks,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.B, "context": wl.T, "m": wl.m, "entries": wl.N, "top_k": wl.k,
+                   "index_heads": wl.HI, "index_dim": wl.dI, "heads": wl.H, "head_dim": wl.d, "window": wl.W,
+                   "input_replicas": r["replicas"], "graph_replay": True},
+        "step_hbm": {"algorithmic_bytes": ab["step"],
+                     "achieved_GBs": ab["step"] / (r["ms_per_step"] * 1e-3) / 1e9,
+                     "frac": ab["step"] / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
+    }
+    if "indexer_ms" in r:
+        ach = ab["indexer"] / (r["indexer_ms"] * 1e-3) / 1e9
+        line["roofline"] = {"kernel": "k_index_scores (lightning indexer)", "bound": "hbm", "achieved": ach,
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                            "bytes_per_launch": ab["indexer"], "avg_launch_us": r["indexer_ms"] * 1e3}
+    also = {}
+    for name in [a for a in args.also.split(",") if a and a != args.workload]:
+        w2 = CONFIGS[name]
+        log(f"[bench] also {w2}")
+        r2 = bench_workload(w2, max(10, args.steps // 2), args.warmup, with_kernel=False)
+        b2 = algorithmic_bytes(w2)["step"]
+        also[w2.name] = {"tokens_per_s": w2.B * w2.Tq / (r2["ms_per_step"] * 1e-3), "ms_per_step": r2["ms_per_step"],
+                         "step_hbm_frac": b2 / (r2["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "algorithmic_bytes": b2}
+    if also:
+        line["also"] = also
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -123,6 +123,18 @@ int csa_index_topk(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k,
                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * csa_index_scores -- the lightning indexer alone (overview page, section 2.2
+ * step 2, scoring part): writes scores[b, i, j] = s[j] as defined for
+ * csa_index_topk for every visible entry and -inf for j >= n_visible(t).
+ * Same arguments and rules as csa_index_topk; no selection, no workspace.
+ *   scores    [B, Tq, N] f32 (output)
+ */
+int csa_index_scores(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int64_t q_pos0,
+                     const void *q_idx, const float *w_idx,
+                     const void *k_idx, int64_t k_bstride,
+                     float *scores, void *stream);
+
+/*
  * csa_sparse_mqa -- shared-KV multi-query attention over the selected
  * entries plus the raw window, one softmax (overview page, section 2.2
  * step 3: selected entries act as both key and value, all heads share them).

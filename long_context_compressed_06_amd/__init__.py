@@ -21,8 +21,8 @@ CSA_F32, CSA_BF16 = 0, 1
 _STATUS = {0: "CSA_OK", -1: "CSA_EINVAL", -2: "CSA_EDTYPE", -3: "CSA_EALIGN", -4: "CSA_EWORKSPACE",
            -5: "CSA_EHIP", -6: "CSA_EUNSUPPORTED"}
 EXPORTS = ("csa_abi_version", "csa_status_string", "csa_last_error_detail", "csa_compress",
-           "csa_index_topk_workspace_bytes", "csa_index_topk", "csa_mqa_workspace_bytes", "csa_sparse_mqa",
-           "hca_dense_mqa")
+           "csa_index_topk_workspace_bytes", "csa_index_topk", "csa_index_scores", "csa_mqa_workspace_bytes",
+           "csa_sparse_mqa", "hca_dense_mqa")
 
 
 class CsaError(RuntimeError):
@@ -54,6 +54,8 @@ def lib():
     L.csa_index_topk_workspace_bytes.restype = SZ
     L.csa_index_topk.argtypes = [I, I, I, I, I, I, I, I, I64, P, P, P, I64, P, P, P, SZ, P]
     L.csa_index_topk.restype = I
+    L.csa_index_scores.argtypes = [I, I, I, I, I, I, I, I64, P, P, P, I64, P, P]
+    L.csa_index_scores.restype = I
     L.csa_mqa_workspace_bytes.argtypes = [I, I, I, I, I]
     L.csa_mqa_workspace_bytes.restype = SZ
     L.csa_sparse_mqa.argtypes = [I, I, I, I, I, I, I, I, I, I64, F, P, P, I64, P, P, I64, I64, I, P, P, P, SZ, P]
@@ -147,6 +149,24 @@ def csa_index_topk(q_idx, w_idx, k_idx, N: int, m: int, k: int, q_pos0: int, top
                                 _bstride(k_idx), _p(topk_idx), _p(scores_out), _p(workspace), ws_bytes,
                                 _stream(q_idx)))
     return topk_idx
+
+
+def csa_index_scores(q_idx, w_idx, k_idx, N: int, m: int, q_pos0: int, scores=None) -> torch.Tensor:
+    """Lightning indexer only: scores [B,Tq,N] f32, -inf for entries not yet visible."""
+    _need(q_idx, "q_idx", dims=4)
+    _need(w_idx, "w_idx", torch.float32, 3)
+    _need(k_idx, "k_idx", q_idx.dtype, 3)
+    B, Tq, HI, dI = q_idx.shape
+    if not q_idx.is_contiguous() or not w_idx.is_contiguous() or k_idx.stride(1) != dI or k_idx.shape[1] < N:
+        raise ValueError("q_idx/w_idx must be contiguous and k_idx rows packed with >= N rows")
+    if scores is None:
+        scores = torch.empty((B, Tq, N), dtype=torch.float32, device=q_idx.device)
+    _need(scores, "scores", torch.float32, 3)
+    if scores.shape != (B, Tq, N) or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous [B, Tq, N] tensor")
+    _check(lib().csa_index_scores(_dt(q_idx), B, Tq, N, HI, dI, m, q_pos0, _p(q_idx), _p(w_idx), _p(k_idx),
+                                  _bstride(k_idx), _p(scores), _stream(q_idx)))
+    return scores
 
 
 def mqa_workspace_bytes(B, Tq, H, d, n_rows_max) -> int:

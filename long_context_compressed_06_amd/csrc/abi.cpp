@@ -151,6 +151,30 @@ int csa_index_topk(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k,
     return hip_status(csa::launch_topk(B, Tq, N, m, k, q_pos0, scores, topk_idx, st), "top-k launch");
 }
 
+int csa_index_scores(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int64_t q_pos0, const void *q_idx,
+                     const float *w_idx, const void *k_idx, int64_t k_bstride, float *scores, void *stream) {
+    if (int s = check_dt(dt)) return s;
+    if (B < 0 || Tq < 0 || N < 0) return fail(CSA_EINVAL, "B, Tq and N must be >= 0");
+    if (H_I < 1 || H_I > 64) return fail(CSA_EUNSUPPORTED, "H_I=%d outside 1..64", H_I);
+    if (!dI_supported(d_I)) return fail(CSA_EUNSUPPORTED, "d_I=%d not in {32,64,128}", d_I);
+    if (m < 1) return fail(CSA_EINVAL, "m=%d must be >= 1", m);
+    if (q_pos0 < 0) return fail(CSA_EINVAL, "q_pos0 must be >= 0");
+    if ((int64_t)B * Tq * N == 0) return ok();
+    if (!q_idx || !w_idx || !k_idx || !scores) return fail(CSA_EINVAL, "NULL tensor pointer");
+    if (k_bstride < (int64_t)N * d_I) return fail(CSA_EINVAL, "k_bstride smaller than N*d_I");
+    if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(w_idx, 4) || !aligned(scores, 4) || k_bstride % 8)
+        return fail(CSA_EALIGN, "q_idx/k_idx need 16-byte alignment, k_bstride a multiple of 8 elements");
+    const size_t es = esize(dt);
+    const Span ss = span(scores, B, (int64_t)Tq * N, (int64_t)Tq * N, 4);
+    if (overlap(ss, span(q_idx, B, (int64_t)Tq * H_I * d_I, (int64_t)Tq * H_I * d_I, es)) ||
+        overlap(ss, span(w_idx, B, (int64_t)Tq * H_I, (int64_t)Tq * H_I, 4)) ||
+        overlap(ss, span(k_idx, B, k_bstride, (int64_t)N * d_I, es)))
+        return fail(CSA_EINVAL, "scores overlaps an input");
+    return hip_status(csa::launch_index_scores(dt, B, Tq, N, H_I, d_I, m, q_pos0, q_idx, w_idx, k_idx, k_bstride,
+                                               scores, (hipStream_t)stream),
+                      "indexer launch");
+}
+
 size_t csa_mqa_workspace_bytes(int B, int Tq, int H, int d, int n_rows_max) {
     if (B <= 0 || Tq <= 0 || H <= 0 || d <= 0) return 0;
     int tps = 0;

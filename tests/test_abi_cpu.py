@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
     import long_context_compressed_06_amd as csa
 
     names = header_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(L, n), n
     assert sorted(csa.EXPORTS) == names
@@ -83,6 +83,9 @@ def test_index_topk_validation(L):
     assert index(L, kk=P + 4) == -3
     assert index(L, kbs=10) == -1
     assert index(L, out=P + 16) == -1  # topk_idx overlaps q_idx
+    sc = lambda **kw: L.csa_index_scores(kw.get("dt", 1), 1, 1, 1000, kw.get("HI", 64), 128, 4, 3999, P,
+                                         P + 0x100000, P + 0x200000, 1000 * 128, kw.get("out", P + 0x3000000), None)
+    assert sc(dt=3) == -2 and sc(HI=0) == -6 and sc(out=0) == -1 and sc(out=P + 0x200000) == -1
     need = L.csa_index_topk_workspace_bytes(2, 3, 1000, 64, 64)
     assert need >= 2 * 3 * 1000 * 4 and need % 256 == 0
 
