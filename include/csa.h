@@ -111,7 +111,9 @@ int csa_compress(int dt, int B, int G, int m, int d,
  *   scores_out optional [B, Tq, N] f32 (output): s[j] for visible j, -inf
  *             for j >= n_visible(t).  NULL: scores stay in the workspace.
  *   workspace device scratch of at least
- *             csa_index_topk_workspace_bytes(B, Tq, N, H_I, k) bytes.
+ *             csa_index_topk_workspace_bytes(B, Tq, N, H_I, k) bytes (always
+ *             required: it also holds the selection's histograms); it must
+ *             not overlap any argument.  N <= 4190208.
  * Scores must not be NaN (inputs must be finite).
  */
 size_t csa_index_topk_workspace_bytes(int B, int Tq, int N, int H_I, int k);

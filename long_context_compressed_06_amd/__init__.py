@@ -142,7 +142,7 @@ def csa_index_topk(q_idx, w_idx, k_idx, N: int, m: int, k: int, q_pos0: int, top
         if scores_out.shape != (B, Tq, N) or not scores_out.is_contiguous():
             raise ValueError("scores_out must be a contiguous [B, Tq, N] tensor")
     need = index_topk_workspace_bytes(B, Tq, N, HI, k)
-    if workspace is None and scores_out is None and need > 0:
+    if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q_idx.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().csa_index_topk(_dt(q_idx), B, Tq, N, HI, dI, m, k, q_pos0, _p(q_idx), _p(w_idx), _p(k_idx),

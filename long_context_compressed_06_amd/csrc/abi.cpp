@@ -100,12 +100,14 @@ int csa_compress(int dt, int B, int G, int m, int d, const void *raw, int64_t ra
                       "compress launch");
 }
 
+static size_t scores_bytes(int64_t rows, int64_t N) { return ((size_t)rows * N * sizeof(float) + 255) / 256 * 256; }
+
 size_t csa_index_topk_workspace_bytes(int B, int Tq, int N, int H_I, int k) {
     (void)H_I;
     (void)k;
-    if (B <= 0 || Tq <= 0 || N <= 0) return 0;
-    const size_t scores = (size_t)B * Tq * N * sizeof(float);
-    return (scores + 255) / 256 * 256;
+    if (B <= 0 || Tq <= 0 || N < 0) return 0;
+    const int64_t rows = (int64_t)B * Tq;
+    return scores_bytes(rows, N) + (csa::topk_scratch_bytes(rows, N) + 255) / 256 * 256;
 }
 
 int csa_index_topk(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k, int64_t q_pos0, const void *q_idx,
@@ -118,20 +120,20 @@ int csa_index_topk(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k,
     if (m < 1) return fail(CSA_EINVAL, "m=%d must be >= 1", m);
     if (k < 1 || k > 2048) return fail(CSA_EUNSUPPORTED, "k=%d outside 1..2048", k);
     if (q_pos0 < 0) return fail(CSA_EINVAL, "q_pos0 must be >= 0");
+    if (N > csa::kTopkMaxEntries) return fail(CSA_EUNSUPPORTED, "N=%d above %lld entries", N, (long long)csa::kTopkMaxEntries);
     if ((int64_t)B * Tq == 0) return ok();
     if (!q_idx || !w_idx || !topk_idx || (N > 0 && !k_idx)) return fail(CSA_EINVAL, "NULL tensor pointer");
     if (N > 0 && k_bstride < (int64_t)N * d_I) return fail(CSA_EINVAL, "k_bstride smaller than N*d_I");
     if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(w_idx, 4) || !aligned(topk_idx, 4) ||
         !aligned(scores_out, 4) || k_bstride % 8)
         return fail(CSA_EALIGN, "q_idx/k_idx need 16-byte alignment, k_bstride a multiple of 8 elements");
-    float *scores = scores_out;
-    if (!scores && N > 0) {
-        const size_t need = csa_index_topk_workspace_bytes(B, Tq, N, H_I, k);
-        if (!workspace || workspace_bytes < need)
-            return fail(CSA_EWORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
-        if (!aligned(workspace, 16)) return fail(CSA_EALIGN, "workspace needs 16-byte alignment");
-        scores = (float *)workspace;
-    }
+    const int64_t rows = (int64_t)B * Tq;
+    const size_t need = csa_index_topk_workspace_bytes(B, Tq, N, H_I, k);
+    if (!workspace || workspace_bytes < need)
+        return fail(CSA_EWORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    if (!aligned(workspace, 16)) return fail(CSA_EALIGN, "workspace needs 16-byte alignment");
+    float *scores = scores_out ? scores_out : (float *)workspace;
+    uint32_t *scratch = (uint32_t *)((char *)workspace + scores_bytes(rows, N));
     const size_t es = esize(dt);
     const Span si = span(topk_idx, B, (int64_t)Tq * k, (int64_t)Tq * k, 4);
     const Span ss = span(scores_out, B, (int64_t)Tq * N, (int64_t)Tq * N, 4);
@@ -141,14 +143,21 @@ int csa_index_topk(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k,
     for (const Span &in : inputs)
         if (overlap(si, in) || overlap(ss, in)) return fail(CSA_EINVAL, "an output overlaps an input");
     if (overlap(si, ss)) return fail(CSA_EINVAL, "topk_idx overlaps scores_out");
+    const Span sw = span(workspace, 1, 0, (int64_t)need, 1);
+    for (const Span &in : inputs)
+        if (overlap(sw, in)) return fail(CSA_EINVAL, "workspace overlaps an input");
+    if (overlap(sw, si) || overlap(sw, ss)) return fail(CSA_EINVAL, "workspace overlaps an output");
     hipStream_t st = (hipStream_t)stream;
     if (N > 0) {
+        // the first radix digit of the selection is counted by the indexer
+        if (int s = hip_status(csa::launch_fill_u32(scratch, rows * csa::kTopkBins, 0u, st), "histogram clear"))
+            return s;
         if (int s = hip_status(csa::launch_index_scores(dt, B, Tq, N, H_I, d_I, m, q_pos0, q_idx, w_idx, k_idx,
-                                                         k_bstride, scores, st),
+                                                         k_bstride, scores, scratch, st),
                                "indexer launch"))
             return s;
     }
-    return hip_status(csa::launch_topk(B, Tq, N, m, k, q_pos0, scores, topk_idx, st), "top-k launch");
+    return hip_status(csa::launch_topk(B, Tq, N, m, k, q_pos0, scores, scratch, topk_idx, st), "top-k launch");
 }
 
 int csa_index_scores(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int64_t q_pos0, const void *q_idx,
@@ -171,7 +180,7 @@ int csa_index_scores(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int6
         overlap(ss, span(k_idx, B, k_bstride, (int64_t)N * d_I, es)))
         return fail(CSA_EINVAL, "scores overlaps an input");
     return hip_status(csa::launch_index_scores(dt, B, Tq, N, H_I, d_I, m, q_pos0, q_idx, w_idx, k_idx, k_bstride,
-                                               scores, (hipStream_t)stream),
+                                               scores, nullptr, (hipStream_t)stream),
                       "indexer launch");
 }
 

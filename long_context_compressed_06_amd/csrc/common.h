@@ -18,6 +18,7 @@ namespace csa {
 typedef uint16_t bf16_t;
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
@@ -69,6 +70,14 @@ __device__ __forceinline__ int64_t n_visible(int64_t t, int m, int64_t N) {
     if (t < 0) return 0;
     int64_t n = (t + 1) / m;
     return n < N ? n : N;
+}
+
+// order-preserving map of a float score to uint32 (larger score, larger key;
+// -0 ranks with +0)
+__device__ __forceinline__ uint32_t order_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 __device__ __forceinline__ float wave_max(float v) {

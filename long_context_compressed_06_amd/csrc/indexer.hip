@@ -11,6 +11,11 @@
 // ReLU, the head weight and the head sum happen in registers, and two
 // cross-lane exchanges finish the sum over the four lane groups.  UNROLL
 // tiles of loads are issued before their MFMAs to keep HBM busy.
+//
+// Optionally (hist != nullptr) the epilogue also counts every visible score
+// by the top 11 bits of its order-preserving key (the first radix digit of
+// the top-k selection): per-wave LDS histograms, flushed to the query's
+// global histogram with one atomic per non-empty bin.
 #include "kernels.h"
 
 namespace csa {
@@ -20,12 +25,16 @@ __global__ __launch_bounds__(256) void k_index_scores(int Tq, int N, int HI, int
                                                        int chunks_per_row, int tiles_per_chunk,
                                                        const T *__restrict__ qI, const float *__restrict__ w,
                                                        const T *__restrict__ kI, int64_t k_bs,
-                                                       float *__restrict__ scores) {
+                                                       float *__restrict__ scores, uint32_t *__restrict__ hist) {
     using E = Elem<T>;
     constexpr int KS = DI / E::KSTEP;
     constexpr int UNROLL = 4;
-    const int lane = threadIdx.x & 63;
-    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    __shared__ uint32_t whist[4][kTopkBins];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t item = (int64_t)blockIdx.x * 4 + wv;
+    if (hist) {
+        for (int i = lane; i < kTopkBins; i += 64) whist[wv][i] = 0;
+    }
     if (item >= n_items) return;
     const int64_t row = item / chunks_per_row;
     const int chunk = (int)(item % chunks_per_row);
@@ -34,7 +43,7 @@ __global__ __launch_bounds__(256) void k_index_scores(int Tq, int N, int HI, int
     const int g = lane >> 4, c = lane & 15;
 
     typename E::frag a[MB][KS];
-    float wv[MB][4];
+    float wgt[MB][4];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
         const int head = mb * 16 + c;
@@ -44,7 +53,7 @@ __global__ __launch_bounds__(256) void k_index_scores(int Tq, int N, int HI, int
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int hh = mb * 16 + 4 * g + e;
-            wv[mb][e] = hh < HI ? w[row * HI + hh] : 0.f;
+            wgt[mb][e] = hh < HI ? w[row * HI + hh] : 0.f;
         }
     }
 
@@ -76,17 +85,26 @@ __global__ __launch_bounds__(256) void k_index_scores(int Tq, int N, int HI, int
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) s += wv[mb][e] * fmaxf(acc[mb][e], 0.f);
+                for (int e = 0; e < 4; ++e) s += wgt[mb][e] * fmaxf(acc[mb][e], 0.f);
             s += __shfl_xor(s, 16);
             s += __shfl_xor(s, 32);
             if (g == 0 && j < j_hi) srow[j] = j < nv ? s : -INFINITY;
+            if (hist && g == 0 && j < nv) atomicAdd(&whist[wv][order_key(s) >> (32 - kTopkBinBits)], 1u);
+        }
+    }
+    if (hist) {
+        // LDS operations of one wave complete in order: the counts are final here
+        uint32_t *grow = hist + row * kTopkBins;
+        for (int i = lane; i < kTopkBins; i += 64) {
+            const uint32_t v = whist[wv][i];
+            if (v) atomicAdd(&grow[i], v);
         }
     }
 }
 
 template <typename T, int DI, int MB>
 static hipError_t launch_t(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const void *qI, const float *w,
-                           const void *kI, int64_t k_bs, float *scores, hipStream_t st) {
+                           const void *kI, int64_t k_bs, float *scores, uint32_t *hist, hipStream_t st) {
     const int64_t rows = (int64_t)B * Tq;
     const int64_t tiles = (N + 15) / 16;
     // aim for ~2048 wavefronts in flight (8 per CU) when there are few queries
@@ -100,32 +118,34 @@ static hipError_t launch_t(int B, int Tq, int N, int HI, int m, int64_t q_pos0, 
     const int64_t items = rows * chunks;
     const int64_t blocks = (items + 3) / 4;
     hipLaunchKernelGGL((k_index_scores<T, DI, MB>), dim3((unsigned)blocks), dim3(256), 0, st, Tq, N, HI, m, q_pos0,
-                       items, (int)chunks, (int)tpc, (const T *)qI, w, (const T *)kI, k_bs, scores);
+                       items, (int)chunks, (int)tpc, (const T *)qI, w, (const T *)kI, k_bs, scores, hist);
     return hipGetLastError();
 }
 
 template <typename T, int DI>
 static hipError_t launch_di(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const void *qI, const float *w,
-                            const void *kI, int64_t k_bs, float *scores, hipStream_t st) {
-    if (HI <= 16) return launch_t<T, DI, 1>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, st);
-    if (HI <= 32) return launch_t<T, DI, 2>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, st);
-    return launch_t<T, DI, 4>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, st);
+                            const void *kI, int64_t k_bs, float *scores, uint32_t *hist, hipStream_t st) {
+    if (HI <= 16) return launch_t<T, DI, 1>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, hist, st);
+    if (HI <= 32) return launch_t<T, DI, 2>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, hist, st);
+    return launch_t<T, DI, 4>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, hist, st);
 }
 
 template <typename T>
 static hipError_t launch_dt(int B, int Tq, int N, int HI, int dI, int m, int64_t q_pos0, const void *qI,
-                            const float *w, const void *kI, int64_t k_bs, float *scores, hipStream_t st) {
+                            const float *w, const void *kI, int64_t k_bs, float *scores, uint32_t *hist,
+                            hipStream_t st) {
     switch (dI) {
-        case 32: return launch_di<T, 32>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, st);
-        case 64: return launch_di<T, 64>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, st);
-        default: return launch_di<T, 128>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, st);
+        case 32: return launch_di<T, 32>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, hist, st);
+        case 64: return launch_di<T, 64>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, hist, st);
+        default: return launch_di<T, 128>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, hist, st);
     }
 }
 
 hipError_t launch_index_scores(int dt, int B, int Tq, int N, int HI, int dI, int m, int64_t q_pos0, const void *qI,
-                               const float *w, const void *kI, int64_t k_bs, float *scores, hipStream_t st) {
-    if (dt == 0) return launch_dt<float>(B, Tq, N, HI, dI, m, q_pos0, qI, w, kI, k_bs, scores, st);
-    return launch_dt<bf16_t>(B, Tq, N, HI, dI, m, q_pos0, qI, w, kI, k_bs, scores, st);
+                               const float *w, const void *kI, int64_t k_bs, float *scores, uint32_t *hist,
+                               hipStream_t st) {
+    if (dt == 0) return launch_dt<float>(B, Tq, N, HI, dI, m, q_pos0, qI, w, kI, k_bs, scores, hist, st);
+    return launch_dt<bf16_t>(B, Tq, N, HI, dI, m, q_pos0, qI, w, kI, k_bs, scores, hist, st);
 }
 
 }  // namespace csa

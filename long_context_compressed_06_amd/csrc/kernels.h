@@ -10,15 +10,44 @@ namespace csa {
 
 // longest score row that the top-k kernel stages in LDS (128 KiB of keys)
 constexpr int kTopkLdsKeys = 32768;
+// first radix digit of the top-k select: the top 11 bits of the score key,
+// counted per query by the indexer epilogue
+constexpr int kTopkBinBits = 11;
+constexpr int kTopkBins = 1 << kTopkBinBits;
+// decode (few queries) top-k: scores per filter workgroup, candidates the
+// final workgroup keeps in LDS, and the largest row it accepts
+constexpr int kTopkFilterChunk = 4096;
+constexpr int kTopkFinalCand = 12288;
+constexpr int64_t kTopkMaxEntries = (int64_t)kTopkFilterChunk * 1023;
+
+struct TopkPlan {
+    bool filter;     // multi-workgroup filter + final path (else one workgroup per query)
+    int64_t nblk;    // filter workgroups per query
+};
+TopkPlan topk_plan(int64_t rows, int64_t N);
+// workspace layout after the score rows: histogram, filter segments, counts
+size_t topk_scratch_bytes(int64_t rows, int64_t N);
 
 hipError_t launch_compress(int dt, int B, int G, int m, int d, const void *raw, int64_t raw_bs,
                            const float *logits, int64_t log_bs, void *out, int64_t out_bs, hipStream_t st);
 
+// hist: optional [rows, kTopkBins] counts, must be zero on entry
 hipError_t launch_index_scores(int dt, int B, int Tq, int N, int HI, int dI, int m, int64_t q_pos0, const void *qI,
-                               const float *w, const void *kI, int64_t k_bs, float *scores, hipStream_t st);
+                               const float *w, const void *kI, int64_t k_bs, float *scores, uint32_t *hist,
+                               hipStream_t st);
 
-hipError_t launch_topk(int B, int Tq, int N, int m, int k, int64_t q_pos0, const float *scores, int32_t *out,
-                       hipStream_t st);
+hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t st);
+
+// scratch: topk_scratch_bytes(rows, N) bytes; its histogram part must have
+// been filled by launch_index_scores (zeroed before it)
+hipError_t launch_topk(int B, int Tq, int N, int m, int k, int64_t q_pos0, const float *scores, void *scratch,
+                       int32_t *out, hipStream_t st);
+
+// attention work split: aim for this many workgroups, at most this many
+// splits of one query's rows, and at most this many 32-row tiles per split
+constexpr int kMqaTargetBlocks = 160;
+constexpr int kMqaMaxSplits = 16;
+constexpr int kMqaMaxTilesPerSplit = 120;
 
 // split count and tiles (of 32 rows) per split for `rows` queries whose row
 // lists hold at most n_rows_max rows

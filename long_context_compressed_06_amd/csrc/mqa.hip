@@ -7,17 +7,24 @@
 // list; split-K partials (unnormalised O, running max, running sum) are merged
 // by k_combine.  With a single split the workgroup writes the final output.
 //
-// Workgroup.  Four wavefronts, each owning 16 query heads.  A tile of 32 rows
-// (gathered entries or raw window rows) is copied from HBM to LDS twice:
-// row-major (Kt) for the logits and d-major (Vt) for the weighted sum, with
-// rows ordered inside each d-row so that every lane's MFMA operand is one
-// contiguous 16-byte LDS read.  Per wave and tile:
-//   S^T[32 rows x 16 heads] = Kt . Q^T   (MFMA, Q^T held in registers)
-//   online softmax per head (running max / sum kept per lane, fp32)
-//   O^T[d x 16 heads]     += Vt . P^T    (MFMA; P split into a bf16 high part
-//                                         and a bf16 low part for bf16 data so
-//                                         the weights keep ~16 bits)
-// O^T lives in registers (d/16 accumulator tiles per wave).
+// Workgroup.  Four wavefronts, each owning 16 query heads.  The split's row
+// addresses (gathered entries, then raw window rows) are resolved once into
+// an LDS table.  Tiles of 32 rows then stream HBM -> LDS with asynchronous
+// 16-byte LDS-DMA loads (global_load_lds_dwordx4), STAGES tiles in flight,
+// so no register staging and no dependent global load sits in the loop.  A
+// tile is stored row-major with the 16-byte chunks of row r XOR-swizzled by
+// swz(r); the swizzle is applied by choosing which source chunk each lane
+// fetches.  Per wave and tile:
+//   S^T[32 rows x 16 heads] = K . Q^T   (MFMA; K rows read with ds_read_b128,
+//                                        Q^T held in registers)
+//   online softmax per head (running max / sum per lane, fp32)
+//   O^T[d x 16 heads]      += V^T . P^T  (MFMA; V^T read straight from the
+//                                        row-major tile with the gfx950
+//                                        transposing ds_read_b64_tr_b16; P is
+//                                        split into bf16 high and low parts so
+//                                        the weights keep ~16 bits)
+// O^T stays in registers (d/16 accumulator tiles per wave).  fp32 data uses
+// the 16x16x4 f32 MFMA with scalar LDS reads instead.
 #include "kernels.h"
 
 namespace csa {
@@ -33,17 +40,52 @@ struct MqaArgs {
 
 template <typename T, int D>
 struct MqaShape {
-    static constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte chunk
-    static constexpr int TR = 32;               // rows per tile
-    static constexpr int KROW = D + VEC;        // padded row of Kt (elements)
-    static constexpr int VROW = TR + VEC;       // padded d-row of Vt (elements)
-    static constexpr size_t lds_bytes =
-        (size_t)(TR * KROW + D * VROW) * sizeof(T) + TR * sizeof(void *);
+    static constexpr int TR = 32;                      // rows per tile
+    static constexpr int ROWB = D * (int)sizeof(T);    // bytes per row
+    static constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
+    static constexpr int TILEB = TR * ROWB;            // bytes per tile
+    static constexpr int NI = TILEB / 1024;            // DMA instructions per tile (1 KiB each)
+    static constexpr int LPW = NI / 4;                 // ... per wavefront
+    // tiles in flight: three for tiles up to 32 KiB, two up to 64 KiB; narrow
+    // rows (fewer than four loads per tile) are not pipelined
+    static constexpr int STAGES = LPW < 1 ? 1 : (TILEB <= 32768 ? 3 : (TILEB <= 65536 ? 2 : 1));
+    static size_t lds_bytes(int tiles_per_split) {
+        return (size_t)STAGES * TILEB + (size_t)tiles_per_split * TR * sizeof(void *);
+    }
 };
 
-// slot of tile row r inside a d-row of Vt: lane group g's rows {4g..4g+3,
-// 16+4g..16+4g+3} become the contiguous slots 8g .. 8g+7
-__device__ __forceinline__ int vt_slot(int r) { return 8 * ((r & 15) >> 2) + 4 * (r >> 4) + (r & 3); }
+// chunk swizzle of tile row r: bijective on the low 4 bits, and rows
+// 4g..4g+3 map to chunks differing in bits 1..3 so that transposing reads
+// of 4 rows x 2 chunks and row-parallel reads of 16 rows avoid bank conflicts
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+    return ((((r & 7) << 1) | ((r >> 3) & 1)) | (r & ~15)) & (CPR - 1);
+}
+
+template <int CPR>
+__device__ __forceinline__ int tile_off(int r, int byte) {
+    return r * CPR * 16 + ((((byte >> 4) ^ swz<CPR>(r)) << 4) | (byte & 15));
+}
+
+// 16 bytes per lane from `src` into LDS at lds_base + 16 * lane.  Issued from
+// inline assembly so that the compiler does not treat every later LDS read as
+// dependent on it (it would drain all tiles in flight); completion is awaited
+// explicitly with wait_vm_barrier.  One wait state separates the M0 write
+// from the LDS-DMA instruction, as the ISA requires.
+__device__ __forceinline__ void dma16(const void *lds_base, const void *src) {
+    const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(l), "v"(src)
+                 : "memory", "m0");
+}
+// wait until at most N vector-memory operations of this wave are in flight,
+// then barrier; one statement, so no LDS access is scheduled across it
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+typedef short v4s __attribute__((ext_vector_type(4)));
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_mqa(const MqaArgs a) {
@@ -51,11 +93,10 @@ __global__ __launch_bounds__(256) void k_mqa(const MqaArgs a) {
     using S = MqaShape<T, D>;
     constexpr int KS = D / E::KSTEP;
     constexpr int NB = D / 16;
-    constexpr int CPR = D / S::VEC;
+    constexpr int CPR = S::CPR;
     extern __shared__ __align__(16) unsigned char smem[];
-    T *Kt = (T *)smem;
-    T *Vt = Kt + S::TR * S::KROW;
-    const T **rsrc = (const T **)(Vt + D * S::VROW);
+    unsigned char *tiles = smem;
+    const T **rtab = (const T **)(smem + S::STAGES * S::TILEB);
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, c = lane & 15;
     const int64_t row = blockIdx.x / a.n_splits;
@@ -66,106 +107,166 @@ __global__ __launch_bounds__(256) void k_mqa(const MqaArgs a) {
     const int64_t w0 = t - a.W + 1 > 0 ? t - a.W + 1 : 0;
     const int64_t n_win = a.W > 0 ? t - w0 + 1 : 0;
     const int64_t n_rows = n_slots + n_win;
-    const int64_t n_tiles = (n_rows + S::TR - 1) / S::TR;
+    const int64_t n_tiles_all = (n_rows + S::TR - 1) / S::TR;
     const int64_t tile_lo = (int64_t)split * a.tiles_per_split;
-    const int64_t tile_hi = min(n_tiles, tile_lo + a.tiles_per_split);
+    const int ntiles = (int)max((int64_t)0, min(n_tiles_all, tile_lo + a.tiles_per_split) - tile_lo);
     const int head = wv * 16 + c;
     const bool wave_on = wv * 16 < a.H;
 
+    // Q^T fragments (B operand of the logits product)
     const T *qrow = (const T *)a.q + (row * a.H + head) * (int64_t)D + g * E::KPL;
     typename E::frag qf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = (wave_on && head < a.H) ? E::load(qrow + ks * E::KSTEP) : E::zero();
+
+    // resolve the split's row addresses once (nullptr = masked row)
+    const T *ent_b = (const T *)a.entries + b * a.e_bs;
+    const T *raw_b = (const T *)a.raw + b * a.raw_bs;
+    const int nr = ntiles * S::TR;
+    for (int i = tid; i < nr; i += 256) {
+        const int64_t r = tile_lo * S::TR + i;
+        const T *src = nullptr;
+        if (r < n_slots) {
+            const int64_t j = a.k > 0 ? (int64_t)a.idx[row * a.k + r] : r;
+            if (j >= 0 && j < nv) src = ent_b + j * D;
+        } else if (r < n_rows) {
+            src = raw_b + (w0 + (r - n_slots) - a.raw_pos0) * D;
+        }
+        rtab[i] = src;
+    }
+    // vmcnt(0) through the intrinsic, so the compiler knows the Q^T loads have
+    // landed and puts no wait for them inside the tile loop
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    // any valid row of the split stands in for masked rows (their weight is 0)
+    const T *dummy = nullptr;
+    for (int i = 0; i < nr && !dummy; ++i) dummy = rtab[i];
 
     floatx4 o[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) o[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    const T *ent_b = (const T *)a.entries + b * a.e_bs;
-    const T *raw_b = (const T *)a.raw + b * a.raw_bs;
-    for (int64_t tile = tile_lo; tile < tile_hi; ++tile) {
-        if (tid < S::TR) {
-            const int64_t r = tile * S::TR + tid;
-            const T *src = nullptr;
-            if (r < n_slots) {
-                const int64_t j = a.k > 0 ? (int64_t)a.idx[row * a.k + r] : r;
-                if (j >= 0 && j < nv) src = ent_b + j * D;
-            } else if (r < n_rows) {
-                src = raw_b + (w0 + (r - n_slots) - a.raw_pos0) * D;
-            }
-            rsrc[tid] = src;
-        }
-        __syncthreads();
-        for (int ci = tid; ci < S::TR * CPR; ci += 256) {
-            const int rr = ci / CPR, cc = ci % CPR;
-            const T *src = rsrc[rr];
-            const u32x4 v = src ? *(const u32x4 *)(src + cc * S::VEC) : u32x4{0u, 0u, 0u, 0u};
-            *(u32x4 *)(Kt + rr * S::KROW + cc * S::VEC) = v;
-            const T *ve = (const T *)&v;
-            const int slot = vt_slot(rr);
+    if (dummy) {
+        // issue the DMA of local tile `lt` into stage buffer lt % STAGES
+        auto issue = [&](int lt) {
+            unsigned char *buf = tiles + (lt % S::STAGES) * S::TILEB;
+            if constexpr (S::LPW >= 1) {
 #pragma unroll
-            for (int e = 0; e < S::VEC; ++e) Vt[(cc * S::VEC + e) * S::VROW + slot] = ve[e];
-        }
-        __syncthreads();
-        if (wave_on) {
-            floatx4 sacc[2];
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                sacc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
-                const T *kr = Kt + (rb * 16 + c) * S::KROW + g * E::KPL;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) sacc[rb] = E::mma(E::load(kr + ks * E::KSTEP), qf[ks], sacc[rb]);
-            }
-            float sv[8];
-            float mx = -INFINITY;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int rl = (q >> 2) * 16 + 4 * g + (q & 3);
-                sv[q] = rsrc[rl] ? sacc[q >> 2][q & 3] * a.scale : -INFINITY;
-                mx = fmaxf(mx, sv[q]);
-            }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = m_new == -INFINITY ? 1.f : expf(m_run - m_new);
-            float p[8], psum = 0.f;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                p[q] = sv[q] == -INFINITY ? 0.f : expf(sv[q] - m_new);
-                psum += p[q];
-            }
-            l_run = l_run * alpha + psum;
-            m_run = m_new;
-            if (__ballot(alpha != 1.f)) {
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) o[nb] *= alpha;
-            }
-            const T *vr = Vt + c * S::VROW + 8 * g;
-            if constexpr (sizeof(T) == 2) {
-                bf16x8 hi, lo;
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const bf16_t h = f32_to_bf16(p[q]);
-                    hi[q] = __builtin_bit_cast(__bf16, h);
-                    lo[q] = __builtin_bit_cast(__bf16, f32_to_bf16(p[q] - bf16_to_f32(h)));
-                }
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const bf16x8 va = *(const bf16x8 *)(vr + nb * 16 * S::VROW);
-                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, hi, o[nb], 0, 0, 0);
-                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, lo, o[nb], 0, 0, 0);
+                for (int u = 0; u < S::LPW; ++u) {
+                    const int ins = u * 4 + wv;
+                    const int q = ins * 64 + lane;  // chunk index within the tile
+                    const int r = q / CPR, pc = q % CPR;
+                    const T *src = rtab[lt * S::TR + r];
+                    src = src ? src : dummy;
+                    const unsigned char *gp = (const unsigned char *)src + ((pc ^ swz<CPR>(r)) << 4);
+                    dma16(buf + ins * 1024, gp);
                 }
             } else {
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                    for (int q = 0; q < 8; ++q)
-                        o[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(((const float *)vr)[nb * 16 * S::VROW + q], p[q],
-                                                                     o[nb], 0, 0, 0);
+                // narrow rows: fewer than four 1 KiB loads per tile
+                for (int ins = wv; ins < S::NI; ins += 4) {
+                    const int q = ins * 64 + lane;
+                    const int r = q / CPR, pc = q % CPR;
+                    const T *src = rtab[lt * S::TR + r];
+                    src = src ? src : dummy;
+                    const unsigned char *gp = (const unsigned char *)src + ((pc ^ swz<CPR>(r)) << 4);
+                    dma16(buf + ins * 1024, gp);
+                }
             }
+        };
+#pragma unroll
+        for (int s = 0; s < S::STAGES - 1; ++s)
+            if (s < ntiles) issue(s);
+
+        for (int lt = 0; lt < ntiles; ++lt) {
+            // keep STAGES-1 younger tiles in flight; wait until this tile's own loads landed
+            if (lt + S::STAGES - 1 < ntiles) issue(lt + S::STAGES - 1);
+            const int younger = min(ntiles - 1 - lt, S::STAGES - 1);
+            if (S::STAGES == 3 && younger == 2)
+                wait_vm_barrier<2 * S::LPW>();
+            else if (S::STAGES >= 2 && younger == 1)
+                wait_vm_barrier<S::LPW>();
+            else
+                wait_vm_barrier<0>();
+            const unsigned char *buf = tiles + (lt % S::STAGES) * S::TILEB;
+            const T *const *rt = rtab + lt * S::TR;
+            if (wave_on) {
+                floatx4 sacc[2];
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+                    sacc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+                    const int r = rb * 16 + c;
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const int byte = (ks * E::KSTEP + g * E::KPL) * (int)sizeof(T);
+                        const typename E::frag kf = *(const typename E::frag *)(buf + tile_off<CPR>(r, byte));
+                        sacc[rb] = E::mma(kf, qf[ks], sacc[rb]);
+                    }
+                }
+                float sv[8];
+                float mx = -INFINITY;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int rl = (q >> 2) * 16 + 4 * g + (q & 3);
+                    sv[q] = rt[rl] ? sacc[q >> 2][q & 3] * a.scale : -INFINITY;
+                    mx = fmaxf(mx, sv[q]);
+                }
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = m_new == -INFINITY ? 1.f : expf(m_run - m_new);
+                float p[8], psum = 0.f;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    p[q] = sv[q] == -INFINITY ? 0.f : expf(sv[q] - m_new);
+                    psum += p[q];
+                }
+                l_run = l_run * alpha + psum;
+                m_run = m_new;
+                if (__ballot(alpha != 1.f)) {
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) o[nb] *= alpha;
+                }
+                if constexpr (sizeof(T) == 2) {
+                    bf16x8 hi, lo;
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const bf16_t h = f32_to_bf16(p[q]);
+                        hi[q] = __builtin_bit_cast(__bf16, h);
+                        lo[q] = __builtin_bit_cast(__bf16, f32_to_bf16(p[q] - bf16_to_f32(h)));
+                    }
+                    // lane (g, c) addresses rows 4g + c/4 (and +16), columns nb*16 + 4*(c%4) .. +3;
+                    // the transposing read hands lane c the column nb*16 + c of rows 4g..4g+3
+                    const int r1 = 4 * g + (c >> 2), r2 = r1 + 16;
+                    const int cb = 8 * (c & 3);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const int byte = nb * 32 + cb;
+                        const v4s v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) v4s *)(buf + tile_off<CPR>(r1, byte)));
+                        const v4s v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) v4s *)(buf + tile_off<CPR>(r2, byte)));
+                        const bf16x8 va = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, v1),
+                                                                  __builtin_bit_cast(bf16x4_t, v2), 0, 1, 2, 3, 4,
+                                                                  5, 6, 7);
+                        o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, hi, o[nb], 0, 0, 0);
+                        o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, lo, o[nb], 0, 0, 0);
+                    }
+                } else {
+                    // fp32: 16x16x4 steps, one row per lane group: lane (g, c) gives
+                    // V[rb*16 + 4g + e][nb*16 + c] with the weight of that row
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) {
+                            const int r = (q >> 2) * 16 + 4 * g + (q & 3);
+                            const float v = *(const float *)(buf + tile_off<CPR>(r, (nb * 16 + c) * 4));
+                            o[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, p[q], o[nb], 0, 0, 0);
+                        }
+                }
+            }
+            lds_barrier();
         }
-        __syncthreads();
     }
 
     if (!wave_on) return;
@@ -224,10 +325,12 @@ __global__ __launch_bounds__(128) void k_combine(int H, int D, int n_splits, con
 int mqa_choose_splits(int64_t rows, int64_t n_rows_max, int *tiles_per_split) {
     int64_t tiles = (n_rows_max + 31) / 32;
     if (tiles < 1) tiles = 1;
-    int64_t s = (256 + rows - 1) / rows;
+    int64_t s = (kMqaTargetBlocks + rows - 1) / rows;
+    if (s > kMqaMaxSplits) s = kMqaMaxSplits;
     if (s < 1) s = 1;
     if (s > tiles) s = tiles;
     int64_t tps = (tiles + s - 1) / s;
+    if (tps > kMqaMaxTilesPerSplit) tps = kMqaMaxTilesPerSplit;  // bounds the LDS row table
     s = (tiles + tps - 1) / tps;
     *tiles_per_split = (int)tps;
     return (int)s;
@@ -236,13 +339,14 @@ int mqa_choose_splits(int64_t rows, int64_t n_rows_max, int *tiles_per_split) {
 template <typename T, int D>
 static hipError_t launch_mqa_t(const MqaArgs &a, int64_t rows, hipStream_t st) {
     using S = MqaShape<T, D>;
-    // one-time opt-in to more than 64 KiB of dynamic LDS for this instantiation
-    static const hipError_t attr = hipFuncSetAttribute(
-        (const void *)k_mqa<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::lds_bytes);
+    // one-time opt-in to the largest dynamic LDS this instantiation may use
+    static const hipError_t attr = hipFuncSetAttribute((const void *)k_mqa<T, D>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
-    hipError_t e;
-    hipLaunchKernelGGL((k_mqa<T, D>), dim3((unsigned)(rows * a.n_splits)), dim3(256), S::lds_bytes, st, a);
-    e = hipGetLastError();
+    const size_t lds = S::lds_bytes(a.tiles_per_split);
+    if (lds > 160 * 1024) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_mqa<T, D>), dim3((unsigned)(rows * a.n_splits)), dim3(256), lds, st, a);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_splits == 1) return e;
     hipLaunchKernelGGL(k_combine, dim3((unsigned)(rows * a.H)), dim3(128), 0, st, a.H, D, a.n_splits, a.part_o,
                        a.part_ml, a.out, a.lse);
