@@ -188,7 +188,7 @@ size_t csa_mqa_workspace_bytes(int B, int Tq, int H, int d, int n_rows_max) {
     if (B <= 0 || Tq <= 0 || H <= 0 || d <= 0) return 0;
     int tps = 0;
     const int64_t rows = (int64_t)B * Tq;
-    const int s = csa::mqa_choose_splits(rows, n_rows_max, &tps);
+    const int s = csa::mqa_choose_splits(rows, n_rows_max, d, &tps);
     if (s <= 1) return 0;
     const size_t bytes = (size_t)rows * s * H * (d + 2) * sizeof(float);
     return (bytes + 255) / 256 * 256;
@@ -233,7 +233,7 @@ static int mqa_common(int dt, int B, int Tq, int H, int d, int N, int m, int k, 
     const int64_t rows = (int64_t)B * Tq;
     const int64_t n_rows_max = (int64_t)(k > 0 ? k : N) + W;
     int tps = 0;
-    const int splits = csa::mqa_choose_splits(rows, n_rows_max, &tps);
+    const int splits = csa::mqa_choose_splits(rows, n_rows_max, d, &tps);
     float *ws = nullptr;
     if (splits > 1) {
         const size_t need = csa_mqa_workspace_bytes(B, Tq, H, d, (int)n_rows_max);

@@ -45,6 +45,8 @@ template <> struct Elem<float> {
     }
     // load the KPL consecutive elements starting at p
     static __device__ __forceinline__ frag load(const float *p) { return *p; }
+    // streaming load that is not kept in the caches
+    static __device__ __forceinline__ frag load_nt(const float *p) { return __builtin_nontemporal_load(p); }
     static __device__ __forceinline__ frag zero() { return 0.f; }
 };
 
@@ -58,6 +60,9 @@ template <> struct Elem<bf16_t> {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
     static __device__ __forceinline__ frag load(const bf16_t *p) { return *(const bf16x8 *)p; }
+    static __device__ __forceinline__ frag load_nt(const bf16_t *p) {
+        return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4 *)p));
+    }
     static __device__ __forceinline__ frag zero() {
         frag z;
         for (int i = 0; i < 8; ++i) z[i] = (__bf16)0.0f;

@@ -9,8 +9,9 @@
 // every key byte is read exactly once with 16-byte loads that cover whole
 // rows.  The 16x16 output tile holds four heads per lane for one entry: the
 // ReLU, the head weight and the head sum happen in registers, and two
-// cross-lane exchanges finish the sum over the four lane groups.  UNROLL
-// tiles of loads are issued before their MFMAs to keep HBM busy.
+// cross-lane exchanges finish the sum over the four lane groups.  Keys are
+// read with non-temporal loads in batches of UNROLL tiles, double-buffered so
+// one batch is in flight while the previous one is scored.
 //
 // Optionally (hist != nullptr) the epilogue also counts every visible score
 // by the top 11 bits of its order-preserving key (the first radix digit of
@@ -48,12 +49,15 @@ __global__ __launch_bounds__(256) void k_index_scores(int Tq, int N, int HI, int
     for (int mb = 0; mb < MB; ++mb) {
         const int head = mb * 16 + c;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            a[mb][ks] = head < HI ? E::load(qI + (row * HI + head) * DI + ks * E::KSTEP + g * E::KPL) : E::zero();
+        for (int ks = 0; ks < KS; ++ks) {
+            const typename E::frag v = E::load(qI + (row * HI + min(head, HI - 1)) * DI + ks * E::KSTEP + g * E::KPL);
+            a[mb][ks] = head < HI ? v : E::zero();
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int hh = mb * 16 + 4 * g + e;
-            wgt[mb][e] = hh < HI ? w[row * HI + hh] : 0.f;
+            const float wv_ = w[row * HI + min(hh, HI - 1)];
+            wgt[mb][e] = hh < HI ? wv_ : 0.f;
         }
     }
 
@@ -61,16 +65,25 @@ __global__ __launch_bounds__(256) void k_index_scores(int Tq, int N, int HI, int
     float *srow = scores + row * (int64_t)N;
     const int64_t j_lo = (int64_t)chunk * tiles_per_chunk * 16;
     const int64_t j_hi = min((int64_t)N, j_lo + (int64_t)tiles_per_chunk * 16);
-    for (int64_t j0 = j_lo; j0 < j_hi; j0 += 16 * UNROLL) {
-        typename E::frag bf[UNROLL][KS];
+    constexpr int BATCH = 16 * UNROLL;  // entries per batch of tiles
+
+    if (nv == 0) {  // nothing visible: the chunk is all -inf
+        for (int64_t j = j_lo + lane; j < j_hi; j += 64) srow[j] = -INFINITY;
+    } else {
+    // one batch: UNROLL tiles of 16 index keys, straight from HBM to registers.
+    // Loads are unconditional so the compiler can wait for exactly one batch:
+    // lanes past the chunk (or past the visible entries) reread its last row.
+    const int64_t j_last = min(j_hi, nv) - 1;
+    auto load_batch = [&](int64_t j0, typename E::frag (&bf)[UNROLL][KS]) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             int64_t jr = j0 + u * 16 + c;
-            jr = jr < nv ? jr : (nv > 0 ? nv - 1 : 0);  // clamp: masked lanes reread a valid row
+            jr = jr < j_last ? jr : j_last;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                bf[u][ks] = nv > 0 ? E::load(kb + jr * DI + ks * E::KSTEP) : E::zero();
+            for (int ks = 0; ks < KS; ++ks) bf[u][ks] = E::load_nt(kb + jr * DI + ks * E::KSTEP);
         }
+    };
+    auto score_batch = [&](int64_t j0, const typename E::frag (&bf)[UNROLL][KS]) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int64_t j = j0 + u * 16 + c;
@@ -89,8 +102,19 @@ __global__ __launch_bounds__(256) void k_index_scores(int Tq, int N, int HI, int
             s += __shfl_xor(s, 16);
             s += __shfl_xor(s, 32);
             if (g == 0 && j < j_hi) srow[j] = j < nv ? s : -INFINITY;
-            if (hist && g == 0 && j < nv) atomicAdd(&whist[wv][order_key(s) >> (32 - kTopkBinBits)], 1u);
+            if (hist && g == 0 && j < j_hi && j < nv)
+                atomicAdd(&whist[wv][order_key(s) >> (32 - kTopkBinBits)], 1u);
         }
+    };
+    // double-buffered: the next batch is in flight while this one is scored
+    typename E::frag b0[UNROLL][KS], b1[UNROLL][KS];
+    if (j_lo < j_hi) load_batch(j_lo, b0);
+    for (int64_t j0 = j_lo; j0 < j_hi; j0 += 2 * BATCH) {
+        load_batch(j0 + BATCH, b1);
+        score_batch(j0, b0);
+        load_batch(j0 + 2 * BATCH, b0);
+        if (j0 + BATCH < j_hi) score_batch(j0 + BATCH, b1);
+    }
     }
     if (hist) {
         // LDS operations of one wave complete in order: the counts are final here

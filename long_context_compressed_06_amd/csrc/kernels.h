@@ -47,11 +47,14 @@ hipError_t launch_topk(int B, int Tq, int N, int m, int k, int64_t q_pos0, const
 // splits of one query's rows, and at most this many 32-row tiles per split
 constexpr int kMqaTargetBlocks = 160;
 constexpr int kMqaMaxSplits = 16;
+// (the row table shares LDS with the tile stages: fp32 rows of d=512 leave
+// room for 56 tiles)
 constexpr int kMqaMaxTilesPerSplit = 120;
+constexpr int mqa_max_tiles_per_split(int d) { return d >= 512 ? 56 : kMqaMaxTilesPerSplit; }
 
 // split count and tiles (of 32 rows) per split for `rows` queries whose row
 // lists hold at most n_rows_max rows
-int mqa_choose_splits(int64_t rows, int64_t n_rows_max, int *tiles_per_split);
+int mqa_choose_splits(int64_t rows, int64_t n_rows_max, int d, int *tiles_per_split);
 
 // ws: split-K partials, rows*n_splits*H*(d+2) floats (unused when n_splits == 1)
 hipError_t launch_mqa(int dt, int B, int Tq, int H, int d, int N, int m, int k, int W, int64_t q_pos0, float scale,

@@ -7,24 +7,29 @@
 // list; split-K partials (unnormalised O, running max, running sum) are merged
 // by k_combine.  With a single split the workgroup writes the final output.
 //
-// Workgroup.  Four wavefronts, each owning 16 query heads.  The split's row
-// addresses (gathered entries, then raw window rows) are resolved once into
-// an LDS table.  Tiles of 32 rows then stream HBM -> LDS with asynchronous
-// 16-byte LDS-DMA loads (global_load_lds_dwordx4), STAGES tiles in flight,
-// so no register staging and no dependent global load sits in the loop.  A
-// tile is stored row-major with the 16-byte chunks of row r XOR-swizzled by
-// swz(r); the swizzle is applied by choosing which source chunk each lane
-// fetches.  Per wave and tile:
-//   S^T[32 rows x 16 heads] = K . Q^T   (MFMA; K rows read with ds_read_b128,
-//                                        Q^T held in registers)
-//   online softmax per head (running max / sum per lane, fp32)
-//   O^T[d x 16 heads]      += V^T . P^T  (MFMA; V^T read straight from the
-//                                        row-major tile with the gfx950
-//                                        transposing ds_read_b64_tr_b16; P is
-//                                        split into bf16 high and low parts so
-//                                        the weights keep ~16 bits)
-// O^T stays in registers (d/16 accumulator tiles per wave).  fp32 data uses
-// the 16x16x4 f32 MFMA with scalar LDS reads instead.
+// Workgroup.  Eight wavefronts: wave w owns the 16 query heads of group
+// w % 4 and the half w / 4 of the latent width d (SPLITD = 2; narrow rows use
+// one wave per head group with the whole width).  The split's row addresses
+// (gathered entries, then raw window rows) are resolved once into an LDS
+// table, with a 32-bit validity mask per tile.  Tiles of 32 rows then stream
+// HBM -> LDS with asynchronous 16-byte LDS-DMA loads
+// (global_load_lds_dwordx4), STAGES tiles in flight, so no register staging
+// and no dependent global load sits in the loop.  One DMA instruction moves
+// up to 1 KiB of one row; rows sit 16 bytes apart beyond their length in LDS,
+// so every LDS offset of the loop is a compile-time immediate.  Per wave and
+// tile:
+//   S^T[32 rows x 16 heads] = K . Q^T over the wave's half of d (MFMA, K rows
+//       read with ds_read_b128, Q^T in registers); the two halves are summed
+//       through LDS, and both waves of the pair run the same softmax
+//   online softmax per head in the base-2 domain; the reference maximum only
+//   moves when the running maximum exceeds it by 2^8, so the accumulator is
+//   rarely rescaled (weights stay <= 256, exact in fp32)
+//   O^T[d/2 x 16 heads] += V^T . P^T (MFMA; V^T read straight from the
+//       row-major tile with the gfx950 transposing ds_read_b64_tr_b16; P is
+//       split into bf16 high and low parts so the weights keep ~16 bits)
+// Splitting d keeps per-wave state at 16 x 256 fp32 accumulators, so two
+// waves per SIMD hide LDS and MFMA latency.  fp32 data uses the 16x16x4 f32
+// MFMA with scalar LDS reads instead.
 #include "kernels.h"
 
 namespace csa {
@@ -38,40 +43,35 @@ struct MqaArgs {
     float *out, *lse, *part_o, *part_ml;
 };
 
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazyRescale = 8.f;  // base-2 headroom of the reference maximum
+constexpr int kMqaThreads = 512;
+
 template <typename T, int D>
 struct MqaShape {
-    static constexpr int TR = 32;                      // rows per tile
-    static constexpr int ROWB = D * (int)sizeof(T);    // bytes per row
-    static constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
-    static constexpr int TILEB = TR * ROWB;            // bytes per tile
-    static constexpr int NI = TILEB / 1024;            // DMA instructions per tile (1 KiB each)
-    static constexpr int LPW = NI / 4;                 // ... per wavefront
-    // tiles in flight: three for tiles up to 32 KiB, two up to 64 KiB; narrow
-    // rows (fewer than four loads per tile) are not pipelined
-    static constexpr int STAGES = LPW < 1 ? 1 : (TILEB <= 32768 ? 3 : (TILEB <= 65536 ? 2 : 1));
+    static constexpr int TR = 32;                          // rows per tile
+    static constexpr int ROWB = D * (int)sizeof(T);        // bytes per row
+    static constexpr int RS = ROWB + 16;                   // LDS row stride (padded)
+    static constexpr int TILEB = TR * RS;                  // LDS bytes per tile
+    static constexpr int IPR = ROWB >= 1024 ? ROWB / 1024 : 1;  // DMA instructions per row
+    static constexpr int LPI = ROWB >= 1024 ? 64 : ROWB / 16;   // active lanes per DMA instruction
+    static constexpr int NW = kMqaThreads / 64;            // wavefronts
+    static constexpr int LPW = (TR / NW) * IPR;            // DMA instructions per wave per tile
+    static constexpr int SPLITD = (D / 2) % Elem<T>::KSTEP == 0 && (D / 2) % 16 == 0 ? 2 : 1;
+    static constexpr int DW = D / SPLITD;                  // latent columns per wave
+    static constexpr int XCH = SPLITD == 2 ? NW * 64 * 8 * 4 : 0;  // partial-logit exchange bytes
+    static constexpr int STAGES = 3 * TILEB + XCH <= 120 * 1024 ? 3 : 2;  // tiles in flight
     static size_t lds_bytes(int tiles_per_split) {
-        return (size_t)STAGES * TILEB + (size_t)tiles_per_split * TR * sizeof(void *);
+        return (size_t)STAGES * TILEB + XCH + (size_t)tiles_per_split * (TR * sizeof(void *) + 4);
     }
 };
 
-// chunk swizzle of tile row r: bijective on the low 4 bits, and rows
-// 4g..4g+3 map to chunks differing in bits 1..3 so that transposing reads
-// of 4 rows x 2 chunks and row-parallel reads of 16 rows avoid bank conflicts
-template <int CPR>
-__device__ __forceinline__ int swz(int r) {
-    return ((((r & 7) << 1) | ((r >> 3) & 1)) | (r & ~15)) & (CPR - 1);
-}
-
-template <int CPR>
-__device__ __forceinline__ int tile_off(int r, int byte) {
-    return r * CPR * 16 + ((((byte >> 4) ^ swz<CPR>(r)) << 4) | (byte & 15));
-}
-
-// 16 bytes per lane from `src` into LDS at lds_base + 16 * lane.  Issued from
-// inline assembly so that the compiler does not treat every later LDS read as
-// dependent on it (it would drain all tiles in flight); completion is awaited
-// explicitly with wait_vm_barrier.  One wait state separates the M0 write
-// from the LDS-DMA instruction, as the ISA requires.
+// 16 bytes per active lane from `src` into LDS at lds_base + 16 * lane.
+// Issued from inline assembly so that the compiler does not treat every
+// later LDS read as dependent on it (it would drain all tiles in flight);
+// completion is awaited explicitly with wait_vm_barrier.  One wait state
+// separates the M0 write from the LDS-DMA instruction, as the ISA requires.
 __device__ __forceinline__ void dma16(const void *lds_base, const void *src) {
     const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(l), "v"(src)
@@ -88,17 +88,20 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 typedef short v4s __attribute__((ext_vector_type(4)));
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_mqa(const MqaArgs a) {
+__global__ __launch_bounds__(kMqaThreads) void k_mqa(const MqaArgs a) {
     using E = Elem<T>;
     using S = MqaShape<T, D>;
-    constexpr int KS = D / E::KSTEP;
-    constexpr int NB = D / 16;
-    constexpr int CPR = S::CPR;
+    constexpr int KS = S::DW / E::KSTEP;   // logits K-steps per wave
+    constexpr int NB = S::DW / 16;         // accumulator tiles per wave
+    constexpr int NHG = S::NW / S::SPLITD; // head groups served
     extern __shared__ __align__(16) unsigned char smem[];
     unsigned char *tiles = smem;
-    const T **rtab = (const T **)(smem + S::STAGES * S::TILEB);
+    floatx4 *xch = (floatx4 *)(smem + S::STAGES * S::TILEB);
+    const T **rtab = (const T **)(smem + S::STAGES * S::TILEB + S::XCH);
+    uint32_t *vmask = (uint32_t *)(rtab + a.tiles_per_split * S::TR);
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, c = lane & 15;
+    const int hg = wv % NHG, dh = wv / NHG;  // head group, half of d
     const int64_t row = blockIdx.x / a.n_splits;
     const int split = blockIdx.x % a.n_splits;
     const int64_t b = row / a.Tq, t = a.q_pos0 + row % a.Tq;
@@ -110,29 +113,39 @@ __global__ __launch_bounds__(256) void k_mqa(const MqaArgs a) {
     const int64_t n_tiles_all = (n_rows + S::TR - 1) / S::TR;
     const int64_t tile_lo = (int64_t)split * a.tiles_per_split;
     const int ntiles = (int)max((int64_t)0, min(n_tiles_all, tile_lo + a.tiles_per_split) - tile_lo);
-    const int head = wv * 16 + c;
-    const bool wave_on = wv * 16 < a.H;
+    const int head = hg * 16 + c;
+    const bool wave_on = hg * 16 < a.H && (S::SPLITD == 2 || wv < NHG);
+    const float scale2 = a.scale * kLog2e;
+    const int dcol0 = dh * S::DW;  // first latent column of this wave
 
-    // Q^T fragments (B operand of the logits product)
-    const T *qrow = (const T *)a.q + (row * a.H + head) * (int64_t)D + g * E::KPL;
+    // Q^T fragments over the wave's columns (B operand of the logits product)
+    const T *qrow = (const T *)a.q + (row * a.H + min(head, a.H - 1)) * (int64_t)D + dcol0 + g * E::KPL;
     typename E::frag qf[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = (wave_on && head < a.H) ? E::load(qrow + ks * E::KSTEP) : E::zero();
+    for (int ks = 0; ks < KS; ++ks) {
+        const typename E::frag v = E::load(qrow + ks * E::KSTEP);
+        qf[ks] = head < a.H ? v : E::zero();
+    }
 
     // resolve the split's row addresses once (nullptr = masked row)
     const T *ent_b = (const T *)a.entries + b * a.e_bs;
     const T *raw_b = (const T *)a.raw + b * a.raw_bs;
     const int nr = ntiles * S::TR;
-    for (int i = tid; i < nr; i += 256) {
-        const int64_t r = tile_lo * S::TR + i;
+    for (int i0 = 0; i0 < nr; i0 += kMqaThreads) {
+        const int i = i0 + tid;
         const T *src = nullptr;
-        if (r < n_slots) {
-            const int64_t j = a.k > 0 ? (int64_t)a.idx[row * a.k + r] : r;
-            if (j >= 0 && j < nv) src = ent_b + j * D;
-        } else if (r < n_rows) {
-            src = raw_b + (w0 + (r - n_slots) - a.raw_pos0) * D;
+        if (i < nr) {
+            const int64_t r = tile_lo * S::TR + i;
+            if (r < n_slots) {
+                const int64_t j = a.k > 0 ? (int64_t)a.idx[row * a.k + r] : r;
+                if (j >= 0 && j < nv) src = ent_b + j * D;
+            } else if (r < n_rows) {
+                src = raw_b + (w0 + (r - n_slots) - a.raw_pos0) * D;
+            }
+            rtab[i] = src;
         }
-        rtab[i] = src;
+        const uint64_t bal = __ballot(src != nullptr);  // bits of tiles i/32 (lanes 0-31) and i/32+1
+        if (i < nr && (lane & 31) == 0) vmask[i >> 5] = (uint32_t)(lane ? bal >> 32 : bal);
     }
     // vmcnt(0) through the intrinsic, so the compiler knows the Q^T loads have
     // landed and puts no wait for them inside the tile loop
@@ -145,32 +158,20 @@ __global__ __launch_bounds__(256) void k_mqa(const MqaArgs a) {
     floatx4 o[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) o[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_ref = -INFINITY, l_run = 0.f;  // base-2 reference maximum, running sum
 
     if (dummy) {
-        // issue the DMA of local tile `lt` into stage buffer lt % STAGES
+        // wave wv loads rows wv*TR/NW .. of local tile lt into stage lt % STAGES
         auto issue = [&](int lt) {
             unsigned char *buf = tiles + (lt % S::STAGES) * S::TILEB;
-            if constexpr (S::LPW >= 1) {
 #pragma unroll
-                for (int u = 0; u < S::LPW; ++u) {
-                    const int ins = u * 4 + wv;
-                    const int q = ins * 64 + lane;  // chunk index within the tile
-                    const int r = q / CPR, pc = q % CPR;
-                    const T *src = rtab[lt * S::TR + r];
-                    src = src ? src : dummy;
-                    const unsigned char *gp = (const unsigned char *)src + ((pc ^ swz<CPR>(r)) << 4);
-                    dma16(buf + ins * 1024, gp);
-                }
-            } else {
-                // narrow rows: fewer than four 1 KiB loads per tile
-                for (int ins = wv; ins < S::NI; ins += 4) {
-                    const int q = ins * 64 + lane;
-                    const int r = q / CPR, pc = q % CPR;
-                    const T *src = rtab[lt * S::TR + r];
-                    src = src ? src : dummy;
-                    const unsigned char *gp = (const unsigned char *)src + ((pc ^ swz<CPR>(r)) << 4);
-                    dma16(buf + ins * 1024, gp);
+            for (int u = 0; u < S::TR / S::NW; ++u) {
+                const int r = wv * (S::TR / S::NW) + u;
+                const T *src = rtab[lt * S::TR + r];
+                const unsigned char *gp = (const unsigned char *)(src ? src : dummy) + lane * 16;
+#pragma unroll
+                for (int ip = 0; ip < S::IPR; ++ip) {
+                    if (S::LPI == 64 || lane < S::LPI) dma16(buf + r * S::RS + ip * 1024, gp + ip * 1024);
                 }
             }
         };
@@ -178,74 +179,92 @@ __global__ __launch_bounds__(256) void k_mqa(const MqaArgs a) {
         for (int s = 0; s < S::STAGES - 1; ++s)
             if (s < ntiles) issue(s);
 
+        // per-lane LDS byte offsets (the rest are immediates)
+        const int cb = dcol0 * (int)sizeof(T);
+        const int k_off = c * S::RS + cb + g * E::KPL * (int)sizeof(T);     // logits product, rows c (+16)
+        const int v_off1 = (4 * g + (c >> 2)) * S::RS + cb + 8 * (c & 3);   // transposing reads, rows 4g..
+        const int v_off2 = v_off1 + 16 * S::RS;                             // ... and 16+4g..
+
         for (int lt = 0; lt < ntiles; ++lt) {
             // keep STAGES-1 younger tiles in flight; wait until this tile's own loads landed
             if (lt + S::STAGES - 1 < ntiles) issue(lt + S::STAGES - 1);
             const int younger = min(ntiles - 1 - lt, S::STAGES - 1);
             if (S::STAGES == 3 && younger == 2)
                 wait_vm_barrier<2 * S::LPW>();
-            else if (S::STAGES >= 2 && younger == 1)
+            else if (younger == 1)
                 wait_vm_barrier<S::LPW>();
             else
                 wait_vm_barrier<0>();
             const unsigned char *buf = tiles + (lt % S::STAGES) * S::TILEB;
-            const T *const *rt = rtab + lt * S::TR;
+            const uint32_t vm = vmask[lt];
+            floatx4 sacc[2];
             if (wave_on) {
-                floatx4 sacc[2];
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb) {
                     sacc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
-                    const int r = rb * 16 + c;
+                    const unsigned char *kr = buf + k_off + rb * 16 * S::RS;
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) {
-                        const int byte = (ks * E::KSTEP + g * E::KPL) * (int)sizeof(T);
-                        const typename E::frag kf = *(const typename E::frag *)(buf + tile_off<CPR>(r, byte));
+                        const typename E::frag kf =
+                            *(const typename E::frag *)(kr + ks * E::KSTEP * (int)sizeof(T));
                         sacc[rb] = E::mma(kf, qf[ks], sacc[rb]);
                     }
                 }
+            }
+            if constexpr (S::SPLITD == 2) {
+                // sum the two halves of the logits: publish, barrier, add the partner's
+                if (wave_on) {
+                    xch[(wv * 2 + 0) * 64 + lane] = sacc[0];
+                    xch[(wv * 2 + 1) * 64 + lane] = sacc[1];
+                }
+                lds_barrier();
+                if (wave_on) {
+                    const int pw = wv ^ NHG;
+                    sacc[0] += xch[(pw * 2 + 0) * 64 + lane];
+                    sacc[1] += xch[(pw * 2 + 1) * 64 + lane];
+                }
+            }
+            if (wave_on) {
                 float sv[8];
                 float mx = -INFINITY;
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
                     const int rl = (q >> 2) * 16 + 4 * g + (q & 3);
-                    sv[q] = rt[rl] ? sacc[q >> 2][q & 3] * a.scale : -INFINITY;
+                    sv[q] = (vm >> rl) & 1u ? sacc[q >> 2][q & 3] * scale2 : -INFINITY;
                     mx = fmaxf(mx, sv[q]);
                 }
                 mx = fmaxf(mx, __shfl_xor(mx, 16));
                 mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float m_new = fmaxf(m_run, mx);
-                const float alpha = m_new == -INFINITY ? 1.f : expf(m_run - m_new);
-                float p[8], psum = 0.f;
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    p[q] = sv[q] == -INFINITY ? 0.f : expf(sv[q] - m_new);
-                    psum += p[q];
-                }
-                l_run = l_run * alpha + psum;
-                m_run = m_new;
-                if (__ballot(alpha != 1.f)) {
+                // move the reference only when the maximum outgrows it by 2^8
+                if (mx > m_ref + kLazyRescale) {
+                    const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - mx);
+                    l_run *= alpha;
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) o[nb] *= alpha;
+                    m_ref = mx;
+                }
+                float p[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    p[q] = sv[q] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[q] - m_ref);
+                    l_run += p[q];
                 }
                 if constexpr (sizeof(T) == 2) {
                     bf16x8 hi, lo;
 #pragma unroll
                     for (int q = 0; q < 8; ++q) {
-                        const bf16_t h = f32_to_bf16(p[q]);
-                        hi[q] = __builtin_bit_cast(__bf16, h);
-                        lo[q] = __builtin_bit_cast(__bf16, f32_to_bf16(p[q] - bf16_to_f32(h)));
+                        const __bf16 h = (__bf16)p[q];
+                        hi[q] = h;
+                        lo[q] = (__bf16)(p[q] - (float)h);
                     }
                     // lane (g, c) addresses rows 4g + c/4 (and +16), columns nb*16 + 4*(c%4) .. +3;
                     // the transposing read hands lane c the column nb*16 + c of rows 4g..4g+3
-                    const int r1 = 4 * g + (c >> 2), r2 = r1 + 16;
-                    const int cb = 8 * (c & 3);
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
-                        const int byte = nb * 32 + cb;
                         const v4s v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) v4s *)(buf + tile_off<CPR>(r1, byte)));
+                            (__attribute__((address_space(3))) v4s *)(buf + v_off1 + nb * 32));
                         const v4s v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) v4s *)(buf + tile_off<CPR>(r2, byte)));
+                            (__attribute__((address_space(3))) v4s *)(buf + v_off2 + nb * 32));
                         const bf16x8 va = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, v1),
                                                                   __builtin_bit_cast(bf16x4_t, v2), 0, 1, 2, 3, 4,
                                                                   5, 6, 7);
@@ -260,7 +279,7 @@ __global__ __launch_bounds__(256) void k_mqa(const MqaArgs a) {
 #pragma unroll
                         for (int q = 0; q < 8; ++q) {
                             const int r = (q >> 2) * 16 + 4 * g + (q & 3);
-                            const float v = *(const float *)(buf + tile_off<CPR>(r, (nb * 16 + c) * 4));
+                            const float v = *(const float *)(buf + r * S::RS + cb + (nb * 16 + c) * 4);
                             o[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, p[q], o[nb], 0, 0, 0);
                         }
                 }
@@ -276,24 +295,24 @@ __global__ __launch_bounds__(256) void k_mqa(const MqaArgs a) {
     if (head >= a.H) return;
     if (a.n_splits == 1) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        float *orow = a.out + (row * a.H + head) * (int64_t)D + 4 * g;
+        float *orow = a.out + (row * a.H + head) * (int64_t)D + dcol0 + 4 * g;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) *(floatx4 *)(orow + nb * 16) = o[nb] * inv;
-        if (a.lse && g == 0) a.lse[row * a.H + head] = l > 0.f ? m_run + logf(l) : -INFINITY;
+        if (a.lse && g == 0 && dh == 0) a.lse[row * a.H + head] = l > 0.f ? (m_ref + __log2f(l)) * kLn2 : -INFINITY;
     } else {
         const int64_t slot = (row * a.n_splits + split) * a.H + head;
-        float *po = a.part_o + slot * D + 4 * g;
+        float *po = a.part_o + slot * D + dcol0 + 4 * g;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) *(floatx4 *)(po + nb * 16) = o[nb];
-        if (g == 0) {
-            a.part_ml[slot * 2 + 0] = m_run;
+        if (g == 0 && dh == 0) {
+            a.part_ml[slot * 2 + 0] = m_ref;  // base 2
             a.part_ml[slot * 2 + 1] = l;
         }
     }
 }
 
 // Merge the split-K partials of one (query, head): a 4-wide column slice
-// per thread.  Empty splits carry l = 0 and are skipped.
+// per thread.  Maxima are base-2; empty splits carry l = 0 and are skipped.
 __global__ __launch_bounds__(128) void k_combine(int H, int D, int n_splits, const float *__restrict__ part_o,
                                                  const float *__restrict__ part_ml, float *__restrict__ out,
                                                  float *__restrict__ lse) {
@@ -312,17 +331,17 @@ __global__ __launch_bounds__(128) void k_combine(int H, int D, int n_splits, con
         const int64_t slot = (row * n_splits + s) * H + h;
         const float ls = part_ml[slot * 2 + 1];
         if (ls > 0.f) {
-            const float wgt = expf(part_ml[slot * 2] - M);
+            const float wgt = __builtin_amdgcn_exp2f(part_ml[slot * 2] - M);
             L += ls * wgt;
             if (x < D) acc += wgt * *(const floatx4 *)(part_o + slot * D + x);
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     if (x < D) *(floatx4 *)(out + rh * D + x) = acc * inv;
-    if (lse && threadIdx.x == 0) lse[rh] = L > 0.f ? M + logf(L) : -INFINITY;
+    if (lse && threadIdx.x == 0) lse[rh] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
 }
 
-int mqa_choose_splits(int64_t rows, int64_t n_rows_max, int *tiles_per_split) {
+int mqa_choose_splits(int64_t rows, int64_t n_rows_max, int d, int *tiles_per_split) {
     int64_t tiles = (n_rows_max + 31) / 32;
     if (tiles < 1) tiles = 1;
     int64_t s = (kMqaTargetBlocks + rows - 1) / rows;
@@ -330,7 +349,7 @@ int mqa_choose_splits(int64_t rows, int64_t n_rows_max, int *tiles_per_split) {
     if (s < 1) s = 1;
     if (s > tiles) s = tiles;
     int64_t tps = (tiles + s - 1) / s;
-    if (tps > kMqaMaxTilesPerSplit) tps = kMqaMaxTilesPerSplit;  // bounds the LDS row table
+    if (tps > mqa_max_tiles_per_split(d)) tps = mqa_max_tiles_per_split(d);  // bounds the LDS row table
     s = (tiles + tps - 1) / tps;
     *tiles_per_split = (int)tps;
     return (int)s;
@@ -345,7 +364,7 @@ static hipError_t launch_mqa_t(const MqaArgs &a, int64_t rows, hipStream_t st) {
     if (attr != hipSuccess) return attr;
     const size_t lds = S::lds_bytes(a.tiles_per_split);
     if (lds > 160 * 1024) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_mqa<T, D>), dim3((unsigned)(rows * a.n_splits)), dim3(256), lds, st, a);
+    hipLaunchKernelGGL((k_mqa<T, D>), dim3((unsigned)(rows * a.n_splits)), dim3(kMqaThreads), lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_splits == 1) return e;
     hipLaunchKernelGGL(k_combine, dim3((unsigned)(rows * a.H)), dim3(128), 0, st, a.H, D, a.n_splits, a.part_o,
