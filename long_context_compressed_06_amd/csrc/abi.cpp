@@ -150,7 +150,8 @@ int csa_index_topk(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k,
     hipStream_t st = (hipStream_t)stream;
     if (N > 0) {
         // the first radix digit of the selection is counted by the indexer
-        if (int s = hip_status(csa::launch_fill_u32(scratch, rows * csa::kTopkBins, 0u, st), "histogram clear"))
+        if (int s = hip_status(csa::launch_fill_u32(scratch, (int64_t)csa::topk_clear_words(rows, N), 0u, st),
+                               "histogram clear"))
             return s;
         if (int s = hip_status(csa::launch_index_scores(dt, B, Tq, N, H_I, d_I, m, q_pos0, q_idx, w_idx, k_idx,
                                                          k_bstride, scores, scratch, st),

@@ -14,10 +14,10 @@ constexpr int kTopkLdsKeys = 32768;
 // counted per query by the indexer epilogue
 constexpr int kTopkBinBits = 11;
 constexpr int kTopkBins = 1 << kTopkBinBits;
-// decode (few queries) top-k: scores per filter workgroup, candidates the
-// final workgroup keeps in LDS, and the largest row it accepts
+// decode (few queries) top-k: scores per filter workgroup, (index, key)
+// pairs the final workgroup gathers into LDS, and the longest row accepted
 constexpr int kTopkFilterChunk = 4096;
-constexpr int kTopkFinalCand = 12288;
+constexpr int kTopkFinalItems = 16384;
 constexpr int64_t kTopkMaxEntries = (int64_t)kTopkFilterChunk * 1023;
 
 struct TopkPlan {
@@ -25,8 +25,10 @@ struct TopkPlan {
     int64_t nblk;    // filter workgroups per query
 };
 TopkPlan topk_plan(int64_t rows, int64_t N);
-// workspace layout after the score rows: histogram, filter segments, counts
+// top-k scratch after the score rows; its first topk_clear_words(rows, N)
+// 32-bit words must be zero when the indexer starts (histograms, counters)
 size_t topk_scratch_bytes(int64_t rows, int64_t N);
+size_t topk_clear_words(int64_t rows, int64_t N);
 
 hipError_t launch_compress(int dt, int B, int G, int m, int d, const void *raw, int64_t raw_bs,
                            const float *logits, int64_t log_bs, void *out, int64_t out_bs, hipStream_t st);

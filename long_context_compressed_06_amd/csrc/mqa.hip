@@ -16,7 +16,8 @@
 // (global_load_lds_dwordx4), STAGES tiles in flight, so no register staging
 // and no dependent global load sits in the loop.  One DMA instruction moves
 // up to 1 KiB of one row; rows sit 16 bytes apart beyond their length in LDS,
-// so every LDS offset of the loop is a compile-time immediate.  Per wave and
+// in a permuted order (row_slot) that keeps both read patterns free of bank
+// conflicts, and every LDS offset of the loop is a compile-time immediate.  Per wave and
 // tile:
 //   S^T[32 rows x 16 heads] = K . Q^T over the wave's half of d (MFMA, K rows
 //       read with ds_read_b128, Q^T in registers); the two halves are summed
@@ -87,6 +88,41 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 
+// Eight transposing LDS reads (lane (g, c): rows of slot base and base+16
+// rows, columns nb*16 + 4*(c%4) .. +3 for nb = NB0 .. NB0+3) at immediate
+// offsets from one address register, waited for inside the same statement.
+template <int RS, int NB0>
+__device__ __forceinline__ void tr_read4(uint32_t addr, bf16x8 (&va)[4]) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    u32x2 r0, r1, r2, r3, r4, r5, r6, r7;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%9\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:%10\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:%11\n\t"
+        "ds_read_b64_tr_b16 %3, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %5, %8 offset:%14\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:%15\n\t"
+        "ds_read_b64_tr_b16 %7, %8 offset:%16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(r0), "=v"(r1), "=v"(r2), "=v"(r3), "=v"(r4), "=v"(r5), "=v"(r6), "=v"(r7)
+        : "v"(addr), "n"(NB0 * 32), "n"(NB0 * 32 + 16 * RS), "n"(NB0 * 32 + 32), "n"(NB0 * 32 + 32 + 16 * RS),
+          "n"(NB0 * 32 + 64), "n"(NB0 * 32 + 64 + 16 * RS), "n"(NB0 * 32 + 96), "n"(NB0 * 32 + 96 + 16 * RS)
+        : "memory");
+    const u32x2 lo_[4] = {r0, r2, r4, r6}, hi_[4] = {r1, r3, r5, r7};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const uint32_t w[4] = {lo_[u].x, lo_[u].y, hi_[u].x, hi_[u].y};
+        va[u] = __builtin_bit_cast(bf16x8, *(const u32x4 *)w);
+    }
+}
+
+// LDS slot of tile row r.  With a row stride of 4 banks (mod 64), rows r and
+// 16+r read together by the logits product need distinct slots mod 16, and
+// the four rows 4g..4g+3 of a transposing read need slots two apart so that
+// their 8-bank windows do not overlap: even slots for rows 0-7, odd for 8-15.
+__device__ __forceinline__ int row_slot(int r) { return (r & 16) | ((r & 7) << 1) | ((r >> 3) & 1); }
+
 template <typename T, int D>
 __global__ __launch_bounds__(kMqaThreads) void k_mqa(const MqaArgs a) {
     using E = Elem<T>;
@@ -154,6 +190,10 @@ __global__ __launch_bounds__(kMqaThreads) void k_mqa(const MqaArgs a) {
     // any valid row of the split stands in for masked rows (their weight is 0)
     const T *dummy = nullptr;
     for (int i = 0; i < nr && !dummy; ++i) dummy = rtab[i];
+    __syncthreads();
+    for (int i = tid; i < nr; i += kMqaThreads)
+        if (!rtab[i]) rtab[i] = dummy;
+    __syncthreads();
 
     floatx4 o[NB];
 #pragma unroll
@@ -167,11 +207,11 @@ __global__ __launch_bounds__(kMqaThreads) void k_mqa(const MqaArgs a) {
 #pragma unroll
             for (int u = 0; u < S::TR / S::NW; ++u) {
                 const int r = wv * (S::TR / S::NW) + u;
-                const T *src = rtab[lt * S::TR + r];
-                const unsigned char *gp = (const unsigned char *)(src ? src : dummy) + lane * 16;
+                const unsigned char *gp = (const unsigned char *)rtab[lt * S::TR + r] + lane * 16;
 #pragma unroll
                 for (int ip = 0; ip < S::IPR; ++ip) {
-                    if (S::LPI == 64 || lane < S::LPI) dma16(buf + r * S::RS + ip * 1024, gp + ip * 1024);
+                    if (S::LPI == 64 || lane < S::LPI)
+                        dma16(buf + row_slot(r) * S::RS + ip * 1024, gp + ip * 1024);
                 }
             }
         };
@@ -181,34 +221,35 @@ __global__ __launch_bounds__(kMqaThreads) void k_mqa(const MqaArgs a) {
 
         // per-lane LDS byte offsets (the rest are immediates)
         const int cb = dcol0 * (int)sizeof(T);
-        const int k_off = c * S::RS + cb + g * E::KPL * (int)sizeof(T);     // logits product, rows c (+16)
-        const int v_off1 = (4 * g + (c >> 2)) * S::RS + cb + 8 * (c & 3);   // transposing reads, rows 4g..
-        const int v_off2 = v_off1 + 16 * S::RS;                             // ... and 16+4g..
+        const int k_off = row_slot(c) * S::RS + cb + g * E::KPL * (int)sizeof(T);  // logits, rows c (+16)
+        const int v_off1 = row_slot(4 * g + (c >> 2)) * S::RS + cb + 8 * (c & 3);  // transposing, rows 4g..
 
         for (int lt = 0; lt < ntiles; ++lt) {
-            // keep STAGES-1 younger tiles in flight; wait until this tile's own loads landed
-            if (lt + S::STAGES - 1 < ntiles) issue(lt + S::STAGES - 1);
-            const int younger = min(ntiles - 1 - lt, S::STAGES - 1);
-            if (S::STAGES == 3 && younger == 2)
-                wait_vm_barrier<2 * S::LPW>();
-            else if (younger == 1)
+            // wait until this tile's loads landed (STAGES-2 younger tiles may
+            // still fly); the barrier also proves every wave is done with the
+            // previous tile, whose stage the next DMA reuses
+            const int younger = min(ntiles - 1 - lt, S::STAGES - 2);
+            if (S::STAGES == 3 && younger == 1)
                 wait_vm_barrier<S::LPW>();
             else
                 wait_vm_barrier<0>();
+            if (lt + S::STAGES - 1 < ntiles) issue(lt + S::STAGES - 1);
             const unsigned char *buf = tiles + (lt % S::STAGES) * S::TILEB;
             const uint32_t vm = vmask[lt];
             floatx4 sacc[2];
             if (wave_on) {
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb) {
+                    // all K fragments of the row block first, so the reads overlap
                     sacc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
                     const unsigned char *kr = buf + k_off + rb * 16 * S::RS;
+                    typename E::frag kf[KS];
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) {
-                        const typename E::frag kf =
-                            *(const typename E::frag *)(kr + ks * E::KSTEP * (int)sizeof(T));
-                        sacc[rb] = E::mma(kf, qf[ks], sacc[rb]);
-                    }
+                    for (int ks = 0; ks < KS; ++ks)
+                        kf[ks] = *(const typename E::frag *)(kr + ks * E::KSTEP * (int)sizeof(T));
+                    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of their MFMAs
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) sacc[rb] = E::mma(kf[ks], qf[ks], sacc[rb]);
                 }
             }
             if constexpr (S::SPLITD == 2) {
@@ -225,16 +266,23 @@ __global__ __launch_bounds__(kMqaThreads) void k_mqa(const MqaArgs a) {
                 }
             }
             if (wave_on) {
+                // raw logits (masked rows -inf); scale2 > 0 keeps the order
                 float sv[8];
-                float mx = -INFINITY;
+                if (vm == 0xffffffffu) {
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const int rl = (q >> 2) * 16 + 4 * g + (q & 3);
-                    sv[q] = (vm >> rl) & 1u ? sacc[q >> 2][q & 3] * scale2 : -INFINITY;
-                    mx = fmaxf(mx, sv[q]);
+                    for (int q = 0; q < 8; ++q) sv[q] = sacc[q >> 2][q & 3];
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const int rl = (q >> 2) * 16 + 4 * g + (q & 3);
+                        sv[q] = (vm >> rl) & 1u ? sacc[q >> 2][q & 3] : -INFINITY;
+                    }
                 }
+                float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                                 fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
                 mx = fmaxf(mx, __shfl_xor(mx, 16));
                 mx = fmaxf(mx, __shfl_xor(mx, 32));
+                mx *= scale2;  // base-2 logit maximum of this tile
                 // move the reference only when the maximum outgrows it by 2^8
                 if (mx > m_ref + kLazyRescale) {
                     const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - mx);
@@ -243,10 +291,12 @@ __global__ __launch_bounds__(kMqaThreads) void k_mqa(const MqaArgs a) {
                     for (int nb = 0; nb < NB; ++nb) o[nb] *= alpha;
                     m_ref = mx;
                 }
+                // m_ref stays -inf only while no row has been valid: nothing to add
+                if (m_ref == -INFINITY) continue;
                 float p[8];
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
-                    p[q] = sv[q] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[q] - m_ref);
+                    p[q] = __builtin_amdgcn_exp2f(fmaf(sv[q], scale2, -m_ref));  // exp2(-inf) = 0
                     l_run += p[q];
                 }
                 if constexpr (sizeof(T) == 2) {
@@ -259,17 +309,38 @@ __global__ __launch_bounds__(kMqaThreads) void k_mqa(const MqaArgs a) {
                     }
                     // lane (g, c) addresses rows 4g + c/4 (and +16), columns nb*16 + 4*(c%4) .. +3;
                     // the transposing read hands lane c the column nb*16 + c of rows 4g..4g+3
+                    if constexpr (NB % 4 == 0) {
+                        // batches of four column blocks: eight transposing reads, then eight MFMAs
+                        const uint32_t vaddr = (uint32_t)(uintptr_t)(buf + v_off1);
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) {
-                        const v4s v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) v4s *)(buf + v_off1 + nb * 32));
-                        const v4s v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) v4s *)(buf + v_off2 + nb * 32));
-                        const bf16x8 va = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, v1),
-                                                                  __builtin_bit_cast(bf16x4_t, v2), 0, 1, 2, 3, 4,
-                                                                  5, 6, 7);
-                        o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, hi, o[nb], 0, 0, 0);
-                        o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, lo, o[nb], 0, 0, 0);
+                        for (int nb0 = 0; nb0 < NB; nb0 += 4) {
+                            bf16x8 va[4];
+                            switch (nb0) {  // the offsets are immediates
+#define CSA_TR4(K) case K: tr_read4<S::RS, K>(vaddr, va); break;
+                                CSA_TR4(0) CSA_TR4(4) CSA_TR4(8) CSA_TR4(12) CSA_TR4(16) CSA_TR4(20) CSA_TR4(24)
+                                CSA_TR4(28)
+#undef CSA_TR4
+                            }
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) {
+                                o[nb0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u], hi, o[nb0 + u], 0, 0, 0);
+                                o[nb0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u], lo, o[nb0 + u], 0, 0, 0);
+                            }
+                        }
+                    } else {
+                        // narrow rows: the same reads through the builtin
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) {
+                            const v4s v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (__attribute__((address_space(3))) v4s *)(buf + v_off1 + nb * 32));
+                            const v4s v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (__attribute__((address_space(3))) v4s *)(buf + v_off1 + 16 * S::RS + nb * 32));
+                            const bf16x8 va = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, v1),
+                                                                      __builtin_bit_cast(bf16x4_t, v2), 0, 1, 2, 3,
+                                                                      4, 5, 6, 7);
+                            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, hi, o[nb], 0, 0, 0);
+                            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, lo, o[nb], 0, 0, 0);
+                        }
                     }
                 } else {
                     // fp32: 16x16x4 steps, one row per lane group: lane (g, c) gives
@@ -279,12 +350,11 @@ __global__ __launch_bounds__(kMqaThreads) void k_mqa(const MqaArgs a) {
 #pragma unroll
                         for (int q = 0; q < 8; ++q) {
                             const int r = (q >> 2) * 16 + 4 * g + (q & 3);
-                            const float v = *(const float *)(buf + r * S::RS + cb + (nb * 16 + c) * 4);
+                            const float v = *(const float *)(buf + row_slot(r) * S::RS + cb + (nb * 16 + c) * 4);
                             o[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, p[q], o[nb], 0, 0, 0);
                         }
                 }
             }
-            lds_barrier();
         }
     }
 

@@ -12,12 +12,13 @@
 // 10 bits, LDS histograms) and, for keys that are fully equal, by index.
 //
 // Few queries (decode): one query's row is cut into chunks of
-// kTopkFilterChunk scores; a filter workgroup per chunk writes the kept and
-// the candidate indices of its chunk, in index order, to a segment of the
-// workspace, and one final workgroup per query selects among the candidates
-// in LDS and merges both sorted lists.  Many queries (prefill): one
-// workgroup per query with the row staged in LDS.  Either way the kept set
-// leaves in ascending index order through block scans, never a sort.
+// kTopkFilterChunk scores; a workgroup per chunk writes the (index, key) pairs
+// of its chunk whose digit is >= D, in index order, to a segment of the
+// workspace; then one workgroup per query gathers all segments into LDS,
+// resolves the candidates and writes the kept set.  Many queries (prefill):
+// one workgroup per query with the row staged in LDS.  Either way the kept
+// set leaves in ascending index order through one scan over wavefront
+// totals and in-wave ballots, never a sort.
 #include "kernels.h"
 
 namespace csa {
@@ -108,36 +109,53 @@ __device__ void refine(KeyAt key_at, int64_t n, uint32_t &prefix, uint32_t &mask
     }
 }
 
-// Walk n items in index order; keep those above the prefix and the first
-// `rem` equal to it; emit(pos, i) for the kept ones, pos ascending.
-template <int NT, class KeyAt, class Emit>
-__device__ void ordered_keep(KeyAt key_at, int64_t n, uint32_t prefix, uint32_t mask, int rem, int *sh, Emit emit) {
-    int out_base = 0, eq_base = 0;
-    for (int64_t c0 = 0; c0 < n; c0 += NT) {
-        const int64_t i = c0 + threadIdx.x;
-        int gt = 0, eq = 0;
-        if (i < n) {
-            const uint32_t km = key_at(i) & mask;
-            gt = km > prefix;
-            eq = km == prefix;
-        }
-        int eq_tot, sel_tot;
-        const int eq_before = eq_base + block_excl_scan<NT>(eq, sh, &eq_tot);
-        const int sel = gt || (eq && eq_before < rem);
-        const int pos = out_base + block_excl_scan<NT>(sel, sh, &sel_tot);
-        if (sel) emit(pos, i);
-        eq_base += eq_tot;
-        out_base += sel_tot;
-    }
+// popcount of the bits of m below this lane
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-__device__ __forceinline__ int lower_bound(const int32_t *a, int n, int32_t x) {
-    int lo = 0, hi = n;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (a[mid] < x) lo = mid + 1; else hi = mid;
+// Walk n items in index order; keep those above the prefix and the first
+// `rem` equal to it; emit(pos, i) for the kept ones.  Wavefront w owns one
+// contiguous run of the items: a first pass counts its kept and tied items,
+// one exchange of the per-wave totals gives each run its starting position,
+// and a second pass places the items with ballots.  sh: 2*NT/64 ints.
+template <int NT, class KeyAt, class Emit>
+__device__ void ordered_keep(KeyAt key_at, int64_t n, uint32_t prefix, uint32_t mask, int rem, int *sh, Emit emit) {
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t per = ((n + NW - 1) / NW + 63) / 64 * 64;
+    const int64_t s0 = min(n, (int64_t)wv * per), s1 = min(n, s0 + per);
+    int gt = 0, eq = 0;
+    for (int64_t c = s0; c < s1; c += 64) {
+        const int64_t i = c + lane;
+        const uint32_t km = i < s1 ? key_at(i) & mask : 0u;
+        gt += __popcll(__ballot(i < s1 && km > prefix));
+        eq += __popcll(__ballot(i < s1 && km == prefix));
     }
-    return lo;
+    if (lane == 0) {
+        sh[wv] = gt;
+        sh[NW + wv] = eq;
+    }
+    __syncthreads();
+    int gt_b = 0, eq_b = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        gt_b += i < wv ? sh[i] : 0;
+        eq_b += i < wv ? sh[NW + i] : 0;
+    }
+    __syncthreads();
+    int pos = gt_b + min(eq_b, rem);
+    for (int64_t c = s0; c < s1; c += 64) {
+        const int64_t i = c + lane;
+        const uint32_t km = i < s1 ? key_at(i) & mask : 0u;
+        const bool e = i < s1 && km == prefix;
+        const uint64_t em = __ballot(e);
+        const bool sel = (i < s1 && km > prefix) || (e && eq_b + lanes_below(em) < rem);
+        const uint64_t sm = __ballot(sel);
+        if (sel) emit(pos + lanes_below(sm), i);
+        pos += __popcll(sm);
+        eq_b += __popcll(em);
+    }
 }
 
 constexpr int kNT = 1024;   // threads of the per-query workgroups
@@ -162,7 +180,7 @@ __global__ __launch_bounds__(kNT) void k_topk_rows(int Tq, int N, int m, int k, 
                                                    const uint32_t *__restrict__ ghist, int32_t *__restrict__ out) {
     extern __shared__ uint32_t lds_keys[];
     __shared__ uint32_t hist[2048];
-    __shared__ int sh[kNT / 64];
+    __shared__ int sh[2 * kNT / 64];
     __shared__ Digit shd;
     const int64_t row = blockIdx.x;
     const int64_t nv = n_visible(q_pos0 + row % Tq, m, N);
@@ -183,9 +201,22 @@ __global__ __launch_bounds__(kNT) void k_topk_rows(int Tq, int N, int m, int k, 
 }
 
 // ----------------------------------------------------- decode: filter + final
+// k_topk_filter: kFT threads per workgroup, nblk workgroups per query.  Each
+// workgroup writes the (index, key) pairs of its chunk whose first digit is at
+// least D (kept ones and candidates alike) to the chunk's segment, in index
+// order, and their number to counts.
+// k_topk_final: one workgroup per query gathers the segments into LDS (the
+// pairs arrive in index order), resolves the candidates and writes the kept
+// indices.  (A kernel boundary separates the two: on this multi-die GPU a
+// device-scope fence inside one kernel costs more.)
+struct IdxKey {
+    int32_t j;
+    uint32_t key;
+};
+
 __global__ __launch_bounds__(kFT) void k_topk_filter(int Tq, int N, int m, int k, int64_t q_pos0, int nblk,
                                                      const float *__restrict__ scores,
-                                                     const uint32_t *__restrict__ ghist, int32_t *__restrict__ seg,
+                                                     const uint32_t *__restrict__ ghist, IdxKey *__restrict__ seg,
                                                      int32_t *__restrict__ counts) {
     __shared__ int sh[kFT / 64];
     __shared__ Digit shd;
@@ -196,81 +227,49 @@ __global__ __launch_bounds__(kFT) void k_topk_filter(int Tq, int N, int m, int k
     const Digit d = find_digit<kFT>(ghist + row * kTopkBins, kTopkBins, k, sh, &shd);
     const float *srow = scores + row * (int64_t)N;
     const int64_t j0 = (int64_t)blk * kTopkFilterChunk + threadIdx.x * kFPT;
-    uint32_t sure_bits = 0, cand_bits = 0;
+    uint32_t keys[kFPT];
+    uint32_t bits = 0;
 #pragma unroll
     for (int u = 0; u < kFPT; ++u) {
         const int64_t j = j0 + u;
-        if (j < nv) {
-            const uint32_t dg = order_key(srow[j]) >> (32 - kTopkBinBits);
-            sure_bits |= (uint32_t)(dg > d.digit) << u;
-            cand_bits |= (uint32_t)(dg == d.digit) << u;
-        }
+        keys[u] = j < nv ? order_key(srow[j]) : 0u;
+        bits |= (uint32_t)(j < nv && (keys[u] >> (32 - kTopkBinBits)) >= d.digit) << u;
     }
-    // one scan of both counts: kept in the high half, candidates in the low half
     int total;
-    const int pre = block_excl_scan<kFT>((int)((__popc(sure_bits) << 16) | __popc(cand_bits)), sh, &total);
-    int ps = pre >> 16, pc = pre & 0xffff;
-    int32_t *sg = seg + (row * nblk + blk) * (int64_t)kTopkFilterChunk;
+    int pos = block_excl_scan<kFT>(__popc(bits), sh, &total);
+    IdxKey *sg = seg + (row * nblk + blk) * (int64_t)kTopkFilterChunk;
 #pragma unroll
-    for (int u = 0; u < kFPT; ++u) {
-        if ((sure_bits >> u) & 1) sg[ps++] = (int32_t)(j0 + u);
-        if ((cand_bits >> u) & 1) sg[kTopkFilterChunk - 1 - pc++] = (int32_t)(j0 + u);
-    }
-    if (threadIdx.x == 0) {
-        counts[(row * nblk + blk) * 2 + 0] = total >> 16;
-        counts[(row * nblk + blk) * 2 + 1] = total & 0xffff;
-    }
+    for (int u = 0; u < kFPT; ++u)
+        if ((bits >> u) & 1) sg[pos++] = IdxKey{(int32_t)(j0 + u), keys[u]};
+    if (threadIdx.x == 0) counts[row * nblk + blk] = total;
 }
 
 __global__ __launch_bounds__(kNT) void k_topk_final(int Tq, int N, int m, int k, int64_t q_pos0, int nblk,
                                                     const float *__restrict__ scores,
                                                     const uint32_t *__restrict__ ghist,
-                                                    const int32_t *__restrict__ seg,
+                                                    const IdxKey *__restrict__ seg,
                                                     const int32_t *__restrict__ counts, int32_t *__restrict__ out) {
-    extern __shared__ int32_t dyn[];
+    extern __shared__ IdxKey items[];  // [kTopkFinalItems]
     __shared__ uint32_t hist[2048];
-    __shared__ int sh[kNT / 64];
+    __shared__ int pre[kNT + 1];       // segment starts (nblk <= 1023)
+    __shared__ int sh[2 * kNT / 64];
     __shared__ Digit shd;
-    __shared__ int tot_s, tot_c;
     const int64_t row = blockIdx.x;
     const int64_t nv = n_visible(q_pos0 + row % Tq, m, N);
     int32_t *orow = out + row * k;
     if (trivial_row(nv, k, orow)) return;
-    const float *srow = scores + row * (int64_t)N;
+    // the segment sizes are fetched alongside the histogram
+    const int cnt = (int)threadIdx.x < nblk ? counts[row * nblk + threadIdx.x] : 0;
     const Digit d = find_digit<kNT>(ghist + row * kTopkBins, kTopkBins, k, sh, &shd);
-    const uint32_t prefix0 = d.digit << (32 - kTopkBinBits), mask0 = ~0u << (32 - kTopkBinBits);
-    const int rem0 = k - d.above;  // candidates to keep
-
-    // prefix sums of the per-chunk kept / candidate counts (nblk <= kNT)
-    int32_t *ps = dyn;                 // [nblk + 1]
-    int32_t *pc = ps + (nblk + 1);     // [nblk + 1]
-    int32_t *sidx = pc + (nblk + 1);   // [k]  kept indices
-    int32_t *sel = sidx + k;           // [k]  chosen candidates
-    int32_t *cidx = sel + k;           // [kTopkFinalCand]
-    uint32_t *ckey = (uint32_t *)(cidx + kTopkFinalCand);
-    {
-        const int i = threadIdx.x;
-        const int cs = i < nblk ? counts[(row * nblk + i) * 2 + 0] : 0;
-        const int cc = i < nblk ? counts[(row * nblk + i) * 2 + 1] : 0;
-        int ts, tc;
-        const int xs = block_excl_scan<kNT>(cs, sh, &ts);
-        const int xc = block_excl_scan<kNT>(cc, sh, &tc);
-        if (i <= nblk) {
-            ps[i] = xs;
-            pc[i] = xc;
-        }
-        if (i == 0) {
-            tot_s = ts;
-            tot_c = tc;
-        }
-        __syncthreads();
-    }
-    const int S = tot_s, C = tot_c;
-    const int32_t *segr = seg + row * nblk * (int64_t)kTopkFilterChunk;
-    if (C > kTopkFinalCand || S != d.above) {
-        // too many candidates for LDS: exact select straight over the row
-        uint32_t prefix = prefix0, mask = mask0;
-        int rem = rem0;
+    int M;
+    const int x = block_excl_scan<kNT>(cnt, sh, &M);
+    if ((int)threadIdx.x <= nblk) pre[threadIdx.x] = (int)threadIdx.x < nblk ? x : M;
+    __syncthreads();
+    uint32_t prefix = d.digit << (32 - kTopkBinBits), mask = ~0u << (32 - kTopkBinBits);
+    int rem = k - d.above;  // keys of digit D to keep
+    if (M > kTopkFinalItems || M != d.above + d.at) {
+        // more pairs than LDS holds: exact select straight over the row
+        const float *srow = scores + row * (int64_t)N;
         auto key_at = [&](int64_t j) -> uint32_t { return order_key(srow[j]); };
         if (d.at != rem) refine<kNT>(key_at, nv, prefix, mask, rem, hist, sh, &shd);
         ordered_keep<kNT>(key_at, nv, prefix, mask, rem, sh, [&](int pos, int64_t j) {
@@ -278,35 +277,32 @@ __global__ __launch_bounds__(kNT) void k_topk_final(int Tq, int N, int m, int k,
         });
         return;
     }
-    // candidates (index order) and kept indices (index order) into LDS
-    for (int i = threadIdx.x; i < C; i += kNT) {
-        const int b = lower_bound(pc, nblk + 1, i + 1) - 1;  // last chunk with pc[b] <= i
-        const int32_t j = segr[b * (int64_t)kTopkFilterChunk + kTopkFilterChunk - 1 - (i - pc[b])];
-        cidx[i] = j;
-        ckey[i] = order_key(srow[j]);
-    }
-    for (int i = threadIdx.x; i < S; i += kNT) {
-        const int b = lower_bound(ps, nblk + 1, i + 1) - 1;
-        sidx[i] = segr[b * (int64_t)kTopkFilterChunk + (i - ps[b])];
+    // gather: batches of four pairs per thread, all loads in flight together
+    const IdxKey *segr = seg + row * nblk * (int64_t)kTopkFilterChunk;
+    for (int i0 = 0; i0 < M; i0 += 4 * kNT) {
+        IdxKey v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = min(i0 + u * kNT + (int)threadIdx.x, M - 1);
+            int lo = 0, hi = nblk;  // last segment b with pre[b] <= i
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (pre[mid] <= i) lo = mid; else hi = mid;
+            }
+            v[u] = segr[lo * (int64_t)kTopkFilterChunk + (i - pre[lo])];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u * kNT + (int)threadIdx.x;
+            if (i < M) items[i] = v[u];
+        }
     }
     __syncthreads();
-    uint32_t prefix = prefix0, mask = mask0;
-    int rem = rem0;
-    auto ckey_at = [&](int64_t i) -> uint32_t { return ckey[i]; };
-    if (d.at != rem) refine<kNT>(ckey_at, C, prefix, mask, rem, hist, sh, &shd);
-    ordered_keep<kNT>(ckey_at, C, prefix, mask, rem, sh, [&](int pos, int64_t i) {
-        if (pos < k) sel[pos] = cidx[i];
+    auto ikey_at = [&](int64_t i) -> uint32_t { return items[i].key; };
+    if (d.at != rem) refine<kNT>(ikey_at, M, prefix, mask, rem, hist, sh, &shd);
+    ordered_keep<kNT>(ikey_at, M, prefix, mask, rem, sh, [&](int pos, int64_t i) {
+        if (pos < k) orow[pos] = items[i].j;
     });
-    __syncthreads();
-    // merge the two ascending lists
-    for (int i = threadIdx.x; i < S; i += kNT) {
-        const int pos = i + lower_bound(sel, rem0, sidx[i]);
-        if (pos < k) orow[pos] = sidx[i];
-    }
-    for (int i = threadIdx.x; i < rem0; i += kNT) {
-        const int pos = i + lower_bound(sidx, S, sel[i]);
-        if (pos < k) orow[pos] = sel[i];
-    }
 }
 
 // ------------------------------------------------------------------ host side
@@ -318,10 +314,20 @@ TopkPlan topk_plan(int64_t rows, int64_t N) {
     return p;
 }
 
+// scratch layout: histograms [rows][kTopkBins] u32 (cleared before the
+// indexer), then (filter path) counts [rows][nblk] i32 and segments
+// [rows][nblk][chunk] of (index, key) pairs
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t topk_clear_words(int64_t rows, int64_t N) {
+    (void)N;
+    return (size_t)rows * kTopkBins;
+}
+
 size_t topk_scratch_bytes(int64_t rows, int64_t N) {
     const TopkPlan p = topk_plan(rows, N);
-    size_t bytes = (size_t)rows * kTopkBins * 4;
-    if (p.filter) bytes += (size_t)rows * p.nblk * (kTopkFilterChunk + 2) * 4;
+    size_t bytes = align256(topk_clear_words(rows, N) * 4);
+    if (p.filter) bytes += align256((size_t)rows * p.nblk * 4) + (size_t)rows * p.nblk * kTopkFilterChunk * 8;
     return bytes;
 }
 
@@ -347,17 +353,18 @@ hipError_t launch_topk(int B, int Tq, int N, int m, int k, int64_t q_pos0, const
                            hist, out);
         return hipGetLastError();
     }
-    int32_t *seg = (int32_t *)(hist + rows * kTopkBins);
-    int32_t *counts = seg + rows * p.nblk * kTopkFilterChunk;
+    char *base = (char *)scratch + align256(topk_clear_words(rows, N) * 4);
+    int32_t *counts = (int32_t *)base;
+    IdxKey *seg = (IdxKey *)(base + align256((size_t)rows * p.nblk * 4));
     if (N > 0) {
         hipLaunchKernelGGL(k_topk_filter, dim3((unsigned)(rows * p.nblk)), dim3(kFT), 0, st, Tq, N, m, k, q_pos0,
                            (int)p.nblk, scores, hist, seg, counts);
-        hipError_t e = hipGetLastError();
+        const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const size_t lds = (size_t)(2 * (p.nblk + 1) + 2 * k + 2 * kTopkFinalCand) * 4;
+    const size_t lds = (size_t)kTopkFinalItems * sizeof(IdxKey);
     static const hipError_t attr =
-        hipFuncSetAttribute((const void *)k_topk_final, hipFuncAttributeMaxDynamicSharedMemorySize, 144 * 1024);
+        hipFuncSetAttribute((const void *)k_topk_final, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL(k_topk_final, dim3((unsigned)rows), dim3(kNT), lds, st, Tq, N, m, k, q_pos0, (int)p.nblk,
                        scores, hist, seg, counts, out);
