@@ -100,7 +100,10 @@ int csa_compress(int dt, int B, int G, int m, int d, const void *raw, int64_t ra
                       "compress launch");
 }
 
-static size_t scores_bytes(int64_t rows, int64_t N) { return ((size_t)rows * N * sizeof(float) + 255) / 256 * 256; }
+// the score rows the top-k reads, padded to csa::topk_score_stride(N) floats
+static size_t scores_bytes(int64_t rows, int64_t N) {
+    return ((size_t)rows * csa::topk_score_stride(N) * sizeof(float) + 255) / 256 * 256;
+}
 
 size_t csa_index_topk_workspace_bytes(int B, int Tq, int N, int H_I, int k) {
     (void)H_I;
@@ -132,7 +135,7 @@ int csa_index_topk(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k,
     if (!workspace || workspace_bytes < need)
         return fail(CSA_EWORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
     if (!aligned(workspace, 16)) return fail(CSA_EALIGN, "workspace needs 16-byte alignment");
-    float *scores = scores_out ? scores_out : (float *)workspace;
+    float *scores = (float *)workspace;
     uint32_t *scratch = (uint32_t *)((char *)workspace + scores_bytes(rows, N));
     const size_t es = esize(dt);
     const Span si = span(topk_idx, B, (int64_t)Tq * k, (int64_t)Tq * k, 4);
@@ -154,7 +157,8 @@ int csa_index_topk(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k,
                                "histogram clear"))
             return s;
         if (int s = hip_status(csa::launch_index_scores(dt, B, Tq, N, H_I, d_I, m, q_pos0, q_idx, w_idx, k_idx,
-                                                         k_bstride, scores, scratch, st),
+                                                         k_bstride, scores, csa::topk_score_stride(N), scores_out,
+                                                         scratch, st),
                                "indexer launch"))
             return s;
     }
@@ -181,7 +185,7 @@ int csa_index_scores(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int6
         overlap(ss, span(k_idx, B, k_bstride, (int64_t)N * d_I, es)))
         return fail(CSA_EINVAL, "scores overlaps an input");
     return hip_status(csa::launch_index_scores(dt, B, Tq, N, H_I, d_I, m, q_pos0, q_idx, w_idx, k_idx, k_bstride,
-                                               scores, nullptr, (hipStream_t)stream),
+                                               scores, N, nullptr, nullptr, (hipStream_t)stream),
                       "indexer launch");
 }
 

@@ -26,7 +26,8 @@ __global__ __launch_bounds__(256) void k_index_scores(int Tq, int N, int HI, int
                                                        int chunks_per_row, int tiles_per_chunk,
                                                        const T *__restrict__ qI, const float *__restrict__ w,
                                                        const T *__restrict__ kI, int64_t k_bs,
-                                                       float *__restrict__ scores, uint32_t *__restrict__ hist) {
+                                                       float *__restrict__ scores, int64_t s_stride,
+                                                       float *__restrict__ scores2, uint32_t *__restrict__ hist) {
     using E = Elem<T>;
     constexpr int KS = DI / E::KSTEP;
     constexpr int UNROLL = 4;
@@ -62,13 +63,17 @@ __global__ __launch_bounds__(256) void k_index_scores(int Tq, int N, int HI, int
     }
 
     const T *kb = kI + b * k_bs + g * E::KPL;
-    float *srow = scores + row * (int64_t)N;
+    float *srow = scores + row * s_stride;
+    float *srow2 = scores2 ? scores2 + row * (int64_t)N : nullptr;
     const int64_t j_lo = (int64_t)chunk * tiles_per_chunk * 16;
     const int64_t j_hi = min((int64_t)N, j_lo + (int64_t)tiles_per_chunk * 16);
     constexpr int BATCH = 16 * UNROLL;  // entries per batch of tiles
 
     if (nv == 0) {  // nothing visible: the chunk is all -inf
-        for (int64_t j = j_lo + lane; j < j_hi; j += 64) srow[j] = -INFINITY;
+        for (int64_t j = j_lo + lane; j < j_hi; j += 64) {
+            srow[j] = -INFINITY;
+            if (srow2) srow2[j] = -INFINITY;
+        }
     } else {
     // one batch: UNROLL tiles of 16 index keys, straight from HBM to registers.
     // Loads are unconditional so the compiler can wait for exactly one batch:
@@ -101,7 +106,10 @@ __global__ __launch_bounds__(256) void k_index_scores(int Tq, int N, int HI, int
                 for (int e = 0; e < 4; ++e) s += wgt[mb][e] * fmaxf(acc[mb][e], 0.f);
             s += __shfl_xor(s, 16);
             s += __shfl_xor(s, 32);
-            if (g == 0 && j < j_hi) srow[j] = j < nv ? s : -INFINITY;
+            if (g == 0 && j < j_hi) {
+                srow[j] = j < nv ? s : -INFINITY;
+                if (srow2) srow2[j] = j < nv ? s : -INFINITY;
+            }
             if (hist && g == 0 && j < j_hi && j < nv)
                 atomicAdd(&whist[wv][order_key(s) >> (32 - kTopkBinBits)], 1u);
         }
@@ -128,7 +136,7 @@ __global__ __launch_bounds__(256) void k_index_scores(int Tq, int N, int HI, int
 
 template <typename T, int DI, int MB>
 static hipError_t launch_t(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const void *qI, const float *w,
-                           const void *kI, int64_t k_bs, float *scores, uint32_t *hist, hipStream_t st) {
+                           const void *kI, int64_t k_bs, float *scores, int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
     const int64_t rows = (int64_t)B * Tq;
     const int64_t tiles = (N + 15) / 16;
     // aim for ~2048 wavefronts in flight (8 per CU) when there are few queries
@@ -142,34 +150,43 @@ static hipError_t launch_t(int B, int Tq, int N, int HI, int m, int64_t q_pos0, 
     const int64_t items = rows * chunks;
     const int64_t blocks = (items + 3) / 4;
     hipLaunchKernelGGL((k_index_scores<T, DI, MB>), dim3((unsigned)blocks), dim3(256), 0, st, Tq, N, HI, m, q_pos0,
-                       items, (int)chunks, (int)tpc, (const T *)qI, w, (const T *)kI, k_bs, scores, hist);
+                       items, (int)chunks, (int)tpc, (const T *)qI, w, (const T *)kI, k_bs, scores, s_stride,
+                       scores2, hist);
     return hipGetLastError();
 }
 
 template <typename T, int DI>
 static hipError_t launch_di(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const void *qI, const float *w,
-                            const void *kI, int64_t k_bs, float *scores, uint32_t *hist, hipStream_t st) {
-    if (HI <= 16) return launch_t<T, DI, 1>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, hist, st);
-    if (HI <= 32) return launch_t<T, DI, 2>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, hist, st);
-    return launch_t<T, DI, 4>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, hist, st);
+                            const void *kI, int64_t k_bs, float *scores, int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
+    if (HI <= 16) return launch_t<T, DI, 1>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride, scores2,
+                                                   hist, st);
+    if (HI <= 32) return launch_t<T, DI, 2>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride, scores2,
+                                                   hist, st);
+    return launch_t<T, DI, 4>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride, scores2,
+                                                   hist, st);
 }
 
 template <typename T>
 static hipError_t launch_dt(int B, int Tq, int N, int HI, int dI, int m, int64_t q_pos0, const void *qI,
-                            const float *w, const void *kI, int64_t k_bs, float *scores, uint32_t *hist,
-                            hipStream_t st) {
+                            const float *w, const void *kI, int64_t k_bs, float *scores, int64_t s_stride, float *scores2,
+                            uint32_t *hist, hipStream_t st) {
     switch (dI) {
-        case 32: return launch_di<T, 32>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, hist, st);
-        case 64: return launch_di<T, 64>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, hist, st);
-        default: return launch_di<T, 128>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, hist, st);
+        case 32: return launch_di<T, 32>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride, scores2,
+                                                   hist, st);
+        case 64: return launch_di<T, 64>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride, scores2,
+                                                   hist, st);
+        default: return launch_di<T, 128>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride, scores2,
+                                                   hist, st);
     }
 }
 
 hipError_t launch_index_scores(int dt, int B, int Tq, int N, int HI, int dI, int m, int64_t q_pos0, const void *qI,
-                               const float *w, const void *kI, int64_t k_bs, float *scores, uint32_t *hist,
-                               hipStream_t st) {
-    if (dt == 0) return launch_dt<float>(B, Tq, N, HI, dI, m, q_pos0, qI, w, kI, k_bs, scores, hist, st);
-    return launch_dt<bf16_t>(B, Tq, N, HI, dI, m, q_pos0, qI, w, kI, k_bs, scores, hist, st);
+                               const float *w, const void *kI, int64_t k_bs, float *scores, int64_t s_stride, float *scores2,
+                               uint32_t *hist, hipStream_t st) {
+    if (dt == 0) return launch_dt<float>(B, Tq, N, HI, dI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride,
+                                          scores2, hist, st);
+    return launch_dt<bf16_t>(B, Tq, N, HI, dI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride,
+                                          scores2, hist, st);
 }
 
 }  // namespace csa

@@ -8,8 +8,6 @@
 
 namespace csa {
 
-// longest score row that the top-k kernel stages in LDS (128 KiB of keys)
-constexpr int kTopkLdsKeys = 32768;
 // first radix digit of the top-k select: the top 11 bits of the score key,
 // counted per query by the indexer epilogue
 constexpr int kTopkBinBits = 11;
@@ -18,10 +16,15 @@ constexpr int kTopkBins = 1 << kTopkBinBits;
 // pairs the final workgroup gathers into LDS, and the longest row accepted
 constexpr int kTopkFilterChunk = 4096;
 constexpr int kTopkFinalItems = 16384;
+// with at least kTopkCompactMinRows queries, rows of up to kTopkCompactMax
+// scores are selected in one pass by one workgroup per query (scores held in
+// registers); otherwise the filter + final path spreads each row over CUs
+constexpr int kTopkCompactMax = 65536;
+constexpr int kTopkCompactMinRows = 256;
 constexpr int64_t kTopkMaxEntries = (int64_t)kTopkFilterChunk * 1023;
 
 struct TopkPlan {
-    bool filter;     // multi-workgroup filter + final path (else one workgroup per query)
+    bool filter;     // multi-workgroup filter + final path (else one pass, one workgroup per query)
     int64_t nblk;    // filter workgroups per query
 };
 TopkPlan topk_plan(int64_t rows, int64_t N);
@@ -33,15 +36,21 @@ size_t topk_clear_words(int64_t rows, int64_t N);
 hipError_t launch_compress(int dt, int B, int G, int m, int d, const void *raw, int64_t raw_bs,
                            const float *logits, int64_t log_bs, void *out, int64_t out_bs, hipStream_t st);
 
-// hist: optional [rows, kTopkBins] counts, must be zero on entry
+// scores: [rows][s_stride] (s_stride >= N); scores2: optional second copy,
+// [rows][N]; hist: optional [rows, kTopkBins] counts, must be zero on entry
 hipError_t launch_index_scores(int dt, int B, int Tq, int N, int HI, int dI, int m, int64_t q_pos0, const void *qI,
-                               const float *w, const void *kI, int64_t k_bs, float *scores, uint32_t *hist,
-                               hipStream_t st);
+                               const float *w, const void *kI, int64_t k_bs, float *scores, int64_t s_stride,
+                               float *scores2, uint32_t *hist, hipStream_t st);
+
+// row stride of the score rows the top-k reads: N rounded up to 64 floats, so
+// every row starts 256-byte aligned and 16-byte loads never leave the row
+constexpr int64_t topk_score_stride(int64_t N) { return (N + 63) / 64 * 64; }
 
 hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t st);
 
-// scratch: topk_scratch_bytes(rows, N) bytes; its histogram part must have
-// been filled by launch_index_scores (zeroed before it)
+// scores: [rows][topk_score_stride(N)], 16-byte aligned.  scratch:
+// topk_scratch_bytes(rows, N) bytes; its histogram part must have been filled
+// by launch_index_scores (zeroed before it)
 hipError_t launch_topk(int B, int Tq, int N, int m, int k, int64_t q_pos0, const float *scores, void *scratch,
                        int32_t *out, hipStream_t st);
 

@@ -11,14 +11,16 @@
 // keys with digit D are the candidates, resolved by two more digits (11 and
 // 10 bits, LDS histograms) and, for keys that are fully equal, by index.
 //
-// Few queries (decode): one query's row is cut into chunks of
-// kTopkFilterChunk scores; a workgroup per chunk writes the (index, key) pairs
-// of its chunk whose digit is >= D, in index order, to a segment of the
-// workspace; then one workgroup per query gathers all segments into LDS,
-// resolves the candidates and writes the kept set.  Many queries (prefill):
-// one workgroup per query with the row staged in LDS.  Either way the kept
-// set leaves in ascending index order through one scan over wavefront
-// totals and in-wave ballots, never a sort.
+// Many queries with rows of up to kTopkCompactMax scores (prefill chunks):
+// one workgroup per query holds its row in registers, packs the pairs of digit
+// >= D into LDS and resolves them there.  Few queries (decode) or long rows
+// (1M context): the row is
+// cut into chunks of kTopkFilterChunk scores; a workgroup per chunk writes
+// the (index, key) pairs of its chunk whose digit is >= D, in index order, to
+// a segment of the workspace; then one workgroup per query gathers all
+// segments into LDS and resolves them.  Either way the kept set leaves in
+// ascending index order through one exchange of per-wavefront totals and
+// in-wave ballots, never a sort.
 #include "kernels.h"
 
 namespace csa {
@@ -173,34 +175,120 @@ __device__ __forceinline__ bool trivial_row(int64_t nv, int k, int32_t *orow) {
     return true;
 }
 
-// --------------------------------------------------- one workgroup per query
-template <bool IN_LDS>
-__global__ __launch_bounds__(kNT) void k_topk_rows(int Tq, int N, int m, int k, int64_t q_pos0,
-                                                   const float *__restrict__ scores,
-                                                   const uint32_t *__restrict__ ghist, int32_t *__restrict__ out) {
-    extern __shared__ uint32_t lds_keys[];
-    __shared__ uint32_t hist[2048];
-    __shared__ int sh[2 * kNT / 64];
-    __shared__ Digit shd;
-    const int64_t row = blockIdx.x;
-    const int64_t nv = n_visible(q_pos0 + row % Tq, m, N);
-    int32_t *orow = out + row * k;
-    if (trivial_row(nv, k, orow)) return;
-    const float *srow = scores + row * (int64_t)N;
-    if (IN_LDS) {
-        for (int64_t j = threadIdx.x; j < nv; j += kNT) lds_keys[j] = order_key(srow[j]);
-    }
-    auto key_at = [&](int64_t j) -> uint32_t { return IN_LDS ? lds_keys[j] : order_key(srow[j]); };
-    const Digit d = find_digit<kNT>(ghist + row * kTopkBins, kTopkBins, k, sh, &shd);
+struct IdxKey {
+    int32_t j;
+    uint32_t key;
+};
+
+// Exact select straight over a score row in global memory (used only when
+// the pairs of digit >= D do not fit in LDS).
+__device__ void select_row_global(const float *srow, int64_t nv, int k, Digit d, int32_t *orow, uint32_t *hist,
+                                  int *sh, Digit *shd) {
     uint32_t prefix = d.digit << (32 - kTopkBinBits), mask = ~0u << (32 - kTopkBinBits);
     int rem = k - d.above;
-    if (d.at != rem) refine<kNT>(key_at, nv, prefix, mask, rem, hist, sh, &shd);
+    auto key_at = [&](int64_t j) -> uint32_t { return order_key(srow[j]); };
+    if (d.at != rem) refine<kNT>(key_at, nv, prefix, mask, rem, hist, sh, shd);
     ordered_keep<kNT>(key_at, nv, prefix, mask, rem, sh, [&](int pos, int64_t j) {
         if (pos < k) orow[pos] = (int32_t)j;
     });
 }
 
-// ----------------------------------------------------- decode: filter + final
+// The M pairs of digit >= D sit in LDS in index order: resolve digit D with
+// the lower digits and write the kept indices, ascending.
+__device__ void select_items(const IdxKey *items, int M, int k, Digit d, int32_t *orow, uint32_t *hist, int *sh,
+                             Digit *shd) {
+    uint32_t prefix = d.digit << (32 - kTopkBinBits), mask = ~0u << (32 - kTopkBinBits);
+    int rem = k - d.above;  // keys of digit D to keep
+    auto key_at = [&](int64_t i) -> uint32_t { return items[i].key; };
+    if (d.at != rem) refine<kNT>(key_at, M, prefix, mask, rem, hist, sh, shd);
+    ordered_keep<kNT>(key_at, M, prefix, mask, rem, sh, [&](int pos, int64_t i) {
+        if (pos < k) orow[pos] = items[i].j;
+    });
+}
+
+// ------------------------------------- rows of up to kNT*KPL scores: one pass
+// One workgroup per query.  Wavefront w owns a contiguous run of the row and
+// loads it into registers (KPL scores per lane, as 16-byte vectors of four
+// consecutive scores) while the digit D is found from the histogram; the
+// pairs of digit >= D are then packed into LDS in index order (run offsets
+// from one exchange of per-wave counts, in-run offsets from ballots) and
+// resolved there.
+template <int KPL>
+__global__ __launch_bounds__(kNT) void k_topk_compact(int Tq, int N, int m, int k, int64_t q_pos0,
+                                                      const float *__restrict__ scores,
+                                                      const uint32_t *__restrict__ ghist, int32_t *__restrict__ out) {
+    extern __shared__ IdxKey items[];  // [kTopkFinalItems]
+    __shared__ uint32_t hist[2048];
+    __shared__ int sh[2 * kNT / 64];
+    __shared__ Digit shd;
+    constexpr int NW = kNT / 64;
+    constexpr int F4 = KPL / 4;        // 16-byte vectors per lane
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t row = blockIdx.x;
+    const int64_t nv = n_visible(q_pos0 + row % Tq, m, N);
+    int32_t *orow = out + row * k;
+    if (trivial_row(nv, k, orow)) return;
+    const int stride = (int)topk_score_stride(N);
+    const float *srow = scores + row * stride;
+    const int per = (int)((nv + NW * 256 - 1) / (NW * 256)) * 256;  // run length, <= 64*KPL
+    const int s0 = wv * per;
+    const int s1 = (int)min((int64_t)s0 + per, nv);
+    // unconditional loads (vectors past the row's end reread its last one) so
+    // that all F4 are in flight together; positions >= s1 are masked below
+    float4 sc[F4];
+#pragma unroll
+    for (int c = 0; c < F4; ++c) sc[c] = *(const float4 *)(srow + min(s0 + c * 256 + lane * 4, stride - 4));
+    const Digit d = find_digit<kNT>(ghist + row * kTopkBins, kTopkBins, k, sh, &shd);
+    auto selected = [&](int c, int e, uint32_t &key) -> bool {
+        const float4 v = sc[c];
+        key = order_key(e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w);
+        return s0 + c * 256 + lane * 4 + e < s1 && (key >> (32 - kTopkBinBits)) >= d.digit;
+    };
+    int cnt = 0;
+#pragma unroll
+    for (int c = 0; c < F4; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            uint32_t key;
+            cnt += __popcll(__ballot(selected(c, e, key)));
+        }
+    if (lane == 0) sh[NW + wv] = cnt;
+    __syncthreads();
+    int base = 0, M = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int v = sh[NW + i];
+        base += i < wv ? v : 0;
+        M += v;
+    }
+    __syncthreads();
+    if (M > kTopkFinalItems || M != d.above + d.at) {
+        select_row_global(srow, nv, k, d, orow, hist, sh, &shd);
+        return;
+    }
+#pragma unroll
+    for (int c = 0; c < F4; ++c) {
+        uint32_t key[4];
+        bool sel[4];
+        int before = 0, chunk = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sel[e] = selected(c, e, key[e]);
+            const uint64_t bm = __ballot(sel[e]);
+            before += lanes_below(bm);
+            chunk += __popcll(bm);
+        }
+        int pos = base + before;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (sel[e]) items[pos++] = IdxKey{s0 + c * 256 + lane * 4 + e, key[e]};
+        base += chunk;
+    }
+    __syncthreads();
+    select_items(items, M, k, d, orow, hist, sh, &shd);
+}
+
+// ----------------------------------------------------- long rows: filter + final
 // k_topk_filter: kFT threads per workgroup, nblk workgroups per query.  Each
 // workgroup writes the (index, key) pairs of its chunk whose first digit is at
 // least D (kept ones and candidates alike) to the chunk's segment, in index
@@ -209,11 +297,6 @@ __global__ __launch_bounds__(kNT) void k_topk_rows(int Tq, int N, int m, int k, 
 // pairs arrive in index order), resolves the candidates and writes the kept
 // indices.  (A kernel boundary separates the two: on this multi-die GPU a
 // device-scope fence inside one kernel costs more.)
-struct IdxKey {
-    int32_t j;
-    uint32_t key;
-};
-
 __global__ __launch_bounds__(kFT) void k_topk_filter(int Tq, int N, int m, int k, int64_t q_pos0, int nblk,
                                                      const float *__restrict__ scores,
                                                      const uint32_t *__restrict__ ghist, IdxKey *__restrict__ seg,
@@ -224,17 +307,27 @@ __global__ __launch_bounds__(kFT) void k_topk_filter(int Tq, int N, int m, int k
     const int blk = blockIdx.x % nblk;
     const int64_t nv = n_visible(q_pos0 + row % Tq, m, N);
     if (nv <= k) return;
-    const Digit d = find_digit<kFT>(ghist + row * kTopkBins, kTopkBins, k, sh, &shd);
-    const float *srow = scores + row * (int64_t)N;
+    const int64_t stride = topk_score_stride(N);
+    const float *srow = scores + row * stride;
     const int64_t j0 = (int64_t)blk * kTopkFilterChunk + threadIdx.x * kFPT;
+    // the chunk's scores (16-byte vectors; past the row's end its last vector
+    // is reread and masked) are in flight while the digit is found
+    float4 sc[kFPT / 4];
+#pragma unroll
+    for (int u = 0; u < kFPT / 4; ++u) sc[u] = *(const float4 *)(srow + min(j0 + 4 * u, stride - 4));
+    const Digit d = find_digit<kFT>(ghist + row * kTopkBins, kTopkBins, k, sh, &shd);
     uint32_t keys[kFPT];
     uint32_t bits = 0;
 #pragma unroll
-    for (int u = 0; u < kFPT; ++u) {
-        const int64_t j = j0 + u;
-        keys[u] = j < nv ? order_key(srow[j]) : 0u;
-        bits |= (uint32_t)(j < nv && (keys[u] >> (32 - kTopkBinBits)) >= d.digit) << u;
+    for (int u = 0; u < kFPT / 4; ++u) {
+        keys[4 * u + 0] = order_key(sc[u].x);
+        keys[4 * u + 1] = order_key(sc[u].y);
+        keys[4 * u + 2] = order_key(sc[u].z);
+        keys[4 * u + 3] = order_key(sc[u].w);
     }
+#pragma unroll
+    for (int u = 0; u < kFPT; ++u)
+        bits |= (uint32_t)(j0 + u < nv && (keys[u] >> (32 - kTopkBinBits)) >= d.digit) << u;
     int total;
     int pos = block_excl_scan<kFT>(__popc(bits), sh, &total);
     IdxKey *sg = seg + (row * nblk + blk) * (int64_t)kTopkFilterChunk;
@@ -265,16 +358,9 @@ __global__ __launch_bounds__(kNT) void k_topk_final(int Tq, int N, int m, int k,
     const int x = block_excl_scan<kNT>(cnt, sh, &M);
     if ((int)threadIdx.x <= nblk) pre[threadIdx.x] = (int)threadIdx.x < nblk ? x : M;
     __syncthreads();
-    uint32_t prefix = d.digit << (32 - kTopkBinBits), mask = ~0u << (32 - kTopkBinBits);
-    int rem = k - d.above;  // keys of digit D to keep
     if (M > kTopkFinalItems || M != d.above + d.at) {
-        // more pairs than LDS holds: exact select straight over the row
-        const float *srow = scores + row * (int64_t)N;
-        auto key_at = [&](int64_t j) -> uint32_t { return order_key(srow[j]); };
-        if (d.at != rem) refine<kNT>(key_at, nv, prefix, mask, rem, hist, sh, &shd);
-        ordered_keep<kNT>(key_at, nv, prefix, mask, rem, sh, [&](int pos, int64_t j) {
-            if (pos < k) orow[pos] = (int32_t)j;
-        });
+        // more pairs than LDS holds
+        select_row_global(scores + row * topk_score_stride(N), nv, k, d, orow, hist, sh, &shd);
         return;
     }
     // gather: batches of four pairs per thread, all loads in flight together
@@ -298,17 +384,15 @@ __global__ __launch_bounds__(kNT) void k_topk_final(int Tq, int N, int m, int k,
         }
     }
     __syncthreads();
-    auto ikey_at = [&](int64_t i) -> uint32_t { return items[i].key; };
-    if (d.at != rem) refine<kNT>(ikey_at, M, prefix, mask, rem, hist, sh, &shd);
-    ordered_keep<kNT>(ikey_at, M, prefix, mask, rem, sh, [&](int pos, int64_t i) {
-        if (pos < k) orow[pos] = items[i].j;
-    });
+    select_items(items, M, k, d, orow, hist, sh, &shd);
 }
 
 // ------------------------------------------------------------------ host side
 TopkPlan topk_plan(int64_t rows, int64_t N) {
     TopkPlan p;
-    p.filter = rows < 256 || N > kTopkLdsKeys;
+    // one pass needs enough queries to spread the score rows over the CUs (one
+    // CU streaming a 128 KiB row is slower than eight CUs filtering it)
+    p.filter = rows < kTopkCompactMinRows || N > kTopkCompactMax;
     p.nblk = (N + kTopkFilterChunk - 1) / kTopkFilterChunk;
     if (p.nblk < 1) p.nblk = 1;
     return p;
@@ -339,19 +423,29 @@ hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <int KPL>
+static hipError_t launch_compact(int64_t rows, int Tq, int N, int m, int k, int64_t q_pos0, const float *scores,
+                                 const uint32_t *hist, int32_t *out, hipStream_t st) {
+    static_assert(KPL * kNT <= kTopkCompactMax, "row longer than the one-pass limit");
+    const size_t lds = (size_t)kTopkFinalItems * sizeof(IdxKey);
+    static const hipError_t attr =
+        hipFuncSetAttribute((const void *)k_topk_compact<KPL>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(k_topk_compact<KPL>, dim3((unsigned)rows), dim3(kNT), lds, st, Tq, N, m, k, q_pos0, scores,
+                       hist, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_topk(int B, int Tq, int N, int m, int k, int64_t q_pos0, const float *scores, void *scratch,
                        int32_t *out, hipStream_t st) {
     const int64_t rows = (int64_t)B * Tq;
     const TopkPlan p = topk_plan(rows, N);
     uint32_t *hist = (uint32_t *)scratch;
     if (!p.filter) {
-        static const hipError_t attr = hipFuncSetAttribute(
-            (const void *)k_topk_rows<true>, hipFuncAttributeMaxDynamicSharedMemorySize, kTopkLdsKeys * 4);
-        if (attr != hipSuccess) return attr;
-        const size_t lds = (size_t)(N > 0 ? N : 1) * sizeof(uint32_t);
-        hipLaunchKernelGGL(k_topk_rows<true>, dim3((unsigned)rows), dim3(kNT), lds, st, Tq, N, m, k, q_pos0, scores,
-                           hist, out);
-        return hipGetLastError();
+        if (N <= 8 * kNT) return launch_compact<8>(rows, Tq, N, m, k, q_pos0, scores, hist, out, st);
+        if (N <= 16 * kNT) return launch_compact<16>(rows, Tq, N, m, k, q_pos0, scores, hist, out, st);
+        if (N <= 32 * kNT) return launch_compact<32>(rows, Tq, N, m, k, q_pos0, scores, hist, out, st);
+        return launch_compact<64>(rows, Tq, N, m, k, q_pos0, scores, hist, out, st);
     }
     char *base = (char *)scratch + align256(topk_clear_words(rows, N) * 4);
     int32_t *counts = (int32_t *)base;

@@ -148,6 +148,27 @@ def test_topk_exact_integer_scores(csa):
     assert np.array_equal(to_np(step.topk_idx), ref["idx"])
 
 
+@pytest.mark.parametrize("n_entries,tq", [(20000, 2), (70000, 2), (20000, 256)],
+                         ids=["filter_20k", "filter_70k", "one_pass_20k"])
+def test_topk_all_scores_equal(csa, n_entries, tq):
+    """Zero index queries make every visible score 0: all keys tie, more pairs
+    than the LDS holds share the k-th digit, and the kept set must be the
+    first k visible entries (ties go to the lower index)."""
+    wl = Workload("equal", "bf16", B=1, T=4 * n_entries, Tq=tq, m=4, d=128, H=8, W=4, k=1000, HI=16, dI=32,
+                  seed_base=76000)
+    say(wl)
+    x = make_inputs(wl, "cuda")
+    x["q_idx"].zero_()
+    xh = host_inputs(x)
+    step = csa.AttentionStep.for_workload(wl)
+    step(x)
+    torch.cuda.synchronize()
+    ref = oracle_step(wl, xh)
+    got = to_np(step.topk_idx)
+    assert np.array_equal(got, ref["idx"])
+    assert np.array_equal(got[0, 0], np.arange(wl.k))
+
+
 def test_scores_out_and_masking(csa):
     wl = Workload("scores", "bf16", B=2, T=4 * 700 + 3, Tq=5, m=4, d=128, H=16, W=4, k=64, HI=64, dI=128,
                   seed_base=78000)
