@@ -2,7 +2,9 @@
 //     s[t, j] = sum_h w[t, h] * ReLU(qI[t, h, :] . kI[j, :])
 // for every entry j visible to query t; invisible entries get -inf.
 //
-// Mapping.  One wavefront owns one query and a contiguous chunk of entries.
+// Mapping.  A query's entries are read in batches of four 16-entry tiles,
+// dealt round-robin to the query's wavefronts (so that they sweep the keys
+// front to back together).
 // The query's index heads sit in registers as the MFMA A operand (M = 16
 // heads per block, K = d_I); each 16-entry tile of index keys is streamed
 // from HBM straight into registers as the B operand (N = 16 entries), so
@@ -23,7 +25,7 @@ namespace csa {
 
 template <typename T, int DI, int MB>
 __global__ __launch_bounds__(256) void k_index_scores(int Tq, int N, int HI, int m, int64_t q_pos0, int64_t n_items,
-                                                       int chunks_per_row, int tiles_per_chunk,
+                                                       int chunks_per_row,
                                                        const T *__restrict__ qI, const float *__restrict__ w,
                                                        const T *__restrict__ kI, int64_t k_bs,
                                                        float *__restrict__ scores, int64_t s_stride,
@@ -65,20 +67,24 @@ __global__ __launch_bounds__(256) void k_index_scores(int Tq, int N, int HI, int
     const T *kb = kI + b * k_bs + g * E::KPL;
     float *srow = scores + row * s_stride;
     float *srow2 = scores2 ? scores2 + row * (int64_t)N : nullptr;
-    const int64_t j_lo = (int64_t)chunk * tiles_per_chunk * 16;
-    const int64_t j_hi = min((int64_t)N, j_lo + (int64_t)tiles_per_chunk * 16);
     constexpr int BATCH = 16 * UNROLL;  // entries per batch of tiles
+    // the row's batches are dealt round-robin to its chunks_per_row waves, so
+    // that together they sweep the keys front to back
+    const int64_t j_lo = (int64_t)chunk * BATCH;
+    const int64_t j_hi = N;
+    const int64_t jstep = (int64_t)chunks_per_row * BATCH;
 
-    if (nv == 0) {  // nothing visible: the chunk is all -inf
-        for (int64_t j = j_lo + lane; j < j_hi; j += 64) {
-            srow[j] = -INFINITY;
-            if (srow2) srow2[j] = -INFINITY;
-        }
+    if (nv == 0) {  // nothing visible: the wave's batches are all -inf
+        for (int64_t j0 = j_lo; j0 < j_hi; j0 += jstep)
+            for (int64_t j = j0 + lane; j < min(j0 + BATCH, j_hi); j += 64) {
+                srow[j] = -INFINITY;
+                if (srow2) srow2[j] = -INFINITY;
+            }
     } else {
     // one batch: UNROLL tiles of 16 index keys, straight from HBM to registers.
     // Loads are unconditional so the compiler can wait for exactly one batch:
-    // lanes past the chunk (or past the visible entries) reread its last row.
-    const int64_t j_last = min(j_hi, nv) - 1;
+    // lanes past the visible entries reread the last visible row.
+    const int64_t j_last = nv - 1;
     auto load_batch = [&](int64_t j0, typename E::frag (&bf)[UNROLL][KS]) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
@@ -117,11 +123,11 @@ __global__ __launch_bounds__(256) void k_index_scores(int Tq, int N, int HI, int
     // double-buffered: the next batch is in flight while this one is scored
     typename E::frag b0[UNROLL][KS], b1[UNROLL][KS];
     if (j_lo < j_hi) load_batch(j_lo, b0);
-    for (int64_t j0 = j_lo; j0 < j_hi; j0 += 2 * BATCH) {
-        load_batch(j0 + BATCH, b1);
+    for (int64_t j0 = j_lo; j0 < j_hi; j0 += 2 * jstep) {
+        load_batch(j0 + jstep, b1);
         score_batch(j0, b0);
-        load_batch(j0 + 2 * BATCH, b0);
-        if (j0 + BATCH < j_hi) score_batch(j0 + BATCH, b1);
+        load_batch(j0 + 2 * jstep, b0);
+        if (j0 + jstep < j_hi) score_batch(j0 + jstep, b1);
     }
     }
     if (hist) {
@@ -134,23 +140,236 @@ __global__ __launch_bounds__(256) void k_index_scores(int Tq, int N, int HI, int
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 keys: LDS-DMA streaming.
+//
+// One workgroup of kIdxWaves wavefronts works on one query; a query's 16-entry
+// key tiles are dealt round-robin to the wavefronts of its workgroups.  Each
+// wavefront streams its tiles HBM -> LDS with global_load_lds_dwordx4 into a
+// private ring of kIdxStages tiles (no VGPRs held by loads in flight, and each
+// instruction reads one contiguous KiB).  Within every key row the 16-byte
+// chunks are stored XOR-swizzled by the row, so that the MFMA B-operand reads
+// (ds_read_b128: 16 rows, one chunk each) hit 16 distinct bank groups.  The
+// query's index heads are staged once per workgroup through LDS into the MFMA
+// A operand; the epilogue (ReLU * w, head sum, score store, optional first
+// top-k digit count) is the same as above, with one LDS histogram per
+// workgroup.
+constexpr int kIdxWaves = 4;
+
+template <int DI>
+struct IdxDma {
+    static constexpr int RB = DI * 2;        // bytes per key row
+    static constexpr int CPR = RB / 16;      // 16-byte chunks per row
+    static constexpr int TB = 16 * RB;       // bytes per 16-row tile
+    static constexpr int IPT = TB / 1024;    // DMA instructions per tile
+    static constexpr int RPS = 16 / CPR;     // consecutive rows sharing one swizzle
+    static constexpr int STAGES = 8;         // ring slots per wavefront
+    static constexpr int RING = kIdxWaves * STAGES * TB;
+    static constexpr int QS = 64 * DI * 2;   // staged index query (up to 64 heads)
+    static constexpr int LDS = RING + QS + kTopkBins * 4;
+    // chunk position of row r's chunk ch (an involution, so it also maps back)
+    static __device__ __forceinline__ int swz(int r, int ch) { return ch ^ ((r / RPS) % CPR); }
+};
+
+// 16 bytes per lane from `src` into LDS at lds_addr + 16 * lane, non-temporal
+// (the keys are read once).  Inline assembly keeps the compiler from draining
+// the loads in flight before every LDS read; completion is awaited explicitly.
+// One wait state separates the M0 write from the LDS-DMA instruction.
+__device__ __forceinline__ void lds_dma16_nt(uint32_t lds_addr, const void *src) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(lds_addr), "v"(src)
+                 : "memory", "m0");
+}
+
+// max(x, 0) on the bit pattern: negative floats are negative integers, so one
+// integer max (no NaN canonicalisation of the MFMA result first)
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// sum over the four 16-lane groups (each lane gets the sum for its l % 16)
+__device__ __forceinline__ float sum_lane_groups(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+template <int DI, int MB>
+__global__ __launch_bounds__(kIdxWaves * 64) void k_index_dma(int Tq, int N, int HI, int m, int64_t q_pos0,
+                                                               int blocks_per_row, const bf16_t *__restrict__ qI,
+                                                               const float *__restrict__ w,
+                                                               const bf16_t *__restrict__ kI, int64_t k_bs,
+                                                               float *__restrict__ scores, int64_t s_stride,
+                                                               float *__restrict__ scores2,
+                                                               uint32_t *__restrict__ hist) {
+    using S = IdxDma<DI>;
+    constexpr int KS = DI / 32;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    unsigned char *ring = lds;
+    bf16_t *qs = (bf16_t *)(lds + S::RING);
+    uint32_t *bh = (uint32_t *)(lds + S::RING + S::QS);
+
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // (uniform: keeps tile logic scalar)
+    const int g = lane >> 4, c = lane & 15;
+    const int64_t row = blockIdx.x / blocks_per_row;
+    const int part = blockIdx.x % blocks_per_row;
+    const int64_t b = row / Tq, ti = row % Tq;
+    const int64_t nv = n_visible(q_pos0 + ti, m, N);
+    const int wpr = blocks_per_row * kIdxWaves;       // wavefronts per query
+    const int gw = part * kIdxWaves + wv;             // this wavefront's rank
+    const int tiles = (N + 15) / 16;
+    const int vtiles = (int)((nv + 15) / 16);
+    const int n_all = tiles > gw ? (tiles - gw + wpr - 1) / wpr : 0;    // tiles of this wavefront
+    const int n_vis = vtiles > gw ? (vtiles - gw + wpr - 1) / wpr : 0;  // ... holding visible entries
+
+    // ---- DMA of one tile into ring slot `slot`.  Lane addresses step by a
+    // fixed stride from tile to tile; in the tile that holds the last visible
+    // entry, rows past it reread that entry's row (their scores are masked).
+    const bf16_t *kb = kI + b * k_bs;
+    unsigned char *my_ring = ring + wv * S::STAGES * S::TB;
+    const uint32_t ring_addr = (uint32_t)(uintptr_t)my_ring;
+    const int64_t tstride = (int64_t)wpr * 16 * DI;  // elements between this wavefront's tiles
+    const bf16_t *src0[S::IPT];
+#pragma unroll
+    for (int ip = 0; ip < S::IPT; ++ip) {
+        const int byte = ip * 1024 + lane * 16;       // within the tile
+        const int r = byte / S::RB, pos = (byte % S::RB) / 16;
+        src0[ip] = kb + ((int64_t)gw * 16 + r) * DI + S::swz(r, pos) * 8;
+    }
+    auto issue = [&](int i) {
+        const int t = gw + i * wpr;
+        const int slot = i % S::STAGES;
+        const bool whole = (int64_t)t * 16 + 16 <= nv;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the slot are done
+#pragma unroll
+        for (int ip = 0; ip < S::IPT; ++ip) {
+            const bf16_t *src = src0[ip] + i * tstride;
+            if (!whole) {
+                const int byte = ip * 1024 + lane * 16;
+                const int r = byte / S::RB, pos = (byte % S::RB) / 16;
+                src = kb + min((int64_t)t * 16 + r, nv - 1) * DI + S::swz(r, pos) * 8;
+            }
+            lds_dma16_nt(__builtin_amdgcn_readfirstlane(ring_addr + slot * S::TB + ip * 1024), src);
+        }
+    };
+
+    // ---- stage the index query and clear the histogram
+    for (int i = threadIdx.x; i < HI * DI / 8; i += kIdxWaves * 64)
+        *(u32x4 *)(qs + i * 8) = *(const u32x4 *)(qI + row * HI * DI + i * 8);
+    if (hist)
+        for (int i = threadIdx.x; i < kTopkBins; i += kIdxWaves * 64) bh[i] = 0;
+    float wgt[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int hh = mb * 16 + 4 * g + e;
+            const float v = w[row * HI + min(hh, HI - 1)];
+            wgt[mb][e] = hh < HI ? v : 0.f;
+        }
+
+    __syncthreads();
+    bf16x8 a[MB][KS];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int head = mb * 16 + c;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            bf16x8 v = *(const bf16x8 *)(qs + min(head, HI - 1) * DI + ks * 32 + g * 8);
+            if (head >= HI) v = Elem<bf16_t>::zero();
+            a[mb][ks] = v;
+        }
+    }
+    // (issued after the barrier above, which waits for every load in flight)
+    for (int i = 0; i < S::STAGES - 1 && i < n_vis; ++i) issue(i);
+
+    float *srow = scores + row * s_stride;
+    float *srow2 = scores2 ? scores2 + row * (int64_t)N : nullptr;
+    for (int i = 0; i < n_vis; ++i) {
+        if (i + S::STAGES - 1 < n_vis) {
+            issue(i + S::STAGES - 1);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"((S::STAGES - 1) * S::IPT) : "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        const unsigned char *tile = my_ring + (i % S::STAGES) * S::TB;
+        bf16x8 kf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            kf[ks] = *(const bf16x8 *)(tile + c * S::RB + S::swz(c, ks * 4 + g) * 16);
+        floatx4 acc[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb][ks], kf[ks], acc[mb], 0, 0, 0);
+        float sc = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sc += wgt[mb][e] * relu(acc[mb][e]);
+        sc = sum_lane_groups(sc);
+        const int64_t j = (int64_t)(gw + i * wpr) * 16 + c;
+        if (g == 0 && j < N) {
+            const float v = j < nv ? sc : -INFINITY;
+            srow[j] = v;
+            if (srow2) srow2[j] = v;
+            if (hist && j < nv) atomicAdd(&bh[order_key(sc) >> (32 - kTopkBinBits)], 1u);
+        }
+    }
+    // tiles with no visible entry
+    for (int i = n_vis; i < n_all; ++i) {
+        const int64_t j = (int64_t)(gw + i * wpr) * 16 + lane;
+        if (lane < 16 && j < N) {
+            srow[j] = -INFINITY;
+            if (srow2) srow2[j] = -INFINITY;
+        }
+    }
+    if (hist) {
+        __syncthreads();
+        uint32_t *grow = hist + row * kTopkBins;
+        for (int i = threadIdx.x; i < kTopkBins; i += kIdxWaves * 64) {
+            const uint32_t v = bh[i];
+            if (v) atomicAdd(&grow[i], v);
+        }
+    }
+}
+
+template <int DI, int MB>
+static hipError_t launch_dma(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const void *qI, const float *w,
+                             const void *kI, int64_t k_bs, float *scores, int64_t s_stride, float *scores2,
+                             uint32_t *hist, hipStream_t st) {
+    using S = IdxDma<DI>;
+    static const hipError_t attr = hipFuncSetAttribute((const void *)k_index_dma<DI, MB>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
+    if (attr != hipSuccess) return attr;
+    const int64_t rows = (int64_t)B * Tq;
+    const int64_t tiles = (N + 15) / 16;
+    // one workgroup per CU in total when there are few queries, at least one per query
+    int64_t bpr = (256 + rows - 1) / rows;
+    const int64_t max_bpr = (tiles + kIdxWaves - 1) / kIdxWaves;
+    if (bpr > max_bpr) bpr = max_bpr;
+    if (bpr < 1) bpr = 1;
+    hipLaunchKernelGGL((k_index_dma<DI, MB>), dim3((unsigned)(rows * bpr)), dim3(kIdxWaves * 64), S::LDS, st, Tq, N,
+                       HI, m, q_pos0, (int)bpr, (const bf16_t *)qI, w, (const bf16_t *)kI, k_bs, scores, s_stride,
+                       scores2, hist);
+    return hipGetLastError();
+}
+
 template <typename T, int DI, int MB>
 static hipError_t launch_t(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const void *qI, const float *w,
                            const void *kI, int64_t k_bs, float *scores, int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
     const int64_t rows = (int64_t)B * Tq;
-    const int64_t tiles = (N + 15) / 16;
+    const int64_t batches = (N + 63) / 64;  // batches of four 16-entry tiles
     // aim for ~2048 wavefronts in flight (8 per CU) when there are few queries
     int64_t chunks = (2048 + rows - 1) / rows;
-    if (chunks > tiles) chunks = tiles;
-    if (chunks < 1) chunks = 1;
-    int64_t tpc = (tiles + chunks - 1) / chunks;
-    tpc = (tpc + 3) / 4 * 4;
-    chunks = (tiles + tpc - 1) / tpc;
+    if (chunks > batches) chunks = batches;
     if (chunks < 1) chunks = 1;
     const int64_t items = rows * chunks;
     const int64_t blocks = (items + 3) / 4;
     hipLaunchKernelGGL((k_index_scores<T, DI, MB>), dim3((unsigned)blocks), dim3(256), 0, st, Tq, N, HI, m, q_pos0,
-                       items, (int)chunks, (int)tpc, (const T *)qI, w, (const T *)kI, k_bs, scores, s_stride,
+                       items, (int)chunks, (const T *)qI, w, (const T *)kI, k_bs, scores, s_stride,
                        scores2, hist);
     return hipGetLastError();
 }
@@ -158,6 +377,13 @@ static hipError_t launch_t(int B, int Tq, int N, int HI, int m, int64_t q_pos0, 
 template <typename T, int DI>
 static hipError_t launch_di(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const void *qI, const float *w,
                             const void *kI, int64_t k_bs, float *scores, int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
+    if constexpr (sizeof(T) == 2) {
+        if (HI <= 16) return launch_dma<DI, 1>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride, scores2,
+                                               hist, st);
+        if (HI <= 32) return launch_dma<DI, 2>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride, scores2,
+                                               hist, st);
+        return launch_dma<DI, 4>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride, scores2, hist, st);
+    }
     if (HI <= 16) return launch_t<T, DI, 1>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride, scores2,
                                                    hist, st);
     if (HI <= 32) return launch_t<T, DI, 2>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride, scores2,
