@@ -382,32 +382,47 @@ __global__ __launch_bounds__(kMqaThreads) void k_mqa(const MqaArgs a) {
 }
 
 // Merge the split-K partials of one (query, head): a 4-wide column slice
-// per thread.  Maxima are base-2; empty splits carry l = 0 and are skipped.
+// per thread.  Splits are taken kMqaMaxSplits at a time, every (max, sum)
+// and column slice of a batch loaded up front (indices past n_splits reread
+// the last split with zero weight) so the loads are in flight together.
+// Maxima are base-2; empty splits carry l = 0 and get weight 0.
 __global__ __launch_bounds__(128) void k_combine(int H, int D, int n_splits, const float *__restrict__ part_o,
                                                  const float *__restrict__ part_ml, float *__restrict__ out,
                                                  float *__restrict__ lse) {
     const int64_t rh = blockIdx.x;
     const int64_t row = rh / H;
     const int h = (int)(rh % H);
-    float M = -INFINITY;
-    for (int s = 0; s < n_splits; ++s) {
-        const int64_t slot = (row * n_splits + s) * H + h;
-        if (part_ml[slot * 2 + 1] > 0.f) M = fmaxf(M, part_ml[slot * 2]);
-    }
-    float L = 0.f;
+    const int x = min((int)threadIdx.x * 4, D - 4);
+    float M = -INFINITY, L = 0.f;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    const int x = threadIdx.x * 4;
-    for (int s = 0; s < n_splits; ++s) {
-        const int64_t slot = (row * n_splits + s) * H + h;
-        const float ls = part_ml[slot * 2 + 1];
-        if (ls > 0.f) {
-            const float wgt = __builtin_amdgcn_exp2f(part_ml[slot * 2] - M);
-            L += ls * wgt;
-            if (x < D) acc += wgt * *(const floatx4 *)(part_o + slot * D + x);
+    for (int s0 = 0; s0 < n_splits; s0 += kMqaMaxSplits) {
+        float ms[kMqaMaxSplits], ls[kMqaMaxSplits];
+        floatx4 po[kMqaMaxSplits];
+#pragma unroll
+        for (int u = 0; u < kMqaMaxSplits; ++u) {
+            const int64_t slot = (row * n_splits + min(s0 + u, n_splits - 1)) * H + h;
+            ms[u] = part_ml[slot * 2];
+            ls[u] = s0 + u < n_splits ? part_ml[slot * 2 + 1] : 0.f;
+            po[u] = *(const floatx4 *)(part_o + slot * D + x);
+        }
+        float Mc = M;
+#pragma unroll
+        for (int u = 0; u < kMqaMaxSplits; ++u) Mc = ls[u] > 0.f ? fmaxf(Mc, ms[u]) : Mc;
+        if (Mc > M) {  // (more than one batch of splits only)
+            const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mc);
+            L *= sc;
+            acc *= sc;
+            M = Mc;
+        }
+#pragma unroll
+        for (int u = 0; u < kMqaMaxSplits; ++u) {
+            const float wgt = ls[u] > 0.f ? __builtin_amdgcn_exp2f(ms[u] - M) : 0.f;
+            L += ls[u] * wgt;
+            acc += wgt * po[u];
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    if (x < D) *(floatx4 *)(out + rh * D + x) = acc * inv;
+    if ((int)threadIdx.x * 4 < D) *(floatx4 *)(out + rh * D + x) = acc * inv;
     if (lse && threadIdx.x == 0) lse[rh] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
 }
 
