@@ -56,7 +56,7 @@ hipError_t launch_topk(int B, int Tq, int N, int m, int k, int64_t q_pos0, const
 
 // attention work split: aim for this many workgroups, at most this many
 // splits of one query's rows, and at most this many 32-row tiles per split
-constexpr int kMqaTargetBlocks = 160;
+constexpr int kMqaTargetBlocks = 256;
 constexpr int kMqaMaxSplits = 16;
 // (the row table shares LDS with the tile stages: fp32 rows of d=512 leave
 // room for 56 tiles)
