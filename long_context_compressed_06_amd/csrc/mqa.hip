@@ -117,11 +117,14 @@ __device__ __forceinline__ void tr_read4(uint32_t addr, bf16x8 (&va)[4]) {
     }
 }
 
-// LDS slot of tile row r.  With a row stride of 4 banks (mod 64), rows r and
-// 16+r read together by the logits product need distinct slots mod 16, and
-// the four rows 4g..4g+3 of a transposing read need slots two apart so that
-// their 8-bank windows do not overlap: even slots for rows 0-7, odd for 8-15.
-__device__ __forceinline__ int row_slot(int r) { return (r & 16) | ((r & 7) << 1) | ((r >> 3) & 1); }
+// LDS slot of tile row r.  LDS serves 128 bytes (32 four-byte banks) per
+// cycle, and the row stride is 4 banks (mod 32): the logits product reads 16
+// bytes of rows c and c+8 in one cycle per eight lanes, so rows 0-7 (and
+// 8-15, ...) need slots distinct mod 8; a transposing read takes 8 bytes of
+// rows 4g..4g+3 in one cycle per sixteen lanes, so those four rows need slots
+// two apart mod 8 (disjoint 8-bank windows): rows 4g..4g+3 go to even slots
+// for even g and odd slots for odd g.
+__device__ __forceinline__ int row_slot(int r) { return (r & 24) | ((r & 3) << 1) | ((r >> 2) & 1); }
 
 template <typename T, int D>
 __global__ __launch_bounds__(kMqaThreads) void k_mqa(const MqaArgs a) {
