@@ -61,8 +61,12 @@ struct MqaShape {
     static constexpr int LPW = (TR / NW) * IPR;            // DMA instructions per wave per tile
     static constexpr int SPLITD = (D / 2) % Elem<T>::KSTEP == 0 && (D / 2) % 16 == 0 ? 2 : 1;
     static constexpr int DW = D / SPLITD;                  // latent columns per wave
-    static constexpr int XCH = SPLITD == 2 ? NW * 64 * 8 * 4 : 0;  // partial-logit exchange bytes
-    static constexpr int STAGES = 3 * TILEB + XCH <= 120 * 1024 ? 3 : 2;  // tiles in flight
+    static constexpr int XCH1 = NW * 64 * 8 * 4;                  // one partial-logit exchange buffer
+    // three stages with a double-buffered exchange (one barrier per tile) when
+    // they fit, else two stages with one exchange buffer (two barriers per tile)
+    static constexpr bool PIPE = SPLITD == 2 && 3 * TILEB + 2 * XCH1 <= 136 * 1024;
+    static constexpr int STAGES = PIPE || (SPLITD == 1 && 3 * TILEB <= 120 * 1024) ? 3 : 2;  // tiles in flight
+    static constexpr int XCH = SPLITD == 2 ? (PIPE ? 2 : 1) * XCH1 : 0;  // exchange bytes
     static size_t lds_bytes(int tiles_per_split) {
         return (size_t)STAGES * TILEB + XCH + (size_t)tiles_per_split * (TR * sizeof(void *) + 4);
     }
@@ -227,136 +231,180 @@ __global__ __launch_bounds__(kMqaThreads) void k_mqa(const MqaArgs a) {
         const int k_off = row_slot(c) * S::RS + cb + g * E::KPL * (int)sizeof(T);  // logits, rows c (+16)
         const int v_off1 = row_slot(4 * g + (c >> 2)) * S::RS + cb + 8 * (c & 3);  // transposing, rows 4g..
 
-        for (int lt = 0; lt < ntiles; ++lt) {
-            // wait until this tile's loads landed (STAGES-2 younger tiles may
-            // still fly); the barrier also proves every wave is done with the
-            // previous tile, whose stage the next DMA reuses
-            const int younger = min(ntiles - 1 - lt, S::STAGES - 2);
-            if (S::STAGES == 3 && younger == 1)
+        // logits of tile lt over this wave's half of d (S^T: rows 4g+e (+16), head c)
+        auto logits = [&](int lt, floatx4 (&sacc)[2]) {
+            const unsigned char *buf = tiles + (lt % S::STAGES) * S::TILEB;
+            // all K fragments of both row blocks first, so the reads overlap;
+            // then four independent accumulation chains (row block x K-step parity)
+            typename E::frag kf[2][KS];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    kf[rb][ks] = *(const typename E::frag *)(buf + k_off + rb * 16 * S::RS +
+                                                             ks * E::KSTEP * (int)sizeof(T));
+            __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of their MFMAs
+            floatx4 acc[2][2];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) acc[rb][0] = acc[rb][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) acc[rb][ks & 1] = E::mma(kf[rb][ks], qf[ks], acc[rb][ks & 1]);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) sacc[rb] = acc[rb][0] + acc[rb][1];
+        };
+        // online softmax of tile lt's logits and the weighted sum of its rows
+        auto softmax_pv = [&](int lt, const floatx4 (&sacc)[2]) {
+            const unsigned char *buf = tiles + (lt % S::STAGES) * S::TILEB;
+            const uint32_t vm = vmask[lt];
+            // raw logits (masked rows -inf); scale2 > 0 keeps the order
+            float sv[8];
+            if (vm == 0xffffffffu) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) sv[q] = sacc[q >> 2][q & 3];
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int rl = (q >> 2) * 16 + 4 * g + (q & 3);
+                    sv[q] = (vm >> rl) & 1u ? sacc[q >> 2][q & 3] : -INFINITY;
+                }
+            }
+            float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                             fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx *= scale2;  // base-2 logit maximum of this tile
+            // move the reference only when the maximum outgrows it by 2^8
+            if (mx > m_ref + kLazyRescale) {
+                const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - mx);
+                l_run *= alpha;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) o[nb] *= alpha;
+                m_ref = mx;
+            }
+            // m_ref stays -inf only while no row has been valid: nothing to add
+            if (m_ref == -INFINITY) return;
+            float p[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                p[q] = __builtin_amdgcn_exp2f(fmaf(sv[q], scale2, -m_ref));  // exp2(-inf) = 0
+                l_run += p[q];
+            }
+            if constexpr (sizeof(T) == 2) {
+                bf16x8 hi, lo;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const __bf16 h = (__bf16)p[q];
+                    hi[q] = h;
+                    lo[q] = (__bf16)(p[q] - (float)h);
+                }
+                // lane (g, c) addresses rows 4g + c/4 (and +16), columns nb*16 + 4*(c%4) .. +3;
+                // the transposing read hands lane c the column nb*16 + c of rows 4g..4g+3
+                if constexpr (NB % 4 == 0) {
+                    // batches of four column blocks: eight transposing reads, then eight MFMAs
+                    const uint32_t vaddr = (uint32_t)(uintptr_t)(buf + v_off1);
+#pragma unroll
+                    for (int nb0 = 0; nb0 < NB; nb0 += 4) {
+                        bf16x8 va[4];
+                        switch (nb0) {  // the offsets are immediates
+#define CSA_TR4(K) case K: tr_read4<S::RS, K>(vaddr, va); break;
+                            CSA_TR4(0) CSA_TR4(4) CSA_TR4(8) CSA_TR4(12) CSA_TR4(16) CSA_TR4(20) CSA_TR4(24)
+                            CSA_TR4(28)
+#undef CSA_TR4
+                        }
+                        // the high-part products first, so no MFMA waits on the one before it
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            o[nb0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u], hi, o[nb0 + u], 0, 0, 0);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            o[nb0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u], lo, o[nb0 + u], 0, 0, 0);
+                    }
+                } else {
+                    // narrow rows: the same reads through the builtin
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const v4s v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) v4s *)(buf + v_off1 + nb * 32));
+                        const v4s v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) v4s *)(buf + v_off1 + 16 * S::RS + nb * 32));
+                        const bf16x8 va = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, v1),
+                                                                  __builtin_bit_cast(bf16x4_t, v2), 0, 1, 2, 3,
+                                                                  4, 5, 6, 7);
+                        o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, hi, o[nb], 0, 0, 0);
+                        o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, lo, o[nb], 0, 0, 0);
+                    }
+                }
+            } else {
+                // fp32: 16x16x4 steps, one row per lane group: lane (g, c) gives
+                // V[rb*16 + 4g + e][nb*16 + c] with the weight of that row
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const int r = (q >> 2) * 16 + 4 * g + (q & 3);
+                        const float v = *(const float *)(buf + row_slot(r) * S::RS + cb + (nb * 16 + c) * 4);
+                        o[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, p[q], o[nb], 0, 0, 0);
+                    }
+            }
+        };
+        if constexpr (S::PIPE) {
+            // One barrier per tile.  Iteration lt: publish tile lt's partial
+            // logits, wait for this wave's share of tile lt+1, barrier (so the
+            // logits exchange, tile lt+1 and the end of every wave's use of
+            // tile lt-1 are all settled), refill tile lt-1's stage, then the
+            // softmax and weighted sum of tile lt and the logits of tile lt+1
+            // run back to back.  The exchange is double-buffered by tile parity.
+            floatx4 sacc[2];
+            if (S::STAGES == 3 && ntiles > 1)
                 wait_vm_barrier<S::LPW>();
             else
                 wait_vm_barrier<0>();
-            if (lt + S::STAGES - 1 < ntiles) issue(lt + S::STAGES - 1);
-            const unsigned char *buf = tiles + (lt % S::STAGES) * S::TILEB;
-            const uint32_t vm = vmask[lt];
-            floatx4 sacc[2];
-            if (wave_on) {
-#pragma unroll
-                for (int rb = 0; rb < 2; ++rb) {
-                    // all K fragments of the row block first, so the reads overlap
-                    sacc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
-                    const unsigned char *kr = buf + k_off + rb * 16 * S::RS;
-                    typename E::frag kf[KS];
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks)
-                        kf[ks] = *(const typename E::frag *)(kr + ks * E::KSTEP * (int)sizeof(T));
-                    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of their MFMAs
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) sacc[rb] = E::mma(kf[ks], qf[ks], sacc[rb]);
-                }
-            }
-            if constexpr (S::SPLITD == 2) {
-                // sum the two halves of the logits: publish, barrier, add the partner's
+            if (wave_on) logits(0, sacc);
+            for (int lt = 0; lt < ntiles; ++lt) {
+                floatx4 *xb = xch + (lt & 1) * (S::NW * 2 * 64);
                 if (wave_on) {
-                    xch[(wv * 2 + 0) * 64 + lane] = sacc[0];
-                    xch[(wv * 2 + 1) * 64 + lane] = sacc[1];
+                    xb[(wv * 2 + 0) * 64 + lane] = sacc[0];
+                    xb[(wv * 2 + 1) * 64 + lane] = sacc[1];
                 }
-                lds_barrier();
+                wait_vm_barrier<0>();
+                if (lt + S::STAGES - 1 < ntiles) issue(lt + S::STAGES - 1);
                 if (wave_on) {
                     const int pw = wv ^ NHG;
-                    sacc[0] += xch[(pw * 2 + 0) * 64 + lane];
-                    sacc[1] += xch[(pw * 2 + 1) * 64 + lane];
+                    sacc[0] += xb[(pw * 2 + 0) * 64 + lane];
+                    sacc[1] += xb[(pw * 2 + 1) * 64 + lane];
+                    softmax_pv(lt, sacc);
+                    if (lt + 1 < ntiles) logits(lt + 1, sacc);
                 }
             }
-            if (wave_on) {
-                // raw logits (masked rows -inf); scale2 > 0 keeps the order
-                float sv[8];
-                if (vm == 0xffffffffu) {
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) sv[q] = sacc[q >> 2][q & 3];
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const int rl = (q >> 2) * 16 + 4 * g + (q & 3);
-                        sv[q] = (vm >> rl) & 1u ? sacc[q >> 2][q & 3] : -INFINITY;
+        } else {
+            for (int lt = 0; lt < ntiles; ++lt) {
+                // wait until this tile's loads landed (STAGES-2 younger tiles may
+                // still fly); the barrier also proves every wave is done with the
+                // previous tile, whose stage the next DMA reuses
+                const int younger = min(ntiles - 1 - lt, S::STAGES - 2);
+                if (S::STAGES == 3 && younger == 1)
+                    wait_vm_barrier<S::LPW>();
+                else
+                    wait_vm_barrier<0>();
+                if (lt + S::STAGES - 1 < ntiles) issue(lt + S::STAGES - 1);
+                floatx4 sacc[2];
+                if (wave_on) logits(lt, sacc);
+                if constexpr (S::SPLITD == 2) {
+                    // sum the two halves of the logits: publish, barrier, add the partner's
+                    if (wave_on) {
+                        xch[(wv * 2 + 0) * 64 + lane] = sacc[0];
+                        xch[(wv * 2 + 1) * 64 + lane] = sacc[1];
+                    }
+                    lds_barrier();
+                    if (wave_on) {
+                        const int pw = wv ^ NHG;
+                        sacc[0] += xch[(pw * 2 + 0) * 64 + lane];
+                        sacc[1] += xch[(pw * 2 + 1) * 64 + lane];
                     }
                 }
-                float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                                 fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                mx *= scale2;  // base-2 logit maximum of this tile
-                // move the reference only when the maximum outgrows it by 2^8
-                if (mx > m_ref + kLazyRescale) {
-                    const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - mx);
-                    l_run *= alpha;
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) o[nb] *= alpha;
-                    m_ref = mx;
-                }
-                // m_ref stays -inf only while no row has been valid: nothing to add
-                if (m_ref == -INFINITY) continue;
-                float p[8];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    p[q] = __builtin_amdgcn_exp2f(fmaf(sv[q], scale2, -m_ref));  // exp2(-inf) = 0
-                    l_run += p[q];
-                }
-                if constexpr (sizeof(T) == 2) {
-                    bf16x8 hi, lo;
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const __bf16 h = (__bf16)p[q];
-                        hi[q] = h;
-                        lo[q] = (__bf16)(p[q] - (float)h);
-                    }
-                    // lane (g, c) addresses rows 4g + c/4 (and +16), columns nb*16 + 4*(c%4) .. +3;
-                    // the transposing read hands lane c the column nb*16 + c of rows 4g..4g+3
-                    if constexpr (NB % 4 == 0) {
-                        // batches of four column blocks: eight transposing reads, then eight MFMAs
-                        const uint32_t vaddr = (uint32_t)(uintptr_t)(buf + v_off1);
-#pragma unroll
-                        for (int nb0 = 0; nb0 < NB; nb0 += 4) {
-                            bf16x8 va[4];
-                            switch (nb0) {  // the offsets are immediates
-#define CSA_TR4(K) case K: tr_read4<S::RS, K>(vaddr, va); break;
-                                CSA_TR4(0) CSA_TR4(4) CSA_TR4(8) CSA_TR4(12) CSA_TR4(16) CSA_TR4(20) CSA_TR4(24)
-                                CSA_TR4(28)
-#undef CSA_TR4
-                            }
-#pragma unroll
-                            for (int u = 0; u < 4; ++u) {
-                                o[nb0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u], hi, o[nb0 + u], 0, 0, 0);
-                                o[nb0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u], lo, o[nb0 + u], 0, 0, 0);
-                            }
-                        }
-                    } else {
-                        // narrow rows: the same reads through the builtin
-#pragma unroll
-                        for (int nb = 0; nb < NB; ++nb) {
-                            const v4s v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                (__attribute__((address_space(3))) v4s *)(buf + v_off1 + nb * 32));
-                            const v4s v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                (__attribute__((address_space(3))) v4s *)(buf + v_off1 + 16 * S::RS + nb * 32));
-                            const bf16x8 va = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, v1),
-                                                                      __builtin_bit_cast(bf16x4_t, v2), 0, 1, 2, 3,
-                                                                      4, 5, 6, 7);
-                            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, hi, o[nb], 0, 0, 0);
-                            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, lo, o[nb], 0, 0, 0);
-                        }
-                    }
-                } else {
-                    // fp32: 16x16x4 steps, one row per lane group: lane (g, c) gives
-                    // V[rb*16 + 4g + e][nb*16 + c] with the weight of that row
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                        for (int q = 0; q < 8; ++q) {
-                            const int r = (q >> 2) * 16 + 4 * g + (q & 3);
-                            const float v = *(const float *)(buf + row_slot(r) * S::RS + cb + (nb * 16 + c) * 4);
-                            o[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, p[q], o[nb], 0, 0, 0);
-                        }
-                }
+                if (wave_on) softmax_pv(lt, sacc);
             }
         }
     }
