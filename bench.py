@@ -27,6 +27,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+# counter-based HBM traffic of the indexer, measured by rocprofv3 on this
+# workload and kept with the source digest of the kernel it was taken on
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_traffic_csa_decode_128K.txt")
+INDEXER_SOURCES = ["long_context_compressed_06_amd/csrc/indexer.hip", "long_context_compressed_06_amd/csrc/common.h",
+                   "long_context_compressed_06_amd/csrc/kernels.h"]
 
 
 def log(*a):
@@ -56,6 +61,32 @@ def algorithmic_bytes(wl) -> dict:
     # compression of the new groups: logits, raw rows outside the window, the entry write
     step += wl.B * (wl.G_new * wl.m * 4 + wl.G_new * wl.d * es)
     return {"step": step, "indexer": idx_kernel}
+
+
+def indexer_source_digest() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in INDEXER_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def indexer_traffic():
+    """Counter-based bytes per indexer launch, or None when the profile is
+    missing or was taken on different kernel source."""
+    try:
+        fields = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line and not line.startswith(" "))
+    except OSError:
+        return None
+    fields = {k.strip(): v.strip() for k, v in fields.items()}
+    if fields.get("indexer_source_sha256") != indexer_source_digest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def replicas_for(x: dict) -> int:
@@ -170,6 +201,8 @@ def main():
     ap.add_argument("--workload", default="c2", help="c2 (default), c3 or c5")
     ap.add_argument("--also", default="c3,c5", help="secondary decode workloads ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -209,7 +242,7 @@ def main():
     if "indexer_ms" in r:
         ach = ab["indexer"] / (r["indexer_ms"] * 1e-3) / 1e9
         line["roofline"] = {"kernel": "k_index_scores (lightning indexer)", "bound": "hbm", "achieved": ach,
-                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": indexer_traffic(),
                             "bytes_per_launch": ab["indexer"], "avg_launch_us": r["indexer_ms"] * 1e3}
     also = {}
     for name in [a for a in args.also.split(",") if a and a != args.workload]:
@@ -222,6 +255,13 @@ def main():
                          "algorithmic_bytes": b2}
     if also:
         line["also"] = also
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")  # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(wl)
