@@ -241,7 +241,7 @@ def main():
     }
     if "indexer_ms" in r:
         ach = ab["indexer"] / (r["indexer_ms"] * 1e-3) / 1e9
-        line["roofline"] = {"kernel": "k_index_scores (lightning indexer)", "bound": "hbm", "achieved": ach,
+        line["roofline"] = {"kernel": "k_index_dma (lightning indexer, bf16 keys)", "bound": "hbm", "achieved": ach,
                             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": indexer_traffic(),
                             "bytes_per_launch": ab["indexer"], "avg_launch_us": r["indexer_ms"] * 1e3}
     also = {}
