@@ -374,10 +374,188 @@ static hipError_t launch_t(int B, int Tq, int N, int HI, int m, int64_t q_pos0, 
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// bf16 keys, many queries (prefill chunks): query-blocked.
+//
+// One workgroup of kPreWaves wavefronts serves kPreWaves consecutive queries
+// of one sequence, one query per wavefront, so every key tile staged in LDS
+// feeds kPreWaves queries (a decode-style kernel would stream the keys once
+// per query).  Each wavefront keeps its query's index heads in registers as
+// the MFMA A operand and computes a 64-entry x H_I tile per step: 4 K-steps x
+// 4 entry blocks x MB head blocks of v_mfma_f32_16x16x32_bf16, reading the
+// key fragments (B operand) from the shared LDS tile; the epilogue is the
+// decode kernel's (ReLU, head weights, head sum across lane groups), with one
+// LDS histogram per query for the first top-k digit.  Key tiles of 64 rows
+// stream HBM -> LDS by LDS-DMA with kPreStages tiles in flight, rows
+// XOR-swizzled as in k_index_dma.  Entries past a query's visible count are
+// -inf; tiles past every query of the workgroup are not computed.
+constexpr int kPreWaves = 8;
+constexpr int kPreMinQueries = 64;  // queries per sequence from which the query-blocked kernel is used
+constexpr int kPreRows = 64;       // entries per key tile
+constexpr int kPreStages = 3;
+
+template <int DI>
+struct IdxPre {
+    static constexpr int RB = DI * 2;                 // bytes per key row
+    static constexpr int CPR = RB / 16;               // 16-byte chunks per row
+    static constexpr int RPS = 16 / CPR;              // consecutive rows sharing one swizzle
+    static constexpr int TB = kPreRows * RB;          // bytes per key tile
+    static constexpr int IPT = TB / 1024;             // DMA instructions per tile
+    static constexpr int LDS = kPreStages * TB + kPreWaves * kTopkBins * 4;
+    static __device__ __forceinline__ int swz(int r, int ch) { return ch ^ ((r / RPS) % CPR); }
+};
+
+template <int DI, int MB>
+__global__ __launch_bounds__(kPreWaves * 64) void k_index_prefill(int Tq, int N, int HI, int m, int64_t q_pos0,
+                                                                   int blocks_per_seq, const bf16_t *__restrict__ qI,
+                                                                   const float *__restrict__ w,
+                                                                   const bf16_t *__restrict__ kI, int64_t k_bs,
+                                                                   float *__restrict__ scores, int64_t s_stride,
+                                                                   float *__restrict__ scores2,
+                                                                   uint32_t *__restrict__ hist) {
+    using S = IdxPre<DI>;
+    constexpr int KS = DI / 32;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    unsigned char *ring = lds;
+    uint32_t *qh = (uint32_t *)(lds + kPreStages * S::TB);  // [kPreWaves][kTopkBins]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, c = lane & 15;
+    const int64_t b = blockIdx.x / blocks_per_seq;
+    const int q0 = (blockIdx.x % blocks_per_seq) * kPreWaves;  // first query of the workgroup
+    const int ti = q0 + wv;
+    const bool on = ti < Tq;
+    const int64_t row = b * Tq + min(ti, Tq - 1);
+    const int64_t nv = on ? n_visible(q_pos0 + ti, m, N) : 0;
+    // visible entries of the workgroup's last query bound every tile it computes
+    const int64_t nv_max = n_visible(q_pos0 + min(q0 + kPreWaves, Tq) - 1, m, N);
+    const int tiles = (N + kPreRows - 1) / kPreRows;
+    const int vtiles = (int)((nv_max + kPreRows - 1) / kPreRows);
+
+    if (hist)
+        for (int i = lane; i < kTopkBins; i += 64) qh[wv * kTopkBins + i] = 0;
+    // the query's index heads (A operand) and head weights
+    bf16x8 a[MB][KS];
+    float wgt[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int head = mb * 16 + c;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 v = *(const bf16x8 *)(qI + (row * HI + min(head, HI - 1)) * DI + ks * 32 + g * 8);
+            a[mb][ks] = head < HI ? v : Elem<bf16_t>::zero();
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int hh = mb * 16 + 4 * g + e;
+            const float v = w[row * HI + min(hh, HI - 1)];
+            wgt[mb][e] = hh < HI ? v : 0.f;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // (vmcnt(0): the loads above are done before the DMAs start)
+
+    // DMA of key tile t into stage t % kPreStages: wave wv moves KiB wv, wv + kPreWaves, ...
+    const bf16_t *kb = kI + b * k_bs;
+    const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
+    auto issue = [&](int t) {
+        const uint32_t stage = ring_addr + (t % kPreStages) * S::TB;
+        for (int ip = wv; ip < S::IPT; ip += kPreWaves) {
+            const int byte = ip * 1024 + lane * 16;
+            const int r = byte / S::RB, pos = (byte % S::RB) / 16;
+            const int64_t jr = min((int64_t)t * kPreRows + r, nv_max - 1);
+            lds_dma16_nt(__builtin_amdgcn_readfirstlane(stage + ip * 1024), kb + jr * DI + S::swz(r, pos) * 8);
+        }
+    };
+    // DMA instructions per wave per tile: every wave moves IPW KiB, or (short
+    // tiles) IPW or none, so vmcnt((stages - 2) * IPW) always covers the older tiles
+    constexpr int IPW = (S::IPT + kPreWaves - 1) / kPreWaves;
+    static_assert(S::IPT % kPreWaves == 0 || S::IPT < kPreWaves, "uneven shares of a tile's DMA");
+    for (int t = 0; t < kPreStages - 1 && t < vtiles; ++t) issue(t);
+
+    float *srow = scores + row * s_stride;
+    float *srow2 = scores2 ? scores2 + row * (int64_t)N : nullptr;
+    for (int t = 0; t < vtiles; ++t) {
+        // this wave's share of tile t has landed (kPreStages-2 younger tiles may fly), then
+        // the barrier: every share has landed and every wave is done with tile t-1
+        if (t + kPreStages - 2 < vtiles)
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((kPreStages - 2) * IPW) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        if (t + kPreStages - 1 < vtiles) issue(t + kPreStages - 1);
+        const unsigned char *tile = ring + (t % kPreStages) * S::TB;
+#pragma unroll
+        for (int nb = 0; nb < kPreRows / 16; ++nb) {
+            bf16x8 kf[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                kf[ks] = *(const bf16x8 *)(tile + (nb * 16 + c) * S::RB + S::swz(nb * 16 + c, ks * 4 + g) * 16);
+            floatx4 acc[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb][ks], kf[ks], acc[mb], 0, 0, 0);
+            float sc = 0.f;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sc += wgt[mb][e] * relu(acc[mb][e]);
+            sc = sum_lane_groups(sc);
+            const int64_t j = (int64_t)t * kPreRows + nb * 16 + c;
+            if (on && g == 0 && j < N) {
+                const float v = j < nv ? sc : -INFINITY;
+                srow[j] = v;
+                if (srow2) srow2[j] = v;
+                if (hist && j < nv) atomicAdd(&qh[wv * kTopkBins + (order_key(sc) >> (32 - kTopkBinBits))], 1u);
+            }
+        }
+    }
+    // entries past every query of the workgroup
+    if (on)
+        for (int64_t j = (int64_t)vtiles * kPreRows + lane; j < N; j += 64) {
+            srow[j] = -INFINITY;
+            if (srow2) srow2[j] = -INFINITY;
+        }
+    if (hist && on) {
+        // LDS operations of one wave complete in order: its histogram is final here
+        uint32_t *grow = hist + row * kTopkBins;
+        for (int i = lane; i < kTopkBins; i += 64) {
+            const uint32_t v = qh[wv * kTopkBins + i];
+            if (v) atomicAdd(&grow[i], v);
+        }
+    }
+}
+
+template <int DI, int MB>
+static hipError_t launch_prefill(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const void *qI, const float *w,
+                                 const void *kI, int64_t k_bs, float *scores, int64_t s_stride, float *scores2,
+                                 uint32_t *hist, hipStream_t st) {
+    using S = IdxPre<DI>;
+    static const hipError_t attr = hipFuncSetAttribute((const void *)k_index_prefill<DI, MB>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
+    if (attr != hipSuccess) return attr;
+    const int bps = (Tq + kPreWaves - 1) / kPreWaves;
+    hipLaunchKernelGGL((k_index_prefill<DI, MB>), dim3((unsigned)((int64_t)B * bps)), dim3(kPreWaves * 64), S::LDS,
+                       st, Tq, N, HI, m, q_pos0, bps, (const bf16_t *)qI, w, (const bf16_t *)kI, k_bs, scores,
+                       s_stride, scores2, hist);
+    return hipGetLastError();
+}
+
 template <typename T, int DI>
 static hipError_t launch_di(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const void *qI, const float *w,
                             const void *kI, int64_t k_bs, float *scores, int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
     if constexpr (sizeof(T) == 2) {
+        // many queries per sequence: the query-blocked kernel
+        if (Tq >= kPreMinQueries) {
+            if (HI <= 16) return launch_prefill<DI, 1>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride,
+                                                       scores2, hist, st);
+            if (HI <= 32) return launch_prefill<DI, 2>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride,
+                                                       scores2, hist, st);
+            return launch_prefill<DI, 4>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride, scores2, hist, st);
+        }
         if (HI <= 16) return launch_dma<DI, 1>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride, scores2,
                                                hist, st);
         if (HI <= 32) return launch_dma<DI, 2>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride, scores2,

@@ -115,6 +115,8 @@ SMALL = [
     ("csa_bf16_w1_h1", "bf16", 2, 4097, 2, 4, 512, 1, 1, 1000, 1, 32),
     ("csa_bf16_early_queries", "bf16", 1, 40, 40, 4, 128, 8, 3, 5, 4, 32),
     ("csa_bf16_big_row", "bf16", 1, 4 * 40000, 1, 4, 128, 16, 128, 1024, 64, 128),
+    ("csa_bf16_prefill_blocks", "bf16", 2, 2403, 100, 4, 128, 16, 8, 64, 20, 64),
+    ("csa_bf16_prefill_d32", "bf16", 1, 1000, 70, 4, 64, 8, 4, 50, 4, 32),
     ("hca_bf16_ragged", "bf16", 2, 128 * 77 + 5, 3, 128, 512, 64, 128, 0, 0, 0),
     ("hca_f32_m1_w0", "f32", 1, 150, 150, 1, 64, 4, 0, 0, 0, 0),
     ("hca_bf16_window_only", "bf16", 1, 100, 100, 128, 128, 64, 16, 0, 0, 0),
@@ -169,8 +171,9 @@ def test_topk_all_scores_equal(csa, n_entries, tq):
     assert np.array_equal(got[0, 0], np.arange(wl.k))
 
 
-def test_scores_out_and_masking(csa):
-    wl = Workload("scores", "bf16", B=2, T=4 * 700 + 3, Tq=5, m=4, d=128, H=16, W=4, k=64, HI=64, dI=128,
+@pytest.mark.parametrize("tq", [5, 80], ids=["few_queries", "query_blocked"])
+def test_scores_out_and_masking(csa, tq):
+    wl = Workload("scores", "bf16", B=2, T=4 * 700 + 3, Tq=tq, m=4, d=128, H=16, W=4, k=64, HI=64, dI=128,
                   seed_base=78000)
     say(wl)
     x = make_inputs(wl, "cuda")
