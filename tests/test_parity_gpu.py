@@ -117,7 +117,9 @@ SMALL = [
     ("csa_bf16_big_row", "bf16", 1, 4 * 40000, 1, 4, 128, 16, 128, 1024, 64, 128),
     ("csa_bf16_prefill_blocks", "bf16", 2, 2403, 100, 4, 128, 16, 8, 64, 20, 64),
     ("csa_bf16_prefill_d32", "bf16", 1, 1000, 70, 4, 64, 8, 4, 50, 4, 32),
+    ("csa_bf16_many_queries", "bf16", 2, 1300, 300, 4, 256, 8, 16, 40, 16, 32),
     ("hca_bf16_ragged", "bf16", 2, 128 * 77 + 5, 3, 128, 512, 64, 128, 0, 0, 0),
+    ("hca_bf16_many_queries", "bf16", 1, 128 * 10 + 600, 600, 128, 128, 16, 32, 0, 0, 0),
     ("hca_f32_m1_w0", "f32", 1, 150, 150, 1, 64, 4, 0, 0, 0, 0),
     ("hca_bf16_window_only", "bf16", 1, 100, 100, 128, 128, 64, 16, 0, 0, 0),
 ]
