@@ -430,7 +430,6 @@ __global__ __launch_bounds__(kPreWaves * 64) void k_index_prefill(int Tq, int N,
     const int64_t nv = on ? n_visible(q_pos0 + ti, m, N) : 0;
     // visible entries of the workgroup's last query bound every tile it computes
     const int64_t nv_max = n_visible(q_pos0 + min(q0 + kPreWaves, Tq) - 1, m, N);
-    const int tiles = (N + kPreRows - 1) / kPreRows;
     const int vtiles = (int)((nv_max + kPreRows - 1) / kPreRows);
 
     if (hist)
