@@ -16,6 +16,9 @@ checks argument shapes.  Every function follows the DeepSeek-V4 overview page
 * ``sparse_mqa``    -- step 3: shared-KV MQA over the selected entries plus a
                        window of recent raw tokens, one softmax.
 * ``dense_mqa``     -- section 2.3: the same attention over every visible entry.
+* ``mx4_quantize`` / ``mx4_dequantize`` -- the FP4 indexer operands (section 9,
+                       item 5), read as OCP MXFP4; the indexer then runs on the
+                       exact dequantised values.
 
 Parity-pin status of each function is listed in ``tests/test_oracle_pins.py``.
 """
@@ -66,8 +69,10 @@ def _load():
     lib.oracle_topk.argtypes = [I, I, I, I, I, L, P, P, I]
     lib.oracle_sparse_mqa.argtypes = [I, I, I, I, I, I, I, L, D, P, P, P, P, L, I, P, P, I]
     lib.oracle_dense_mqa.argtypes = [I, I, I, I, I, I, I, L, D, P, P, P, L, I, P, P, I]
+    lib.oracle_mx4_quantize.argtypes = [L, P, P, P]
+    lib.oracle_mx4_dequantize.argtypes = [L, P, P, P]
     for f in ("oracle_compress", "oracle_round_bf16", "oracle_index_scores", "oracle_topk",
-              "oracle_sparse_mqa", "oracle_dense_mqa"):
+              "oracle_sparse_mqa", "oracle_dense_mqa", "oracle_mx4_quantize", "oracle_mx4_dequantize"):
         getattr(lib, f).restype = None
     _lib = lib
     return lib
@@ -134,6 +139,33 @@ def index_scores(q_idx, w_idx, k_idx, m: int, q_pos0: int, nthreads: int | None 
     _load().oracle_index_scores(B, Tq, N, HI, dI, m, int(q_pos0), _ptr(q), _ptr(w), _ptr(k), _ptr(s),
                                 nthreads or default_threads())
     return s
+
+
+def mx4_quantize(x):
+    """MXFP4 of x [..., d] (d a multiple of 32) -> (codes uint8 [..., d/2], scales uint8 [..., d/32]).
+
+    OCP microscaling FP4: 32-element blocks with one E8M0 scale, E2M1 elements,
+    two codes per byte (even element in the low nibble); the reading of the
+    overview page's FP4 indexer operands (section 9, item 5)."""
+    x = _f32(x)
+    d = x.shape[-1]
+    assert d % 32 == 0
+    nb = x.size // 32
+    codes = np.empty(x.shape[:-1] + (d // 2,), dtype=np.uint8)
+    scales = np.empty(x.shape[:-1] + (d // 32,), dtype=np.uint8)
+    _load().oracle_mx4_quantize(nb, _ptr(x), _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def mx4_dequantize(codes, scales) -> np.ndarray:
+    """The exact values of MXFP4 codes [..., d/2] with scales [..., d/32] -> float32 [..., d]."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    d = codes.shape[-1] * 2
+    assert scales.shape[-1] * 32 == d and codes.shape[:-1] == scales.shape[:-1]
+    out = np.empty(codes.shape[:-1] + (d,), dtype=np.float32)
+    _load().oracle_mx4_dequantize(scales.size, _ptr(codes), _ptr(scales), _ptr(out))
+    return out
 
 
 def topk(scores: np.ndarray, k: int, m: int, q_pos0: int, nthreads: int | None = None) -> np.ndarray:

@@ -219,6 +219,80 @@ void oracle_index_scores(int B, int Tq, int N, int HI, int dI, int m, long q_pos
 }
 
 /* ------------------------------------------------------------------ */
+/* Low-precision indexer operands: MXFP4.                              */
+/* The overview page (section 9, summary of key innovations, item 5)   */
+/* quantises the indexer's queries and keys to FP4 without giving the  */
+/* block format.  The reading here is the OCP microscaling format      */
+/* MXFP4: every 32 consecutive elements share one E8M0 scale           */
+/* X = 2^(E - 127); the elements are FP4 E2M1 (a sign, 2 exponent bits */
+/* with bias 1, 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).*/
+/* Conversion of a block: X = 2^(floor(log2 max|v|) - 2), 2 being the  */
+/* largest E2M1 exponent, with the exponent kept inside E8M0's range   */
+/* [-127, 127]; each v / X goes to the nearest magnitude, a tie to the */
+/* one whose mantissa bit is 0, and magnitudes past 6 saturate to 6; a */
+/* negative v keeps its sign bit even when it rounds to zero.  A block */
+/* of zeros gets E = 0 and zero codes.  Two codes per byte, the even   */
+/* element in the low nibble.  Inputs must be finite.                  */
+/* ------------------------------------------------------------------ */
+static const double fp4_magnitude[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+/* nearest E2M1 code of v (already divided by the block scale) */
+static int fp4_code(double v) {
+    double a = fabs(v), best_err = INFINITY;
+    int best = 0, i;
+    for (i = 0; i < 8; i++) {
+        double err = fabs(a - fp4_magnitude[i]);
+        if (err < best_err || (err == best_err && (i & 1) == 0)) {
+            best_err = err;
+            best = i;
+        }
+    }
+    return (v < 0.0 ? 8 : 0) | best;
+}
+
+void oracle_mx4_quantize(long n_blocks, const float *x, uint8_t *codes, uint8_t *scales) {
+    long blk;
+    int i;
+    for (blk = 0; blk < n_blocks; blk++) {
+        const float *v = x + blk * 32;
+        uint8_t *cb = codes + blk * 16;
+        double amax = 0.0, X;
+        int se, ex;
+        for (i = 0; i < 32; i++)
+            if (fabs((double)v[i]) > amax) amax = fabs((double)v[i]);
+        if (amax == 0.0) {
+            scales[blk] = 0;
+            memset(cb, 0, 16);
+            continue;
+        }
+        (void)frexp(amax, &ex);  /* amax = f * 2^ex, 0.5 <= f < 1: floor(log2 amax) = ex - 1 */
+        se = ex - 1 - 2;
+        if (se < -127) se = -127;
+        if (se > 127) se = 127;
+        scales[blk] = (uint8_t)(se + 127);
+        X = ldexp(1.0, se);
+        for (i = 0; i < 32; i += 2) {
+            int lo = fp4_code((double)v[i] / X), hi = fp4_code((double)v[i + 1] / X);
+            cb[i / 2] = (uint8_t)(lo | (hi << 4));
+        }
+    }
+}
+
+/* the exact value of every element (representable in float) */
+void oracle_mx4_dequantize(long n_blocks, const uint8_t *codes, const uint8_t *scales, float *out) {
+    long blk;
+    int i;
+    for (blk = 0; blk < n_blocks; blk++) {
+        double X = ldexp(1.0, (int)scales[blk] - 127);
+        for (i = 0; i < 32; i++) {
+            int c = (codes[blk * 16 + i / 2] >> (4 * (i & 1))) & 15;
+            double mag = fp4_magnitude[c & 7] * X;
+            out[blk * 32 + i] = (float)((c & 8) ? -mag : mag);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
 /* Step 3: per-query top-k.                                            */
 /* Keep the k visible entries that come first in the total order       */
 /* (score descending, index ascending).  If n_visible <= k every       */

@@ -15,6 +15,13 @@ Pin status per oracle function:
   index_scores  -- pinned: numpy matmul + ReLU at one head, linearity in w,
                    head-permutation invariance, causal mask positions.
   topk          -- pinned: brute-force full sort, tie-heavy inputs, k >= n_visible.
+  mx4_quantize /
+  mx4_dequantize -- pinned: E2M1 values from the bit-field definition, E8M0
+                   scale as a power of two, exact round trip of representable
+                   blocks, brute-force nearest value with ties to the even
+                   mantissa, hand-checked ties and saturation, the block
+                   maximum landing on 4 or 6 (the scale exponent), power-of-two
+                   equivariance, zero blocks.
   sparse_mqa /
   dense_mqa     -- pinned: torch SDPA (causal MQA and banded window), scipy
                    softmax / logsumexp on basis rows, two-row closed form,
@@ -408,3 +415,99 @@ def test_csa_with_k_ge_visible_equals_hca(orc):
     b, lb = orc.dense_mqa(q, entries, raw, 0, m, W, q_pos0)
     np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-14)
     np.testing.assert_allclose(la, lb, rtol=1e-14)
+
+
+# ---------------------------------------------------------------- MXFP4
+def e2m1_from_bits(code):
+    """E2M1 by its bit fields: sign, 2 exponent bits (bias 1), 1 mantissa bit."""
+    s, e, mbit = (code >> 3) & 1, (code >> 1) & 3, code & 1
+    mag = (mbit / 2.0) if e == 0 else (2.0 ** (e - 1)) * (1.0 + mbit / 2.0)
+    return -mag if s else mag
+
+
+def pack_codes(codes):
+    codes = np.asarray(codes, dtype=np.uint8)
+    return (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+
+
+def test_mx4_element_values_from_bit_fields():
+    from oracle import mx4_dequantize
+    codes = np.arange(32, dtype=np.uint8) % 16
+    out = mx4_dequantize(pack_codes(codes)[None], np.array([[127]], dtype=np.uint8))[0]
+    np.testing.assert_array_equal(out, [e2m1_from_bits(int(c)) for c in codes])
+    assert sorted(set(abs(float(v)) for v in out)) == [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+
+
+def test_mx4_scale_is_a_power_of_two():
+    from oracle import mx4_dequantize
+    codes = pack_codes(np.full(32, 2, dtype=np.uint8))  # all 1.0
+    for E in (0, 1, 100, 127, 128, 254):
+        out = mx4_dequantize(codes[None], np.array([[E]], dtype=np.uint8))[0]
+        assert np.all(out == np.float32(math.ldexp(1.0, E - 127)))
+
+
+def test_mx4_representable_blocks_round_trip():
+    from oracle import mx4_dequantize, mx4_quantize
+    r = rng(71)
+    for trial in range(200):
+        e = int(r.integers(-20, 20))
+        codes = r.integers(0, 16, 32).astype(np.uint8)
+        codes[codes == 8] = 0                   # (a negative zero reads back as +0)
+        codes[int(r.integers(0, 32))] = int(r.choice([6, 7, 14, 15]))  # block maximum 4 or 6
+        x = mx4_dequantize(pack_codes(codes)[None], np.array([[127 + e]], dtype=np.uint8))
+        c2, s2 = mx4_quantize(x)
+        assert s2[0, 0] == 127 + e
+        np.testing.assert_array_equal(c2[0], pack_codes(codes))
+
+
+def test_mx4_nearest_value_brute_force():
+    from oracle import mx4_dequantize, mx4_quantize
+    r = rng(72)
+    grid = np.array([e2m1_from_bits(c) for c in range(16)])
+    x = (r.standard_normal((300, 32)) * np.exp(r.uniform(-6, 6, (300, 1)))).astype(np.float32)
+    codes, scales = mx4_quantize(x)
+    deq = mx4_dequantize(codes, scales).astype(np.float64)
+    X = np.ldexp(1.0, scales.astype(np.int64) - 127)
+    for b in range(x.shape[0]):
+        cand = grid * X[b, 0]
+        for i in range(32):
+            err = np.abs(cand - float(x[b, i]))
+            best = err.min()
+            ok = [c for c in range(16) if err[c] == best]
+            even = [c for c in ok if c % 2 == 0]
+            pick = even if even else ok
+            assert any(cand[c] == deq[b, i] for c in pick), (b, i, x[b, i], deq[b, i])
+
+
+def test_mx4_hand_checked_ties_and_saturation():
+    from oracle import mx4_dequantize, mx4_quantize
+    vals = [6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -2.5, 7.0, 0.0]
+    want = [6.0, 0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, -0.0, -2.0, 6.0, 0.0]
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, :len(vals)] = vals
+    codes, scales = mx4_quantize(x)
+    assert scales[0, 0] == 127  # max 7.0: floor(log2 7) - 2 = 0
+    out = mx4_dequantize(codes, scales)[0, :len(vals)]
+    np.testing.assert_array_equal(out, np.array(want, dtype=np.float32))
+    assert (codes[0, 4] & 15) == 8  # -0.25 keeps its sign bit
+
+
+def test_mx4_block_maximum_lands_on_four_or_six_and_equivariance():
+    from oracle import mx4_dequantize, mx4_quantize
+    r = rng(73)
+    x = (r.standard_normal((200, 32)) * np.exp(r.uniform(-8, 8, (200, 1)))).astype(np.float32)
+    codes, scales = mx4_quantize(x)
+    deq = mx4_dequantize(codes, scales).astype(np.float64)
+    X = np.ldexp(1.0, scales.astype(np.int64) - 127)
+    top = np.abs(deq).max(axis=1) / X[:, 0]
+    assert set(np.unique(top)) <= {4.0, 6.0}
+    for k in (-5, 3):
+        c2, s2 = mx4_quantize(x * np.float32(2.0 ** k))
+        np.testing.assert_array_equal(c2, codes)
+        np.testing.assert_array_equal(s2.astype(int), scales.astype(int) + k)
+
+
+def test_mx4_zero_block():
+    from oracle import mx4_quantize
+    codes, scales = mx4_quantize(np.zeros((2, 64), dtype=np.float32))
+    assert np.all(codes == 0) and np.all(scales == 0)
