@@ -42,6 +42,18 @@ hipError_t launch_index_scores(int dt, int B, int Tq, int N, int HI, int dI, int
                                const float *w, const void *kI, int64_t k_bs, float *scores, int64_t s_stride,
                                float *scores2, uint32_t *hist, hipStream_t st);
 
+// MXFP4 operands (32-element blocks, one E8M0 scale byte each, E2M1 codes two
+// per byte): quantise n_blocks blocks of x (dt elements) into codes
+// [n_blocks][16] and scales [n_blocks]
+hipError_t launch_mx4_quantize(int dt, int64_t n_blocks, const void *x, uint8_t *codes, uint8_t *scales,
+                               hipStream_t st);
+// the indexer on MXFP4 queries (codes [rows, HI, dI/2], scales [rows, HI, dI/32])
+// and keys (codes [B][k_bs rows][dI/2], scales [B][k_bs rows][dI/32]); outputs
+// as launch_index_scores
+hipError_t launch_index_mx4(int B, int Tq, int N, int HI, int dI, int m, int64_t q_pos0, const uint8_t *qc,
+                            const uint8_t *qs, const float *w, const uint8_t *kc, const uint8_t *ks, int64_t k_bs,
+                            float *scores, int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st);
+
 // row stride of the score rows the top-k reads: N rounded up to 64 floats, so
 // every row starts 256-byte aligned and 16-byte loads never leave the row
 constexpr int64_t topk_score_stride(int64_t N) { return (N + 63) / 64 * 64; }

@@ -1,0 +1,247 @@
+// FP4 operands of the lightning indexer (DeepSeek-V4 overview page, section
+// 9, summary of key innovations, item 5: the indexer's queries and keys are
+// quantised to FP4).  The block format is OCP MXFP4, the format gfx950's
+// scaled MFMA consumes: 32 consecutive elements share one E8M0 scale
+// X = 2^(E - 127), each element is FP4 E2M1 (magnitudes 0, 0.5, 1, 1.5, 2,
+// 3, 4, 6), two codes per byte with the even element in the low nibble.
+//
+// k_mx4_quantize: one thread per 32-element block.  X = 2^(floor(log2 max|v|)
+// - 2) with the exponent kept inside [-127, 127]; v / X (exact: a power-of-two
+// scaling) rounds to the nearest magnitude, ties to the even mantissa,
+// saturating at 6, written as a sum of threshold tests (strict at the ties
+// that round down, inclusive at the ties that round up); the sign bit is set
+// for v < 0.  A block of zeros gets E = 0.
+//
+// k_index_mx4: the decode indexer of indexer.hip with FP4 operands.  A query's
+// entries are read in batches of 16-entry tiles dealt round-robin to its
+// wavefronts; one v_mfma_scale_f32_16x16x128_f8f6f4 per 16 heads x 16 entries
+// covers all of d_I = 128 (lane l holds 32 consecutive K values of row / column
+// l % 16, block l / 16, with that block's scale byte), so each tile is one
+// 16-byte load per lane (the tile's 16 rows of 64 code bytes, contiguous) and
+// one scale-byte load.  The epilogue is the bf16 kernel's: ReLU, head weight,
+// head sum across the lane groups, score store and the first top-k digit.
+#include "kernels.h"
+
+namespace csa {
+
+typedef int int32x8 __attribute__((ext_vector_type(8)));
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_mx4_quantize(int64_t n_blocks, const T *__restrict__ x,
+                                                      uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
+    const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (blk >= n_blocks) return;
+    float v[32];
+    const T *src = x + blk * 32;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = Elem<T>::to_f32(src[i]);
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    u32x4 packed = {0u, 0u, 0u, 0u};
+    uint32_t e8 = 0;
+    if (amax > 0.f) {
+        int ex;
+        (void)frexpf(amax, &ex);  // amax = f * 2^ex, 0.5 <= f < 1: floor(log2 amax) = ex - 1
+        int se = ex - 1 - 2;
+        se = se < -127 ? -127 : (se > 127 ? 127 : se);
+        e8 = (uint32_t)(se + 127);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const float y = ldexpf(v[i], -se);
+            const float a = fabsf(y);
+            uint32_t code = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                            (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                            (uint32_t)(a > 5.f);
+            if (v[i] < 0.f) code |= 8u;
+            packed[i / 8] |= code << (4 * (i % 8));
+        }
+    }
+    *(u32x4 *)(codes + blk * 16) = packed;
+    scales[blk] = (uint8_t)e8;
+}
+
+template <int DI, int MB>
+__global__ __launch_bounds__(256) void k_index_mx4(int Tq, int N, int HI, int m, int64_t q_pos0, int64_t n_items,
+                                                   int chunks_per_row, const uint8_t *__restrict__ qc,
+                                                   const uint8_t *__restrict__ qs, const float *__restrict__ w,
+                                                   const uint8_t *__restrict__ kc, const uint8_t *__restrict__ ks,
+                                                   int64_t k_bs, float *__restrict__ scores, int64_t s_stride,
+                                                   float *__restrict__ scores2, uint32_t *__restrict__ hist) {
+    constexpr int KB = DI / 32;  // 32-element blocks per row
+    constexpr int RB = DI / 2;   // code bytes per row
+    constexpr int UNROLL = 8;    // tiles per batch
+    constexpr int BATCH = 16 * UNROLL;
+    __shared__ uint32_t whist[4][kTopkBins];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t item = (int64_t)blockIdx.x * 4 + wv;
+    if (hist) {
+        for (int i = lane; i < kTopkBins; i += 64) whist[wv][i] = 0;
+    }
+    if (item >= n_items) return;
+    const int64_t row = item / chunks_per_row;
+    const int chunk = (int)(item % chunks_per_row);
+    const int64_t b = row / Tq, ti = row % Tq;
+    const int64_t nv = n_visible(q_pos0 + ti, m, N);
+    const int g = lane >> 4, c = lane & 15;
+    const bool kon = g < KB;  // lanes that hold a K block (d_I < 128 leaves the rest zero)
+
+    // the query's index heads (A operand) with their block scales, and head weights
+    int32x8 a[MB];
+    int as[MB];
+    float wgt[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int head = mb * 16 + c;
+        const int64_t hr = row * HI + min(head, HI - 1);
+        u32x4 v = {0u, 0u, 0u, 0u};
+        int sc = 127;
+        if (kon && head < HI) {
+            v = *(const u32x4 *)(qc + hr * RB + g * 16);
+            sc = qs[hr * KB + g];
+        }
+        a[mb] = int32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        as[mb] = sc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int hh = mb * 16 + 4 * g + e;
+            const float wv_ = w[row * HI + min(hh, HI - 1)];
+            wgt[mb][e] = hh < HI ? wv_ : 0.f;
+        }
+    }
+
+    const uint8_t *kcb = kc + b * k_bs * RB + (kon ? g : 0) * 16;
+    const uint8_t *ksb = ks + b * k_bs * KB + (kon ? g : 0);
+    float *srow = scores + row * s_stride;
+    float *srow2 = scores2 ? scores2 + row * (int64_t)N : nullptr;
+    // the row's batches are dealt round-robin to its chunks_per_row waves
+    const int64_t j_lo = (int64_t)chunk * BATCH;
+    const int64_t j_hi = N;
+    const int64_t jstep = (int64_t)chunks_per_row * BATCH;
+
+    if (nv == 0) {  // nothing visible: the wave's batches are all -inf
+        for (int64_t j0 = j_lo; j0 < j_hi; j0 += jstep)
+            for (int64_t j = j0 + lane; j < min(j0 + BATCH, j_hi); j += 64) {
+                srow[j] = -INFINITY;
+                if (srow2) srow2[j] = -INFINITY;
+            }
+    } else {
+        // one batch: UNROLL tiles of 16 keys.  Loads are unconditional (lanes
+        // past the visible entries reread the last visible row) so the
+        // compiler can wait for exactly one batch.
+        const int64_t j_last = nv - 1;
+        auto load_batch = [&](int64_t j0, u32x4 (&kd)[UNROLL], int (&kx)[UNROLL]) {
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                int64_t jr = j0 + u * 16 + c;
+                jr = jr < j_last ? jr : j_last;
+                kd[u] = __builtin_nontemporal_load((const u32x4 *)(kcb + jr * RB));
+                kx[u] = ksb[jr * KB];
+            }
+        };
+        auto score_batch = [&](int64_t j0, const u32x4 (&kd)[UNROLL], const int (&kx)[UNROLL]) {
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int64_t j = j0 + u * 16 + c;
+                const u32x4 z = kon ? kd[u] : u32x4{0u, 0u, 0u, 0u};
+                const int32x8 bk = {(int)z[0], (int)z[1], (int)z[2], (int)z[3], 0, 0, 0, 0};
+                const int bs = kon ? kx[u] : 127;
+                float s = 0.f;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const floatx4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        a[mb], bk, floatx4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, as[mb], 0, bs);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s += wgt[mb][e] * fmaxf(acc[e], 0.f);
+                }
+                s += __shfl_xor(s, 16);
+                s += __shfl_xor(s, 32);
+                if (g == 0 && j < j_hi) {
+                    srow[j] = j < nv ? s : -INFINITY;
+                    if (srow2) srow2[j] = j < nv ? s : -INFINITY;
+                }
+                if (hist && g == 0 && j < j_hi && j < nv)
+                    atomicAdd(&whist[wv][order_key(s) >> (32 - kTopkBinBits)], 1u);
+            }
+        };
+        // double-buffered: the next batch is in flight while this one is scored
+        u32x4 d0[UNROLL], d1[UNROLL];
+        int x0[UNROLL], x1[UNROLL];
+        if (j_lo < j_hi) load_batch(j_lo, d0, x0);
+        for (int64_t j0 = j_lo; j0 < j_hi; j0 += 2 * jstep) {
+            load_batch(j0 + jstep, d1, x1);
+            score_batch(j0, d0, x0);
+            load_batch(j0 + 2 * jstep, d0, x0);
+            if (j0 + jstep < j_hi) score_batch(j0 + jstep, d1, x1);
+        }
+    }
+    if (hist) {
+        // LDS operations of one wave complete in order: the counts are final here
+        uint32_t *grow = hist + row * kTopkBins;
+        for (int i = lane; i < kTopkBins; i += 64) {
+            const uint32_t v = whist[wv][i];
+            if (v) atomicAdd(&grow[i], v);
+        }
+    }
+}
+
+hipError_t launch_mx4_quantize(int dt, int64_t n_blocks, const void *x, uint8_t *codes, uint8_t *scales,
+                               hipStream_t st) {
+    if (n_blocks <= 0) return hipSuccess;
+    const unsigned grid = (unsigned)((n_blocks + 255) / 256);
+    if (dt == 0)
+        hipLaunchKernelGGL(k_mx4_quantize<float>, dim3(grid), dim3(256), 0, st, n_blocks, (const float *)x, codes,
+                           scales);
+    else
+        hipLaunchKernelGGL(k_mx4_quantize<bf16_t>, dim3(grid), dim3(256), 0, st, n_blocks, (const bf16_t *)x, codes,
+                           scales);
+    return hipGetLastError();
+}
+
+template <int DI, int MB>
+static hipError_t launch_mx4_t(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const uint8_t *qc,
+                               const uint8_t *qs, const float *w, const uint8_t *kc, const uint8_t *ks, int64_t k_bs,
+                               float *scores, int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
+    const int64_t rows = (int64_t)B * Tq;
+    const int64_t batches = (N + 127) / 128;  // batches of eight 16-entry tiles
+    // aim for ~2048 wavefronts in flight (8 per CU) when there are few queries
+    int64_t chunks = (2048 + rows - 1) / rows;
+    if (chunks > batches) chunks = batches;
+    if (chunks < 1) chunks = 1;
+    const int64_t items = rows * chunks;
+    const int64_t blocks = (items + 3) / 4;
+    hipLaunchKernelGGL((k_index_mx4<DI, MB>), dim3((unsigned)blocks), dim3(256), 0, st, Tq, N, HI, m, q_pos0, items,
+                       (int)chunks, qc, qs, w, kc, ks, k_bs, scores, s_stride, scores2, hist);
+    return hipGetLastError();
+}
+
+template <int DI>
+static hipError_t launch_mx4_di(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const uint8_t *qc,
+                                const uint8_t *qs, const float *w, const uint8_t *kc, const uint8_t *ks, int64_t k_bs,
+                                float *scores, int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
+    if (HI <= 16)
+        return launch_mx4_t<DI, 1>(B, Tq, N, HI, m, q_pos0, qc, qs, w, kc, ks, k_bs, scores, s_stride, scores2, hist,
+                                   st);
+    if (HI <= 32)
+        return launch_mx4_t<DI, 2>(B, Tq, N, HI, m, q_pos0, qc, qs, w, kc, ks, k_bs, scores, s_stride, scores2, hist,
+                                   st);
+    return launch_mx4_t<DI, 4>(B, Tq, N, HI, m, q_pos0, qc, qs, w, kc, ks, k_bs, scores, s_stride, scores2, hist, st);
+}
+
+hipError_t launch_index_mx4(int B, int Tq, int N, int HI, int dI, int m, int64_t q_pos0, const uint8_t *qc,
+                            const uint8_t *qs, const float *w, const uint8_t *kc, const uint8_t *ks, int64_t k_bs,
+                            float *scores, int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
+    switch (dI) {
+        case 32:
+            return launch_mx4_di<32>(B, Tq, N, HI, m, q_pos0, qc, qs, w, kc, ks, k_bs, scores, s_stride, scores2,
+                                     hist, st);
+        case 64:
+            return launch_mx4_di<64>(B, Tq, N, HI, m, q_pos0, qc, qs, w, kc, ks, k_bs, scores, s_stride, scores2,
+                                     hist, st);
+        default:
+            return launch_mx4_di<128>(B, Tq, N, HI, m, q_pos0, qc, qs, w, kc, ks, k_bs, scores, s_stride, scores2,
+                                      hist, st);
+    }
+}
+
+}  // namespace csa

@@ -21,14 +21,14 @@ def header_functions():
     with open(os.path.join(ROOT, "include", "csa.h")) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b((?:csa|hca)_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:csa|hca)_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(L):
     import long_context_compressed_06_amd as csa
 
     names = header_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(L, n), n
     assert sorted(csa.EXPORTS) == names
@@ -125,3 +125,33 @@ def test_mqa_workspace_sizes(L):
     # decode at batch 32 over 1152 rows: split-K partials of (d + 2) floats per head
     n = L.csa_mqa_workspace_bytes(32, 1, 64, 512, 1152)
     assert n > 0 and n % 256 == 0 and n % (32 * 64 * 514 * 4) < 256
+
+
+def test_mx4_calls_reject_bad_arguments(L):
+    import long_context_compressed_06_amd as csa
+
+    L.csa_mx4_quantize.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int] + [ctypes.c_void_p] * 4
+    assert L.csa_mx4_quantize(1, 4, 48, P, P + 0x10000, P + 0x20000, None) == -6   # d not a multiple of 32
+    assert L.csa_mx4_quantize(7, 4, 64, P, P + 0x10000, P + 0x20000, None) == -2   # element type
+    assert L.csa_mx4_quantize(1, 4, 64, P + 4, P + 0x10000, P + 0x20000, None) == -3  # alignment
+    assert L.csa_mx4_quantize(1, 4, 64, P, P + 16, P + 0x20000, None) == -1  # codes overlap x
+    assert L.csa_mx4_quantize(1, 0, 64, None, None, None, None) == 0        # nothing to do
+    f = csa.lib().csa_index_topk_mx4
+    ws = csa.index_topk_workspace_bytes(1, 1, 256, 64, 64)
+    args = dict(B=1, Tq=1, N=256, HI=64, dI=128, m=4, k=64, q0=1023, qc=P, qs=P + 0x10000, w=P + 0x20000,
+                kc=P + 0x30000, ks=P + 0x40000, kbs=256, idx=P + 0x50000, so=None, ws=P + 0x100000, wsb=ws)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["B"], a["Tq"], a["N"], a["HI"], a["dI"], a["m"], a["k"], a["q0"], a["qc"], a["qs"], a["w"],
+                 a["kc"], a["ks"], a["kbs"], a["idx"], a["so"], a["ws"], a["wsb"], None)
+
+    assert call(dI=96) == -6
+    assert call(HI=65) == -6
+    assert call(k=0) == -6
+    assert call(kbs=255) == -1
+    assert call(kc=P + 0x30004) == -3
+    assert call(wsb=ws - 1) == -4
+    assert call(idx=P + 0x30000) == -1   # output overlaps the key codes
+    assert call(qc=None) == -1
+    assert call(B=0) == 0
