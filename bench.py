@@ -49,7 +49,15 @@ def algorithmic_bytes(wl) -> dict:
         n_win = min(wl.W, t + 1)
         q = wl.H * wl.d * es
         out = wl.H * wl.d * 4
-        if wl.mode == "csa":
+        if wl.mode == "csa" and wl.index_fmt == "mx4":
+            # FP4 keys and queries: dI/2 code bytes + dI/32 scale bytes per row; the
+            # bf16 index queries are read once by the quantiser
+            row4 = wl.dI // 2 + wl.dI // 32
+            ki = nv * row4 + wl.HI * (row4 + wl.dI * es) + wl.HI * 4
+            idx_kernel += ki
+            rows = (min(wl.k, nv) + n_win) * wl.d * es
+            step += ki + wl.HI * row4 + rows + q + out + 2 * wl.k * 4
+        elif wl.mode == "csa":
             ki = nv * wl.dI * es + wl.HI * wl.dI * es + wl.HI * 4
             idx_kernel += ki
             rows = (min(wl.k, nv) + n_win) * wl.d * es
@@ -140,6 +148,11 @@ def bench_workload(wl, steps, warmup, with_kernel=True):
     from workloads import make_inputs
 
     x0 = make_inputs(wl, "cuda")
+    if wl.index_fmt == "mx4":
+        # the cache holds the keys' FP4 form (quantised when they entered it)
+        csa.AttentionStep.quantize_index_keys(x0)
+        del x0["k_idx"]
+        torch.cuda.synchronize()
     R = replicas_for(x0)
     xs = [x0] + [clone_inputs(x0) for _ in range(R - 1)]
     steps_ = [csa.AttentionStep.for_workload(wl) for _ in xs]
@@ -151,7 +164,7 @@ def bench_workload(wl, steps, warmup, with_kernel=True):
     multi = capture(lambda: [s(x) for s, x in zip(steps_, xs)])
     ms = time_graphs(graphs, steps, warmup, multi, R)
     res = {"ms_per_step": ms, "replicas": R}
-    if with_kernel and wl.mode == "csa":
+    if with_kernel and wl.mode == "csa" and wl.index_fmt == "elem":
         # the lightning indexer alone, same launch configuration, 8 launches per
         # graph over the replicas, timed with HIP events on the stream it runs on
         sc = [torch.empty((wl.B, wl.Tq, wl.N), dtype=torch.float32, device="cuda") for _ in xs]
@@ -199,7 +212,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2", help="c2 (default), c3 or c5")
-    ap.add_argument("--also", default="c3,c5", help="secondary decode workloads ('' for none)")
+    ap.add_argument("--also", default="c3,c5,c2x,c5x",
+                    help="secondary decode workloads ('' for none); c2x/c5x: FP4 (MXFP4) indexer operands")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for the HBM byte counters)")

@@ -149,7 +149,7 @@ int csa_index_scores(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int6
  * csa_mx4_quantize -- codes and scales of n_rows rows of d elements (d a
  * multiple of 32).  Per block: E = 127 + clamp(floor(log2 max|v|) - 2, -127,
  * 127); each v / 2^(E-127) goes to the nearest E2M1 magnitude, ties to the even
- * mantissa, magnitudes beyond 6 saturate to 6; the sign bit is set for v < 0.
+ * mantissa, magnitudes beyond 6 saturate to 6; the sign bit is v's sign bit.
  * A block of zeros gets E = 0 and zero codes.  Inputs must be finite.
  *   x       [n_rows, d]      dt (dense)
  *   codes   [n_rows, d/2]    uint8 (output, dense)
@@ -160,20 +160,23 @@ int csa_mx4_quantize(int dt, int64_t n_rows, int d, const void *x,
                      uint8_t *codes, uint8_t *scales, void *stream);
 
 /*
- * csa_index_topk_mx4 -- csa_index_topk with MXFP4 index queries and keys: the
- * scores are the same formula on the exact values the codes and scales stand
- * for, accumulated in float32.
- *   q_codes   [B, Tq, H_I, d_I/2]   uint8     q_scales [B, Tq, H_I, d_I/32] uint8
+ * csa_index_topk_mx4 -- csa_index_topk with MXFP4 index operands: the index
+ * queries arrive in the element type dt and are quantised inside the call
+ * exactly as csa_mx4_quantize does; the keys arrive as MXFP4 codes and scales
+ * (quantised once, when they entered the cache).  The scores are the same
+ * formula on the exact values the codes and scales stand for, accumulated in
+ * float32.
+ *   q_idx     [B, Tq, H_I, d_I]     dt
  *   w_idx     [B, Tq, H_I]          f32
- *   k_codes   [B, N, d_I/2]         uint8     k_scales [B, N, d_I/32]       uint8
+ *   k_codes   [B, N, d_I/2]         uint8     k_scales [B, N, d_I/32]  uint8
  *             both with a batch stride of k_bstride ROWS (entries)
  *   topk_idx, scores_out, workspace: as csa_index_topk, with the same
  *             workspace size (csa_index_topk_workspace_bytes).
- * q_codes and k_codes 16-byte aligned.  d_I in {32, 64, 128}.
+ * q_idx and k_codes 16-byte aligned.  d_I in {32, 64, 128}.
  */
-int csa_index_topk_mx4(int B, int Tq, int N, int H_I, int d_I, int m, int k,
+int csa_index_topk_mx4(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k,
                        int64_t q_pos0,
-                       const uint8_t *q_codes, const uint8_t *q_scales, const float *w_idx,
+                       const void *q_idx, const float *w_idx,
                        const uint8_t *k_codes, const uint8_t *k_scales, int64_t k_bstride,
                        int32_t *topk_idx, float *scores_out,
                        void *workspace, size_t workspace_bytes, void *stream);

@@ -64,7 +64,7 @@ def lib():
     L.hca_dense_mqa.restype = I
     L.csa_mx4_quantize.argtypes = [I, I64, I, P, P, P, P]
     L.csa_mx4_quantize.restype = I
-    L.csa_index_topk_mx4.argtypes = [I, I, I, I, I, I, I, I64, P, P, P, P, P, I64, P, P, P, SZ, P]
+    L.csa_index_topk_mx4.argtypes = [I, I, I, I, I, I, I, I, I64, P, P, P, P, I64, P, P, P, SZ, P]
     L.csa_index_topk_mx4.restype = I
     _lib = L
     return L
@@ -193,29 +193,28 @@ def csa_mx4_quantize(x: torch.Tensor, codes=None, scales=None):
     return codes, scales
 
 
-def csa_index_topk_mx4(q_codes, q_scales, w_idx, k_codes, k_scales, N: int, m: int, k: int, q_pos0: int,
-                       topk_idx=None, scores_out=None, workspace=None) -> torch.Tensor:
-    """MXFP4 indexer + top-k.  q_codes [B,Tq,H_I,d_I/2], q_scales [B,Tq,H_I,d_I/32], w_idx [B,Tq,H_I] f32,
-    k_codes [B,cap,d_I/2], k_scales [B,cap,d_I/32] (first N rows used) -> topk_idx [B,Tq,k] int32."""
-    _need(q_codes, "q_codes", torch.uint8, 4)
-    _need(q_scales, "q_scales", torch.uint8, 4)
+def csa_index_topk_mx4(q_idx, w_idx, k_codes, k_scales, N: int, m: int, k: int, q_pos0: int, topk_idx=None,
+                       scores_out=None, workspace=None) -> torch.Tensor:
+    """FP4 (MXFP4) indexer + top-k.  q_idx [B,Tq,H_I,d_I] (f32/bf16, quantised inside the call), w_idx
+    [B,Tq,H_I] f32, k_codes [B,cap,d_I/2], k_scales [B,cap,d_I/32] (first N rows used) -> topk_idx [B,Tq,k]."""
+    _need(q_idx, "q_idx", dims=4)
     _need(w_idx, "w_idx", torch.float32, 3)
     _need(k_codes, "k_codes", torch.uint8, 3)
     _need(k_scales, "k_scales", torch.uint8, 3)
-    B, Tq, HI, rb = q_codes.shape
-    dI = rb * 2
-    if (q_scales.shape != (B, Tq, HI, dI // 32) or w_idx.shape != (B, Tq, HI) or k_codes.shape[2] != rb
-            or k_scales.shape[:2] != k_codes.shape[:2] or k_scales.shape[2] != dI // 32):
-        raise ValueError("shape mismatch between the MXFP4 operands")
-    if not (q_codes.is_contiguous() and q_scales.is_contiguous() and w_idx.is_contiguous()):
-        raise ValueError("q_codes, q_scales and w_idx must be contiguous")
+    B, Tq, HI, dI = q_idx.shape
+    rb = dI // 2
+    if (w_idx.shape != (B, Tq, HI) or k_codes.shape[2] != rb or k_scales.shape[:2] != k_codes.shape[:2]
+            or k_scales.shape[2] != dI // 32):
+        raise ValueError("shape mismatch between the index operands")
+    if not (q_idx.is_contiguous() and w_idx.is_contiguous()):
+        raise ValueError("q_idx and w_idx must be contiguous")
     if k_codes.stride(1) != rb or k_scales.stride(1) != dI // 32 or k_codes.shape[1] < N:
         raise ValueError("k_codes / k_scales rows must be packed, with >= N rows")
     cap = k_codes.stride(0) // rb
     if k_codes.stride(0) != cap * rb or k_scales.stride(0) != cap * (dI // 32):
         raise ValueError("k_codes and k_scales must share one batch stride in rows")
     if topk_idx is None:
-        topk_idx = torch.empty((B, Tq, k), dtype=torch.int32, device=q_codes.device)
+        topk_idx = torch.empty((B, Tq, k), dtype=torch.int32, device=q_idx.device)
     _need(topk_idx, "topk_idx", torch.int32, 3)
     if scores_out is not None:
         _need(scores_out, "scores_out", torch.float32, 3)
@@ -223,11 +222,11 @@ def csa_index_topk_mx4(q_codes, q_scales, w_idx, k_codes, k_scales, N: int, m: i
             raise ValueError("scores_out must be a contiguous [B, Tq, N] tensor")
     need = index_topk_workspace_bytes(B, Tq, N, HI, k)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q_codes.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_idx.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().csa_index_topk_mx4(B, Tq, N, HI, dI, m, k, q_pos0, _p(q_codes), _p(q_scales), _p(w_idx),
-                                    _p(k_codes), _p(k_scales), cap, _p(topk_idx), _p(scores_out), _p(workspace),
-                                    ws_bytes, _stream(q_codes)))
+    _check(lib().csa_index_topk_mx4(_dt(q_idx), B, Tq, N, HI, dI, m, k, q_pos0, _p(q_idx), _p(w_idx), _p(k_codes),
+                                    _p(k_scales), cap, _p(topk_idx), _p(scores_out), _p(workspace), ws_bytes,
+                                    _stream(q_idx)))
     return topk_idx
 
 

@@ -203,10 +203,11 @@ int csa_mx4_quantize(int dt, int64_t n_rows, int d, const void *x, uint8_t *code
                       "quantise launch");
 }
 
-int csa_index_topk_mx4(int B, int Tq, int N, int H_I, int d_I, int m, int k, int64_t q_pos0, const uint8_t *q_codes,
-                       const uint8_t *q_scales, const float *w_idx, const uint8_t *k_codes, const uint8_t *k_scales,
+int csa_index_topk_mx4(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k, int64_t q_pos0,
+                       const void *q_idx, const float *w_idx, const uint8_t *k_codes, const uint8_t *k_scales,
                        int64_t k_bstride, int32_t *topk_idx, float *scores_out, void *workspace,
                        size_t workspace_bytes, void *stream) {
+    if (int s = check_dt(dt)) return s;
     if (B < 0 || Tq < 0 || N < 0) return fail(CSA_EINVAL, "B, Tq and N must be >= 0");
     if (H_I < 1 || H_I > 64) return fail(CSA_EUNSUPPORTED, "H_I=%d outside 1..64", H_I);
     if (!dI_supported(d_I)) return fail(CSA_EUNSUPPORTED, "d_I=%d not in {32,64,128}", d_I);
@@ -215,12 +216,12 @@ int csa_index_topk_mx4(int B, int Tq, int N, int H_I, int d_I, int m, int k, int
     if (q_pos0 < 0) return fail(CSA_EINVAL, "q_pos0 must be >= 0");
     if (N > csa::kTopkMaxEntries) return fail(CSA_EUNSUPPORTED, "N=%d above %lld entries", N, (long long)csa::kTopkMaxEntries);
     if ((int64_t)B * Tq == 0) return ok();
-    if (!q_codes || !q_scales || !w_idx || !topk_idx || (N > 0 && (!k_codes || !k_scales)))
+    if (!q_idx || !w_idx || !topk_idx || (N > 0 && (!k_codes || !k_scales)))
         return fail(CSA_EINVAL, "NULL tensor pointer");
     if (N > 0 && k_bstride < N) return fail(CSA_EINVAL, "k_bstride smaller than N rows");
-    if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(w_idx, 4) || !aligned(topk_idx, 4) ||
+    if (!aligned(q_idx, 16) || !aligned(k_codes, 16) || !aligned(w_idx, 4) || !aligned(topk_idx, 4) ||
         !aligned(scores_out, 4))
-        return fail(CSA_EALIGN, "q_codes/k_codes need 16-byte alignment");
+        return fail(CSA_EALIGN, "q_idx/k_codes need 16-byte alignment");
     const int64_t rows = (int64_t)B * Tq;
     const size_t need = csa_index_topk_workspace_bytes(B, Tq, N, H_I, k);
     if (!workspace || workspace_bytes < need)
@@ -229,8 +230,8 @@ int csa_index_topk_mx4(int B, int Tq, int N, int H_I, int d_I, int m, int k, int
     const int64_t rb = d_I / 2, kb = d_I / 32;
     const Span si = span(topk_idx, B, (int64_t)Tq * k, (int64_t)Tq * k, 4);
     const Span ss = span(scores_out, B, (int64_t)Tq * N, (int64_t)Tq * N, 4);
-    const Span inputs[5] = {span(q_codes, 1, 0, rows * H_I * rb, 1), span(q_scales, 1, 0, rows * H_I * kb, 1),
-                            span(w_idx, 1, 0, rows * H_I, 4), span(k_codes, B, k_bstride * rb, (int64_t)N * rb, 1),
+    const Span inputs[4] = {span(q_idx, 1, 0, rows * H_I * d_I, esize(dt)), span(w_idx, 1, 0, rows * H_I, 4),
+                            span(k_codes, B, k_bstride * rb, (int64_t)N * rb, 1),
                             span(k_scales, B, k_bstride * kb, (int64_t)N * kb, 1)};
     const Span sw = span(workspace, 1, 0, (int64_t)need, 1);
     for (const Span &in : inputs)
@@ -245,9 +246,9 @@ int csa_index_topk_mx4(int B, int Tq, int N, int H_I, int d_I, int m, int k, int
         if (int s = hip_status(csa::launch_fill_u32(scratch, (int64_t)csa::topk_clear_words(rows, N), 0u, st),
                                "histogram clear"))
             return s;
-        if (int s = hip_status(csa::launch_index_mx4(B, Tq, N, H_I, d_I, m, q_pos0, q_codes, q_scales, w_idx,
-                                                      k_codes, k_scales, k_bstride, scores,
-                                                      csa::topk_score_stride(N), scores_out, scratch, st),
+        if (int s = hip_status(csa::launch_index_mx4(dt, B, Tq, N, H_I, d_I, m, q_pos0, q_idx, w_idx, k_codes,
+                                                      k_scales, k_bstride, scores, csa::topk_score_stride(N),
+                                                      scores_out, scratch, st),
                                "indexer launch"))
             return s;
     }

@@ -47,12 +47,12 @@ hipError_t launch_index_scores(int dt, int B, int Tq, int N, int HI, int dI, int
 // [n_blocks][16] and scales [n_blocks]
 hipError_t launch_mx4_quantize(int dt, int64_t n_blocks, const void *x, uint8_t *codes, uint8_t *scales,
                                hipStream_t st);
-// the indexer on MXFP4 queries (codes [rows, HI, dI/2], scales [rows, HI, dI/32])
-// and keys (codes [B][k_bs rows][dI/2], scales [B][k_bs rows][dI/32]); outputs
-// as launch_index_scores
-hipError_t launch_index_mx4(int B, int Tq, int N, int HI, int dI, int m, int64_t q_pos0, const uint8_t *qc,
-                            const uint8_t *qs, const float *w, const uint8_t *kc, const uint8_t *ks, int64_t k_bs,
-                            float *scores, int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st);
+// the indexer on MXFP4 operands: queries qI [rows, HI, dI] in element type dt,
+// quantised inside the kernel; keys as codes [B][k_bs rows][dI/2] and scales
+// [B][k_bs rows][dI/32]; outputs as launch_index_scores
+hipError_t launch_index_mx4(int dt, int B, int Tq, int N, int HI, int dI, int m, int64_t q_pos0, const void *qI,
+                            const float *w, const uint8_t *kc, const uint8_t *ks, int64_t k_bs, float *scores,
+                            int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st);
 
 // row stride of the score rows the top-k reads: N rounded up to 64 floats, so
 // every row starts 256-byte aligned and 16-byte loads never leave the row

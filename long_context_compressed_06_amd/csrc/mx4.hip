@@ -8,13 +8,16 @@
 // k_mx4_quantize: one thread per 32-element block.  X = 2^(floor(log2 max|v|)
 // - 2) with the exponent kept inside [-127, 127]; v / X (exact: a power-of-two
 // scaling) rounds to the nearest magnitude, ties to the even mantissa,
-// saturating at 6, written as a sum of threshold tests (strict at the ties
-// that round down, inclusive at the ties that round up); the sign bit is set
-// for v < 0.  A block of zeros gets E = 0.
+// saturating at 6, by the hardware's scaled FP4 conversion (or, for a
+// subnormal X, a sum of threshold tests: strict at the ties that round down,
+// inclusive at the ties that round up); the sign bit is the sign bit of v.  A
+// block of zeros gets E = 0 and zero codes.
 //
-// k_index_mx4: the decode indexer of indexer.hip with FP4 operands.  A query's
-// entries are read in batches of 16-entry tiles dealt round-robin to its
-// wavefronts; one v_mfma_scale_f32_16x16x128_f8f6f4 per 16 heads x 16 entries
+// k_index_mx4: the decode indexer of indexer.hip with FP4 operands.  The
+// query's index heads arrive in the element type and are quantised in the
+// prologue by the same block routine (lane (g, c) of a head block holds
+// exactly one 32-element block).  A query's entries are read in batches of
+// 16-entry tiles dealt round-robin to its wavefronts; one v_mfma_scale_f32_16x16x128_f8f6f4 per 16 heads x 16 entries
 // covers all of d_I = 128 (lane l holds 32 consecutive K values of row / column
 // l % 16, block l / 16, with that block's scale byte), so each tile is one
 // 16-byte load per lane (the tile's 16 rows of 64 code bytes, contiguous) and
@@ -26,51 +29,116 @@ namespace csa {
 
 typedef int int32x8 __attribute__((ext_vector_type(8)));
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// one 32-element block (32 consecutive elements at src, 16-byte aligned) ->
+// 16 code bytes and its scale byte.  The element conversion is gfx950's scaled
+// FP4 conversion (v / X to the nearest E2M1 value, ties to even, saturating,
+// the sign bit taken from v), four bytes per dword by byte select; a block
+// whose scale would be a subnormal float (max |v| < 2^-124) takes the same
+// rule in software.
+template <typename T>
+__device__ __forceinline__ void quantize_block32(const T *src, u32x4 &packed, uint32_t &e8) {
+    constexpr int NQ = 32 * (int)sizeof(T) / 16;  // 16-byte pieces of the block
+    u32x4 r[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) r[q] = ((const u32x4 *)src)[q];
+    float amax;
+    if constexpr (sizeof(T) == 2) {
+        // |bf16| bit patterns order like the values: a packed 16-bit integer max
+        u16x2 mx = {0, 0};
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, r[q][e] & 0x7fff7fffu));
+        amax = __uint_as_float((uint32_t)(mx[0] > mx[1] ? mx[0] : mx[1]) << 16);
+    } else {
+        amax = 0.f;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(__uint_as_float(r[q][e])));
+    }
+    packed = u32x4{0u, 0u, 0u, 0u};
+    e8 = 0;
+    if (!(amax > 0.f)) return;  // a block of zeros
+    int ex;
+    (void)frexpf(amax, &ex);  // amax = f * 2^ex, 0.5 <= f < 1: floor(log2 amax) = ex - 1
+    int se = ex - 1 - 2;
+    se = se < -127 ? -127 : (se > 127 ? 127 : se);
+    e8 = (uint32_t)(se + 127);
+    if (se >= -126) {
+        const float X = __uint_as_float((uint32_t)(se + 127) << 23);  // 2^se, a normal float
+        // byte bt of dword wd holds elements 8*wd + 2*bt (low nibble) and the next one
+#define CSA_CVT_BYTE(BT)                                                                                  \
+    if constexpr (sizeof(T) == 2) {                                                                       \
+        const int i = 8 * wd + 2 * (BT);                                                                  \
+        const uint32_t pr = r[i / 8][(i % 8) / 2];                                                        \
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, __uint_as_float(pr << 16),                        \
+                                                     __uint_as_float(pr & 0xffff0000u), X, BT);           \
+    } else {                                                                                              \
+        const int i = 8 * wd + 2 * (BT);                                                                  \
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, __uint_as_float(r[i / 4][i % 4]),                 \
+                                                     __uint_as_float(r[i / 4][i % 4 + 1]), X, BT);        \
+    }
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+            uint32_t w = 0;
+            CSA_CVT_BYTE(0)
+            CSA_CVT_BYTE(1)
+            CSA_CVT_BYTE(2)
+            CSA_CVT_BYTE(3)
+            packed[wd] = w;
+        }
+#undef CSA_CVT_BYTE
+    } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const float v = sizeof(T) == 2 ? __uint_as_float(((r[i / 8][(i % 8) / 2] >> (16 * (i % 2))) & 0xffffu) << 16)
+                                           : __uint_as_float(r[i / 4][i % 4]);
+            const float a = fabsf(ldexpf(v, -se));
+            uint32_t code = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                            (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                            (uint32_t)(a > 5.f);
+            if (signbit(v)) code |= 8u;
+            packed[i / 8] |= code << (4 * (i % 8));
+        }
+    }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_mx4_quantize(int64_t n_blocks, const T *__restrict__ x,
                                                       uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
     const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (blk >= n_blocks) return;
-    float v[32];
-    const T *src = x + blk * 32;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = Elem<T>::to_f32(src[i]);
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    u32x4 packed = {0u, 0u, 0u, 0u};
-    uint32_t e8 = 0;
-    if (amax > 0.f) {
-        int ex;
-        (void)frexpf(amax, &ex);  // amax = f * 2^ex, 0.5 <= f < 1: floor(log2 amax) = ex - 1
-        int se = ex - 1 - 2;
-        se = se < -127 ? -127 : (se > 127 ? 127 : se);
-        e8 = (uint32_t)(se + 127);
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const float y = ldexpf(v[i], -se);
-            const float a = fabsf(y);
-            uint32_t code = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                            (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                            (uint32_t)(a > 5.f);
-            if (v[i] < 0.f) code |= 8u;
-            packed[i / 8] |= code << (4 * (i % 8));
-        }
-    }
+    u32x4 packed;
+    uint32_t e8;
+    quantize_block32(x + blk * 32, packed, e8);
     *(u32x4 *)(codes + blk * 16) = packed;
     scales[blk] = (uint8_t)e8;
 }
 
-template <int DI, int MB>
+// sum over the four 16-lane groups (each lane gets the sum for its l % 16)
+__device__ __forceinline__ float mx4_sum_lane_groups(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+// max(x, 0) on the bit pattern (one integer max, no NaN canonicalisation of the MFMA result)
+__device__ __forceinline__ float mx4_relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+template <typename T, int DI, int MB>
 __global__ __launch_bounds__(256) void k_index_mx4(int Tq, int N, int HI, int m, int64_t q_pos0, int64_t n_items,
-                                                   int chunks_per_row, const uint8_t *__restrict__ qc,
-                                                   const uint8_t *__restrict__ qs, const float *__restrict__ w,
+                                                   int chunks_per_row, const T *__restrict__ qI,
+                                                   const float *__restrict__ w,
                                                    const uint8_t *__restrict__ kc, const uint8_t *__restrict__ ks,
                                                    int64_t k_bs, float *__restrict__ scores, int64_t s_stride,
                                                    float *__restrict__ scores2, uint32_t *__restrict__ hist) {
     constexpr int KB = DI / 32;  // 32-element blocks per row
     constexpr int RB = DI / 2;   // code bytes per row
-    constexpr int UNROLL = 8;    // tiles per batch
+    constexpr int UNROLL = 4;    // tiles per batch (more waves per SIMD beat deeper batches)
     constexpr int BATCH = 16 * UNROLL;
     __shared__ uint32_t whist[4][kTopkBins];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -86,7 +154,8 @@ __global__ __launch_bounds__(256) void k_index_mx4(int Tq, int N, int HI, int m,
     const int g = lane >> 4, c = lane & 15;
     const bool kon = g < KB;  // lanes that hold a K block (d_I < 128 leaves the rest zero)
 
-    // the query's index heads (A operand) with their block scales, and head weights
+    // the query's index heads quantised in place (A operand: lane (g, c) holds
+    // block g of head mb*16 + c, exactly one MXFP4 block), and head weights
     int32x8 a[MB];
     int as[MB];
     float wgt[MB][4];
@@ -95,13 +164,10 @@ __global__ __launch_bounds__(256) void k_index_mx4(int Tq, int N, int HI, int m,
         const int head = mb * 16 + c;
         const int64_t hr = row * HI + min(head, HI - 1);
         u32x4 v = {0u, 0u, 0u, 0u};
-        int sc = 127;
-        if (kon && head < HI) {
-            v = *(const u32x4 *)(qc + hr * RB + g * 16);
-            sc = qs[hr * KB + g];
-        }
+        uint32_t sc = 127;
+        if (kon && head < HI) quantize_block32(qI + hr * DI + g * 32, v, sc);
         a[mb] = int32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-        as[mb] = sc;
+        as[mb] = (int)sc;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int hh = mb * 16 + 4 * g + e;
@@ -152,10 +218,9 @@ __global__ __launch_bounds__(256) void k_index_mx4(int Tq, int N, int HI, int m,
                     const floatx4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                         a[mb], bk, floatx4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, as[mb], 0, bs);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) s += wgt[mb][e] * fmaxf(acc[e], 0.f);
+                    for (int e = 0; e < 4; ++e) s += wgt[mb][e] * mx4_relu(acc[e]);
                 }
-                s += __shfl_xor(s, 16);
-                s += __shfl_xor(s, 32);
+                s = mx4_sum_lane_groups(s);
                 if (g == 0 && j < j_hi) {
                     srow[j] = j < nv ? s : -INFINITY;
                     if (srow2) srow2[j] = j < nv ? s : -INFINITY;
@@ -198,50 +263,61 @@ hipError_t launch_mx4_quantize(int dt, int64_t n_blocks, const void *x, uint8_t 
     return hipGetLastError();
 }
 
-template <int DI, int MB>
-static hipError_t launch_mx4_t(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const uint8_t *qc,
-                               const uint8_t *qs, const float *w, const uint8_t *kc, const uint8_t *ks, int64_t k_bs,
-                               float *scores, int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
+template <typename T, int DI, int MB>
+static hipError_t launch_mx4_t(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const void *qI, const float *w,
+                               const uint8_t *kc, const uint8_t *ks, int64_t k_bs, float *scores, int64_t s_stride,
+                               float *scores2, uint32_t *hist, hipStream_t st) {
     const int64_t rows = (int64_t)B * Tq;
-    const int64_t batches = (N + 127) / 128;  // batches of eight 16-entry tiles
+    const int64_t batches = (N + 63) / 64;  // batches of four 16-entry tiles
     // aim for ~2048 wavefronts in flight (8 per CU) when there are few queries
     int64_t chunks = (2048 + rows - 1) / rows;
     if (chunks > batches) chunks = batches;
     if (chunks < 1) chunks = 1;
     const int64_t items = rows * chunks;
     const int64_t blocks = (items + 3) / 4;
-    hipLaunchKernelGGL((k_index_mx4<DI, MB>), dim3((unsigned)blocks), dim3(256), 0, st, Tq, N, HI, m, q_pos0, items,
-                       (int)chunks, qc, qs, w, kc, ks, k_bs, scores, s_stride, scores2, hist);
+    hipLaunchKernelGGL((k_index_mx4<T, DI, MB>), dim3((unsigned)blocks), dim3(256), 0, st, Tq, N, HI, m, q_pos0,
+                       items, (int)chunks, (const T *)qI, w, kc, ks, k_bs, scores, s_stride, scores2, hist);
     return hipGetLastError();
 }
 
-template <int DI>
-static hipError_t launch_mx4_di(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const uint8_t *qc,
-                                const uint8_t *qs, const float *w, const uint8_t *kc, const uint8_t *ks, int64_t k_bs,
-                                float *scores, int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
+template <typename T, int DI>
+static hipError_t launch_mx4_di(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const void *qI, const float *w,
+                                const uint8_t *kc, const uint8_t *ks, int64_t k_bs, float *scores, int64_t s_stride,
+                                float *scores2, uint32_t *hist, hipStream_t st) {
     if (HI <= 16)
-        return launch_mx4_t<DI, 1>(B, Tq, N, HI, m, q_pos0, qc, qs, w, kc, ks, k_bs, scores, s_stride, scores2, hist,
-                                   st);
+        return launch_mx4_t<T, DI, 1>(B, Tq, N, HI, m, q_pos0, qI, w, kc, ks, k_bs, scores, s_stride, scores2, hist,
+                                      st);
     if (HI <= 32)
-        return launch_mx4_t<DI, 2>(B, Tq, N, HI, m, q_pos0, qc, qs, w, kc, ks, k_bs, scores, s_stride, scores2, hist,
-                                   st);
-    return launch_mx4_t<DI, 4>(B, Tq, N, HI, m, q_pos0, qc, qs, w, kc, ks, k_bs, scores, s_stride, scores2, hist, st);
+        return launch_mx4_t<T, DI, 2>(B, Tq, N, HI, m, q_pos0, qI, w, kc, ks, k_bs, scores, s_stride, scores2, hist,
+                                      st);
+    return launch_mx4_t<T, DI, 4>(B, Tq, N, HI, m, q_pos0, qI, w, kc, ks, k_bs, scores, s_stride, scores2, hist, st);
 }
 
-hipError_t launch_index_mx4(int B, int Tq, int N, int HI, int dI, int m, int64_t q_pos0, const uint8_t *qc,
-                            const uint8_t *qs, const float *w, const uint8_t *kc, const uint8_t *ks, int64_t k_bs,
-                            float *scores, int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
+template <typename T>
+static hipError_t launch_mx4_dt(int B, int Tq, int N, int HI, int dI, int m, int64_t q_pos0, const void *qI,
+                                const float *w, const uint8_t *kc, const uint8_t *ks, int64_t k_bs, float *scores,
+                                int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
     switch (dI) {
         case 32:
-            return launch_mx4_di<32>(B, Tq, N, HI, m, q_pos0, qc, qs, w, kc, ks, k_bs, scores, s_stride, scores2,
-                                     hist, st);
+            return launch_mx4_di<T, 32>(B, Tq, N, HI, m, q_pos0, qI, w, kc, ks, k_bs, scores, s_stride, scores2, hist,
+                                        st);
         case 64:
-            return launch_mx4_di<64>(B, Tq, N, HI, m, q_pos0, qc, qs, w, kc, ks, k_bs, scores, s_stride, scores2,
-                                     hist, st);
+            return launch_mx4_di<T, 64>(B, Tq, N, HI, m, q_pos0, qI, w, kc, ks, k_bs, scores, s_stride, scores2, hist,
+                                        st);
         default:
-            return launch_mx4_di<128>(B, Tq, N, HI, m, q_pos0, qc, qs, w, kc, ks, k_bs, scores, s_stride, scores2,
-                                      hist, st);
+            return launch_mx4_di<T, 128>(B, Tq, N, HI, m, q_pos0, qI, w, kc, ks, k_bs, scores, s_stride, scores2,
+                                         hist, st);
     }
+}
+
+hipError_t launch_index_mx4(int dt, int B, int Tq, int N, int HI, int dI, int m, int64_t q_pos0, const void *qI,
+                            const float *w, const uint8_t *kc, const uint8_t *ks, int64_t k_bs, float *scores,
+                            int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
+    if (dt == 0)
+        return launch_mx4_dt<float>(B, Tq, N, HI, dI, m, q_pos0, qI, w, kc, ks, k_bs, scores, s_stride, scores2, hist,
+                                    st);
+    return launch_mx4_dt<bf16_t>(B, Tq, N, HI, dI, m, q_pos0, qI, w, kc, ks, k_bs, scores, s_stride, scores2, hist,
+                                 st);
 }
 
 }  // namespace csa

@@ -1,7 +1,11 @@
 """One layer step of hybrid compressed attention, composed from the C-ABI calls.
 
 CSA (DeepSeek-V4 overview page, section 2.2):  compress the new groups ->
-lightning indexer + top-k -> sparse shared-KV MQA with the raw window.
+lightning indexer + top-k -> sparse shared-KV MQA with the raw window.  With
+FP4 indexer operands (section 9, item 5; index_fmt "mx4") the indexer
+quantises the index queries to MXFP4 itself and scores them against MXFP4
+keys that were quantised once, when they entered the cache
+(quantize_index_keys).
 HCA (section 2.3):  compress the new group -> dense shared-KV MQA.
 
 The step owns its outputs and workspaces (allocated once, so the step can be
@@ -11,8 +15,8 @@ from __future__ import annotations
 
 import torch
 
-from . import csa_compress, csa_index_topk, csa_sparse_mqa, hca_dense_mqa, index_topk_workspace_bytes, \
-    mqa_workspace_bytes
+from . import csa_compress, csa_index_topk, csa_index_topk_mx4, csa_mx4_quantize, csa_sparse_mqa, hca_dense_mqa, \
+    index_topk_workspace_bytes, mqa_workspace_bytes
 
 
 class AttentionStep:
@@ -24,9 +28,10 @@ class AttentionStep:
     """
 
     def __init__(self, *, mode: str, N: int, m: int, W: int, q_pos0: int, raw_pos0: int, g0: int, k: int = 0,
-                 scale: float | None = None):
-        assert mode in ("csa", "hca")
+                 scale: float | None = None, index_fmt: str = "elem"):
+        assert mode in ("csa", "hca") and index_fmt in ("elem", "mx4")
         self.mode, self.N, self.m, self.W, self.k = mode, N, m, W, k
+        self.index_fmt = index_fmt
         self.q_pos0, self.raw_pos0, self.g0 = q_pos0, raw_pos0, g0
         self.scale = scale
         self._ready = False
@@ -43,6 +48,7 @@ class AttentionStep:
         if self.mode == "csa":
             HI = x["q_idx"].shape[2]
             self.topk_idx = torch.empty((B, Tq, self.k), dtype=torch.int32, device=dev)
+
             nb = index_topk_workspace_bytes(B, Tq, self.N, HI, self.k)
             self.idx_ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
         self._ready = True
@@ -56,9 +62,13 @@ class AttentionStep:
             r0 = self.g0 * self.m - self.raw_pos0
             csa_compress(raw[:, r0:r0 + (self.N - self.g0) * self.m], x["logits"], self.m,
                          entries[:, self.g0:self.N])
-        if self.mode == "csa":
+        if self.mode == "csa" and self.index_fmt == "mx4":
+            csa_index_topk_mx4(x["q_idx"], x["w_idx"], x["k_codes"], x["k_scales"], self.N, self.m, self.k,
+                               self.q_pos0, topk_idx=self.topk_idx, workspace=self.idx_ws)
+        elif self.mode == "csa":
             csa_index_topk(x["q_idx"], x["w_idx"], x["k_idx"], self.N, self.m, self.k, self.q_pos0,
                            topk_idx=self.topk_idx, workspace=self.idx_ws)
+        if self.mode == "csa":
             csa_sparse_mqa(x["q"], entries, self.topk_idx, raw, self.N, self.m, self.W, self.q_pos0, self.raw_pos0,
                            scale=self.scale, out=self.out, lse=self.lse, workspace=self.mqa_ws)
         else:
@@ -66,7 +76,13 @@ class AttentionStep:
                           out=self.out, lse=self.lse, workspace=self.mqa_ws)
         return self.out
 
+    @staticmethod
+    def quantize_index_keys(x: dict) -> dict:
+        """Give x the MXFP4 form of its index keys (k_codes, k_scales), as a cache stores them."""
+        x["k_codes"], x["k_scales"] = csa_mx4_quantize(x["k_idx"])
+        return x
+
     @classmethod
     def for_workload(cls, wl) -> "AttentionStep":
         return cls(mode=wl.mode, N=wl.N, m=wl.m, W=wl.W, q_pos0=wl.q_pos0, raw_pos0=wl.raw_pos0, g0=wl.g0, k=wl.k,
-                   scale=wl.scale)
+                   scale=wl.scale, index_fmt=getattr(wl, "index_fmt", "elem"))

@@ -230,8 +230,9 @@ void oracle_index_scores(int B, int Tq, int N, int HI, int dI, int m, long q_pos
 /* largest E2M1 exponent, with the exponent kept inside E8M0's range   */
 /* [-127, 127]; each v / X goes to the nearest magnitude, a tie to the */
 /* one whose mantissa bit is 0, and magnitudes past 6 saturate to 6; a */
-/* negative v keeps its sign bit even when it rounds to zero.  A block */
-/* of zeros gets E = 0 and zero codes.  Two codes per byte, the even   */
+/* code's sign bit is v's sign bit (so -0 and negatives that round to */
+/* zero encode as negative zero).  A block whose elements are all zero */
+/* gets E = 0 and zero codes.  Two codes per byte, the even            */
 /* element in the low nibble.  Inputs must be finite.                  */
 /* ------------------------------------------------------------------ */
 static const double fp4_magnitude[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
@@ -247,7 +248,7 @@ static int fp4_code(double v) {
             best = i;
         }
     }
-    return (v < 0.0 ? 8 : 0) | best;
+    return (signbit(v) ? 8 : 0) | best;
 }
 
 void oracle_mx4_quantize(long n_blocks, const float *x, uint8_t *codes, uint8_t *scales) {

@@ -45,7 +45,11 @@ def oracle_step(wl, xh: dict, rows=None) -> dict:
         qp = wl.q_pos0 + a
         q = xh["q"][:, a:b]
         if wl.mode == "csa":
-            s = orc.index_scores(xh["q_idx"][:, a:b], xh["w_idx"][:, a:b], xh["k_idx"][:, :N], m, qp)
+            qi, ki = xh["q_idx"][:, a:b], xh["k_idx"][:, :N]
+            if getattr(wl, "index_fmt", "elem") == "mx4":  # the FP4 operands' exact values
+                qi = orc.mx4_dequantize(*orc.mx4_quantize(qi))
+                ki = orc.mx4_dequantize(*orc.mx4_quantize(ki))
+            s = orc.index_scores(qi, xh["w_idx"][:, a:b], ki, m, qp)
             idx = orc.topk(s, wl.k, m, qp)
             o, l = orc.sparse_mqa(q, ent, idx, xh["raw"], wl.raw_pos0, wl.W, qp, wl.scale)
             scs.append(s)

@@ -138,12 +138,12 @@ def test_mx4_calls_reject_bad_arguments(L):
     assert L.csa_mx4_quantize(1, 0, 64, None, None, None, None) == 0        # nothing to do
     f = csa.lib().csa_index_topk_mx4
     ws = csa.index_topk_workspace_bytes(1, 1, 256, 64, 64)
-    args = dict(B=1, Tq=1, N=256, HI=64, dI=128, m=4, k=64, q0=1023, qc=P, qs=P + 0x10000, w=P + 0x20000,
+    args = dict(dt=1, B=1, Tq=1, N=256, HI=64, dI=128, m=4, k=64, q0=1023, q=P, w=P + 0x20000,
                 kc=P + 0x30000, ks=P + 0x40000, kbs=256, idx=P + 0x50000, so=None, ws=P + 0x100000, wsb=ws)
 
     def call(**kw):
         a = dict(args, **kw)
-        return f(a["B"], a["Tq"], a["N"], a["HI"], a["dI"], a["m"], a["k"], a["q0"], a["qc"], a["qs"], a["w"],
+        return f(a["dt"], a["B"], a["Tq"], a["N"], a["HI"], a["dI"], a["m"], a["k"], a["q0"], a["q"], a["w"],
                  a["kc"], a["ks"], a["kbs"], a["idx"], a["so"], a["ws"], a["wsb"], None)
 
     assert call(dI=96) == -6
@@ -153,5 +153,7 @@ def test_mx4_calls_reject_bad_arguments(L):
     assert call(kc=P + 0x30004) == -3
     assert call(wsb=ws - 1) == -4
     assert call(idx=P + 0x30000) == -1   # output overlaps the key codes
-    assert call(qc=None) == -1
+    assert call(q=None) == -1
+    assert call(dt=5) == -2
+    assert call(q=P + 8) == -3
     assert call(B=0) == 0

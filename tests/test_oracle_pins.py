@@ -452,7 +452,6 @@ def test_mx4_representable_blocks_round_trip():
     for trial in range(200):
         e = int(r.integers(-20, 20))
         codes = r.integers(0, 16, 32).astype(np.uint8)
-        codes[codes == 8] = 0                   # (a negative zero reads back as +0)
         codes[int(r.integers(0, 32))] = int(r.choice([6, 7, 14, 15]))  # block maximum 4 or 6
         x = mx4_dequantize(pack_codes(codes)[None], np.array([[127 + e]], dtype=np.uint8))
         c2, s2 = mx4_quantize(x)
@@ -490,6 +489,7 @@ def test_mx4_hand_checked_ties_and_saturation():
     out = mx4_dequantize(codes, scales)[0, :len(vals)]
     np.testing.assert_array_equal(out, np.array(want, dtype=np.float32))
     assert (codes[0, 4] & 15) == 8  # -0.25 keeps its sign bit
+    assert (codes[0, 6] >> 4) == 0  # +0.0
 
 
 def test_mx4_block_maximum_lands_on_four_or_six_and_equivariance():

@@ -39,6 +39,8 @@ def run_and_check(csa, wl: Workload, rows=None, entries_capacity=None):
     say(wl)
     x = make_inputs(wl, "cuda", entries_capacity=entries_capacity)
     xh = host_inputs(x)
+    if wl.index_fmt == "mx4":  # the cache holds the keys' FP4 form
+        csa.AttentionStep.quantize_index_keys(x)
     step = csa.AttentionStep.for_workload(wl)
     out = step(x)
     torch.cuda.synchronize()
@@ -104,6 +106,14 @@ def test_c5_csa_decode_1m_stress(csa):
     run_and_check(csa, CONFIGS["c5"])
 
 
+def test_c2x_csa_decode_128k_fp4_indexer(csa):
+    run_and_check(csa, CONFIGS["c2x"])
+
+
+def test_c5x_csa_decode_1m_stress_fp4_indexer(csa):
+    run_and_check(csa, CONFIGS["c5x"])
+
+
 # ------------------------------------------------------- small and ragged shapes
 SMALL = [
     # name, dtype, B, T, Tq, m, d, H, W, k, HI, dI
@@ -118,6 +128,7 @@ SMALL = [
     ("csa_bf16_prefill_blocks", "bf16", 2, 2403, 100, 4, 128, 16, 8, 64, 20, 64),
     ("csa_bf16_prefill_d32", "bf16", 1, 1000, 70, 4, 64, 8, 4, 50, 4, 32),
     ("csa_bf16_many_queries", "bf16", 2, 1300, 300, 4, 256, 8, 16, 40, 16, 32),
+    ("csa_bf16_fp4_indexer", "bf16:mx4", 2, 4 * 2000 + 3, 5, 4, 128, 16, 16, 300, 64, 128),
     ("hca_bf16_ragged", "bf16", 2, 128 * 77 + 5, 3, 128, 512, 64, 128, 0, 0, 0),
     ("hca_bf16_many_queries", "bf16", 1, 128 * 10 + 600, 600, 128, 128, 16, 32, 0, 0, 0),
     ("hca_f32_m1_w0", "f32", 1, 150, 150, 1, 64, 4, 0, 0, 0, 0),
@@ -128,8 +139,9 @@ SMALL = [
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_small_shapes(csa, case):
     name, dt, B, T, Tq, m, d, H, W, k, HI, dI = case
+    dt, _, fmt = dt.partition(":")
     wl = Workload(name, dt, B=B, T=T, Tq=Tq, m=m, d=d, H=H, W=W, k=k, HI=HI, dI=dI,
-                  seed_base=90000 + 1000 * SMALL.index(case))
+                  seed_base=90000 + 1000 * SMALL.index(case), index_fmt=fmt or "elem")
     run_and_check(csa, wl, entries_capacity=wl.N + 40)
 
 

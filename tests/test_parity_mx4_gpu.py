@@ -82,10 +82,10 @@ MX_CASES = [
 def run_mx4(csa, orc, wl: Workload, cap_extra: int):
     say(wl, "mx4 indexer")
     x = make_inputs(wl, "cuda", entries_capacity=wl.N + cap_extra)
-    qc, qs = csa.csa_mx4_quantize(x["q_idx"].contiguous())
+    qc, qs = csa.csa_mx4_quantize(x["q_idx"].contiguous())  # (the same block routine the indexer runs inside)
     kc, ks = csa.csa_mx4_quantize(x["k_idx"].contiguous())
     sc = torch.empty((wl.B, wl.Tq, wl.N), dtype=torch.float32, device="cuda")
-    idx = csa.csa_index_topk_mx4(qc, qs, x["w_idx"], kc, ks, wl.N, wl.m, wl.k, wl.q_pos0, scores_out=sc)
+    idx = csa.csa_index_topk_mx4(x["q_idx"], x["w_idx"], kc, ks, wl.N, wl.m, wl.k, wl.q_pos0, scores_out=sc)
     torch.cuda.synchronize()
     # the oracle quantises the same inputs itself
     rqc, rqs = orc.mx4_quantize(x["q_idx"].float().cpu().numpy())

@@ -44,6 +44,7 @@ class Workload:
     dI: int = 0         # index width (CSA)
     stress_frac: float = 0.0   # fraction of entries whose row and index key are scaled by 8
     seed_base: int = 0  # 1000 * workload number
+    index_fmt: str = "elem"    # indexer operands: "elem" (the element type) or "mx4" (MXFP4 codes + scales)
 
     # ---- derived shapes (bookkeeping only) ----
     @property
@@ -98,6 +99,10 @@ CONFIGS = {
     "c5": Workload("csa_decode_bf16_B4_ctx1M_stress", "bf16", B=4, T=1048576, Tq=1, m=4, d=512, H=64, W=128,
                    k=1024, HI=64, dI=128, stress_frac=0.01, seed_base=5000),
 }
+# the 128K and 1M CSA decode steps with FP4 (MXFP4) index queries and keys:
+# the same seeded inputs, the keys quantised once when the cache is prepared
+CONFIGS["c2x"] = dataclasses.replace(CONFIGS["c2"], name="csa_decode_mx4idx_B32_ctx128K", index_fmt="mx4")
+CONFIGS["c5x"] = dataclasses.replace(CONFIGS["c5"], name="csa_decode_mx4idx_B4_ctx1M_stress", index_fmt="mx4")
 
 
 def _gen(wl: Workload, name: str, device) -> torch.Generator:
