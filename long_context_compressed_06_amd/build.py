@@ -16,11 +16,15 @@ ARCH = "gfx950"
 # packed-fp32 instructions are disabled for all device code
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
          "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-result"]
+# per-source additions: the indexers' MFMA results go to VGPRs (each epilogue
+# reads every one of them; results in AGPRs cost one accvgpr read each)
+_VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+SOURCE_FLAGS = {"indexer.hip": _VGPR_MFMA, "mx4.hip": _VGPR_MFMA}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -250,6 +250,197 @@ __global__ __launch_bounds__(256) void k_index_mx4(int Tq, int N, int HI, int m,
     }
 }
 
+// ---------------------------------------------------------------------------
+// FP4 keys, d_I = 128: LDS-DMA streaming (the structure of k_index_dma).
+//
+// One workgroup of kMx4Waves wavefronts works on one query; the query's
+// 16-entry tiles are dealt round-robin to the wavefronts of its workgroups,
+// and each wavefront streams its tiles HBM -> LDS into a private ring of
+// kMx4Stages slots: the tile's 1 KiB of codes with one non-temporal
+// global_load_lds_dwordx4 (16-byte chunks XOR-swizzled by row, so the B
+// operand reads are conflict-free) and its 16 rows' scale dwords with one
+// global_load_lds_dword (16 lanes, a row each).  In the tile that holds the
+// last visible entry, rows past it reread that entry (their scores are
+// masked).  The workgroup quantises the query once (one 32-element block per
+// thread) into LDS, from where every wavefront takes its A operands.
+constexpr int kMx4Waves = 4;
+constexpr int kMx4Stages = 4;
+constexpr int kMx4Slot = 1024 + 64;  // codes of 16 rows of 64 bytes, then their 16 scale dwords
+constexpr int kMx4Ring = kMx4Waves * kMx4Stages * kMx4Slot;
+constexpr int kMx4QBlocks = 64 * 4;  // the query's 32-element blocks: 64 heads x 4
+constexpr int kMx4Lds = kMx4Ring + kMx4QBlocks * (16 + 4) + kTopkBins * 4;  // ring, query codes + scales, histogram
+
+// chunk position of row r's 16-byte chunk ch (an involution): four rows share one swizzle
+__device__ __forceinline__ int mx4_swz(int r, int ch) { return ch ^ ((r >> 2) & 3); }
+
+__device__ __forceinline__ void lds_dma16_nt_mx4(uint32_t lds_addr, const void *src) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(lds_addr), "v"(src)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4_nt_mx4(uint32_t lds_addr, const void *src) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off nt" ::"s"(lds_addr), "v"(src)
+                 : "memory", "m0");
+}
+
+template <typename T, int MB>
+__global__ __launch_bounds__(kMx4Waves * 64) void k_index_mx4_dma(int Tq, int N, int HI, int m, int64_t q_pos0,
+                                                                 int blocks_per_row, const T *__restrict__ qI,
+                                                                 const float *__restrict__ w,
+                                                                 const uint8_t *__restrict__ kc,
+                                                                 const uint8_t *__restrict__ ks, int64_t k_bs,
+                                                                 float *__restrict__ scores, int64_t s_stride,
+                                                                 float *__restrict__ scores2,
+                                                                 uint32_t *__restrict__ hist) {
+    constexpr int DI = 128, RB = 64, KB = 4;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    unsigned char *ring = lds;
+    u32x4 *qcodes = (u32x4 *)(lds + kMx4Ring);                             // [head][block] 16 bytes
+    uint32_t *qscale = (uint32_t *)(lds + kMx4Ring + kMx4QBlocks * 16);    // [head][block]
+    uint32_t *bh = (uint32_t *)(lds + kMx4Ring + kMx4QBlocks * (16 + 4));
+
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, c = lane & 15;
+    const int64_t row = blockIdx.x / blocks_per_row;
+    const int part = blockIdx.x % blocks_per_row;
+    const int64_t b = row / Tq, ti = row % Tq;
+    const int64_t nv = n_visible(q_pos0 + ti, m, N);
+    const int wpr = blocks_per_row * kMx4Waves;
+    const int gw = part * kMx4Waves + wv;
+    const int tiles = (N + 15) / 16;
+    const int vtiles = (int)((nv + 15) / 16);
+    const int n_all = tiles > gw ? (tiles - gw + wpr - 1) / wpr : 0;
+    const int n_vis = vtiles > gw ? (vtiles - gw + wpr - 1) / wpr : 0;
+
+    const uint8_t *kcb = kc + b * k_bs * RB;
+    const uint8_t *ksb = ks + b * k_bs * KB;
+    unsigned char *my_ring = ring + wv * kMx4Stages * kMx4Slot;
+    const uint32_t ring_addr = (uint32_t)(uintptr_t)my_ring;
+    // this lane's chunk of a tile's codes: row r = lane / 4, position lane % 4 holding source chunk swz(r, pos)
+    const int cr = lane >> 2, cpos = lane & 3;
+    const int64_t tstride_c = (int64_t)wpr * 16 * RB;  // code bytes between this wavefront's tiles
+    const uint8_t *csrc0 = kcb + ((int64_t)gw * 16 + cr) * RB + mx4_swz(cr, cpos) * 16;
+    const uint8_t *ssrc0 = ksb + ((int64_t)gw * 16 + (lane & 15)) * KB;
+    auto issue = [&](int i) {
+        const int t = gw + i * wpr;
+        const int slot = i % kMx4Stages;
+        const bool whole = (int64_t)t * 16 + 16 <= nv;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the slot are done
+        const uint8_t *cs = csrc0 + i * tstride_c;
+        const uint8_t *ss = ssrc0 + (int64_t)i * wpr * 16 * KB;
+        if (!whole) {
+            cs = kcb + min((int64_t)t * 16 + cr, nv - 1) * RB + mx4_swz(cr, cpos) * 16;
+            ss = ksb + min((int64_t)t * 16 + (lane & 15), nv - 1) * KB;
+        }
+        const uint32_t base = __builtin_amdgcn_readfirstlane(ring_addr + slot * kMx4Slot);
+        lds_dma16_nt_mx4(base, cs);
+        if (lane < 16) lds_dma4_nt_mx4(base + 1024, ss);
+    };
+
+    // the first tiles stream in while the query is quantised (the ring is
+    // disjoint from the query and histogram areas)
+    for (int i = 0; i < kMx4Stages - 1 && i < n_vis; ++i) issue(i);
+
+    // ---- quantise the query once per workgroup, clear the histogram
+    {
+        static_assert(kMx4Waves * 64 == kMx4QBlocks, "one query block per thread");
+        const int blk = threadIdx.x;
+        const int head = blk >> 2;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        uint32_t sc = 127;
+        if (head < HI) quantize_block32(qI + (row * HI + head) * DI + (blk & 3) * 32, v, sc);
+        qcodes[blk] = v;
+        qscale[blk] = sc;
+    }
+    if (hist)
+        for (int i = threadIdx.x; i < kTopkBins; i += kMx4Waves * 64) bh[i] = 0;
+    float wgt[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int hh = mb * 16 + 4 * g + e;
+            const float v = w[row * HI + min(hh, HI - 1)];
+            wgt[mb][e] = hh < HI ? v : 0.f;
+        }
+    __syncthreads();
+    int32x8 a[MB];
+    int as[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int head = mb * 16 + c;  // (heads past HI were quantised as zero blocks)
+        const u32x4 v = qcodes[head * 4 + g];
+        a[mb] = int32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        as[mb] = (int)qscale[head * 4 + g];
+    }
+
+    float *srow = scores + row * s_stride;
+    float *srow2 = scores2 ? scores2 + row * (int64_t)N : nullptr;
+    for (int i = 0; i < n_vis; ++i) {
+        // two DMA instructions per tile (the scale one only in 16 lanes, still one count)
+        if (i + kMx4Stages - 1 < n_vis) {
+            issue(i + kMx4Stages - 1);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kMx4Stages - 1) * 2) : "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        const unsigned char *tile = my_ring + (i % kMx4Stages) * kMx4Slot;
+        const u32x4 kd = *(const u32x4 *)(tile + c * RB + mx4_swz(c, g) * 16);
+        const int bs = tile[1024 + c * 4 + g];
+        const int32x8 bk = {(int)kd[0], (int)kd[1], (int)kd[2], (int)kd[3], 0, 0, 0, 0};
+        float sc = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const floatx4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                a[mb], bk, floatx4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, as[mb], 0, bs);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sc += wgt[mb][e] * mx4_relu(acc[e]);
+        }
+        sc = mx4_sum_lane_groups(sc);
+        const int64_t j = (int64_t)(gw + i * wpr) * 16 + c;
+        if (g == 0 && j < N) {
+            const float v = j < nv ? sc : -INFINITY;
+            srow[j] = v;
+            if (srow2) srow2[j] = v;
+            if (hist && j < nv) atomicAdd(&bh[order_key(sc) >> (32 - kTopkBinBits)], 1u);
+        }
+    }
+    // tiles with no visible entry
+    for (int i = n_vis; i < n_all; ++i) {
+        const int64_t j = (int64_t)(gw + i * wpr) * 16 + lane;
+        if (lane < 16 && j < N) {
+            srow[j] = -INFINITY;
+            if (srow2) srow2[j] = -INFINITY;
+        }
+    }
+    if (hist) {
+        __syncthreads();
+        uint32_t *grow = hist + row * kTopkBins;
+        for (int i = threadIdx.x; i < kTopkBins; i += kMx4Waves * 64) {
+            const uint32_t v = bh[i];
+            if (v) atomicAdd(&grow[i], v);
+        }
+    }
+}
+
+template <typename T, int MB>
+static hipError_t launch_mx4_dma(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const void *qI, const float *w,
+                                 const uint8_t *kc, const uint8_t *ks, int64_t k_bs, float *scores, int64_t s_stride,
+                                 float *scores2, uint32_t *hist, hipStream_t st) {
+    static const hipError_t attr = hipFuncSetAttribute((const void *)k_index_mx4_dma<T, MB>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMx4Lds);
+    if (attr != hipSuccess) return attr;
+    const int64_t rows = (int64_t)B * Tq;
+    const int64_t tiles = (N + 15) / 16;
+    int64_t bpr = (1280 + rows - 1) / rows;  // five workgroups per CU in total when there are few queries
+    const int64_t max_bpr = (tiles + kMx4Waves - 1) / kMx4Waves;
+    if (bpr > max_bpr) bpr = max_bpr;
+    if (bpr < 1) bpr = 1;
+    hipLaunchKernelGGL((k_index_mx4_dma<T, MB>), dim3((unsigned)(rows * bpr)), dim3(kMx4Waves * 64), kMx4Lds, st, Tq,
+                       N, HI, m, q_pos0, (int)bpr, (const T *)qI, w, kc, ks, k_bs, scores, s_stride, scores2, hist);
+    return hipGetLastError();
+}
+
 hipError_t launch_mx4_quantize(int dt, int64_t n_blocks, const void *x, uint8_t *codes, uint8_t *scales,
                                hipStream_t st) {
     if (n_blocks <= 0) return hipSuccess;
@@ -297,6 +488,16 @@ template <typename T>
 static hipError_t launch_mx4_dt(int B, int Tq, int N, int HI, int dI, int m, int64_t q_pos0, const void *qI,
                                 const float *w, const uint8_t *kc, const uint8_t *ks, int64_t k_bs, float *scores,
                                 int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
+    if (dI == 128 && ((uintptr_t)ks % 4) == 0) {  // (scale rows move as dwords)
+        if (HI <= 16)
+            return launch_mx4_dma<T, 1>(B, Tq, N, HI, m, q_pos0, qI, w, kc, ks, k_bs, scores, s_stride, scores2,
+                                        hist, st);
+        if (HI <= 32)
+            return launch_mx4_dma<T, 2>(B, Tq, N, HI, m, q_pos0, qI, w, kc, ks, k_bs, scores, s_stride, scores2,
+                                        hist, st);
+        return launch_mx4_dma<T, 4>(B, Tq, N, HI, m, q_pos0, qI, w, kc, ks, k_bs, scores, s_stride, scores2, hist,
+                                    st);
+    }
     switch (dI) {
         case 32:
             return launch_mx4_di<T, 32>(B, Tq, N, HI, m, q_pos0, qI, w, kc, ks, k_bs, scores, s_stride, scores2, hist,

@@ -76,14 +76,20 @@ MX_CASES = [
     ("queries_causal_d64", 2, 4 * 500, 37, 4, 16, 64, 64, 8),
     ("queries_early_d32", 1, 70, 70, 4, 4, 32, 5, 0),
     ("decode_m1_heads20", 2, 2500, 2, 1, 20, 128, 300, 16),
+    ("queries_causal_d128", 2, 4 * 700 + 3, 40, 4, 64, 128, 128, 8),
+    ("queries_early_d128", 1, 70, 70, 4, 8, 128, 5, 0),
 ]
 
 
-def run_mx4(csa, orc, wl: Workload, cap_extra: int):
-    say(wl, "mx4 indexer")
+def run_mx4(csa, orc, wl: Workload, cap_extra: int, scale_offset: int = 0):
+    say(wl, "mx4 indexer", f"scale offset {scale_offset}")
     x = make_inputs(wl, "cuda", entries_capacity=wl.N + cap_extra)
     qc, qs = csa.csa_mx4_quantize(x["q_idx"].contiguous())  # (the same block routine the indexer runs inside)
     kc, ks = csa.csa_mx4_quantize(x["k_idx"].contiguous())
+    if scale_offset:  # scales at an address that is not a multiple of 4 bytes
+        buf = torch.zeros(ks.numel() + scale_offset, dtype=torch.uint8, device="cuda")
+        ks = buf[scale_offset:].view(ks.shape)
+        ks.copy_(csa.csa_mx4_quantize(x["k_idx"].contiguous())[1])
     sc = torch.empty((wl.B, wl.Tq, wl.N), dtype=torch.float32, device="cuda")
     idx = csa.csa_index_topk_mx4(x["q_idx"], x["w_idx"], kc, ks, wl.N, wl.m, wl.k, wl.q_pos0, scores_out=sc)
     torch.cuda.synchronize()
@@ -114,6 +120,13 @@ def test_index_topk_mx4(csa, orc, case):
     wl = Workload(name, "bf16", B=B, T=T, Tq=Tq, m=m, d=128, H=8, W=4, k=k, HI=HI, dI=dI,
                   seed_base=70000 + 1000 * MX_CASES.index(case))
     run_mx4(csa, orc, wl, cap_extra)
+
+
+def test_index_topk_mx4_unaligned_scales(csa, orc):
+    """Key scales at an odd address (read a byte at a time rather than as dwords)."""
+    wl = Workload("mx4_scales_odd", "bf16", B=2, T=4 * 1500 + 1, Tq=3, m=4, d=128, H=8, W=4, k=200, HI=64, dI=128,
+                  seed_base=78000)
+    run_mx4(csa, orc, wl, 4, scale_offset=1)
 
 
 def test_index_topk_mx4_decode_128k(csa, orc):
