@@ -96,6 +96,27 @@ int csa_compress(int dt, int B, int G, int m, int d,
                  void *out, int64_t out_bstride, void *stream);
 
 /*
+ * csa_append_rows -- cache maintenance between steps (overview page, section
+ * 2.2 step 1: the raw tokens of a group are kept until its m-th token
+ * arrives and the group becomes one entry; the window of raw tokens is kept
+ * for the attention).  Copies rows into a cache or a raw-token ring:
+ *     ring == 0:  dst[b, pos0 + i] = rows[b, i]
+ *     ring == R:  dst[b, (pos0+i) mod R] = dst[b, (pos0+i) mod R + R] = rows[b, i]
+ * for b < B, i < n.  The ring is mirrored (2R slots), so positions
+ * p .. p+L-1 (L <= R) of a ring sit in slots p mod R .. p mod R + L - 1 and a
+ * window of the raw stream is a plain strided view of it.  Rows are opaque
+ * bytes (element rows, f32 logits, FP4 codes or scale bytes).
+ *   rows  [B, n] rows of row_bytes bytes, packed; batch stride rows_bstride BYTES
+ *   dst   [B, dst_rows] rows of row_bytes bytes; batch stride dst_bstride BYTES
+ *         (ring == 0: pos0 + n <= dst_rows; ring > 0: n <= ring, 2*ring <= dst_rows)
+ * `rows` must not overlap `dst`.  B <= 65535.  Any alignment (wider moves
+ * when row_bytes, pointers and strides allow).
+ */
+int csa_append_rows(int B, int n, int64_t row_bytes, const void *rows, int64_t rows_bstride,
+                    void *dst, int64_t dst_bstride, int64_t dst_rows, int64_t pos0, int64_t ring,
+                    void *stream);
+
+/*
  * csa_index_topk -- lightning indexer and per-query top-k (overview page,
  * section 2.2 step 2; indexer form fixed as a sum over index heads of a
  * head weight times ReLU of a query-key dot product).  For query row i of

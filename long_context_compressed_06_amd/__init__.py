@@ -22,7 +22,7 @@ _STATUS = {0: "CSA_OK", -1: "CSA_EINVAL", -2: "CSA_EDTYPE", -3: "CSA_EALIGN", -4
            -5: "CSA_EHIP", -6: "CSA_EUNSUPPORTED"}
 EXPORTS = ("csa_abi_version", "csa_status_string", "csa_last_error_detail", "csa_compress",
            "csa_index_topk_workspace_bytes", "csa_index_topk", "csa_index_scores", "csa_mqa_workspace_bytes",
-           "csa_sparse_mqa", "hca_dense_mqa", "csa_mx4_quantize", "csa_index_topk_mx4")
+           "csa_sparse_mqa", "hca_dense_mqa", "csa_mx4_quantize", "csa_index_topk_mx4", "csa_append_rows")
 
 
 class CsaError(RuntimeError):
@@ -66,6 +66,8 @@ def lib():
     L.csa_mx4_quantize.restype = I
     L.csa_index_topk_mx4.argtypes = [I, I, I, I, I, I, I, I, I64, P, P, P, P, I64, P, P, P, SZ, P]
     L.csa_index_topk_mx4.restype = I
+    L.csa_append_rows.argtypes = [I, I, I64, P, I64, P, I64, I64, I64, I64, P]
+    L.csa_append_rows.restype = I
     _lib = L
     return L
 
@@ -230,6 +232,27 @@ def csa_index_topk_mx4(q_idx, w_idx, k_codes, k_scales, N: int, m: int, k: int, 
     return topk_idx
 
 
+def csa_append_rows(rows: torch.Tensor, dst: torch.Tensor, pos0: int, ring: int = 0) -> torch.Tensor:
+    """rows [B, n, *row] -> dst [B, cap, *row] at rows pos0.. (ring 0) or into a mirrored ring of `ring`
+    positions (dst holds 2*ring slots: position p goes to slots p % ring and p % ring + ring)."""
+    _need(rows, "rows")
+    _need(dst, "dst", rows.dtype)
+    if rows.dim() < 2 or rows.shape[0] != dst.shape[0] or rows.shape[2:] != dst.shape[2:]:
+        raise ValueError("rows and dst must be [B, n, ...] and [B, cap, ...] with the same row shape")
+    B, n = rows.shape[0], rows.shape[1]
+    per_row = 1
+    for x in rows.shape[2:]:
+        per_row *= x
+    es = rows.element_size()
+    for t, name in ((rows, "rows"), (dst, "dst")):
+        packed = t[0:1].is_contiguous() if t.shape[0] else True
+        if not packed:
+            raise ValueError(f"{name}: the rows of one batch must be packed")
+    _check(lib().csa_append_rows(B, n, per_row * es, _p(rows), rows.stride(0) * es, _p(dst), dst.stride(0) * es,
+                                 dst.shape[1], pos0, ring, _stream(rows)))
+    return dst
+
+
 def mqa_workspace_bytes(B, Tq, H, d, n_rows_max) -> int:
     return int(lib().csa_mqa_workspace_bytes(B, Tq, H, d, n_rows_max))
 
@@ -288,3 +311,4 @@ def hca_dense_mqa(q, entries, raw, N: int, m: int, W: int, q_pos0: int, raw_pos0
 
 
 from .step import AttentionStep  # noqa: E402  (uses the functions above)
+from .stream import StreamingLayer, chunk_plan, ring_size  # noqa: E402

@@ -100,6 +100,34 @@ int csa_compress(int dt, int B, int G, int m, int d, const void *raw, int64_t ra
                       "compress launch");
 }
 
+int csa_append_rows(int B, int n, int64_t row_bytes, const void *rows, int64_t rows_bstride, void *dst,
+                    int64_t dst_bstride, int64_t dst_rows, int64_t pos0, int64_t ring, void *stream) {
+    if (B < 0 || n < 0) return fail(CSA_EINVAL, "B=%d and n=%d must be >= 0", B, n);
+    if (B > 65535) return fail(CSA_EUNSUPPORTED, "B=%d above 65535", B);
+    if (row_bytes < 1) return fail(CSA_EINVAL, "row_bytes=%lld must be >= 1", (long long)row_bytes);
+    if (pos0 < 0 || ring < 0 || dst_rows < 0) return fail(CSA_EINVAL, "pos0, ring and dst_rows must be >= 0");
+    if (ring == 0 && pos0 + n > dst_rows)
+        return fail(CSA_EINVAL, "rows %lld..%lld outside the %lld destination rows", (long long)pos0,
+                    (long long)(pos0 + n - 1), (long long)dst_rows);
+    if (ring > 0 && (n > ring || 2 * ring > dst_rows))
+        return fail(CSA_EINVAL, "a ring of %lld positions needs n <= ring and %lld slots (have %lld)",
+                    (long long)ring, (long long)(2 * ring), (long long)dst_rows);
+    if ((int64_t)B * n == 0) return ok();
+    if (!rows || !dst) return fail(CSA_EINVAL, "NULL tensor pointer");
+    if (rows_bstride < (int64_t)n * row_bytes || dst_bstride < dst_rows * row_bytes)
+        return fail(CSA_EINVAL, "a batch stride is smaller than one batch's extent");
+    const Span ss = span(rows, B, rows_bstride, (int64_t)n * row_bytes, 1);
+    const Span sd = span(dst, B, dst_bstride, dst_rows * row_bytes, 1);
+    if (overlap(ss, sd)) return fail(CSA_EINVAL, "rows overlap the destination");
+    int vw = 16;
+    while (vw > 1 && (row_bytes % vw || !aligned(rows, vw) || !aligned(dst, vw) || rows_bstride % vw ||
+                      dst_bstride % vw))
+        vw /= 2;
+    return hip_status(csa::launch_append_rows(B, n, row_bytes, vw, rows, rows_bstride, dst, dst_bstride, pos0, ring,
+                                              (hipStream_t)stream),
+                      "append launch");
+}
+
 // the score rows the top-k reads, padded to csa::topk_score_stride(N) floats
 static size_t scores_bytes(int64_t rows, int64_t N) {
     return ((size_t)rows * csa::topk_score_stride(N) * sizeof(float) + 255) / 256 * 256;

@@ -60,6 +60,12 @@ constexpr int64_t topk_score_stride(int64_t N) { return (N + 63) / 64 * 64; }
 
 hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t st);
 
+// rows [B][n] of row_bytes (packed, batch stride src_bs bytes) -> dst rows
+// pos0 .. (ring == 0) or the mirrored ring of `ring` positions (2*ring slots);
+// vw: bytes per vector, dividing row_bytes, both pointers and both strides
+hipError_t launch_append_rows(int B, int64_t n, int64_t row_bytes, int vw, const void *src, int64_t src_bs,
+                              void *dst, int64_t dst_bs, int64_t pos0, int64_t ring, hipStream_t st);
+
 // scores: [rows][topk_score_stride(N)], 16-byte aligned.  scratch:
 // topk_scratch_bytes(rows, N) bytes; its histogram part must have been filled
 // by launch_index_scores (zeroed before it)

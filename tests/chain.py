@@ -65,3 +65,26 @@ def oracle_step(wl, xh: dict, rows=None) -> dict:
         res["scores"] = np.concatenate(scs, axis=1)
         res["idx"] = np.concatenate(idxs, axis=1)
     return res
+
+
+def oracle_sequence(sq, xh: dict) -> dict:
+    """Oracle results for a whole stream processed from position 0 (host inputs of make_sequence)."""
+    G, m = sq.G, sq.m
+    e = orc.compress(xh["raw"][:, :G * m], xh["logits"][:, :G * m], m) if G > 0 else None
+    ent = np.zeros((sq.B, max(G, 1), sq.d), dtype=np.float32)
+    if G > 0:
+        ent[:, :G] = orc.round_bf16(e) if sq.dtype == "bf16" else e.astype(np.float32)
+    res = {"e": e}
+    if sq.mode == "csa":
+        qi, ki = xh["q_idx"], xh["k_idx"]
+        if sq.index_fmt == "mx4":
+            qi = orc.mx4_dequantize(*orc.mx4_quantize(qi))
+            ki = orc.mx4_dequantize(*orc.mx4_quantize(ki))
+        s = orc.index_scores(qi, xh["w_idx"], ki, m, 0)
+        idx = orc.topk(s, sq.k, m, 0)
+        o, l = orc.sparse_mqa(xh["q"], ent[:, :G], idx, xh["raw"], 0, sq.W, 0, sq.scale)
+        res.update(scores=s, idx=idx)
+    else:
+        o, l = orc.dense_mqa(xh["q"], ent[:, :G], xh["raw"], 0, m, sq.W, 0, sq.scale)
+    res.update(out=o, lse=l)
+    return res

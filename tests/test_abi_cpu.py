@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
     import long_context_compressed_06_amd as csa
 
     names = header_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(L, n), n
     assert sorted(csa.EXPORTS) == names
@@ -157,3 +157,24 @@ def test_mx4_calls_reject_bad_arguments(L):
     assert call(dt=5) == -2
     assert call(q=P + 8) == -3
     assert call(B=0) == 0
+
+
+def test_append_rows_rejects_bad_arguments(L):
+    f = L.csa_append_rows
+
+    def call(B=2, n=4, rb=256, rows=P, rbs=4 * 256, dst=P + 0x100000, dbs=64 * 256, drows=64, pos0=0, ring=0):
+        return f(B, n, rb, rows, rbs, dst, dbs, drows, pos0, ring, None)
+
+    assert call(n=-1) == -1
+    assert call(B=70000) == -6
+    assert call(rb=0) == -1
+    assert call(pos0=-1) == -1
+    assert call(pos0=61) == -1                 # rows 61..64 past the 64 destination rows
+    assert call(ring=3) == -1                  # more rows than ring positions
+    assert call(ring=33) == -1                 # 66 slots needed, 64 present
+    assert call(rows=None) == -1
+    assert call(rbs=3 * 256) == -1             # batch stride below one batch's rows
+    assert call(dbs=63 * 256) == -1
+    assert call(dst=P + 0x100) == -1           # destination overlaps the rows
+    assert call(B=0, rows=None, dst=None) == 0  # nothing to do
+    assert call(n=0, rows=None, dst=None) == 0

@@ -161,3 +161,64 @@ def make_inputs(wl: Workload, device="cpu", entries_capacity: int | None = None)
 def scaled(wl: Workload, **changes) -> Workload:
     """A copy of ``wl`` with some fields replaced (used by tests for reduced shapes)."""
     return dataclasses.replace(wl, **changes)
+
+
+# ---------------------------------------------------------------- sequences
+@dataclasses.dataclass(frozen=True)
+class Sequence:
+    """A whole token stream for one layer, processed from position 0: prefill in
+    the given chunks, then the rest of the T tokens decoded one at a time."""
+    name: str
+    dtype: str
+    B: int
+    T: int
+    m: int
+    d: int
+    H: int
+    W: int
+    k: int = 0
+    HI: int = 0
+    dI: int = 0
+    index_fmt: str = "elem"
+    chunks: tuple = ()
+    seed_base: int = 0
+
+    @property
+    def mode(self) -> str:
+        return "csa" if self.k > 0 else "hca"
+
+    @property
+    def G(self) -> int:  # groups complete at the end of the stream
+        return self.T // self.m
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def schedule(self) -> list:
+        """Chunk lengths covering 0 .. T-1: the prefill chunks, then ones."""
+        sizes = list(self.chunks)
+        assert sum(sizes) <= self.T
+        return sizes + [1] * (self.T - sum(sizes))
+
+
+def make_sequence(sq: Sequence, device="cpu") -> dict:
+    """Draw a whole stream on the CPU generator (then move it to ``device``):
+      raw [B, T, d], logits [B, T] f32, q [B, T, H, d]; for CSA one index key
+      per group k_idx [B, G, dI], q_idx [B, T, HI, dI], w_idx [B, T, HI] f32.
+    Distributions as make_inputs."""
+    dt = sq.torch_dtype
+    out = {}
+    out["raw"] = _randn(sq, "raw", (sq.B, sq.T, sq.d), "cpu").to(dt)
+    out["logits"] = _randn(sq, "logits", (sq.B, sq.T), "cpu")
+    out["q"] = _randn(sq, "q", (sq.B, sq.T, sq.H, sq.d), "cpu").to(dt)
+    if sq.mode == "csa":
+        s = 1.0 / math.sqrt(sq.dI)
+        out["k_idx"] = _randn(sq, "k_idx", (sq.B, sq.G, sq.dI), "cpu", std=s).to(dt)
+        out["q_idx"] = _randn(sq, "q_idx", (sq.B, sq.T, sq.HI, sq.dI), "cpu", std=s).to(dt)
+        out["w_idx"] = torch.rand((sq.B, sq.T, sq.HI), generator=_gen(sq, "w_idx", "cpu"), dtype=torch.float32)
+    return {k: v.to(device) for k, v in out.items()}
