@@ -179,6 +179,135 @@ def bench_workload(wl, steps, warmup, with_kernel=True):
     return res
 
 
+LOOP_LAYERS = 2  # layer states alternating in the decode loop (the keys of one do not fit the Infinity Cache)
+
+
+def loop_bytes(sq) -> int:
+    """Algorithmic bytes of one decode cycle (m steps per layer, every layer): per step the
+    visible index keys, index query and weights, the selected and window rows, q, the fp32
+    output, the appended raw row and logit; per cycle one group's compression (its logits,
+    the entry write) and the appended index key."""
+    es = 2 if sq.dtype == "bf16" else 4
+    row_i = (sq.dI // 2 + sq.dI // 32) if sq.index_fmt == "mx4" else sq.dI * es
+    total = 0
+    for j in range(sq.m):
+        t = sq.T + j
+        nv = (t + 1) // sq.m
+        total += nv * row_i + sq.HI * sq.dI * es + sq.HI * 4
+        total += (min(sq.k, nv) + min(sq.W, t + 1)) * sq.d * es + sq.H * sq.d * es + sq.H * sq.d * 4 + 2 * sq.k * 4
+        total += sq.d * es + 4
+    total += sq.m * 4 + sq.d * es + row_i
+    return total * sq.B * LOOP_LAYERS
+
+
+def bench_loop(sq, cycles, warmup):
+    """Decode loop with cache maintenance: LOOP_LAYERS layers resumed at position T, one graph of m
+    decode steps on each (positions T .. T+m-1; the m-th emits a group), replayed."""
+    import torch
+
+    import long_context_compressed_06_amd as csa
+
+    B, m, R_ = sq.B, sq.m, None
+    g = torch.Generator(device="cuda")
+    g.manual_seed(sq.seed_base + 11)
+    rn = lambda *shape, std=1.0: torch.randn(shape, generator=g, device="cuda") * std
+    layers = []
+    for _ in range(LOOP_LAYERS):
+        L = csa.StreamingLayer(mode=sq.mode, B=B, H=sq.H, d=sq.d, m=m, W=sq.W, capacity=sq.T + m, chunk=1,
+                               dtype=sq.torch_dtype, k=sq.k, HI=sq.HI, dI=sq.dI, index_fmt=sq.index_fmt,
+                               scale=sq.scale)
+        N0 = sq.T // m
+        L.entries[:, :N0] = rn(B, N0, sq.d).to(L.entries.dtype)
+        kI = rn(B, N0, sq.dI, std=sq.dI ** -0.5).to(sq.torch_dtype)
+        if sq.index_fmt == "mx4":
+            c, s_ = csa.csa_mx4_quantize(kI)
+            L.k_codes[:, :N0], L.k_scales[:, :N0] = c, s_
+        else:
+            L.k_idx[:, :N0] = kI
+        del kI
+        half = rn(B, L.R, sq.d).to(sq.torch_dtype)
+        L.raw_ring[:, :L.R], L.raw_ring[:, L.R:] = half, half
+        lg = rn(B, L.R, 1)
+        L.logit_ring[:, :L.R], L.logit_ring[:, L.R:] = lg, lg
+        R_ = L.R
+        layers.append(L)
+    # per-step inputs (one token per sequence)
+    steps_in = []
+    for j in range(m):
+        x = {"raw": rn(B, 1, sq.d).to(sq.torch_dtype), "logits": rn(B, 1), "q": rn(B, 1, sq.H, sq.d).to(sq.torch_dtype),
+             "q_idx": rn(B, 1, sq.HI, sq.dI, std=sq.dI ** -0.5).to(sq.torch_dtype),
+             "w_idx": torch.rand((B, 1, sq.HI), generator=g, device="cuda"),
+             "k_idx_new": rn(B, 1, sq.dI, std=sq.dI ** -0.5).to(sq.torch_dtype)}
+        steps_in.append(x)
+    outs = [(torch.empty((B, 1, sq.H, sq.d), device="cuda"), torch.empty((B, 1, sq.H), device="cuda"),
+             torch.empty((B, 1, sq.k), dtype=torch.int32, device="cuda")) for _ in range(m * LOOP_LAYERS)]
+
+    def cycle():
+        for L in layers:
+            L.resume(sq.T)
+        for j in range(m):
+            x = steps_in[j]
+            for li, L in enumerate(layers):
+                o, l_, ti = outs[j * LOOP_LAYERS + li]
+                kin = x["k_idx_new"] if L.plan(1).g_new else None
+                L.step(x["raw"], x["logits"], x["q"], k_idx_new=kin, q_idx=x["q_idx"], w_idx=x["w_idx"], out=o,
+                       lse=l_, topk_idx=ti)
+
+    cycle()
+    torch.cuda.synchronize()
+    graph = capture(cycle)
+    ms = time_graphs([graph], cycles, warmup)
+    del graph, layers, steps_in, outs
+    torch.cuda.empty_cache()
+    return {"ms_per_cycle": ms, "ring_positions": R_}
+
+
+def bench_prefill(sq, reps, warmup):
+    """A whole prefill from position 0 through the streaming layer (chunks of sq.chunks), one graph."""
+    import torch
+
+    import long_context_compressed_06_amd as csa
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(sq.seed_base + 11)
+    rn = lambda shape, std=1.0: torch.randn(shape, generator=g, device="cuda") * std
+    B, T = sq.B, sq.T
+    dt = sq.torch_dtype
+    x = {"raw": rn((B, T, sq.d)).to(dt), "logits": rn((B, T)), "q": rn((B, T, sq.H, sq.d)).to(dt),
+         "k_idx": rn((B, T // sq.m, sq.dI), sq.dI ** -0.5).to(dt),
+         "q_idx": rn((B, T, sq.HI, sq.dI), sq.dI ** -0.5).to(dt),
+         "w_idx": torch.rand((B, T, sq.HI), generator=g, device="cuda")}
+    sched = sq.schedule()
+    C = max(sched)
+    layer = csa.StreamingLayer(mode=sq.mode, B=B, H=sq.H, d=sq.d, m=sq.m, W=sq.W, capacity=T, chunk=C, dtype=dt,
+                               k=sq.k, HI=sq.HI, dI=sq.dI, index_fmt=sq.index_fmt, scale=sq.scale)
+    out = torch.empty((B, C, sq.H, sq.d), device="cuda")
+    lse = torch.empty((B, C, sq.H), device="cuda")
+    idx = torch.empty((B, C, sq.k), dtype=torch.int32, device="cuda")
+    # contiguous per-chunk inputs, prepared once
+    chunks, p = [], 0
+    for n in sched:
+        chunks.append({k: x[k][:, p:p + n].contiguous() for k in ("raw", "logits", "q", "q_idx", "w_idx")})
+        p += n
+
+    def prefill():
+        layer.resume(0)
+        p = 0
+        for n, c in zip(sched, chunks):
+            pl = layer.plan(n)
+            layer.step(c["raw"], c["logits"], c["q"], k_idx_new=x["k_idx"][:, pl.g0:pl.g0 + pl.g_new],
+                       q_idx=c["q_idx"], w_idx=c["w_idx"], out=out[:, :n], lse=lse[:, :n], topk_idx=idx[:, :n])
+            p += n
+
+    prefill()
+    torch.cuda.synchronize()
+    graph = capture(prefill)
+    ms = time_graphs([graph], reps, warmup)
+    del graph, layer, x, chunks
+    torch.cuda.empty_cache()
+    return {"ms_per_prefill": ms, "chunks": len(sched), "chunk": C}
+
+
 def cpu_baseline(wl, min_seconds=10.0, max_reps=5):
     """The oracle, as it stands, on the same workload's inputs (host copies)."""
     import torch
@@ -212,8 +341,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2", help="c2 (default), c3 or c5")
-    ap.add_argument("--also", default="c3,c5,c2x,c5x",
-                    help="secondary decode workloads ('' for none); c2x/c5x: FP4 (MXFP4) indexer operands")
+    ap.add_argument("--also", default="c3,c5,c2x,c5x,l2,l2x,p1",
+                    help="secondary workloads ('' for none); c2x/c5x: FP4 (MXFP4) indexer operands; "
+                         "l2/l2x: decode loops with cache maintenance; p1: a whole chunked prefill from 0")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for the HBM byte counters)")
@@ -225,7 +355,7 @@ def main():
 
     import torch
 
-    from workloads import CONFIGS
+    from workloads import CONFIGS, LOOPS, PREFILLS
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl = CONFIGS[args.workload]
@@ -260,6 +390,29 @@ def main():
                             "bytes_per_launch": ab["indexer"], "avg_launch_us": r["indexer_ms"] * 1e3}
     also = {}
     for name in [a for a in args.also.split(",") if a and a != args.workload]:
+        if name in PREFILLS:
+            sq = PREFILLS[name]
+            log(f"[bench] also {sq}")
+            r2 = bench_prefill(sq, 3, 1)
+            also[sq.name] = {"tokens_per_s": sq.B * sq.T / (r2["ms_per_prefill"] * 1e-3),
+                             "ms_per_prefill": r2["ms_per_prefill"],
+                             "prefill": f"{sq.B} x {sq.T} tokens from position 0 in {r2['chunks']} chunks of "
+                                        f"{r2['chunk']}: append, compress, index-key append, index + top-k, "
+                                        f"attention per chunk"}
+            continue
+        if name in LOOPS:
+            sq = LOOPS[name]
+            log(f"[bench] also {sq}")
+            r2 = bench_loop(sq, max(5, args.steps // 4), max(2, args.warmup // 4))
+            toks = sq.B * sq.m * LOOP_LAYERS
+            b2 = loop_bytes(sq)
+            also[sq.name] = {"tokens_per_s": toks / (r2["ms_per_cycle"] * 1e-3),
+                             "ms_per_layer_step": r2["ms_per_cycle"] / (sq.m * LOOP_LAYERS),
+                             "step_hbm_frac": b2 / (r2["ms_per_cycle"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                             "algorithmic_bytes_per_cycle": b2,
+                             "cycle": f"{sq.m} decode steps x {LOOP_LAYERS} layers from position {sq.T}, "
+                                      f"ring of {r2['ring_positions']} positions, one group emitted per layer"}
+            continue
         w2 = CONFIGS[name]
         log(f"[bench] also {w2}")
         r2 = bench_workload(w2, max(10, args.steps // 2), args.warmup, with_kernel=False)

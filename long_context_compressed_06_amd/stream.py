@@ -114,6 +114,13 @@ class StreamingLayer:
         s = lo % self.R
         return ring[:, s:s + length]
 
+    def resume(self, pos: int):
+        """Continue a stream at position `pos` whose state the caller has put in place: entries (and
+        index keys) 0 .. pos//m - 1 and the ring's positions max(0, pos-R) .. pos-1 (both mirror slots)."""
+        if pos < 0 or pos // self.m > self.cap_e:
+            raise ValueError("position outside the layer's capacity")
+        self.pos, self.N = pos, pos // self.m
+
     def plan(self, n: int) -> ChunkPlan:
         return chunk_plan(self.pos, n, self.N, self.m, self.W, self.R)
 

@@ -131,3 +131,72 @@ def test_append_rows_exact(csa, row_shape, dtype, ring, pos0, n):
         else:
             want[:, p] = src[:, i]
     assert torch.equal(dst.cpu().view(torch.uint8), want.view(torch.uint8))
+
+
+@pytest.mark.parametrize("fmt", ["elem", "mx4"])
+def test_decode_loop_128k_resumed(csa, fmt):
+    """The benchmark's decode loop at its full context (two of its 32 sequences): a layer resumed at
+    position 131072 with 32768 cached entries decodes 4 tokens; the 4th emits group 32768 from the ring.
+    Every output is compared with the oracle over the same cache (the cached entries as given, the new
+    group compressed by the oracle, the window from the raw stream)."""
+    import dataclasses
+
+    import oracle as orc
+    from workloads import LOOPS
+
+    sq = dataclasses.replace(LOOPS["l2"], B=2, index_fmt=fmt, seed_base=86000)
+    say(sq)
+    B, T, m, d, H = sq.B, sq.T, sq.m, sq.d, sq.H
+    N0 = T // m
+    layer = csa.StreamingLayer(mode="csa", B=B, H=H, d=d, m=m, W=sq.W, capacity=T + m, chunk=1,
+                               dtype=sq.torch_dtype, k=sq.k, HI=sq.HI, dI=sq.dI, index_fmt=fmt, scale=sq.scale)
+    R = layer.R
+    g = torch.Generator().manual_seed(sq.seed_base)
+    rn = lambda *shape, std=1.0: (torch.randn(shape, generator=g) * std)
+    ent = rn(B, N0, d).to(torch.bfloat16)
+    kI = rn(B, N0 + 1, sq.dI, std=sq.dI ** -0.5).to(torch.bfloat16)
+    raw = rn(B, R + m, d).to(torch.bfloat16)     # positions T-R .. T+m-1
+    logits = rn(B, R + m)
+    q = rn(B, m, H, d).to(torch.bfloat16)
+    qi = rn(B, m, sq.HI, sq.dI, std=sq.dI ** -0.5).to(torch.bfloat16)
+    wi = torch.rand((B, m, sq.HI), generator=g)
+    # the cached state, put in place on the GPU
+    layer.entries[:, :N0] = ent.cuda()
+    if fmt == "mx4":
+        c, s = csa.csa_mx4_quantize(kI[:, :N0].contiguous().cuda())
+        layer.k_codes[:, :N0], layer.k_scales[:, :N0] = c, s
+    else:
+        layer.k_idx[:, :N0] = kI[:, :N0].cuda()
+    csa.csa_append_rows(raw[:, :R].cuda(), layer.raw_ring, T - R, ring=R)
+    csa.csa_append_rows(logits[:, :R].reshape(B, R, 1).cuda(), layer.logit_ring, T - R, ring=R)
+    layer.resume(T)
+    outs, lses, idxs = [], [], []
+    for j in range(m):
+        kin = kI[:, N0:N0 + 1].cuda() if layer.plan(1).g_new else None
+        o, l, ti = layer.step(raw[:, R + j:R + j + 1].cuda(), logits[:, R + j:R + j + 1].cuda(),
+                              q[:, j:j + 1].cuda(), k_idx_new=kin, q_idx=qi[:, j:j + 1].cuda(),
+                              w_idx=wi[:, j:j + 1].cuda())
+        outs.append(o.clone()), lses.append(l.clone()), idxs.append(ti.clone())
+    torch.cuda.synchronize()
+    assert layer.N == N0 + 1
+    # oracle: the new group from the raw stream, the cached entries as they are
+    rawh, logh = raw.float().numpy(), logits.numpy()
+    e_new = orc.compress(rawh[:, R:R + m], logh[:, R:R + m], m)
+    assert_close(layer.entries[:, N0:N0 + 1], e_new, "bf16", "emitted entry")
+    entries = np.concatenate([ent.float().numpy(), orc.round_bf16(e_new)], axis=1)
+    kih, qih = kI.float().numpy(), qi.float().numpy()
+    if fmt == "mx4":
+        kih = orc.mx4_dequantize(*orc.mx4_quantize(kih))
+        qih = orc.mx4_dequantize(*orc.mx4_quantize(qih))
+    s = orc.index_scores(qih, wi.numpy(), kih, m, T)
+    ridx = orc.topk(s, sq.k, m, T)
+    ro, rl = orc.sparse_mqa(q.float().numpy(), entries, ridx, rawh, T - R, sq.W, T, sq.scale)
+    gidx = np.concatenate([to_np(t) for t in idxs], axis=1)
+    nv = np.tile((T + np.arange(m) + 1) // m, (B, 1))
+    check_topk(gidx, ridx, s, nv, sq.k, "loop topk")
+    same = np.all(gidx == ridx, axis=2)
+    assert same.mean() >= 0.75
+    go = np.concatenate([to_np(t) for t in outs], axis=1)
+    gl = np.concatenate([to_np(t) for t in lses], axis=1)
+    assert_close(go[same], ro[same], "bf16", "loop out")
+    assert_close(gl[same], rl[same], "bf16", "loop lse", row_dims=1)

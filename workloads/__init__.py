@@ -222,3 +222,20 @@ def make_sequence(sq: Sequence, device="cpu") -> dict:
         out["q_idx"] = _randn(sq, "q_idx", (sq.B, sq.T, sq.HI, sq.dI), "cpu", std=s).to(dt)
         out["w_idx"] = torch.rand((sq.B, sq.T, sq.HI), generator=_gen(sq, "w_idx", "cpu"), dtype=torch.float32)
     return {k: v.to(device) for k, v in out.items()}
+
+
+# decode loops for the benchmark: the stream is resumed at position T (T // m
+# entries and their index keys in the cache, the ring holding the last raw
+# tokens) and decoded one token per sequence per step, a group emitted every
+# m steps; two layers' states alternate step by step
+LOOPS = {
+    "l2": Sequence("csa_decode_loop_B32_ctx128K", "bf16", B=32, T=131072, m=4, d=512, H=64, W=128, k=1024, HI=64,
+                   dI=128, seed_base=6000),
+}
+LOOPS["l2x"] = dataclasses.replace(LOOPS["l2"], name="csa_decode_loop_mx4idx_B32_ctx128K", index_fmt="mx4")
+
+# a whole prefill from position 0 through the streaming layer, in chunks
+PREFILLS = {
+    "p1": Sequence("csa_prefill_stream_B1_ctx64K_chunk4096", "bf16", B=1, T=65536, m=4, d=512, H=64, W=128,
+                   k=1024, HI=64, dI=128, chunks=(4096,) * 16, seed_base=7000),
+}
