@@ -64,6 +64,7 @@ def _load():
     lib.oracle_window_start.argtypes = [L, I]
     lib.oracle_window_start.restype = L
     lib.oracle_compress.argtypes = [I, I, I, I, P, P, P, I]
+    lib.oracle_compress_channels.argtypes = [I, I, I, I, P, P, P, I]
     lib.oracle_round_bf16.argtypes = [L, P, P]
     lib.oracle_index_scores.argtypes = [I, I, I, I, I, I, L, P, P, P, P, I]
     lib.oracle_topk.argtypes = [I, I, I, I, I, L, P, P, I]
@@ -71,7 +72,7 @@ def _load():
     lib.oracle_dense_mqa.argtypes = [I, I, I, I, I, I, I, L, D, P, P, P, L, I, P, P, I]
     lib.oracle_mx4_quantize.argtypes = [L, P, P, P]
     lib.oracle_mx4_dequantize.argtypes = [L, P, P, P]
-    for f in ("oracle_compress", "oracle_round_bf16", "oracle_index_scores", "oracle_topk",
+    for f in ("oracle_compress", "oracle_compress_channels", "oracle_round_bf16", "oracle_index_scores", "oracle_topk",
               "oracle_sparse_mqa", "oracle_dense_mqa", "oracle_mx4_quantize", "oracle_mx4_dequantize"):
         getattr(lib, f).restype = None
     _lib = lib
@@ -116,6 +117,18 @@ def compress(raw, logits, m: int, nthreads: int | None = None) -> np.ndarray:
     G = Tm // m
     out = np.empty((B, G, d), dtype=np.float64)
     _load().oracle_compress(B, G, m, d, _ptr(raw), _ptr(logits), _ptr(out), nthreads or default_threads())
+    return out
+
+
+def compress_channels(raw, logits, m: int, nthreads: int | None = None) -> np.ndarray:
+    """raw [B, G*m, d], per-channel logits [B, G*m, d] -> exact pooled entries [B, G, d] (float64)."""
+    raw = _f32(raw)
+    logits = _f32(logits)
+    B, Tm, d = raw.shape
+    assert Tm % m == 0 and logits.shape == (B, Tm, d)
+    G = Tm // m
+    out = np.empty((B, G, d), dtype=np.float64)
+    _load().oracle_compress_channels(B, G, m, d, _ptr(raw), _ptr(logits), _ptr(out), nthreads or default_threads())
     return out
 
 

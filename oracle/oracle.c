@@ -139,6 +139,40 @@ void oracle_compress(int B, int G, int m, int d, const float *raw, const float *
     parallel_for((long)B * G, nthreads, compress_item, &c);
 }
 
+/* ------------------------------------------------------------------ */
+/* Step 1 with per-channel pooling logits (a reading of the overview   */
+/* page, section 2.2 step 1, which leaves the form of the learnable    */
+/* softmax weights open): channel x of entry g pools channel x of its  */
+/* m tokens with the softmax over the group of that channel's logits,  */
+/*   e_g[x] = sum_i softmax_i(z[g*m+i, x]) * c[g*m+i, x].              */
+/* Output is the exact (unrounded) double value.                        */
+/* ------------------------------------------------------------------ */
+static void compress_channels_item(void *vctx, long item) {
+    compress_ctx *c = (compress_ctx *)vctx;
+    long b = item / c->G, g = item % c->G;
+    const float *z = c->logits + (b * c->G + g) * (long)c->m * c->d;  /* [m, d] */
+    const float *rows = c->raw + (b * c->G + g) * (long)c->m * c->d;  /* [m, d] */
+    double *e = c->out + (b * c->G + g) * (long)c->d;
+    int i, x;
+    for (x = 0; x < c->d; x++) {
+        double zmax = -INFINITY, denom = 0.0, acc = 0.0;
+        for (i = 0; i < c->m; i++)
+            if ((double)z[(long)i * c->d + x] > zmax) zmax = (double)z[(long)i * c->d + x];
+        for (i = 0; i < c->m; i++) {
+            double a = exp((double)z[(long)i * c->d + x] - zmax);
+            denom += a;
+            acc += a * (double)rows[(long)i * c->d + x];
+        }
+        e[x] = acc / denom;
+    }
+}
+
+void oracle_compress_channels(int B, int G, int m, int d, const float *raw, const float *logits,
+                              double *out, int nthreads) {
+    compress_ctx c = {G, m, d, raw, logits, out};
+    parallel_for((long)B * G, nthreads, compress_channels_item, &c);
+}
+
 /* Round-to-nearest-even of a double to the bfloat16 grid (8 significant
  * bits, exponent range of IEEE single), returned as a float.  This is the
  * rounding the compressed cache applies when it is stored in bf16. */

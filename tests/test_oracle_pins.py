@@ -110,6 +110,62 @@ def test_compress_m1_identity(orc):
     np.testing.assert_array_equal(orc.compress(raw, logits, 1), raw.astype(np.float64))
 
 
+# per-channel pooling logits (the pages leave the form of the softmax weights open)
+def test_compress_channels_equal_logits_reduce_to_token_logits(orc):
+    r = rng(41)
+    B, G, m, d = 2, 5, 4, 24
+    raw = r.standard_normal((B, G * m, d)).astype(np.float32)
+    z = r.standard_normal((B, G * m)).astype(np.float32)
+    zc = np.repeat(z[:, :, None], d, axis=2)
+    np.testing.assert_allclose(orc.compress_channels(raw, zc, m), orc.compress(raw, z, m), rtol=1e-14, atol=1e-15)
+    r2 = rng(42)
+    raw = r2.standard_normal((1, 2 * 128, 8)).astype(np.float32)
+    z = r2.standard_normal((1, 2 * 128)).astype(np.float32)
+    np.testing.assert_allclose(orc.compress_channels(raw, np.repeat(z[:, :, None], 8, axis=2), 128),
+                               orc.compress(raw, z, 128), rtol=1e-13, atol=1e-15)
+
+
+def test_compress_channels_closed_form_weights(orc):
+    # channel 0: logits log(1..4) -> weights 0.1 0.2 0.3 0.4; channel 1: reversed; channel 2: equal
+    raw = np.array([[[1, 10, 3], [2, 20, 5], [4, 40, 7], [8, 80, 11]]], dtype=np.float32)
+    lg = np.log(np.array([[1, 4, 5], [2, 3, 5], [3, 2, 5], [4, 1, 5]], dtype=np.float64)).astype(np.float32)[None]
+    out = orc.compress_channels(raw, lg, 4)[0, 0]
+    want = [0.1 * 1 + 0.2 * 2 + 0.3 * 4 + 0.4 * 8, 0.4 * 10 + 0.3 * 20 + 0.2 * 40 + 0.1 * 80, (3 + 5 + 7 + 11) / 4]
+    np.testing.assert_allclose(out, want, rtol=1e-6)  # (the float32 logits of log k carry ~1e-7 error)
+
+
+def test_compress_channels_one_hot_per_channel(orc):
+    r = rng(43)
+    B, G, m, d = 2, 3, 4, 10
+    raw = r.standard_normal((B, G * m, d)).astype(np.float32)
+    z = np.zeros((B, G * m, d), dtype=np.float32)
+    pick = r.integers(0, m, size=(B, G, d))
+    for b in range(B):
+        for g in range(G):
+            for x in range(d):
+                z[b, g * m + pick[b, g, x], x] = 80.0
+    out = orc.compress_channels(raw, z, m)
+    for b in range(B):
+        for g in range(G):
+            for x in range(d):
+                assert abs(out[b, g, x] - raw[b, g * m + pick[b, g, x], x]) <= 1e-30
+
+
+def test_compress_channels_permutation_shift_and_bounds(orc):
+    r = rng(44)
+    B, G, m, d = 2, 4, 128, 9
+    raw = r.standard_normal((B, G * m, d)).astype(np.float32)
+    z = (np.round(r.uniform(-2, 2, size=(B, G * m, d)) * 64) / 64).astype(np.float32)  # exact under integer shifts
+    out = orc.compress_channels(raw, z, m)
+    perm = r.permutation(d)
+    np.testing.assert_array_equal(orc.compress_channels(raw[:, :, perm], z[:, :, perm], m), out[:, :, perm])
+    shift = np.repeat(r.integers(-300, 300, size=(B, G, 1, d)), m, axis=2).reshape(B, G * m, d).astype(np.float32)
+    np.testing.assert_allclose(orc.compress_channels(raw, z + shift, m), out, rtol=1e-13, atol=1e-15)
+    grp = raw.astype(np.float64).reshape(B, G, m, d)
+    assert np.all(out <= grp.max(axis=2) + 1e-12) and np.all(out >= grp.min(axis=2) - 1e-12)
+    np.testing.assert_array_equal(orc.compress_channels(raw[:, :7], z[:, :7], 1), raw[:, :7].astype(np.float64))
+
+
 def test_compress_batches_and_groups_independent(orc):
     r = rng(6)
     B, G, m, d = 4, 3, 4, 6
