@@ -96,6 +96,25 @@ int csa_compress(int dt, int B, int G, int m, int d,
                  void *out, int64_t out_bstride, void *stream);
 
 /*
+ * csa_compress_channels -- group compression with per-channel pooling
+ * logits (overview page, section 2.2 step 1: the compression weights come
+ * from a learnable softmax normalisation; this is the per-channel form of
+ * it).  For batch b, group g < G and channel x < d:
+ *     alpha_i[x] = softmax_i(logits[b, g*m + i, x]),  i < m
+ *     out[b, g, x] = sum_i alpha_i[x] * raw[b, g*m + i, x]
+ * rounded once to `dt`.  The same call pools an index-key stream into the
+ * entries' index keys (d = d_I) when those keys are produced by the compressor.
+ *   raw     [B, G*m, d]  dt,  batch stride raw_bstride elements
+ *   logits  [B, G*m, d]  f32, batch stride logit_bstride elements (multiple of 4)
+ *   out     [B, G, d]    dt,  batch stride out_bstride elements
+ * raw, logits and out 16-byte aligned; `out` must not overlap raw or logits.
+ */
+int csa_compress_channels(int dt, int B, int G, int m, int d,
+                          const void *raw, int64_t raw_bstride,
+                          const float *logits, int64_t logit_bstride,
+                          void *out, int64_t out_bstride, void *stream);
+
+/*
  * csa_append_rows -- cache maintenance between steps (overview page, section
  * 2.2 step 1: the raw tokens of a group are kept until its m-th token
  * arrives and the group becomes one entry; the window of raw tokens is kept

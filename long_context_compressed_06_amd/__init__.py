@@ -22,7 +22,8 @@ _STATUS = {0: "CSA_OK", -1: "CSA_EINVAL", -2: "CSA_EDTYPE", -3: "CSA_EALIGN", -4
            -5: "CSA_EHIP", -6: "CSA_EUNSUPPORTED"}
 EXPORTS = ("csa_abi_version", "csa_status_string", "csa_last_error_detail", "csa_compress",
            "csa_index_topk_workspace_bytes", "csa_index_topk", "csa_index_scores", "csa_mqa_workspace_bytes",
-           "csa_sparse_mqa", "hca_dense_mqa", "csa_mx4_quantize", "csa_index_topk_mx4", "csa_append_rows")
+           "csa_sparse_mqa", "hca_dense_mqa", "csa_mx4_quantize", "csa_index_topk_mx4", "csa_append_rows",
+           "csa_compress_channels")
 
 
 class CsaError(RuntimeError):
@@ -67,6 +68,8 @@ def lib():
     L.csa_index_topk_mx4.argtypes = [I, I, I, I, I, I, I, I, I64, P, P, P, P, I64, P, P, P, SZ, P]
     L.csa_index_topk_mx4.restype = I
     L.csa_append_rows.argtypes = [I, I, I64, P, I64, P, I64, I64, I64, I64, P]
+    L.csa_compress_channels.argtypes = [I, I, I, I, I, P, I64, P, I64, P, I64, P]
+    L.csa_compress_channels.restype = I
     L.csa_append_rows.restype = I
     _lib = L
     return L
@@ -251,6 +254,25 @@ def csa_append_rows(rows: torch.Tensor, dst: torch.Tensor, pos0: int, ring: int 
     _check(lib().csa_append_rows(B, n, per_row * es, _p(rows), rows.stride(0) * es, _p(dst), dst.stride(0) * es,
                                  dst.shape[1], pos0, ring, _stream(rows)))
     return dst
+
+
+def csa_compress_channels(raw: torch.Tensor, logits: torch.Tensor, m: int, out: torch.Tensor) -> torch.Tensor:
+    """raw [B, G*m, d], per-channel logits [B, G*m, d] f32 -> out [B, G, d] (written in place)."""
+    _need(raw, "raw", dims=3)
+    _need(logits, "logits", torch.float32, 3)
+    _need(out, "out", raw.dtype, 3)
+    B, Gm, d = raw.shape
+    if Gm % m:
+        raise ValueError("raw rows must be a multiple of m")
+    G = Gm // m
+    for t, n in ((raw, "raw"), (out, "out"), (logits, "logits")):
+        if t.stride(1) != d:
+            raise ValueError(f"{n} rows must be packed")
+    if out.shape != (B, G, d) or logits.shape != (B, Gm, d):
+        raise ValueError("shape mismatch between raw, logits and out")
+    _check(lib().csa_compress_channels(_dt(raw), B, G, m, d, _p(raw), _bstride(raw), _p(logits), _bstride(logits),
+                                       _p(out), _bstride(out), _stream(raw)))
+    return out
 
 
 def mqa_workspace_bytes(B, Tq, H, d, n_rows_max) -> int:

@@ -100,6 +100,30 @@ int csa_compress(int dt, int B, int G, int m, int d, const void *raw, int64_t ra
                       "compress launch");
 }
 
+int csa_compress_channels(int dt, int B, int G, int m, int d, const void *raw, int64_t raw_bstride,
+                          const float *logits, int64_t logit_bstride, void *out, int64_t out_bstride, void *stream) {
+    if (int s = check_dt(dt)) return s;
+    if (B < 0 || G < 0) return fail(CSA_EINVAL, "B=%d and G=%d must be >= 0", B, G);
+    if (m < 1 || m > 128) return fail(CSA_EUNSUPPORTED, "m=%d outside 1..128", m);
+    if (!d_supported(d)) return fail(CSA_EUNSUPPORTED, "d=%d not in {32,64,128,256,512}", d);
+    if ((int64_t)B * G == 0) return ok();
+    if (!raw || !logits || !out) return fail(CSA_EINVAL, "NULL tensor pointer");
+    if (raw_bstride < (int64_t)G * m * d || logit_bstride < (int64_t)G * m * d || out_bstride < (int64_t)G * d)
+        return fail(CSA_EINVAL, "a batch stride is smaller than one batch's extent");
+    if (!aligned(raw, 16) || !aligned(out, 16) || !aligned(logits, 16) || raw_bstride % 8 || out_bstride % 8 ||
+        logit_bstride % 4)
+        return fail(CSA_EALIGN, "raw/out/logits need 16-byte alignment, raw/out batch strides a multiple of 8 "
+                                "elements and the logits' a multiple of 4");
+    const size_t es = esize(dt);
+    const Span so = span(out, B, out_bstride, (int64_t)G * d, es);
+    if (overlap(so, span(raw, B, raw_bstride, (int64_t)G * m * d, es)) ||
+        overlap(so, span(logits, B, logit_bstride, (int64_t)G * m * d, 4)))
+        return fail(CSA_EINVAL, "out overlaps raw or logits");
+    return hip_status(csa::launch_compress_channels(dt, B, G, m, d, raw, raw_bstride, logits, logit_bstride, out,
+                                                    out_bstride, (hipStream_t)stream),
+                      "compress launch");
+}
+
 int csa_append_rows(int B, int n, int64_t row_bytes, const void *rows, int64_t rows_bstride, void *dst,
                     int64_t dst_bstride, int64_t dst_rows, int64_t pos0, int64_t ring, void *stream) {
     if (B < 0 || n < 0) return fail(CSA_EINVAL, "B=%d and n=%d must be >= 0", B, n);

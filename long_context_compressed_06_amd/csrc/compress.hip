@@ -73,6 +73,82 @@ __global__ __launch_bounds__(256) void k_compress(int G, int m, int d, int tpr, 
     }
 }
 
+// Per-channel pooling logits: channel x of entry g pools channel x of the
+// group's m rows with the softmax over those rows of logits[., x].  Same
+// partition as k_compress (row slots x 16-byte column vectors, at most
+// kRowsPerThread rows per thread, every load in flight at once); each thread
+// keeps, per column, the maximum of its rows' logits, the sum of their
+// exponentials and the weighted sum of the rows, and the row slots are merged
+// through LDS by rescaling to the common maximum.
+template <typename T>
+__global__ __launch_bounds__(256) void k_compress_channels(int G, int m, int d, int tpr, int slices,
+                                                           const T *__restrict__ raw, int64_t raw_bs,
+                                                           const float *__restrict__ logits, int64_t log_bs,
+                                                           T *__restrict__ out, int64_t out_bs) {
+    constexpr int VEC = 16 / sizeof(T);
+    __shared__ float red[3][256 * VEC];  // per row slot and column: max, sum of exponentials, weighted sum
+
+    const int sl = blockIdx.x % slices;
+    const int bg = blockIdx.x / slices;
+    const int b = bg / G, g = bg % G;
+    const int tid = threadIdx.x;
+    const int rpar = 256 / tpr;
+    const int c = tid % tpr, rs = tid / tpr;
+    const int width = tpr * VEC;
+    const int64_t col0 = (int64_t)sl * width + c * VEC;
+    const T *rows = raw + b * raw_bs + (int64_t)g * m * d + col0;
+    const float *zr = logits + b * log_bs + (int64_t)g * m * d + col0;
+    u32x4 v[kRowsPerThread];
+    float z[kRowsPerThread][VEC];
+#pragma unroll
+    for (int u = 0; u < kRowsPerThread; ++u) {
+        const int i = rs + u * rpar;
+        v[u] = i < m ? *(const u32x4 *)(rows + (int64_t)i * d) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int q = 0; q < VEC / 4; ++q) {
+            const floatx4 zz = i < m ? *(const floatx4 *)(zr + (int64_t)i * d + 4 * q)
+                                     : floatx4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z[u][4 * q + e] = zz[e];
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kRowsPerThread; ++u) mx = fmaxf(mx, z[u][e]);
+        float s = 0.f, a = 0.f;
+        if (mx > -INFINITY) {
+#pragma unroll
+            for (int u = 0; u < kRowsPerThread; ++u) {
+                const float w = expf(z[u][e] - mx);  // rows past m: exp(-inf) = 0
+                s += w;
+                a += w * Elem<T>::to_f32(((const T *)&v[u])[e]);
+            }
+        }
+        const int x = rs * width + c * VEC + e;
+        red[0][x] = mx;
+        red[1][x] = s;
+        red[2][x] = a;
+    }
+    __syncthreads();
+    T *o = out + b * out_bs + (int64_t)g * d + (int64_t)sl * width;
+    for (int x = tid; x < width; x += 256) {
+        float M = -INFINITY;
+        for (int r = 0; r < rpar; ++r) M = fmaxf(M, red[0][r * width + x]);
+        float S = 0.f, A = 0.f;
+        for (int r = 0; r < rpar; ++r) {
+            const float mr = red[0][r * width + x];
+            if (mr > -INFINITY) {
+                const float f = expf(mr - M);
+                S += f * red[1][r * width + x];
+                A += f * red[2][r * width + x];
+            }
+        }
+        o[x] = Elem<T>::from_f32(A / S);
+    }
+}
+
 template <typename T>
 hipError_t launch_compress_t(int B, int G, int m, int d, const void *raw, int64_t raw_bs, const float *logits,
                              int64_t log_bs, void *out, int64_t out_bs, hipStream_t st) {
@@ -87,6 +163,27 @@ hipError_t launch_compress_t(int B, int G, int m, int d, const void *raw, int64_
     hipLaunchKernelGGL(k_compress<T>, dim3((unsigned)((int64_t)B * G * slices)), dim3(256), 0, st, G, m, d, tpr,
                        slices, (const T *)raw, raw_bs, logits, log_bs, (T *)out, out_bs);
     return hipGetLastError();
+}
+template <typename T>
+hipError_t launch_compress_channels_t(int B, int G, int m, int d, const void *raw, int64_t raw_bs,
+                                      const float *logits, int64_t log_bs, void *out, int64_t out_bs,
+                                      hipStream_t st) {
+    constexpr int VEC = 16 / sizeof(T);
+    int tpr = d / VEC;
+    if (tpr > 256 || tpr < 1) return hipErrorInvalidValue;
+    while (tpr > 1 && (256 / tpr) * kRowsPerThread < m) tpr /= 2;
+    if ((256 / tpr) * kRowsPerThread < m) return hipErrorInvalidValue;
+    const int slices = d / VEC / tpr;
+    hipLaunchKernelGGL(k_compress_channels<T>, dim3((unsigned)((int64_t)B * G * slices)), dim3(256), 0, st, G, m,
+                       d, tpr, slices, (const T *)raw, raw_bs, logits, log_bs, (T *)out, out_bs);
+    return hipGetLastError();
+}
+hipError_t launch_compress_channels(int dt, int B, int G, int m, int d, const void *raw, int64_t raw_bs,
+                                    const float *logits, int64_t log_bs, void *out, int64_t out_bs,
+                                    hipStream_t st) {
+    if (dt == 0)
+        return launch_compress_channels_t<float>(B, G, m, d, raw, raw_bs, logits, log_bs, out, out_bs, st);
+    return launch_compress_channels_t<bf16_t>(B, G, m, d, raw, raw_bs, logits, log_bs, out, out_bs, st);
 }
 hipError_t launch_compress(int dt, int B, int G, int m, int d, const void *raw, int64_t raw_bs,
                            const float *logits, int64_t log_bs, void *out, int64_t out_bs, hipStream_t st) {

@@ -35,6 +35,10 @@ size_t topk_clear_words(int64_t rows, int64_t N);
 
 hipError_t launch_compress(int dt, int B, int G, int m, int d, const void *raw, int64_t raw_bs,
                            const float *logits, int64_t log_bs, void *out, int64_t out_bs, hipStream_t st);
+// logits: [B][G*m][d] f32 (per channel), batch stride log_bs elements
+hipError_t launch_compress_channels(int dt, int B, int G, int m, int d, const void *raw, int64_t raw_bs,
+                                    const float *logits, int64_t log_bs, void *out, int64_t out_bs,
+                                    hipStream_t st);
 
 // scores: [rows][s_stride] (s_stride >= N); scores2: optional second copy,
 // [rows][N]; hist: optional [rows, kTopkBins] counts, must be zero on entry

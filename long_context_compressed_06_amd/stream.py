@@ -21,12 +21,17 @@ decoding is a chunk of one token.  A chunk of n tokens at p0 .. p0+n-1:
   1. appends their raw rows and logits to the rings;
   2. compresses the groups that complete inside the chunk (N .. (p0+n)//m - 1)
      out of the ring;
-  3. appends those groups' index keys (one per group, given by the caller:
-     the index-key projection is outside this path), quantised to MXFP4 when
-     the indexer runs on FP4;
+  3. appends those groups' index keys: one per group given by the caller
+     (index_keys="given"), or pooled by the same compressor from per-token
+     index keys kept in their own ring (index_keys="pooled"), quantised to
+     MXFP4 when the indexer runs on FP4;
   4. runs the indexer and top-k for the chunk's queries (CSA);
   5. runs the attention over the selected (CSA) or all visible (HCA)
      entries plus the raw window, read out of the ring.
+Pooling logits are one per token (pool="token") or one per token and
+channel (pool="channel", csa_compress_channels); pooled index keys use the
+entry's weights with per-token logits and their own per-channel logits with
+per-channel pooling.
 Every step is a call into libcsa; this module keeps positions and views.
 """
 from __future__ import annotations
@@ -35,8 +40,8 @@ import dataclasses
 
 import torch
 
-from . import (csa_append_rows, csa_compress, csa_index_topk, csa_index_topk_mx4, csa_mx4_quantize,
-               csa_sparse_mqa, hca_dense_mqa, index_topk_workspace_bytes, mqa_workspace_bytes)
+from . import (csa_append_rows, csa_compress, csa_compress_channels, csa_index_topk, csa_index_topk_mx4,
+               csa_mx4_quantize, csa_sparse_mqa, hca_dense_mqa, index_topk_workspace_bytes, mqa_workspace_bytes)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -80,10 +85,14 @@ class StreamingLayer:
 
     def __init__(self, *, mode: str, B: int, H: int, d: int, m: int, W: int, capacity: int, chunk: int,
                  dtype=torch.bfloat16, k: int = 0, HI: int = 0, dI: int = 0, index_fmt: str = "elem",
-                 scale: float | None = None, device="cuda"):
+                 scale: float | None = None, pool: str = "token", index_keys: str = "given", device="cuda"):
         assert mode in ("csa", "hca") and index_fmt in ("elem", "mx4")
+        assert pool in ("token", "channel") and index_keys in ("given", "pooled")
         if mode == "csa" and (k < 1 or HI < 1 or dI < 1):
             raise ValueError("CSA needs k, HI and dI")
+        if index_keys == "pooled" and index_fmt == "mx4":
+            raise ValueError("pooled index keys are built for element-type index keys only")
+        self.pool, self.index_keys = pool, index_keys
         self.mode, self.B, self.H, self.d, self.m, self.W = mode, B, H, d, m, W
         self.k, self.HI, self.dI, self.index_fmt = k, HI, dI, index_fmt
         self.chunk, self.capacity, self.dtype, self.device = chunk, capacity, dtype, device
@@ -91,7 +100,8 @@ class StreamingLayer:
         self.R = ring_size(chunk, m, W)
         self.cap_e = max(1, capacity // m)
         self.raw_ring = torch.zeros((B, 2 * self.R, d), dtype=dtype, device=device)
-        self.logit_ring = torch.zeros((B, 2 * self.R, 1), dtype=torch.float32, device=device)
+        self.logit_ring = torch.zeros((B, 2 * self.R, d if pool == "channel" else 1), dtype=torch.float32,
+                                      device=device)
         self.entries = torch.zeros((B, self.cap_e, d), dtype=dtype, device=device)
         if mode == "csa":
             if index_fmt == "mx4":
@@ -99,6 +109,10 @@ class StreamingLayer:
                 self.k_scales = torch.zeros((B, self.cap_e, dI // 32), dtype=torch.uint8, device=device)
             else:
                 self.k_idx = torch.zeros((B, self.cap_e, dI), dtype=dtype, device=device)
+            if index_keys == "pooled":
+                self.kidx_ring = torch.zeros((B, 2 * self.R, dI), dtype=dtype, device=device)
+                if pool == "channel":
+                    self.kidx_logit_ring = torch.zeros((B, 2 * self.R, dI), dtype=torch.float32, device=device)
             # (the selection's and the attention's plans change with the number of queries: the
             # workspaces cover every chunk length up to `chunk`, at the full entry capacity)
             nb = max(index_topk_workspace_bytes(B, t, self.cap_e, HI, k) for t in range(1, chunk + 1))
@@ -124,12 +138,22 @@ class StreamingLayer:
     def plan(self, n: int) -> ChunkPlan:
         return chunk_plan(self.pos, n, self.N, self.m, self.W, self.R)
 
+    def _pool(self, rows: torch.Tensor, logits: torch.Tensor, out: torch.Tensor):
+        if self.pool == "channel":
+            csa_compress_channels(rows, logits, self.m, out)
+        else:
+            csa_compress(rows, logits[..., 0], self.m, out)
+
     def step(self, raw: torch.Tensor, logits: torch.Tensor, q: torch.Tensor, k_idx_new: torch.Tensor | None = None,
              q_idx: torch.Tensor | None = None, w_idx: torch.Tensor | None = None, out: torch.Tensor | None = None,
-             lse: torch.Tensor | None = None, topk_idx: torch.Tensor | None = None):
-        """Advance by one chunk.  raw [B, n, d], logits [B, n] f32, q [B, n, H, d]; CSA also k_idx_new
-        [B, g_new, dI] (index keys of the groups completing in the chunk), q_idx [B, n, HI, dI], w_idx
-        [B, n, HI].  Returns (out [B, n, H, d] f32, lse [B, n, H], topk_idx [B, n, k] or None)."""
+             lse: torch.Tensor | None = None, topk_idx: torch.Tensor | None = None,
+             k_idx_tokens: torch.Tensor | None = None, k_idx_logits: torch.Tensor | None = None):
+        """Advance by one chunk.  raw [B, n, d], logits [B, n] f32 (pool "token") or [B, n, d] (pool
+        "channel"), q [B, n, H, d]; CSA also q_idx [B, n, HI, dI], w_idx [B, n, HI] and the index keys:
+        k_idx_new [B, g_new, dI] (those of the groups completing in the chunk; index_keys "given") or
+        k_idx_tokens [B, n, dI] (per token, pooled into the entries' keys; index_keys "pooled", with
+        k_idx_logits [B, n, dI] f32 under per-channel pooling).
+        Returns (out [B, n, H, d] f32, lse [B, n, H], topk_idx [B, n, k] or None)."""
         B, n = raw.shape[0], raw.shape[1]
         q = q.contiguous()
         if self.mode == "csa":
@@ -141,13 +165,16 @@ class StreamingLayer:
             raise ValueError("entry capacity exhausted")
         # 1. raw rows and logits into the rings
         csa_append_rows(raw, self.raw_ring, p.p0, ring=self.R)
-        csa_append_rows(logits.reshape(B, n, 1), self.logit_ring, p.p0, ring=self.R)
+        csa_append_rows(logits.reshape(B, n, self.logit_ring.shape[2]), self.logit_ring, p.p0, ring=self.R)
+        if self.mode == "csa" and self.index_keys == "pooled":
+            csa_append_rows(k_idx_tokens, self.kidx_ring, p.p0, ring=self.R)
+            if self.pool == "channel":
+                csa_append_rows(k_idx_logits, self.kidx_logit_ring, p.p0, ring=self.R)
         # 2. the groups completing in this chunk
         if p.g_new > 0:
             L = p.g_new * self.m
-            csa_compress(self._ring_view(self.raw_ring, p.comp_lo, L),
-                         self._ring_view(self.logit_ring, p.comp_lo, L)[..., 0],
-                         self.m, self.entries[:, p.g0:p.g0 + p.g_new])
+            self._pool(self._ring_view(self.raw_ring, p.comp_lo, L), self._ring_view(self.logit_ring, p.comp_lo, L),
+                       self.entries[:, p.g0:p.g0 + p.g_new])
         N = p.g0 + p.g_new
         raw_win = self._ring_view(self.raw_ring, p.win_lo, p.win_len)
         if out is None:
@@ -156,7 +183,12 @@ class StreamingLayer:
             lse = torch.empty((B, n, self.H), dtype=torch.float32, device=raw.device)
         if self.mode == "csa":
             # 3. their index keys
-            if p.g_new > 0:
+            if p.g_new > 0 and self.index_keys == "pooled":
+                L = p.g_new * self.m
+                lg = self.kidx_logit_ring if self.pool == "channel" else self.logit_ring
+                self._pool(self._ring_view(self.kidx_ring, p.comp_lo, L), self._ring_view(lg, p.comp_lo, L),
+                           self.k_idx[:, p.g0:p.g0 + p.g_new])
+            elif p.g_new > 0:
                 if k_idx_new is None or k_idx_new.shape[1] != p.g_new:
                     raise ValueError(f"the chunk completes {p.g_new} groups: k_idx_new must hold {p.g_new} rows")
                 if self.index_fmt == "mx4":

@@ -70,13 +70,23 @@ def oracle_step(wl, xh: dict, rows=None) -> dict:
 def oracle_sequence(sq, xh: dict) -> dict:
     """Oracle results for a whole stream processed from position 0 (host inputs of make_sequence)."""
     G, m = sq.G, sq.m
-    e = orc.compress(xh["raw"][:, :G * m], xh["logits"][:, :G * m], m) if G > 0 else None
+    pool = orc.compress_channels if sq.pool == "channel" else orc.compress
+    store = (lambda v: orc.round_bf16(v)) if sq.dtype == "bf16" else (lambda v: v.astype(np.float32))
+    e = pool(xh["raw"][:, :G * m], xh["logits"][:, :G * m], m) if G > 0 else None
     ent = np.zeros((sq.B, max(G, 1), sq.d), dtype=np.float32)
     if G > 0:
-        ent[:, :G] = orc.round_bf16(e) if sq.dtype == "bf16" else e.astype(np.float32)
+        ent[:, :G] = store(e)
     res = {"e": e}
     if sq.mode == "csa":
-        qi, ki = xh["q_idx"], xh["k_idx"]
+        if sq.index_keys == "pooled":
+            # the entries' index keys pooled by the same compressor, stored in the cache's type
+            lg = xh["k_idx_logits"] if sq.pool == "channel" else xh["logits"]
+            kp = pool(xh["k_idx_tokens"][:, :G * m], lg[:, :G * m], m)
+            res["k_pooled"] = kp
+            ki = store(kp)
+        else:
+            ki = xh["k_idx"]
+        qi = xh["q_idx"]
         if sq.index_fmt == "mx4":
             qi = orc.mx4_dequantize(*orc.mx4_quantize(qi))
             ki = orc.mx4_dequantize(*orc.mx4_quantize(ki))

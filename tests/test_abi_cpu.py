@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
     import long_context_compressed_06_amd as csa
 
     names = header_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(L, n), n
     assert sorted(csa.EXPORTS) == names
@@ -178,3 +178,25 @@ def test_append_rows_rejects_bad_arguments(L):
     assert call(dst=P + 0x100) == -1           # destination overlaps the rows
     assert call(B=0, rows=None, dst=None) == 0  # nothing to do
     assert call(n=0, rows=None, dst=None) == 0
+
+
+def test_compress_channels_rejects_bad_arguments(L):
+    f = L.csa_compress_channels
+
+    def call(dt=1, B=2, G=3, m=4, d=128, raw=P, rbs=None, logits=P + 0x100000, lbs=None, out=P + 0x200000,
+             obs=None):
+        rbs = G * m * d if rbs is None else rbs
+        lbs = G * m * d if lbs is None else lbs
+        obs = G * d if obs is None else obs
+        return f(dt, B, G, m, d, raw, rbs, logits, lbs, out, obs, None)
+
+    assert call(dt=7) == -2
+    assert call(m=0) == -6 and call(m=129) == -6
+    assert call(d=96) == -6
+    assert call(B=-1) == -1
+    assert call(logits=None) == -1
+    assert call(lbs=3 * 4 * 128 - 4) == -1     # below one batch of per-channel logits
+    assert call(logits=P + 0x100004) == -3     # logits need 16-byte alignment
+    assert call(lbs=3 * 4 * 128 + 2) == -3     # logit batch stride not a multiple of 4
+    assert call(out=P + 0x100000 + 64) == -1   # out overlaps the logits
+    assert call(G=0, raw=None, logits=None, out=None) == 0

@@ -50,6 +50,17 @@ CASES = [
              chunks=(129, 256, 300), seed_base=84000),
     Sequence("hca_stream_bf16", "bf16", B=2, T=128 * 5 + 60, m=128, d=128, H=8, W=128, chunks=(300, 200),
              seed_base=85000),
+    # per-channel pooling logits and index keys pooled by the same compressor
+    Sequence("csa_stream_bf16_pooled_index_keys", "bf16", B=2, T=4 * 100 + 2, m=4, d=128, H=8, W=16, k=32, HI=8,
+             dI=64, chunks=(50, 150), index_keys="pooled", seed_base=87000),
+    Sequence("csa_stream_bf16_channel_pool", "bf16", B=2, T=4 * 100 + 3, m=4, d=128, H=8, W=16, k=32, HI=8, dI=64,
+             chunks=(1, 97, 200), pool="channel", index_keys="pooled", seed_base=88000),
+    Sequence("csa_stream_f32_channel_pool", "f32", B=1, T=4 * 60 + 1, m=4, d=64, H=4, W=8, k=16, HI=4, dI=32,
+             chunks=(30, 101), pool="channel", index_keys="pooled", seed_base=89000),
+    Sequence("csa_stream_bf16_channel_pool_fp4_indexer", "bf16", B=2, T=4 * 90, m=4, d=128, H=8, W=16, k=24, HI=16,
+             dI=128, chunks=(64, 130), pool="channel", index_fmt="mx4", seed_base=90000),
+    Sequence("hca_stream_bf16_channel_pool", "bf16", B=2, T=128 * 4 + 10, m=128, d=128, H=8, W=128, chunks=(200,),
+             pool="channel", seed_base=91000),
 ]
 
 
@@ -60,7 +71,7 @@ def run_stream(csa, sq: Sequence):
     sched = sq.schedule()
     layer = csa.StreamingLayer(mode=sq.mode, B=sq.B, H=sq.H, d=sq.d, m=sq.m, W=sq.W, capacity=sq.T,
                                chunk=max(sched), dtype=sq.torch_dtype, k=sq.k, HI=sq.HI, dI=sq.dI,
-                               index_fmt=sq.index_fmt, scale=sq.scale)
+                               index_fmt=sq.index_fmt, scale=sq.scale, pool=sq.pool, index_keys=sq.index_keys)
     out = torch.empty((sq.B, sq.T, sq.H, sq.d), dtype=torch.float32, device="cuda")
     lse = torch.empty((sq.B, sq.T, sq.H), dtype=torch.float32, device="cuda")
     idx = torch.empty((sq.B, sq.T, max(sq.k, 1)), dtype=torch.int32, device="cuda")
@@ -69,8 +80,13 @@ def run_stream(csa, sq: Sequence):
         plan = layer.plan(n)
         kw = {}
         if sq.mode == "csa":
-            kw = dict(k_idx_new=x["k_idx"][:, plan.g0:plan.g0 + plan.g_new], q_idx=x["q_idx"][:, p:p + n],
-                      w_idx=x["w_idx"][:, p:p + n])
+            kw = dict(q_idx=x["q_idx"][:, p:p + n], w_idx=x["w_idx"][:, p:p + n])
+            if sq.index_keys == "pooled":
+                kw["k_idx_tokens"] = x["k_idx_tokens"][:, p:p + n]
+                if sq.pool == "channel":
+                    kw["k_idx_logits"] = x["k_idx_logits"][:, p:p + n]
+            else:
+                kw["k_idx_new"] = x["k_idx"][:, plan.g0:plan.g0 + plan.g_new]
         o, l, ti = layer.step(x["raw"][:, p:p + n], x["logits"][:, p:p + n], x["q"][:, p:p + n], **kw)
         out[:, p:p + n] = o
         lse[:, p:p + n] = l
@@ -85,7 +101,11 @@ def run_stream(csa, sq: Sequence):
         t = np.arange(sq.T)
         nv = np.tile((t + 1) // sq.m, (sq.B, 1))
         gidx = to_np(idx)
-        swapped = check_topk(gidx, ref["idx"], ref["scores"], nv, sq.k, "stream topk")
+        slack = None
+        if sq.index_keys == "pooled":
+            assert_close(layer.k_idx[:, :sq.G], ref["k_pooled"], sq.dtype, "pooled index keys")
+            slack = pooled_key_slack(sq, xh, ref["k_pooled"])
+        swapped = check_topk(gidx, ref["idx"], ref["scores"], nv, sq.k, "stream topk", extra_tol=slack)
         same = np.all(gidx == ref["idx"], axis=2)
         assert same.mean() >= 0.9, f"only {same.mean():.2%} of rows select the oracle's exact set"
         assert_close(to_np(out)[same], ref["out"][same], sq.dtype, "stream out")
@@ -94,6 +114,19 @@ def run_stream(csa, sq: Sequence):
     else:
         assert_close(out, ref["out"], sq.dtype, "stream out")
         assert_close(lse, ref["lse"], sq.dtype, "stream lse", row_dims=1)
+
+
+def pooled_key_slack(sq, xh, kp):
+    """Per query row: how far two index scores can move when every pooled index key is stored one or two
+    units in the last place away from the oracle's rounding of the exact pooled value (the kernel pools in
+    float32, the oracle in float64; both round to the cache type).  ReLU is 1-Lipschitz, so a score moves
+    by at most sum_h w_h sum_x |q_hx| |dk_x|; a swap moves two scores."""
+    bits = 8 if sq.dtype == "bf16" else 24
+    a = np.abs(kp)
+    ulp2 = np.where(a > 0, np.exp2(np.floor(np.log2(np.where(a > 0, a, 1.0))) - (bits - 1) + 1), 0.0)
+    A = np.einsum("bth,bthx->btx", xh["w_idx"], np.abs(xh["q_idx"]).astype(np.float64))
+    bound = np.einsum("btx,bjx->btj", A, ulp2)
+    return 2 * bound.max(axis=2)
 
 
 @pytest.mark.parametrize("sq", CASES, ids=[c.name for c in CASES])

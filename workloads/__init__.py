@@ -25,7 +25,7 @@ import math
 
 import torch
 
-ORD = dict(raw=1, logits=2, entries=3, k_idx=4, q_idx=5, w_idx=6, q=7, stress=8)
+ORD = dict(raw=1, logits=2, entries=3, k_idx=4, q_idx=5, w_idx=6, q=7, stress=8, k_idx_logits=9)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -182,6 +182,8 @@ class Sequence:
     index_fmt: str = "elem"
     chunks: tuple = ()
     seed_base: int = 0
+    pool: str = "token"         # pooling logits per token ("token") or per token and channel ("channel")
+    index_keys: str = "given"   # one index key per group ("given") or per token, pooled ("pooled")
 
     @property
     def mode(self) -> str:
@@ -208,17 +210,25 @@ class Sequence:
 
 def make_sequence(sq: Sequence, device="cpu") -> dict:
     """Draw a whole stream on the CPU generator (then move it to ``device``):
-      raw [B, T, d], logits [B, T] f32, q [B, T, H, d]; for CSA one index key
-      per group k_idx [B, G, dI], q_idx [B, T, HI, dI], w_idx [B, T, HI] f32.
-    Distributions as make_inputs."""
+      raw [B, T, d], logits [B, T] f32 ([B, T, d] with per-channel pooling),
+      q [B, T, H, d]; for CSA the index keys -- one per group k_idx [B, G, dI],
+      or one per token k_idx_tokens [B, T, dI] (pooled keys; with per-channel
+      pooling also k_idx_logits [B, T, dI] f32) -- and q_idx [B, T, HI, dI],
+      w_idx [B, T, HI] f32.  Distributions as make_inputs."""
     dt = sq.torch_dtype
     out = {}
     out["raw"] = _randn(sq, "raw", (sq.B, sq.T, sq.d), "cpu").to(dt)
-    out["logits"] = _randn(sq, "logits", (sq.B, sq.T), "cpu")
+    lshape = (sq.B, sq.T, sq.d) if sq.pool == "channel" else (sq.B, sq.T)
+    out["logits"] = _randn(sq, "logits", lshape, "cpu")
     out["q"] = _randn(sq, "q", (sq.B, sq.T, sq.H, sq.d), "cpu").to(dt)
     if sq.mode == "csa":
         s = 1.0 / math.sqrt(sq.dI)
-        out["k_idx"] = _randn(sq, "k_idx", (sq.B, sq.G, sq.dI), "cpu", std=s).to(dt)
+        if sq.index_keys == "pooled":
+            out["k_idx_tokens"] = _randn(sq, "k_idx", (sq.B, sq.T, sq.dI), "cpu", std=s).to(dt)
+            if sq.pool == "channel":
+                out["k_idx_logits"] = _randn(sq, "k_idx_logits", (sq.B, sq.T, sq.dI), "cpu")
+        else:
+            out["k_idx"] = _randn(sq, "k_idx", (sq.B, sq.G, sq.dI), "cpu", std=s).to(dt)
         out["q_idx"] = _randn(sq, "q_idx", (sq.B, sq.T, sq.HI, sq.dI), "cpu", std=s).to(dt)
         out["w_idx"] = torch.rand((sq.B, sq.T, sq.HI), generator=_gen(sq, "w_idx", "cpu"), dtype=torch.float32)
     return {k: v.to(device) for k, v in out.items()}
