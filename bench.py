@@ -189,14 +189,19 @@ def loop_bytes(sq) -> int:
     the entry write) and the appended index key."""
     es = 2 if sq.dtype == "bf16" else 4
     row_i = (sq.dI // 2 + sq.dI // 32) if sq.index_fmt == "mx4" else sq.dI * es
+    lg = sq.d * 4 if sq.pool == "channel" else 4        # one token's pooling logits
     total = 0
     for j in range(sq.m):
         t = sq.T + j
         nv = (t + 1) // sq.m
         total += nv * row_i + sq.HI * sq.dI * es + sq.HI * 4
         total += (min(sq.k, nv) + min(sq.W, t + 1)) * sq.d * es + sq.H * sq.d * es + sq.H * sq.d * 4 + 2 * sq.k * 4
-        total += sq.d * es + 4
-    total += sq.m * 4 + sq.d * es + row_i
+        total += sq.d * es + lg
+        if sq.index_keys == "pooled":  # the token's index key (and its logits) into their ring
+            total += sq.dI * es + (sq.dI * 4 if sq.pool == "channel" else 0)
+    total += sq.m * lg + sq.d * es + row_i
+    if sq.index_keys == "pooled":      # the group's index-key rows (and logits) read by the compressor
+        total += sq.m * sq.dI * es + (sq.m * sq.dI * 4 if sq.pool == "channel" else 0)
     return total * sq.B * LOOP_LAYERS
 
 
@@ -215,7 +220,7 @@ def bench_loop(sq, cycles, warmup):
     for _ in range(LOOP_LAYERS):
         L = csa.StreamingLayer(mode=sq.mode, B=B, H=sq.H, d=sq.d, m=m, W=sq.W, capacity=sq.T + m, chunk=1,
                                dtype=sq.torch_dtype, k=sq.k, HI=sq.HI, dI=sq.dI, index_fmt=sq.index_fmt,
-                               scale=sq.scale)
+                               scale=sq.scale, pool=sq.pool, index_keys=sq.index_keys)
         N0 = sq.T // m
         L.entries[:, :N0] = rn(B, N0, sq.d).to(L.entries.dtype)
         kI = rn(B, N0, sq.dI, std=sq.dI ** -0.5).to(sq.torch_dtype)
@@ -227,14 +232,23 @@ def bench_loop(sq, cycles, warmup):
         del kI
         half = rn(B, L.R, sq.d).to(sq.torch_dtype)
         L.raw_ring[:, :L.R], L.raw_ring[:, L.R:] = half, half
-        lg = rn(B, L.R, 1)
+        lg = rn(B, L.R, L.logit_ring.shape[2])
         L.logit_ring[:, :L.R], L.logit_ring[:, L.R:] = lg, lg
+        if sq.index_keys == "pooled":
+            kt = rn(B, L.R, sq.dI, std=sq.dI ** -0.5).to(sq.torch_dtype)
+            L.kidx_ring[:, :L.R], L.kidx_ring[:, L.R:] = kt, kt
+            if sq.pool == "channel":
+                kl = rn(B, L.R, sq.dI)
+                L.kidx_logit_ring[:, :L.R], L.kidx_logit_ring[:, L.R:] = kl, kl
         R_ = L.R
         layers.append(L)
     # per-step inputs (one token per sequence)
     steps_in = []
     for j in range(m):
-        x = {"raw": rn(B, 1, sq.d).to(sq.torch_dtype), "logits": rn(B, 1), "q": rn(B, 1, sq.H, sq.d).to(sq.torch_dtype),
+        x = {"raw": rn(B, 1, sq.d).to(sq.torch_dtype),
+             "logits": rn(B, 1, sq.d) if sq.pool == "channel" else rn(B, 1),
+             "q": rn(B, 1, sq.H, sq.d).to(sq.torch_dtype),
+             "k_idx_tokens": rn(B, 1, sq.dI, std=sq.dI ** -0.5).to(sq.torch_dtype), "k_idx_logits": rn(B, 1, sq.dI),
              "q_idx": rn(B, 1, sq.HI, sq.dI, std=sq.dI ** -0.5).to(sq.torch_dtype),
              "w_idx": torch.rand((B, 1, sq.HI), generator=g, device="cuda"),
              "k_idx_new": rn(B, 1, sq.dI, std=sq.dI ** -0.5).to(sq.torch_dtype)}
@@ -249,9 +263,15 @@ def bench_loop(sq, cycles, warmup):
             x = steps_in[j]
             for li, L in enumerate(layers):
                 o, l_, ti = outs[j * LOOP_LAYERS + li]
-                kin = x["k_idx_new"] if L.plan(1).g_new else None
-                L.step(x["raw"], x["logits"], x["q"], k_idx_new=kin, q_idx=x["q_idx"], w_idx=x["w_idx"], out=o,
-                       lse=l_, topk_idx=ti)
+                kw = {}
+                if sq.index_keys == "pooled":
+                    kw["k_idx_tokens"] = x["k_idx_tokens"]
+                    if sq.pool == "channel":
+                        kw["k_idx_logits"] = x["k_idx_logits"]
+                elif L.plan(1).g_new:
+                    kw["k_idx_new"] = x["k_idx_new"]
+                L.step(x["raw"], x["logits"], x["q"], q_idx=x["q_idx"], w_idx=x["w_idx"], out=o, lse=l_,
+                       topk_idx=ti, **kw)
 
     cycle()
     torch.cuda.synchronize()
@@ -341,9 +361,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2", help="c2 (default), c3 or c5")
-    ap.add_argument("--also", default="c3,c5,c2x,c5x,l2,l2x,p1",
+    ap.add_argument("--also", default="c3,c5,c2x,c5x,l2,l2x,l2c,p1",
                     help="secondary workloads ('' for none); c2x/c5x: FP4 (MXFP4) indexer operands; "
-                         "l2/l2x: decode loops with cache maintenance; p1: a whole chunked prefill from 0")
+                         "l2/l2x/l2c: decode loops with cache maintenance (l2c: per-channel pooling, pooled "
+                         "index keys); p1: a whole chunked prefill from 0")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for the HBM byte counters)")

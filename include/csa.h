@@ -136,6 +136,25 @@ int csa_append_rows(int B, int n, int64_t row_bytes, const void *rows, int64_t r
                     void *stream);
 
 /*
+ * csa_append_rows_multi -- several csa_append_rows in one launch (a decode
+ * step appends a token's raw row, its logits and, with pooled index keys,
+ * its index key and their logits).  Job i does exactly what
+ * csa_append_rows(jobs[i].B, jobs[i].n, ...) does, with the same checks;
+ * besides, no job's destination may overlap another job's rows or
+ * destination.  count <= 8; the job array is read during the call only.
+ * Errors name the job.
+ */
+typedef struct {
+    int B, n;
+    int64_t row_bytes;
+    const void *rows;
+    int64_t rows_bstride;
+    void *dst;
+    int64_t dst_bstride, dst_rows, pos0, ring;
+} csa_append_job;
+int csa_append_rows_multi(int count, const csa_append_job *jobs, void *stream);
+
+/*
  * csa_index_topk -- lightning indexer and per-query top-k (overview page,
  * section 2.2 step 2; indexer form fixed as a sum over index heads of a
  * head weight times ReLU of a query-key dot product).  For query row i of

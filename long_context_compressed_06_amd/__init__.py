@@ -23,7 +23,14 @@ _STATUS = {0: "CSA_OK", -1: "CSA_EINVAL", -2: "CSA_EDTYPE", -3: "CSA_EALIGN", -4
 EXPORTS = ("csa_abi_version", "csa_status_string", "csa_last_error_detail", "csa_compress",
            "csa_index_topk_workspace_bytes", "csa_index_topk", "csa_index_scores", "csa_mqa_workspace_bytes",
            "csa_sparse_mqa", "hca_dense_mqa", "csa_mx4_quantize", "csa_index_topk_mx4", "csa_append_rows",
-           "csa_compress_channels")
+           "csa_compress_channels", "csa_append_rows_multi")
+
+
+class AppendJob(ctypes.Structure):
+    """csa_append_job of include/csa.h."""
+    _fields_ = [("B", ctypes.c_int), ("n", ctypes.c_int), ("row_bytes", ctypes.c_int64), ("rows", ctypes.c_void_p),
+                ("rows_bstride", ctypes.c_int64), ("dst", ctypes.c_void_p), ("dst_bstride", ctypes.c_int64),
+                ("dst_rows", ctypes.c_int64), ("pos0", ctypes.c_int64), ("ring", ctypes.c_int64)]
 
 
 class CsaError(RuntimeError):
@@ -70,6 +77,8 @@ def lib():
     L.csa_append_rows.argtypes = [I, I, I64, P, I64, P, I64, I64, I64, I64, P]
     L.csa_compress_channels.argtypes = [I, I, I, I, I, P, I64, P, I64, P, I64, P]
     L.csa_compress_channels.restype = I
+    L.csa_append_rows_multi.argtypes = [I, P, P]
+    L.csa_append_rows_multi.restype = I
     L.csa_append_rows.restype = I
     _lib = L
     return L
@@ -254,6 +263,31 @@ def csa_append_rows(rows: torch.Tensor, dst: torch.Tensor, pos0: int, ring: int 
     _check(lib().csa_append_rows(B, n, per_row * es, _p(rows), rows.stride(0) * es, _p(dst), dst.stride(0) * es,
                                  dst.shape[1], pos0, ring, _stream(rows)))
     return dst
+
+
+def _append_job(rows: torch.Tensor, dst: torch.Tensor, pos0: int, ring: int) -> AppendJob:
+    _need(rows, "rows")
+    _need(dst, "dst", rows.dtype)
+    if rows.dim() < 2 or rows.shape[0] != dst.shape[0] or rows.shape[2:] != dst.shape[2:]:
+        raise ValueError("rows and dst must be [B, n, ...] and [B, cap, ...] with the same row shape")
+    per_row = 1
+    for x in rows.shape[2:]:
+        per_row *= x
+    es = rows.element_size()
+    for t, name in ((rows, "rows"), (dst, "dst")):
+        if t.shape[0] and not t[0:1].is_contiguous():
+            raise ValueError(f"{name}: the rows of one batch must be packed")
+    return AppendJob(rows.shape[0], rows.shape[1], per_row * es, rows.data_ptr(), rows.stride(0) * es,
+                     dst.data_ptr(), dst.stride(0) * es, dst.shape[1], pos0, ring)
+
+
+def csa_append_rows_multi(jobs) -> None:
+    """jobs: (rows, dst, pos0, ring) tuples, each as csa_append_rows; one launch for all of them."""
+    jobs = list(jobs)
+    if not jobs:
+        return
+    arr = (AppendJob * len(jobs))(*[_append_job(*j) for j in jobs])
+    _check(lib().csa_append_rows_multi(len(jobs), ctypes.cast(arr, ctypes.c_void_p), _stream(jobs[0][0])))
 
 
 def csa_compress_channels(raw: torch.Tensor, logits: torch.Tensor, m: int, out: torch.Tensor) -> torch.Tensor:

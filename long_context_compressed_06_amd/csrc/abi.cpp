@@ -124,8 +124,9 @@ int csa_compress_channels(int dt, int B, int G, int m, int d, const void *raw, i
                       "compress launch");
 }
 
-int csa_append_rows(int B, int n, int64_t row_bytes, const void *rows, int64_t rows_bstride, void *dst,
-                    int64_t dst_bstride, int64_t dst_rows, int64_t pos0, int64_t ring, void *stream) {
+// the checks of one append; on success *vw is the widest move the job allows
+static int check_append(int B, int n, int64_t row_bytes, const void *rows, int64_t rows_bstride, const void *dst,
+                        int64_t dst_bstride, int64_t dst_rows, int64_t pos0, int64_t ring, int *vw) {
     if (B < 0 || n < 0) return fail(CSA_EINVAL, "B=%d and n=%d must be >= 0", B, n);
     if (B > 65535) return fail(CSA_EUNSUPPORTED, "B=%d above 65535", B);
     if (row_bytes < 1) return fail(CSA_EINVAL, "row_bytes=%lld must be >= 1", (long long)row_bytes);
@@ -143,10 +144,59 @@ int csa_append_rows(int B, int n, int64_t row_bytes, const void *rows, int64_t r
     const Span ss = span(rows, B, rows_bstride, (int64_t)n * row_bytes, 1);
     const Span sd = span(dst, B, dst_bstride, dst_rows * row_bytes, 1);
     if (overlap(ss, sd)) return fail(CSA_EINVAL, "rows overlap the destination");
-    int vw = 16;
-    while (vw > 1 && (row_bytes % vw || !aligned(rows, vw) || !aligned(dst, vw) || rows_bstride % vw ||
-                      dst_bstride % vw))
-        vw /= 2;
+    int w = 16;
+    while (w > 1 && (row_bytes % w || !aligned(rows, w) || !aligned(dst, w) || rows_bstride % w || dst_bstride % w))
+        w /= 2;
+    *vw = w;
+    return ok();
+}
+
+int csa_append_rows_multi(int count, const csa_append_job *jobs, void *stream) {
+    if (count < 0 || count > csa::kMaxAppendJobs)
+        return fail(CSA_EUNSUPPORTED, "count=%d outside 0..%d", count, csa::kMaxAppendJobs);
+    if (count > 0 && !jobs) return fail(CSA_EINVAL, "NULL job array");
+    csa::AppendJobs aj{};
+    int live = 0;
+    for (int i = 0; i < count; ++i) {
+        const csa_append_job &J = jobs[i];
+        int vw = 1;
+        if (int s = check_append(J.B, J.n, J.row_bytes, J.rows, J.rows_bstride, J.dst, J.dst_bstride, J.dst_rows,
+                                 J.pos0, J.ring, &vw)) {
+            std::string d = "job " + std::to_string(i) + ": " + g_detail;
+            return fail(s, "%s", d.c_str());
+        }
+        if ((int64_t)J.B * J.n == 0) continue;
+        // no job may write where another reads or writes
+        const Span di = span(J.dst, J.B, J.dst_bstride, J.dst_rows * J.row_bytes, 1);
+        for (int k = 0; k < count; ++k) {
+            const csa_append_job &K = jobs[k];
+            if (k == i || (int64_t)K.B * K.n == 0) continue;
+            if (overlap(di, span(K.rows, K.B, K.rows_bstride, (int64_t)K.n * K.row_bytes, 1)) ||
+                (k < i && overlap(di, span(K.dst, K.B, K.dst_bstride, K.dst_rows * K.row_bytes, 1))))
+                return fail(CSA_EINVAL, "job %d's destination overlaps job %d's rows or destination", i, k);
+        }
+        csa::AppendJob &A = aj.j[live++];
+        A.src = (const unsigned char *)J.rows;
+        A.dst = (unsigned char *)J.dst;
+        A.n = J.n;
+        A.row_bytes = J.row_bytes;
+        A.src_bs = J.rows_bstride;
+        A.dst_bs = J.dst_bstride;
+        A.pos0 = J.pos0;
+        A.ring = J.ring;
+        A.vw = vw;
+        A.B = J.B;
+    }
+    if (live == 0) return ok();
+    return hip_status(csa::launch_append_multi(aj, live, (hipStream_t)stream), "append launch");
+}
+
+int csa_append_rows(int B, int n, int64_t row_bytes, const void *rows, int64_t rows_bstride, void *dst,
+                    int64_t dst_bstride, int64_t dst_rows, int64_t pos0, int64_t ring, void *stream) {
+    int vw = 1;
+    if (int s = check_append(B, n, row_bytes, rows, rows_bstride, dst, dst_bstride, dst_rows, pos0, ring, &vw))
+        return s;
+    if ((int64_t)B * n == 0) return ok();
     return hip_status(csa::launch_append_rows(B, n, row_bytes, vw, rows, rows_bstride, dst, dst_bstride, pos0, ring,
                                               (hipStream_t)stream),
                       "append launch");

@@ -51,6 +51,53 @@ __global__ __launch_bounds__(256) void k_append_rows(int64_t n, int64_t vpr, con
     }
 }
 
+// several appends in one launch: blockIdx.z selects the job, blockIdx.y the batch
+template <int VW>
+__device__ __forceinline__ void append_job_body(const AppendJob &J) {
+    typedef typename Vec<VW>::T V;
+    const int64_t b = blockIdx.y;
+    const int64_t vpr = J.row_bytes / VW;
+    const unsigned char *s = J.src + b * J.src_bs;
+    unsigned char *d = J.dst + b * J.dst_bs;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < J.n * vpr; e += (int64_t)gridDim.x * 256) {
+        const int64_t i = e / vpr, v = e % vpr;
+        const V x = *(const V *)(s + i * J.row_bytes + v * VW);
+        const int64_t p = J.pos0 + i;
+        if (J.ring == 0) {
+            *(V *)(d + p * J.row_bytes + v * VW) = x;
+        } else {
+            const int64_t slot = p % J.ring;
+            *(V *)(d + slot * J.row_bytes + v * VW) = x;
+            *(V *)(d + (slot + J.ring) * J.row_bytes + v * VW) = x;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_append_multi(AppendJobs jobs) {
+    const AppendJob &J = jobs.j[blockIdx.z];
+    if ((int)blockIdx.y >= J.B) return;
+    switch (J.vw) {
+        case 16: append_job_body<16>(J); break;
+        case 8: append_job_body<8>(J); break;
+        case 4: append_job_body<4>(J); break;
+        case 2: append_job_body<2>(J); break;
+        default: append_job_body<1>(J); break;
+    }
+}
+
+hipError_t launch_append_multi(const AppendJobs &jobs, int count, hipStream_t st) {
+    int64_t blocks = 1, bmax = 1;
+    for (int i = 0; i < count; ++i) {
+        const int64_t b = (jobs.j[i].n * (jobs.j[i].row_bytes / jobs.j[i].vw) + 255) / 256;
+        blocks = b > blocks ? b : blocks;
+        bmax = jobs.j[i].B > bmax ? jobs.j[i].B : bmax;
+    }
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(k_append_multi, dim3((unsigned)blocks, (unsigned)bmax, (unsigned)count), dim3(256), 0, st,
+                       jobs);
+    return hipGetLastError();
+}
+
 hipError_t launch_append_rows(int B, int64_t n, int64_t row_bytes, int vw, const void *src, int64_t src_bs,
                               void *dst, int64_t dst_bs, int64_t pos0, int64_t ring, hipStream_t st) {
     const int64_t vpr = row_bytes / vw;

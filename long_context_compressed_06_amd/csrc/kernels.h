@@ -69,6 +69,18 @@ hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t st);
 // vw: bytes per vector, dividing row_bytes, both pointers and both strides
 hipError_t launch_append_rows(int B, int64_t n, int64_t row_bytes, int vw, const void *src, int64_t src_bs,
                               void *dst, int64_t dst_bs, int64_t pos0, int64_t ring, hipStream_t st);
+// up to kMaxAppendJobs appends (each as launch_append_rows) in one launch
+constexpr int kMaxAppendJobs = 8;
+struct AppendJob {
+    const unsigned char *src;
+    unsigned char *dst;
+    int64_t n, row_bytes, src_bs, dst_bs, pos0, ring;
+    int vw, B;
+};
+struct AppendJobs {
+    AppendJob j[kMaxAppendJobs];
+};
+hipError_t launch_append_multi(const AppendJobs &jobs, int count, hipStream_t st);
 
 // scores: [rows][topk_score_stride(N)], 16-byte aligned.  scratch:
 // topk_scratch_bytes(rows, N) bytes; its histogram part must have been filled

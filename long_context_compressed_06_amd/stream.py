@@ -40,7 +40,7 @@ import dataclasses
 
 import torch
 
-from . import (csa_append_rows, csa_compress, csa_compress_channels, csa_index_topk, csa_index_topk_mx4,
+from . import (csa_append_rows_multi, csa_compress, csa_compress_channels, csa_index_topk, csa_index_topk_mx4,
                csa_mx4_quantize, csa_sparse_mqa, hca_dense_mqa, index_topk_workspace_bytes, mqa_workspace_bytes)
 
 
@@ -163,13 +163,14 @@ class StreamingLayer:
         p = self.plan(n)
         if p.g0 + p.g_new > self.cap_e:
             raise ValueError("entry capacity exhausted")
-        # 1. raw rows and logits into the rings
-        csa_append_rows(raw, self.raw_ring, p.p0, ring=self.R)
-        csa_append_rows(logits.reshape(B, n, self.logit_ring.shape[2]), self.logit_ring, p.p0, ring=self.R)
+        # 1. raw rows and logits (and per-token index keys) into the rings, one launch
+        jobs = [(raw, self.raw_ring, p.p0, self.R),
+                (logits.reshape(B, n, self.logit_ring.shape[2]), self.logit_ring, p.p0, self.R)]
         if self.mode == "csa" and self.index_keys == "pooled":
-            csa_append_rows(k_idx_tokens, self.kidx_ring, p.p0, ring=self.R)
+            jobs.append((k_idx_tokens, self.kidx_ring, p.p0, self.R))
             if self.pool == "channel":
-                csa_append_rows(k_idx_logits, self.kidx_logit_ring, p.p0, ring=self.R)
+                jobs.append((k_idx_logits, self.kidx_logit_ring, p.p0, self.R))
+        csa_append_rows_multi(jobs)
         # 2. the groups completing in this chunk
         if p.g_new > 0:
             L = p.g_new * self.m
@@ -193,10 +194,9 @@ class StreamingLayer:
                     raise ValueError(f"the chunk completes {p.g_new} groups: k_idx_new must hold {p.g_new} rows")
                 if self.index_fmt == "mx4":
                     codes, scales = csa_mx4_quantize(k_idx_new.contiguous())
-                    csa_append_rows(codes, self.k_codes, p.g0)
-                    csa_append_rows(scales, self.k_scales, p.g0)
+                    csa_append_rows_multi([(codes, self.k_codes, p.g0, 0), (scales, self.k_scales, p.g0, 0)])
                 else:
-                    csa_append_rows(k_idx_new, self.k_idx, p.g0)
+                    csa_append_rows_multi([(k_idx_new, self.k_idx, p.g0, 0)])
             # 4. indexer + top-k
             if topk_idx is None:
                 topk_idx = torch.empty((B, n, self.k), dtype=torch.int32, device=raw.device)

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
     import long_context_compressed_06_amd as csa
 
     names = header_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
     assert sorted(csa.EXPORTS) == names
@@ -200,3 +200,24 @@ def test_compress_channels_rejects_bad_arguments(L):
     assert call(lbs=3 * 4 * 128 + 2) == -3     # logit batch stride not a multiple of 4
     assert call(out=P + 0x100000 + 64) == -1   # out overlaps the logits
     assert call(G=0, raw=None, logits=None, out=None) == 0
+
+
+def test_append_rows_multi_rejects_bad_arguments(L):
+    import long_context_compressed_06_amd as csa
+
+    def job(B=2, n=4, rb=256, rows=P, rbs=4 * 256, dst=P + 0x100000, dbs=64 * 256, drows=64, pos0=0, ring=0):
+        return csa.AppendJob(B, n, rb, rows, rbs, dst, dbs, drows, pos0, ring)
+
+    def call(*jobs):
+        arr = (csa.AppendJob * len(jobs))(*jobs)
+        return L.csa_append_rows_multi(len(jobs), ctypes.cast(arr, ctypes.c_void_p), None)
+
+    assert L.csa_append_rows_multi(9, None, None) == -6
+    assert L.csa_append_rows_multi(1, None, None) == -1
+    assert L.csa_append_rows_multi(0, None, None) == 0
+    assert call(job(), job(pos0=61)) == -1                        # job 1 past its destination
+    assert b"job 1" in L.csa_last_error_detail()
+    assert call(job(), job(rows=P + 0x200000, dst=P + 0x100000 + 256)) == -1   # two jobs write the same rows
+    assert call(job(), job(rows=P + 0x100000, dst=P + 0x300000)) == -1         # job 1 reads what job 0 writes
+    assert call(job(ring=3)) == -1
+    assert call(job(n=0, rows=None, dst=None), job(B=0, rows=None, dst=None)) == 0

@@ -233,3 +233,29 @@ def test_decode_loop_128k_resumed(csa, fmt):
     gl = np.concatenate([to_np(t) for t in lses], axis=1)
     assert_close(go[same], ro[same], "bf16", "loop out")
     assert_close(gl[same], rl[same], "bf16", "loop lse", row_dims=1)
+
+
+def test_append_rows_multi_exact(csa):
+    """Four appends of different row widths, batch counts and ring / cache forms in one launch."""
+    say("append multi")
+    g = torch.Generator().manual_seed(9200)
+    specs = [((64,), torch.bfloat16, 3, 20, 38, 7), ((1,), torch.float32, 3, 11, 7, 11),
+             ((17,), torch.uint8, 2, 0, 3, 33), ((4, 8), torch.float32, 1, 0, 5, 2)]
+    jobs, checks = [], []
+    for row_shape, dtype, B, ring, pos0, n in specs:
+        cap = 2 * ring if ring else pos0 + n + 4
+        src_full = (torch.randn((B, n + 2) + row_shape, generator=g) * 50).to(dtype)
+        dst0 = (torch.randn((B, cap) + row_shape, generator=g) * 50).to(dtype)
+        dst = dst0.cuda()
+        jobs.append((src_full.cuda()[:, 1:n + 1], dst, pos0, ring))
+        want = dst0.clone()
+        for i in range(n):
+            p = pos0 + i
+            slots = [p % ring, p % ring + ring] if ring else [p]
+            for sl in slots:
+                want[:, sl] = src_full[:, 1 + i]
+        checks.append((dst, want))
+    csa.csa_append_rows_multi(jobs)
+    torch.cuda.synchronize()
+    for dst, want in checks:
+        assert torch.equal(dst.cpu().view(torch.uint8), want.view(torch.uint8))

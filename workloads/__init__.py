@@ -243,6 +243,9 @@ LOOPS = {
                    dI=128, seed_base=6000),
 }
 LOOPS["l2x"] = dataclasses.replace(LOOPS["l2"], name="csa_decode_loop_mx4idx_B32_ctx128K", index_fmt="mx4")
+# the same loop with per-channel pooling logits and index keys pooled by the compressor from per-token keys
+LOOPS["l2c"] = dataclasses.replace(LOOPS["l2"], name="csa_decode_loop_chpool_B32_ctx128K", pool="channel",
+                                   index_keys="pooled")
 
 # a whole prefill from position 0 through the streaming layer, in chunks
 PREFILLS = {
