@@ -138,10 +138,20 @@ int csa_append_rows(int B, int n, int64_t row_bytes, const void *rows, int64_t r
 /*
  * csa_append_rows_multi -- several csa_append_rows in one launch (a decode
  * step appends a token's raw row, its logits and, with pooled index keys,
- * its index key and their logits).  Job i does exactly what
- * csa_append_rows(jobs[i].B, jobs[i].n, ...) does, with the same checks;
- * besides, no job's destination may overlap another job's rows or
- * destination.  count <= 8; the job array is read during the call only.
+ * its index key and their logits).  With pos == NULL and every == 0, job i
+ * does exactly what csa_append_rows(jobs[i].B, jobs[i].n, ...) does, with the
+ * same checks.  Two extensions serve ragged batches (each sequence at its own
+ * position):
+ *   pos    device array [B] (int64): batch b's rows start at position
+ *          pos0 + pos[b] instead of pos0;
+ *   every  > 0: only the row of a token that completes a group of `every`
+ *          tokens is kept (position p with (p+1) mod every == 0), written to
+ *          that group's row (p+1)/every - 1 (an entry's index key enters
+ *          the cache when its group is emitted).
+ * Positions read from memory are not checked by the host: the kernel skips
+ * rows whose destination falls outside [0, dst_rows) (ring == 0) or whose
+ * position is negative.  No job's destination may overlap another job's rows
+ * or destination.  count <= 8; the job array is read during the call only.
  * Errors name the job.
  */
 typedef struct {
@@ -151,8 +161,73 @@ typedef struct {
     int64_t rows_bstride;
     void *dst;
     int64_t dst_bstride, dst_rows, pos0, ring;
+    const int64_t *pos;
+    int64_t every;
 } csa_append_job;
 int csa_append_rows_multi(int count, const csa_append_job *jobs, void *stream);
+
+/*
+ * Ragged batches: B sequences, each at its own length, decoding one token
+ * each.  pos is a device array [B] (int64) holding each sequence's newest
+ * token position t_b; it is read by the kernels, so a step captured in a HIP
+ * graph keeps working as the positions advance (csa_positions_advance).  The
+ * host cannot check device positions: every ragged call is memory-safe for
+ * any values (visibility is clamped to N, ring rows are taken mod ring,
+ * destinations outside a cache are skipped), and positions outside what the
+ * caches hold give meaningless but bounded results.
+ *
+ * csa_positions_advance -- pos[b] += delta for b < B.
+ *
+ * csa_ragged_compress -- a1 for ragged batches (overview page, section 2.2
+ * step 1: a group becomes an entry when its m-th token arrives).  For every
+ * sequence whose newest token completes a group ((t_b + 1) mod m == 0) the
+ * group g = (t_b+1)/m - 1 is pooled as csa_compress does, from its m rows
+ * and logits in mirrored rings (position p at ring row p mod ring; the rings
+ * hold 2*ring rows, m <= ring), into out[b, g] if g < out_rows.
+ *   raw_ring    [B, 2*ring, d]  dt,  batch stride ring_bstride elements
+ *   logit_ring  [B, 2*ring]     f32, batch stride logit_bstride elements
+ *   out         [B, out_rows, d] dt, batch stride out_bstride elements
+ *
+ * csa_ragged_index_topk / csa_ragged_index_topk_mx4 -- csa_index_topk /
+ * csa_index_topk_mx4 with one query per sequence at position t_b (Tq = 1;
+ * n_visible(t_b) entries of the N in the cache are scored).  Same workspace
+ * (csa_index_topk_workspace_bytes(B, 1, N, H_I, k)) and outputs.
+ *
+ * csa_ragged_sparse_mqa / hca_ragged_dense_mqa -- csa_sparse_mqa /
+ * hca_dense_mqa with one query per sequence at position t_b; the window's
+ * raw rows come from a ring (position p at row p mod ring, ring >= W), so no
+ * raw_pos0 is needed.  q [B, 1, H, d]; workspace as for Tq = 1.
+ */
+int csa_positions_advance(int B, int64_t *pos, int64_t delta, void *stream);
+int csa_ragged_compress(int dt, int B, int m, int d, const int64_t *pos,
+                        const void *raw_ring, int64_t ring_bstride,
+                        const float *logit_ring, int64_t logit_bstride, int64_t ring,
+                        void *out, int64_t out_bstride, int64_t out_rows, void *stream);
+int csa_ragged_index_topk(int dt, int B, int N, int H_I, int d_I, int m, int k, const int64_t *pos,
+                          const void *q_idx, const float *w_idx,
+                          const void *k_idx, int64_t k_bstride,
+                          int32_t *topk_idx, float *scores_out,
+                          void *workspace, size_t workspace_bytes, void *stream);
+int csa_ragged_index_topk_mx4(int dt, int B, int N, int H_I, int d_I, int m, int k, const int64_t *pos,
+                              const void *q_idx, const float *w_idx,
+                              const uint8_t *k_codes, const uint8_t *k_scales, int64_t k_bstride,
+                              int32_t *topk_idx, float *scores_out,
+                              void *workspace, size_t workspace_bytes, void *stream);
+int csa_ragged_sparse_mqa(int dt, int B, int H, int d, int N, int m, int k, int W,
+                          const int64_t *pos, float scale,
+                          const void *q,
+                          const void *entries, int64_t e_bstride,
+                          const int32_t *topk_idx,
+                          const void *raw_ring, int64_t ring_bstride, int64_t ring,
+                          float *out, float *lse,
+                          void *workspace, size_t workspace_bytes, void *stream);
+int hca_ragged_dense_mqa(int dt, int B, int H, int d, int N, int m, int W,
+                         const int64_t *pos, float scale,
+                         const void *q,
+                         const void *entries, int64_t e_bstride,
+                         const void *raw_ring, int64_t ring_bstride, int64_t ring,
+                         float *out, float *lse,
+                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * csa_index_topk -- lightning indexer and per-query top-k (overview page,

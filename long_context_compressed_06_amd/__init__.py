@@ -23,14 +23,16 @@ _STATUS = {0: "CSA_OK", -1: "CSA_EINVAL", -2: "CSA_EDTYPE", -3: "CSA_EALIGN", -4
 EXPORTS = ("csa_abi_version", "csa_status_string", "csa_last_error_detail", "csa_compress",
            "csa_index_topk_workspace_bytes", "csa_index_topk", "csa_index_scores", "csa_mqa_workspace_bytes",
            "csa_sparse_mqa", "hca_dense_mqa", "csa_mx4_quantize", "csa_index_topk_mx4", "csa_append_rows",
-           "csa_compress_channels", "csa_append_rows_multi")
+           "csa_compress_channels", "csa_append_rows_multi", "csa_positions_advance", "csa_ragged_compress",
+           "csa_ragged_index_topk", "csa_ragged_index_topk_mx4", "csa_ragged_sparse_mqa", "hca_ragged_dense_mqa")
 
 
 class AppendJob(ctypes.Structure):
     """csa_append_job of include/csa.h."""
     _fields_ = [("B", ctypes.c_int), ("n", ctypes.c_int), ("row_bytes", ctypes.c_int64), ("rows", ctypes.c_void_p),
                 ("rows_bstride", ctypes.c_int64), ("dst", ctypes.c_void_p), ("dst_bstride", ctypes.c_int64),
-                ("dst_rows", ctypes.c_int64), ("pos0", ctypes.c_int64), ("ring", ctypes.c_int64)]
+                ("dst_rows", ctypes.c_int64), ("pos0", ctypes.c_int64), ("ring", ctypes.c_int64),
+                ("pos", ctypes.c_void_p), ("every", ctypes.c_int64)]
 
 
 class CsaError(RuntimeError):
@@ -79,6 +81,18 @@ def lib():
     L.csa_compress_channels.restype = I
     L.csa_append_rows_multi.argtypes = [I, P, P]
     L.csa_append_rows_multi.restype = I
+    L.csa_positions_advance.argtypes = [I, P, I64, P]
+    L.csa_positions_advance.restype = I
+    L.csa_ragged_compress.argtypes = [I, I, I, I, P, P, I64, P, I64, I64, P, I64, I64, P]
+    L.csa_ragged_compress.restype = I
+    L.csa_ragged_index_topk.argtypes = [I, I, I, I, I, I, I, P, P, P, P, I64, P, P, P, SZ, P]
+    L.csa_ragged_index_topk.restype = I
+    L.csa_ragged_index_topk_mx4.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, I64, P, P, P, SZ, P]
+    L.csa_ragged_index_topk_mx4.restype = I
+    L.csa_ragged_sparse_mqa.argtypes = [I, I, I, I, I, I, I, I, P, F, P, P, I64, P, P, I64, I64, P, P, P, SZ, P]
+    L.csa_ragged_sparse_mqa.restype = I
+    L.hca_ragged_dense_mqa.argtypes = [I, I, I, I, I, I, I, P, F, P, P, I64, P, I64, I64, P, P, P, SZ, P]
+    L.hca_ragged_dense_mqa.restype = I
     L.csa_append_rows.restype = I
     _lib = L
     return L
@@ -265,7 +279,7 @@ def csa_append_rows(rows: torch.Tensor, dst: torch.Tensor, pos0: int, ring: int 
     return dst
 
 
-def _append_job(rows: torch.Tensor, dst: torch.Tensor, pos0: int, ring: int) -> AppendJob:
+def _append_job(rows: torch.Tensor, dst: torch.Tensor, pos0: int, ring: int, pos=None, every: int = 0) -> AppendJob:
     _need(rows, "rows")
     _need(dst, "dst", rows.dtype)
     if rows.dim() < 2 or rows.shape[0] != dst.shape[0] or rows.shape[2:] != dst.shape[2:]:
@@ -277,12 +291,18 @@ def _append_job(rows: torch.Tensor, dst: torch.Tensor, pos0: int, ring: int) -> 
     for t, name in ((rows, "rows"), (dst, "dst")):
         if t.shape[0] and not t[0:1].is_contiguous():
             raise ValueError(f"{name}: the rows of one batch must be packed")
+    if pos is not None:
+        _need(pos, "pos", torch.int64, 1)
+        if pos.shape[0] != rows.shape[0] or not pos.is_contiguous():
+            raise ValueError("pos must be a contiguous [B] int64 tensor")
     return AppendJob(rows.shape[0], rows.shape[1], per_row * es, rows.data_ptr(), rows.stride(0) * es,
-                     dst.data_ptr(), dst.stride(0) * es, dst.shape[1], pos0, ring)
+                     dst.data_ptr(), dst.stride(0) * es, dst.shape[1], pos0, ring,
+                     None if pos is None else pos.data_ptr(), every)
 
 
 def csa_append_rows_multi(jobs) -> None:
-    """jobs: (rows, dst, pos0, ring) tuples, each as csa_append_rows; one launch for all of them."""
+    """jobs: (rows, dst, pos0, ring[, pos[, every]]) tuples, each as csa_append_rows (pos: per-batch device
+    positions added to pos0; every: keep only the token completing a group, at that group's row); one launch."""
     jobs = list(jobs)
     if not jobs:
         return
@@ -306,6 +326,120 @@ def csa_compress_channels(raw: torch.Tensor, logits: torch.Tensor, m: int, out: 
         raise ValueError("shape mismatch between raw, logits and out")
     _check(lib().csa_compress_channels(_dt(raw), B, G, m, d, _p(raw), _bstride(raw), _p(logits), _bstride(logits),
                                        _p(out), _bstride(out), _stream(raw)))
+    return out
+
+
+def csa_positions_advance(pos: torch.Tensor, delta: int = 1) -> torch.Tensor:
+    """pos [B] int64 (device) += delta."""
+    _need(pos, "pos", torch.int64, 1)
+    if not pos.is_contiguous():
+        raise ValueError("pos must be contiguous")
+    _check(lib().csa_positions_advance(pos.shape[0], _p(pos), delta, _stream(pos)))
+    return pos
+
+
+def _ragged_pos(pos, B):
+    _need(pos, "pos", torch.int64, 1)
+    if pos.shape[0] != B or not pos.is_contiguous():
+        raise ValueError("pos must be a contiguous [B] int64 tensor")
+
+
+def csa_ragged_compress(raw_ring: torch.Tensor, logit_ring: torch.Tensor, ring: int, m: int, pos: torch.Tensor,
+                        out: torch.Tensor) -> torch.Tensor:
+    """Per sequence, the group its newest token (position pos[b]) completes, pooled out of the mirrored rings
+    raw_ring [B, 2*ring, d] / logit_ring [B, 2*ring] into out [B, cap, d] at row (pos[b]+1)/m - 1."""
+    _need(raw_ring, "raw_ring", dims=3)
+    _need(logit_ring, "logit_ring", torch.float32)
+    _need(out, "out", raw_ring.dtype, 3)
+    B, _, d = raw_ring.shape
+    _ragged_pos(pos, B)
+    if raw_ring.stride(1) != d or out.stride(1) != d or logit_ring.stride(1) != 1:
+        raise ValueError("ring and cache rows must be packed")
+    _check(lib().csa_ragged_compress(_dt(raw_ring), B, m, d, _p(pos), _p(raw_ring), _bstride(raw_ring),
+                                     _p(logit_ring), _bstride(logit_ring), ring, _p(out), _bstride(out), out.shape[1],
+                                     _stream(raw_ring)))
+    return out
+
+
+def csa_ragged_index_topk(q_idx, w_idx, k_idx, N: int, m: int, k: int, pos, topk_idx=None, scores_out=None,
+                          workspace=None) -> torch.Tensor:
+    """One query per sequence at position pos[b]: q_idx [B,1,H_I,d_I], w_idx [B,1,H_I], k_idx [B,cap,d_I]."""
+    _need(q_idx, "q_idx", dims=4)
+    _need(w_idx, "w_idx", torch.float32, 3)
+    _need(k_idx, "k_idx", q_idx.dtype, 3)
+    B, Tq, HI, dI = q_idx.shape
+    _ragged_pos(pos, B)
+    if Tq != 1 or w_idx.shape != (B, 1, HI) or k_idx.shape[2] != dI or k_idx.stride(1) != dI or k_idx.shape[1] < N:
+        raise ValueError("shape mismatch between the index operands")
+    if not (q_idx.is_contiguous() and w_idx.is_contiguous()):
+        raise ValueError("q_idx and w_idx must be contiguous")
+    if topk_idx is None:
+        topk_idx = torch.empty((B, 1, k), dtype=torch.int32, device=q_idx.device)
+    need = index_topk_workspace_bytes(B, 1, N, HI, k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_idx.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().csa_ragged_index_topk(_dt(q_idx), B, N, HI, dI, m, k, _p(pos), _p(q_idx), _p(w_idx), _p(k_idx),
+                                       _bstride(k_idx), _p(topk_idx), _p(scores_out), _p(workspace), ws_bytes,
+                                       _stream(q_idx)))
+    return topk_idx
+
+
+def csa_ragged_index_topk_mx4(q_idx, w_idx, k_codes, k_scales, N: int, m: int, k: int, pos, topk_idx=None,
+                              scores_out=None, workspace=None) -> torch.Tensor:
+    """csa_ragged_index_topk on MXFP4 keys (codes [B,cap,d_I/2], scales [B,cap,d_I/32])."""
+    _need(q_idx, "q_idx", dims=4)
+    _need(w_idx, "w_idx", torch.float32, 3)
+    B, Tq, HI, dI = q_idx.shape
+    _ragged_pos(pos, B)
+    rb = dI // 2
+    if Tq != 1 or k_codes.shape[2] != rb or k_scales.shape[2] != dI // 32 or k_codes.shape[1] < N:
+        raise ValueError("shape mismatch between the index operands")
+    cap = k_codes.stride(0) // rb
+    if k_codes.stride(0) != cap * rb or k_scales.stride(0) != cap * (dI // 32):
+        raise ValueError("k_codes and k_scales must share one batch stride in rows")
+    if topk_idx is None:
+        topk_idx = torch.empty((B, 1, k), dtype=torch.int32, device=q_idx.device)
+    need = index_topk_workspace_bytes(B, 1, N, HI, k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_idx.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().csa_ragged_index_topk_mx4(_dt(q_idx), B, N, HI, dI, m, k, _p(pos), _p(q_idx), _p(w_idx),
+                                           _p(k_codes), _p(k_scales), cap, _p(topk_idx), _p(scores_out),
+                                           _p(workspace), ws_bytes, _stream(q_idx)))
+    return topk_idx
+
+
+def csa_ragged_sparse_mqa(q, entries, topk_idx, raw_ring, ring: int, N: int, m: int, W: int, pos,
+                          scale: float | None = None, out=None, lse=None, workspace=None):
+    """One query per sequence at position pos[b]; window rows from raw_ring (position p at row p % ring)."""
+    B, Tq, H, d, out = _mqa_checks(q, entries, raw_ring, out, lse)
+    _ragged_pos(pos, B)
+    k = topk_idx.shape[2]
+    scale = (1.0 / d ** 0.5) if scale is None else scale
+    need = mqa_workspace_bytes(B, 1, H, d, k + W)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().csa_ragged_sparse_mqa(_dt(q), B, H, d, N, m, k, W, _p(pos), scale, _p(q), _p(entries),
+                                       _bstride(entries), _p(topk_idx), _p(raw_ring), _bstride(raw_ring), ring,
+                                       _p(out), _p(lse), _p(workspace), ws_bytes, _stream(q)))
+    return out
+
+
+def hca_ragged_dense_mqa(q, entries, raw_ring, ring: int, N: int, m: int, W: int, pos, scale: float | None = None,
+                         out=None, lse=None, workspace=None):
+    """HCA with one query per sequence at position pos[b]; window rows from raw_ring."""
+    B, Tq, H, d, out = _mqa_checks(q, entries, raw_ring, out, lse)
+    _ragged_pos(pos, B)
+    scale = (1.0 / d ** 0.5) if scale is None else scale
+    need = mqa_workspace_bytes(B, 1, H, d, N + W)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().hca_ragged_dense_mqa(_dt(q), B, H, d, N, m, W, _p(pos), scale, _p(q), _p(entries), _bstride(entries),
+                                      _p(raw_ring), _bstride(raw_ring), ring, _p(out), _p(lse), _p(workspace),
+                                      ws_bytes, _stream(q)))
     return out
 
 
@@ -368,3 +502,4 @@ def hca_dense_mqa(q, entries, raw, N: int, m: int, W: int, q_pos0: int, raw_pos0
 
 from .step import AttentionStep  # noqa: E402  (uses the functions above)
 from .stream import StreamingLayer, chunk_plan, ring_size  # noqa: E402
+from .ragged import RaggedLayer  # noqa: E402

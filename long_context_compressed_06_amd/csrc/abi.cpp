@@ -160,8 +160,12 @@ int csa_append_rows_multi(int count, const csa_append_job *jobs, void *stream) {
     for (int i = 0; i < count; ++i) {
         const csa_append_job &J = jobs[i];
         int vw = 1;
+        if (J.every < 0) return fail(CSA_EINVAL, "job %d: every must be >= 0", i);
+        if (J.pos && !aligned(J.pos, 8)) return fail(CSA_EALIGN, "job %d: pos needs 8-byte alignment", i);
+        // with positions from memory the destination rows are checked on the device (rows outside are
+        // skipped); the host checks what it can: a zero base position
         if (int s = check_append(J.B, J.n, J.row_bytes, J.rows, J.rows_bstride, J.dst, J.dst_bstride, J.dst_rows,
-                                 J.pos0, J.ring, &vw)) {
+                                 (J.pos || J.every) ? 0 : J.pos0, J.ring, &vw)) {
             std::string d = "job " + std::to_string(i) + ": " + g_detail;
             return fail(s, "%s", d.c_str());
         }
@@ -184,11 +188,47 @@ int csa_append_rows_multi(int count, const csa_append_job *jobs, void *stream) {
         A.dst_bs = J.dst_bstride;
         A.pos0 = J.pos0;
         A.ring = J.ring;
+        A.pos = J.pos;
+        A.every = J.every;
+        A.dst_rows = J.dst_rows;
         A.vw = vw;
         A.B = J.B;
     }
     if (live == 0) return ok();
     return hip_status(csa::launch_append_multi(aj, live, (hipStream_t)stream), "append launch");
+}
+
+int csa_positions_advance(int B, int64_t *pos, int64_t delta, void *stream) {
+    if (B < 0) return fail(CSA_EINVAL, "B=%d must be >= 0", B);
+    if (B == 0) return ok();
+    if (!pos) return fail(CSA_EINVAL, "NULL pos");
+    if (!aligned(pos, 8)) return fail(CSA_EALIGN, "pos needs 8-byte alignment");
+    return hip_status(csa::launch_positions_advance(B, pos, delta, (hipStream_t)stream), "advance launch");
+}
+
+int csa_ragged_compress(int dt, int B, int m, int d, const int64_t *pos, const void *raw_ring, int64_t ring_bstride,
+                        const float *logit_ring, int64_t logit_bstride, int64_t ring, void *out, int64_t out_bstride,
+                        int64_t out_rows, void *stream) {
+    if (int s = check_dt(dt)) return s;
+    if (B < 0 || out_rows < 0) return fail(CSA_EINVAL, "B and out_rows must be >= 0");
+    if (m < 1 || m > 128) return fail(CSA_EUNSUPPORTED, "m=%d outside 1..128", m);
+    if (!d_supported(d)) return fail(CSA_EUNSUPPORTED, "d=%d not in {32,64,128,256,512}", d);
+    if (ring < m) return fail(CSA_EINVAL, "a ring of %lld positions cannot hold a group of %d", (long long)ring, m);
+    if (B == 0 || out_rows == 0) return ok();
+    if (!pos || !raw_ring || !logit_ring || !out) return fail(CSA_EINVAL, "NULL tensor pointer");
+    if (ring_bstride < 2 * ring * d || logit_bstride < 2 * ring || out_bstride < out_rows * d)
+        return fail(CSA_EINVAL, "a batch stride is smaller than one batch's extent (rings hold 2*ring rows)");
+    if (!aligned(raw_ring, 16) || !aligned(out, 16) || !aligned(logit_ring, 4) || !aligned(pos, 8) ||
+        ring_bstride % 8 || out_bstride % 8)
+        return fail(CSA_EALIGN, "raw/out need 16-byte alignment and batch strides a multiple of 8 elements");
+    const size_t es = esize(dt);
+    const Span so = span(out, B, out_bstride, out_rows * d, es);
+    if (overlap(so, span(raw_ring, B, ring_bstride, 2 * ring * d, es)) ||
+        overlap(so, span(logit_ring, B, logit_bstride, 2 * ring, 4)) || overlap(so, span(pos, 1, 0, B, 8)))
+        return fail(CSA_EINVAL, "out overlaps an input");
+    return hip_status(csa::launch_compress_ragged(dt, B, m, d, pos, raw_ring, ring_bstride, logit_ring, logit_bstride,
+                                                  ring, out, out_bstride, out_rows, (hipStream_t)stream),
+                      "compress launch");
 }
 
 int csa_append_rows(int B, int n, int64_t row_bytes, const void *rows, int64_t rows_bstride, void *dst,
@@ -215,16 +255,30 @@ size_t csa_index_topk_workspace_bytes(int B, int Tq, int N, int H_I, int k) {
     return scores_bytes(rows, N) + (csa::topk_scratch_bytes(rows, N) + 255) / 256 * 256;
 }
 
-int csa_index_topk(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k, int64_t q_pos0, const void *q_idx,
-                   const float *w_idx, const void *k_idx, int64_t k_bstride, int32_t *topk_idx, float *scores_out,
-                   void *workspace, size_t workspace_bytes, void *stream) {
+// positions: a uniform q_pos0 (>= 0), or per-sequence device positions with Tq = 1
+static int check_qpos(csa::QPos qp, int B, int Tq) {
+    if (qp.pos) {
+        if (Tq != 1) return fail(CSA_EINVAL, "per-sequence positions need one query per sequence");
+        if (!aligned(qp.pos, 8)) return fail(CSA_EALIGN, "pos needs 8-byte alignment");
+    } else if (qp.q_pos0 < 0) {
+        return fail(CSA_EINVAL, "q_pos0 must be >= 0");
+    }
+    (void)B;
+    return CSA_OK;
+}
+
+static int index_topk_impl(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k, csa::QPos q_pos0,
+                           const void *q_idx, const float *w_idx, const void *k_idx, int64_t k_bstride,
+                           int32_t *topk_idx, float *scores_out, void *workspace, size_t workspace_bytes,
+                           void *stream) {
     if (int s = check_dt(dt)) return s;
     if (B < 0 || Tq < 0 || N < 0) return fail(CSA_EINVAL, "B, Tq and N must be >= 0");
     if (H_I < 1 || H_I > 64) return fail(CSA_EUNSUPPORTED, "H_I=%d outside 1..64", H_I);
     if (!dI_supported(d_I)) return fail(CSA_EUNSUPPORTED, "d_I=%d not in {32,64,128}", d_I);
     if (m < 1) return fail(CSA_EINVAL, "m=%d must be >= 1", m);
     if (k < 1 || k > 2048) return fail(CSA_EUNSUPPORTED, "k=%d outside 1..2048", k);
-    if (q_pos0 < 0) return fail(CSA_EINVAL, "q_pos0 must be >= 0");
+    if ((int64_t)B * Tq > 0)
+        if (int s = check_qpos(q_pos0, B, Tq)) return s;
     if (N > csa::kTopkMaxEntries) return fail(CSA_EUNSUPPORTED, "N=%d above %lld entries", N, (long long)csa::kTopkMaxEntries);
     if ((int64_t)B * Tq == 0) return ok();
     if (!q_idx || !w_idx || !topk_idx || (N > 0 && !k_idx)) return fail(CSA_EINVAL, "NULL tensor pointer");
@@ -267,6 +321,23 @@ int csa_index_topk(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k,
     return hip_status(csa::launch_topk(B, Tq, N, m, k, q_pos0, scores, scratch, topk_idx, st), "top-k launch");
 }
 
+int csa_index_topk(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k, int64_t q_pos0, const void *q_idx,
+                   const float *w_idx, const void *k_idx, int64_t k_bstride, int32_t *topk_idx, float *scores_out,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+    if (q_pos0 < 0) return fail(CSA_EINVAL, "q_pos0 must be >= 0");
+    return index_topk_impl(dt, B, Tq, N, H_I, d_I, m, k, csa::QPos(q_pos0), q_idx, w_idx, k_idx, k_bstride, topk_idx,
+                           scores_out, workspace, workspace_bytes, stream);
+}
+
+int csa_ragged_index_topk(int dt, int B, int N, int H_I, int d_I, int m, int k, const int64_t *pos,
+                          const void *q_idx, const float *w_idx, const void *k_idx, int64_t k_bstride,
+                          int32_t *topk_idx, float *scores_out, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+    if (B > 0 && !pos) return fail(CSA_EINVAL, "NULL pos");
+    return index_topk_impl(dt, B, 1, N, H_I, d_I, m, k, csa::QPos(0, pos), q_idx, w_idx, k_idx, k_bstride, topk_idx,
+                           scores_out, workspace, workspace_bytes, stream);
+}
+
 int csa_index_scores(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int64_t q_pos0, const void *q_idx,
                      const float *w_idx, const void *k_idx, int64_t k_bstride, float *scores, void *stream) {
     if (int s = check_dt(dt)) return s;
@@ -305,17 +376,18 @@ int csa_mx4_quantize(int dt, int64_t n_rows, int d, const void *x, uint8_t *code
                       "quantise launch");
 }
 
-int csa_index_topk_mx4(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k, int64_t q_pos0,
-                       const void *q_idx, const float *w_idx, const uint8_t *k_codes, const uint8_t *k_scales,
-                       int64_t k_bstride, int32_t *topk_idx, float *scores_out, void *workspace,
-                       size_t workspace_bytes, void *stream) {
+static int index_topk_mx4_impl(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k, csa::QPos q_pos0,
+                               const void *q_idx, const float *w_idx, const uint8_t *k_codes,
+                               const uint8_t *k_scales, int64_t k_bstride, int32_t *topk_idx, float *scores_out,
+                               void *workspace, size_t workspace_bytes, void *stream) {
     if (int s = check_dt(dt)) return s;
     if (B < 0 || Tq < 0 || N < 0) return fail(CSA_EINVAL, "B, Tq and N must be >= 0");
     if (H_I < 1 || H_I > 64) return fail(CSA_EUNSUPPORTED, "H_I=%d outside 1..64", H_I);
     if (!dI_supported(d_I)) return fail(CSA_EUNSUPPORTED, "d_I=%d not in {32,64,128}", d_I);
     if (m < 1) return fail(CSA_EINVAL, "m=%d must be >= 1", m);
     if (k < 1 || k > 2048) return fail(CSA_EUNSUPPORTED, "k=%d outside 1..2048", k);
-    if (q_pos0 < 0) return fail(CSA_EINVAL, "q_pos0 must be >= 0");
+    if ((int64_t)B * Tq > 0)
+        if (int s = check_qpos(q_pos0, B, Tq)) return s;
     if (N > csa::kTopkMaxEntries) return fail(CSA_EUNSUPPORTED, "N=%d above %lld entries", N, (long long)csa::kTopkMaxEntries);
     if ((int64_t)B * Tq == 0) return ok();
     if (!q_idx || !w_idx || !topk_idx || (N > 0 && (!k_codes || !k_scales)))
@@ -357,6 +429,24 @@ int csa_index_topk_mx4(int dt, int B, int Tq, int N, int H_I, int d_I, int m, in
     return hip_status(csa::launch_topk(B, Tq, N, m, k, q_pos0, scores, scratch, topk_idx, st), "top-k launch");
 }
 
+int csa_index_topk_mx4(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k, int64_t q_pos0,
+                       const void *q_idx, const float *w_idx, const uint8_t *k_codes, const uint8_t *k_scales,
+                       int64_t k_bstride, int32_t *topk_idx, float *scores_out, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    if (q_pos0 < 0) return fail(CSA_EINVAL, "q_pos0 must be >= 0");
+    return index_topk_mx4_impl(dt, B, Tq, N, H_I, d_I, m, k, csa::QPos(q_pos0), q_idx, w_idx, k_codes, k_scales,
+                               k_bstride, topk_idx, scores_out, workspace, workspace_bytes, stream);
+}
+
+int csa_ragged_index_topk_mx4(int dt, int B, int N, int H_I, int d_I, int m, int k, const int64_t *pos,
+                              const void *q_idx, const float *w_idx, const uint8_t *k_codes,
+                              const uint8_t *k_scales, int64_t k_bstride, int32_t *topk_idx, float *scores_out,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+    if (B > 0 && !pos) return fail(CSA_EINVAL, "NULL pos");
+    return index_topk_mx4_impl(dt, B, 1, N, H_I, d_I, m, k, csa::QPos(0, pos), q_idx, w_idx, k_codes, k_scales,
+                               k_bstride, topk_idx, scores_out, workspace, workspace_bytes, stream);
+}
+
 size_t csa_mqa_workspace_bytes(int B, int Tq, int H, int d, int n_rows_max) {
     if (B <= 0 || Tq <= 0 || H <= 0 || d <= 0) return 0;
     int tps = 0;
@@ -367,10 +457,11 @@ size_t csa_mqa_workspace_bytes(int B, int Tq, int H, int d, int n_rows_max) {
     return (bytes + 255) / 256 * 256;
 }
 
-static int mqa_common(int dt, int B, int Tq, int H, int d, int N, int m, int k, int W, int64_t q_pos0, float scale,
+// raw_ring > 0 (with per-sequence positions): the raw rows are a ring, position p at row p mod raw_ring
+static int mqa_common(int dt, int B, int Tq, int H, int d, int N, int m, int k, int W, csa::QPos q_pos0, float scale,
                       const void *q, const void *entries, int64_t e_bstride, const int32_t *idx, const void *raw,
-                      int64_t raw_bstride, int64_t raw_pos0, int raw_len, float *out, float *lse, void *workspace,
-                      size_t workspace_bytes, void *stream) {
+                      int64_t raw_bstride, int64_t raw_pos0, int64_t raw_len, int64_t raw_ring, float *out,
+                      float *lse, void *workspace, size_t workspace_bytes, void *stream) {
     if (int s = check_dt(dt)) return s;
     if (B < 0 || Tq < 0 || N < 0 || W < 0 || raw_len < 0) return fail(CSA_EINVAL, "B, Tq, N, W, raw_len must be >= 0");
     if (H < 1 || H > 64) return fail(CSA_EUNSUPPORTED, "H=%d outside 1..64", H);
@@ -378,13 +469,21 @@ static int mqa_common(int dt, int B, int Tq, int H, int d, int N, int m, int k, 
     if (m < 1) return fail(CSA_EINVAL, "m=%d must be >= 1", m);
     if (k < 0 || k > 2048) return fail(CSA_EUNSUPPORTED, "k=%d outside 1..2048", k);
     if (!(scale > 0.f) || !std::isfinite(scale)) return fail(CSA_EINVAL, "scale must be finite and > 0");
-    if (q_pos0 < 0 || raw_pos0 < 0) return fail(CSA_EINVAL, "positions must be >= 0");
+    if (raw_pos0 < 0 || raw_ring < 0) return fail(CSA_EINVAL, "positions must be >= 0");
     if ((int64_t)B * Tq == 0) return ok();
-    if (W > 0) {
-        const int64_t win0 = q_pos0 - W + 1 > 0 ? q_pos0 - W + 1 : 0;
-        if (raw_pos0 > win0 || raw_pos0 + raw_len < q_pos0 + Tq)
+    if (int s = check_qpos(q_pos0, B, Tq)) return s;
+    if (W > 0 && raw_ring > 0) {
+        // per-sequence positions: the window is whatever the ring holds (any position maps inside it)
+        if (raw_ring < W) return fail(CSA_EINVAL, "a ring of %lld positions cannot hold a window of %d",
+                                      (long long)raw_ring, W);
+        if (!raw) return fail(CSA_EINVAL, "NULL raw with W > 0");
+        if (raw_bstride < raw_len * d) return fail(CSA_EINVAL, "raw_bstride smaller than the ring's rows");
+    } else if (W > 0) {
+        const int64_t qp = q_pos0.q_pos0;
+        const int64_t win0 = qp - W + 1 > 0 ? qp - W + 1 : 0;
+        if (raw_pos0 > win0 || raw_pos0 + raw_len < qp + Tq)
             return fail(CSA_EINVAL, "raw rows [%lld, %lld) do not cover the window [%lld, %lld)", (long long)raw_pos0,
-                        (long long)(raw_pos0 + raw_len), (long long)win0, (long long)(q_pos0 + Tq));
+                        (long long)(raw_pos0 + raw_len), (long long)win0, (long long)(qp + Tq));
         if (!raw) return fail(CSA_EINVAL, "NULL raw with W > 0");
         if (raw_bstride < (int64_t)raw_len * d) return fail(CSA_EINVAL, "raw_bstride smaller than raw_len*d");
     }
@@ -416,7 +515,8 @@ static int mqa_common(int dt, int B, int Tq, int H, int d, int N, int m, int k, 
         ws = (float *)workspace;
     }
     return hip_status(csa::launch_mqa(dt, B, Tq, H, d, N, m, k, W, q_pos0, scale, q, entries, e_bstride, idx, raw,
-                                      raw_bstride, raw_pos0, out, lse, ws, splits, tps, (hipStream_t)stream),
+                                      raw_bstride, raw_pos0, raw_ring, out, lse, ws, splits, tps,
+                                      (hipStream_t)stream),
                       "attention launch");
 }
 
@@ -425,15 +525,38 @@ int csa_sparse_mqa(int dt, int B, int Tq, int H, int d, int N, int m, int k, int
                    int64_t raw_bstride, int64_t raw_pos0, int raw_len, float *out, float *lse, void *workspace,
                    size_t workspace_bytes, void *stream) {
     if (k < 1 || k > 2048) return fail(CSA_EUNSUPPORTED, "k=%d outside 1..2048", k);
-    return mqa_common(dt, B, Tq, H, d, N, m, k, W, q_pos0, scale, q, entries, e_bstride, topk_idx, raw, raw_bstride,
-                      raw_pos0, raw_len, out, lse, workspace, workspace_bytes, stream);
+    if (q_pos0 < 0) return fail(CSA_EINVAL, "positions must be >= 0");
+    return mqa_common(dt, B, Tq, H, d, N, m, k, W, csa::QPos(q_pos0), scale, q, entries, e_bstride, topk_idx, raw,
+                      raw_bstride, raw_pos0, raw_len, 0, out, lse, workspace, workspace_bytes, stream);
+}
+
+int csa_ragged_sparse_mqa(int dt, int B, int H, int d, int N, int m, int k, int W, const int64_t *pos, float scale,
+                          const void *q, const void *entries, int64_t e_bstride, const int32_t *topk_idx,
+                          const void *raw_ring, int64_t ring_bstride, int64_t ring, float *out, float *lse,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    if (k < 1 || k > 2048) return fail(CSA_EUNSUPPORTED, "k=%d outside 1..2048", k);
+    if (B > 0 && !pos) return fail(CSA_EINVAL, "NULL pos");
+    if (ring < 1) return fail(CSA_EINVAL, "ring must be >= 1");
+    return mqa_common(dt, B, 1, H, d, N, m, k, W, csa::QPos(0, pos), scale, q, entries, e_bstride, topk_idx,
+                      raw_ring, ring_bstride, 0, ring, ring, out, lse, workspace, workspace_bytes, stream);
+}
+
+int hca_ragged_dense_mqa(int dt, int B, int H, int d, int N, int m, int W, const int64_t *pos, float scale,
+                         const void *q, const void *entries, int64_t e_bstride, const void *raw_ring,
+                         int64_t ring_bstride, int64_t ring, float *out, float *lse, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    if (B > 0 && !pos) return fail(CSA_EINVAL, "NULL pos");
+    if (ring < 1) return fail(CSA_EINVAL, "ring must be >= 1");
+    return mqa_common(dt, B, 1, H, d, N, m, 0, W, csa::QPos(0, pos), scale, q, entries, e_bstride, nullptr, raw_ring,
+                      ring_bstride, 0, ring, ring, out, lse, workspace, workspace_bytes, stream);
 }
 
 int hca_dense_mqa(int dt, int B, int Tq, int H, int d, int N, int m, int W, int64_t q_pos0, float scale, const void *q,
                   const void *entries, int64_t e_bstride, const void *raw, int64_t raw_bstride, int64_t raw_pos0,
                   int raw_len, float *out, float *lse, void *workspace, size_t workspace_bytes, void *stream) {
-    return mqa_common(dt, B, Tq, H, d, N, m, 0, W, q_pos0, scale, q, entries, e_bstride, nullptr, raw, raw_bstride,
-                      raw_pos0, raw_len, out, lse, workspace, workspace_bytes, stream);
+    if (q_pos0 < 0) return fail(CSA_EINVAL, "positions must be >= 0");
+    return mqa_common(dt, B, Tq, H, d, N, m, 0, W, csa::QPos(q_pos0), scale, q, entries, e_bstride, nullptr, raw,
+                      raw_bstride, raw_pos0, raw_len, 0, out, lse, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -11,6 +11,9 @@
 // FP4 codes and scale bytes all move through the same kernel.
 //
 // k_append_rows: a grid-stride copy per batch (blockIdx.y), VW-byte vectors.
+// k_append_multi: up to eight such copies in one launch (blockIdx.z); a job
+// may take each batch's position from device memory (ragged batches) and may
+// keep only the token that completes a group, writing it to that group's row.
 #include "kernels.h"
 
 namespace csa {
@@ -59,11 +62,18 @@ __device__ __forceinline__ void append_job_body(const AppendJob &J) {
     const int64_t vpr = J.row_bytes / VW;
     const unsigned char *s = J.src + b * J.src_bs;
     unsigned char *d = J.dst + b * J.dst_bs;
+    const int64_t base = J.pos0 + (J.pos ? J.pos[b] : 0);
     for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < J.n * vpr; e += (int64_t)gridDim.x * 256) {
         const int64_t i = e / vpr, v = e % vpr;
+        int64_t p = base + i;
+        if (J.every > 0) {  // only the token that completes a group: its row goes to that group's index
+            if (p < 0 || (p + 1) % J.every != 0) continue;
+            p = (p + 1) / J.every - 1;
+        }
+        if (p < 0) continue;  // (positions read from memory are not checked by the host)
         const V x = *(const V *)(s + i * J.row_bytes + v * VW);
-        const int64_t p = J.pos0 + i;
         if (J.ring == 0) {
+            if (p >= J.dst_rows) continue;
             *(V *)(d + p * J.row_bytes + v * VW) = x;
         } else {
             const int64_t slot = p % J.ring;
@@ -95,6 +105,17 @@ hipError_t launch_append_multi(const AppendJobs &jobs, int count, hipStream_t st
     if (blocks > 1024) blocks = 1024;
     hipLaunchKernelGGL(k_append_multi, dim3((unsigned)blocks, (unsigned)bmax, (unsigned)count), dim3(256), 0, st,
                        jobs);
+    return hipGetLastError();
+}
+
+__global__ void k_positions_advance(int B, int64_t *pos, int64_t delta) {
+    const int b = blockIdx.x * 256 + threadIdx.x;
+    if (b < B) pos[b] += delta;
+}
+
+hipError_t launch_positions_advance(int B, int64_t *pos, int64_t delta, hipStream_t st) {
+    if (B <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_positions_advance, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, st, B, pos, delta);
     return hipGetLastError();
 }
 

@@ -70,6 +70,17 @@ template <> struct Elem<bf16_t> {
     }
 };
 
+// Query positions: every sequence's queries at q_pos0, q_pos0 + 1, ...
+// (uniform batches), or, with `pos` set, sequence b's queries at pos[b],
+// pos[b] + 1, ... read from device memory (ragged batches: each sequence at
+// its own length).  Converts from a plain position.
+struct QPos {
+    int64_t q_pos0;
+    const int64_t *pos;
+    __host__ __device__ QPos(int64_t p = 0, const int64_t *ps = nullptr) : q_pos0(p), pos(ps) {}
+    __device__ __forceinline__ int64_t at(int64_t b, int64_t ti) const { return (pos ? pos[b] : q_pos0) + ti; }
+};
+
 // Entries visible to a query at absolute position t: complete groups only.
 __device__ __forceinline__ int64_t n_visible(int64_t t, int m, int64_t N) {
     if (t < 0) return 0;

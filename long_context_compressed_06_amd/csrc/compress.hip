@@ -16,29 +16,27 @@ namespace csa {
 
 constexpr int kRowsPerThread = 4;
 
+// One workgroup's share of one group: rows = the group's first row at this
+// slice's first column (rows d apart), z = its m logits, o = the entry at this
+// slice's first column.
 template <typename T>
-__global__ __launch_bounds__(256) void k_compress(int G, int m, int d, int tpr, int slices, const T *__restrict__ raw,
-                                                   int64_t raw_bs, const float *__restrict__ logits,
-                                                   int64_t log_bs, T *__restrict__ out, int64_t out_bs) {
+__device__ __forceinline__ void compress_group(const T *__restrict__ rows, const float *__restrict__ z, int m, int d,
+                                               int tpr, T *__restrict__ o) {
     constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte vector
     __shared__ float alpha[128];
     __shared__ float red[256 * VEC];
 
-    const int sl = blockIdx.x % slices;
-    const int bg = blockIdx.x / slices;
-    const int b = bg / G, g = bg % G;
     const int tid = threadIdx.x, lane = tid & 63;
     const int rpar = 256 / tpr;        // rows accumulated in parallel
     const int c = tid % tpr, rs = tid / tpr;
     const int width = tpr * VEC;       // columns of this slice
-    const T *rows = raw + b * raw_bs + (int64_t)g * m * d + sl * width + c * VEC;
+    rows += c * VEC;
     u32x4 v[kRowsPerThread];
 #pragma unroll
     for (int u = 0; u < kRowsPerThread; ++u) {
         const int i = rs + u * rpar;
         v[u] = i < m ? *(const u32x4 *)(rows + (int64_t)i * d) : u32x4{0u, 0u, 0u, 0u};
     }
-    const float *z = logits + b * log_bs + (int64_t)g * m;
     if (tid < 64) {
         const float z0 = lane < m ? z[lane] : -INFINITY;
         const float z1 = lane + 64 < m ? z[lane + 64] : -INFINITY;
@@ -65,12 +63,46 @@ __global__ __launch_bounds__(256) void k_compress(int G, int m, int d, int tpr, 
 #pragma unroll
     for (int e = 0; e < VEC; ++e) red[rs * width + c * VEC + e] = acc[e];
     __syncthreads();
-    T *o = out + b * out_bs + (int64_t)g * d + sl * width;
     for (int x = tid; x < width; x += 256) {
         float s = 0.f;
         for (int r = 0; r < rpar; ++r) s += red[r * width + x];
         o[x] = Elem<T>::from_f32(s);
     }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_compress(int G, int m, int d, int tpr, int slices, const T *__restrict__ raw,
+                                                   int64_t raw_bs, const float *__restrict__ logits,
+                                                   int64_t log_bs, T *__restrict__ out, int64_t out_bs) {
+    const int sl = blockIdx.x % slices;
+    const int bg = blockIdx.x / slices;
+    const int b = bg / G, g = bg % G;
+    const int width = tpr * (16 / (int)sizeof(T));
+    compress_group(raw + b * raw_bs + (int64_t)g * m * d + sl * width, logits + b * log_bs + (int64_t)g * m, m, d,
+                   tpr, out + b * out_bs + (int64_t)g * d + sl * width);
+}
+
+// Ragged batches: sequence b's newest token is at position pos[b]; when it
+// completes a group (pos[b] + 1 a multiple of m) that group g = (pos[b]+1)/m - 1
+// is pooled out of the mirrored raw and logit rings (position p at row p mod
+// ring; the group's m rows are consecutive from row (g*m) mod ring) into entry g,
+// if g < out_rows.  Other sequences' workgroups return at once.
+template <typename T>
+__global__ __launch_bounds__(256) void k_compress_ragged(int m, int d, int tpr, int slices,
+                                                          const int64_t *__restrict__ pos, const T *__restrict__ raw,
+                                                          int64_t raw_bs, const float *__restrict__ logits,
+                                                          int64_t log_bs, int64_t ring, T *__restrict__ out,
+                                                          int64_t out_bs, int64_t out_rows) {
+    const int sl = blockIdx.x % slices;
+    const int64_t b = blockIdx.x / slices;
+    const int64_t p = pos[b];
+    if (p < 0 || (p + 1) % m != 0) return;
+    const int64_t g = (p + 1) / m - 1;
+    if (g >= out_rows) return;
+    const int64_t r0 = (g * m) % ring;
+    const int width = tpr * (16 / (int)sizeof(T));
+    compress_group(raw + b * raw_bs + r0 * d + sl * width, logits + b * log_bs + r0, m, d, tpr,
+                   out + b * out_bs + g * d + sl * width);
 }
 
 // Per-channel pooling logits: channel x of entry g pools channel x of the
@@ -164,6 +196,30 @@ hipError_t launch_compress_t(int B, int G, int m, int d, const void *raw, int64_
                        slices, (const T *)raw, raw_bs, logits, log_bs, (T *)out, out_bs);
     return hipGetLastError();
 }
+template <typename T>
+hipError_t launch_compress_ragged_t(int B, int m, int d, const int64_t *pos, const void *raw, int64_t raw_bs,
+                                    const float *logits, int64_t log_bs, int64_t ring, void *out, int64_t out_bs,
+                                    int64_t out_rows, hipStream_t st) {
+    constexpr int VEC = 16 / sizeof(T);
+    int tpr = d / VEC;
+    if (tpr > 256) return hipErrorInvalidValue;
+    while (tpr > 1 && (256 / tpr) * kRowsPerThread < m) tpr /= 2;
+    if ((256 / tpr) * kRowsPerThread < m) return hipErrorInvalidValue;
+    const int slices = d / VEC / tpr;
+    hipLaunchKernelGGL(k_compress_ragged<T>, dim3((unsigned)((int64_t)B * slices)), dim3(256), 0, st, m, d, tpr,
+                       slices, pos, (const T *)raw, raw_bs, logits, log_bs, ring, (T *)out, out_bs, out_rows);
+    return hipGetLastError();
+}
+hipError_t launch_compress_ragged(int dt, int B, int m, int d, const int64_t *pos, const void *raw, int64_t raw_bs,
+                                  const float *logits, int64_t log_bs, int64_t ring, void *out, int64_t out_bs,
+                                  int64_t out_rows, hipStream_t st) {
+    if (dt == 0)
+        return launch_compress_ragged_t<float>(B, m, d, pos, raw, raw_bs, logits, log_bs, ring, out, out_bs,
+                                               out_rows, st);
+    return launch_compress_ragged_t<bf16_t>(B, m, d, pos, raw, raw_bs, logits, log_bs, ring, out, out_bs, out_rows,
+                                            st);
+}
+
 template <typename T>
 hipError_t launch_compress_channels_t(int B, int G, int m, int d, const void *raw, int64_t raw_bs,
                                       const float *logits, int64_t log_bs, void *out, int64_t out_bs,

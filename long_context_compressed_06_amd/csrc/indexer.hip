@@ -24,7 +24,7 @@
 namespace csa {
 
 template <typename T, int DI, int MB>
-__global__ __launch_bounds__(256) void k_index_scores(int Tq, int N, int HI, int m, int64_t q_pos0, int64_t n_items,
+__global__ __launch_bounds__(256) void k_index_scores(int Tq, int N, int HI, int m, QPos q_pos0, int64_t n_items,
                                                        int chunks_per_row,
                                                        const T *__restrict__ qI, const float *__restrict__ w,
                                                        const T *__restrict__ kI, int64_t k_bs,
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void k_index_scores(int Tq, int N, int HI, int
     const int64_t row = item / chunks_per_row;
     const int chunk = (int)(item % chunks_per_row);
     const int64_t b = row / Tq, ti = row % Tq;
-    const int64_t nv = n_visible(q_pos0 + ti, m, N);
+    const int64_t nv = n_visible(q_pos0.at(b, ti), m, N);
     const int g = lane >> 4, c = lane & 15;
 
     typename E::frag a[MB][KS];
@@ -193,7 +193,7 @@ __device__ __forceinline__ float sum_lane_groups(float x) {
 }
 
 template <int DI, int MB>
-__global__ __launch_bounds__(kIdxWaves * 64) void k_index_dma(int Tq, int N, int HI, int m, int64_t q_pos0,
+__global__ __launch_bounds__(kIdxWaves * 64) void k_index_dma(int Tq, int N, int HI, int m, QPos q_pos0,
                                                                int blocks_per_row, const bf16_t *__restrict__ qI,
                                                                const float *__restrict__ w,
                                                                const bf16_t *__restrict__ kI, int64_t k_bs,
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_dma(int Tq, int N, int
     const int64_t row = blockIdx.x / blocks_per_row;
     const int part = blockIdx.x % blocks_per_row;
     const int64_t b = row / Tq, ti = row % Tq;
-    const int64_t nv = n_visible(q_pos0 + ti, m, N);
+    const int64_t nv = n_visible(q_pos0.at(b, ti), m, N);
     const int wpr = blocks_per_row * kIdxWaves;       // wavefronts per query
     const int gw = part * kIdxWaves + wv;             // this wavefront's rank
     const int tiles = (N + 15) / 16;
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_dma(int Tq, int N, int
 }
 
 template <int DI, int MB>
-static hipError_t launch_dma(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const void *qI, const float *w,
+static hipError_t launch_dma(int B, int Tq, int N, int HI, int m, QPos q_pos0, const void *qI, const float *w,
                              const void *kI, int64_t k_bs, float *scores, int64_t s_stride, float *scores2,
                              uint32_t *hist, hipStream_t st) {
     using S = IdxDma<DI>;
@@ -358,7 +358,7 @@ static hipError_t launch_dma(int B, int Tq, int N, int HI, int m, int64_t q_pos0
 }
 
 template <typename T, int DI, int MB>
-static hipError_t launch_t(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const void *qI, const float *w,
+static hipError_t launch_t(int B, int Tq, int N, int HI, int m, QPos q_pos0, const void *qI, const float *w,
                            const void *kI, int64_t k_bs, float *scores, int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
     const int64_t rows = (int64_t)B * Tq;
     const int64_t batches = (N + 63) / 64;  // batches of four 16-entry tiles
@@ -406,7 +406,7 @@ struct IdxPre {
 };
 
 template <int DI, int MB>
-__global__ __launch_bounds__(kPreWaves * 64) void k_index_prefill(int Tq, int N, int HI, int m, int64_t q_pos0,
+__global__ __launch_bounds__(kPreWaves * 64) void k_index_prefill(int Tq, int N, int HI, int m, QPos q_pos0,
                                                                    int blocks_per_seq, const bf16_t *__restrict__ qI,
                                                                    const float *__restrict__ w,
                                                                    const bf16_t *__restrict__ kI, int64_t k_bs,
@@ -427,9 +427,9 @@ __global__ __launch_bounds__(kPreWaves * 64) void k_index_prefill(int Tq, int N,
     const int ti = q0 + wv;
     const bool on = ti < Tq;
     const int64_t row = b * Tq + min(ti, Tq - 1);
-    const int64_t nv = on ? n_visible(q_pos0 + ti, m, N) : 0;
+    const int64_t nv = on ? n_visible(q_pos0.at(b, ti), m, N) : 0;
     // visible entries of the workgroup's last query bound every tile it computes
-    const int64_t nv_max = n_visible(q_pos0 + min(q0 + kPreWaves, Tq) - 1, m, N);
+    const int64_t nv_max = n_visible(q_pos0.at(b, min(q0 + kPreWaves, Tq) - 1), m, N);
     const int vtiles = (int)((nv_max + kPreRows - 1) / kPreRows);
 
     if (hist)
@@ -529,7 +529,7 @@ __global__ __launch_bounds__(kPreWaves * 64) void k_index_prefill(int Tq, int N,
 }
 
 template <int DI, int MB>
-static hipError_t launch_prefill(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const void *qI, const float *w,
+static hipError_t launch_prefill(int B, int Tq, int N, int HI, int m, QPos q_pos0, const void *qI, const float *w,
                                  const void *kI, int64_t k_bs, float *scores, int64_t s_stride, float *scores2,
                                  uint32_t *hist, hipStream_t st) {
     using S = IdxPre<DI>;
@@ -544,7 +544,7 @@ static hipError_t launch_prefill(int B, int Tq, int N, int HI, int m, int64_t q_
 }
 
 template <typename T, int DI>
-static hipError_t launch_di(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const void *qI, const float *w,
+static hipError_t launch_di(int B, int Tq, int N, int HI, int m, QPos q_pos0, const void *qI, const float *w,
                             const void *kI, int64_t k_bs, float *scores, int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
     if constexpr (sizeof(T) == 2) {
         // many queries per sequence: the query-blocked kernel
@@ -570,7 +570,7 @@ static hipError_t launch_di(int B, int Tq, int N, int HI, int m, int64_t q_pos0,
 }
 
 template <typename T>
-static hipError_t launch_dt(int B, int Tq, int N, int HI, int dI, int m, int64_t q_pos0, const void *qI,
+static hipError_t launch_dt(int B, int Tq, int N, int HI, int dI, int m, QPos q_pos0, const void *qI,
                             const float *w, const void *kI, int64_t k_bs, float *scores, int64_t s_stride, float *scores2,
                             uint32_t *hist, hipStream_t st) {
     switch (dI) {
@@ -583,7 +583,7 @@ static hipError_t launch_dt(int B, int Tq, int N, int HI, int dI, int m, int64_t
     }
 }
 
-hipError_t launch_index_scores(int dt, int B, int Tq, int N, int HI, int dI, int m, int64_t q_pos0, const void *qI,
+hipError_t launch_index_scores(int dt, int B, int Tq, int N, int HI, int dI, int m, QPos q_pos0, const void *qI,
                                const float *w, const void *kI, int64_t k_bs, float *scores, int64_t s_stride, float *scores2,
                                uint32_t *hist, hipStream_t st) {
     if (dt == 0) return launch_dt<float>(B, Tq, N, HI, dI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride,

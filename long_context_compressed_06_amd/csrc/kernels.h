@@ -35,6 +35,11 @@ size_t topk_clear_words(int64_t rows, int64_t N);
 
 hipError_t launch_compress(int dt, int B, int G, int m, int d, const void *raw, int64_t raw_bs,
                            const float *logits, int64_t log_bs, void *out, int64_t out_bs, hipStream_t st);
+// ragged batches: per sequence, the group completed by its newest token (position pos[b]), read out of
+// mirrored raw / logit rings of `ring` positions, into entry row (pos[b]+1)/m - 1 when below out_rows
+hipError_t launch_compress_ragged(int dt, int B, int m, int d, const int64_t *pos, const void *raw, int64_t raw_bs,
+                                  const float *logits, int64_t log_bs, int64_t ring, void *out, int64_t out_bs,
+                                  int64_t out_rows, hipStream_t st);
 // logits: [B][G*m][d] f32 (per channel), batch stride log_bs elements
 hipError_t launch_compress_channels(int dt, int B, int G, int m, int d, const void *raw, int64_t raw_bs,
                                     const float *logits, int64_t log_bs, void *out, int64_t out_bs,
@@ -42,7 +47,7 @@ hipError_t launch_compress_channels(int dt, int B, int G, int m, int d, const vo
 
 // scores: [rows][s_stride] (s_stride >= N); scores2: optional second copy,
 // [rows][N]; hist: optional [rows, kTopkBins] counts, must be zero on entry
-hipError_t launch_index_scores(int dt, int B, int Tq, int N, int HI, int dI, int m, int64_t q_pos0, const void *qI,
+hipError_t launch_index_scores(int dt, int B, int Tq, int N, int HI, int dI, int m, QPos q_pos0, const void *qI,
                                const float *w, const void *kI, int64_t k_bs, float *scores, int64_t s_stride,
                                float *scores2, uint32_t *hist, hipStream_t st);
 
@@ -54,7 +59,7 @@ hipError_t launch_mx4_quantize(int dt, int64_t n_blocks, const void *x, uint8_t 
 // the indexer on MXFP4 operands: queries qI [rows, HI, dI] in element type dt,
 // quantised inside the kernel; keys as codes [B][k_bs rows][dI/2] and scales
 // [B][k_bs rows][dI/32]; outputs as launch_index_scores
-hipError_t launch_index_mx4(int dt, int B, int Tq, int N, int HI, int dI, int m, int64_t q_pos0, const void *qI,
+hipError_t launch_index_mx4(int dt, int B, int Tq, int N, int HI, int dI, int m, QPos q_pos0, const void *qI,
                             const float *w, const uint8_t *kc, const uint8_t *ks, int64_t k_bs, float *scores,
                             int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st);
 
@@ -74,18 +79,21 @@ constexpr int kMaxAppendJobs = 8;
 struct AppendJob {
     const unsigned char *src;
     unsigned char *dst;
-    int64_t n, row_bytes, src_bs, dst_bs, pos0, ring;
+    const int64_t *pos;  // optional per-batch position added to pos0
+    int64_t n, row_bytes, src_bs, dst_bs, dst_rows, pos0, ring, every;
     int vw, B;
 };
 struct AppendJobs {
     AppendJob j[kMaxAppendJobs];
 };
 hipError_t launch_append_multi(const AppendJobs &jobs, int count, hipStream_t st);
+// pos[b] += delta for b < B
+hipError_t launch_positions_advance(int B, int64_t *pos, int64_t delta, hipStream_t st);
 
 // scores: [rows][topk_score_stride(N)], 16-byte aligned.  scratch:
 // topk_scratch_bytes(rows, N) bytes; its histogram part must have been filled
 // by launch_index_scores (zeroed before it)
-hipError_t launch_topk(int B, int Tq, int N, int m, int k, int64_t q_pos0, const float *scores, void *scratch,
+hipError_t launch_topk(int B, int Tq, int N, int m, int k, QPos q_pos0, const float *scores, void *scratch,
                        int32_t *out, hipStream_t st);
 
 // attention work split: aim for this many workgroups, at most this many
@@ -102,9 +110,10 @@ constexpr int mqa_max_tiles_per_split(int d) { return d >= 512 ? 56 : kMqaMaxTil
 int mqa_choose_splits(int64_t rows, int64_t n_rows_max, int d, int *tiles_per_split);
 
 // ws: split-K partials, rows*n_splits*H*(d+2) floats (unused when n_splits == 1)
-hipError_t launch_mqa(int dt, int B, int Tq, int H, int d, int N, int m, int k, int W, int64_t q_pos0, float scale,
+// raw_ring: 0 -> raw row r is position raw_pos0 + r; R > 0 -> position p is raw row p mod R
+hipError_t launch_mqa(int dt, int B, int Tq, int H, int d, int N, int m, int k, int W, QPos q_pos0, float scale,
                       const void *q, const void *entries, int64_t e_bs, const int32_t *idx, const void *raw,
-                      int64_t raw_bs, int64_t raw_pos0, float *out, float *lse, float *ws, int n_splits,
-                      int tiles_per_split, hipStream_t st);
+                      int64_t raw_bs, int64_t raw_pos0, int64_t raw_ring, float *out, float *lse, float *ws,
+                      int n_splits, int tiles_per_split, hipStream_t st);
 
 }  // namespace csa

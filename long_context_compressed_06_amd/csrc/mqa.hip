@@ -38,6 +38,8 @@ namespace csa {
 struct MqaArgs {
     int Tq, H, N, m, k, W, n_splits, tiles_per_split;
     int64_t q_pos0, raw_pos0, e_bs, raw_bs;
+    const int64_t *pos;  // optional: sequence b's query position (ragged batches, Tq = 1)
+    int64_t raw_ring;    // 0: raw rows are positions raw_pos0 ..; R: position p is ring row p mod R
     float scale;
     const void *q, *entries, *raw;
     const int32_t *idx;
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(kMqaThreads) void k_mqa(const MqaArgs a) {
     const int hg = wv % NHG, dh = wv / NHG;  // head group, half of d
     const int64_t row = blockIdx.x / a.n_splits;
     const int split = blockIdx.x % a.n_splits;
-    const int64_t b = row / a.Tq, t = a.q_pos0 + row % a.Tq;
+    const int64_t b = row / a.Tq, t = (a.pos ? a.pos[b] : a.q_pos0) + row % a.Tq;
     const int64_t nv = n_visible(t, a.m, a.N);
     const int64_t n_slots = a.k > 0 ? a.k : nv;
     const int64_t w0 = t - a.W + 1 > 0 ? t - a.W + 1 : 0;
@@ -183,7 +185,8 @@ __global__ __launch_bounds__(kMqaThreads) void k_mqa(const MqaArgs a) {
                 const int64_t j = a.k > 0 ? (int64_t)a.idx[row * a.k + r] : r;
                 if (j >= 0 && j < nv) src = ent_b + j * D;
             } else if (r < n_rows) {
-                src = raw_b + (w0 + (r - n_slots) - a.raw_pos0) * D;
+                const int64_t p = w0 + (r - n_slots);
+                src = raw_b + (a.raw_ring ? p % a.raw_ring : p - a.raw_pos0) * D;
             }
             rtab[i] = src;
         }
@@ -519,15 +522,15 @@ static hipError_t launch_mqa_dt(int d, const MqaArgs &a, int64_t rows, hipStream
     }
 }
 
-hipError_t launch_mqa(int dt, int B, int Tq, int H, int d, int N, int m, int k, int W, int64_t q_pos0, float scale,
+hipError_t launch_mqa(int dt, int B, int Tq, int H, int d, int N, int m, int k, int W, QPos q_pos0, float scale,
                       const void *q, const void *entries, int64_t e_bs, const int32_t *idx, const void *raw,
-                      int64_t raw_bs, int64_t raw_pos0, float *out, float *lse, float *ws, int n_splits,
-                      int tiles_per_split, hipStream_t st) {
+                      int64_t raw_bs, int64_t raw_pos0, int64_t raw_ring, float *out, float *lse, float *ws,
+                      int n_splits, int tiles_per_split, hipStream_t st) {
     const int64_t rows = (int64_t)B * Tq;
     MqaArgs a;
     a.Tq = Tq; a.H = H; a.N = N; a.m = m; a.k = k; a.W = W;
     a.n_splits = n_splits; a.tiles_per_split = tiles_per_split;
-    a.q_pos0 = q_pos0; a.raw_pos0 = raw_pos0; a.e_bs = e_bs; a.raw_bs = raw_bs; a.scale = scale;
+    a.q_pos0 = q_pos0.q_pos0; a.pos = q_pos0.pos; a.raw_ring = raw_ring; a.raw_pos0 = raw_pos0; a.e_bs = e_bs; a.raw_bs = raw_bs; a.scale = scale;
     a.q = q; a.entries = entries; a.raw = raw; a.idx = idx; a.out = out; a.lse = lse;
     a.part_o = ws;
     a.part_ml = ws ? ws + rows * n_splits * H * (int64_t)d : nullptr;

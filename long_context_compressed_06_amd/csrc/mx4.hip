@@ -130,7 +130,7 @@ __device__ __forceinline__ float mx4_sum_lane_groups(float x) {
 __device__ __forceinline__ float mx4_relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 template <typename T, int DI, int MB>
-__global__ __launch_bounds__(256) void k_index_mx4(int Tq, int N, int HI, int m, int64_t q_pos0, int64_t n_items,
+__global__ __launch_bounds__(256) void k_index_mx4(int Tq, int N, int HI, int m, QPos q_pos0, int64_t n_items,
                                                    int chunks_per_row, const T *__restrict__ qI,
                                                    const float *__restrict__ w,
                                                    const uint8_t *__restrict__ kc, const uint8_t *__restrict__ ks,
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) void k_index_mx4(int Tq, int N, int HI, int m,
     const int64_t row = item / chunks_per_row;
     const int chunk = (int)(item % chunks_per_row);
     const int64_t b = row / Tq, ti = row % Tq;
-    const int64_t nv = n_visible(q_pos0 + ti, m, N);
+    const int64_t nv = n_visible(q_pos0.at(b, ti), m, N);
     const int g = lane >> 4, c = lane & 15;
     const bool kon = g < KB;  // lanes that hold a K block (d_I < 128 leaves the rest zero)
 
@@ -283,7 +283,7 @@ __device__ __forceinline__ void lds_dma4_nt_mx4(uint32_t lds_addr, const void *s
 }
 
 template <typename T, int MB>
-__global__ __launch_bounds__(kMx4Waves * 64) void k_index_mx4_dma(int Tq, int N, int HI, int m, int64_t q_pos0,
+__global__ __launch_bounds__(kMx4Waves * 64) void k_index_mx4_dma(int Tq, int N, int HI, int m, QPos q_pos0,
                                                                  int blocks_per_row, const T *__restrict__ qI,
                                                                  const float *__restrict__ w,
                                                                  const uint8_t *__restrict__ kc,
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(kMx4Waves * 64) void k_index_mx4_dma(int Tq, int N,
     const int64_t row = blockIdx.x / blocks_per_row;
     const int part = blockIdx.x % blocks_per_row;
     const int64_t b = row / Tq, ti = row % Tq;
-    const int64_t nv = n_visible(q_pos0 + ti, m, N);
+    const int64_t nv = n_visible(q_pos0.at(b, ti), m, N);
     const int wpr = blocks_per_row * kMx4Waves;
     const int gw = part * kMx4Waves + wv;
     const int tiles = (N + 15) / 16;
@@ -424,7 +424,7 @@ __global__ __launch_bounds__(kMx4Waves * 64) void k_index_mx4_dma(int Tq, int N,
 }
 
 template <typename T, int MB>
-static hipError_t launch_mx4_dma(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const void *qI, const float *w,
+static hipError_t launch_mx4_dma(int B, int Tq, int N, int HI, int m, QPos q_pos0, const void *qI, const float *w,
                                  const uint8_t *kc, const uint8_t *ks, int64_t k_bs, float *scores, int64_t s_stride,
                                  float *scores2, uint32_t *hist, hipStream_t st) {
     static const hipError_t attr = hipFuncSetAttribute((const void *)k_index_mx4_dma<T, MB>,
@@ -455,7 +455,7 @@ hipError_t launch_mx4_quantize(int dt, int64_t n_blocks, const void *x, uint8_t 
 }
 
 template <typename T, int DI, int MB>
-static hipError_t launch_mx4_t(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const void *qI, const float *w,
+static hipError_t launch_mx4_t(int B, int Tq, int N, int HI, int m, QPos q_pos0, const void *qI, const float *w,
                                const uint8_t *kc, const uint8_t *ks, int64_t k_bs, float *scores, int64_t s_stride,
                                float *scores2, uint32_t *hist, hipStream_t st) {
     const int64_t rows = (int64_t)B * Tq;
@@ -472,7 +472,7 @@ static hipError_t launch_mx4_t(int B, int Tq, int N, int HI, int m, int64_t q_po
 }
 
 template <typename T, int DI>
-static hipError_t launch_mx4_di(int B, int Tq, int N, int HI, int m, int64_t q_pos0, const void *qI, const float *w,
+static hipError_t launch_mx4_di(int B, int Tq, int N, int HI, int m, QPos q_pos0, const void *qI, const float *w,
                                 const uint8_t *kc, const uint8_t *ks, int64_t k_bs, float *scores, int64_t s_stride,
                                 float *scores2, uint32_t *hist, hipStream_t st) {
     if (HI <= 16)
@@ -485,7 +485,7 @@ static hipError_t launch_mx4_di(int B, int Tq, int N, int HI, int m, int64_t q_p
 }
 
 template <typename T>
-static hipError_t launch_mx4_dt(int B, int Tq, int N, int HI, int dI, int m, int64_t q_pos0, const void *qI,
+static hipError_t launch_mx4_dt(int B, int Tq, int N, int HI, int dI, int m, QPos q_pos0, const void *qI,
                                 const float *w, const uint8_t *kc, const uint8_t *ks, int64_t k_bs, float *scores,
                                 int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
     if (dI == 128 && ((uintptr_t)ks % 4) == 0) {  // (scale rows move as dwords)
@@ -511,7 +511,7 @@ static hipError_t launch_mx4_dt(int B, int Tq, int N, int HI, int dI, int m, int
     }
 }
 
-hipError_t launch_index_mx4(int dt, int B, int Tq, int N, int HI, int dI, int m, int64_t q_pos0, const void *qI,
+hipError_t launch_index_mx4(int dt, int B, int Tq, int N, int HI, int dI, int m, QPos q_pos0, const void *qI,
                             const float *w, const uint8_t *kc, const uint8_t *ks, int64_t k_bs, float *scores,
                             int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
     if (dt == 0)

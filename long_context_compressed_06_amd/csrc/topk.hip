@@ -214,7 +214,7 @@ __device__ void select_items(const IdxKey *items, int M, int k, Digit d, int32_t
 // from one exchange of per-wave counts, in-run offsets from ballots) and
 // resolved there.
 template <int KPL>
-__global__ __launch_bounds__(kNT) void k_topk_compact(int Tq, int N, int m, int k, int64_t q_pos0,
+__global__ __launch_bounds__(kNT) void k_topk_compact(int Tq, int N, int m, int k, QPos q_pos0,
                                                       const float *__restrict__ scores,
                                                       const uint32_t *__restrict__ ghist, int32_t *__restrict__ out) {
     extern __shared__ IdxKey items[];  // [kTopkFinalItems]
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(kNT) void k_topk_compact(int Tq, int N, int m, int 
     constexpr int F4 = KPL / 4;        // 16-byte vectors per lane
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int64_t row = blockIdx.x;
-    const int64_t nv = n_visible(q_pos0 + row % Tq, m, N);
+    const int64_t nv = n_visible(q_pos0.at(row / Tq, row % Tq), m, N);
     int32_t *orow = out + row * k;
     if (trivial_row(nv, k, orow)) return;
     const int stride = (int)topk_score_stride(N);
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(kNT) void k_topk_compact(int Tq, int N, int m, int 
 // pairs arrive in index order), resolves the candidates and writes the kept
 // indices.  (A kernel boundary separates the two: on this multi-die GPU a
 // device-scope fence inside one kernel costs more.)
-__global__ __launch_bounds__(kFT) void k_topk_filter(int Tq, int N, int m, int k, int64_t q_pos0, int nblk,
+__global__ __launch_bounds__(kFT) void k_topk_filter(int Tq, int N, int m, int k, QPos q_pos0, int nblk,
                                                      const float *__restrict__ scores,
                                                      const uint32_t *__restrict__ ghist, IdxKey *__restrict__ seg,
                                                      int32_t *__restrict__ counts) {
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(kFT) void k_topk_filter(int Tq, int N, int m, int k
     __shared__ Digit shd;
     const int64_t row = blockIdx.x / nblk;
     const int blk = blockIdx.x % nblk;
-    const int64_t nv = n_visible(q_pos0 + row % Tq, m, N);
+    const int64_t nv = n_visible(q_pos0.at(row / Tq, row % Tq), m, N);
     if (nv <= k) return;
     const int64_t stride = topk_score_stride(N);
     const float *srow = scores + row * stride;
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(kFT) void k_topk_filter(int Tq, int N, int m, int k
     if (threadIdx.x == 0) counts[row * nblk + blk] = total;
 }
 
-__global__ __launch_bounds__(kNT) void k_topk_final(int Tq, int N, int m, int k, int64_t q_pos0, int nblk,
+__global__ __launch_bounds__(kNT) void k_topk_final(int Tq, int N, int m, int k, QPos q_pos0, int nblk,
                                                     const float *__restrict__ scores,
                                                     const uint32_t *__restrict__ ghist,
                                                     const IdxKey *__restrict__ seg,
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(kNT) void k_topk_final(int Tq, int N, int m, int k,
     __shared__ int sh[2 * kNT / 64];
     __shared__ Digit shd;
     const int64_t row = blockIdx.x;
-    const int64_t nv = n_visible(q_pos0 + row % Tq, m, N);
+    const int64_t nv = n_visible(q_pos0.at(row / Tq, row % Tq), m, N);
     int32_t *orow = out + row * k;
     if (trivial_row(nv, k, orow)) return;
     // the segment sizes are fetched alongside the histogram
@@ -424,7 +424,7 @@ hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t st) {
 }
 
 template <int KPL>
-static hipError_t launch_compact(int64_t rows, int Tq, int N, int m, int k, int64_t q_pos0, const float *scores,
+static hipError_t launch_compact(int64_t rows, int Tq, int N, int m, int k, QPos q_pos0, const float *scores,
                                  const uint32_t *hist, int32_t *out, hipStream_t st) {
     static_assert(KPL * kNT <= kTopkCompactMax, "row longer than the one-pass limit");
     const size_t lds = (size_t)kTopkFinalItems * sizeof(IdxKey);
@@ -436,7 +436,7 @@ static hipError_t launch_compact(int64_t rows, int Tq, int N, int m, int k, int6
     return hipGetLastError();
 }
 
-hipError_t launch_topk(int B, int Tq, int N, int m, int k, int64_t q_pos0, const float *scores, void *scratch,
+hipError_t launch_topk(int B, int Tq, int N, int m, int k, QPos q_pos0, const float *scores, void *scratch,
                        int32_t *out, hipStream_t st) {
     const int64_t rows = (int64_t)B * Tq;
     const TopkPlan p = topk_plan(rows, N);

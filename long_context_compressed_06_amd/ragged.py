@@ -1,0 +1,120 @@
+"""Ragged decode: one attention layer's cache for B sequences at different lengths.
+
+DeepSeek-V4 overview page, section 2.2 (CSA) and 2.3 (HCA), in the serving
+form: every sequence decodes one token per step, each at its own position.
+The positions live in device memory (``pos``, int64 [B]: the position the
+next token of each sequence takes) and every kernel of the step reads them,
+so a whole decode step is one fixed sequence of launches: it can be captured
+in a HIP graph once and replayed for every later token, the positions
+advancing on the GPU.
+
+A step (new token of sequence b at position t_b = pos[b]):
+  1. one batched append: the raw row and logit into the mirrored rings at
+     t_b mod R, and -- for the sequences whose token completes a group -- the
+     group's index key into the key cache (given per token; only the
+     completing token's key is kept, quantised first when the indexer runs
+     on FP4);
+  2. ragged compression: those sequences' groups pooled out of the rings;
+  3. ragged index + top-k (CSA) over each sequence's visible entries;
+  4. ragged attention (selected or all visible entries, window from the ring);
+  5. pos += 1.
+Ring of R = max(W, m) positions: the window of the newest token and the
+tokens of the group it completes.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (csa_append_rows, csa_append_rows_multi, csa_mx4_quantize, csa_positions_advance,
+               csa_ragged_compress, csa_ragged_index_topk, csa_ragged_index_topk_mx4, csa_ragged_sparse_mqa,
+               hca_ragged_dense_mqa, index_topk_workspace_bytes, mqa_workspace_bytes)
+
+
+class RaggedLayer:
+    def __init__(self, *, mode: str, B: int, H: int, d: int, m: int, W: int, capacity: int, dtype=torch.bfloat16,
+                 k: int = 0, HI: int = 0, dI: int = 0, index_fmt: str = "elem", scale: float | None = None,
+                 device="cuda"):
+        assert mode in ("csa", "hca") and index_fmt in ("elem", "mx4")
+        if mode == "csa" and (k < 1 or HI < 1 or dI < 1):
+            raise ValueError("CSA needs k, HI and dI")
+        self.mode, self.B, self.H, self.d, self.m, self.W = mode, B, H, d, m, W
+        self.k, self.HI, self.dI, self.index_fmt, self.dtype = k, HI, dI, index_fmt, dtype
+        self.scale = (1.0 / d ** 0.5) if scale is None else scale
+        self.R = max(W, m, 1)
+        self.cap_e = max(1, capacity // m)
+        self.pos = torch.zeros((B,), dtype=torch.int64, device=device)
+        self.raw_ring = torch.zeros((B, 2 * self.R, d), dtype=dtype, device=device)
+        self.logit_ring = torch.zeros((B, 2 * self.R, 1), dtype=torch.float32, device=device)
+        self.entries = torch.zeros((B, self.cap_e, d), dtype=dtype, device=device)
+        if mode == "csa":
+            if index_fmt == "mx4":
+                self.k_codes = torch.zeros((B, self.cap_e, dI // 2), dtype=torch.uint8, device=device)
+                self.k_scales = torch.zeros((B, self.cap_e, dI // 32), dtype=torch.uint8, device=device)
+                self._codes = torch.empty((B, 1, dI // 2), dtype=torch.uint8, device=device)
+                self._scales = torch.empty((B, 1, dI // 32), dtype=torch.uint8, device=device)
+            else:
+                self.k_idx = torch.zeros((B, self.cap_e, dI), dtype=dtype, device=device)
+            nb = index_topk_workspace_bytes(B, 1, self.cap_e, HI, k)
+            self.idx_ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=device)
+            self.topk_idx = torch.empty((B, 1, k), dtype=torch.int32, device=device)
+        rows_max = (k if mode == "csa" else self.cap_e) + W
+        nb = mqa_workspace_bytes(B, 1, H, d, rows_max)
+        self.mqa_ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=device)
+        self.out = torch.empty((B, 1, H, d), dtype=torch.float32, device=device)
+        self.lse = torch.empty((B, 1, H), dtype=torch.float32, device=device)
+
+    def seed(self, b: int, pos_b: int, raw_tail: torch.Tensor, logits_tail: torch.Tensor,
+             entries: torch.Tensor | None = None, k_idx: torch.Tensor | None = None):
+        """Put sequence b's state in place: it has consumed positions 0 .. pos_b-1; raw_tail [L, d] and
+        logits_tail [L] are its last L = min(R, pos_b) tokens; entries [pos_b//m, d] and (CSA) their index
+        keys k_idx [pos_b//m, dI] are its cache."""
+        L = min(self.R, pos_b)
+        n_e = pos_b // self.m
+        if raw_tail.shape[0] != L or logits_tail.shape[0] != L:
+            raise ValueError(f"the ring holds the last {L} tokens")
+        if n_e > self.cap_e:
+            raise ValueError("entry capacity exceeded")
+        if L:
+            csa_append_rows(raw_tail[None], self.raw_ring[b:b + 1], pos_b - L, ring=self.R)
+            csa_append_rows(logits_tail.reshape(1, L, 1), self.logit_ring[b:b + 1], pos_b - L, ring=self.R)
+        if n_e:
+            self.entries[b, :n_e] = entries
+            if self.mode == "csa":
+                if self.index_fmt == "mx4":
+                    c, s = csa_mx4_quantize(k_idx.contiguous())
+                    self.k_codes[b, :n_e], self.k_scales[b, :n_e] = c, s
+                else:
+                    self.k_idx[b, :n_e] = k_idx
+        self.pos[b] = pos_b
+
+    def step(self, raw: torch.Tensor, logits: torch.Tensor, q: torch.Tensor, k_idx_tok: torch.Tensor | None = None,
+             q_idx: torch.Tensor | None = None, w_idx: torch.Tensor | None = None):
+        """One token per sequence: raw [B, 1, d], logits [B, 1] f32, q [B, 1, H, d] (contiguous); CSA also
+        k_idx_tok [B, 1, dI] (the index key of the group this token completes; read only for the sequences
+        whose token completes one), q_idx [B, 1, HI, dI], w_idx [B, 1, HI].  Writes self.out, self.lse
+        (and self.topk_idx) and advances self.pos.  Fixed launches: capturable in a HIP graph."""
+        B = self.B
+        jobs = [(raw, self.raw_ring, 0, self.R, self.pos), (logits.reshape(B, 1, 1), self.logit_ring, 0, self.R, self.pos)]
+        if self.mode == "csa":
+            if self.index_fmt == "mx4":
+                csa_mx4_quantize(k_idx_tok, codes=self._codes, scales=self._scales)
+                jobs += [(self._codes, self.k_codes, 0, 0, self.pos, self.m),
+                         (self._scales, self.k_scales, 0, 0, self.pos, self.m)]
+            else:
+                jobs.append((k_idx_tok, self.k_idx, 0, 0, self.pos, self.m))
+        csa_append_rows_multi(jobs)
+        csa_ragged_compress(self.raw_ring, self.logit_ring[..., 0], self.R, self.m, self.pos, self.entries)
+        if self.mode == "csa":
+            if self.index_fmt == "mx4":
+                csa_ragged_index_topk_mx4(q_idx, w_idx, self.k_codes, self.k_scales, self.cap_e, self.m, self.k,
+                                          self.pos, topk_idx=self.topk_idx, workspace=self.idx_ws)
+            else:
+                csa_ragged_index_topk(q_idx, w_idx, self.k_idx, self.cap_e, self.m, self.k, self.pos,
+                                      topk_idx=self.topk_idx, workspace=self.idx_ws)
+            csa_ragged_sparse_mqa(q, self.entries, self.topk_idx, self.raw_ring, self.R, self.cap_e, self.m, self.W,
+                                  self.pos, scale=self.scale, out=self.out, lse=self.lse, workspace=self.mqa_ws)
+        else:
+            hca_ragged_dense_mqa(q, self.entries, self.raw_ring, self.R, self.cap_e, self.m, self.W, self.pos,
+                                 scale=self.scale, out=self.out, lse=self.lse, workspace=self.mqa_ws)
+        csa_positions_advance(self.pos, 1)
+        return self.out

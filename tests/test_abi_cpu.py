@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
     import long_context_compressed_06_amd as csa
 
     names = header_functions()
-    assert len(names) == 15, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(L, n), n
     assert sorted(csa.EXPORTS) == names
@@ -221,3 +221,42 @@ def test_append_rows_multi_rejects_bad_arguments(L):
     assert call(job(), job(rows=P + 0x100000, dst=P + 0x300000)) == -1         # job 1 reads what job 0 writes
     assert call(job(ring=3)) == -1
     assert call(job(n=0, rows=None, dst=None), job(B=0, rows=None, dst=None)) == 0
+
+
+def test_ragged_calls_reject_bad_arguments(L):
+    import long_context_compressed_06_amd as csa
+
+    assert L.csa_positions_advance(-1, P, 1, None) == -1
+    assert L.csa_positions_advance(2, None, 1, None) == -1
+    assert L.csa_positions_advance(2, P + 4, 1, None) == -3
+    assert L.csa_positions_advance(0, None, 1, None) == 0
+    rc = L.csa_ragged_compress
+    args = dict(dt=1, B=2, m=4, d=128, pos=P, raw=P + 0x10000, rbs=2 * 16 * 128, lg=P + 0x100000, lbs=32, ring=16,
+                out=P + 0x200000, obs=64 * 128, orows=64)
+
+    def comp(**kw):
+        a = dict(args, **kw)
+        return rc(a["dt"], a["B"], a["m"], a["d"], a["pos"], a["raw"], a["rbs"], a["lg"], a["lbs"], a["ring"],
+                  a["out"], a["obs"], a["orows"], None)
+
+    assert comp(m=0) == -6 and comp(d=100) == -6
+    assert comp(ring=3) == -1                 # a group does not fit the ring
+    assert comp(pos=None) == -1
+    assert comp(rbs=16 * 128) == -1           # rings hold 2*ring rows
+    assert comp(pos=P + 4) == -3
+    assert comp(out=P + 0x10000 + 256) == -1  # out overlaps the raw ring
+    assert comp(B=0, pos=None) == 0
+    ws = csa.index_topk_workspace_bytes(2, 1, 256, 64, 64)
+    ri = lambda pos=P, **kw: L.csa_ragged_index_topk(1, 2, 256, 64, 128, 4, kw.get("k", 64), pos, P + 0x10000,
+                                                     P + 0x40000, P + 0x80000, 256 * 128, P + 0x200000, None,
+                                                     P + 0x300000, kw.get("wsb", ws), None)
+    assert ri(pos=None) == -1
+    assert ri(pos=P + 4) == -3
+    assert ri(k=0) == -6
+    assert ri(wsb=ws - 1) == -4
+    rm = lambda **kw: L.csa_ragged_sparse_mqa(1, 2, 64, 512, 1000, 4, 64, kw.get("W", 128), kw.get("pos", P), 0.04,
+                                              P + 0x10000, P + 0x100000, 1000 * 512, P + 0x2000000, P + 0x3000000,
+                                              2 * 128 * 512, kw.get("ring", 128), P + 0x4000000, None, None, 0, None)
+    assert rm(pos=None) == -1
+    assert rm(ring=0) == -1
+    assert rm(W=129) == -1                    # the ring cannot hold the window

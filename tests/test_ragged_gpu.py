@@ -1,0 +1,219 @@
+"""GPU parity of ragged decode: B sequences at different lengths, one token each per step.
+
+Each sequence's cache is put in place at its own position (entries and index keys
+drawn, the ring holding its last raw tokens; one sequence starts empty at
+position 0), then every sequence decodes S tokens together.  Groups complete at
+different steps for different sequences; the kernels read each sequence's
+position from device memory.  The oracle is run per sequence and step: the
+cached entries as given, each new group pooled from the raw stream when its m-th
+token arrives, its index key appended then, index + top-k + attention for the
+token at its own position.  Rules as in test_parity_gpu.  A second test captures
+one step in a HIP graph and replays it for every later token (inputs copied into
+the captured buffers between replays): every replay must equal an eager run.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from helpers import assert_close, check_topk, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def csa():
+    import long_context_compressed_06_amd as m
+
+    m.lib()
+    assert torch.cuda.is_available(), "no GPU visible"
+    return m
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@dataclasses.dataclass(frozen=True)
+class Case:
+    name: str
+    mode: str
+    dtype: str
+    positions: tuple
+    steps: int
+    m: int
+    d: int
+    H: int
+    W: int
+    k: int = 0
+    HI: int = 0
+    dI: int = 0
+    index_fmt: str = "elem"
+    seed: int = 0
+
+
+CASES = [
+    Case("csa_ragged_bf16", "csa", "bf16", (0, 37, 130, 401), 9, 4, 128, 8, 16, k=32, HI=8, dI=64, seed=96000),
+    Case("csa_ragged_f32", "csa", "f32", (3, 50), 6, 4, 64, 4, 8, k=16, HI=4, dI=32, seed=96100),
+    Case("csa_ragged_bf16_fp4_indexer", "csa", "bf16", (5, 66, 203), 7, 4, 128, 8, 16, k=24, HI=16, dI=128,
+         index_fmt="mx4", seed=96200),
+    Case("csa_ragged_bf16_d512", "csa", "bf16", (700, 1029), 5, 4, 512, 16, 128, k=64, HI=64, dI=128, seed=96300),
+    Case("hca_ragged_bf16", "hca", "bf16", (126, 250, 509), 6, 128, 128, 8, 128, seed=96400),
+]
+
+
+def draw(c: Case):
+    g = torch.Generator().manual_seed(c.seed)
+    tdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+    rn = lambda *shape, std=1.0: torch.randn(shape, generator=g) * std
+    R = max(c.W, c.m)
+    seqs = []
+    for p in c.positions:
+        L, n_e = min(R, p), p // c.m
+        s = {"tail": rn(L, c.d).to(tdt), "tail_logits": rn(L), "entries": rn(n_e, c.d).to(tdt)}
+        if c.mode == "csa":
+            s["k_idx"] = rn(n_e, c.dI, std=c.dI ** -0.5).to(tdt)
+        seqs.append(s)
+    B, S = len(c.positions), c.steps
+    new = {"raw": rn(B, S, c.d).to(tdt), "logits": rn(B, S), "q": rn(B, S, c.H, c.d).to(tdt)}
+    if c.mode == "csa":
+        new["q_idx"] = rn(B, S, c.HI, c.dI, std=c.dI ** -0.5).to(tdt)
+        new["w_idx"] = torch.rand((B, S, c.HI), generator=g)
+        new["k_tok"] = rn(B, S, c.dI, std=c.dI ** -0.5).to(tdt)
+    return seqs, new
+
+
+def make_layer(csa, c: Case, seqs):
+    B = len(c.positions)
+    tdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+    cap = max(c.positions) + c.steps + c.m
+    layer = csa.RaggedLayer(mode=c.mode, B=B, H=c.H, d=c.d, m=c.m, W=c.W, capacity=cap, dtype=tdt, k=c.k, HI=c.HI,
+                            dI=c.dI, index_fmt=c.index_fmt, scale=c.d ** -0.5)
+    for b, (p, s) in enumerate(zip(c.positions, seqs)):
+        layer.seed(b, p, s["tail"].cuda(), s["tail_logits"].cuda(), s["entries"].cuda(),
+                   s["k_idx"].cuda() if c.mode == "csa" else None)
+    return layer
+
+
+def step_inputs(c, new, j):
+    x = {"raw": new["raw"][:, j:j + 1].contiguous().cuda(), "logits": new["logits"][:, j:j + 1].contiguous().cuda(),
+         "q": new["q"][:, j:j + 1].contiguous().cuda()}
+    if c.mode == "csa":
+        x.update(k_idx_tok=new["k_tok"][:, j:j + 1].contiguous().cuda(),
+                 q_idx=new["q_idx"][:, j:j + 1].contiguous().cuda(), w_idx=new["w_idx"][:, j:j + 1].contiguous().cuda())
+    return x
+
+
+def oracle_sequence_steps(c: Case, b: int, s: dict, new: dict):
+    """Oracle outputs of sequence b for each of the S steps (host arrays)."""
+    p, m, S = c.positions[b], c.m, c.steps
+    f = lambda t: t.float().numpy()
+    L = s["tail"].shape[0]
+    raw = np.concatenate([f(s["tail"]), f(new["raw"][b])], axis=0)[None]          # positions p-L .. p+S-1
+    logits = np.concatenate([f(s["tail_logits"]), f(new["logits"][b])], axis=0)[None]
+    raw0 = p - L
+    ent = [f(s["entries"])]
+    keys = [f(s["k_idx"])] if c.mode == "csa" else []
+    e_new = []
+    res = []
+    for j in range(S):
+        t = p + j
+        if (t + 1) % m == 0:  # group g completes: pooled from the raw stream
+            g0 = t + 1 - m
+            e = orc.compress(raw[:, g0 - raw0:g0 - raw0 + m], logits[:, g0 - raw0:g0 - raw0 + m], m)
+            e_new.append(e[0, 0])
+            ent.append(orc.round_bf16(e[0]) if c.dtype == "bf16" else e[0].astype(np.float32))
+            if c.mode == "csa":
+                keys.append(f(new["k_tok"][b, j:j + 1]))
+        E = np.concatenate(ent, axis=0)[None]
+        q = f(new["q"][b, j:j + 1])[None]
+        r = {}
+        if c.mode == "csa":
+            K = np.concatenate(keys, axis=0)[None]
+            qi = f(new["q_idx"][b, j:j + 1])[None]
+            if c.index_fmt == "mx4":
+                K = orc.mx4_dequantize(*orc.mx4_quantize(K))
+                qi = orc.mx4_dequantize(*orc.mx4_quantize(qi))
+            sc = orc.index_scores(qi, new["w_idx"][b, j:j + 1].numpy()[None], K, m, t)
+            idx = orc.topk(sc, c.k, m, t)
+            o, l = orc.sparse_mqa(q, E, idx, raw[:, :t + 1 - raw0], raw0, c.W, t, c.d ** -0.5)
+            r.update(scores=sc[0, 0], idx=idx[0, 0], nvis=(t + 1) // m)
+        else:
+            o, l = orc.dense_mqa(q, E, raw[:, :t + 1 - raw0], raw0, m, c.W, t, c.d ** -0.5)
+        r.update(out=o[0, 0], lse=l[0, 0])
+        res.append(r)
+    return res, (np.stack(e_new) if e_new else None)
+
+
+@pytest.mark.parametrize("c", CASES, ids=[c.name for c in CASES])
+def test_ragged_decode(csa, c):
+    say(c)
+    seqs, new = draw(c)
+    layer = make_layer(csa, c, seqs)
+    B, S = len(c.positions), c.steps
+    outs, lses, idxs = [], [], []
+    for j in range(S):
+        layer.step(**step_inputs(c, new, j))
+        outs.append(layer.out.clone())
+        lses.append(layer.lse.clone())
+        if c.mode == "csa":
+            idxs.append(layer.topk_idx.clone())
+    torch.cuda.synchronize()
+    assert to_np(layer.pos).tolist() == [p + S for p in c.positions]
+    for b in range(B):
+        ref, e_new = oracle_sequence_steps(c, b, seqs[b], new)
+        n0 = c.positions[b] // c.m
+        if e_new is not None:
+            assert_close(layer.entries[b, n0:n0 + e_new.shape[0]], e_new, c.dtype, f"seq {b} emitted entries")
+        go = np.stack([to_np(o[b, 0]) for o in outs])
+        gl = np.stack([to_np(x[b, 0]) for x in lses])
+        ro = np.stack([r["out"] for r in ref])
+        rl = np.stack([r["lse"] for r in ref])
+        if c.mode == "csa":
+            gi = np.stack([to_np(x[b, 0]) for x in idxs])
+            ri = np.stack([r["idx"] for r in ref])
+            N_max = max(len(r["scores"]) for r in ref)
+            sc = np.full((S, N_max), -np.inf)
+            for j, r in enumerate(ref):
+                sc[j, :len(r["scores"])] = r["scores"]
+            check_topk(gi, ri, sc, np.array([r["nvis"] for r in ref]), c.k, f"seq {b} topk")
+            same = np.all(gi == ri, axis=1)
+            assert same.mean() >= 0.75
+            assert_close(go[same], ro[same], c.dtype, f"seq {b} out")
+            assert_close(gl[same], rl[same], c.dtype, f"seq {b} lse", row_dims=1)
+        else:
+            assert_close(go, ro, c.dtype, f"seq {b} out")
+            assert_close(gl, rl, c.dtype, f"seq {b} lse", row_dims=1)
+
+
+def test_ragged_decode_graph_replay(csa):
+    """One captured decode step replayed for every token equals the eager steps exactly."""
+    c = CASES[0]
+    say(c, "graph replay")
+    seqs, new = draw(c)
+    eager = make_layer(csa, c, seqs)
+    graphed = make_layer(csa, c, seqs)
+    eager.step(**step_inputs(c, new, 0))  # (first launches outside the capture)
+    bufs = step_inputs(c, new, 0)
+    torch.cuda.synchronize()
+    # capture (the capture itself runs nothing); the graph advances graphed.pos on every replay
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        graphed.step(**bufs)
+    for j in range(c.steps):
+        x = step_inputs(c, new, j)
+        for kk, v in x.items():
+            bufs[kk].copy_(v)
+        g.replay()
+        if j > 0:
+            eager.step(**x)
+        torch.cuda.synchronize()
+        assert torch.equal(graphed.out, eager.out), j
+        assert torch.equal(graphed.lse, eager.lse), j
+        assert torch.equal(graphed.topk_idx, eager.topk_idx), j
+    assert torch.equal(graphed.pos, eager.pos)
+    assert torch.equal(graphed.entries, eager.entries) and torch.equal(graphed.k_idx, eager.k_idx)
