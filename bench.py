@@ -328,6 +328,66 @@ def bench_prefill(sq, reps, warmup):
     return {"ms_per_prefill": ms, "chunks": len(sched), "chunk": C}
 
 
+def ragged_bytes(rs) -> int:
+    """Algorithmic bytes of one stack step at the starting positions: per layer and sequence the visible
+    index keys (CSA), index query and weights, the attended rows (selected or all visible entries plus the
+    window), q, the fp32 output, the appended raw row and logit; one group's compression every m tokens."""
+    es = 2 if rs.dtype == "bf16" else 4
+    total = 0
+    for spec in rs.specs():
+        m = spec["m"]
+        for t in rs.lengths:
+            nv = (t + 1) // m
+            row = rs.H * rs.d * es + rs.H * rs.d * 4 + rs.d * es + 4
+            if spec["mode"] == "csa":
+                row += nv * spec["dI"] * es + spec["HI"] * spec["dI"] * es + spec["HI"] * 4
+                row += (min(spec["k"], nv) + rs.W) * rs.d * es + 2 * spec["k"] * 4
+                row += (m * 4 + rs.d * es + spec["dI"] * es) / m
+            else:
+                row += (nv + rs.W) * rs.d * es + (m * 4 + rs.d * es) / m
+            total += row
+    return int(total)
+
+
+def bench_ragged(rs, steps, warmup):
+    """Ragged decode through a stack of layers: one captured stack step replayed for every token, the
+    positions advancing on the GPU (groups are emitted whenever a sequence completes one)."""
+    import torch
+
+    import long_context_compressed_06_amd as csa
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(rs.seed_base + 11)
+    dt = torch.bfloat16 if rs.dtype == "bf16" else torch.float32
+    B = rs.B
+    cap = max(rs.lengths) + steps + warmup + 256
+    stack = csa.HybridStack(rs.specs(), B=B, H=rs.H, d=rs.d, W=rs.W, capacity=cap, dtype=dt)
+    pos = torch.tensor(rs.lengths, dtype=torch.int64, device="cuda")
+    inputs = []
+    for L in stack.layers:
+        for t in [L.entries] + ([L.k_idx] if L.mode == "csa" else []):
+            for b in range(B):  # (per sequence: bounded temporaries)
+                t[b].copy_(torch.randn(t[b].shape, generator=g, device="cuda") * (t.shape[2] ** -0.5 if t is not L.entries else 1.0))
+        L.raw_ring.copy_(torch.randn(L.raw_ring.shape, generator=g, device="cuda"))
+        L.logit_ring.copy_(torch.randn(L.logit_ring.shape, generator=g, device="cuda"))
+        L.pos.copy_(pos)
+        x = {"raw": torch.randn((B, 1, rs.d), generator=g, device="cuda").to(dt),
+             "logits": torch.randn((B, 1), generator=g, device="cuda"),
+             "q": torch.randn((B, 1, rs.H, rs.d), generator=g, device="cuda").to(dt)}
+        if L.mode == "csa":
+            x.update(k_idx_tok=(torch.randn((B, 1, L.dI), generator=g, device="cuda") * L.dI ** -0.5).to(dt),
+                     q_idx=(torch.randn((B, 1, L.HI, L.dI), generator=g, device="cuda") * L.dI ** -0.5).to(dt),
+                     w_idx=torch.rand((B, 1, L.HI), generator=g, device="cuda"))
+        inputs.append(x)
+    stack.step(inputs)  # (first launches outside the capture)
+    torch.cuda.synchronize()
+    graph = capture(lambda: stack.step(inputs))
+    ms = time_graphs([graph], steps, warmup)
+    del graph, stack, inputs
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms}
+
+
 def cpu_baseline(wl, min_seconds=10.0, max_reps=5):
     """The oracle, as it stands, on the same workload's inputs (host copies)."""
     import torch
@@ -361,10 +421,11 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2", help="c2 (default), c3 or c5")
-    ap.add_argument("--also", default="c3,c5,c2x,c5x,l2,l2x,l2c,p1",
+    ap.add_argument("--also", default="c3,c5,c2x,c5x,l2,l2x,l2c,p1,r1,r2",
                     help="secondary workloads ('' for none); c2x/c5x: FP4 (MXFP4) indexer operands; "
                          "l2/l2x/l2c: decode loops with cache maintenance (l2c: per-channel pooling, pooled "
-                         "index keys); p1: a whole chunked prefill from 0")
+                         "index keys); p1: a whole chunked prefill from 0; r1/r2: ragged decode (lengths "
+                         "96K..158K) through one CSA layer / a CSA + HCA stack, one graph per token")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for the HBM byte counters)")
@@ -376,7 +437,7 @@ def main():
 
     import torch
 
-    from workloads import CONFIGS, LOOPS, PREFILLS
+    from workloads import CONFIGS, LOOPS, PREFILLS, RAGGED
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl = CONFIGS[args.workload]
@@ -411,6 +472,19 @@ def main():
                             "bytes_per_launch": ab["indexer"], "avg_launch_us": r["indexer_ms"] * 1e3}
     also = {}
     for name in [a for a in args.also.split(",") if a and a != args.workload]:
+        if name in RAGGED:
+            rs = RAGGED[name]
+            log(f"[bench] also {rs.name}")
+            r2 = bench_ragged(rs, max(16, args.steps), max(4, args.warmup // 2))
+            b2 = ragged_bytes(rs)
+            also[rs.name] = {"tokens_per_s": rs.B / (r2["ms_per_step"] * 1e-3), "ms_per_step": r2["ms_per_step"],
+                             "layers": "+".join(s["mode"] for s in rs.specs()),
+                             "step_hbm_frac": b2 / (r2["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                             "algorithmic_bytes": b2,
+                             "step": f"one token of each of {rs.B} sequences (lengths {min(rs.lengths)}.."
+                                     f"{max(rs.lengths)}) through every layer, one captured graph replayed per "
+                                     f"token, positions advancing on the GPU"}
+            continue
         if name in PREFILLS:
             sq = PREFILLS[name]
             log(f"[bench] also {sq}")

@@ -503,3 +503,4 @@ def hca_dense_mqa(q, entries, raw, N: int, m: int, W: int, q_pos0: int, raw_pos0
 from .step import AttentionStep  # noqa: E402  (uses the functions above)
 from .stream import StreamingLayer, chunk_plan, ring_size  # noqa: E402
 from .ragged import RaggedLayer  # noqa: E402
+from .hybrid import HybridStack, alternating  # noqa: E402

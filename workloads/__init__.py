@@ -252,3 +252,34 @@ PREFILLS = {
     "p1": Sequence("csa_prefill_stream_B1_ctx64K_chunk4096", "bf16", B=1, T=65536, m=4, d=512, H=64, W=128,
                    k=1024, HI=64, dI=128, chunks=(4096,) * 16, seed_base=7000),
 }
+
+
+# ragged decode for the benchmark: B sequences at different lengths, every
+# sequence one token per step through a stack of layers alternating CSA and HCA
+@dataclasses.dataclass(frozen=True)
+class RaggedStack:
+    name: str
+    B: int
+    lengths: tuple            # each sequence's position when timing starts
+    d: int
+    H: int
+    W: int
+    csa: tuple = (("m", 4), ("k", 1024), ("HI", 64), ("dI", 128))
+    hca: tuple = (("m", 128),)
+    n_layers: int = 2
+    dtype: str = "bf16"
+    seed_base: int = 0
+
+    def specs(self) -> list:
+        return [dict(dict(self.csa), mode="csa") if i % 2 == 0 else dict(dict(self.hca), mode="hca")
+                for i in range(self.n_layers)]
+
+
+RAGGED = {
+    # lengths 96K .. 158K in steps of 2K (mean ~127K), CSA then HCA
+    "r2": RaggedStack("hybrid_decode_ragged_B32_ctx96K-158K", B=32, lengths=tuple(98304 + 2048 * b for b in range(32)),
+                      d=512, H=64, W=128, seed_base=8000),
+    # the same batch through one CSA layer
+    "r1": RaggedStack("csa_decode_ragged_B32_ctx96K-158K", B=32, lengths=tuple(98304 + 2048 * b for b in range(32)),
+                      d=512, H=64, W=128, n_layers=1, seed_base=8100),
+}
