@@ -88,6 +88,50 @@ __device__ __forceinline__ int64_t n_visible(int64_t t, int m, int64_t N) {
     return n < N ? n : N;
 }
 
+// Ragged batches (one query per row, rows = B, row b at position pos[b]):
+// share the G workgroups of a launch among the rows in proportion to their
+// visible 16-entry tiles, every row getting at least one:
+//     parts_b = 1 + tiles_b * (G - B) / sum_j tiles_j      (G >= B)
+// and workgroup i serves row b with parts_{<b} <= i < parts_{<=b}.  Every
+// wavefront computes the same answer from pos (no barrier); false for the
+// workgroups left over by the rounding.
+__device__ __forceinline__ bool ragged_share(const int64_t *__restrict__ pos, int B, int m, int64_t N, int G,
+                                             int64_t *row, int *part, int *parts) {
+    const int lane = threadIdx.x & 63;
+    auto tiles_of = [&](int b) -> int64_t { return b < B ? (n_visible(pos[b], m, N) + 15) / 16 : 0; };
+    int64_t total = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {
+        int64_t t = tiles_of(b0 + lane);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o);
+        total += t;
+    }
+    const int64_t spare = G - B;
+    const int i = blockIdx.x;
+    int64_t base = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {
+        const int b = b0 + lane;
+        const int64_t pb = b < B ? 1 + (total > 0 ? tiles_of(b) * spare / total : 0) : 0;
+        int64_t incl = pb;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int64_t y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        const int64_t lo = base + incl - pb;
+        const uint64_t hit = __ballot(b < B && lo <= i && i < base + incl);
+        if (hit) {
+            const int src = __builtin_ctzll(hit);
+            *row = b0 + src;
+            *part = (int)(i - __shfl(lo, src));
+            *parts = (int)__shfl(pb, src);
+            return true;
+        }
+        base += __shfl(incl, 63);
+    }
+    return false;
+}
+
 // order-preserving map of a float score to uint32 (larger score, larger key;
 // -0 ranks with +0)
 __device__ __forceinline__ uint32_t order_key(float f) {

@@ -301,11 +301,14 @@ __global__ __launch_bounds__(kMx4Waves * 64) void k_index_mx4_dma(int Tq, int N,
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, c = lane & 15;
-    const int64_t row = blockIdx.x / blocks_per_row;
-    const int part = blockIdx.x % blocks_per_row;
+    int64_t row = blockIdx.x / blocks_per_row;
+    int part = blockIdx.x % blocks_per_row, parts = blocks_per_row;
+    if (q_pos0.pos && !ragged_share(q_pos0.pos, (int)(gridDim.x / blocks_per_row), m, N, gridDim.x, &row, &part,
+                                    &parts))
+        return;  // (ragged rows: workgroups shared by visible tiles; uniform per workgroup)
     const int64_t b = row / Tq, ti = row % Tq;
     const int64_t nv = n_visible(q_pos0.at(b, ti), m, N);
-    const int wpr = blocks_per_row * kMx4Waves;
+    const int wpr = parts * kMx4Waves;
     const int gw = part * kMx4Waves + wv;
     const int tiles = (N + 15) / 16;
     const int vtiles = (int)((nv + 15) / 16);

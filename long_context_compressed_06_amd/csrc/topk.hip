@@ -307,6 +307,10 @@ __global__ __launch_bounds__(kFT) void k_topk_filter(int Tq, int N, int m, int k
     const int blk = blockIdx.x % nblk;
     const int64_t nv = n_visible(q_pos0.at(row / Tq, row % Tq), m, N);
     if (nv <= k) return;
+    if ((int64_t)blk * kTopkFilterChunk >= nv) {  // a chunk past the visible entries holds no pair
+        if (threadIdx.x == 0) counts[row * nblk + blk] = 0;
+        return;
+    }
     const int64_t stride = topk_score_stride(N);
     const float *srow = scores + row * stride;
     const int64_t j0 = (int64_t)blk * kTopkFilterChunk + threadIdx.x * kFPT;
