@@ -141,7 +141,22 @@ def time_graphs(graphs, steps, warmup, multi=None, per_multi=1):
     return start.elapsed_time(end) / steps  # ms
 
 
-def bench_workload(wl, steps, warmup, with_kernel=True):
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
+
+
+def algorithmic_flops(wl) -> dict:
+    """Indexer 2*n_vis*H_I*d_I and attention 4*(min(k, n_vis) + window)*H*d FLOPs per query, summed."""
+    idx = att = 0
+    for ti in range(wl.Tq):
+        t = wl.q_pos0 + ti
+        nv = min(wl.N, (t + 1) // wl.m)
+        n_win = min(wl.W, t + 1)
+        idx += 2 * nv * wl.HI * wl.dI
+        att += 4 * ((min(wl.k, nv) if wl.mode == "csa" else nv) + n_win) * wl.H * wl.d
+    return {"indexer": idx * wl.B, "attention": att * wl.B}
+
+
+def bench_workload(wl, steps, warmup, with_kernel=True, with_mfma=False):
     import torch
 
     import long_context_compressed_06_amd as csa
@@ -174,6 +189,17 @@ def bench_workload(wl, steps, warmup, with_kernel=True):
         km = capture(lambda: [idx_call[i % R]() for i in range(8)])
         res["indexer_ms"] = time_graphs(kg, steps, warmup, km, 8)
         del sc, kg, km
+    if with_mfma and wl.mode == "csa" and wl.index_fmt == "elem":
+        # the two MFMA-bound kernels alone (prefill chunks), each timed from graphs over the replicas
+        sc = [torch.empty((wl.B, wl.Tq, wl.N), dtype=torch.float32, device="cuda") for _ in xs]
+        idx_call = [lambda x=x, o=o: csa.csa_index_scores(x["q_idx"], x["w_idx"], x["k_idx"], wl.N, wl.m,
+                                                          wl.q_pos0, scores=o) for x, o in zip(xs, sc)]
+        res["indexer_ms"] = time_graphs([capture(f) for f in idx_call], max(3, steps // 4), 2)
+        del sc
+        att_call = [lambda s=s, x=x: csa.csa_sparse_mqa(x["q"], x["entries"], s.topk_idx, x["raw"], wl.N, wl.m, wl.W,
+                                                        wl.q_pos0, wl.raw_pos0, scale=wl.scale, out=s.out, lse=s.lse,
+                                                        workspace=s.mqa_ws) for s, x in zip(steps_, xs)]
+        res["attention_ms"] = time_graphs([capture(f) for f in att_call], max(3, steps // 4), 2)
     del graphs, steps_, xs, x0
     torch.cuda.empty_cache()
     return res
@@ -388,6 +414,31 @@ def bench_ragged(rs, steps, warmup):
     return {"ms_per_step": ms}
 
 
+def stream_ceiling_gbs(fronts: int, reps=10) -> float:
+    """Measured streaming-read reference on the same GPU: csa_stream_read over 2 GiB (beyond the 256 MB
+    Infinity Cache) as `fronts` concurrent fronts, bytes read per second."""
+    import torch
+
+    import long_context_compressed_06_amd as csa
+
+    buf = torch.empty(1 << 31, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        csa.csa_stream_read(buf, fronts, sink)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        csa.csa_stream_read(buf, fronts, sink)
+    b.record()
+    b.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del buf, sink
+    torch.cuda.empty_cache()
+    return (1 << 31) / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(wl, min_seconds=10.0, max_reps=5):
     """The oracle, as it stands, on the same workload's inputs (host copies)."""
     import torch
@@ -421,8 +472,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2", help="c2 (default), c3 or c5")
-    ap.add_argument("--also", default="c3,c5,c2x,c5x,l2,l2x,l2c,p1,r1,r2",
-                    help="secondary workloads ('' for none); c2x/c5x: FP4 (MXFP4) indexer operands; "
+    ap.add_argument("--also", default="c3,c5,c4,c2x,c5x,l2,l2x,l2c,p1,r1,r2",
+                    help="secondary workloads ('' for none); c4: the 64K prefill chunk (tokens/s and the MFMA "
+                         "fractions of its indexer and attention); c2x/c5x: FP4 (MXFP4) indexer operands; "
                          "l2/l2x/l2c: decode loops with cache maintenance (l2c: per-channel pooling, pooled "
                          "index keys); p1: a whole chunked prefill from 0; r1/r2: ragged decode (lengths "
                          "96K..158K) through one CSA layer / a CSA + HCA stack, one graph per token")
@@ -467,9 +519,14 @@ def main():
     }
     if "indexer_ms" in r:
         ach = ab["indexer"] / (r["indexer_ms"] * 1e-3) / 1e9
+        c1, c32 = stream_ceiling_gbs(1), stream_ceiling_gbs(32)
         line["roofline"] = {"kernel": "k_index_dma (lightning indexer, bf16 keys)", "bound": "hbm", "achieved": ach,
                             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": indexer_traffic(),
-                            "bytes_per_launch": ab["indexer"], "avg_launch_us": r["indexer_ms"] * 1e3}
+                            "bytes_per_launch": ab["indexer"], "avg_launch_us": r["indexer_ms"] * 1e3,
+                            "measured_ceiling": {"what": "csa_stream_read of 2 GiB on the same GPU (the indexer's "
+                                                         "LDS-DMA load path), bytes read per second",
+                                                 "one_front_GBs": c1, "32_fronts_GBs": c32},
+                            "frac_of_measured_ceiling": ach / c32}
     also = {}
     for name in [a for a in args.also.split(",") if a and a != args.workload]:
         if name in RAGGED:
@@ -510,11 +567,20 @@ def main():
             continue
         w2 = CONFIGS[name]
         log(f"[bench] also {w2}")
-        r2 = bench_workload(w2, max(10, args.steps // 2), args.warmup, with_kernel=False)
+        prefill = w2.Tq > 1
+        r2 = bench_workload(w2, max(10, args.steps // 2) if not prefill else max(5, args.steps // 5), args.warmup,
+                            with_kernel=False, with_mfma=prefill)
         b2 = algorithmic_bytes(w2)["step"]
         also[w2.name] = {"tokens_per_s": w2.B * w2.Tq / (r2["ms_per_step"] * 1e-3), "ms_per_step": r2["ms_per_step"],
                          "step_hbm_frac": b2 / (r2["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                          "algorithmic_bytes": b2}
+        if "attention_ms" in r2:
+            fl = algorithmic_flops(w2)
+            for kern in ("indexer", "attention"):
+                tf = fl[kern] / (r2[kern + "_ms"] * 1e-3) / 1e12
+                also[w2.name][kern + "_mfma"] = {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
+                                                 "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
+                                                 "flops_per_launch": fl[kern], "avg_launch_ms": r2[kern + "_ms"]}
     if also:
         line["also"] = also
     if args.copy_calibration:

@@ -361,6 +361,18 @@ int hca_dense_mqa(int dt, int B, int Tq, int H, int d, int N, int m, int W,
                   float *out, float *lse,
                   void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * csa_stream_read -- measurement helper (not part of the method): reads
+ * `bytes` of `buf` as `fronts` contiguous fronts streamed at the same time,
+ * with the indexer's load path (1 KiB non-temporal LDS-DMA per instruction,
+ * 32 KiB in flight per wavefront, 1024 wavefronts), and XOR-folds one word
+ * per wavefront into sink[0..63] (uint32, caller-owned, read-modify-write).
+ * The lightning indexer streams one front per query; this is the reference
+ * its HBM rate is compared with.  fronts a divisor of 1024, bytes a multiple
+ * of 1 KiB * fronts, buf 16-byte aligned.
+ */
+int csa_stream_read(const void *buf, int64_t bytes, int fronts, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ EXPORTS = ("csa_abi_version", "csa_status_string", "csa_last_error_detail", "csa
            "csa_index_topk_workspace_bytes", "csa_index_topk", "csa_index_scores", "csa_mqa_workspace_bytes",
            "csa_sparse_mqa", "hca_dense_mqa", "csa_mx4_quantize", "csa_index_topk_mx4", "csa_append_rows",
            "csa_compress_channels", "csa_append_rows_multi", "csa_positions_advance", "csa_ragged_compress",
-           "csa_ragged_index_topk", "csa_ragged_index_topk_mx4", "csa_ragged_sparse_mqa", "hca_ragged_dense_mqa")
+           "csa_ragged_index_topk", "csa_ragged_index_topk_mx4", "csa_ragged_sparse_mqa", "hca_ragged_dense_mqa", "csa_stream_read")
 
 
 class AppendJob(ctypes.Structure):
@@ -93,6 +93,8 @@ def lib():
     L.csa_ragged_sparse_mqa.restype = I
     L.hca_ragged_dense_mqa.argtypes = [I, I, I, I, I, I, I, P, F, P, P, I64, P, I64, I64, P, P, P, SZ, P]
     L.hca_ragged_dense_mqa.restype = I
+    L.csa_stream_read.argtypes = [P, I64, I, P, P]
+    L.csa_stream_read.restype = I
     L.csa_append_rows.restype = I
     _lib = L
     return L
@@ -441,6 +443,16 @@ def hca_ragged_dense_mqa(q, entries, raw_ring, ring: int, N: int, m: int, W: int
                                       _p(raw_ring), _bstride(raw_ring), ring, _p(out), _p(lse), _p(workspace),
                                       ws_bytes, _stream(q)))
     return out
+
+
+def csa_stream_read(buf: torch.Tensor, fronts: int, sink: torch.Tensor) -> None:
+    """Measurement helper: stream-read buf (contiguous, bytes a multiple of 1 KiB x fronts) as `fronts` fronts."""
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    _need(sink, "sink", torch.int32)
+    if sink.numel() < 64 or not sink.is_contiguous():
+        raise ValueError("sink must be a contiguous int32 tensor of at least 64 elements")
+    _check(lib().csa_stream_read(_p(buf), buf.numel() * buf.element_size(), fronts, _p(sink), _stream(buf)))
 
 
 def mqa_workspace_bytes(B, Tq, H, d, n_rows_max) -> int:

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcsa.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["abi.cpp", "compress.hip", "indexer.hip", "topk.hip", "mqa.hip", "mx4.hip", "cache.hip"]
+SOURCES = ["abi.cpp", "compress.hip", "indexer.hip", "topk.hip", "mqa.hip", "mx4.hip", "cache.hip", "probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # packed-fp32 instructions are disabled for all device code

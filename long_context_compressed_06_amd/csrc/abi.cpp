@@ -198,6 +198,18 @@ int csa_append_rows_multi(int count, const csa_append_job *jobs, void *stream) {
     return hip_status(csa::launch_append_multi(aj, live, (hipStream_t)stream), "append launch");
 }
 
+int csa_stream_read(const void *buf, int64_t bytes, int fronts, uint32_t *sink, void *stream) {
+    if (fronts < 1 || fronts > 1024 || 1024 % fronts)
+        return fail(CSA_EUNSUPPORTED, "fronts=%d is not a divisor of 1024", fronts);
+    if (bytes < 0 || bytes % ((int64_t)1024 * fronts))
+        return fail(CSA_EINVAL, "bytes must be a multiple of 1 KiB per front");
+    if (bytes == 0) return ok();
+    if (!buf || !sink) return fail(CSA_EINVAL, "NULL pointer");
+    if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(CSA_EALIGN, "buf needs 16-byte alignment");
+    if (overlap(span(buf, 1, 0, bytes, 1), span(sink, 1, 0, 64, 4))) return fail(CSA_EINVAL, "sink overlaps buf");
+    return hip_status(csa::launch_stream_read(buf, bytes, fronts, sink, (hipStream_t)stream), "stream read launch");
+}
+
 int csa_positions_advance(int B, int64_t *pos, int64_t delta, void *stream) {
     if (B < 0) return fail(CSA_EINVAL, "B=%d must be >= 0", B);
     if (B == 0) return ok();

@@ -87,6 +87,9 @@ struct AppendJobs {
     AppendJob j[kMaxAppendJobs];
 };
 hipError_t launch_append_multi(const AppendJobs &jobs, int count, hipStream_t st);
+// measurement helper: stream-read `bytes` (a multiple of 16 KiB * fronts, 16-byte aligned) as `fronts` concurrent
+// contiguous fronts, XOR-folding into sink[0..63]
+hipError_t launch_stream_read(const void *p, int64_t bytes, int fronts, uint32_t *sink, hipStream_t st);
 // pos[b] += delta for b < B
 hipError_t launch_positions_advance(int B, int64_t *pos, int64_t delta, hipStream_t st);
 

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
     import long_context_compressed_06_amd as csa
 
     names = header_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(L, n), n
     assert sorted(csa.EXPORTS) == names
@@ -260,3 +260,13 @@ def test_ragged_calls_reject_bad_arguments(L):
     assert rm(pos=None) == -1
     assert rm(ring=0) == -1
     assert rm(W=129) == -1                    # the ring cannot hold the window
+
+
+def test_stream_read_rejects_bad_arguments(L):
+    assert L.csa_stream_read(P, 1 << 20, 0, P + 0x200000, None) == -6
+    assert L.csa_stream_read(P, (1 << 20) + 16, 1, P + 0x200000, None) == -1
+    assert L.csa_stream_read(P, 1 << 20, 3, P + 0x200000, None) == -6   # not a divisor of 1024
+    assert L.csa_stream_read(P, 1 << 14, 32, P + 0x200000, None) == -1  # not 1 KiB per front
+    assert L.csa_stream_read(P + 8, 1 << 20, 1, P + 0x200000, None) == -3
+    assert L.csa_stream_read(P, 1 << 20, 1, P + 0x100, None) == -1      # sink inside the buffer
+    assert L.csa_stream_read(P, 0, 1, None, None) == 0
