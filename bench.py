@@ -392,8 +392,9 @@ def bench_ragged(rs, steps, warmup):
     inputs = []
     for L in stack.layers:
         for t in [L.entries] + ([L.k_idx] if L.mode == "csa" else []):
-            for b in range(B):  # (per sequence: bounded temporaries)
-                t[b].copy_(torch.randn(t[b].shape, generator=g, device="cuda") * (t.shape[2] ** -0.5 if t is not L.entries else 1.0))
+            sc = t.shape[-1] ** -0.5 if t is not L.entries else 1.0
+            for part in t.view(-1, t.shape[-1]).split(1 << 20):  # (bounded temporaries; any cache layout)
+                part.copy_(torch.randn(part.shape, generator=g, device="cuda") * sc)
         L.raw_ring.copy_(torch.randn(L.raw_ring.shape, generator=g, device="cuda"))
         L.logit_ring.copy_(torch.randn(L.logit_ring.shape, generator=g, device="cuda"))
         L.pos.copy_(pos)
@@ -472,12 +473,13 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2", help="c2 (default), c3 or c5")
-    ap.add_argument("--also", default="c3,c5,c4,c2x,c5x,l2,l2x,l2c,p1,r1,r2",
+    ap.add_argument("--also", default="c3,c5,c4,c2x,c5x,l2,l2x,l2c,p1,r1,r1p,r2",
                     help="secondary workloads ('' for none); c4: the 64K prefill chunk (tokens/s and the MFMA "
                          "fractions of its indexer and attention); c2x/c5x: FP4 (MXFP4) indexer operands; "
                          "l2/l2x/l2c: decode loops with cache maintenance (l2c: per-channel pooling, pooled "
                          "index keys); p1: a whole chunked prefill from 0; r1/r2: ragged decode (lengths "
-                         "96K..158K) through one CSA layer / a CSA + HCA stack, one graph per token")
+                         "96K..158K) through one CSA layer / a CSA + HCA stack, one graph per token; r1p: r1 with "
+                         "caches in 64-row pages")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for the HBM byte counters)")
@@ -536,6 +538,7 @@ def main():
             b2 = ragged_bytes(rs)
             also[rs.name] = {"tokens_per_s": rs.B / (r2["ms_per_step"] * 1e-3), "ms_per_step": r2["ms_per_step"],
                              "layers": "+".join(s["mode"] for s in rs.specs()),
+                             "page_rows": [s.get("page_rows", 0) for s in rs.specs()],
                              "step_hbm_frac": b2 / (r2["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                              "algorithmic_bytes": b2,
                              "step": f"one token of each of {rs.B} sequences (lengths {min(rs.lengths)}.."

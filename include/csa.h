@@ -163,6 +163,9 @@ typedef struct {
     int64_t dst_bstride, dst_rows, pos0, ring;
     const int64_t *pos;
     int64_t every;
+    const int32_t *page_table;  /* paged destination (ring == 0): see "Paged caches" below */
+    int max_pages, page_rows;
+    int64_t n_pages;
 } csa_append_job;
 int csa_append_rows_multi(int count, const csa_append_job *jobs, void *stream);
 
@@ -197,26 +200,42 @@ int csa_append_rows_multi(int count, const csa_append_job *jobs, void *stream);
  * hca_dense_mqa with one query per sequence at position t_b; the window's
  * raw rows come from a ring (position p at row p mod ring, ring >= W), so no
  * raw_pos0 is needed.  q [B, 1, H, d]; workspace as for Tq = 1.
+ *
+ * Paged caches (every ragged call and append job that addresses a cache):
+ * with page_table == NULL a cache is [B, rows, row] with the batch stride
+ * given; otherwise it is a pool of n_pages pages of page_rows rows (a power
+ * of two >= 16) shared by the batch, row j of sequence b lying in row
+ * j mod page_rows of page page_table[b * max_pages + j / page_rows]
+ * (int32, max_pages <= 1024 entries per sequence, covering N / out_rows).
+ * The batch stride is then ignored.  Page ids read from memory are clamped
+ * into [0, n_pages).  Paged index keys need d_I = 128 (bf16 keys, or FP4
+ * codes with 4-byte aligned scales).  Entries and index keys of one layer
+ * may share one table.
  */
 int csa_positions_advance(int B, int64_t *pos, int64_t delta, void *stream);
 int csa_ragged_compress(int dt, int B, int m, int d, const int64_t *pos,
                         const void *raw_ring, int64_t ring_bstride,
                         const float *logit_ring, int64_t logit_bstride, int64_t ring,
-                        void *out, int64_t out_bstride, int64_t out_rows, void *stream);
+                        void *out, int64_t out_bstride, int64_t out_rows,
+                        const int32_t *page_table, int max_pages, int page_rows, int64_t n_pages,
+                        void *stream);
 int csa_ragged_index_topk(int dt, int B, int N, int H_I, int d_I, int m, int k, const int64_t *pos,
                           const void *q_idx, const float *w_idx,
                           const void *k_idx, int64_t k_bstride,
+                          const int32_t *page_table, int max_pages, int page_rows, int64_t n_pages,
                           int32_t *topk_idx, float *scores_out,
                           void *workspace, size_t workspace_bytes, void *stream);
 int csa_ragged_index_topk_mx4(int dt, int B, int N, int H_I, int d_I, int m, int k, const int64_t *pos,
                               const void *q_idx, const float *w_idx,
                               const uint8_t *k_codes, const uint8_t *k_scales, int64_t k_bstride,
+                              const int32_t *page_table, int max_pages, int page_rows, int64_t n_pages,
                               int32_t *topk_idx, float *scores_out,
                               void *workspace, size_t workspace_bytes, void *stream);
 int csa_ragged_sparse_mqa(int dt, int B, int H, int d, int N, int m, int k, int W,
                           const int64_t *pos, float scale,
                           const void *q,
                           const void *entries, int64_t e_bstride,
+                          const int32_t *page_table, int max_pages, int page_rows, int64_t n_pages,
                           const int32_t *topk_idx,
                           const void *raw_ring, int64_t ring_bstride, int64_t ring,
                           float *out, float *lse,
@@ -225,6 +244,7 @@ int hca_ragged_dense_mqa(int dt, int B, int H, int d, int N, int m, int W,
                          const int64_t *pos, float scale,
                          const void *q,
                          const void *entries, int64_t e_bstride,
+                         const int32_t *page_table, int max_pages, int page_rows, int64_t n_pages,
                          const void *raw_ring, int64_t ring_bstride, int64_t ring,
                          float *out, float *lse,
                          void *workspace, size_t workspace_bytes, void *stream);

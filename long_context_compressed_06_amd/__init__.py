@@ -32,7 +32,8 @@ class AppendJob(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("n", ctypes.c_int), ("row_bytes", ctypes.c_int64), ("rows", ctypes.c_void_p),
                 ("rows_bstride", ctypes.c_int64), ("dst", ctypes.c_void_p), ("dst_bstride", ctypes.c_int64),
                 ("dst_rows", ctypes.c_int64), ("pos0", ctypes.c_int64), ("ring", ctypes.c_int64),
-                ("pos", ctypes.c_void_p), ("every", ctypes.c_int64)]
+                ("pos", ctypes.c_void_p), ("every", ctypes.c_int64), ("page_table", ctypes.c_void_p),
+                ("max_pages", ctypes.c_int), ("page_rows", ctypes.c_int), ("n_pages", ctypes.c_int64)]
 
 
 class CsaError(RuntimeError):
@@ -83,15 +84,16 @@ def lib():
     L.csa_append_rows_multi.restype = I
     L.csa_positions_advance.argtypes = [I, P, I64, P]
     L.csa_positions_advance.restype = I
-    L.csa_ragged_compress.argtypes = [I, I, I, I, P, P, I64, P, I64, I64, P, I64, I64, P]
+    L.csa_ragged_compress.argtypes = [I, I, I, I, P, P, I64, P, I64, I64, P, I64, I64, P, I, I, I64, P]
     L.csa_ragged_compress.restype = I
-    L.csa_ragged_index_topk.argtypes = [I, I, I, I, I, I, I, P, P, P, P, I64, P, P, P, SZ, P]
+    L.csa_ragged_index_topk.argtypes = [I, I, I, I, I, I, I, P, P, P, P, I64, P, I, I, I64, P, P, P, SZ, P]
     L.csa_ragged_index_topk.restype = I
-    L.csa_ragged_index_topk_mx4.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, I64, P, P, P, SZ, P]
+    L.csa_ragged_index_topk_mx4.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, I64, P, I, I, I64, P, P, P, SZ, P]
     L.csa_ragged_index_topk_mx4.restype = I
-    L.csa_ragged_sparse_mqa.argtypes = [I, I, I, I, I, I, I, I, P, F, P, P, I64, P, P, I64, I64, P, P, P, SZ, P]
+    L.csa_ragged_sparse_mqa.argtypes = [I, I, I, I, I, I, I, I, P, F, P, P, I64, P, I, I, I64, P, P, I64, I64, P, P, P,
+                                        SZ, P]
     L.csa_ragged_sparse_mqa.restype = I
-    L.hca_ragged_dense_mqa.argtypes = [I, I, I, I, I, I, I, P, F, P, P, I64, P, I64, I64, P, P, P, SZ, P]
+    L.hca_ragged_dense_mqa.argtypes = [I, I, I, I, I, I, I, P, F, P, P, I64, P, I, I, I64, P, I64, I64, P, P, P, SZ, P]
     L.hca_ragged_dense_mqa.restype = I
     L.csa_stream_read.argtypes = [P, I64, I, P, P]
     L.csa_stream_read.restype = I
@@ -281,9 +283,36 @@ def csa_append_rows(rows: torch.Tensor, dst: torch.Tensor, pos0: int, ring: int 
     return dst
 
 
-def _append_job(rows: torch.Tensor, dst: torch.Tensor, pos0: int, ring: int, pos=None, every: int = 0) -> AppendJob:
+def _pages(pages, B):
+    """pages: None, or (page_table [B, max_pages] int32, page_rows, n_pages) -> ctypes arguments."""
+    if pages is None:
+        return None, 0, 0, 0
+    table, page_rows, n_pages = pages
+    _need(table, "page_table", torch.int32, 2)
+    if table.shape[0] != B or not table.is_contiguous():
+        raise ValueError("page_table must be a contiguous [B, max_pages] int32 tensor")
+    return _p(table), table.shape[1], page_rows, n_pages
+
+
+def _append_job(rows: torch.Tensor, dst: torch.Tensor, pos0: int, ring: int, pos=None, every: int = 0,
+                pages=None) -> AppendJob:
     _need(rows, "rows")
     _need(dst, "dst", rows.dtype)
+    if pages is not None:  # dst is a page pool [n_pages, page_rows, ...]
+        if rows.dim() < 2 or rows.shape[2:] != dst.shape[2:] or not dst.is_contiguous():
+            raise ValueError("rows [B, n, ...] and a contiguous pool [n_pages, page_rows, ...] with the same row shape")
+        per_row = 1
+        for x in rows.shape[2:]:
+            per_row *= x
+        es = rows.element_size()
+        if rows.shape[0] and not rows[0:1].is_contiguous():
+            raise ValueError("rows: the rows of one batch must be packed")
+        pt, mp, pr, npg = _pages(pages, rows.shape[0])
+        if pos is not None:
+            _need(pos, "pos", torch.int64, 1)
+        return AppendJob(rows.shape[0], rows.shape[1], per_row * es, rows.data_ptr(), rows.stride(0) * es,
+                         dst.data_ptr(), 0, mp * pr, pos0, ring, None if pos is None else pos.data_ptr(), every,
+                         pt, mp, pr, npg)
     if rows.dim() < 2 or rows.shape[0] != dst.shape[0] or rows.shape[2:] != dst.shape[2:]:
         raise ValueError("rows and dst must be [B, n, ...] and [B, cap, ...] with the same row shape")
     per_row = 1
@@ -299,12 +328,13 @@ def _append_job(rows: torch.Tensor, dst: torch.Tensor, pos0: int, ring: int, pos
             raise ValueError("pos must be a contiguous [B] int64 tensor")
     return AppendJob(rows.shape[0], rows.shape[1], per_row * es, rows.data_ptr(), rows.stride(0) * es,
                      dst.data_ptr(), dst.stride(0) * es, dst.shape[1], pos0, ring,
-                     None if pos is None else pos.data_ptr(), every)
+                     None if pos is None else pos.data_ptr(), every, None, 0, 0, 0)
 
 
 def csa_append_rows_multi(jobs) -> None:
-    """jobs: (rows, dst, pos0, ring[, pos[, every]]) tuples, each as csa_append_rows (pos: per-batch device
-    positions added to pos0; every: keep only the token completing a group, at that group's row); one launch."""
+    """jobs: (rows, dst, pos0, ring[, pos[, every[, pages]]]) tuples, each as csa_append_rows (pos: per-batch
+    device positions added to pos0; every: keep only the token completing a group, at that group's row; pages:
+    (page_table, page_rows, n_pages) with dst a page pool); one launch."""
     jobs = list(jobs)
     if not jobs:
         return
@@ -347,7 +377,7 @@ def _ragged_pos(pos, B):
 
 
 def csa_ragged_compress(raw_ring: torch.Tensor, logit_ring: torch.Tensor, ring: int, m: int, pos: torch.Tensor,
-                        out: torch.Tensor) -> torch.Tensor:
+                        out: torch.Tensor, pages=None) -> torch.Tensor:
     """Per sequence, the group its newest token (position pos[b]) completes, pooled out of the mirrored rings
     raw_ring [B, 2*ring, d] / logit_ring [B, 2*ring] into out [B, cap, d] at row (pos[b]+1)/m - 1."""
     _need(raw_ring, "raw_ring", dims=3)
@@ -357,22 +387,27 @@ def csa_ragged_compress(raw_ring: torch.Tensor, logit_ring: torch.Tensor, ring: 
     _ragged_pos(pos, B)
     if raw_ring.stride(1) != d or out.stride(1) != d or logit_ring.stride(1) != 1:
         raise ValueError("ring and cache rows must be packed")
+    pt, mp, pr, npg = _pages(pages, B)
+    rows = mp * pr if pages is not None else out.shape[1]
     _check(lib().csa_ragged_compress(_dt(raw_ring), B, m, d, _p(pos), _p(raw_ring), _bstride(raw_ring),
-                                     _p(logit_ring), _bstride(logit_ring), ring, _p(out), _bstride(out), out.shape[1],
+                                     _p(logit_ring), _bstride(logit_ring), ring, _p(out),
+                                     0 if pages is not None else _bstride(out), rows, pt, mp, pr, npg,
                                      _stream(raw_ring)))
     return out
 
 
 def csa_ragged_index_topk(q_idx, w_idx, k_idx, N: int, m: int, k: int, pos, topk_idx=None, scores_out=None,
-                          workspace=None) -> torch.Tensor:
+                          workspace=None, pages=None) -> torch.Tensor:
     """One query per sequence at position pos[b]: q_idx [B,1,H_I,d_I], w_idx [B,1,H_I], k_idx [B,cap,d_I]."""
     _need(q_idx, "q_idx", dims=4)
     _need(w_idx, "w_idx", torch.float32, 3)
     _need(k_idx, "k_idx", q_idx.dtype, 3)
     B, Tq, HI, dI = q_idx.shape
     _ragged_pos(pos, B)
-    if Tq != 1 or w_idx.shape != (B, 1, HI) or k_idx.shape[2] != dI or k_idx.stride(1) != dI or k_idx.shape[1] < N:
+    if Tq != 1 or w_idx.shape != (B, 1, HI) or k_idx.shape[2] != dI or k_idx.stride(1) != dI or (
+            pages is None and k_idx.shape[1] < N):
         raise ValueError("shape mismatch between the index operands")
+    pt, mp, pr, npg = _pages(pages, B)
     if not (q_idx.is_contiguous() and w_idx.is_contiguous()):
         raise ValueError("q_idx and w_idx must be contiguous")
     if topk_idx is None:
@@ -382,21 +417,22 @@ def csa_ragged_index_topk(q_idx, w_idx, k_idx, N: int, m: int, k: int, pos, topk
         workspace = torch.empty(need, dtype=torch.uint8, device=q_idx.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().csa_ragged_index_topk(_dt(q_idx), B, N, HI, dI, m, k, _p(pos), _p(q_idx), _p(w_idx), _p(k_idx),
-                                       _bstride(k_idx), _p(topk_idx), _p(scores_out), _p(workspace), ws_bytes,
-                                       _stream(q_idx)))
+                                       _bstride(k_idx), pt, mp, pr, npg, _p(topk_idx), _p(scores_out), _p(workspace),
+                                       ws_bytes, _stream(q_idx)))
     return topk_idx
 
 
 def csa_ragged_index_topk_mx4(q_idx, w_idx, k_codes, k_scales, N: int, m: int, k: int, pos, topk_idx=None,
-                              scores_out=None, workspace=None) -> torch.Tensor:
+                              scores_out=None, workspace=None, pages=None) -> torch.Tensor:
     """csa_ragged_index_topk on MXFP4 keys (codes [B,cap,d_I/2], scales [B,cap,d_I/32])."""
     _need(q_idx, "q_idx", dims=4)
     _need(w_idx, "w_idx", torch.float32, 3)
     B, Tq, HI, dI = q_idx.shape
     _ragged_pos(pos, B)
     rb = dI // 2
-    if Tq != 1 or k_codes.shape[2] != rb or k_scales.shape[2] != dI // 32 or k_codes.shape[1] < N:
+    if Tq != 1 or k_codes.shape[2] != rb or k_scales.shape[2] != dI // 32 or (pages is None and k_codes.shape[1] < N):
         raise ValueError("shape mismatch between the index operands")
+    pt, mp, pr, npg = _pages(pages, B)
     cap = k_codes.stride(0) // rb
     if k_codes.stride(0) != cap * rb or k_scales.stride(0) != cap * (dI // 32):
         raise ValueError("k_codes and k_scales must share one batch stride in rows")
@@ -407,15 +443,17 @@ def csa_ragged_index_topk_mx4(q_idx, w_idx, k_codes, k_scales, N: int, m: int, k
         workspace = torch.empty(need, dtype=torch.uint8, device=q_idx.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().csa_ragged_index_topk_mx4(_dt(q_idx), B, N, HI, dI, m, k, _p(pos), _p(q_idx), _p(w_idx),
-                                           _p(k_codes), _p(k_scales), cap, _p(topk_idx), _p(scores_out),
-                                           _p(workspace), ws_bytes, _stream(q_idx)))
+                                           _p(k_codes), _p(k_scales), cap, pt, mp, pr, npg, _p(topk_idx),
+                                           _p(scores_out), _p(workspace), ws_bytes, _stream(q_idx)))
     return topk_idx
 
 
 def csa_ragged_sparse_mqa(q, entries, topk_idx, raw_ring, ring: int, N: int, m: int, W: int, pos,
-                          scale: float | None = None, out=None, lse=None, workspace=None):
-    """One query per sequence at position pos[b]; window rows from raw_ring (position p at row p % ring)."""
+                          scale: float | None = None, out=None, lse=None, workspace=None, pages=None):
+    """One query per sequence at position pos[b]; window rows from raw_ring (position p at row p % ring);
+    pages: (page_table, page_rows, n_pages) with entries a page pool [n_pages, page_rows, d]."""
     B, Tq, H, d, out = _mqa_checks(q, entries, raw_ring, out, lse)
+    pt, mp, pr, npg = _pages(pages, B)
     _ragged_pos(pos, B)
     k = topk_idx.shape[2]
     scale = (1.0 / d ** 0.5) if scale is None else scale
@@ -424,15 +462,17 @@ def csa_ragged_sparse_mqa(q, entries, topk_idx, raw_ring, ring: int, N: int, m: 
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().csa_ragged_sparse_mqa(_dt(q), B, H, d, N, m, k, W, _p(pos), scale, _p(q), _p(entries),
-                                       _bstride(entries), _p(topk_idx), _p(raw_ring), _bstride(raw_ring), ring,
-                                       _p(out), _p(lse), _p(workspace), ws_bytes, _stream(q)))
+                                       _bstride(entries), pt, mp, pr, npg, _p(topk_idx), _p(raw_ring),
+                                       _bstride(raw_ring), ring, _p(out), _p(lse), _p(workspace), ws_bytes,
+                                       _stream(q)))
     return out
 
 
 def hca_ragged_dense_mqa(q, entries, raw_ring, ring: int, N: int, m: int, W: int, pos, scale: float | None = None,
-                         out=None, lse=None, workspace=None):
-    """HCA with one query per sequence at position pos[b]; window rows from raw_ring."""
+                         out=None, lse=None, workspace=None, pages=None):
+    """HCA with one query per sequence at position pos[b]; window rows from raw_ring; pages as above."""
     B, Tq, H, d, out = _mqa_checks(q, entries, raw_ring, out, lse)
+    pt, mp, pr, npg = _pages(pages, B)
     _ragged_pos(pos, B)
     scale = (1.0 / d ** 0.5) if scale is None else scale
     need = mqa_workspace_bytes(B, 1, H, d, N + W)
@@ -440,8 +480,8 @@ def hca_ragged_dense_mqa(q, entries, raw_ring, ring: int, N: int, m: int, W: int
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().hca_ragged_dense_mqa(_dt(q), B, H, d, N, m, W, _p(pos), scale, _p(q), _p(entries), _bstride(entries),
-                                      _p(raw_ring), _bstride(raw_ring), ring, _p(out), _p(lse), _p(workspace),
-                                      ws_bytes, _stream(q)))
+                                      pt, mp, pr, npg, _p(raw_ring), _bstride(raw_ring), ring, _p(out), _p(lse),
+                                      _p(workspace), ws_bytes, _stream(q)))
     return out
 
 

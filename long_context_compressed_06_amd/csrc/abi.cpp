@@ -57,6 +57,25 @@ int hip_status(hipError_t e, const char *what) {
     return ok();
 }
 
+// a paged cache: page_rows a power of two >= 16, at most kMaxPagesPerSeq pages per sequence covering N rows,
+// a pool of n_pages pages; on success *map addresses the pool
+int check_pages(const int32_t *page_table, int B, int max_pages, int page_rows, int64_t n_pages, int64_t N,
+                       csa::RowMap *map) {
+    if (page_rows < 16 || (page_rows & (page_rows - 1)))
+        return fail(CSA_EUNSUPPORTED, "page_rows=%d is not a power of two >= 16", page_rows);
+    if (max_pages < 1 || max_pages > csa::kMaxPagesPerSeq)
+        return fail(CSA_EUNSUPPORTED, "max_pages=%d outside 1..%d", max_pages, csa::kMaxPagesPerSeq);
+    if ((int64_t)max_pages * page_rows < N)
+        return fail(CSA_EINVAL, "%d pages of %d rows do not cover N=%lld", max_pages, page_rows, (long long)N);
+    if (n_pages < 1) return fail(CSA_EINVAL, "n_pages must be >= 1");
+    if (!aligned(page_table, 4)) return fail(CSA_EALIGN, "page_table needs 4-byte alignment");
+    int sh = 0;
+    while ((1 << sh) < page_rows) ++sh;
+    *map = csa::RowMap(0, page_table, max_pages, sh, n_pages);
+    (void)B;
+    return CSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -125,8 +144,10 @@ int csa_compress_channels(int dt, int B, int G, int m, int d, const void *raw, i
 }
 
 // the checks of one append; on success *vw is the widest move the job allows
+// paged: dst is a pool of dst_rows rows shared by the batch (dst_bstride unused)
 static int check_append(int B, int n, int64_t row_bytes, const void *rows, int64_t rows_bstride, const void *dst,
-                        int64_t dst_bstride, int64_t dst_rows, int64_t pos0, int64_t ring, int *vw) {
+                        int64_t dst_bstride, int64_t dst_rows, int64_t pos0, int64_t ring, int *vw,
+                        bool paged = false) {
     if (B < 0 || n < 0) return fail(CSA_EINVAL, "B=%d and n=%d must be >= 0", B, n);
     if (B > 65535) return fail(CSA_EUNSUPPORTED, "B=%d above 65535", B);
     if (row_bytes < 1) return fail(CSA_EINVAL, "row_bytes=%lld must be >= 1", (long long)row_bytes);
@@ -139,13 +160,14 @@ static int check_append(int B, int n, int64_t row_bytes, const void *rows, int64
                     (long long)ring, (long long)(2 * ring), (long long)dst_rows);
     if ((int64_t)B * n == 0) return ok();
     if (!rows || !dst) return fail(CSA_EINVAL, "NULL tensor pointer");
-    if (rows_bstride < (int64_t)n * row_bytes || dst_bstride < dst_rows * row_bytes)
+    if (rows_bstride < (int64_t)n * row_bytes || (!paged && dst_bstride < dst_rows * row_bytes))
         return fail(CSA_EINVAL, "a batch stride is smaller than one batch's extent");
     const Span ss = span(rows, B, rows_bstride, (int64_t)n * row_bytes, 1);
-    const Span sd = span(dst, B, dst_bstride, dst_rows * row_bytes, 1);
+    const Span sd = paged ? span(dst, 1, 0, dst_rows * row_bytes, 1) : span(dst, B, dst_bstride, dst_rows * row_bytes, 1);
     if (overlap(ss, sd)) return fail(CSA_EINVAL, "rows overlap the destination");
     int w = 16;
-    while (w > 1 && (row_bytes % w || !aligned(rows, w) || !aligned(dst, w) || rows_bstride % w || dst_bstride % w))
+    while (w > 1 &&
+           (row_bytes % w || !aligned(rows, w) || !aligned(dst, w) || rows_bstride % w || (!paged && dst_bstride % w)))
         w /= 2;
     *vw = w;
     return ok();
@@ -161,22 +183,35 @@ int csa_append_rows_multi(int count, const csa_append_job *jobs, void *stream) {
         const csa_append_job &J = jobs[i];
         int vw = 1;
         if (J.every < 0) return fail(CSA_EINVAL, "job %d: every must be >= 0", i);
+        csa::RowMap dmap;
+        if (J.page_table) {
+            if (J.ring != 0) return fail(CSA_EINVAL, "job %d: a paged destination cannot be a ring", i);
+            if (int s = check_pages(J.page_table, J.B, J.max_pages, J.page_rows, J.n_pages, J.dst_rows, &dmap)) {
+                std::string d = "job " + std::to_string(i) + ": " + g_detail;
+                return fail(s, "%s", d.c_str());
+            }
+        }
         if (J.pos && !aligned(J.pos, 8)) return fail(CSA_EALIGN, "job %d: pos needs 8-byte alignment", i);
         // with positions from memory the destination rows are checked on the device (rows outside are
         // skipped); the host checks what it can: a zero base position
-        if (int s = check_append(J.B, J.n, J.row_bytes, J.rows, J.rows_bstride, J.dst, J.dst_bstride, J.dst_rows,
-                                 (J.pos || J.every) ? 0 : J.pos0, J.ring, &vw)) {
+        // (paged destination: its pool is checked as one span of n_pages * page_rows rows)
+        const int64_t d_rows = J.page_table ? J.n_pages * J.page_rows : J.dst_rows;
+        if (int s = check_append(J.B, J.n, J.row_bytes, J.rows, J.rows_bstride, J.dst, J.dst_bstride, d_rows,
+                                 (J.pos || J.every) ? 0 : J.pos0, J.ring, &vw, J.page_table != nullptr)) {
             std::string d = "job " + std::to_string(i) + ": " + g_detail;
             return fail(s, "%s", d.c_str());
         }
         if ((int64_t)J.B * J.n == 0) continue;
         // no job may write where another reads or writes
-        const Span di = span(J.dst, J.B, J.dst_bstride, J.dst_rows * J.row_bytes, 1);
+        const Span di = J.page_table ? span(J.dst, 1, 0, J.n_pages * J.page_rows * J.row_bytes, 1)
+                                     : span(J.dst, J.B, J.dst_bstride, J.dst_rows * J.row_bytes, 1);
         for (int k = 0; k < count; ++k) {
             const csa_append_job &K = jobs[k];
             if (k == i || (int64_t)K.B * K.n == 0) continue;
+            const Span dk = K.page_table ? span(K.dst, 1, 0, K.n_pages * K.page_rows * K.row_bytes, 1)
+                                         : span(K.dst, K.B, K.dst_bstride, K.dst_rows * K.row_bytes, 1);
             if (overlap(di, span(K.rows, K.B, K.rows_bstride, (int64_t)K.n * K.row_bytes, 1)) ||
-                (k < i && overlap(di, span(K.dst, K.B, K.dst_bstride, K.dst_rows * K.row_bytes, 1))))
+                (k < i && overlap(di, dk)))
                 return fail(CSA_EINVAL, "job %d's destination overlaps job %d's rows or destination", i, k);
         }
         csa::AppendJob &A = aj.j[live++];
@@ -191,6 +226,7 @@ int csa_append_rows_multi(int count, const csa_append_job *jobs, void *stream) {
         A.pos = J.pos;
         A.every = J.every;
         A.dst_rows = J.dst_rows;
+        A.dmap = dmap;
         A.vw = vw;
         A.B = J.B;
     }
@@ -220,7 +256,8 @@ int csa_positions_advance(int B, int64_t *pos, int64_t delta, void *stream) {
 
 int csa_ragged_compress(int dt, int B, int m, int d, const int64_t *pos, const void *raw_ring, int64_t ring_bstride,
                         const float *logit_ring, int64_t logit_bstride, int64_t ring, void *out, int64_t out_bstride,
-                        int64_t out_rows, void *stream) {
+                        int64_t out_rows, const int32_t *page_table, int max_pages, int page_rows, int64_t n_pages,
+                        void *stream) {
     if (int s = check_dt(dt)) return s;
     if (B < 0 || out_rows < 0) return fail(CSA_EINVAL, "B and out_rows must be >= 0");
     if (m < 1 || m > 128) return fail(CSA_EUNSUPPORTED, "m=%d outside 1..128", m);
@@ -228,18 +265,26 @@ int csa_ragged_compress(int dt, int B, int m, int d, const int64_t *pos, const v
     if (ring < m) return fail(CSA_EINVAL, "a ring of %lld positions cannot hold a group of %d", (long long)ring, m);
     if (B == 0 || out_rows == 0) return ok();
     if (!pos || !raw_ring || !logit_ring || !out) return fail(CSA_EINVAL, "NULL tensor pointer");
-    if (ring_bstride < 2 * ring * d || logit_bstride < 2 * ring || out_bstride < out_rows * d)
+    csa::RowMap omap(out_bstride);
+    int64_t o_span_b = B, o_span_stride = out_bstride, o_span_inner = out_rows * d;
+    if (page_table) {
+        if (int s = check_pages(page_table, B, max_pages, page_rows, n_pages, out_rows, &omap)) return s;
+        o_span_b = 1, o_span_stride = 0, o_span_inner = n_pages * page_rows * d;
+    } else if (out_bstride < out_rows * d) {
+        return fail(CSA_EINVAL, "out_bstride smaller than out_rows*d");
+    }
+    if (ring_bstride < 2 * ring * d || logit_bstride < 2 * ring)
         return fail(CSA_EINVAL, "a batch stride is smaller than one batch's extent (rings hold 2*ring rows)");
     if (!aligned(raw_ring, 16) || !aligned(out, 16) || !aligned(logit_ring, 4) || !aligned(pos, 8) ||
         ring_bstride % 8 || out_bstride % 8)
         return fail(CSA_EALIGN, "raw/out need 16-byte alignment and batch strides a multiple of 8 elements");
     const size_t es = esize(dt);
-    const Span so = span(out, B, out_bstride, out_rows * d, es);
+    const Span so = span(out, o_span_b, o_span_stride, o_span_inner, es);
     if (overlap(so, span(raw_ring, B, ring_bstride, 2 * ring * d, es)) ||
         overlap(so, span(logit_ring, B, logit_bstride, 2 * ring, 4)) || overlap(so, span(pos, 1, 0, B, 8)))
         return fail(CSA_EINVAL, "out overlaps an input");
     return hip_status(csa::launch_compress_ragged(dt, B, m, d, pos, raw_ring, ring_bstride, logit_ring, logit_bstride,
-                                                  ring, out, out_bstride, out_rows, (hipStream_t)stream),
+                                                  ring, out, omap, out_rows, (hipStream_t)stream),
                       "compress launch");
 }
 
@@ -282,7 +327,8 @@ static int check_qpos(csa::QPos qp, int B, int Tq) {
 static int index_topk_impl(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k, csa::QPos q_pos0,
                            const void *q_idx, const float *w_idx, const void *k_idx, int64_t k_bstride,
                            int32_t *topk_idx, float *scores_out, void *workspace, size_t workspace_bytes,
-                           void *stream) {
+                           void *stream, const int32_t *page_table = nullptr, int max_pages = 0, int page_rows = 0,
+                           int64_t n_pages = 0) {
     if (int s = check_dt(dt)) return s;
     if (B < 0 || Tq < 0 || N < 0) return fail(CSA_EINVAL, "B, Tq and N must be >= 0");
     if (H_I < 1 || H_I > 64) return fail(CSA_EUNSUPPORTED, "H_I=%d outside 1..64", H_I);
@@ -294,7 +340,16 @@ static int index_topk_impl(int dt, int B, int Tq, int N, int H_I, int d_I, int m
     if (N > csa::kTopkMaxEntries) return fail(CSA_EUNSUPPORTED, "N=%d above %lld entries", N, (long long)csa::kTopkMaxEntries);
     if ((int64_t)B * Tq == 0) return ok();
     if (!q_idx || !w_idx || !topk_idx || (N > 0 && !k_idx)) return fail(CSA_EINVAL, "NULL tensor pointer");
-    if (N > 0 && k_bstride < (int64_t)N * d_I) return fail(CSA_EINVAL, "k_bstride smaller than N*d_I");
+    csa::RowMap kmap(k_bstride);
+    int64_t k_span_b = B, k_span_stride = k_bstride, k_span_inner = (int64_t)N * d_I;
+    if (page_table) {
+        if (dt != CSA_BF16 || d_I != 128)
+            return fail(CSA_EUNSUPPORTED, "paged index keys need bf16 keys with d_I = 128");
+        if (int s = check_pages(page_table, B, max_pages, page_rows, n_pages, N, &kmap)) return s;
+        k_span_b = 1, k_span_stride = 0, k_span_inner = n_pages * page_rows * d_I;
+    } else if (N > 0 && k_bstride < (int64_t)N * d_I) {
+        return fail(CSA_EINVAL, "k_bstride smaller than N*d_I");
+    }
     if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(w_idx, 4) || !aligned(topk_idx, 4) ||
         !aligned(scores_out, 4) || k_bstride % 8)
         return fail(CSA_EALIGN, "q_idx/k_idx need 16-byte alignment, k_bstride a multiple of 8 elements");
@@ -310,7 +365,7 @@ static int index_topk_impl(int dt, int B, int Tq, int N, int H_I, int d_I, int m
     const Span ss = span(scores_out, B, (int64_t)Tq * N, (int64_t)Tq * N, 4);
     const Span inputs[3] = {span(q_idx, B, (int64_t)Tq * H_I * d_I, (int64_t)Tq * H_I * d_I, es),
                             span(w_idx, B, (int64_t)Tq * H_I, (int64_t)Tq * H_I, 4),
-                            span(k_idx, B, k_bstride, (int64_t)N * d_I, es)};
+                            span(k_idx, k_span_b, k_span_stride, k_span_inner, es)};
     for (const Span &in : inputs)
         if (overlap(si, in) || overlap(ss, in)) return fail(CSA_EINVAL, "an output overlaps an input");
     if (overlap(si, ss)) return fail(CSA_EINVAL, "topk_idx overlaps scores_out");
@@ -325,7 +380,7 @@ static int index_topk_impl(int dt, int B, int Tq, int N, int H_I, int d_I, int m
                                "histogram clear"))
             return s;
         if (int s = hip_status(csa::launch_index_scores(dt, B, Tq, N, H_I, d_I, m, q_pos0, q_idx, w_idx, k_idx,
-                                                         k_bstride, scores, csa::topk_score_stride(N), scores_out,
+                                                         kmap, scores, csa::topk_score_stride(N), scores_out,
                                                          scratch, st),
                                "indexer launch"))
             return s;
@@ -343,11 +398,13 @@ int csa_index_topk(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k,
 
 int csa_ragged_index_topk(int dt, int B, int N, int H_I, int d_I, int m, int k, const int64_t *pos,
                           const void *q_idx, const float *w_idx, const void *k_idx, int64_t k_bstride,
+                          const int32_t *page_table, int max_pages, int page_rows, int64_t n_pages,
                           int32_t *topk_idx, float *scores_out, void *workspace, size_t workspace_bytes,
                           void *stream) {
     if (B > 0 && !pos) return fail(CSA_EINVAL, "NULL pos");
     return index_topk_impl(dt, B, 1, N, H_I, d_I, m, k, csa::QPos(0, pos), q_idx, w_idx, k_idx, k_bstride, topk_idx,
-                           scores_out, workspace, workspace_bytes, stream);
+                           scores_out, workspace, workspace_bytes, stream, page_table, max_pages, page_rows,
+                           n_pages);
 }
 
 int csa_index_scores(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int64_t q_pos0, const void *q_idx,
@@ -391,7 +448,9 @@ int csa_mx4_quantize(int dt, int64_t n_rows, int d, const void *x, uint8_t *code
 static int index_topk_mx4_impl(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k, csa::QPos q_pos0,
                                const void *q_idx, const float *w_idx, const uint8_t *k_codes,
                                const uint8_t *k_scales, int64_t k_bstride, int32_t *topk_idx, float *scores_out,
-                               void *workspace, size_t workspace_bytes, void *stream) {
+                               void *workspace, size_t workspace_bytes, void *stream,
+                               const int32_t *page_table = nullptr, int max_pages = 0, int page_rows = 0,
+                               int64_t n_pages = 0) {
     if (int s = check_dt(dt)) return s;
     if (B < 0 || Tq < 0 || N < 0) return fail(CSA_EINVAL, "B, Tq and N must be >= 0");
     if (H_I < 1 || H_I > 64) return fail(CSA_EUNSUPPORTED, "H_I=%d outside 1..64", H_I);
@@ -404,7 +463,16 @@ static int index_topk_mx4_impl(int dt, int B, int Tq, int N, int H_I, int d_I, i
     if ((int64_t)B * Tq == 0) return ok();
     if (!q_idx || !w_idx || !topk_idx || (N > 0 && (!k_codes || !k_scales)))
         return fail(CSA_EINVAL, "NULL tensor pointer");
-    if (N > 0 && k_bstride < N) return fail(CSA_EINVAL, "k_bstride smaller than N rows");
+    csa::RowMap kmap(k_bstride);
+    int64_t k_span_b = B, k_span_rows = k_bstride, k_inner_rows = N;
+    if (page_table) {
+        if (d_I != 128 || !aligned(k_scales, 4))
+            return fail(CSA_EUNSUPPORTED, "paged FP4 keys need d_I = 128 and 4-byte aligned scales");
+        if (int s = check_pages(page_table, B, max_pages, page_rows, n_pages, N, &kmap)) return s;
+        k_span_b = 1, k_span_rows = 0, k_inner_rows = n_pages * page_rows;
+    } else if (N > 0 && k_bstride < N) {
+        return fail(CSA_EINVAL, "k_bstride smaller than N rows");
+    }
     if (!aligned(q_idx, 16) || !aligned(k_codes, 16) || !aligned(w_idx, 4) || !aligned(topk_idx, 4) ||
         !aligned(scores_out, 4))
         return fail(CSA_EALIGN, "q_idx/k_codes need 16-byte alignment");
@@ -417,8 +485,8 @@ static int index_topk_mx4_impl(int dt, int B, int Tq, int N, int H_I, int d_I, i
     const Span si = span(topk_idx, B, (int64_t)Tq * k, (int64_t)Tq * k, 4);
     const Span ss = span(scores_out, B, (int64_t)Tq * N, (int64_t)Tq * N, 4);
     const Span inputs[4] = {span(q_idx, 1, 0, rows * H_I * d_I, esize(dt)), span(w_idx, 1, 0, rows * H_I, 4),
-                            span(k_codes, B, k_bstride * rb, (int64_t)N * rb, 1),
-                            span(k_scales, B, k_bstride * kb, (int64_t)N * kb, 1)};
+                            span(k_codes, k_span_b, k_span_rows * rb, k_inner_rows * rb, 1),
+                            span(k_scales, k_span_b, k_span_rows * kb, k_inner_rows * kb, 1)};
     const Span sw = span(workspace, 1, 0, (int64_t)need, 1);
     for (const Span &in : inputs)
         if (overlap(si, in) || overlap(ss, in) || overlap(sw, in))
@@ -433,7 +501,7 @@ static int index_topk_mx4_impl(int dt, int B, int Tq, int N, int H_I, int d_I, i
                                "histogram clear"))
             return s;
         if (int s = hip_status(csa::launch_index_mx4(dt, B, Tq, N, H_I, d_I, m, q_pos0, q_idx, w_idx, k_codes,
-                                                      k_scales, k_bstride, scores, csa::topk_score_stride(N),
+                                                      k_scales, kmap, scores, csa::topk_score_stride(N),
                                                       scores_out, scratch, st),
                                "indexer launch"))
             return s;
@@ -452,11 +520,13 @@ int csa_index_topk_mx4(int dt, int B, int Tq, int N, int H_I, int d_I, int m, in
 
 int csa_ragged_index_topk_mx4(int dt, int B, int N, int H_I, int d_I, int m, int k, const int64_t *pos,
                               const void *q_idx, const float *w_idx, const uint8_t *k_codes,
-                              const uint8_t *k_scales, int64_t k_bstride, int32_t *topk_idx, float *scores_out,
+                              const uint8_t *k_scales, int64_t k_bstride, const int32_t *page_table, int max_pages,
+                              int page_rows, int64_t n_pages, int32_t *topk_idx, float *scores_out,
                               void *workspace, size_t workspace_bytes, void *stream) {
     if (B > 0 && !pos) return fail(CSA_EINVAL, "NULL pos");
     return index_topk_mx4_impl(dt, B, 1, N, H_I, d_I, m, k, csa::QPos(0, pos), q_idx, w_idx, k_codes, k_scales,
-                               k_bstride, topk_idx, scores_out, workspace, workspace_bytes, stream);
+                               k_bstride, topk_idx, scores_out, workspace, workspace_bytes, stream, page_table,
+                               max_pages, page_rows, n_pages);
 }
 
 size_t csa_mqa_workspace_bytes(int B, int Tq, int H, int d, int n_rows_max) {
@@ -473,7 +543,9 @@ size_t csa_mqa_workspace_bytes(int B, int Tq, int H, int d, int n_rows_max) {
 static int mqa_common(int dt, int B, int Tq, int H, int d, int N, int m, int k, int W, csa::QPos q_pos0, float scale,
                       const void *q, const void *entries, int64_t e_bstride, const int32_t *idx, const void *raw,
                       int64_t raw_bstride, int64_t raw_pos0, int64_t raw_len, int64_t raw_ring, float *out,
-                      float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+                      float *lse, void *workspace, size_t workspace_bytes, void *stream,
+                      const int32_t *page_table = nullptr, int max_pages = 0, int page_rows = 0,
+                      int64_t n_pages = 0) {
     if (int s = check_dt(dt)) return s;
     if (B < 0 || Tq < 0 || N < 0 || W < 0 || raw_len < 0) return fail(CSA_EINVAL, "B, Tq, N, W, raw_len must be >= 0");
     if (H < 1 || H > 64) return fail(CSA_EUNSUPPORTED, "H=%d outside 1..64", H);
@@ -500,7 +572,14 @@ static int mqa_common(int dt, int B, int Tq, int H, int d, int N, int m, int k, 
         if (raw_bstride < (int64_t)raw_len * d) return fail(CSA_EINVAL, "raw_bstride smaller than raw_len*d");
     }
     if (!q || !out || (N > 0 && !entries) || (k > 0 && !idx)) return fail(CSA_EINVAL, "NULL tensor pointer");
-    if (N > 0 && e_bstride < (int64_t)N * d) return fail(CSA_EINVAL, "e_bstride smaller than N*d");
+    csa::RowMap emap(e_bstride);
+    int64_t e_span_b = B, e_span_stride = e_bstride, e_span_inner = (int64_t)N * d;
+    if (page_table) {
+        if (int s = check_pages(page_table, B, max_pages, page_rows, n_pages, N, &emap)) return s;
+        e_span_b = 1, e_span_stride = 0, e_span_inner = n_pages * page_rows * d;
+    } else if (N > 0 && e_bstride < (int64_t)N * d) {
+        return fail(CSA_EINVAL, "e_bstride smaller than N*d");
+    }
     if (!aligned(q, 16) || !aligned(entries, 16) || !aligned(raw, 16) || !aligned(out, 16) || !aligned(idx, 4) ||
         !aligned(lse, 4) || e_bstride % 8 || raw_bstride % 8)
         return fail(CSA_EALIGN, "q/entries/raw/out need 16-byte alignment, strides a multiple of 8 elements");
@@ -508,7 +587,7 @@ static int mqa_common(int dt, int B, int Tq, int H, int d, int N, int m, int k, 
     const Span so = span(out, B, (int64_t)Tq * H * d, (int64_t)Tq * H * d, 4);
     const Span sl = span(lse, B, (int64_t)Tq * H, (int64_t)Tq * H, 4);
     const Span inputs[4] = {span(q, B, (int64_t)Tq * H * d, (int64_t)Tq * H * d, es),
-                            span(entries, B, e_bstride, (int64_t)N * d, es),
+                            span(entries, e_span_b, e_span_stride, e_span_inner, es),
                             span(raw, B, raw_bstride, (int64_t)raw_len * d, es),
                             span(idx, B, (int64_t)Tq * k, (int64_t)Tq * k, 4)};
     for (const Span &in : inputs)
@@ -526,7 +605,7 @@ static int mqa_common(int dt, int B, int Tq, int H, int d, int N, int m, int k, 
         if (!aligned(workspace, 16)) return fail(CSA_EALIGN, "workspace needs 16-byte alignment");
         ws = (float *)workspace;
     }
-    return hip_status(csa::launch_mqa(dt, B, Tq, H, d, N, m, k, W, q_pos0, scale, q, entries, e_bstride, idx, raw,
+    return hip_status(csa::launch_mqa(dt, B, Tq, H, d, N, m, k, W, q_pos0, scale, q, entries, emap, idx, raw,
                                       raw_bstride, raw_pos0, raw_ring, out, lse, ws, splits, tps,
                                       (hipStream_t)stream),
                       "attention launch");
@@ -543,24 +622,28 @@ int csa_sparse_mqa(int dt, int B, int Tq, int H, int d, int N, int m, int k, int
 }
 
 int csa_ragged_sparse_mqa(int dt, int B, int H, int d, int N, int m, int k, int W, const int64_t *pos, float scale,
-                          const void *q, const void *entries, int64_t e_bstride, const int32_t *topk_idx,
+                          const void *q, const void *entries, int64_t e_bstride, const int32_t *page_table,
+                          int max_pages, int page_rows, int64_t n_pages, const int32_t *topk_idx,
                           const void *raw_ring, int64_t ring_bstride, int64_t ring, float *out, float *lse,
                           void *workspace, size_t workspace_bytes, void *stream) {
     if (k < 1 || k > 2048) return fail(CSA_EUNSUPPORTED, "k=%d outside 1..2048", k);
     if (B > 0 && !pos) return fail(CSA_EINVAL, "NULL pos");
     if (ring < 1) return fail(CSA_EINVAL, "ring must be >= 1");
     return mqa_common(dt, B, 1, H, d, N, m, k, W, csa::QPos(0, pos), scale, q, entries, e_bstride, topk_idx,
-                      raw_ring, ring_bstride, 0, ring, ring, out, lse, workspace, workspace_bytes, stream);
+                      raw_ring, ring_bstride, 0, ring, ring, out, lse, workspace, workspace_bytes, stream, page_table,
+                      max_pages, page_rows, n_pages);
 }
 
 int hca_ragged_dense_mqa(int dt, int B, int H, int d, int N, int m, int W, const int64_t *pos, float scale,
-                         const void *q, const void *entries, int64_t e_bstride, const void *raw_ring,
+                         const void *q, const void *entries, int64_t e_bstride, const int32_t *page_table,
+                         int max_pages, int page_rows, int64_t n_pages, const void *raw_ring,
                          int64_t ring_bstride, int64_t ring, float *out, float *lse, void *workspace,
                          size_t workspace_bytes, void *stream) {
     if (B > 0 && !pos) return fail(CSA_EINVAL, "NULL pos");
     if (ring < 1) return fail(CSA_EINVAL, "ring must be >= 1");
     return mqa_common(dt, B, 1, H, d, N, m, 0, W, csa::QPos(0, pos), scale, q, entries, e_bstride, nullptr, raw_ring,
-                      ring_bstride, 0, ring, ring, out, lse, workspace, workspace_bytes, stream);
+                      ring_bstride, 0, ring, ring, out, lse, workspace, workspace_bytes, stream, page_table,
+                      max_pages, page_rows, n_pages);
 }
 
 int hca_dense_mqa(int dt, int B, int Tq, int H, int d, int N, int m, int W, int64_t q_pos0, float scale, const void *q,

@@ -61,7 +61,7 @@ __device__ __forceinline__ void append_job_body(const AppendJob &J) {
     const int64_t b = blockIdx.y;
     const int64_t vpr = J.row_bytes / VW;
     const unsigned char *s = J.src + b * J.src_bs;
-    unsigned char *d = J.dst + b * J.dst_bs;
+    unsigned char *d = J.dst + (J.dmap.ptab ? 0 : b * J.dst_bs);  // (paged: rows of the pool)
     const int64_t base = J.pos0 + (J.pos ? J.pos[b] : 0);
     for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < J.n * vpr; e += (int64_t)gridDim.x * 256) {
         const int64_t i = e / vpr, v = e % vpr;
@@ -74,7 +74,8 @@ __device__ __forceinline__ void append_job_body(const AppendJob &J) {
         const V x = *(const V *)(s + i * J.row_bytes + v * VW);
         if (J.ring == 0) {
             if (p >= J.dst_rows) continue;
-            *(V *)(d + p * J.row_bytes + v * VW) = x;
+            const int64_t row = J.dmap.ptab ? J.dmap.paged_row(b, p) : p;
+            *(V *)(d + row * J.row_bytes + v * VW) = x;
         } else {
             const int64_t slot = p % J.ring;
             *(V *)(d + slot * J.row_bytes + v * VW) = x;

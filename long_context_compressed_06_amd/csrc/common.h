@@ -81,6 +81,36 @@ struct QPos {
     __device__ __forceinline__ int64_t at(int64_t b, int64_t ti) const { return (pos ? pos[b] : q_pos0) + ti; }
 };
 
+// Rows of a per-sequence cache (entries or index keys).  Contiguous caches:
+// sequence b starts bstride units into the buffer (the unit is the caller's:
+// offset() takes it in elements).  Paged caches (ptab set): row j of sequence
+// b is row j & (2^pshift - 1) of page ptab[b * pstride + (j >> pshift)] of
+// one pool of npages pages of 2^pshift rows; page ids read from memory are
+// clamped into the pool.  Converts from a plain batch stride.
+struct RowMap {
+    int64_t bstride;
+    const int32_t *ptab;
+    int pstride, pshift;
+    int64_t npages;
+    __host__ __device__ RowMap(int64_t bs = 0, const int32_t *t = nullptr, int ps = 0, int sh = 0, int64_t np = 0)
+        : bstride(bs), ptab(t), pstride(ps), pshift(sh), npages(np) {}
+    __device__ __forceinline__ int64_t page_of(int64_t b, int64_t pidx) const {
+        int64_t pg = ptab[b * pstride + pidx];
+        return pg < 0 ? 0 : (pg >= npages ? npages - 1 : pg);
+    }
+    // pool row of sequence b's row j (paged maps only)
+    __device__ __forceinline__ int64_t paged_row(int64_t b, int64_t j) const {
+        return (page_of(b, j >> pshift) << pshift) | (j & ((1 << pshift) - 1));
+    }
+    // element offset of sequence b's row j, rows of rowlen elements (bstride in elements)
+    __device__ __forceinline__ int64_t offset(int64_t b, int64_t j, int64_t rowlen) const {
+        return ptab ? paged_row(b, j) * rowlen : b * bstride + j * rowlen;
+    }
+};
+// page list of one sequence staged in LDS by the indexers (pages of at most
+// this many entries per sequence)
+constexpr int kMaxPagesPerSeq = 1024;
+
 // Entries visible to a query at absolute position t: complete groups only.
 __device__ __forceinline__ int64_t n_visible(int64_t t, int m, int64_t N) {
     if (t < 0) return 0;

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void k_compress_ragged(int m, int d, int tpr, 
                                                           const int64_t *__restrict__ pos, const T *__restrict__ raw,
                                                           int64_t raw_bs, const float *__restrict__ logits,
                                                           int64_t log_bs, int64_t ring, T *__restrict__ out,
-                                                          int64_t out_bs, int64_t out_rows) {
+                                                          RowMap om, int64_t out_rows) {
     const int sl = blockIdx.x % slices;
     const int64_t b = blockIdx.x / slices;
     const int64_t p = pos[b];
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(256) void k_compress_ragged(int m, int d, int tpr, 
     const int64_t r0 = (g * m) % ring;
     const int width = tpr * (16 / (int)sizeof(T));
     compress_group(raw + b * raw_bs + r0 * d + sl * width, logits + b * log_bs + r0, m, d, tpr,
-                   out + b * out_bs + g * d + sl * width);
+                   out + om.offset(b, g, d) + sl * width);
 }
 
 // Per-channel pooling logits: channel x of entry g pools channel x of the
@@ -198,7 +198,7 @@ hipError_t launch_compress_t(int B, int G, int m, int d, const void *raw, int64_
 }
 template <typename T>
 hipError_t launch_compress_ragged_t(int B, int m, int d, const int64_t *pos, const void *raw, int64_t raw_bs,
-                                    const float *logits, int64_t log_bs, int64_t ring, void *out, int64_t out_bs,
+                                    const float *logits, int64_t log_bs, int64_t ring, void *out, RowMap out_bs,
                                     int64_t out_rows, hipStream_t st) {
     constexpr int VEC = 16 / sizeof(T);
     int tpr = d / VEC;
@@ -211,7 +211,7 @@ hipError_t launch_compress_ragged_t(int B, int m, int d, const int64_t *pos, con
     return hipGetLastError();
 }
 hipError_t launch_compress_ragged(int dt, int B, int m, int d, const int64_t *pos, const void *raw, int64_t raw_bs,
-                                  const float *logits, int64_t log_bs, int64_t ring, void *out, int64_t out_bs,
+                                  const float *logits, int64_t log_bs, int64_t ring, void *out, RowMap out_bs,
                                   int64_t out_rows, hipStream_t st) {
     if (dt == 0)
         return launch_compress_ragged_t<float>(B, m, d, pos, raw, raw_bs, logits, log_bs, ring, out, out_bs,

@@ -166,7 +166,7 @@ struct IdxDma {
     static constexpr int STAGES = 8;         // ring slots per wavefront
     static constexpr int RING = kIdxWaves * STAGES * TB;
     static constexpr int QS = 64 * DI * 2;   // staged index query (up to 64 heads)
-    static constexpr int LDS = RING + QS + kTopkBins * 4;
+    static constexpr int LDS = RING + QS + kTopkBins * 4 + kMaxPagesPerSeq * 4;  // (+ page list, paged caches)
     // chunk position of row r's chunk ch (an involution, so it also maps back)
     static __device__ __forceinline__ int swz(int r, int ch) { return ch ^ ((r / RPS) % CPR); }
 };
@@ -196,7 +196,7 @@ template <int DI, int MB>
 __global__ __launch_bounds__(kIdxWaves * 64) void k_index_dma(int Tq, int N, int HI, int m, QPos q_pos0,
                                                                int blocks_per_row, const bf16_t *__restrict__ qI,
                                                                const float *__restrict__ w,
-                                                               const bf16_t *__restrict__ kI, int64_t k_bs,
+                                                               const bf16_t *__restrict__ kI, RowMap kl,
                                                                float *__restrict__ scores, int64_t s_stride,
                                                                float *__restrict__ scores2,
                                                                uint32_t *__restrict__ hist) {
@@ -206,6 +206,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_dma(int Tq, int N, int
     unsigned char *ring = lds;
     bf16_t *qs = (bf16_t *)(lds + S::RING);
     uint32_t *bh = (uint32_t *)(lds + S::RING + S::QS);
+    int32_t *pl = (int32_t *)(lds + S::RING + S::QS + kTopkBins * 4);  // the query's pages (paged caches)
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // (uniform: keeps tile logic scalar)
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_dma(int Tq, int N, int
     // ---- DMA of one tile into ring slot `slot`.  Lane addresses step by a
     // fixed stride from tile to tile; in the tile that holds the last visible
     // entry, rows past it reread that entry's row (their scores are masked).
-    const bf16_t *kb = kI + b * k_bs;
+    const bf16_t *kb = kI + (kl.ptab ? 0 : b * kl.bstride);
     unsigned char *my_ring = ring + wv * S::STAGES * S::TB;
     const uint32_t ring_addr = (uint32_t)(uintptr_t)my_ring;
     const int64_t tstride = (int64_t)wpr * 16 * DI;  // elements between this wavefront's tiles
@@ -243,10 +244,19 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_dma(int Tq, int N, int
         const int slot = i % S::STAGES;
         const bool whole = (int64_t)t * 16 + 16 <= nv;
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the slot are done
+        // paged: the tile's 16 rows lie in one page (pages are multiples of 16 rows)
+        const int64_t prow = kl.ptab ? ((int64_t)pl[((int64_t)t * 16) >> kl.pshift] << kl.pshift) |
+                                           (((int64_t)t * 16) & ((1 << kl.pshift) - 1))
+                                     : 0;
 #pragma unroll
         for (int ip = 0; ip < S::IPT; ++ip) {
             const bf16_t *src = src0[ip] + i * tstride;
-            if (!whole) {
+            if (kl.ptab) {
+                const int byte = ip * 1024 + lane * 16;
+                const int r = byte / S::RB, pos = (byte % S::RB) / 16;
+                const int64_t rr = whole ? r : min((int64_t)t * 16 + r, nv - 1) - (int64_t)t * 16;
+                src = kI + (prow + rr) * DI + S::swz(r, pos) * 8;
+            } else if (!whole) {
                 const int byte = ip * 1024 + lane * 16;
                 const int r = byte / S::RB, pos = (byte % S::RB) / 16;
                 src = kb + min((int64_t)t * 16 + r, nv - 1) * DI + S::swz(r, pos) * 8;
@@ -260,6 +270,10 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_dma(int Tq, int N, int
         *(u32x4 *)(qs + i * 8) = *(const u32x4 *)(qI + row * HI * DI + i * 8);
     if (hist)
         for (int i = threadIdx.x; i < kTopkBins; i += kIdxWaves * 64) bh[i] = 0;
+    if (kl.ptab)
+        for (int i = threadIdx.x; i < (int)min((nv + (1 << kl.pshift) - 1) >> kl.pshift, (int64_t)kl.pstride);
+             i += kIdxWaves * 64)
+            pl[i] = (int32_t)kl.page_of(b, i);
     float wgt[MB][4];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -341,7 +355,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_dma(int Tq, int N, int
 
 template <int DI, int MB>
 static hipError_t launch_dma(int B, int Tq, int N, int HI, int m, QPos q_pos0, const void *qI, const float *w,
-                             const void *kI, int64_t k_bs, float *scores, int64_t s_stride, float *scores2,
+                             const void *kI, RowMap k_bs, float *scores, int64_t s_stride, float *scores2,
                              uint32_t *hist, hipStream_t st) {
     using S = IdxDma<DI>;
     static const hipError_t attr = hipFuncSetAttribute((const void *)k_index_dma<DI, MB>,
@@ -362,7 +376,7 @@ static hipError_t launch_dma(int B, int Tq, int N, int HI, int m, QPos q_pos0, c
 
 template <typename T, int DI, int MB>
 static hipError_t launch_t(int B, int Tq, int N, int HI, int m, QPos q_pos0, const void *qI, const float *w,
-                           const void *kI, int64_t k_bs, float *scores, int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
+                           const void *kI, RowMap k_bs, float *scores, int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
     const int64_t rows = (int64_t)B * Tq;
     const int64_t batches = (N + 63) / 64;  // batches of four 16-entry tiles
     // aim for ~2048 wavefronts in flight (8 per CU) when there are few queries
@@ -372,7 +386,7 @@ static hipError_t launch_t(int B, int Tq, int N, int HI, int m, QPos q_pos0, con
     const int64_t items = rows * chunks;
     const int64_t blocks = (items + 3) / 4;
     hipLaunchKernelGGL((k_index_scores<T, DI, MB>), dim3((unsigned)blocks), dim3(256), 0, st, Tq, N, HI, m, q_pos0,
-                       items, (int)chunks, (const T *)qI, w, (const T *)kI, k_bs, scores, s_stride,
+                       items, (int)chunks, (const T *)qI, w, (const T *)kI, k_bs.bstride, scores, s_stride,
                        scores2, hist);
     return hipGetLastError();
 }
@@ -533,7 +547,7 @@ __global__ __launch_bounds__(kPreWaves * 64) void k_index_prefill(int Tq, int N,
 
 template <int DI, int MB>
 static hipError_t launch_prefill(int B, int Tq, int N, int HI, int m, QPos q_pos0, const void *qI, const float *w,
-                                 const void *kI, int64_t k_bs, float *scores, int64_t s_stride, float *scores2,
+                                 const void *kI, RowMap k_bs, float *scores, int64_t s_stride, float *scores2,
                                  uint32_t *hist, hipStream_t st) {
     using S = IdxPre<DI>;
     static const hipError_t attr = hipFuncSetAttribute((const void *)k_index_prefill<DI, MB>,
@@ -541,17 +555,17 @@ static hipError_t launch_prefill(int B, int Tq, int N, int HI, int m, QPos q_pos
     if (attr != hipSuccess) return attr;
     const int bps = (Tq + kPreWaves - 1) / kPreWaves;
     hipLaunchKernelGGL((k_index_prefill<DI, MB>), dim3((unsigned)((int64_t)B * bps)), dim3(kPreWaves * 64), S::LDS,
-                       st, Tq, N, HI, m, q_pos0, bps, (const bf16_t *)qI, w, (const bf16_t *)kI, k_bs, scores,
+                       st, Tq, N, HI, m, q_pos0, bps, (const bf16_t *)qI, w, (const bf16_t *)kI, k_bs.bstride, scores,
                        s_stride, scores2, hist);
     return hipGetLastError();
 }
 
 template <typename T, int DI>
 static hipError_t launch_di(int B, int Tq, int N, int HI, int m, QPos q_pos0, const void *qI, const float *w,
-                            const void *kI, int64_t k_bs, float *scores, int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
+                            const void *kI, RowMap k_bs, float *scores, int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
     if constexpr (sizeof(T) == 2) {
-        // many queries per sequence: the query-blocked kernel
-        if (Tq >= kPreMinQueries) {
+        // many queries per sequence: the query-blocked kernel (contiguous keys only)
+        if (Tq >= kPreMinQueries && !k_bs.ptab) {
             if (HI <= 16) return launch_prefill<DI, 1>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride,
                                                        scores2, hist, st);
             if (HI <= 32) return launch_prefill<DI, 2>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride,
@@ -574,7 +588,7 @@ static hipError_t launch_di(int B, int Tq, int N, int HI, int m, QPos q_pos0, co
 
 template <typename T>
 static hipError_t launch_dt(int B, int Tq, int N, int HI, int dI, int m, QPos q_pos0, const void *qI,
-                            const float *w, const void *kI, int64_t k_bs, float *scores, int64_t s_stride, float *scores2,
+                            const float *w, const void *kI, RowMap k_bs, float *scores, int64_t s_stride, float *scores2,
                             uint32_t *hist, hipStream_t st) {
     switch (dI) {
         case 32: return launch_di<T, 32>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride, scores2,
@@ -587,7 +601,7 @@ static hipError_t launch_dt(int B, int Tq, int N, int HI, int dI, int m, QPos q_
 }
 
 hipError_t launch_index_scores(int dt, int B, int Tq, int N, int HI, int dI, int m, QPos q_pos0, const void *qI,
-                               const float *w, const void *kI, int64_t k_bs, float *scores, int64_t s_stride, float *scores2,
+                               const float *w, const void *kI, RowMap k_bs, float *scores, int64_t s_stride, float *scores2,
                                uint32_t *hist, hipStream_t st) {
     if (dt == 0) return launch_dt<float>(B, Tq, N, HI, dI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride,
                                           scores2, hist, st);

@@ -38,7 +38,7 @@ hipError_t launch_compress(int dt, int B, int G, int m, int d, const void *raw, 
 // ragged batches: per sequence, the group completed by its newest token (position pos[b]), read out of
 // mirrored raw / logit rings of `ring` positions, into entry row (pos[b]+1)/m - 1 when below out_rows
 hipError_t launch_compress_ragged(int dt, int B, int m, int d, const int64_t *pos, const void *raw, int64_t raw_bs,
-                                  const float *logits, int64_t log_bs, int64_t ring, void *out, int64_t out_bs,
+                                  const float *logits, int64_t log_bs, int64_t ring, void *out, RowMap out_map,
                                   int64_t out_rows, hipStream_t st);
 // logits: [B][G*m][d] f32 (per channel), batch stride log_bs elements
 hipError_t launch_compress_channels(int dt, int B, int G, int m, int d, const void *raw, int64_t raw_bs,
@@ -47,8 +47,9 @@ hipError_t launch_compress_channels(int dt, int B, int G, int m, int d, const vo
 
 // scores: [rows][s_stride] (s_stride >= N); scores2: optional second copy,
 // [rows][N]; hist: optional [rows, kTopkBins] counts, must be zero on entry
+// k_bs: the key cache's rows (a batch stride, or a page table: d_I = 128 bf16 only)
 hipError_t launch_index_scores(int dt, int B, int Tq, int N, int HI, int dI, int m, QPos q_pos0, const void *qI,
-                               const float *w, const void *kI, int64_t k_bs, float *scores, int64_t s_stride,
+                               const float *w, const void *kI, RowMap k_bs, float *scores, int64_t s_stride,
                                float *scores2, uint32_t *hist, hipStream_t st);
 
 // MXFP4 operands (32-element blocks, one E8M0 scale byte each, E2M1 codes two
@@ -60,7 +61,7 @@ hipError_t launch_mx4_quantize(int dt, int64_t n_blocks, const void *x, uint8_t 
 // quantised inside the kernel; keys as codes [B][k_bs rows][dI/2] and scales
 // [B][k_bs rows][dI/32]; outputs as launch_index_scores
 hipError_t launch_index_mx4(int dt, int B, int Tq, int N, int HI, int dI, int m, QPos q_pos0, const void *qI,
-                            const float *w, const uint8_t *kc, const uint8_t *ks, int64_t k_bs, float *scores,
+                            const float *w, const uint8_t *kc, const uint8_t *ks, RowMap k_bs, float *scores,
                             int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st);
 
 // row stride of the score rows the top-k reads: N rounded up to 64 floats, so
@@ -82,6 +83,7 @@ struct AppendJob {
     const int64_t *pos;  // optional per-batch position added to pos0
     int64_t n, row_bytes, src_bs, dst_bs, dst_rows, pos0, ring, every;
     int vw, B;
+    RowMap dmap;         // with a page table: destination rows of a paged cache (ring == 0)
 };
 struct AppendJobs {
     AppendJob j[kMaxAppendJobs];
@@ -115,7 +117,7 @@ int mqa_choose_splits(int64_t rows, int64_t n_rows_max, int d, int *tiles_per_sp
 // ws: split-K partials, rows*n_splits*H*(d+2) floats (unused when n_splits == 1)
 // raw_ring: 0 -> raw row r is position raw_pos0 + r; R > 0 -> position p is raw row p mod R
 hipError_t launch_mqa(int dt, int B, int Tq, int H, int d, int N, int m, int k, int W, QPos q_pos0, float scale,
-                      const void *q, const void *entries, int64_t e_bs, const int32_t *idx, const void *raw,
+                      const void *q, const void *entries, RowMap e_bs, const int32_t *idx, const void *raw,
                       int64_t raw_bs, int64_t raw_pos0, int64_t raw_ring, float *out, float *lse, float *ws,
                       int n_splits, int tiles_per_split, hipStream_t st);
 

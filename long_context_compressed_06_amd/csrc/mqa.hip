@@ -37,7 +37,8 @@ namespace csa {
 
 struct MqaArgs {
     int Tq, H, N, m, k, W, n_splits, tiles_per_split;
-    int64_t q_pos0, raw_pos0, e_bs, raw_bs;
+    int64_t q_pos0, raw_pos0, raw_bs;
+    RowMap em;           // entry rows (a batch stride or a page table)
     const int64_t *pos;  // optional: sequence b's query position (ragged batches, Tq = 1)
     int64_t raw_ring;    // 0: raw rows are positions raw_pos0 ..; R: position p is ring row p mod R
     float scale;
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(kMqaThreads) void k_mqa(const MqaArgs a) {
     }
 
     // resolve the split's row addresses once (nullptr = masked row)
-    const T *ent_b = (const T *)a.entries + b * a.e_bs;
+    const T *ent = (const T *)a.entries;
     const T *raw_b = (const T *)a.raw + b * a.raw_bs;
     const int nr = ntiles * S::TR;
     for (int i0 = 0; i0 < nr; i0 += kMqaThreads) {
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(kMqaThreads) void k_mqa(const MqaArgs a) {
             const int64_t r = tile_lo * S::TR + i;
             if (r < n_slots) {
                 const int64_t j = a.k > 0 ? (int64_t)a.idx[row * a.k + r] : r;
-                if (j >= 0 && j < nv) src = ent_b + j * D;
+                if (j >= 0 && j < nv) src = ent + a.em.offset(b, j, D);
             } else if (r < n_rows) {
                 const int64_t p = w0 + (r - n_slots);
                 src = raw_b + (a.raw_ring ? p % a.raw_ring : p - a.raw_pos0) * D;
@@ -523,14 +524,14 @@ static hipError_t launch_mqa_dt(int d, const MqaArgs &a, int64_t rows, hipStream
 }
 
 hipError_t launch_mqa(int dt, int B, int Tq, int H, int d, int N, int m, int k, int W, QPos q_pos0, float scale,
-                      const void *q, const void *entries, int64_t e_bs, const int32_t *idx, const void *raw,
+                      const void *q, const void *entries, RowMap e_bs, const int32_t *idx, const void *raw,
                       int64_t raw_bs, int64_t raw_pos0, int64_t raw_ring, float *out, float *lse, float *ws,
                       int n_splits, int tiles_per_split, hipStream_t st) {
     const int64_t rows = (int64_t)B * Tq;
     MqaArgs a;
     a.Tq = Tq; a.H = H; a.N = N; a.m = m; a.k = k; a.W = W;
     a.n_splits = n_splits; a.tiles_per_split = tiles_per_split;
-    a.q_pos0 = q_pos0.q_pos0; a.pos = q_pos0.pos; a.raw_ring = raw_ring; a.raw_pos0 = raw_pos0; a.e_bs = e_bs; a.raw_bs = raw_bs; a.scale = scale;
+    a.q_pos0 = q_pos0.q_pos0; a.pos = q_pos0.pos; a.raw_ring = raw_ring; a.raw_pos0 = raw_pos0; a.em = e_bs; a.raw_bs = raw_bs; a.scale = scale;
     a.q = q; a.entries = entries; a.raw = raw; a.idx = idx; a.out = out; a.lse = lse;
     a.part_o = ws;
     a.part_ml = ws ? ws + rows * n_splits * H * (int64_t)d : nullptr;

@@ -268,7 +268,8 @@ constexpr int kMx4Stages = 4;
 constexpr int kMx4Slot = 1024 + 64;  // codes of 16 rows of 64 bytes, then their 16 scale dwords
 constexpr int kMx4Ring = kMx4Waves * kMx4Stages * kMx4Slot;
 constexpr int kMx4QBlocks = 64 * 4;  // the query's 32-element blocks: 64 heads x 4
-constexpr int kMx4Lds = kMx4Ring + kMx4QBlocks * (16 + 4) + kTopkBins * 4;  // ring, query codes + scales, histogram
+// ring, query codes + scales, histogram, page list (paged caches)
+constexpr int kMx4Lds = kMx4Ring + kMx4QBlocks * (16 + 4) + kTopkBins * 4 + kMaxPagesPerSeq * 4;
 
 // chunk position of row r's 16-byte chunk ch (an involution): four rows share one swizzle
 __device__ __forceinline__ int mx4_swz(int r, int ch) { return ch ^ ((r >> 2) & 3); }
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(kMx4Waves * 64) void k_index_mx4_dma(int Tq, int N,
                                                                  int blocks_per_row, const T *__restrict__ qI,
                                                                  const float *__restrict__ w,
                                                                  const uint8_t *__restrict__ kc,
-                                                                 const uint8_t *__restrict__ ks, int64_t k_bs,
+                                                                 const uint8_t *__restrict__ ks, RowMap kl,
                                                                  float *__restrict__ scores, int64_t s_stride,
                                                                  float *__restrict__ scores2,
                                                                  uint32_t *__restrict__ hist) {
@@ -297,6 +298,7 @@ __global__ __launch_bounds__(kMx4Waves * 64) void k_index_mx4_dma(int Tq, int N,
     u32x4 *qcodes = (u32x4 *)(lds + kMx4Ring);                             // [head][block] 16 bytes
     uint32_t *qscale = (uint32_t *)(lds + kMx4Ring + kMx4QBlocks * 16);    // [head][block]
     uint32_t *bh = (uint32_t *)(lds + kMx4Ring + kMx4QBlocks * (16 + 4));
+    int32_t *pl = (int32_t *)(lds + kMx4Ring + kMx4QBlocks * (16 + 4) + kTopkBins * 4);  // the query's pages
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -315,8 +317,9 @@ __global__ __launch_bounds__(kMx4Waves * 64) void k_index_mx4_dma(int Tq, int N,
     const int n_all = tiles > gw ? (tiles - gw + wpr - 1) / wpr : 0;
     const int n_vis = vtiles > gw ? (vtiles - gw + wpr - 1) / wpr : 0;
 
-    const uint8_t *kcb = kc + b * k_bs * RB;
-    const uint8_t *ksb = ks + b * k_bs * KB;
+    const int64_t kb_rows = kl.ptab ? 0 : b * kl.bstride;
+    const uint8_t *kcb = kc + kb_rows * RB;
+    const uint8_t *ksb = ks + kb_rows * KB;
     unsigned char *my_ring = ring + wv * kMx4Stages * kMx4Slot;
     const uint32_t ring_addr = (uint32_t)(uintptr_t)my_ring;
     // this lane's chunk of a tile's codes: row r = lane / 4, position lane % 4 holding source chunk swz(r, pos)
@@ -331,7 +334,14 @@ __global__ __launch_bounds__(kMx4Waves * 64) void k_index_mx4_dma(int Tq, int N,
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the slot are done
         const uint8_t *cs = csrc0 + i * tstride_c;
         const uint8_t *ss = ssrc0 + (int64_t)i * wpr * 16 * KB;
-        if (!whole) {
+        if (kl.ptab) {  // the tile's 16 rows lie in one page (pages are multiples of 16 rows)
+            const int64_t r0 = (int64_t)t * 16;
+            const int64_t prow = ((int64_t)pl[r0 >> kl.pshift] << kl.pshift) | (r0 & ((1 << kl.pshift) - 1));
+            const int64_t rc = whole ? cr : min(r0 + cr, nv - 1) - r0;
+            const int64_t rs = whole ? (lane & 15) : min(r0 + (lane & 15), nv - 1) - r0;
+            cs = kc + (prow + rc) * RB + mx4_swz(cr, cpos) * 16;
+            ss = ks + (prow + rs) * KB;
+        } else if (!whole) {
             cs = kcb + min((int64_t)t * 16 + cr, nv - 1) * RB + mx4_swz(cr, cpos) * 16;
             ss = ksb + min((int64_t)t * 16 + (lane & 15), nv - 1) * KB;
         }
@@ -340,6 +350,13 @@ __global__ __launch_bounds__(kMx4Waves * 64) void k_index_mx4_dma(int Tq, int N,
         if (lane < 16) lds_dma4_nt_mx4(base + 1024, ss);
     };
 
+    // paged caches: the query's page list first (the tile addresses need it)
+    if (kl.ptab) {
+        for (int i = threadIdx.x; i < (int)min((nv + (1 << kl.pshift) - 1) >> kl.pshift, (int64_t)kl.pstride);
+             i += kMx4Waves * 64)
+            pl[i] = (int32_t)kl.page_of(b, i);
+        __syncthreads();
+    }
     // the first tiles stream in while the query is quantised (the ring is
     // disjoint from the query and histogram areas)
     for (int i = 0; i < kMx4Stages - 1 && i < n_vis; ++i) issue(i);
@@ -428,7 +445,7 @@ __global__ __launch_bounds__(kMx4Waves * 64) void k_index_mx4_dma(int Tq, int N,
 
 template <typename T, int MB>
 static hipError_t launch_mx4_dma(int B, int Tq, int N, int HI, int m, QPos q_pos0, const void *qI, const float *w,
-                                 const uint8_t *kc, const uint8_t *ks, int64_t k_bs, float *scores, int64_t s_stride,
+                                 const uint8_t *kc, const uint8_t *ks, RowMap k_bs, float *scores, int64_t s_stride,
                                  float *scores2, uint32_t *hist, hipStream_t st) {
     static const hipError_t attr = hipFuncSetAttribute((const void *)k_index_mx4_dma<T, MB>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kMx4Lds);
@@ -459,7 +476,7 @@ hipError_t launch_mx4_quantize(int dt, int64_t n_blocks, const void *x, uint8_t 
 
 template <typename T, int DI, int MB>
 static hipError_t launch_mx4_t(int B, int Tq, int N, int HI, int m, QPos q_pos0, const void *qI, const float *w,
-                               const uint8_t *kc, const uint8_t *ks, int64_t k_bs, float *scores, int64_t s_stride,
+                               const uint8_t *kc, const uint8_t *ks, RowMap k_bs, float *scores, int64_t s_stride,
                                float *scores2, uint32_t *hist, hipStream_t st) {
     const int64_t rows = (int64_t)B * Tq;
     const int64_t batches = (N + 63) / 64;  // batches of four 16-entry tiles
@@ -470,13 +487,13 @@ static hipError_t launch_mx4_t(int B, int Tq, int N, int HI, int m, QPos q_pos0,
     const int64_t items = rows * chunks;
     const int64_t blocks = (items + 3) / 4;
     hipLaunchKernelGGL((k_index_mx4<T, DI, MB>), dim3((unsigned)blocks), dim3(256), 0, st, Tq, N, HI, m, q_pos0,
-                       items, (int)chunks, (const T *)qI, w, kc, ks, k_bs, scores, s_stride, scores2, hist);
+                       items, (int)chunks, (const T *)qI, w, kc, ks, k_bs.bstride, scores, s_stride, scores2, hist);
     return hipGetLastError();
 }
 
 template <typename T, int DI>
 static hipError_t launch_mx4_di(int B, int Tq, int N, int HI, int m, QPos q_pos0, const void *qI, const float *w,
-                                const uint8_t *kc, const uint8_t *ks, int64_t k_bs, float *scores, int64_t s_stride,
+                                const uint8_t *kc, const uint8_t *ks, RowMap k_bs, float *scores, int64_t s_stride,
                                 float *scores2, uint32_t *hist, hipStream_t st) {
     if (HI <= 16)
         return launch_mx4_t<T, DI, 1>(B, Tq, N, HI, m, q_pos0, qI, w, kc, ks, k_bs, scores, s_stride, scores2, hist,
@@ -489,7 +506,7 @@ static hipError_t launch_mx4_di(int B, int Tq, int N, int HI, int m, QPos q_pos0
 
 template <typename T>
 static hipError_t launch_mx4_dt(int B, int Tq, int N, int HI, int dI, int m, QPos q_pos0, const void *qI,
-                                const float *w, const uint8_t *kc, const uint8_t *ks, int64_t k_bs, float *scores,
+                                const float *w, const uint8_t *kc, const uint8_t *ks, RowMap k_bs, float *scores,
                                 int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
     if (dI == 128 && ((uintptr_t)ks % 4) == 0) {  // (scale rows move as dwords)
         if (HI <= 16)
@@ -515,7 +532,7 @@ static hipError_t launch_mx4_dt(int B, int Tq, int N, int HI, int dI, int m, QPo
 }
 
 hipError_t launch_index_mx4(int dt, int B, int Tq, int N, int HI, int dI, int m, QPos q_pos0, const void *qI,
-                            const float *w, const uint8_t *kc, const uint8_t *ks, int64_t k_bs, float *scores,
+                            const float *w, const uint8_t *kc, const uint8_t *ks, RowMap k_bs, float *scores,
                             int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
     if (dt == 0)
         return launch_mx4_dt<float>(B, Tq, N, HI, dI, m, q_pos0, qI, w, kc, ks, k_bs, scores, s_stride, scores2, hist,

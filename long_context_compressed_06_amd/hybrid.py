@@ -25,12 +25,14 @@ def alternating(n_layers: int, csa: dict, hca: dict) -> list:
 class HybridStack:
     def __init__(self, specs: list, *, B: int, H: int, d: int, W: int, capacity: int, dtype=torch.bfloat16,
                  device="cuda"):
-        """specs: per layer a dict with mode ("csa"/"hca"), m, and for CSA k, HI, dI (optional index_fmt)."""
+        """specs: per layer a dict with mode ("csa"/"hca"), m, and for CSA k, HI, dI (optional index_fmt;
+        optional page_rows for paged caches)."""
         self.B = B
         self.layers = [RaggedLayer(mode=s["mode"], B=B, H=H, d=d, m=s["m"], W=W, capacity=capacity, dtype=dtype,
                                    k=s.get("k", 0), HI=s.get("HI", 0), dI=s.get("dI", 0),
-                                   index_fmt=s.get("index_fmt", "elem"), scale=s.get("scale"), device=device)
-                       for s in specs]
+                                   index_fmt=s.get("index_fmt", "elem"), scale=s.get("scale"),
+                                   page_rows=s.get("page_rows", 0), device=device, seed=i)
+                       for i, s in enumerate(specs)]
 
     def step(self, inputs: list) -> list:
         """inputs[l]: the keyword arguments of layer l's RaggedLayer.step.  Returns each layer's out."""

@@ -20,6 +20,12 @@ A step (new token of sequence b at position t_b = pos[b]):
   5. pos += 1.
 Ring of R = max(W, m) positions: the window of the newest token and the
 tokens of the group it completes.
+
+Paged caches (page_rows = P, a power of two >= 16): the entries and index
+keys of all sequences live in pools of P-row pages, sequence b's entry j in
+row j mod P of page page_table[b, j // P]; one table serves both caches.
+By default each sequence gets its pages from a shuffled free list up front
+(assign_pages hands out other layouts).
 """
 from __future__ import annotations
 
@@ -33,7 +39,7 @@ from . import (csa_append_rows, csa_append_rows_multi, csa_mx4_quantize, csa_pos
 class RaggedLayer:
     def __init__(self, *, mode: str, B: int, H: int, d: int, m: int, W: int, capacity: int, dtype=torch.bfloat16,
                  k: int = 0, HI: int = 0, dI: int = 0, index_fmt: str = "elem", scale: float | None = None,
-                 device="cuda"):
+                 page_rows: int = 0, n_pages: int = 0, device="cuda", seed: int = 0):
         assert mode in ("csa", "hca") and index_fmt in ("elem", "mx4")
         if mode == "csa" and (k < 1 or HI < 1 or dI < 1):
             raise ValueError("CSA needs k, HI and dI")
@@ -45,15 +51,29 @@ class RaggedLayer:
         self.pos = torch.zeros((B,), dtype=torch.int64, device=device)
         self.raw_ring = torch.zeros((B, 2 * self.R, d), dtype=dtype, device=device)
         self.logit_ring = torch.zeros((B, 2 * self.R, 1), dtype=torch.float32, device=device)
-        self.entries = torch.zeros((B, self.cap_e, d), dtype=dtype, device=device)
+        self.page_rows = page_rows
+        if page_rows:
+            self.max_pages = -(-self.cap_e // page_rows)
+            self.n_pages = n_pages or B * self.max_pages
+            lead = (self.n_pages, page_rows)
+            self.page_table = torch.zeros((B, self.max_pages), dtype=torch.int32, device=device)
+            if self.n_pages >= B * self.max_pages:  # every sequence its own pages, interleaved in the pool
+                g = torch.Generator().manual_seed(seed)
+                perm = torch.randperm(self.n_pages, generator=g)[:B * self.max_pages].to(torch.int32)
+                self.page_table.copy_(perm.reshape(B, self.max_pages))
+            self.pages = (self.page_table, page_rows, self.n_pages)
+        else:
+            lead = (B, self.cap_e)
+            self.pages = None
+        self.entries = torch.zeros(lead + (d,), dtype=dtype, device=device)
         if mode == "csa":
             if index_fmt == "mx4":
-                self.k_codes = torch.zeros((B, self.cap_e, dI // 2), dtype=torch.uint8, device=device)
-                self.k_scales = torch.zeros((B, self.cap_e, dI // 32), dtype=torch.uint8, device=device)
+                self.k_codes = torch.zeros(lead + (dI // 2,), dtype=torch.uint8, device=device)
+                self.k_scales = torch.zeros(lead + (dI // 32,), dtype=torch.uint8, device=device)
                 self._codes = torch.empty((B, 1, dI // 2), dtype=torch.uint8, device=device)
                 self._scales = torch.empty((B, 1, dI // 32), dtype=torch.uint8, device=device)
             else:
-                self.k_idx = torch.zeros((B, self.cap_e, dI), dtype=dtype, device=device)
+                self.k_idx = torch.zeros(lead + (dI,), dtype=dtype, device=device)
             nb = index_topk_workspace_bytes(B, 1, self.cap_e, HI, k)
             self.idx_ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=device)
             self.topk_idx = torch.empty((B, 1, k), dtype=torch.int32, device=device)
@@ -62,6 +82,19 @@ class RaggedLayer:
         self.mqa_ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=device)
         self.out = torch.empty((B, 1, H, d), dtype=torch.float32, device=device)
         self.lse = torch.empty((B, 1, H), dtype=torch.float32, device=device)
+
+    def assign_pages(self, b: int, page_ids):
+        """Give sequence b the listed pages of the pool (its entries 0 .. P-1 in the first, and so on)."""
+        ids = torch.as_tensor(page_ids, dtype=torch.int32)
+        self.page_table[b, :ids.numel()] = ids.to(self.page_table.device)
+
+    def _cache_rows(self, t: torch.Tensor, b: int, n: int):
+        """Sequence b's first n cache rows of t as a list of (view, lo, hi) pieces (one per page when paged)."""
+        if not self.page_rows:
+            return [(t[b, :n], 0, n)]
+        P = self.page_rows
+        ids = self.page_table[b].tolist()
+        return [(t[ids[i // P], :min(P, n - i)], i, min(i + P, n)) for i in range(0, n, P)]
 
     def seed(self, b: int, pos_b: int, raw_tail: torch.Tensor, logits_tail: torch.Tensor,
              entries: torch.Tensor | None = None, k_idx: torch.Tensor | None = None):
@@ -78,13 +111,18 @@ class RaggedLayer:
             csa_append_rows(raw_tail[None], self.raw_ring[b:b + 1], pos_b - L, ring=self.R)
             csa_append_rows(logits_tail.reshape(1, L, 1), self.logit_ring[b:b + 1], pos_b - L, ring=self.R)
         if n_e:
-            self.entries[b, :n_e] = entries
+            for view, lo, hi in self._cache_rows(self.entries, b, n_e):
+                view.copy_(entries[lo:hi])
             if self.mode == "csa":
                 if self.index_fmt == "mx4":
                     c, s = csa_mx4_quantize(k_idx.contiguous())
-                    self.k_codes[b, :n_e], self.k_scales[b, :n_e] = c, s
+                    for view, lo, hi in self._cache_rows(self.k_codes, b, n_e):
+                        view.copy_(c[lo:hi])
+                    for view, lo, hi in self._cache_rows(self.k_scales, b, n_e):
+                        view.copy_(s[lo:hi])
                 else:
-                    self.k_idx[b, :n_e] = k_idx
+                    for view, lo, hi in self._cache_rows(self.k_idx, b, n_e):
+                        view.copy_(k_idx[lo:hi])
         self.pos[b] = pos_b
 
     def step(self, raw: torch.Tensor, logits: torch.Tensor, q: torch.Tensor, k_idx_tok: torch.Tensor | None = None,
@@ -96,25 +134,29 @@ class RaggedLayer:
         B = self.B
         jobs = [(raw, self.raw_ring, 0, self.R, self.pos), (logits.reshape(B, 1, 1), self.logit_ring, 0, self.R, self.pos)]
         if self.mode == "csa":
+            pg = self.pages
             if self.index_fmt == "mx4":
                 csa_mx4_quantize(k_idx_tok, codes=self._codes, scales=self._scales)
-                jobs += [(self._codes, self.k_codes, 0, 0, self.pos, self.m),
-                         (self._scales, self.k_scales, 0, 0, self.pos, self.m)]
+                jobs += [(self._codes, self.k_codes, 0, 0, self.pos, self.m, pg),
+                         (self._scales, self.k_scales, 0, 0, self.pos, self.m, pg)]
             else:
-                jobs.append((k_idx_tok, self.k_idx, 0, 0, self.pos, self.m))
+                jobs.append((k_idx_tok, self.k_idx, 0, 0, self.pos, self.m, pg))
         csa_append_rows_multi(jobs)
-        csa_ragged_compress(self.raw_ring, self.logit_ring[..., 0], self.R, self.m, self.pos, self.entries)
+        csa_ragged_compress(self.raw_ring, self.logit_ring[..., 0], self.R, self.m, self.pos, self.entries,
+                            pages=self.pages)
         if self.mode == "csa":
             if self.index_fmt == "mx4":
                 csa_ragged_index_topk_mx4(q_idx, w_idx, self.k_codes, self.k_scales, self.cap_e, self.m, self.k,
-                                          self.pos, topk_idx=self.topk_idx, workspace=self.idx_ws)
+                                          self.pos, topk_idx=self.topk_idx, workspace=self.idx_ws, pages=self.pages)
             else:
                 csa_ragged_index_topk(q_idx, w_idx, self.k_idx, self.cap_e, self.m, self.k, self.pos,
-                                      topk_idx=self.topk_idx, workspace=self.idx_ws)
+                                      topk_idx=self.topk_idx, workspace=self.idx_ws, pages=self.pages)
             csa_ragged_sparse_mqa(q, self.entries, self.topk_idx, self.raw_ring, self.R, self.cap_e, self.m, self.W,
-                                  self.pos, scale=self.scale, out=self.out, lse=self.lse, workspace=self.mqa_ws)
+                                  self.pos, scale=self.scale, out=self.out, lse=self.lse, workspace=self.mqa_ws,
+                                  pages=self.pages)
         else:
             hca_ragged_dense_mqa(q, self.entries, self.raw_ring, self.R, self.cap_e, self.m, self.W, self.pos,
-                                 scale=self.scale, out=self.out, lse=self.lse, workspace=self.mqa_ws)
+                                 scale=self.scale, out=self.out, lse=self.lse, workspace=self.mqa_ws,
+                                 pages=self.pages)
         csa_positions_advance(self.pos, 1)
         return self.out

@@ -237,7 +237,7 @@ def test_ragged_calls_reject_bad_arguments(L):
     def comp(**kw):
         a = dict(args, **kw)
         return rc(a["dt"], a["B"], a["m"], a["d"], a["pos"], a["raw"], a["rbs"], a["lg"], a["lbs"], a["ring"],
-                  a["out"], a["obs"], a["orows"], None)
+                  a["out"], a["obs"], a["orows"], a.get("pt"), a.get("mp", 0), a.get("pr", 0), a.get("npg", 0), None)
 
     assert comp(m=0) == -6 and comp(d=100) == -6
     assert comp(ring=3) == -1                 # a group does not fit the ring
@@ -246,20 +246,33 @@ def test_ragged_calls_reject_bad_arguments(L):
     assert comp(pos=P + 4) == -3
     assert comp(out=P + 0x10000 + 256) == -1  # out overlaps the raw ring
     assert comp(B=0, pos=None) == 0
+    # paged destination: page size a power of two >= 16, at most 1024 pages per sequence covering the rows
+    assert comp(pt=P + 0x300000, mp=4, pr=24, npg=8) == -6
+    assert comp(pt=P + 0x300000, mp=2000, pr=16, npg=8) == -6
+    assert comp(pt=P + 0x300000, mp=2, pr=16, npg=8) == -1      # 32 rows do not cover out_rows = 64
+    assert comp(pt=P + 0x300000, mp=4, pr=16, npg=0) == -1
+    assert comp(pt=P + 0x300002, mp=4, pr=16, npg=8) == -3
     ws = csa.index_topk_workspace_bytes(2, 1, 256, 64, 64)
-    ri = lambda pos=P, **kw: L.csa_ragged_index_topk(1, 2, 256, 64, 128, 4, kw.get("k", 64), pos, P + 0x10000,
-                                                     P + 0x40000, P + 0x80000, 256 * 128, P + 0x200000, None,
-                                                     P + 0x300000, kw.get("wsb", ws), None)
+    ri = lambda pos=P, **kw: L.csa_ragged_index_topk(kw.get("dt", 1), 2, 256, 64, kw.get("dI", 128), 4,
+                                                     kw.get("k", 64), pos, P + 0x10000, P + 0x40000, P + 0x80000,
+                                                     256 * 128, kw.get("pt"), kw.get("mp", 0), kw.get("pr", 0),
+                                                     kw.get("npg", 0), P + 0x200000, None, P + 0x300000,
+                                                     kw.get("wsb", ws), None)
     assert ri(pos=None) == -1
     assert ri(pos=P + 4) == -3
     assert ri(k=0) == -6
     assert ri(wsb=ws - 1) == -4
+    assert ri(pt=P + 0x1000000, mp=16, pr=16, npg=32, dI=64) == -6   # paged keys need d_I = 128
+    assert ri(pt=P + 0x1000000, mp=16, pr=16, npg=32, dt=0) == -6    # ... in bf16
+    assert ri(pt=P + 0x1000000, mp=8, pr=16, npg=32) == -1           # 128 rows do not cover N = 256
     rm = lambda **kw: L.csa_ragged_sparse_mqa(1, 2, 64, 512, 1000, 4, 64, kw.get("W", 128), kw.get("pos", P), 0.04,
-                                              P + 0x10000, P + 0x100000, 1000 * 512, P + 0x2000000, P + 0x3000000,
+                                              P + 0x10000, P + 0x100000, 1000 * 512, kw.get("pt"), kw.get("mp", 0),
+                                              kw.get("pr", 0), kw.get("npg", 0), P + 0x2000000, P + 0x3000000,
                                               2 * 128 * 512, kw.get("ring", 128), P + 0x4000000, None, None, 0, None)
     assert rm(pos=None) == -1
     assert rm(ring=0) == -1
     assert rm(W=129) == -1                    # the ring cannot hold the window
+    assert rm(pt=P + 0x5000000, mp=8, pr=64, npg=40) == -1   # 512 rows do not cover N = 1000
 
 
 def test_stream_read_rejects_bad_arguments(L):

@@ -54,6 +54,7 @@ class Case:
     dI: int = 0
     index_fmt: str = "elem"
     seed: int = 0
+    page_rows: int = 0
 
 
 CASES = [
@@ -63,6 +64,14 @@ CASES = [
          index_fmt="mx4", seed=96200),
     Case("csa_ragged_bf16_d512", "csa", "bf16", (700, 1029), 5, 4, 512, 16, 128, k=64, HI=64, dI=128, seed=96300),
     Case("hca_ragged_bf16", "hca", "bf16", (126, 250, 509), 6, 128, 128, 8, 128, seed=96400),
+    # paged caches (pages interleaved across sequences in one pool)
+    Case("csa_ragged_bf16_paged16", "csa", "bf16", (0, 37, 130, 401), 9, 4, 128, 8, 16, k=32, HI=8, dI=128,
+         seed=96500, page_rows=16),
+    Case("csa_ragged_bf16_fp4_indexer_paged32", "csa", "bf16", (5, 66, 203), 7, 4, 128, 8, 16, k=24, HI=16, dI=128,
+         index_fmt="mx4", seed=96600, page_rows=32),
+    Case("csa_ragged_bf16_d512_paged64", "csa", "bf16", (700, 1029), 5, 4, 512, 16, 128, k=64, HI=64, dI=128,
+         seed=96700, page_rows=64),
+    Case("hca_ragged_bf16_paged16", "hca", "bf16", (126, 250, 509), 6, 128, 128, 8, 128, seed=96800, page_rows=16),
 ]
 
 
@@ -92,7 +101,7 @@ def make_layer(csa, c: Case, seqs):
     tdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
     cap = max(c.positions) + c.steps + c.m
     layer = csa.RaggedLayer(mode=c.mode, B=B, H=c.H, d=c.d, m=c.m, W=c.W, capacity=cap, dtype=tdt, k=c.k, HI=c.HI,
-                            dI=c.dI, index_fmt=c.index_fmt, scale=c.d ** -0.5)
+                            dI=c.dI, index_fmt=c.index_fmt, scale=c.d ** -0.5, page_rows=c.page_rows, seed=c.seed)
     for b, (p, s) in enumerate(zip(c.positions, seqs)):
         layer.seed(b, p, s["tail"].cuda(), s["tail_logits"].cuda(), s["entries"].cuda(),
                    s["k_idx"].cuda() if c.mode == "csa" else None)
@@ -168,7 +177,8 @@ def test_ragged_decode(csa, c):
         ref, e_new = oracle_sequence_steps(c, b, seqs[b], new)
         n0 = c.positions[b] // c.m
         if e_new is not None:
-            assert_close(layer.entries[b, n0:n0 + e_new.shape[0]], e_new, c.dtype, f"seq {b} emitted entries")
+            got = torch.cat([v for v, _, _ in layer._cache_rows(layer.entries, b, n0 + e_new.shape[0])])[n0:]
+            assert_close(got, e_new, c.dtype, f"seq {b} emitted entries")
         go = np.stack([to_np(o[b, 0]) for o in outs])
         gl = np.stack([to_np(x[b, 0]) for x in lses])
         ro = np.stack([r["out"] for r in ref])
@@ -283,3 +293,27 @@ def test_hybrid_stack_alternating(csa):
         torch.cuda.synchronize()
         for le, lg in zip(eager.layers, graphed.layers):
             assert torch.equal(le.out, lg.out) and torch.equal(le.lse, lg.lse), j
+
+
+@pytest.mark.parametrize("c", [c for c in CASES if c.page_rows], ids=[c.name for c in CASES if c.page_rows])
+def test_ragged_paged_equals_contiguous(csa, c):
+    """The same decode with paged and with contiguous caches gives bit-identical outputs and cache rows."""
+    say(c, "paged vs contiguous")
+    seqs, new = draw(c)
+    paged = make_layer(csa, c, seqs)
+    flat = make_layer(csa, dataclasses.replace(c, page_rows=0), seqs)
+    for j in range(c.steps):
+        x = step_inputs(c, new, j)
+        paged.step(**x)
+        flat.step(**x)
+        torch.cuda.synchronize()
+        assert torch.equal(paged.out, flat.out) and torch.equal(paged.lse, flat.lse), j
+        if c.mode == "csa":
+            assert torch.equal(paged.topk_idx, flat.topk_idx), j
+    for b, p in enumerate(c.positions):
+        n = (p + c.steps) // c.m
+        got = torch.cat([v for v, _, _ in paged._cache_rows(paged.entries, b, n)])
+        assert torch.equal(got, flat.entries[b, :n])
+        if c.mode == "csa" and c.index_fmt == "elem":
+            got = torch.cat([v for v, _, _ in paged._cache_rows(paged.k_idx, b, n)])
+            assert torch.equal(got, flat.k_idx[b, :n])

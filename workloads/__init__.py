@@ -282,4 +282,9 @@ RAGGED = {
     # the same batch through one CSA layer
     "r1": RaggedStack("csa_decode_ragged_B32_ctx96K-158K", B=32, lengths=tuple(98304 + 2048 * b for b in range(32)),
                       d=512, H=64, W=128, n_layers=1, seed_base=8100),
+    # the same batch and layer with paged caches: entries and index keys in pages of 64 rows, each
+    # sequence's pages drawn from a shuffled pool
+    "r1p": RaggedStack("csa_decode_ragged_paged64_B32_ctx96K-158K", B=32,
+                       lengths=tuple(98304 + 2048 * b for b in range(32)), d=512, H=64, W=128, n_layers=1,
+                       csa=(("m", 4), ("k", 1024), ("HI", 64), ("dI", 128), ("page_rows", 64)), seed_base=8200),
 }
