@@ -192,7 +192,7 @@ __device__ __forceinline__ float sum_lane_groups(float x) {
     return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
-template <int DI, int MB>
+template <int DI, int MB, bool PAGED>
 __global__ __launch_bounds__(kIdxWaves * 64) void k_index_dma(int Tq, int N, int HI, int m, QPos q_pos0,
                                                                int blocks_per_row, const bf16_t *__restrict__ qI,
                                                                const float *__restrict__ w,
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_dma(int Tq, int N, int
     // ---- DMA of one tile into ring slot `slot`.  Lane addresses step by a
     // fixed stride from tile to tile; in the tile that holds the last visible
     // entry, rows past it reread that entry's row (their scores are masked).
-    const bf16_t *kb = kI + (kl.ptab ? 0 : b * kl.bstride);
+    const bf16_t *kb = kI + (PAGED ? 0 : b * kl.bstride);
     unsigned char *my_ring = ring + wv * S::STAGES * S::TB;
     const uint32_t ring_addr = (uint32_t)(uintptr_t)my_ring;
     const int64_t tstride = (int64_t)wpr * 16 * DI;  // elements between this wavefront's tiles
@@ -245,13 +245,13 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_dma(int Tq, int N, int
         const bool whole = (int64_t)t * 16 + 16 <= nv;
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the slot are done
         // paged: the tile's 16 rows lie in one page (pages are multiples of 16 rows)
-        const int64_t prow = kl.ptab ? ((int64_t)pl[((int64_t)t * 16) >> kl.pshift] << kl.pshift) |
+        const int64_t prow = PAGED ? ((int64_t)pl[((int64_t)t * 16) >> kl.pshift] << kl.pshift) |
                                            (((int64_t)t * 16) & ((1 << kl.pshift) - 1))
                                      : 0;
 #pragma unroll
         for (int ip = 0; ip < S::IPT; ++ip) {
             const bf16_t *src = src0[ip] + i * tstride;
-            if (kl.ptab) {
+            if constexpr (PAGED) {
                 const int byte = ip * 1024 + lane * 16;
                 const int r = byte / S::RB, pos = (byte % S::RB) / 16;
                 const int64_t rr = whole ? r : min((int64_t)t * 16 + r, nv - 1) - (int64_t)t * 16;
@@ -270,7 +270,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_dma(int Tq, int N, int
         *(u32x4 *)(qs + i * 8) = *(const u32x4 *)(qI + row * HI * DI + i * 8);
     if (hist)
         for (int i = threadIdx.x; i < kTopkBins; i += kIdxWaves * 64) bh[i] = 0;
-    if (kl.ptab)
+    if constexpr (PAGED)
         for (int i = threadIdx.x; i < (int)min((nv + (1 << kl.pshift) - 1) >> kl.pshift, (int64_t)kl.pstride);
              i += kIdxWaves * 64)
             pl[i] = (int32_t)kl.page_of(b, i);
@@ -353,13 +353,14 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_dma(int Tq, int N, int
     }
 }
 
-template <int DI, int MB>
-static hipError_t launch_dma(int B, int Tq, int N, int HI, int m, QPos q_pos0, const void *qI, const float *w,
-                             const void *kI, RowMap k_bs, float *scores, int64_t s_stride, float *scores2,
-                             uint32_t *hist, hipStream_t st) {
+template <int DI, int MB, bool PAGED>
+static hipError_t launch_dma_p(int B, int Tq, int N, int HI, int m, QPos q_pos0, const void *qI, const float *w,
+                               const void *kI, RowMap k_bs, float *scores, int64_t s_stride, float *scores2,
+                               uint32_t *hist, hipStream_t st) {
     using S = IdxDma<DI>;
-    static const hipError_t attr = hipFuncSetAttribute((const void *)k_index_dma<DI, MB>,
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
+    constexpr int lds = PAGED ? S::LDS : S::LDS - kMaxPagesPerSeq * 4;  // (the page list: paged keys only)
+    static const hipError_t attr = hipFuncSetAttribute((const void *)k_index_dma<DI, MB, PAGED>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (attr != hipSuccess) return attr;
     const int64_t rows = (int64_t)B * Tq;
     const int64_t tiles = (N + 15) / 16;
@@ -368,10 +369,21 @@ static hipError_t launch_dma(int B, int Tq, int N, int HI, int m, QPos q_pos0, c
     const int64_t max_bpr = (tiles + kIdxWaves - 1) / kIdxWaves;
     if (bpr > max_bpr) bpr = max_bpr;
     if (bpr < 1) bpr = 1;
-    hipLaunchKernelGGL((k_index_dma<DI, MB>), dim3((unsigned)(rows * bpr)), dim3(kIdxWaves * 64), S::LDS, st, Tq, N,
-                       HI, m, q_pos0, (int)bpr, (const bf16_t *)qI, w, (const bf16_t *)kI, k_bs, scores, s_stride,
-                       scores2, hist);
+    hipLaunchKernelGGL((k_index_dma<DI, MB, PAGED>), dim3((unsigned)(rows * bpr)), dim3(kIdxWaves * 64), lds, st,
+                       Tq, N, HI, m, q_pos0, (int)bpr, (const bf16_t *)qI, w, (const bf16_t *)kI, k_bs, scores,
+                       s_stride, scores2, hist);
     return hipGetLastError();
+}
+
+// paging is a template parameter: the contiguous kernel carries no page-table code
+template <int DI, int MB>
+static hipError_t launch_dma(int B, int Tq, int N, int HI, int m, QPos q_pos0, const void *qI, const float *w,
+                             const void *kI, RowMap k_bs, float *scores, int64_t s_stride, float *scores2,
+                             uint32_t *hist, hipStream_t st) {
+    if (k_bs.ptab)
+        return launch_dma_p<DI, MB, true>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride, scores2, hist,
+                                          st);
+    return launch_dma_p<DI, MB, false>(B, Tq, N, HI, m, q_pos0, qI, w, kI, k_bs, scores, s_stride, scores2, hist, st);
 }
 
 template <typename T, int DI, int MB>

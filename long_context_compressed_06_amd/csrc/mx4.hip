@@ -283,7 +283,7 @@ __device__ __forceinline__ void lds_dma4_nt_mx4(uint32_t lds_addr, const void *s
                  : "memory", "m0");
 }
 
-template <typename T, int MB>
+template <typename T, int MB, bool PAGED>
 __global__ __launch_bounds__(kMx4Waves * 64) void k_index_mx4_dma(int Tq, int N, int HI, int m, QPos q_pos0,
                                                                  int blocks_per_row, const T *__restrict__ qI,
                                                                  const float *__restrict__ w,
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(kMx4Waves * 64) void k_index_mx4_dma(int Tq, int N,
     const int n_all = tiles > gw ? (tiles - gw + wpr - 1) / wpr : 0;
     const int n_vis = vtiles > gw ? (vtiles - gw + wpr - 1) / wpr : 0;
 
-    const int64_t kb_rows = kl.ptab ? 0 : b * kl.bstride;
+    const int64_t kb_rows = PAGED ? 0 : b * kl.bstride;
     const uint8_t *kcb = kc + kb_rows * RB;
     const uint8_t *ksb = ks + kb_rows * KB;
     unsigned char *my_ring = ring + wv * kMx4Stages * kMx4Slot;
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(kMx4Waves * 64) void k_index_mx4_dma(int Tq, int N,
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the slot are done
         const uint8_t *cs = csrc0 + i * tstride_c;
         const uint8_t *ss = ssrc0 + (int64_t)i * wpr * 16 * KB;
-        if (kl.ptab) {  // the tile's 16 rows lie in one page (pages are multiples of 16 rows)
+        if constexpr (PAGED) {  // the tile's 16 rows lie in one page (pages are multiples of 16 rows)
             const int64_t r0 = (int64_t)t * 16;
             const int64_t prow = ((int64_t)pl[r0 >> kl.pshift] << kl.pshift) | (r0 & ((1 << kl.pshift) - 1));
             const int64_t rc = whole ? cr : min(r0 + cr, nv - 1) - r0;
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(kMx4Waves * 64) void k_index_mx4_dma(int Tq, int N,
     };
 
     // paged caches: the query's page list first (the tile addresses need it)
-    if (kl.ptab) {
+    if constexpr (PAGED) {
         for (int i = threadIdx.x; i < (int)min((nv + (1 << kl.pshift) - 1) >> kl.pshift, (int64_t)kl.pstride);
              i += kMx4Waves * 64)
             pl[i] = (int32_t)kl.page_of(b, i);
@@ -443,12 +443,13 @@ __global__ __launch_bounds__(kMx4Waves * 64) void k_index_mx4_dma(int Tq, int N,
     }
 }
 
-template <typename T, int MB>
-static hipError_t launch_mx4_dma(int B, int Tq, int N, int HI, int m, QPos q_pos0, const void *qI, const float *w,
-                                 const uint8_t *kc, const uint8_t *ks, RowMap k_bs, float *scores, int64_t s_stride,
-                                 float *scores2, uint32_t *hist, hipStream_t st) {
-    static const hipError_t attr = hipFuncSetAttribute((const void *)k_index_mx4_dma<T, MB>,
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMx4Lds);
+template <typename T, int MB, bool PAGED>
+static hipError_t launch_mx4_dma_p(int B, int Tq, int N, int HI, int m, QPos q_pos0, const void *qI, const float *w,
+                                   const uint8_t *kc, const uint8_t *ks, RowMap k_bs, float *scores,
+                                   int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
+    constexpr int lds = PAGED ? kMx4Lds : kMx4Lds - kMaxPagesPerSeq * 4;  // (the page list: paged keys only)
+    static const hipError_t attr = hipFuncSetAttribute((const void *)k_index_mx4_dma<T, MB, PAGED>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (attr != hipSuccess) return attr;
     const int64_t rows = (int64_t)B * Tq;
     const int64_t tiles = (N + 15) / 16;
@@ -456,9 +457,22 @@ static hipError_t launch_mx4_dma(int B, int Tq, int N, int HI, int m, QPos q_pos
     const int64_t max_bpr = (tiles + kMx4Waves - 1) / kMx4Waves;
     if (bpr > max_bpr) bpr = max_bpr;
     if (bpr < 1) bpr = 1;
-    hipLaunchKernelGGL((k_index_mx4_dma<T, MB>), dim3((unsigned)(rows * bpr)), dim3(kMx4Waves * 64), kMx4Lds, st, Tq,
-                       N, HI, m, q_pos0, (int)bpr, (const T *)qI, w, kc, ks, k_bs, scores, s_stride, scores2, hist);
+    hipLaunchKernelGGL((k_index_mx4_dma<T, MB, PAGED>), dim3((unsigned)(rows * bpr)), dim3(kMx4Waves * 64), lds, st,
+                       Tq, N, HI, m, q_pos0, (int)bpr, (const T *)qI, w, kc, ks, k_bs, scores, s_stride, scores2,
+                       hist);
     return hipGetLastError();
+}
+
+// paging is a template parameter: the contiguous kernel carries no page-table code
+template <typename T, int MB>
+static hipError_t launch_mx4_dma(int B, int Tq, int N, int HI, int m, QPos q_pos0, const void *qI, const float *w,
+                                 const uint8_t *kc, const uint8_t *ks, RowMap k_bs, float *scores, int64_t s_stride,
+                                 float *scores2, uint32_t *hist, hipStream_t st) {
+    if (k_bs.ptab)
+        return launch_mx4_dma_p<T, MB, true>(B, Tq, N, HI, m, q_pos0, qI, w, kc, ks, k_bs, scores, s_stride, scores2,
+                                             hist, st);
+    return launch_mx4_dma_p<T, MB, false>(B, Tq, N, HI, m, q_pos0, qI, w, kc, ks, k_bs, scores, s_stride, scores2,
+                                          hist, st);
 }
 
 hipError_t launch_mx4_quantize(int dt, int64_t n_blocks, const void *x, uint8_t *codes, uint8_t *scales,
