@@ -118,6 +118,17 @@ __device__ __forceinline__ int64_t n_visible(int64_t t, int m, int64_t N) {
     return n < N ? n : N;
 }
 
+// Rank of this workgroup with consecutive ranks on one XCD.  The dispatcher
+// deals workgroups to the 8 XCDs round-robin (workgroup i to XCD i mod 8),
+// so rank (i mod 8) * (G / 8) + i / 8 gives XCD x the ranks [x G/8, (x+1) G/8)
+// when G, the grid size, is a multiple of 8 (else the rank is i).  The
+// indexers map consecutive ranks to the workgroups of one query row, which
+// keeps a row's key stream, query and histogram on one XCD.
+__device__ __forceinline__ int xcd_rank(int G) {
+    const int i = blockIdx.x;
+    return (G & 7) ? i : (i & 7) * (G >> 3) + (i >> 3);
+}
+
 // Ragged batches (one query per row, rows = B, row b at position pos[b]):
 // share the G workgroups of a launch among the rows in proportion to their
 // visible 16-entry tiles, every row getting at least one:
@@ -125,7 +136,7 @@ __device__ __forceinline__ int64_t n_visible(int64_t t, int m, int64_t N) {
 // and workgroup i serves row b with parts_{<b} <= i < parts_{<=b}.  Every
 // wavefront computes the same answer from pos (no barrier); false for the
 // workgroups left over by the rounding.
-__device__ __forceinline__ bool ragged_share(const int64_t *__restrict__ pos, int B, int m, int64_t N, int G,
+__device__ __forceinline__ bool ragged_share(const int64_t *__restrict__ pos, int B, int m, int64_t N, int G, int i,
                                              int64_t *row, int *part, int *parts) {
     const int lane = threadIdx.x & 63;
     auto tiles_of = [&](int b) -> int64_t { return b < B ? (n_visible(pos[b], m, N) + 15) / 16 : 0; };
@@ -137,7 +148,6 @@ __device__ __forceinline__ bool ragged_share(const int64_t *__restrict__ pos, in
         total += t;
     }
     const int64_t spare = G - B;
-    const int i = blockIdx.x;
     int64_t base = 0;
     for (int b0 = 0; b0 < B; b0 += 64) {
         const int b = b0 + lane;

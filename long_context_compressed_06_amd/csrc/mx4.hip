@@ -303,9 +303,10 @@ __global__ __launch_bounds__(kMx4Waves * 64) void k_index_mx4_dma(int Tq, int N,
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, c = lane & 15;
-    int64_t row = blockIdx.x / blocks_per_row;
-    int part = blockIdx.x % blocks_per_row, parts = blocks_per_row;
-    if (q_pos0.pos && !ragged_share(q_pos0.pos, (int)(gridDim.x / blocks_per_row), m, N, gridDim.x, &row, &part,
+    const int rank = xcd_rank(gridDim.x);
+    int64_t row = rank / blocks_per_row;
+    int part = rank % blocks_per_row, parts = blocks_per_row;
+    if (q_pos0.pos && !ragged_share(q_pos0.pos, (int)(gridDim.x / blocks_per_row), m, N, gridDim.x, rank, &row, &part,
                                     &parts))
         return;  // (ragged rows: workgroups shared by visible tiles; uniform per workgroup)
     const int64_t b = row / Tq, ti = row % Tq;
