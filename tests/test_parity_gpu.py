@@ -130,6 +130,9 @@ SMALL = [
     ("csa_bf16_many_queries", "bf16", 2, 1300, 300, 4, 256, 8, 16, 40, 16, 32),
     ("csa_bf16_fp4_indexer", "bf16:mx4", 2, 4 * 2000 + 3, 5, 4, 128, 16, 16, 300, 64, 128),
     ("hca_bf16_ragged", "bf16", 2, 128 * 77 + 5, 3, 128, 512, 64, 128, 0, 0, 0),
+    # d = 512 bf16 with few queries: head groups of 16 (a partial group here), one split per query below
+    ("csa_bf16_d512_h20", "bf16", 2, 3001, 3, 4, 512, 20, 33, 200, 17, 128),
+    ("csa_bf16_d512_one_split", "bf16", 1, 2000, 70, 4, 512, 64, 16, 100, 16, 64),
     ("hca_bf16_many_queries", "bf16", 1, 128 * 10 + 600, 600, 128, 128, 16, 32, 0, 0, 0),
     ("hca_f32_m1_w0", "f32", 1, 150, 150, 1, 64, 4, 0, 0, 0, 0),
     ("hca_bf16_window_only", "bf16", 1, 100, 100, 128, 128, 64, 16, 0, 0, 0),
@@ -204,10 +207,11 @@ def test_scores_out_and_masking(csa, tq):
 
 
 # ------------------------------------------------------ poison, empty, determinism
-def test_poisoned_memory_is_never_read(csa):
+@pytest.mark.parametrize("d", [256, 512])
+def test_poisoned_memory_is_never_read(csa, d):
     """Entries and index keys beyond N, and raw rows outside every window, are
     filled with large finite values: outputs must not change by a single bit."""
-    wl = Workload("poison", "bf16", B=2, T=4 * 2000 + 2, Tq=4, m=4, d=256, H=64, W=32, k=300, HI=64, dI=128,
+    wl = Workload("poison", "bf16", B=2, T=4 * 2000 + 2, Tq=4, m=4, d=d, H=64, W=32, k=300, HI=64, dI=128,
                   seed_base=79000)
     say(wl)
     outs = []
@@ -224,18 +228,19 @@ def test_poisoned_memory_is_never_read(csa):
         assert torch.equal(a, b)
 
 
-def test_empty_and_invisible(csa):
-    say("empty batch / no visible rows")
-    q = torch.randn((1, 1, 16, 64), device="cuda").to(torch.bfloat16)
-    e = torch.randn((1, 8, 64), device="cuda").to(torch.bfloat16)
-    raw = torch.randn((1, 4, 64), device="cuda").to(torch.bfloat16)
+@pytest.mark.parametrize("d", [64, 512])
+def test_empty_and_invisible(csa, d):
+    say("empty batch / no visible rows", d)
+    q = torch.randn((1, 1, 16, d), device="cuda").to(torch.bfloat16)
+    e = torch.randn((1, 8, d), device="cuda").to(torch.bfloat16)
+    raw = torch.randn((1, 4, d), device="cuda").to(torch.bfloat16)
     # query at position 2 with m=4: no complete group, W=0: empty row set
     lse = torch.empty((1, 1, 16), device="cuda")
     out = csa.hca_dense_mqa(q, e, raw, 8, 4, 0, 2, 0, lse=lse)
     torch.cuda.synchronize()
     assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
     # zero-sized batch enqueues nothing
-    q0 = torch.empty((0, 1, 16, 64), device="cuda", dtype=torch.bfloat16)
+    q0 = torch.empty((0, 1, 16, d), device="cuda", dtype=torch.bfloat16)
     csa.hca_dense_mqa(q0, e[:0], raw[:0], 8, 4, 2, 2, 0)
 
 
