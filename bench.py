@@ -486,7 +486,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        log("bench.py measures one GPU: this build has no multi-GPU path (one process, one MI355X). Use --gpus 1.")
+        log("bench.py measures one GPU: the library has no multi-GPU path (one process, one MI355X). Use --gpus 1.")
         sys.exit(2)
 
     import torch
