@@ -70,6 +70,56 @@ __device__ __forceinline__ void compress_group(const T *__restrict__ rows, const
     }
 }
 
+// Small groups (m no larger than the row slots of k_compress with a whole-row
+// slice, and at most kWaveRows): one wavefront per (batch, group, slice of
+// 64 vectors) pools the m rows itself, without LDS, so it can run beside
+// kernels that hold a CU's LDS.  The weights are computed as k_compress
+// computes them (one wavefront, lane i holding row i's), each product is
+// rounded on its own and the products are added in row order from zero, as
+// k_compress's LDS reduction adds them: the entries are bit-identical.
+constexpr int kWaveRows = 8;
+
+template <typename T>
+__global__ __launch_bounds__(64) void k_compress_wave(int G, int m, int d, int slices, const T *__restrict__ raw,
+                                                      int64_t raw_bs, const float *__restrict__ logits,
+                                                      int64_t log_bs, T *__restrict__ out, int64_t out_bs) {
+#pragma clang fp contract(off)  // each product rounded before it is added, as in the LDS reduction
+    constexpr int VEC = 16 / sizeof(T);
+    const int lane = threadIdx.x;
+    const int sl = blockIdx.x % slices;
+    const int64_t bg = blockIdx.x / slices;
+    const int64_t b = bg / G, g = bg % G;
+    const T *rows = raw + b * raw_bs + g * m * (int64_t)d;
+    const float *z = logits + b * log_bs + g * m;
+    const int col = (sl * 64 + lane) * VEC;
+    const bool on = col < d;
+    u32x4 v[kWaveRows];
+#pragma unroll
+    for (int i = 0; i < kWaveRows; ++i)
+        v[i] = on && i < m ? *(const u32x4 *)(rows + (int64_t)i * d + col) : u32x4{0u, 0u, 0u, 0u};
+    const float z0 = lane < m ? z[lane] : -INFINITY;
+    const float mx = wave_max(fmaxf(z0, -INFINITY));
+    const float e0 = lane < m ? expf(z0 - mx) : 0.f;
+    const float s = wave_sum(e0 + 0.f);
+    const float al = e0 / s;
+    float acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kWaveRows; ++i) {
+        if (i >= m) break;
+        const float a = __shfl(al, i);
+        const T *ve = (const T *)&v[i];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] = acc[e] + a * Elem<T>::to_f32(ve[e]);
+    }
+    if (on) {
+        T *o = out + b * out_bs + g * (int64_t)d + col;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[e] = Elem<T>::from_f32(acc[e]);
+    }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_compress(int G, int m, int d, int tpr, int slices, const T *__restrict__ raw,
                                                    int64_t raw_bs, const float *__restrict__ logits,
@@ -192,6 +242,12 @@ hipError_t launch_compress_t(int B, int G, int m, int d, const void *raw, int64_
     while (tpr > 1 && (256 / tpr) * kRowsPerThread < m) tpr /= 2;
     if ((256 / tpr) * kRowsPerThread < m) return hipErrorInvalidValue;
     const int slices = d / VEC / tpr;
+    if (tpr == d / VEC && m <= 256 / tpr && m <= kWaveRows) {  // each row slot holds one row: the LDS-free form
+        const int wslices = (d / VEC + 63) / 64;
+        hipLaunchKernelGGL(k_compress_wave<T>, dim3((unsigned)((int64_t)B * G * wslices)), dim3(64), 0, st, G, m, d,
+                           wslices, (const T *)raw, raw_bs, logits, log_bs, (T *)out, out_bs);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(k_compress<T>, dim3((unsigned)((int64_t)B * G * slices)), dim3(256), 0, st, G, m, d, tpr,
                        slices, (const T *)raw, raw_bs, logits, log_bs, (T *)out, out_bs);
     return hipGetLastError();

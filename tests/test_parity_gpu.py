@@ -282,3 +282,36 @@ def test_graph_replay_matches_eager(csa):
         assert torch.equal(step.out, eager[0]) and torch.equal(step.topk_idx, eager[1]), i
         assert torch.equal(step.lse, eager[2]), i
         _ = (x["q"].float() * 2).sum().item()  # unrelated eager work between replays
+
+
+# ------------------------------------------------ compression: two kernel forms
+@pytest.mark.parametrize("dtype,m,d", [("bf16", 4, 512), ("bf16", 4, 128), ("bf16", 1, 256), ("f32", 4, 512),
+                                       ("bf16", 8, 256), ("f32", 2, 32)])
+def test_compress_forms_bit_identical(csa, dtype, m, d):
+    """Small groups are pooled by one wavefront per group without LDS; the ragged
+    compression pools the same group with the LDS reduction.  Both compute the
+    same weights, round each product once and add the products in row order:
+    the entries must agree bit for bit."""
+    say("compress forms", dtype, m, d)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    B, G = 5, 3
+    g = torch.Generator().manual_seed(4242 + m * 1000 + d)
+    raw = (torch.randn((B, G * m, d), generator=g) * 3).to(dt).cuda()
+    logits = (torch.randn((B, G * m), generator=g) * 2).cuda()
+    out = torch.empty((B, G, d), dtype=dt, device="cuda")
+    csa.csa_compress(raw, logits, m, out)
+    # the ragged form, one group per call: group gi sits at ring rows 0 .. m-1
+    for gi in range(G):
+        ring = max(m, 1)
+        raw_ring = torch.zeros((B, 2 * ring, d), dtype=dt, device="cuda")
+        logit_ring = torch.zeros((B, 2 * ring), dtype=torch.float32, device="cuda")
+        raw_ring[:, :m] = raw[:, gi * m:(gi + 1) * m]
+        raw_ring[:, ring:ring + m] = raw[:, gi * m:(gi + 1) * m]
+        logit_ring[:, :m] = logits[:, gi * m:(gi + 1) * m]
+        logit_ring[:, ring:ring + m] = logits[:, gi * m:(gi + 1) * m]
+        pos = torch.full((B,), m - 1, dtype=torch.int64, device="cuda")
+        cache = torch.empty((B, 1, d), dtype=dt, device="cuda")
+        csa.csa_ragged_compress(raw_ring, logit_ring, ring, m, pos, cache)
+        torch.cuda.synchronize()
+        assert torch.equal(cache[:, 0].view(torch.int16 if dtype == "bf16" else torch.int32),
+                           out[:, gi].view(torch.int16 if dtype == "bf16" else torch.int32)), gi
