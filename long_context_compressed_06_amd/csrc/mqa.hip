@@ -173,9 +173,11 @@ __global__ __launch_bounds__(kMqaThreads) void k_mqa(const MqaArgs a) {
         qf[ks] = head < a.H ? v : E::zero();
     }
 
-    // resolve the split's row addresses once (nullptr = masked row)
+    // resolve the split's row addresses once; masked rows (weight 0, marked in
+    // vmask) load the query's own first row, in bounds and finite
     const T *ent = (const T *)a.entries;
     const T *raw_b = (const T *)a.raw + b * a.raw_bs;
+    const T *fallback = (const T *)a.q + row * a.H * (int64_t)D;
     const int nr = ntiles * S::TR;
     for (int i0 = 0; i0 < nr; i0 += kMqaThreads) {
         const int i = i0 + tid;
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(kMqaThreads) void k_mqa(const MqaArgs a) {
                 const int64_t p = w0 + (r - n_slots);
                 src = raw_b + (a.raw_ring ? p % a.raw_ring : p - a.raw_pos0) * D;
             }
-            rtab[i] = src;
+            rtab[i] = src ? src : fallback;
         }
         const uint64_t bal = __ballot(src != nullptr);  // bits of tiles i/32 (lanes 0-31) and i/32+1
         if (i < nr && (lane & 31) == 0) vmask[i >> 5] = (uint32_t)(lane ? bal >> 32 : bal);
@@ -198,20 +200,13 @@ __global__ __launch_bounds__(kMqaThreads) void k_mqa(const MqaArgs a) {
     // landed and puts no wait for them inside the tile loop
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    // any valid row of the split stands in for masked rows (their weight is 0)
-    const T *dummy = nullptr;
-    for (int i = 0; i < nr && !dummy; ++i) dummy = rtab[i];
-    __syncthreads();
-    for (int i = tid; i < nr; i += kMqaThreads)
-        if (!rtab[i]) rtab[i] = dummy;
-    __syncthreads();
 
     floatx4 o[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) o[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
     float m_ref = -INFINITY, l_run = 0.f;  // base-2 reference maximum, running sum
 
-    if (dummy) {
+    if (ntiles > 0) {
         // wave wv loads rows wv*TR/NW .. of local tile lt into stage lt % STAGES
         auto issue = [&](int lt) {
             unsigned char *buf = tiles + (lt % S::STAGES) * S::TILEB;
