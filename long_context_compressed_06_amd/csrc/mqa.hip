@@ -95,35 +95,6 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 
-// Eight transposing LDS reads (lane (g, c): rows of slot base and base+16
-// rows, columns nb*16 + 4*(c%4) .. +3 for nb = NB0 .. NB0+3) at immediate
-// offsets from one address register, waited for inside the same statement.
-template <int RS, int NB0>
-__device__ __forceinline__ void tr_read4(uint32_t addr, bf16x8 (&va)[4]) {
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    u32x2 r0, r1, r2, r3, r4, r5, r6, r7;
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8 offset:%9\n\t"
-        "ds_read_b64_tr_b16 %1, %8 offset:%10\n\t"
-        "ds_read_b64_tr_b16 %2, %8 offset:%11\n\t"
-        "ds_read_b64_tr_b16 %3, %8 offset:%12\n\t"
-        "ds_read_b64_tr_b16 %4, %8 offset:%13\n\t"
-        "ds_read_b64_tr_b16 %5, %8 offset:%14\n\t"
-        "ds_read_b64_tr_b16 %6, %8 offset:%15\n\t"
-        "ds_read_b64_tr_b16 %7, %8 offset:%16\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=v"(r0), "=v"(r1), "=v"(r2), "=v"(r3), "=v"(r4), "=v"(r5), "=v"(r6), "=v"(r7)
-        : "v"(addr), "n"(NB0 * 32), "n"(NB0 * 32 + 16 * RS), "n"(NB0 * 32 + 32), "n"(NB0 * 32 + 32 + 16 * RS),
-          "n"(NB0 * 32 + 64), "n"(NB0 * 32 + 64 + 16 * RS), "n"(NB0 * 32 + 96), "n"(NB0 * 32 + 96 + 16 * RS)
-        : "memory");
-    const u32x2 lo_[4] = {r0, r2, r4, r6}, hi_[4] = {r1, r3, r5, r7};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const uint32_t w[4] = {lo_[u].x, lo_[u].y, hi_[u].x, hi_[u].y};
-        va[u] = __builtin_bit_cast(bf16x8, *(const u32x4 *)w);
-    }
-}
-
 // LDS slot of tile row r.  LDS serves 128 bytes (32 four-byte banks) per
 // cycle, and the row stride is 4 banks (mod 32): the logits product reads 16
 // bytes of rows c and c+8 in one cycle per eight lanes, so rows 0-7 (and
@@ -298,43 +269,26 @@ __global__ __launch_bounds__(kMqaThreads) void k_mqa(const MqaArgs a) {
                     hi[q] = h;
                     lo[q] = (__bf16)(p[q] - (float)h);
                 }
-                // lane (g, c) addresses rows 4g + c/4 (and +16), columns nb*16 + 4*(c%4) .. +3;
-                // the transposing read hands lane c the column nb*16 + c of rows 4g..4g+3
-                if constexpr (NB % 4 == 0) {
-                    // batches of four column blocks: eight transposing reads, then eight MFMAs
-                    const uint32_t vaddr = (uint32_t)(uintptr_t)(buf + v_off1);
+                // lane (g, c) addresses rows 4g + c/4 (and +16), columns nb*16 + 4*(c%4) .. +3; the
+                // transposing read hands lane c the column nb*16 + c of rows 4g..4g+3.  Every read of
+                // the tile is issued first (the compiler waits for each only before its MFMA), then
+                // the high-part products of all column blocks, then the low-part ones
+                bf16x8 va[NB];
 #pragma unroll
-                    for (int nb0 = 0; nb0 < NB; nb0 += 4) {
-                        bf16x8 va[4];
-                        switch (nb0) {  // the offsets are immediates
-#define CSA_TR4(K) case K: tr_read4<S::RS, K>(vaddr, va); break;
-                            CSA_TR4(0) CSA_TR4(4) CSA_TR4(8) CSA_TR4(12) CSA_TR4(16) CSA_TR4(20) CSA_TR4(24)
-                            CSA_TR4(28)
-#undef CSA_TR4
-                        }
-                        // the high-part products first, so no MFMA waits on the one before it
-#pragma unroll
-                        for (int u = 0; u < 4; ++u)
-                            o[nb0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u], hi, o[nb0 + u], 0, 0, 0);
-#pragma unroll
-                        for (int u = 0; u < 4; ++u)
-                            o[nb0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u], lo, o[nb0 + u], 0, 0, 0);
-                    }
-                } else {
-                    // narrow rows: the same reads through the builtin
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) {
-                        const v4s v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) v4s *)(buf + v_off1 + nb * 32));
-                        const v4s v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) v4s *)(buf + v_off1 + 16 * S::RS + nb * 32));
-                        const bf16x8 va = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, v1),
-                                                                  __builtin_bit_cast(bf16x4_t, v2), 0, 1, 2, 3,
-                                                                  4, 5, 6, 7);
-                        o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, hi, o[nb], 0, 0, 0);
-                        o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, lo, o[nb], 0, 0, 0);
-                    }
+                for (int nb = 0; nb < NB; ++nb) {
+                    const v4s v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4s *)(buf + v_off1 + nb * 32));
+                    const v4s v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4s *)(buf + v_off1 + 16 * S::RS + nb * 32));
+                    va[nb] = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, v1), __builtin_bit_cast(bf16x4_t, v2),
+                                                     0, 1, 2, 3, 4, 5, 6, 7);
                 }
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[nb], hi, o[nb], 0, 0, 0);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[nb], lo, o[nb], 0, 0, 0);
             } else {
                 // fp32: 16x16x4 steps, one row per lane group: lane (g, c) gives
                 // V[rb*16 + 4g + e][nb*16 + c] with the weight of that row
