@@ -3,7 +3,7 @@
 // the selected entries are both key and value and every query head shares
 // them; section 2.3: HCA attends to every entry).
 //
-// Grid.  One 256-thread workgroup per (query, split) of the query's row
+// Grid.  One 512-thread workgroup per (query, split) of the query's row
 // list; split-K partials (unnormalised O, running max, running sum) are merged
 // by k_combine.  With a single split the workgroup writes the final output.
 //
@@ -11,14 +11,15 @@
 // w % 4 and the half w / 4 of the latent width d (SPLITD = 2; narrow rows use
 // one wave per head group with the whole width).  The split's row addresses
 // (gathered entries, then raw window rows) are resolved once into an LDS
-// table, with a 32-bit validity mask per tile.  Tiles of 32 rows then stream
+// table, with a 32-bit validity mask per tile (masked rows point at the
+// query's own first row: in bounds, finite, weight 0).  Tiles of 32 rows then stream
 // HBM -> LDS with asynchronous 16-byte LDS-DMA loads
 // (global_load_lds_dwordx4), STAGES tiles in flight, so no register staging
 // and no dependent global load sits in the loop.  One DMA instruction moves
 // up to 1 KiB of one row; rows sit 16 bytes apart beyond their length in LDS,
 // in a permuted order (row_slot) that keeps both read patterns free of bank
-// conflicts, and every LDS offset of the loop is a compile-time immediate.  Per wave and
-// tile:
+// conflicts, and the loop's LDS offsets are fixed per lane (the compiler folds
+// them into immediates).  Per wave and tile:
 //   S^T[32 rows x 16 heads] = K . Q^T over the wave's half of d (MFMA, K rows
 //       read with ds_read_b128, Q^T in registers); the two halves are summed
 //       through LDS, and both waves of the pair run the same softmax
@@ -26,8 +27,9 @@
 //   moves when the running maximum exceeds it by 2^8, so the accumulator is
 //   rarely rescaled (weights stay <= 256, exact in fp32)
 //   O^T[d/2 x 16 heads] += V^T . P^T (MFMA; V^T read straight from the
-//       row-major tile with the gfx950 transposing ds_read_b64_tr_b16; P is
-//       split into bf16 high and low parts so the weights keep ~16 bits)
+//       row-major tile with the gfx950 transposing ds_read_b64_tr_b16, all
+//       of a tile's reads issued before its MFMAs; P is split into bf16 high
+//       and low parts so the weights keep ~16 bits)
 // Splitting d keeps per-wave state at 16 x 256 fp32 accumulators, so two
 // waves per SIMD hide LDS and MFMA latency.  fp32 data uses the 16x16x4 f32
 // MFMA with scalar LDS reads instead.
