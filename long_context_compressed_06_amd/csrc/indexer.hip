@@ -421,7 +421,7 @@ static hipError_t launch_t(int B, int Tq, int N, int HI, int m, QPos q_pos0, con
 // -inf; tiles past every query of the workgroup are not computed.
 constexpr int kPreWaves = 8;
 constexpr int kPreMinQueries = 64;  // queries per sequence from which the query-blocked kernel is used
-constexpr int kPreRows = 64;       // entries per key tile
+constexpr int kPreRows = 128;      // entries per key tile
 constexpr int kPreStages = 3;
 
 template <int DI>
