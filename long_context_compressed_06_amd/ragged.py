@@ -25,7 +25,9 @@ Paged caches (page_rows = P, a power of two >= 16): the entries and index
 keys of all sequences live in pools of P-row pages, sequence b's entry j in
 row j mod P of page page_table[b, j // P]; one table serves both caches.
 By default each sequence gets its pages from a shuffled free list up front
-(assign_pages hands out other layouts).
+(assign_pages hands out other layouts).  A pool of fewer than B * max_pages
+pages starts with an all-zero table: assign_pages must then give every
+sequence its own pages before the layer is used.
 """
 from __future__ import annotations
 
