@@ -388,10 +388,12 @@ __global__ __launch_bounds__(kMqaThreads) void k_mqa(const MqaArgs a) {
 }
 
 // Merge the split-K partials of one (query, head): a 4-wide column slice
-// per thread.  Splits are taken kMqaMaxSplits at a time, every (max, sum)
+// per thread.  Splits are taken CB at a time (8 when there are at most 8,
+// else kMqaMaxSplits), every (max, sum)
 // and column slice of a batch loaded up front (indices past n_splits reread
 // the last split with zero weight) so the loads are in flight together.
 // Maxima are base-2; empty splits carry l = 0 and get weight 0.
+template <int CB>
 __global__ __launch_bounds__(128) void k_combine(int H, int D, int n_splits, const float *__restrict__ part_o,
                                                  const float *__restrict__ part_ml, float *__restrict__ out,
                                                  float *__restrict__ lse) {
@@ -401,11 +403,11 @@ __global__ __launch_bounds__(128) void k_combine(int H, int D, int n_splits, con
     const int x = min((int)threadIdx.x * 4, D - 4);
     float M = -INFINITY, L = 0.f;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < n_splits; s0 += kMqaMaxSplits) {
-        float ms[kMqaMaxSplits], ls[kMqaMaxSplits];
-        floatx4 po[kMqaMaxSplits];
+    for (int s0 = 0; s0 < n_splits; s0 += CB) {
+        float ms[CB], ls[CB];
+        floatx4 po[CB];
 #pragma unroll
-        for (int u = 0; u < kMqaMaxSplits; ++u) {
+        for (int u = 0; u < CB; ++u) {
             const int64_t slot = (row * n_splits + min(s0 + u, n_splits - 1)) * H + h;
             ms[u] = part_ml[slot * 2];
             ls[u] = s0 + u < n_splits ? part_ml[slot * 2 + 1] : 0.f;
@@ -413,7 +415,7 @@ __global__ __launch_bounds__(128) void k_combine(int H, int D, int n_splits, con
         }
         float Mc = M;
 #pragma unroll
-        for (int u = 0; u < kMqaMaxSplits; ++u) Mc = ls[u] > 0.f ? fmaxf(Mc, ms[u]) : Mc;
+        for (int u = 0; u < CB; ++u) Mc = ls[u] > 0.f ? fmaxf(Mc, ms[u]) : Mc;
         if (Mc > M) {  // (more than one batch of splits only)
             const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mc);
             L *= sc;
@@ -421,7 +423,7 @@ __global__ __launch_bounds__(128) void k_combine(int H, int D, int n_splits, con
             M = Mc;
         }
 #pragma unroll
-        for (int u = 0; u < kMqaMaxSplits; ++u) {
+        for (int u = 0; u < CB; ++u) {
             const float wgt = ls[u] > 0.f ? __builtin_amdgcn_exp2f(ms[u] - M) : 0.f;
             L += ls[u] * wgt;
             acc += wgt * po[u];
@@ -458,8 +460,12 @@ static hipError_t launch_mqa_t(const MqaArgs &a, int64_t rows, hipStream_t st) {
     hipLaunchKernelGGL((k_mqa<T, D>), dim3((unsigned)(rows * a.n_splits)), dim3(kMqaThreads), lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_splits == 1) return e;
-    hipLaunchKernelGGL(k_combine, dim3((unsigned)(rows * a.H)), dim3(128), 0, st, a.H, D, a.n_splits, a.part_o,
-                       a.part_ml, a.out, a.lse);
+    if (a.n_splits <= 8)  // one batch of eight loads per thread
+        hipLaunchKernelGGL(k_combine<8>, dim3((unsigned)(rows * a.H)), dim3(128), 0, st, a.H, D, a.n_splits,
+                           a.part_o, a.part_ml, a.out, a.lse);
+    else
+        hipLaunchKernelGGL(k_combine<kMqaMaxSplits>, dim3((unsigned)(rows * a.H)), dim3(128), 0, st, a.H, D,
+                           a.n_splits, a.part_o, a.part_ml, a.out, a.lse);
     return hipGetLastError();
 }
 
