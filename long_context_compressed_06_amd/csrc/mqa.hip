@@ -388,8 +388,8 @@ __global__ __launch_bounds__(kMqaThreads) void k_mqa(const MqaArgs a) {
 }
 
 // Merge the split-K partials of one (query, head): a 4-wide column slice
-// per thread.  Splits are taken CB at a time (8 when there are at most 8,
-// else kMqaMaxSplits), every (max, sum)
+// per thread.  Splits are taken CB at a time (the split count rounded up to a
+// multiple of four, at most kMqaMaxSplits), every (max, sum)
 // and column slice of a batch loaded up front (indices past n_splits reread
 // the last split with zero weight) so the loads are in flight together.
 // Maxima are base-2; empty splits carry l = 0 and get weight 0.
@@ -460,12 +460,20 @@ static hipError_t launch_mqa_t(const MqaArgs &a, int64_t rows, hipStream_t st) {
     hipLaunchKernelGGL((k_mqa<T, D>), dim3((unsigned)(rows * a.n_splits)), dim3(kMqaThreads), lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_splits == 1) return e;
-    if (a.n_splits <= 8)  // one batch of eight loads per thread
-        hipLaunchKernelGGL(k_combine<8>, dim3((unsigned)(rows * a.H)), dim3(128), 0, st, a.H, D, a.n_splits,
-                           a.part_o, a.part_ml, a.out, a.lse);
+    // one batch of partial loads per thread, rounded up to a multiple of four splits
+    const dim3 grid((unsigned)(rows * a.H));
+    if (a.n_splits <= 4)
+        hipLaunchKernelGGL(k_combine<4>, grid, dim3(128), 0, st, a.H, D, a.n_splits, a.part_o, a.part_ml, a.out,
+                           a.lse);
+    else if (a.n_splits <= 8)
+        hipLaunchKernelGGL(k_combine<8>, grid, dim3(128), 0, st, a.H, D, a.n_splits, a.part_o, a.part_ml, a.out,
+                           a.lse);
+    else if (a.n_splits <= 12)
+        hipLaunchKernelGGL(k_combine<12>, grid, dim3(128), 0, st, a.H, D, a.n_splits, a.part_o, a.part_ml, a.out,
+                           a.lse);
     else
-        hipLaunchKernelGGL(k_combine<kMqaMaxSplits>, dim3((unsigned)(rows * a.H)), dim3(128), 0, st, a.H, D,
-                           a.n_splits, a.part_o, a.part_ml, a.out, a.lse);
+        hipLaunchKernelGGL(k_combine<kMqaMaxSplits>, grid, dim3(128), 0, st, a.H, D, a.n_splits, a.part_o,
+                           a.part_ml, a.out, a.lse);
     return hipGetLastError();
 }
 
