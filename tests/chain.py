@@ -76,7 +76,7 @@ def oracle_sequence(sq, xh: dict) -> dict:
     ent = np.zeros((sq.B, max(G, 1), sq.d), dtype=np.float32)
     if G > 0:
         ent[:, :G] = store(e)
-    res = {"e": e}
+    res = {"e": e, "entries": ent[:, :G]}
     if sq.mode == "csa":
         if sq.index_keys == "pooled":
             # the entries' index keys pooled by the same compressor, stored in the cache's type
@@ -98,3 +98,10 @@ def oracle_sequence(sq, xh: dict) -> dict:
         o, l = orc.dense_mqa(xh["q"], ent[:, :G], xh["raw"], 0, m, sq.W, 0, sq.scale)
     res.update(out=o, lse=l)
     return res
+
+
+def oracle_attention_on(q, entries, idx, raw, raw_pos0: int, W: int, q_pos0: int, scale: float):
+    """The oracle's sparse attention evaluated on a given selection (e.g. the GPU's own top-k set, once it
+    has passed the near-tie rule): the chain's output is compared with this on every row, so a legal swap
+    is not counted as an attention error and no row goes unchecked."""
+    return orc.sparse_mqa(q, entries, np.ascontiguousarray(idx, dtype=np.int32), raw, raw_pos0, W, q_pos0, scale)

@@ -97,8 +97,13 @@ def test_compress_shift_invariance_and_convexity(orc):
     b = orc.compress(raw, (logits.astype(np.float64) + shift).astype(np.float32), m)
     # the shifted logits are rounded to float32, so compare loosely; exact shift below
     assert np.max(np.abs(a - b)) < 1e-3
-    big = orc.compress(raw, logits + np.float32(1000.0), m)  # exact in float32 for |z|<8? no: check finite
-    assert np.all(np.isfinite(big))
+    # logits on a 2^-10 grid with |z| < 8: z + 1000 is exact in float32 (its ulp there is 2^-14), the shift
+    # cancels exactly in z - max z, so the entries must be identical bit for bit
+    zq = (np.round(logits.astype(np.float64) * 1024) / 1024).astype(np.float32)
+    assert np.all(np.abs(zq) < 8)
+    zs = zq + np.float32(1000.0)
+    assert np.array_equal(zs.astype(np.float64) - 1000.0, zq.astype(np.float64))
+    np.testing.assert_array_equal(orc.compress(raw, zs, m), orc.compress(raw, zq, m))
     grp = raw.astype(np.float64).reshape(B, G, m, d)
     assert np.all(a <= grp.max(axis=2) + 1e-12) and np.all(a >= grp.min(axis=2) - 1e-12)
 

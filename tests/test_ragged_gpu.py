@@ -117,8 +117,9 @@ def step_inputs(c, new, j):
     return x
 
 
-def oracle_sequence_steps(c: Case, b: int, s: dict, new: dict):
-    """Oracle outputs of sequence b for each of the S steps (host arrays)."""
+def oracle_sequence_steps(c: Case, b: int, s: dict, new: dict, sel=None):
+    """Oracle outputs of sequence b for each of the S steps (host arrays).  sel (CSA, optional): the GPU's
+    selection [S, k] of each step; the oracle's attention on it is returned as out_own / lse_own."""
     p, m, S = c.positions[b], c.m, c.steps
     f = lambda t: t.float().numpy()
     L = s["tail"].shape[0]
@@ -151,6 +152,10 @@ def oracle_sequence_steps(c: Case, b: int, s: dict, new: dict):
             idx = orc.topk(sc, c.k, m, t)
             o, l = orc.sparse_mqa(q, E, idx, raw[:, :t + 1 - raw0], raw0, c.W, t, c.d ** -0.5)
             r.update(scores=sc[0, 0], idx=idx[0, 0], nvis=(t + 1) // m)
+            if sel is not None:
+                oo, lo = orc.sparse_mqa(q, E, np.ascontiguousarray(sel[j][None, None], dtype=np.int32),
+                                        raw[:, :t + 1 - raw0], raw0, c.W, t, c.d ** -0.5)
+                r.update(out_own=oo[0, 0], lse_own=lo[0, 0])
         else:
             o, l = orc.dense_mqa(q, E, raw[:, :t + 1 - raw0], raw0, m, c.W, t, c.d ** -0.5)
         r.update(out=o[0, 0], lse=l[0, 0])
@@ -174,7 +179,8 @@ def test_ragged_decode(csa, c):
     torch.cuda.synchronize()
     assert to_np(layer.pos).tolist() == [p + S for p in c.positions]
     for b in range(B):
-        ref, e_new = oracle_sequence_steps(c, b, seqs[b], new)
+        gi = np.stack([to_np(x[b, 0]) for x in idxs]) if c.mode == "csa" else None
+        ref, e_new = oracle_sequence_steps(c, b, seqs[b], new, sel=gi)
         n0 = c.positions[b] // c.m
         if e_new is not None:
             got = torch.cat([v for v, _, _ in layer._cache_rows(layer.entries, b, n0 + e_new.shape[0])])[n0:]
@@ -184,17 +190,15 @@ def test_ragged_decode(csa, c):
         ro = np.stack([r["out"] for r in ref])
         rl = np.stack([r["lse"] for r in ref])
         if c.mode == "csa":
-            gi = np.stack([to_np(x[b, 0]) for x in idxs])
             ri = np.stack([r["idx"] for r in ref])
             N_max = max(len(r["scores"]) for r in ref)
             sc = np.full((S, N_max), -np.inf)
             for j, r in enumerate(ref):
                 sc[j, :len(r["scores"])] = r["scores"]
             check_topk(gi, ri, sc, np.array([r["nvis"] for r in ref]), c.k, f"seq {b} topk")
-            same = np.all(gi == ri, axis=1)
-            assert same.mean() >= 0.75
-            assert_close(go[same], ro[same], c.dtype, f"seq {b} out")
-            assert_close(gl[same], rl[same], c.dtype, f"seq {b} lse", row_dims=1)
+            # every step against the oracle's attention on the GPU's own selection
+            assert_close(go, np.stack([r["out_own"] for r in ref]), c.dtype, f"seq {b} out")
+            assert_close(gl, np.stack([r["lse_own"] for r in ref]), c.dtype, f"seq {b} lse", row_dims=1)
         else:
             assert_close(go, ro, c.dtype, f"seq {b} out")
             assert_close(gl, rl, c.dtype, f"seq {b} lse", row_dims=1)
@@ -263,17 +267,23 @@ def test_hybrid_stack_alternating(csa):
     torch.cuda.synchronize()
     for li, (c, (seqs, new)) in enumerate(zip(cases, drawn)):
         for b in range(len(P)):
-            ref, _ = oracle_sequence_steps(c, b, seqs[b], new)
+            gi = np.stack([to_np(o[2][b, 0]) for o in outs[li]]) if c.mode == "csa" else None
+            ref, _ = oracle_sequence_steps(c, b, seqs[b], new, sel=gi)
             go = np.stack([to_np(o[0][b, 0]) for o in outs[li]])
-            ro = np.stack([r["out"] for r in ref])
+            gl = np.stack([to_np(o[1][b, 0]) for o in outs[li]])
             if c.mode == "csa":
-                gi = np.stack([to_np(o[2][b, 0]) for o in outs[li]])
                 ri = np.stack([r["idx"] for r in ref])
-                same = np.all(gi == ri, axis=1)
-                assert same.mean() >= 0.75, (li, b)
-                assert_close(go[same], ro[same], "bf16", f"layer {li} seq {b} out")
+                N_max = max(len(r["scores"]) for r in ref)
+                sc = np.full((S, N_max), -np.inf)
+                for j, r in enumerate(ref):
+                    sc[j, :len(r["scores"])] = r["scores"]
+                check_topk(gi, ri, sc, np.array([r["nvis"] for r in ref]), c.k, f"layer {li} seq {b} topk")
+                assert_close(go, np.stack([r["out_own"] for r in ref]), "bf16", f"layer {li} seq {b} out")
+                assert_close(gl, np.stack([r["lse_own"] for r in ref]), "bf16", f"layer {li} seq {b} lse",
+                             row_dims=1)
             else:
-                assert_close(go, ro, "bf16", f"layer {li} seq {b} out")
+                assert_close(go, np.stack([r["out"] for r in ref]), "bf16", f"layer {li} seq {b} out")
+                assert_close(gl, np.stack([r["lse"] for r in ref]), "bf16", f"layer {li} seq {b} lse", row_dims=1)
     # the stack step as one graph
     eager, graphed = build(), build()
     eager.step([step_inputs(c, new, 0) for c, (_, new) in zip(cases, drawn)])

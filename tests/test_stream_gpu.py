@@ -18,7 +18,7 @@ import numpy as np
 import pytest
 import torch
 
-from chain import oracle_sequence
+from chain import oracle_attention_on, oracle_sequence
 from helpers import assert_close, check_topk, to_np
 from workloads import Sequence, make_sequence
 
@@ -106,10 +106,10 @@ def run_stream(csa, sq: Sequence):
             assert_close(layer.k_idx[:, :sq.G], ref["k_pooled"], sq.dtype, "pooled index keys")
             slack = pooled_key_slack(sq, xh, ref["k_pooled"])
         swapped = check_topk(gidx, ref["idx"], ref["scores"], nv, sq.k, "stream topk", extra_tol=slack)
-        same = np.all(gidx == ref["idx"], axis=2)
-        assert same.mean() >= 0.9, f"only {same.mean():.2%} of rows select the oracle's exact set"
-        assert_close(to_np(out)[same], ref["out"][same], sq.dtype, "stream out")
-        assert_close(to_np(lse)[same], ref["lse"][same], sq.dtype, "stream lse", row_dims=1)
+        # every row against the oracle's attention on the GPU's own selection
+        ro, rl = oracle_attention_on(xh["q"], ref["entries"], gidx, xh["raw"], 0, sq.W, 0, sq.scale)
+        assert_close(out, ro, sq.dtype, "stream out")
+        assert_close(lse, rl, sq.dtype, "stream lse", row_dims=1)
         say(f"rows with a legal near-tie swap: {swapped} of {sq.B * sq.T}")
     else:
         assert_close(out, ref["out"], sq.dtype, "stream out")
@@ -223,16 +223,18 @@ def test_decode_loop_128k_resumed(csa, fmt):
         qih = orc.mx4_dequantize(*orc.mx4_quantize(qih))
     s = orc.index_scores(qih, wi.numpy(), kih, m, T)
     ridx = orc.topk(s, sq.k, m, T)
-    ro, rl = orc.sparse_mqa(q.float().numpy(), entries, ridx, rawh, T - R, sq.W, T, sq.scale)
+    ro, _ = orc.sparse_mqa(q.float().numpy(), entries, ridx, rawh, T - R, sq.W, T, sq.scale)
     gidx = np.concatenate([to_np(t) for t in idxs], axis=1)
     nv = np.tile((T + np.arange(m) + 1) // m, (B, 1))
     check_topk(gidx, ridx, s, nv, sq.k, "loop topk")
-    same = np.all(gidx == ridx, axis=2)
-    assert same.mean() >= 0.75
     go = np.concatenate([to_np(t) for t in outs], axis=1)
     gl = np.concatenate([to_np(t) for t in lses], axis=1)
-    assert_close(go[same], ro[same], "bf16", "loop out")
-    assert_close(gl[same], rl[same], "bf16", "loop lse", row_dims=1)
+    # every row against the oracle's attention on the GPU's own selection; the oracle's selection for information
+    oo, ol = oracle_attention_on(q.float().numpy(), entries, gidx, rawh, T - R, sq.W, T, sq.scale)
+    assert_close(go, oo, "bf16", "loop out")
+    assert_close(gl, ol, "bf16", "loop lse", row_dims=1)
+    say(f"loop rows with a legal near-tie swap: {int((~np.all(gidx == ridx, axis=2)).sum())}; end-to-end max "
+        f"|out - oracle| on the oracle's selection {np.abs(go - ro).max():.3e}")
 
 
 def test_append_rows_multi_exact(csa):
