@@ -382,6 +382,32 @@ int hca_dense_mqa(int dt, int B, int Tq, int H, int d, int N, int m, int W,
                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * csa_index_topk_noalloc -- csa_index_topk for callers that cannot allocate
+ * (code under HIP graph capture that may not call hipMalloc, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, outputs and
+ * errors as csa_index_topk, without the workspace: the call uses a
+ * scratch array of CSA_NOALLOC_SCRATCH_BYTES held in the library, one per
+ * GPU, allocated when the library is loaded on that GPU and kept until the
+ * process ends.  It calls no allocator.  Sizes whose
+ * csa_index_topk_workspace_bytes(B, Tq, N, H_I, k) exceeds
+ * CSA_NOALLOC_SCRATCH_BYTES return CSA_EWORKSPACE before anything is
+ * enqueued (16 MiB holds e.g. 32 decode queries over 32768 entries or 4
+ * over 262144).  Every call on one GPU shares that GPU's array and the array
+ * keeps the last call's contents (the part that must start at zero is
+ * cleared by the call itself): calls that overlap in time on one GPU (on
+ * different streams, or from different threads without ordering) race and
+ * must be serialised by the caller.  The first call on each device looks up
+ * the array's device address (hipGetSymbolAddress) with that device
+ * current; a failure there returns CSA_EHIP.
+ */
+#define CSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int csa_index_topk_noalloc(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k,
+                           int64_t q_pos0,
+                           const void *q_idx, const float *w_idx,
+                           const void *k_idx, int64_t k_bstride,
+                           int32_t *topk_idx, float *scores_out, void *stream);
+
+/*
  * csa_stream_read -- measurement helper (not part of the method): reads
  * `bytes` of `buf` as `fronts` contiguous fronts streamed at the same time,
  * with the indexer's load path (1 KiB non-temporal LDS-DMA per instruction,

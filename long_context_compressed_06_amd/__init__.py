@@ -24,7 +24,8 @@ EXPORTS = ("csa_abi_version", "csa_status_string", "csa_last_error_detail", "csa
            "csa_index_topk_workspace_bytes", "csa_index_topk", "csa_index_scores", "csa_mqa_workspace_bytes",
            "csa_sparse_mqa", "hca_dense_mqa", "csa_mx4_quantize", "csa_index_topk_mx4", "csa_append_rows",
            "csa_compress_channels", "csa_append_rows_multi", "csa_positions_advance", "csa_ragged_compress",
-           "csa_ragged_index_topk", "csa_ragged_index_topk_mx4", "csa_ragged_sparse_mqa", "hca_ragged_dense_mqa", "csa_stream_read")
+           "csa_ragged_index_topk", "csa_ragged_index_topk_mx4", "csa_ragged_sparse_mqa", "hca_ragged_dense_mqa", "csa_stream_read",
+           "csa_index_topk_noalloc")
 
 
 class AppendJob(ctypes.Structure):
@@ -95,6 +96,8 @@ def lib():
     L.csa_ragged_sparse_mqa.restype = I
     L.hca_ragged_dense_mqa.argtypes = [I, I, I, I, I, I, I, P, F, P, P, I64, P, I, I, I64, P, I64, I64, P, P, P, SZ, P]
     L.hca_ragged_dense_mqa.restype = I
+    L.csa_index_topk_noalloc.argtypes = [I, I, I, I, I, I, I, I, I64, P, P, P, I64, P, P, P]
+    L.csa_index_topk_noalloc.restype = I
     L.csa_stream_read.argtypes = [P, I64, I, P, P]
     L.csa_stream_read.restype = I
     L.csa_append_rows.restype = I
@@ -184,6 +187,31 @@ def csa_index_topk(q_idx, w_idx, k_idx, N: int, m: int, k: int, q_pos0: int, top
     _check(lib().csa_index_topk(_dt(q_idx), B, Tq, N, HI, dI, m, k, q_pos0, _p(q_idx), _p(w_idx), _p(k_idx),
                                 _bstride(k_idx), _p(topk_idx), _p(scores_out), _p(workspace), ws_bytes,
                                 _stream(q_idx)))
+    return topk_idx
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # CSA_NOALLOC_SCRATCH_BYTES of include/csa.h
+
+
+def csa_index_topk_noalloc(q_idx, w_idx, k_idx, N: int, m: int, k: int, q_pos0: int, topk_idx,
+                           scores_out=None) -> torch.Tensor:
+    """csa_index_topk on the library's static scratch: the call itself allocates nothing (topk_idx, and
+    scores_out if wanted, are the caller's).  Calls on one GPU share the scratch and must not overlap."""
+    _need(q_idx, "q_idx", dims=4)
+    _need(w_idx, "w_idx", torch.float32, 3)
+    _need(k_idx, "k_idx", q_idx.dtype, 3)
+    _need(topk_idx, "topk_idx", torch.int32, 3)
+    B, Tq, HI, dI = q_idx.shape
+    if not q_idx.is_contiguous() or not w_idx.is_contiguous() or k_idx.stride(1) != dI or k_idx.shape[1] < N:
+        raise ValueError("q_idx/w_idx must be contiguous and k_idx rows packed with >= N rows")
+    if topk_idx.shape != (B, Tq, k) or not topk_idx.is_contiguous():
+        raise ValueError("topk_idx must be a contiguous [B, Tq, k] tensor")
+    if scores_out is not None:
+        _need(scores_out, "scores_out", torch.float32, 3)
+        if scores_out.shape != (B, Tq, N) or not scores_out.is_contiguous():
+            raise ValueError("scores_out must be a contiguous [B, Tq, N] tensor")
+    _check(lib().csa_index_topk_noalloc(_dt(q_idx), B, Tq, N, HI, dI, m, k, q_pos0, _p(q_idx), _p(w_idx), _p(k_idx),
+                                        _bstride(k_idx), _p(topk_idx), _p(scores_out), _stream(q_idx)))
     return topk_idx
 
 

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/csa.h"
@@ -73,6 +74,34 @@ int check_pages(const int32_t *page_table, int B, int max_pages, int page_rows, 
     while ((1 << sh) < page_rows) ++sh;
     *map = csa::RowMap(0, page_table, max_pages, sh, n_pages);
     (void)B;
+    return CSA_OK;
+}
+
+// The workspace of csa_index_topk_noalloc: one array per GPU, alive until the
+// process ends.  In host code `scratch` names a host-side stand-in, never a
+// device address; the device address is looked up once per device
+// (scratch_on_current_device) and only that pointer is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[CSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// device address of `scratch` on the calling thread's current device
+int scratch_on_current_device(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(CSA_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(CSA_EUNSUPPORTED, "device %d outside 0..%d", dev, kMaxDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(CSA_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
     return CSA_OK;
 }
 
@@ -394,6 +423,21 @@ int csa_index_topk(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k,
     if (q_pos0 < 0) return fail(CSA_EINVAL, "q_pos0 must be >= 0");
     return index_topk_impl(dt, B, Tq, N, H_I, d_I, m, k, csa::QPos(q_pos0), q_idx, w_idx, k_idx, k_bstride, topk_idx,
                            scores_out, workspace, workspace_bytes, stream);
+}
+
+int csa_index_topk_noalloc(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k, int64_t q_pos0,
+                           const void *q_idx, const float *w_idx, const void *k_idx, int64_t k_bstride,
+                           int32_t *topk_idx, float *scores_out, void *stream) {
+    if (q_pos0 < 0) return fail(CSA_EINVAL, "q_pos0 must be >= 0");
+    const size_t need = csa_index_topk_workspace_bytes(B, Tq, N, H_I, k);
+    if (need > (size_t)CSA_NOALLOC_SCRATCH_BYTES)
+        return fail(CSA_EWORKSPACE, "B=%d, Tq=%d, N=%d needs %zu bytes of scratch, the static scratch holds %zu", B,
+                    Tq, N, need, (size_t)CSA_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if ((int64_t)B * Tq > 0)
+        if (int s = scratch_on_current_device(&ws)) return s;
+    return index_topk_impl(dt, B, Tq, N, H_I, d_I, m, k, csa::QPos(q_pos0), q_idx, w_idx, k_idx, k_bstride, topk_idx,
+                           scores_out, ws, CSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int csa_ragged_index_topk(int dt, int B, int N, int H_I, int d_I, int m, int k, const int64_t *pos,

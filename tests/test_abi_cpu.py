@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
     import long_context_compressed_06_amd as csa
 
     names = header_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(L, n), n
     assert sorted(csa.EXPORTS) == names
@@ -70,6 +70,19 @@ def index(L, dt=1, B=1, Tq=1, N=1000, HI=64, dI=128, m=4, k=64, q_pos0=3999, ws=
           scores=None, kbs=None, q=P, w=P + 0x100000, kk=P + 0x200000, out=P + 0x3000000):
     kbs = N * dI if kbs is None else kbs
     return L.csa_index_topk(dt, B, Tq, N, HI, dI, m, k, q_pos0, q, w, kk, kbs, out, scores, ws, wsb, None)
+
+
+def test_index_topk_noalloc_validation(L):
+    """The static-scratch variant refuses what its scratch cannot hold, and checks its arguments, before it
+    touches the device (no device lookup happens on these paths)."""
+    def call(B=1, Tq=1, N=1000, q_pos0=3999, k=64):
+        return L.csa_index_topk_noalloc(1, B, Tq, N, 64, 128, 4, k, q_pos0, P, P + 0x100000, P + 0x200000,
+                                        N * 128, P + 0x3000000, None, None)
+    assert call(B=1, Tq=4096, N=16384, q_pos0=61440) == -4   # 256 MiB of score rows
+    assert b"static scratch" in L.csa_last_error_detail()
+    assert call(B=64, N=65536, q_pos0=4 * 65536 - 1) == -4
+    assert call(q_pos0=-1) == -1
+    assert call(B=0) == 0 and call(Tq=0) == 0
 
 
 def test_index_topk_validation(L):
