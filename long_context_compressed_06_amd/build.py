@@ -10,16 +10,18 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcsa.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["abi.cpp", "compress.hip", "indexer.hip", "topk.hip", "mqa.hip", "mx4.hip", "cache.hip", "probe.hip"]
+SOURCES = ["abi.cpp", "compress.hip", "indexer.hip", "topk.hip", "mqa.hip", "mqa_wide.hip", "mx4.hip", "cache.hip", "probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # packed-fp32 instructions are disabled for all device code
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
          "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-result"]
-# per-source additions: the indexers' MFMA results go to VGPRs (each epilogue
-# reads every one of them; results in AGPRs cost one accvgpr read each)
+# per-source additions: MFMA results go to VGPRs for the indexers (each
+# epilogue reads every one of them; results in AGPRs cost one accvgpr read
+# each) and for the wide attention kernel (its accumulator is rescaled by VALU
+# code; in AGPRs the compiler keeps a second, VGPR copy of it every tile)
 _VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-SOURCE_FLAGS = {"indexer.hip": _VGPR_MFMA, "mx4.hip": _VGPR_MFMA}
+SOURCE_FLAGS = {"indexer.hip": _VGPR_MFMA, "mx4.hip": _VGPR_MFMA, "mqa_wide.hip": _VGPR_MFMA}
 
 
 def _compile(src: str) -> str:

@@ -105,14 +105,19 @@ hipError_t launch_topk(int B, int Tq, int N, int m, int k, QPos q_pos0, const fl
 // splits of one query's rows, and at most this many 32-row tiles per split
 constexpr int kMqaTargetBlocks = 256;
 constexpr int kMqaMaxSplits = 16;
-// (the row table shares LDS with the tile stages: fp32 rows of d=512 leave
-// room for 56 tiles)
+// (the row table shares LDS with the tile stages: four stages of bf16 rows of
+// d=512, or three of fp32 ones, leave room for 48 tiles)
 constexpr int kMqaMaxTilesPerSplit = 120;
-constexpr int mqa_max_tiles_per_split(int d) { return d >= 512 ? 56 : kMqaMaxTilesPerSplit; }
+constexpr int mqa_max_tiles_per_split(int d) { return d >= 512 ? 48 : kMqaMaxTilesPerSplit; }
 
 // split count and tiles (of 32 rows) per split for `rows` queries whose row
 // lists hold at most n_rows_max rows
 int mqa_choose_splits(int64_t rows, int64_t n_rows_max, int d, int *tiles_per_split);
+struct MqaArgs;
+// bf16 rows of d = 512 with 33..64 heads: the 32-head-wave kernel (its split-K
+// partials are merged by the caller)
+hipError_t launch_mqa_wide(const MqaArgs &a, int64_t rows, hipStream_t st);
+size_t mqa_wide_lds_bytes(int tiles_per_split);
 
 // ws: split-K partials, rows*n_splits*H*(d+2) floats (unused when n_splits == 1)
 // raw_ring: 0 -> raw row r is position raw_pos0 + r; R > 0 -> position p is raw row p mod R

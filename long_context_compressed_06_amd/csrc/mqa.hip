@@ -33,26 +33,9 @@
 // Splitting d keeps per-wave state at 16 x 256 fp32 accumulators, so two
 // waves per SIMD hide LDS and MFMA latency.  fp32 data uses the 16x16x4 f32
 // MFMA with scalar LDS reads instead.
-#include "kernels.h"
+#include "mqa.h"
 
 namespace csa {
-
-struct MqaArgs {
-    int Tq, H, N, m, k, W, n_splits, tiles_per_split;
-    int64_t q_pos0, raw_pos0, raw_bs;
-    RowMap em;           // entry rows (a batch stride or a page table)
-    const int64_t *pos;  // optional: sequence b's query position (ragged batches, Tq = 1)
-    int64_t raw_ring;    // 0: raw rows are positions raw_pos0 ..; R: position p is ring row p mod R
-    float scale;
-    const void *q, *entries, *raw;
-    const int32_t *idx;
-    float *out, *lse, *part_o, *part_ml;
-};
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLazyRescale = 8.f;  // base-2 headroom of the reference maximum
-constexpr int kMqaThreads = 512;
 
 template <typename T, int D>
 struct MqaShape {
@@ -76,35 +59,6 @@ struct MqaShape {
         return (size_t)STAGES * TILEB + XCH + (size_t)tiles_per_split * (TR * sizeof(void *) + 4);
     }
 };
-
-// 16 bytes per active lane from `src` into LDS at lds_base + 16 * lane.
-// Issued from inline assembly so that the compiler does not treat every
-// later LDS read as dependent on it (it would drain all tiles in flight);
-// completion is awaited explicitly with wait_vm_barrier.  One wait state
-// separates the M0 write from the LDS-DMA instruction, as the ISA requires.
-__device__ __forceinline__ void dma16(const void *lds_base, const void *src) {
-    const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(l), "v"(src)
-                 : "memory", "m0");
-}
-// wait until at most N vector-memory operations of this wave are in flight,
-// then barrier; one statement, so no LDS access is scheduled across it
-template <int N>
-__device__ __forceinline__ void wait_vm_barrier() {
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-typedef short v4s __attribute__((ext_vector_type(4)));
-
-// LDS slot of tile row r.  LDS serves 128 bytes (32 four-byte banks) per
-// cycle, and the row stride is 4 banks (mod 32): the logits product reads 16
-// bytes of rows c and c+8 in one cycle per eight lanes, so rows 0-7 (and
-// 8-15, ...) need slots distinct mod 8; a transposing read takes 8 bytes of
-// rows 4g..4g+3 in one cycle per sixteen lanes, so those four rows need slots
-// two apart mod 8 (disjoint 8-bank windows): rows 4g..4g+3 go to even slots
-// for even g and odd slots for odd g.
-__device__ __forceinline__ int row_slot(int r) { return (r & 24) | ((r & 3) << 1) | ((r >> 2) & 1); }
 
 template <typename T, int D>
 __global__ __launch_bounds__(kMqaThreads) void k_mqa(const MqaArgs a) {
@@ -397,7 +351,9 @@ template <int CB>
 __global__ __launch_bounds__(128) void k_combine(int H, int D, int n_splits, const float *__restrict__ part_o,
                                                  const float *__restrict__ part_ml, float *__restrict__ out,
                                                  float *__restrict__ lse) {
-    const int64_t rh = blockIdx.x;
+    // rows on the XCD whose L2 holds their partials (the attention kernels place
+    // a query's splits by the same rank)
+    const int64_t rh = xcd_rank((int)gridDim.x);
     const int64_t row = rh / H;
     const int h = (int)(rh % H);
     const int x = min((int)threadIdx.x * 4, D - 4);
@@ -448,18 +404,8 @@ int mqa_choose_splits(int64_t rows, int64_t n_rows_max, int d, int *tiles_per_sp
     return (int)s;
 }
 
-template <typename T, int D>
-static hipError_t launch_mqa_t(const MqaArgs &a, int64_t rows, hipStream_t st) {
-    using S = MqaShape<T, D>;
-    // one-time opt-in to the largest dynamic LDS this instantiation may use
-    static const hipError_t attr = hipFuncSetAttribute((const void *)k_mqa<T, D>,
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (attr != hipSuccess) return attr;
-    const size_t lds = S::lds_bytes(a.tiles_per_split);
-    if (lds > 160 * 1024) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_mqa<T, D>), dim3((unsigned)(rows * a.n_splits)), dim3(kMqaThreads), lds, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.n_splits == 1) return e;
+static hipError_t launch_combine(const MqaArgs &a, int64_t rows, int D, hipStream_t st) {
+    if (a.n_splits == 1) return hipSuccess;
     // one batch of partial loads per thread, rounded up to a multiple of four splits
     const dim3 grid((unsigned)(rows * a.H));
     if (a.n_splits <= 4)
@@ -475,6 +421,21 @@ static hipError_t launch_mqa_t(const MqaArgs &a, int64_t rows, hipStream_t st) {
         hipLaunchKernelGGL(k_combine<kMqaMaxSplits>, grid, dim3(128), 0, st, a.H, D, a.n_splits, a.part_o,
                            a.part_ml, a.out, a.lse);
     return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_mqa_t(const MqaArgs &a, int64_t rows, hipStream_t st) {
+    using S = MqaShape<T, D>;
+    // one-time opt-in to the largest dynamic LDS this instantiation may use
+    static const hipError_t attr = hipFuncSetAttribute((const void *)k_mqa<T, D>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (attr != hipSuccess) return attr;
+    const size_t lds = S::lds_bytes(a.tiles_per_split);
+    if (lds > 160 * 1024) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_mqa<T, D>), dim3((unsigned)(rows * a.n_splits)), dim3(kMqaThreads), lds, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_combine(a, rows, D, st);
 }
 
 template <typename T>
@@ -501,6 +462,12 @@ hipError_t launch_mqa(int dt, int B, int Tq, int H, int d, int N, int m, int k, 
     a.part_o = ws;
     a.part_ml = ws ? ws + rows * n_splits * H * (int64_t)d : nullptr;
     if (dt == 0) return launch_mqa_dt<float>(d, a, rows, st);
+    if (d == 512 && H > 32) {
+        // 32-head waves with 32x32x16 MFMAs (mqa_wide.hip)
+        const hipError_t e = launch_mqa_wide(a, rows, st);
+        if (e != hipSuccess) return e;
+        return launch_combine(a, rows, d, st);
+    }
     return launch_mqa_dt<bf16_t>(d, a, rows, st);
 }
 
