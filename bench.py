@@ -39,36 +39,37 @@ def log(*a):
 
 
 def algorithmic_bytes(wl) -> dict:
-    """Bytes the method must move once per step (overheads like scores and
-    split-K partials excluded), and the indexer kernel's share."""
+    """Unique HBM bytes the method must move once per step (overheads like
+    scores, histograms and split-K partials excluded), and the indexer's share.
+
+    Per sequence: the index keys visible to its last query (each read once),
+    every query's index query and head weights, its q and fp32 output, its
+    selection written and read back, the distinct entry rows attended (at most
+    the visible entries; for one query, its selected rows), the distinct raw
+    positions its windows cover, the new groups' logits and entry writes.  For
+    a block of queries that share a cache (a prefill chunk) rows reused across
+    queries count once: their re-reads are served by the caches."""
     es = 2 if wl.dtype == "bf16" else 4
-    step = idx_kernel = 0
-    for ti in range(wl.Tq):
-        t = wl.q_pos0 + ti
-        nv = min(wl.N, (t + 1) // wl.m)
-        n_win = min(wl.W, t + 1)
-        q = wl.H * wl.d * es
-        out = wl.H * wl.d * 4
-        if wl.mode == "csa" and wl.index_fmt == "mx4":
-            # FP4 keys and queries: dI/2 code bytes + dI/32 scale bytes per row; the
-            # bf16 index queries are read once by the quantiser
-            row4 = wl.dI // 2 + wl.dI // 32
-            ki = nv * row4 + wl.HI * (row4 + wl.dI * es) + wl.HI * 4
-            idx_kernel += ki
-            rows = (min(wl.k, nv) + n_win) * wl.d * es
-            step += ki + wl.HI * row4 + rows + q + out + 2 * wl.k * 4
-        elif wl.mode == "csa":
-            ki = nv * wl.dI * es + wl.HI * wl.dI * es + wl.HI * 4
-            idx_kernel += ki
-            rows = (min(wl.k, nv) + n_win) * wl.d * es
-            step += ki + rows + q + out + 2 * wl.k * 4
+    t_last = wl.q_pos0 + wl.Tq - 1
+    nv_max = min(wl.N, (t_last + 1) // wl.m)
+    win_span = min(wl.W + wl.Tq - 1, t_last + 1) if wl.W > 0 else 0
+    per_query = wl.H * wl.d * es + wl.H * wl.d * 4
+    if wl.mode == "csa":
+        if wl.index_fmt == "mx4":
+            # FP4 keys: dI/2 code bytes + dI/32 scale bytes per row; the element-type
+            # index queries are read once by the quantiser
+            key_row = wl.dI // 2 + wl.dI // 32
         else:
-            step += (nv + n_win) * wl.d * es + q + out
-    step *= wl.B
-    idx_kernel *= wl.B
-    # compression of the new groups: logits, raw rows outside the window, the entry write
-    step += wl.B * (wl.G_new * wl.m * 4 + wl.G_new * wl.d * es)
-    return {"step": step, "indexer": idx_kernel}
+            key_row = wl.dI * es
+        iq = wl.HI * wl.dI * es + wl.HI * 4
+        indexer = nv_max * key_row + wl.Tq * iq
+        sel_rows = min(sum(min(wl.k, min(wl.N, (wl.q_pos0 + ti + 1) // wl.m)) for ti in range(wl.Tq)), nv_max)
+        step = indexer + wl.Tq * (per_query + 2 * wl.k * 4) + (sel_rows + win_span) * wl.d * es
+    else:
+        indexer = 0
+        step = wl.Tq * per_query + (nv_max + win_span) * wl.d * es
+    step += wl.G_new * wl.m * 4 + wl.G_new * wl.d * es  # new groups: logits, entry writes
+    return {"step": step * wl.B, "indexer": indexer * wl.B}
 
 
 def indexer_source_digest() -> str:
@@ -440,8 +441,14 @@ def stream_ceiling_gbs(fronts: int, reps=10) -> float:
     return (1 << 31) / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(wl, min_seconds=10.0, max_reps=5):
-    """The oracle, as it stands, on the same workload's inputs (host copies)."""
+# the prefill chunk's oracle baseline runs on these query rows (its first and
+# last 128): every row of the chunk would take minutes of host time
+PREFILL_BASELINE_ROWS = 128
+
+
+def cpu_baseline(wl, min_seconds=10.0, max_reps=40):
+    """The oracle, as it stands, on the same workload's inputs (host copies):
+    the whole step, or for a block of many queries a stated subset of rows."""
     import torch
 
     import oracle
@@ -454,17 +461,37 @@ def cpu_baseline(wl, min_seconds=10.0, max_reps=5):
     xh = host_inputs(x)
     del x
     torch.cuda.empty_cache()
+    rows = None
+    n_rows = wl.B * wl.Tq
+    if wl.Tq > 2 * PREFILL_BASELINE_ROWS:
+        rows = [(0, PREFILL_BASELINE_ROWS), (wl.Tq - PREFILL_BASELINE_ROWS, wl.Tq)]
+        n_rows = wl.B * 2 * PREFILL_BASELINE_ROWS
     reps, t0 = 0, time.perf_counter()
     while reps < max_reps:
-        oracle_step(wl, xh)
+        oracle_step(wl, xh, rows)
         reps += 1
         if time.perf_counter() - t0 >= min_seconds:
             break
     el = time.perf_counter() - t0
-    return {"value": wl.B * wl.Tq * reps / el, "unit": "tokens/s", "cores": oracle.default_threads(),
-            "kind": "oracle",
-            "sample": f"whole step of the {wl.name} workload (all {wl.B} sequences: compression, indexer over "
-                      f"{wl.N} entries, top-{wl.k}, attention) repeated {reps}x in {el:.1f} s"}
+    what = (f"whole step of the {wl.name} workload (all {wl.B} sequences: compression, "
+            + (f"indexer over {wl.N} entries, top-{wl.k}, attention)" if wl.mode == "csa"
+               else f"dense attention over {wl.N} entries)"))
+    if rows is not None:
+        what = (f"query rows 0-{PREFILL_BASELINE_ROWS - 1} and {wl.Tq - PREFILL_BASELINE_ROWS}-{wl.Tq - 1} of the "
+                f"{wl.name} workload ({n_rows} of {wl.B * wl.Tq} rows; compression of all new groups, indexer over "
+                f"up to {wl.N} entries, top-{wl.k}, attention), tokens/s = rows/s")
+    return {"value": n_rows * reps / el, "unit": "tokens/s", "cores": oracle.default_threads(), "kind": "oracle",
+            "sample": f"{what} repeated {reps}x in {el:.1f} s"}
+
+
+def checked_frac(frac: float, what: str) -> float:
+    """A fraction of a peak above 1 means the bytes or FLOPs counted are wrong."""
+    assert frac <= 1.0, f"{what}: fraction {frac:.3f} of the peak is above 1"
+    return frac
+
+
+# secondary workloads that also get an oracle baseline (the 1M decodes and the prefill chunk)
+BASELINE_ALSO = ("c3", "c5", "c4")
 
 
 def main():
@@ -472,7 +499,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c2", help="c2 (default), c3 or c5")
+    ap.add_argument("--workload", default="c2", help="c2 (default; the metric's configuration) or another config")
     ap.add_argument("--also", default="c3,c5,c4,c2x,c5x,l2,l2x,l2c,p1,r1,r1p,r2",
                     help="secondary workloads ('' for none); c4: the 64K prefill chunk (tokens/s and the MFMA "
                          "fractions of its indexer and attention); c2x/c5x: FP4 (MXFP4) indexer operands; "
@@ -517,13 +544,14 @@ def main():
                    "input_replicas": r["replicas"], "graph_replay": "one graph per pass over the replicas"},
         "step_hbm": {"algorithmic_bytes": ab["step"],
                      "achieved_GBs": ab["step"] / (r["ms_per_step"] * 1e-3) / 1e9,
-                     "frac": ab["step"] / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                     "frac": checked_frac(ab["step"] / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, wl.name)},
     }
     if "indexer_ms" in r:
         ach = ab["indexer"] / (r["indexer_ms"] * 1e-3) / 1e9
         c1, c32 = stream_ceiling_gbs(1), stream_ceiling_gbs(32)
         line["roofline"] = {"kernel": "k_index_dma (lightning indexer, bf16 keys)", "bound": "hbm", "achieved": ach,
-                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": indexer_traffic(),
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": checked_frac(ach / HBM_PEAK_GBS, "indexer"), "traffic": indexer_traffic(),
                             "bytes_per_launch": ab["indexer"], "avg_launch_us": r["indexer_ms"] * 1e3,
                             "measured_ceiling": {"what": "csa_stream_read of 2 GiB on the same GPU (the indexer's "
                                                          "LDS-DMA load path), bytes read per second",
@@ -539,7 +567,8 @@ def main():
             also[rs.name] = {"tokens_per_s": rs.B / (r2["ms_per_step"] * 1e-3), "ms_per_step": r2["ms_per_step"],
                              "layers": "+".join(s["mode"] for s in rs.specs()),
                              "page_rows": [s.get("page_rows", 0) for s in rs.specs()],
-                             "step_hbm_frac": b2 / (r2["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                             "step_hbm_frac": checked_frac(b2 / (r2["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                                           rs.name),
                              "algorithmic_bytes": b2,
                              "step": f"one token of each of {rs.B} sequences (lengths {min(rs.lengths)}.."
                                      f"{max(rs.lengths)}) through every layer, one captured graph replayed per "
@@ -563,7 +592,8 @@ def main():
             b2 = loop_bytes(sq)
             also[sq.name] = {"tokens_per_s": toks / (r2["ms_per_cycle"] * 1e-3),
                              "ms_per_layer_step": r2["ms_per_cycle"] / (sq.m * LOOP_LAYERS),
-                             "step_hbm_frac": b2 / (r2["ms_per_cycle"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                             "step_hbm_frac": checked_frac(b2 / (r2["ms_per_cycle"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                                           sq.name),
                              "algorithmic_bytes_per_cycle": b2,
                              "cycle": f"{sq.m} decode steps x {LOOP_LAYERS} layers from position {sq.T}, "
                                       f"ring of {r2['ring_positions']} positions, one group emitted per layer"}
@@ -575,15 +605,19 @@ def main():
                             with_kernel=False, with_mfma=prefill)
         b2 = algorithmic_bytes(w2)["step"]
         also[w2.name] = {"tokens_per_s": w2.B * w2.Tq / (r2["ms_per_step"] * 1e-3), "ms_per_step": r2["ms_per_step"],
-                         "step_hbm_frac": b2 / (r2["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "step_hbm_frac": checked_frac(b2 / (r2["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, w2.name),
                          "algorithmic_bytes": b2}
         if "attention_ms" in r2:
             fl = algorithmic_flops(w2)
             for kern in ("indexer", "attention"):
                 tf = fl[kern] / (r2[kern + "_ms"] * 1e-3) / 1e12
                 also[w2.name][kern + "_mfma"] = {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
-                                                 "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
+                                                 "unit": "TFLOP/s",
+                                                 "frac": checked_frac(tf / MFMA_BF16_PEAK_TFLOPS, w2.name + " " + kern),
                                                  "flops_per_launch": fl[kern], "avg_launch_ms": r2[kern + "_ms"]}
+        if not args.no_cpu_baseline and name in BASELINE_ALSO:
+            log(f"[bench] cpu baseline (oracle) {w2.name}")
+            also[w2.name]["cpu_baseline"] = cpu_baseline(w2)
     if also:
         line["also"] = also
     if args.copy_calibration:

@@ -26,7 +26,8 @@ def oracle_step(wl, xh: dict, rows=None) -> dict:
     """Oracle results for workload ``wl`` on host inputs ``xh``.
 
     rows: query rows (0..Tq-1) to evaluate for the indexer / top-k /
-    attention; None evaluates every row.  Compression is always complete.
+    attention, as a list of row numbers or of (start, stop) ranges; None
+    evaluates every row.  Compression is always complete.
     """
     N, m, g0 = wl.N, wl.m, wl.g0
     r0 = g0 * m - wl.raw_pos0
@@ -35,11 +36,11 @@ def oracle_step(wl, xh: dict, rows=None) -> dict:
     if e is not None:
         ent[:, g0:N] = orc.round_bf16(e) if wl.dtype == "bf16" else e.astype(np.float32)
     res = {"e": e, "entries": ent}
-    sel = list(range(wl.Tq)) if rows is None else list(rows)
     if rows is None:
         groups = [(0, wl.Tq)]
     else:
-        groups = [(ti, ti + 1) for ti in sel]
+        groups = [tuple(r) if isinstance(r, (tuple, list)) else (r, r + 1) for r in rows]
+    sel = [ti for a, b in groups for ti in range(a, b)]
     outs, lses, idxs, scs = [], [], [], []
     for a, b in groups:
         qp = wl.q_pos0 + a
