@@ -38,6 +38,7 @@ namespace csa {
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWT = 256;                // threads (four wavefronts)
 constexpr int kTR = 32;                 // rows per tile
@@ -47,6 +48,17 @@ constexpr int kTileB = kTR * kRS;       // LDS bytes per tile
 constexpr int kStages = 4;
 constexpr int kXch = 4 * 64 * 16 * 4;   // partial logits: 4 waves x 64 lanes x 16 floats
 constexpr int kDmaPerWave = kTR / 4;    // rows (one 1 KiB DMA each) per wave per tile
+constexpr int kOutRS = kD + 4;          // floats per head row of the output staging (16 bytes of padding)
+static_assert(64 * kOutRS * 4 <= kStages * kTileB, "the output block fits in the tile stages");
+
+// 16 bytes per lane from src + voff into LDS at lds_base + 16 * lane, the
+// address in scalar registers (see dma16).  Five wait states before the load:
+// the address may have just been written by the vector unit (readfirstlane),
+// which the code generator does not track into inline assembly.
+__device__ __forceinline__ void dma16_s(uint32_t lds_base, uint32_t voff, uint64_t src) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(src)
+                 : "memory", "m0");
+}
 
 __device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -66,7 +78,8 @@ __device__ __forceinline__ int wide_slot(int r) { return (r & 16) | ((r & 3) << 
 }  // namespace
 
 size_t mqa_wide_lds_bytes(int tiles_per_split) {
-    return (size_t)kStages * kTileB + kXch + (size_t)tiles_per_split * (kTR * sizeof(void *) + 4);
+    return (size_t)kStages * kTileB + kXch + (size_t)(tiles_per_split + 2) * kTR * sizeof(void *) +
+           (size_t)tiles_per_split * 4;
 }
 
 __global__ __launch_bounds__(kWT) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_mqa_wide(const MqaArgs a) {
@@ -74,9 +87,10 @@ __global__ __launch_bounds__(kWT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     unsigned char *tiles = smem;
     floatx4 *xch = (floatx4 *)(smem + kStages * kTileB);
     const bf16_t **rtab = (const bf16_t **)(smem + kStages * kTileB + kXch);
-    uint32_t *vmask = (uint32_t *)(rtab + a.tiles_per_split * kTR);
+    uint32_t *vmask = (uint32_t *)(rtab + (a.tiles_per_split + 2) * kTR);
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // (wave-uniform: scalar)
     const int hg = wv >> 1, dh = wv & 1;        // head group of 32, half of d
     const int j = lane & 31, hh = lane >> 5;    // head within the group; lane half
     // the splits of one query on one XCD (their partials are merged there)
@@ -114,7 +128,9 @@ __global__ __launch_bounds__(kWT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const bf16_t *raw_b = (const bf16_t *)a.raw + b * a.raw_bs;
     const bf16_t *fallback = (const bf16_t *)a.q + row * a.H * (int64_t)kD;
     const int nr = ntiles * kTR;
-    for (int i0 = 0; i0 < nr; i0 += kWT) {
+    // (two tiles past the last one, all fallback rows: loads issued beyond the
+    // split land in a stage that is never read again)
+    for (int i0 = 0; i0 < nr + 2 * kTR; i0 += kWT) {
         const int i = i0 + tid;
         const bf16_t *src = nullptr;
         if (i < nr) {
@@ -126,8 +142,8 @@ __global__ __launch_bounds__(kWT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 const int64_t p = w0 + (r - n_slots);
                 src = raw_b + (a.raw_ring ? p % a.raw_ring : p - a.raw_pos0) * kD;
             }
-            rtab[i] = src ? src : fallback;
         }
+        if (i < nr + 2 * kTR) rtab[i] = src ? src : fallback;
         const uint64_t bal = __ballot(src != nullptr);  // lanes 0-31: tile i/32; lanes 32-63: the next
         if (i < nr && (lane & 31) == 0) vmask[i >> 5] = (uint32_t)(lane ? bal >> 32 : bal);
     }
@@ -146,18 +162,29 @@ __global__ __launch_bounds__(kWT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // Tiles past the split's last one (issued so that every wave always has
         // two tiles in flight and the waits below never change) load the query's
         // own row into a stage nobody reads any more.
-        auto row_src = [&](int lt, int u) -> const unsigned char * {
-            const bf16_t *p = rtab[min(lt, ntiles - 1) * kTR + wv * kDmaPerWave + u];  // (always in the table)
-            return (const unsigned char *)(lt < ntiles ? p : fallback) + lane * 16;
+        // The eight row addresses of this wave for tile lt, wave-uniform: the
+        // loads take them from scalar registers (lane l adds 16 l).
+        auto next_sources = [&](int lt, uint64_t (&nsrc)[kDmaPerWave]) {
+            const uint64_t *t = (const uint64_t *)rtab + lt * kTR + wv * kDmaPerWave;
+#pragma unroll
+            for (int u = 0; u < kDmaPerWave; ++u) {
+                const uint64_t v = t[u];
+                // (readfirstlane returns int: both halves are widened unsigned)
+                const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+                const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+                nsrc[u] = ((uint64_t)hi << 32) | (uint64_t)lo;
+            }
         };
-        auto dma_row = [&](int lt, int u, const unsigned char *src) {
-            dma16(tiles + (lt % kStages) * kTileB + wide_slot(wv * kDmaPerWave + u) * kRS, src);
+        const uint32_t lane16 = (uint32_t)lane * 16;
+        auto dma_row = [&](int lt, int u, uint64_t src) {
+            const uint32_t l = (uint32_t)(uintptr_t)(tiles + (lt % kStages) * kTileB +
+                                                      wide_slot(wv * kDmaPerWave + u) * kRS);
+            dma16_s(__builtin_amdgcn_readfirstlane(l), lane16, src);
         };
 #pragma unroll
         for (int lt = 0; lt < 2; ++lt) {
-            const unsigned char *src[kDmaPerWave];
-#pragma unroll
-            for (int u = 0; u < kDmaPerWave; ++u) src[u] = row_src(lt, u);
+            uint64_t src[kDmaPerWave];
+            next_sources(lt, src);
 #pragma unroll
             for (int u = 0; u < kDmaPerWave; ++u) dma_row(lt, u, src[u]);
         }
@@ -196,169 +223,254 @@ __global__ __launch_bounds__(kWT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
             return sv;
         };
-        // The reference maximum of head j (base 2) is settled as soon as a tile's
-        // logits are known, before that tile's weights are formed: it moves only
-        // when the tile maximum outgrows it by 2^8, and then the accumulator and
-        // the running sum (which so far hold the weighted sums of the earlier
-        // tiles, relative to the old reference) are rescaled.  Weights are
-        // therefore at most 2^8 and need nothing but the reference in force.
-        auto settle_reference = [&](const floatx16 &sv) {
-            float mx = sv[0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sv[r]);
-            {  // with lane l ^ 32 (the other half of the tile's rows), without an LDS round trip
-                const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-                mx = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-            }
-            mx *= scale2;  // base-2 maximum of this tile for head j (scale2 > 0 keeps the order)
-            const bool grow = mx > m_ref + kLazyRescale;
-            if (__ballot(grow)) {  // (wave-uniform; the first valid tile, then rarely)
-                // exp2(-inf) = 0 when the first valid tile arrives
-                const float alpha = __builtin_amdgcn_exp2f(grow ? m_ref - mx : 0.f);
-                l_run *= alpha;
-#pragma unroll
-                for (int nb = 0; nb < 8; ++nb) o[nb] *= alpha;
-                m_ref = grow ? mx : m_ref;
-            }
-        };
-        // weights of one tile relative to the reference in force (at most 2^8),
-        // split into bf16 high and low parts; their sum joins the running sum.
-        // While no row has been valid m_ref is -inf and every logit -inf: 0 is
-        // then used as the reference, so that every weight is exp2(-inf) = 0.
-        auto weights = [&](const floatx16 &sv, bf16x8 (&pw)[2], bf16x8 (&pl)[2]) {
-            const float mneg = m_ref == -INFINITY ? 0.f : -m_ref;
-            float lsum = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float pr = __builtin_amdgcn_exp2f(fmaf(sv[8 * ks + e], scale2, mneg));
-                    const __bf16 w = (__bf16)pr;
-                    pw[ks][e] = w;
-                    pl[ks][e] = (__bf16)(pr - (float)w);
-                    lsum += pr;
-                }
-            l_run += lsum;
-        };
-
-        // Iteration lt:
-        //   barrier A: tile lt landed, the stage of tile lt-2 free
-        //   block 1: the K reads of tile lt and the V^T reads of tile lt-1; the
-        //     logits MFMAs of tile lt with the weights of tile lt-1 (VALU, which
-        //     need only the reference settled for it) between them; this
-        //     wave's half of tile lt's logits published
-        //   barrier B
-        //   block 2: the weighted sum of tile lt-1 (hi, then lo parts) with the
-        //     partner's half of tile lt's logits, their maximum and the DMAs of
-        //     tile lt+2 between its MFMAs; then the reference settled for tile
-        //     lt (the rare rescale comes after the weighted sum it applies to)
-        floatx16 s_prev;  // full logits of the previous tile
-        for (int lt = 0; lt < ntiles; ++lt) {
-            barrier_a();
-            const unsigned char *cur = tiles + (lt % kStages) * kTileB;
+        // this wave's half of the logits of tile lt (one chain of 16 MFMAs) in
+        // a fixed order (scheduling barriers between the steps): eight K reads
+        // ahead of the chain keep it fed; per MFMA the next K read and, on even
+        // steps, one row load of tile lt+2.  The returned partial is this
+        // wave's half of d.
+        auto block1 = [&](int lt, const uint64_t (&nsrc)[kDmaPerWave]) -> floatx16 {
+            const unsigned char *cur = tiles + (lt % kStages) * kTileB + k_off;
             bf16x8 kf[16];
 #pragma unroll
-            for (int ks = 0; ks < 16; ++ks) kf[ks] = *(const bf16x8 *)(cur + k_off + 32 * ks);
-            floatx16 a0, a1;
+            for (int ks = 0; ks < 8; ++ks) kf[ks] = *(const bf16x8 *)(cur + 32 * ks);
+            __builtin_amdgcn_sched_barrier(0);
+            floatx16 acc;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) a0[e] = a1[e] = 0.f;
-            bf16x8 vf[2][8], ph[2], pl[2];
-            if (lt > 0) {
+            for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                    for (int nb = 0; nb < 8; ++nb) vf[ks][nb] = read_v(lt - 1, ks, nb);
+            for (int ks = 0; ks < 16; ++ks) {
+                acc = mfma32(kf[ks], qf[ks], acc);
+                if (ks + 8 < 16) kf[ks + 8] = *(const bf16x8 *)(cur + 32 * (ks + 8));
+                if ((ks & 1) == 0) dma_row(lt + 2, ks >> 1, nsrc[ks >> 1]);
+                // (ties the MFMA to its step: the code generator otherwise places
+                // the whole chain after the loads)
+                asm volatile("" : "+v"(acc));
+                __builtin_amdgcn_sched_barrier(0);
             }
-#pragma unroll
-            for (int ks = 0; ks < 16; ks += 2) {
-                a0 = mfma32(kf[ks], qf[ks], a0);
-                a1 = mfma32(kf[ks + 1], qf[ks + 1], a1);
-            }
-            if (lt > 0) weights(s_prev, ph, pl);
-            const floatx16 acc = a0 + a1;
+            return acc;
+        };
+        auto publish = [&](const floatx16 &acc) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 xch[(wv * 4 + q) * 64 + lane] = floatx4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
-            const unsigned char *nsrc[kDmaPerWave];
-#pragma unroll
-            for (int u = 0; u < kDmaPerWave; ++u) nsrc[u] = row_src(lt + 2, u);
-            lds_barrier();
-            floatx16 sv = acc;
+        };
+        auto with_partner = [&](floatx16 sv) -> floatx16 {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const floatx4 v = xch[((wv ^ 1) * 4 + q) * 64 + lane];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) sv[4 * q + e] += v[e];
             }
-            if (lt > 0) {
+            return sv;
+        };
+        // Q^T stays in the accumulation registers, which the MFMAs read directly
+        auto pin_q = [&]() {
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-                    for (int nb = 0; nb < 8; ++nb) {
-                        o[nb] = mfma32(vf[ks][nb], ph[ks], o[nb]);
-                        if ((nb & 3) == 3) dma_row(lt + 2, 4 * ks + (nb >> 2), nsrc[4 * ks + (nb >> 2)]);
-                    }
-#pragma unroll
-                    for (int nb = 0; nb < 8; ++nb) {
-                        o[nb] = mfma32(vf[ks][nb], pl[ks], o[nb]);
-                        if ((nb & 3) == 3) dma_row(lt + 2, 4 * ks + 2 + (nb >> 2), nsrc[4 * ks + 2 + (nb >> 2)]);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int u = 0; u < kDmaPerWave; ++u) dma_row(lt + 2, u, nsrc[u]);
+            for (int ks = 0; ks < 16; ++ks) asm volatile("" : "+a"(qf[ks]));
+        };
+        // The reference maximum of head j (base 2) moves only when a tile's
+        // maximum outgrows it by 2^8; the weights of that tile are then taken
+        // relative to the new reference, and the accumulator and running sum
+        // (the earlier tiles' weighted sums, relative to the old one) are
+        // scaled by alpha once the pending weighted sum has been added.  So the
+        // weights are at most 2^8 and never wait for a rescale.
+        struct Ref {
+            float m, alpha;
+            bool grow;
+        };
+        auto new_reference = [&](float mx) -> Ref {
+            {  // with lane l ^ 32 (the other half of the tile's rows), without an LDS round trip
+                const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                mx = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
             }
-            s_prev = masked(lt, sv);
-            settle_reference(s_prev);
-        }
-        // the last tile's weights and weighted sum
-        {
-            bf16x8 ph[2], pl[2];
-            weights(s_prev, ph, pl);
+            mx *= scale2;  // base-2 maximum of this tile for head j (scale2 > 0 keeps the order)
+            Ref r;
+            r.grow = mx > m_ref + kLazyRescale;
+            r.m = r.grow ? mx : m_ref;
+            // exp2(-inf) = 0 when the first valid tile arrives (nothing accumulated yet)
+            r.alpha = __builtin_amdgcn_exp2f(r.grow ? m_ref - mx : 0.f);
+            return r;
+        };
+        // Weights of one tile relative to reference m (at most 2^8), split into
+        // a high part (the weight truncated to bf16) and a low part (the exact
+        // remainder, rounded to bf16); their sum is returned.  While no row has
+        // been valid m is -inf and every logit -inf: 0 is then used as the
+        // reference, so that every weight is exp2(-inf) = 0.
+        auto weight_pair = [&](float p0, float p1, bf16x8 &pw, bf16x8 &pl, int e, float &lsum) {
+            const uint32_t b0 = __float_as_uint(p0) & 0xffff0000u, b1 = __float_as_uint(p1) & 0xffff0000u;
+            const bf16x2_t h2 = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(b1, b0, 0x07060302u));
+            const bf16x2_t lo = {(__bf16)(p0 - __uint_as_float(b0)), (__bf16)(p1 - __uint_as_float(b1))};
+            pw[e - 1] = h2[0];
+            pw[e] = h2[1];
+            pl[e - 1] = lo[0];
+            pl[e] = lo[1];
+            lsum += p0 + p1;
+        };
+        auto weights = [&](const floatx16 &sv, float m, bf16x8 (&pw)[2], bf16x8 (&pl)[2]) -> float {
+            const float mneg = m == -INFINITY ? 0.f : -m;
+            float lsum = 0.f;
+#pragma unroll
+            for (int e = 1; e < 16; e += 2)
+                weight_pair(__builtin_amdgcn_exp2f(fmaf(sv[e - 1], scale2, mneg)),
+                            __builtin_amdgcn_exp2f(fmaf(sv[e], scale2, mneg)), pw[e >> 3], pl[e >> 3], e & 7, lsum);
+            return lsum;
+        };
+        // weighted sum of the tile whose V^T fragments are vf, hi then lo parts
+        auto weighted_sum = [&](const bf16x8 (&vf)[2][8], const bf16x8 (&ph)[2], const bf16x8 (&pl)[2]) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                bf16x8 v[8];
 #pragma unroll
-                for (int nb = 0; nb < 8; ++nb) {
-                    v[nb] = read_v(ntiles - 1, ks, nb);
-                    o[nb] = mfma32(v[nb], ph[ks], o[nb]);
+                for (int nb = 0; nb < 8; ++nb) o[nb] = mfma32(vf[ks][nb], ph[ks], o[nb]);
+#pragma unroll
+                for (int nb = 0; nb < 8; ++nb) o[nb] = mfma32(vf[ks][nb], pl[ks], o[nb]);
+            }
+        };
+
+        // Iteration lt (tile 0 is peeled: no weighted sum is pending before it):
+        //   barrier A: tile lt landed, the stage of tile lt-2 free
+        //   block 1: the logits of tile lt with the K reads of tile lt and the
+        //     row loads of tile lt+2; this wave's half of the logits published
+        //   barrier B
+        //   block 2: the weighted sum of tile lt-1 (32 MFMAs, its V^T fragments
+        //     already in registers) with, between them, the partner's half of
+        //     tile lt's logits, tile lt's maximum, reference and weights, and the
+        //     V^T reads of tile lt (each fragment right after its last use);
+        //     then the rare rescale, after the weighted sum it applies to.
+        // Block 1 is bound by the LDS reads of K, block 2 by its MFMAs; the V^T
+        // reads go where the LDS has room.
+        bf16x8 ph[2], pl[2];         // weights of the pending tile
+        bf16x8 vf[2][8];             // its V^T fragments
+        uint64_t nsrc[kDmaPerWave];  // row addresses of the next tile to load
+        next_sources(2, nsrc);
+        {
+            barrier_a();
+            pin_q();
+            const floatx16 acc = block1(0, nsrc);
+            publish(acc);
+            lds_barrier();
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int nb = 0; nb < 8; ++nb) vf[ks][nb] = read_v(0, ks, nb);
+            next_sources(min(3, ntiles + 1), nsrc);  // (tiles past ntiles + 1: not in the table)
+            const floatx16 sv = masked(0, with_partner(acc));
+            float mx = sv[0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sv[i]);
+            const Ref r = new_reference(mx);
+            m_ref = r.m;  // (nothing is accumulated yet)
+            l_run = weights(sv, m_ref, ph, pl);
+        }
+        for (int lt = 1; lt < ntiles; ++lt) {
+            barrier_a();
+            pin_q();
+            const floatx16 acc = block1(lt, nsrc);
+            publish(acc);
+            lds_barrier();
+            // (the weighted sum stays after the barrier: its MFMAs fill the wait
+            // for the partner's logits)
+            asm volatile("" : "+v"(ph[0]), "+v"(ph[1]), "+v"(pl[0]), "+v"(pl[1]));
+            // the first eighth of the weighted sum covers the partner's reads
+            floatx4 pv[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                o[q] = mfma32(vf[0][q], ph[0], o[q]);
+                pv[q] = xch[((wv ^ 1) * 4 + q) * 64 + lane];
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            floatx16 full = acc;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) full[4 * q + e] += pv[q][e];
+            // the next iteration's row addresses (tiles past ntiles + 1 are all
+            // fallback rows, like tile ntiles + 1)
+            next_sources(min(lt + 3, ntiles + 1), nsrc);
+            const floatx16 sv = masked(lt, full);
+            // The other 28 MFMAs in a fixed order (MFMA i: K-step i/16, high
+            // part for i%16 < 8, block i%8), each with a slice of tile lt's work:
+            // its maximum (steps 4-7), reference (8), one weight per step
+            // (9-24), and the V^T fragment that MFMA i used for the last time.
+            float m4[4], pr[16];
+            Ref r;
+            float mneg = 0.f, lsum = 0.f;
+            bf16x8 nh[2], nl[2];
+#pragma unroll
+            for (int i = 4; i < 32; ++i) {
+                const int ks = i >> 4, nb = i & 7;
+                const bool lo = (i & 8) != 0;
+                o[nb] = mfma32(vf[ks][nb], lo ? pl[ks] : ph[ks], o[nb]);
+                if (lo) vf[ks][nb] = read_v(lt, ks, nb);
+                if (i >= 4 && i < 8) {
+                    const int q = i - 4;
+                    m4[q] = fmaxf(fmaxf(sv[4 * q], sv[4 * q + 1]), fmaxf(sv[4 * q + 2], sv[4 * q + 3]));
                 }
+                if (i == 8) {
+                    r = new_reference(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+                    mneg = r.m == -INFINITY ? 0.f : -r.m;
+                    // (kept here: otherwise this is sunk past the MFMAs)
+                    asm volatile("" : "+v"(mneg), "+v"(r.m), "+v"(r.alpha));
+                }
+                if (i >= 9 && i < 25) {
+                    const int e = i - 9;
+                    pr[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], scale2, mneg));
+                    if (e & 1) weight_pair(pr[e - 1], pr[e], nh[e >> 3], nl[e >> 3], e & 7, lsum);
+                }
+                if (i == 24) asm volatile("" : "+v"(nh[0]), "+v"(nh[1]), "+v"(nl[0]), "+v"(nl[1]), "+v"(lsum));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (__ballot(r.grow)) {  // (wave-uniform; rare after the first valid tile)
+                l_run *= r.alpha;
 #pragma unroll
-                for (int nb = 0; nb < 8; ++nb) o[nb] = mfma32(v[nb], pl[ks], o[nb]);
+                for (int nb = 0; nb < 8; ++nb) o[nb] *= r.alpha;
+            }
+            m_ref = r.m;
+            l_run += lsum;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                ph[ks] = nh[ks];
+                pl[ks] = nl[ks];
             }
         }
+        // the last tile's weighted sum
+        weighted_sum(vf, ph, pl);
         // the loads issued past the last tile land before the workgroup's LDS is released
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 
     // lanes j and j + 32 hold the two halves of head j's rows
-    float l = l_run + __shfl_xor(l_run, 32);
-    if (head >= a.H) return;
+    const float l = l_run + __shfl_xor(l_run, 32);
+    // The block of outputs (final or split partial) is H rows of kD floats,
+    // contiguous in memory.  O^T registers hold 16-byte pieces of 32 different
+    // rows per store, so the block is first transposed through the (now idle)
+    // tile stages and then written in whole 1 KiB lines per wavefront.
+    // (Every wave's loads have landed: the wait after the loop; after this
+    // barrier no wave reads a tile any more.)
+    __syncthreads();
+    float *stage = (float *)smem;  // [64 heads][kOutRS]
+    const float f = a.n_splits == 1 ? (l > 0.f ? 1.f / l : 0.f) : 1.f;
     // O^T register r of block nb: column dcol0 + 32 nb + 8 (r/4) + 4 hh + r%4
-    if (a.n_splits == 1) {
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        float *orow = a.out + (row * a.H + head) * (int64_t)kD + dcol0 + 4 * hh;
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb)
+    for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *(floatx4 *)(orow + nb * 32 + 8 * q) =
-                    floatx4{o[nb][4 * q], o[nb][4 * q + 1], o[nb][4 * q + 2], o[nb][4 * q + 3]} * inv;
-        if (a.lse && hh == 0 && dh == 0) a.lse[row * a.H + head] = l > 0.f ? (m_ref + __log2f(l)) * kLn2 : -INFINITY;
-    } else {
-        const int64_t slot = (row * a.n_splits + split) * a.H + head;
-        float *po = a.part_o + slot * kD + dcol0 + 4 * hh;
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *(floatx4 *)(po + nb * 32 + 8 * q) =
-                    floatx4{o[nb][4 * q], o[nb][4 * q + 1], o[nb][4 * q + 2], o[nb][4 * q + 3]};
-        if (hh == 0 && dh == 0) {
+        for (int q = 0; q < 4; ++q)
+            *(floatx4 *)(stage + head * kOutRS + dcol0 + 32 * nb + 8 * q + 4 * hh) =
+                floatx4{o[nb][4 * q], o[nb][4 * q + 1], o[nb][4 * q + 2], o[nb][4 * q + 3]} * f;
+    if (head < a.H && hh == 0 && dh == 0) {
+        if (a.n_splits == 1) {
+            if (a.lse) a.lse[row * a.H + head] = l > 0.f ? (m_ref + __log2f(l)) * kLn2 : -INFINITY;
+        } else {
+            const int64_t slot = (row * a.n_splits + split) * a.H + head;
             a.part_ml[slot * 2 + 0] = m_ref;  // base 2
             a.part_ml[slot * 2 + 1] = l;
         }
     }
+    __syncthreads();
+    float *dst = a.n_splits == 1 ? a.out + row * a.H * (int64_t)kD
+                                 : a.part_o + (row * a.n_splits + split) * a.H * (int64_t)kD;
+    const int n4 = a.H * (kD / 4);
+    for (int f4 = tid; f4 < n4; f4 += kWT)
+        *(floatx4 *)(dst + 4 * (int64_t)f4) = *(const floatx4 *)(stage + (f4 >> 7) * kOutRS + 4 * (f4 & 127));
 }
 
 hipError_t launch_mqa_wide(const MqaArgs &a, int64_t rows, hipStream_t st) {
