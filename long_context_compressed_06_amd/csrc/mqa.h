@@ -17,6 +17,9 @@ struct MqaArgs {
     const void *q, *entries, *raw;
     const int32_t *idx;
     float *out, *lse, *part_o, *part_ml;
+    // the wide kernel's split partials: part_o holds f16 values O / l / sigma,
+    // part_sc the power of two sigma of each (query, split)
+    float *part_sc;
 };
 
 constexpr float kLog2e = 1.4426950408889634f;

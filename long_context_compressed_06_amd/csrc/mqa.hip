@@ -390,6 +390,53 @@ __global__ __launch_bounds__(128) void k_combine(int H, int D, int n_splits, con
     if (lse && threadIdx.x == 0) lse[rh] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
 }
 
+// The same merge for the wide kernel's partials: f16 normalised partials
+// O_s / l_s / sigma_s, so split s enters with weight l_s 2^(m_s - M) sigma_s.
+template <int CB>
+__global__ __launch_bounds__(128) void k_combine16(int H, int D, int n_splits, const _Float16 *__restrict__ part_o,
+                                                   const float *__restrict__ part_ml,
+                                                   const float *__restrict__ part_sc, float *__restrict__ out,
+                                                   float *__restrict__ lse) {
+    typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
+    const int64_t rh = xcd_rank((int)gridDim.x);
+    const int64_t row = rh / H;
+    const int h = (int)(rh % H);
+    const int x = min((int)threadIdx.x * 4, D - 4);
+    float M = -INFINITY, L = 0.f;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < n_splits; s0 += CB) {
+        float ms[CB], ls[CB], ss[CB];
+        halfx4 po[CB];
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+            const int64_t rs = row * n_splits + min(s0 + u, n_splits - 1);
+            const int64_t slot = rs * H + h;
+            ms[u] = part_ml[slot * 2];
+            ls[u] = s0 + u < n_splits ? part_ml[slot * 2 + 1] : 0.f;
+            ss[u] = part_sc[rs];
+            po[u] = *(const halfx4 *)(part_o + slot * D + x);
+        }
+        float Mc = M;
+#pragma unroll
+        for (int u = 0; u < CB; ++u) Mc = ls[u] > 0.f ? fmaxf(Mc, ms[u]) : Mc;
+        if (Mc > M) {  // (more than one batch of splits only)
+            const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mc);
+            L *= sc;
+            acc *= sc;
+            M = Mc;
+        }
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+            const float wl = ls[u] > 0.f ? ls[u] * __builtin_amdgcn_exp2f(ms[u] - M) : 0.f;
+            L += wl;
+            acc += (wl * ss[u]) * __builtin_convertvector(po[u], floatx4);
+        }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    if ((int)threadIdx.x * 4 < D) *(floatx4 *)(out + rh * D + x) = acc * inv;
+    if (lse && threadIdx.x == 0) lse[rh] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+}
+
 int mqa_choose_splits(int64_t rows, int64_t n_rows_max, int d, int *tiles_per_split) {
     int64_t tiles = (n_rows_max + 31) / 32;
     if (tiles < 1) tiles = 1;
@@ -420,6 +467,25 @@ static hipError_t launch_combine(const MqaArgs &a, int64_t rows, int D, hipStrea
     else
         hipLaunchKernelGGL(k_combine<kMqaMaxSplits>, grid, dim3(128), 0, st, a.H, D, a.n_splits, a.part_o,
                            a.part_ml, a.out, a.lse);
+    return hipGetLastError();
+}
+
+static hipError_t launch_combine16(const MqaArgs &a, int64_t rows, int D, hipStream_t st) {
+    if (a.n_splits == 1) return hipSuccess;
+    const dim3 grid((unsigned)(rows * a.H));
+    const _Float16 *po = (const _Float16 *)a.part_o;
+    if (a.n_splits <= 4)
+        hipLaunchKernelGGL(k_combine16<4>, grid, dim3(128), 0, st, a.H, D, a.n_splits, po, a.part_ml, a.part_sc,
+                           a.out, a.lse);
+    else if (a.n_splits <= 8)
+        hipLaunchKernelGGL(k_combine16<8>, grid, dim3(128), 0, st, a.H, D, a.n_splits, po, a.part_ml, a.part_sc,
+                           a.out, a.lse);
+    else if (a.n_splits <= 12)
+        hipLaunchKernelGGL(k_combine16<12>, grid, dim3(128), 0, st, a.H, D, a.n_splits, po, a.part_ml, a.part_sc,
+                           a.out, a.lse);
+    else
+        hipLaunchKernelGGL(k_combine16<kMqaMaxSplits>, grid, dim3(128), 0, st, a.H, D, a.n_splits, po, a.part_ml,
+                           a.part_sc, a.out, a.lse);
     return hipGetLastError();
 }
 
@@ -461,12 +527,14 @@ hipError_t launch_mqa(int dt, int B, int Tq, int H, int d, int N, int m, int k, 
     a.q = q; a.entries = entries; a.raw = raw; a.idx = idx; a.out = out; a.lse = lse;
     a.part_o = ws;
     a.part_ml = ws ? ws + rows * n_splits * H * (int64_t)d : nullptr;
+    // (the wide kernel's f16 partials fill half of part_o; their scales follow)
+    a.part_sc = ws ? (float *)((char *)ws + rows * n_splits * H * (int64_t)d * 2) : nullptr;
     if (dt == 0) return launch_mqa_dt<float>(d, a, rows, st);
     if (d == 512 && H > 32) {
         // 32-head waves with 32x32x16 MFMAs (mqa_wide.hip)
         const hipError_t e = launch_mqa_wide(a, rows, st);
         if (e != hipSuccess) return e;
-        return launch_combine(a, rows, d, st);
+        return launch_combine16(a, rows, d, st);
     }
     return launch_mqa_dt<bf16_t>(d, a, rows, st);
 }

@@ -39,6 +39,7 @@ namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWT = 256;                // threads (four wavefronts)
 constexpr int kTR = 32;                 // rows per tile
@@ -440,22 +441,34 @@ __global__ __launch_bounds__(kWT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     // lanes j and j + 32 hold the two halves of head j's rows
     const float l = l_run + __shfl_xor(l_run, 32);
-    // The block of outputs (final or split partial) is H rows of kD floats,
-    // contiguous in memory.  O^T registers hold 16-byte pieces of 32 different
-    // rows per store, so the block is first transposed through the (now idle)
-    // tile stages and then written in whole 1 KiB lines per wavefront.
+    // The block of outputs is H rows of kD values, contiguous in memory: the
+    // final output (f32) or, with several splits, the split's normalised
+    // partial O / l in f16 (half the bytes of the f32 sum: the merge of the
+    // partials reads them all back), scaled by a power of two sigma that keeps
+    // the block's largest magnitude below 2^14 (sigma = 1 unless the values are
+    // that large).  O^T registers hold 16-byte pieces of 32 different rows per
+    // store, so the block is first transposed through the (now idle) tile
+    // stages and then written in whole lines per wavefront.
     // (Every wave's loads have landed: the wait after the loop; after this
     // barrier no wave reads a tile any more.)
     __syncthreads();
     float *stage = (float *)smem;  // [64 heads][kOutRS]
-    const float f = a.n_splits == 1 ? (l > 0.f ? 1.f / l : 0.f) : 1.f;
+    const float f = l > 0.f ? 1.f / l : 0.f;
     // O^T register r of block nb: column dcol0 + 32 nb + 8 (r/4) + 4 hh + r%4
+    float amax = 0.f;
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            *(floatx4 *)(stage + head * kOutRS + dcol0 + 32 * nb + 8 * q + 4 * hh) =
-                floatx4{o[nb][4 * q], o[nb][4 * q + 1], o[nb][4 * q + 2], o[nb][4 * q + 3]} * f;
+        for (int q = 0; q < 4; ++q) {
+            const floatx4 v = floatx4{o[nb][4 * q], o[nb][4 * q + 1], o[nb][4 * q + 2], o[nb][4 * q + 3]} * f;
+            *(floatx4 *)(stage + head * kOutRS + dcol0 + 32 * nb + 8 * q + 4 * hh) = v;
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+        }
+    if (head >= a.H) amax = 0.f;
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) amax = fmaxf(amax, __shfl_xor(amax, sh));
+    float *red = (float *)xch;  // (the logits exchange area is idle too)
+    if (lane == 0) red[wv] = amax;
     if (head < a.H && hh == 0 && dh == 0) {
         if (a.n_splits == 1) {
             if (a.lse) a.lse[row * a.H + head] = l > 0.f ? (m_ref + __log2f(l)) * kLn2 : -INFINITY;
@@ -466,11 +479,23 @@ __global__ __launch_bounds__(kWT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
     }
     __syncthreads();
-    float *dst = a.n_splits == 1 ? a.out + row * a.H * (int64_t)kD
-                                 : a.part_o + (row * a.n_splits + split) * a.H * (int64_t)kD;
     const int n4 = a.H * (kD / 4);
-    for (int f4 = tid; f4 < n4; f4 += kWT)
-        *(floatx4 *)(dst + 4 * (int64_t)f4) = *(const floatx4 *)(stage + (f4 >> 7) * kOutRS + 4 * (f4 & 127));
+    if (a.n_splits == 1) {
+        float *dst = a.out + row * a.H * (int64_t)kD;
+        for (int f4 = tid; f4 < n4; f4 += kWT)
+            *(floatx4 *)(dst + 4 * (int64_t)f4) = *(const floatx4 *)(stage + (f4 >> 7) * kOutRS + 4 * (f4 & 127));
+    } else {
+        const float bmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        int e = 0;
+        (void)frexpf(bmax, &e);  // bmax < 2^e
+        const int se = e > 14 ? min(e - 14, 115) : 0;
+        const float inv_sigma = __uint_as_float((uint32_t)(127 - se) << 23);  // 2^-se (se <= 115)
+        halfx4 *dst = (halfx4 *)a.part_o + (row * a.n_splits + split) * a.H * (int64_t)(kD / 4);
+        for (int f4 = tid; f4 < n4; f4 += kWT)
+            dst[f4] = __builtin_convertvector(
+                *(const floatx4 *)(stage + (f4 >> 7) * kOutRS + 4 * (f4 & 127)) * inv_sigma, halfx4);
+        if (tid == 0) a.part_sc[row * a.n_splits + split] = __uint_as_float((uint32_t)(127 + se) << 23);
+    }
 }
 
 hipError_t launch_mqa_wide(const MqaArgs &a, int64_t rows, hipStream_t st) {
