@@ -62,6 +62,9 @@ template <int NT>
 __device__ Digit find_digit(const uint32_t *hist, int nbins, int rem, int *sh, Digit *shd) {
     const int per = nbins / NT;
     const int tid = threadIdx.x;
+    // (a histogram holding fewer than rem keys has no such digit: then digit 0
+    // with nothing above it, so the selection stays inside the row and k)
+    if (tid == 0) *shd = Digit{0u, 0, 0};
     int own = 0;
     for (int q = 0; q < per; ++q) own += (int)hist[tid * per + q];
     int total;
@@ -189,7 +192,7 @@ __device__ void select_row_global(const float *srow, int64_t nv, int k, Digit d,
     auto key_at = [&](int64_t j) -> uint32_t { return order_key(srow[j]); };
     if (d.at != rem) refine<kNT>(key_at, nv, prefix, mask, rem, hist, sh, shd);
     ordered_keep<kNT>(key_at, nv, prefix, mask, rem, sh, [&](int pos, int64_t j) {
-        if (pos < k) orow[pos] = (int32_t)j;
+        if (pos >= 0 && pos < k) orow[pos] = (int32_t)j;
     });
 }
 
@@ -202,7 +205,7 @@ __device__ void select_items(const IdxKey *items, int M, int k, Digit d, int32_t
     auto key_at = [&](int64_t i) -> uint32_t { return items[i].key; };
     if (d.at != rem) refine<kNT>(key_at, M, prefix, mask, rem, hist, sh, shd);
     ordered_keep<kNT>(key_at, M, prefix, mask, rem, sh, [&](int pos, int64_t i) {
-        if (pos < k) orow[pos] = items[i].j;
+        if (pos >= 0 && pos < k) orow[pos] = items[i].j;
     });
 }
 
