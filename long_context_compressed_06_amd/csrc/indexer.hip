@@ -179,6 +179,15 @@ __device__ __forceinline__ void lds_dma16_nt(uint32_t lds_addr, const void *src)
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(lds_addr), "v"(src)
                  : "memory", "m0");
 }
+// The same from a wave-uniform base address in scalar registers plus a 32-bit
+// per-lane byte offset.  Five wait states before the load: the base may have
+// just been written by the vector unit (readfirstlane), which the code
+// generator does not track into inline assembly.
+__device__ __forceinline__ void lds_dma16_nt_s(uint32_t lds_addr, uint32_t voff, uint64_t base) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(lds_addr), "v"(voff),
+                 "s"(base)
+                 : "memory", "m0");
+}
 
 // max(x, 0) on the bit pattern: negative floats are negative integers, so one
 // integer max (no NaN canonicalisation of the MFMA result first)
@@ -232,37 +241,53 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_dma(int Tq, int N, int
     const bf16_t *kb = kI + (PAGED ? 0 : b * kl.bstride);
     unsigned char *my_ring = ring + wv * S::STAGES * S::TB;
     const uint32_t ring_addr = (uint32_t)(uintptr_t)my_ring;
-    const int64_t tstride = (int64_t)wpr * 16 * DI;  // elements between this wavefront's tiles
-    const bf16_t *src0[S::IPT];
+    // A whole tile (16 rows, contiguous in memory: pages are multiples of 16
+    // rows) is one wave-uniform base address plus a fixed byte offset per lane.
+    uint32_t voff[S::IPT];
 #pragma unroll
     for (int ip = 0; ip < S::IPT; ++ip) {
-        const int byte = ip * 1024 + lane * 16;       // within the tile
+        const int byte = ip * 1024 + lane * 16;  // within the tile
         const int r = byte / S::RB, pos = (byte % S::RB) / 16;
-        src0[ip] = kb + ((int64_t)gw * 16 + r) * DI + S::swz(r, pos) * 8;
+        voff[ip] = (uint32_t)((r * DI + S::swz(r, pos) * 8) * 2);
     }
+    // paged: the page of the next tile to issue, read from LDS one issue ahead
+    // (so no issue waits on its own page lookup)
+    int32_t pg_next = 0;
+    auto page_entry = [&](int i) -> int32_t {
+        const int64_t t = gw + (int64_t)i * wpr;
+        return pl[min((t * 16) >> kl.pshift, (int64_t)kMaxPagesPerSeq - 1)];
+    };
     auto issue = [&](int i) {
         const int t = gw + i * wpr;
         const int slot = i % S::STAGES;
         const bool whole = (int64_t)t * 16 + 16 <= nv;
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the slot are done
-        // paged: the tile's 16 rows lie in one page (pages are multiples of 16 rows)
-        const int64_t prow = PAGED ? ((int64_t)pl[((int64_t)t * 16) >> kl.pshift] << kl.pshift) |
-                                           (((int64_t)t * 16) & ((1 << kl.pshift) - 1))
-                                     : 0;
+        // earlier reads of the slot (and the page lookup) are done
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        // first row of the tile: the pool row (paged) or the row in the sequence
+        int64_t row0 = (int64_t)t * 16;
+        if constexpr (PAGED) {
+            const int64_t pg = (uint32_t)__builtin_amdgcn_readfirstlane(pg_next);
+            row0 = (pg << kl.pshift) | (row0 & ((1 << kl.pshift) - 1));
+            if (i + 1 < n_vis) pg_next = page_entry(i + 1);
+        }
+        const uint32_t lds0 = __builtin_amdgcn_readfirstlane(ring_addr + slot * S::TB);
+        if (whole) {
+            // (wave-uniform; readfirstlane makes it scalar for the compiler too)
+            const uint64_t b64 = (uint64_t)((PAGED ? kI : kb) + row0 * DI);
+            const uint64_t base = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32)) << 32) |
+                                  (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b64);
 #pragma unroll
-        for (int ip = 0; ip < S::IPT; ++ip) {
-            const bf16_t *src = src0[ip] + i * tstride;
-            if constexpr (PAGED) {
+            for (int ip = 0; ip < S::IPT; ++ip) lds_dma16_nt_s(lds0 + ip * 1024, voff[ip], base);
+        } else {
+            // the tile holding the last visible entry: rows past it reread that entry
+#pragma unroll
+            for (int ip = 0; ip < S::IPT; ++ip) {
                 const int byte = ip * 1024 + lane * 16;
                 const int r = byte / S::RB, pos = (byte % S::RB) / 16;
-                const int64_t rr = whole ? r : min((int64_t)t * 16 + r, nv - 1) - (int64_t)t * 16;
-                src = kI + (prow + rr) * DI + S::swz(r, pos) * 8;
-            } else if (!whole) {
-                const int byte = ip * 1024 + lane * 16;
-                const int r = byte / S::RB, pos = (byte % S::RB) / 16;
-                src = kb + min((int64_t)t * 16 + r, nv - 1) * DI + S::swz(r, pos) * 8;
+                const int64_t rr = min((int64_t)t * 16 + r, nv - 1) - (int64_t)t * 16;
+                const bf16_t *src = (PAGED ? kI : kb) + (row0 + rr) * DI + S::swz(r, pos) * 8;
+                lds_dma16_nt(lds0 + ip * 1024, src);
             }
-            lds_dma16_nt(__builtin_amdgcn_readfirstlane(ring_addr + slot * S::TB + ip * 1024), src);
         }
     };
 
@@ -298,6 +323,8 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_dma(int Tq, int N, int
         }
     }
     // (issued after the barrier above, which waits for every load in flight)
+    if constexpr (PAGED)
+        if (n_vis > 0) pg_next = page_entry(0);
     for (int i = 0; i < S::STAGES - 1 && i < n_vis; ++i) issue(i);
 
     float *srow = scores + row * s_stride;
