@@ -143,6 +143,7 @@ def time_graphs(graphs, steps, warmup, multi=None, per_multi=1):
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
+MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 (MXFP4) MFMA peak
 
 
 def algorithmic_flops(wl) -> dict:
@@ -190,11 +191,16 @@ def bench_workload(wl, steps, warmup, with_kernel=True, with_mfma=False):
         km = capture(lambda: [idx_call[i % R]() for i in range(8)])
         res["indexer_ms"] = time_graphs(kg, steps, warmup, km, 8)
         del sc, kg, km
-    if with_mfma and wl.mode == "csa" and wl.index_fmt == "elem":
+    if with_mfma and wl.mode == "csa":
         # the two MFMA-bound kernels alone (prefill chunks), each timed from graphs over the replicas
         sc = [torch.empty((wl.B, wl.Tq, wl.N), dtype=torch.float32, device="cuda") for _ in xs]
-        idx_call = [lambda x=x, o=o: csa.csa_index_scores(x["q_idx"], x["w_idx"], x["k_idx"], wl.N, wl.m,
-                                                          wl.q_pos0, scores=o) for x, o in zip(xs, sc)]
+        if wl.index_fmt == "mx4":
+            idx_call = [lambda x=x, o=o: csa.csa_index_scores_mx4(x["q_idx"], x["w_idx"], x["k_codes"],
+                                                                  x["k_scales"], wl.N, wl.m, wl.q_pos0, scores=o)
+                        for x, o in zip(xs, sc)]
+        else:
+            idx_call = [lambda x=x, o=o: csa.csa_index_scores(x["q_idx"], x["w_idx"], x["k_idx"], wl.N, wl.m,
+                                                              wl.q_pos0, scores=o) for x, o in zip(xs, sc)]
         res["indexer_ms"] = time_graphs([capture(f) for f in idx_call], max(3, steps // 4), 2)
         del sc
         att_call = [lambda s=s, x=x: csa.csa_sparse_mqa(x["q"], x["entries"], s.topk_idx, x["raw"], wl.N, wl.m, wl.W,
@@ -500,9 +506,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2", help="c2 (default; the metric's configuration) or another config")
-    ap.add_argument("--also", default="c3,c5,c4,c2x,c5x,l2,l2x,l2c,p1,r1,r1p,r2",
+    ap.add_argument("--also", default="c3,c5,c4,c2x,c5x,c4x,l2,l2x,l2c,p1,r1,r1p,r2",
                     help="secondary workloads ('' for none); c4: the 64K prefill chunk (tokens/s and the MFMA "
-                         "fractions of its indexer and attention); c2x/c5x: FP4 (MXFP4) indexer operands; "
+                         "fractions of its indexer and attention); c2x/c5x/c4x: FP4 (MXFP4) indexer operands; "
                          "l2/l2x/l2c: decode loops with cache maintenance (l2c: per-channel pooling, pooled "
                          "index keys); p1: a whole chunked prefill from 0; r1/r2: ragged decode (lengths "
                          "96K..158K) through one CSA layer / a CSA + HCA stack, one graph per token; r1p: r1 with "
@@ -611,9 +617,11 @@ def main():
             fl = algorithmic_flops(w2)
             for kern in ("indexer", "attention"):
                 tf = fl[kern] / (r2[kern + "_ms"] * 1e-3) / 1e12
-                also[w2.name][kern + "_mfma"] = {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
+                # (an FP4 indexer against the FP4 peak, everything else against bf16's)
+                pk = MFMA_FP4_PEAK_TFLOPS if kern == "indexer" and w2.index_fmt == "mx4" else MFMA_BF16_PEAK_TFLOPS
+                also[w2.name][kern + "_mfma"] = {"bound": "mfma", "achieved": tf, "peak": pk,
                                                  "unit": "TFLOP/s",
-                                                 "frac": checked_frac(tf / MFMA_BF16_PEAK_TFLOPS, w2.name + " " + kern),
+                                                 "frac": checked_frac(tf / pk, w2.name + " " + kern),
                                                  "flops_per_launch": fl[kern], "avg_launch_ms": r2[kern + "_ms"]}
         if not args.no_cpu_baseline and name in BASELINE_ALSO:
             log(f"[bench] cpu baseline (oracle) {w2.name}")

@@ -336,6 +336,17 @@ int csa_index_topk_mx4(int dt, int B, int Tq, int N, int H_I, int d_I, int m, in
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * csa_index_scores_mx4 -- the FP4 lightning indexer alone: the scores of
+ * csa_index_topk_mx4 (same operands, quantisation and rules), -inf for
+ * j >= n_visible(t); no selection, no workspace.
+ *   scores    [B, Tq, N] f32 (output, dense)
+ */
+int csa_index_scores_mx4(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int64_t q_pos0,
+                         const void *q_idx, const float *w_idx,
+                         const uint8_t *k_codes, const uint8_t *k_scales, int64_t k_bstride,
+                         float *scores, void *stream);
+
+/*
  * csa_sparse_mqa -- shared-KV multi-query attention over the selected
  * entries plus the raw window, one softmax (overview page, section 2.2
  * step 3: selected entries act as both key and value, all heads share them).

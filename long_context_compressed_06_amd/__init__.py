@@ -25,7 +25,7 @@ EXPORTS = ("csa_abi_version", "csa_status_string", "csa_last_error_detail", "csa
            "csa_sparse_mqa", "hca_dense_mqa", "csa_mx4_quantize", "csa_index_topk_mx4", "csa_append_rows",
            "csa_compress_channels", "csa_append_rows_multi", "csa_positions_advance", "csa_ragged_compress",
            "csa_ragged_index_topk", "csa_ragged_index_topk_mx4", "csa_ragged_sparse_mqa", "hca_ragged_dense_mqa", "csa_stream_read",
-           "csa_index_topk_noalloc")
+           "csa_index_topk_noalloc", "csa_index_scores_mx4")
 
 
 class AppendJob(ctypes.Structure):
@@ -77,6 +77,8 @@ def lib():
     L.csa_mx4_quantize.argtypes = [I, I64, I, P, P, P, P]
     L.csa_mx4_quantize.restype = I
     L.csa_index_topk_mx4.argtypes = [I, I, I, I, I, I, I, I, I64, P, P, P, P, I64, P, P, P, SZ, P]
+    L.csa_index_scores_mx4.argtypes = [I, I, I, I, I, I, I, I64, P, P, P, P, I64, P, P]
+    L.csa_index_scores_mx4.restype = I
     L.csa_index_topk_mx4.restype = I
     L.csa_append_rows.argtypes = [I, I, I64, P, I64, P, I64, I64, I64, I64, P]
     L.csa_compress_channels.argtypes = [I, I, I, I, I, P, I64, P, I64, P, I64, P]
@@ -251,6 +253,35 @@ def csa_mx4_quantize(x: torch.Tensor, codes=None, scales=None):
     n_rows = x.numel() // d if d else 0
     _check(lib().csa_mx4_quantize(_dt(x), n_rows, d, _p(x), _p(codes), _p(scales), _stream(x)))
     return codes, scales
+
+
+def csa_index_scores_mx4(q_idx, w_idx, k_codes, k_scales, N: int, m: int, q_pos0: int, scores=None) -> torch.Tensor:
+    """FP4 (MXFP4) indexer only: scores [B,Tq,N] f32 (-inf for entries not yet visible); operands as for
+    csa_index_topk_mx4."""
+    _need(q_idx, "q_idx", dims=4)
+    _need(w_idx, "w_idx", torch.float32, 3)
+    _need(k_codes, "k_codes", torch.uint8, 3)
+    _need(k_scales, "k_scales", torch.uint8, 3)
+    B, Tq, HI, dI = q_idx.shape
+    rb = dI // 2
+    if (w_idx.shape != (B, Tq, HI) or k_codes.shape[2] != rb or k_scales.shape[:2] != k_codes.shape[:2]
+            or k_scales.shape[2] != dI // 32):
+        raise ValueError("shape mismatch between the index operands")
+    if not (q_idx.is_contiguous() and w_idx.is_contiguous()):
+        raise ValueError("q_idx and w_idx must be contiguous")
+    if k_codes.stride(1) != rb or k_scales.stride(1) != dI // 32 or k_codes.shape[1] < N:
+        raise ValueError("k_codes / k_scales rows must be packed, with >= N rows")
+    cap = k_codes.stride(0) // rb
+    if k_codes.stride(0) != cap * rb or k_scales.stride(0) != cap * (dI // 32):
+        raise ValueError("k_codes and k_scales must share one batch stride in rows")
+    if scores is None:
+        scores = torch.empty((B, Tq, N), dtype=torch.float32, device=q_idx.device)
+    _need(scores, "scores", torch.float32, 3)
+    if scores.shape != (B, Tq, N) or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous [B, Tq, N] tensor")
+    _check(lib().csa_index_scores_mx4(_dt(q_idx), B, Tq, N, HI, dI, m, q_pos0, _p(q_idx), _p(w_idx), _p(k_codes),
+                                      _p(k_scales), cap, _p(scores), _stream(q_idx)))
+    return scores
 
 
 def csa_index_topk_mx4(q_idx, w_idx, k_codes, k_scales, N: int, m: int, k: int, q_pos0: int, topk_idx=None,

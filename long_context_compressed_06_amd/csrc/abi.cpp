@@ -562,6 +562,32 @@ int csa_index_topk_mx4(int dt, int B, int Tq, int N, int H_I, int d_I, int m, in
                                k_bstride, topk_idx, scores_out, workspace, workspace_bytes, stream);
 }
 
+int csa_index_scores_mx4(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int64_t q_pos0, const void *q_idx,
+                         const float *w_idx, const uint8_t *k_codes, const uint8_t *k_scales, int64_t k_bstride,
+                         float *scores, void *stream) {
+    if (int s = check_dt(dt)) return s;
+    if (B < 0 || Tq < 0 || N < 0) return fail(CSA_EINVAL, "B, Tq and N must be >= 0");
+    if (H_I < 1 || H_I > 64) return fail(CSA_EUNSUPPORTED, "H_I=%d outside 1..64", H_I);
+    if (!dI_supported(d_I)) return fail(CSA_EUNSUPPORTED, "d_I=%d not in {32,64,128}", d_I);
+    if (m < 1) return fail(CSA_EINVAL, "m=%d must be >= 1", m);
+    if (q_pos0 < 0) return fail(CSA_EINVAL, "q_pos0 must be >= 0");
+    if ((int64_t)B * Tq * N == 0) return ok();
+    if (!q_idx || !w_idx || !k_codes || !k_scales || !scores) return fail(CSA_EINVAL, "NULL tensor pointer");
+    if (k_bstride < N) return fail(CSA_EINVAL, "k_bstride smaller than N rows");
+    if (!aligned(q_idx, 16) || !aligned(k_codes, 16) || !aligned(w_idx, 4) || !aligned(scores, 4))
+        return fail(CSA_EALIGN, "q_idx/k_codes need 16-byte alignment");
+    const int64_t rows = (int64_t)B * Tq, rb = d_I / 2, kb = d_I / 32;
+    const Span ss = span(scores, B, (int64_t)Tq * N, (int64_t)Tq * N, 4);
+    if (overlap(ss, span(q_idx, 1, 0, rows * H_I * d_I, esize(dt))) || overlap(ss, span(w_idx, 1, 0, rows * H_I, 4)) ||
+        overlap(ss, span(k_codes, B, k_bstride * rb, (int64_t)N * rb, 1)) ||
+        overlap(ss, span(k_scales, B, k_bstride * kb, (int64_t)N * kb, 1)))
+        return fail(CSA_EINVAL, "scores overlaps an input");
+    return hip_status(csa::launch_index_mx4(dt, B, Tq, N, H_I, d_I, m, csa::QPos(q_pos0), q_idx, w_idx, k_codes,
+                                            k_scales, csa::RowMap(k_bstride), scores, N, nullptr, nullptr,
+                                            (hipStream_t)stream),
+                      "indexer launch");
+}
+
 int csa_ragged_index_topk_mx4(int dt, int B, int N, int H_I, int d_I, int m, int k, const int64_t *pos,
                               const void *q_idx, const float *w_idx, const uint8_t *k_codes,
                               const uint8_t *k_scales, int64_t k_bstride, const int32_t *page_table, int max_pages,

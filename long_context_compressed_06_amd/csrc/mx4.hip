@@ -519,11 +519,181 @@ static hipError_t launch_mx4_di(int B, int Tq, int N, int HI, int m, QPos q_pos0
     return launch_mx4_t<T, DI, 4>(B, Tq, N, HI, m, q_pos0, qI, w, kc, ks, k_bs, scores, s_stride, scores2, hist, st);
 }
 
+// ---------------------------------------------------------------------------
+// Many queries per sequence (prefill chunks) with MXFP4 operands: query-blocked
+// like the bf16 prefill indexer (indexer.hip).  One workgroup of kPmWaves
+// wavefronts serves kPmWaves consecutive queries of one sequence, one per
+// wavefront, so every key tile staged in LDS feeds kPmWaves queries.  A lane
+// (g, c) quantises exactly the blocks its A operands need (block g of heads
+// mb*16 + c), so the query never passes through LDS.  Key tiles of kPmRows
+// entries (their codes, 64 bytes per row, chunks swizzled as in
+// k_index_mx4_dma, then their scale dwords) stream HBM -> LDS by LDS-DMA with
+// kPmStages tiles in flight: per tile each wavefront moves one KiB of codes
+// and the scale dwords of 16 rows.  Per 16-entry block and head block, one
+// scaled 16x16x128 MFMA; the epilogue is the decode kernels' (ReLU, head
+// weight, head sum across the lane groups, score store, first top-k digit in a
+// per-query LDS histogram).
+constexpr int kPmWaves = 8;
+constexpr int kPmMinQueries = 64;  // queries per sequence from which the query-blocked kernel is used
+constexpr int kPmRows = 128;                        // entries per key tile
+constexpr int kPmStages = 4;
+constexpr int kPmCodeB = kPmRows * 64;              // code bytes per tile (8 KiB: one KiB per wavefront)
+constexpr int kPmTile = kPmCodeB + kPmRows * 4;     // + the scale dwords
+constexpr int kPmLds = kPmStages * kPmTile + kPmWaves * kTopkBins * 4;
+static_assert(kPmCodeB == kPmWaves * 1024 && kPmRows == kPmWaves * 16, "one KiB and 16 scale rows per wavefront");
+
+template <typename T, int MB>
+__global__ __launch_bounds__(kPmWaves * 64) void k_index_prefill_mx4(int Tq, int N, int HI, int m, QPos q_pos0,
+                                                                     int blocks_per_seq, const T *__restrict__ qI,
+                                                                     const float *__restrict__ w,
+                                                                     const uint8_t *__restrict__ kc,
+                                                                     const uint8_t *__restrict__ ks, int64_t k_bs,
+                                                                     float *__restrict__ scores, int64_t s_stride,
+                                                                     float *__restrict__ scores2,
+                                                                     uint32_t *__restrict__ hist) {
+    constexpr int DI = 128, RB = 64, KB = 4;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    unsigned char *ring = lds;
+    uint32_t *qh = (uint32_t *)(lds + kPmStages * kPmTile);  // [kPmWaves][kTopkBins]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, c = lane & 15;
+    const int64_t b = blockIdx.x / blocks_per_seq;
+    const int q0 = (blockIdx.x % blocks_per_seq) * kPmWaves;  // first query of the workgroup
+    const int ti = q0 + wv;
+    const bool on = ti < Tq;
+    const int64_t row = b * Tq + min(ti, Tq - 1);
+    const int64_t nv = on ? n_visible(q_pos0.at(b, ti), m, N) : 0;
+    // visible entries of the workgroup's last query bound every tile it computes
+    const int64_t nv_max = n_visible(q_pos0.at(b, min(q0 + kPmWaves, Tq) - 1), m, N);
+    const int vtiles = (int)((nv_max + kPmRows - 1) / kPmRows);
+
+    if (hist)
+        for (int i = lane; i < kTopkBins; i += 64) qh[wv * kTopkBins + i] = 0;
+    // the query's index heads as MXFP4 A operands (block g of head mb*16 + c),
+    // and the head weights
+    int32x8 a[MB];
+    int as[MB];
+    float wgt[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int head = mb * 16 + c;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        uint32_t sc = 127;
+        if (head < HI) quantize_block32(qI + (row * HI + head) * DI + g * 32, v, sc);
+        a[mb] = int32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        as[mb] = (int)sc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int hh = mb * 16 + 4 * g + e;
+            const float v = w[row * HI + min(hh, HI - 1)];
+            wgt[mb][e] = hh < HI ? v : 0.f;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // (vmcnt(0): the loads above are done before the DMAs start)
+
+    // DMA of key tile t into stage t % kPmStages: wavefront wv moves KiB wv of
+    // the codes (rows 16 wv .. 16 wv + 15) and, in 16 lanes, those rows' scale
+    // dwords.  Rows past the last visible entry reread it.
+    const uint8_t *kcb = kc + b * k_bs * RB;
+    const uint8_t *ksb = ks + b * k_bs * KB;
+    const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
+    const int cr = 16 * wv + (lane >> 2), cpos = lane & 3;  // this lane's code row and chunk position
+    const int sr = 16 * wv + (lane & 15);                   // its scale row (lanes 0-15)
+    auto issue = [&](int t) {
+        const uint32_t stage = ring_addr + (t % kPmStages) * kPmTile;
+        const int64_t jc = min((int64_t)t * kPmRows + cr, nv_max - 1);
+        const int64_t js = min((int64_t)t * kPmRows + sr, nv_max - 1);
+        lds_dma16_nt_mx4(__builtin_amdgcn_readfirstlane(stage + wv * 1024), kcb + jc * RB + mx4_swz(cr, cpos) * 16);
+        if (lane < 16) lds_dma4_nt_mx4(__builtin_amdgcn_readfirstlane(stage + kPmCodeB + wv * 64), ksb + js * KB);
+    };
+    // two DMA instructions per wavefront per tile (the scale one in 16 lanes, one count)
+    for (int t = 0; t < kPmStages - 1 && t < vtiles; ++t) issue(t);
+
+    float *srow = scores + row * s_stride;
+    float *srow2 = scores2 ? scores2 + row * (int64_t)N : nullptr;
+    for (int t = 0; t < vtiles; ++t) {
+        // this wave's share of tile t has landed (kPmStages-2 younger tiles may fly), then
+        // the barrier: every share has landed and every wave is done with tile t-1
+        if (t + kPmStages - 2 < vtiles)
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((kPmStages - 2) * 2) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        if (t + kPmStages - 1 < vtiles) issue(t + kPmStages - 1);
+        const unsigned char *tile = ring + (t % kPmStages) * kPmTile;
+#pragma unroll
+        for (int nb = 0; nb < kPmRows / 16; ++nb) {
+            const int r = nb * 16 + c;
+            const u32x4 kd = *(const u32x4 *)(tile + r * RB + mx4_swz(r, g) * 16);
+            const int bs = tile[kPmCodeB + r * KB + g];
+            const int32x8 bk = {(int)kd[0], (int)kd[1], (int)kd[2], (int)kd[3], 0, 0, 0, 0};
+            float sc = 0.f;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const floatx4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    a[mb], bk, floatx4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, as[mb], 0, bs);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sc += wgt[mb][e] * mx4_relu(acc[e]);
+            }
+            sc = mx4_sum_lane_groups(sc);
+            const int64_t j = (int64_t)t * kPmRows + r;
+            if (on && g == 0 && j < N) {
+                const float v = j < nv ? sc : -INFINITY;
+                srow[j] = v;
+                if (srow2) srow2[j] = v;
+                if (hist && j < nv) atomicAdd(&qh[wv * kTopkBins + (order_key(sc) >> (32 - kTopkBinBits))], 1u);
+            }
+        }
+    }
+    // entries past every query of the workgroup
+    if (on)
+        for (int64_t j = (int64_t)vtiles * kPmRows + lane; j < N; j += 64) {
+            srow[j] = -INFINITY;
+            if (srow2) srow2[j] = -INFINITY;
+        }
+    // (the loads issued past the last tile land before the workgroup's LDS is released)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (hist && on) {
+        // LDS operations of one wave complete in order: its histogram is final here
+        uint32_t *grow = hist + row * kTopkBins;
+        for (int i = lane; i < kTopkBins; i += 64) {
+            const uint32_t v = qh[wv * kTopkBins + i];
+            if (v) atomicAdd(&grow[i], v);
+        }
+    }
+}
+
+template <typename T, int MB>
+static hipError_t launch_prefill_mx4(int B, int Tq, int N, int HI, int m, QPos q_pos0, const void *qI, const float *w,
+                                     const uint8_t *kc, const uint8_t *ks, RowMap k_bs, float *scores,
+                                     int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
+    static const hipError_t attr = hipFuncSetAttribute((const void *)k_index_prefill_mx4<T, MB>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kPmLds);
+    if (attr != hipSuccess) return attr;
+    const int bps = (Tq + kPmWaves - 1) / kPmWaves;
+    hipLaunchKernelGGL((k_index_prefill_mx4<T, MB>), dim3((unsigned)((int64_t)B * bps)), dim3(kPmWaves * 64),
+                       kPmLds, st, Tq, N, HI, m, q_pos0, bps, (const T *)qI, w, kc, ks, k_bs.bstride, scores,
+                       s_stride, scores2, hist);
+    return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t launch_mx4_dt(int B, int Tq, int N, int HI, int dI, int m, QPos q_pos0, const void *qI,
                                 const float *w, const uint8_t *kc, const uint8_t *ks, RowMap k_bs, float *scores,
                                 int64_t s_stride, float *scores2, uint32_t *hist, hipStream_t st) {
     if (dI == 128 && ((uintptr_t)ks % 4) == 0) {  // (scale rows move as dwords)
+        // many queries per sequence, contiguous keys: the query-blocked kernel
+        if (Tq >= kPmMinQueries && !k_bs.ptab) {
+            if (HI <= 16)
+                return launch_prefill_mx4<T, 1>(B, Tq, N, HI, m, q_pos0, qI, w, kc, ks, k_bs, scores, s_stride,
+                                                scores2, hist, st);
+            if (HI <= 32)
+                return launch_prefill_mx4<T, 2>(B, Tq, N, HI, m, q_pos0, qI, w, kc, ks, k_bs, scores, s_stride,
+                                                scores2, hist, st);
+            return launch_prefill_mx4<T, 4>(B, Tq, N, HI, m, q_pos0, qI, w, kc, ks, k_bs, scores, s_stride, scores2,
+                                            hist, st);
+        }
         if (HI <= 16)
             return launch_mx4_dma<T, 1>(B, Tq, N, HI, m, q_pos0, qI, w, kc, ks, k_bs, scores, s_stride, scores2,
                                         hist, st);

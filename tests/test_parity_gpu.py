@@ -103,6 +103,11 @@ def test_c5x_csa_decode_1m_stress_fp4_indexer(csa):
     run_and_check(csa, CONFIGS["c5x"])
 
 
+def test_c4x_csa_prefill_chunk_fp4_indexer_all_rows(csa):
+    """The 64K prefill chunk with FP4 index operands (the query-blocked FP4 indexer), all 4096 rows."""
+    run_and_check(csa, CONFIGS["c4x"])
+
+
 # ------------------------------------------------------- small and ragged shapes
 SMALL = [
     # name, dtype, B, T, Tq, m, d, H, W, k, HI, dI

@@ -78,6 +78,9 @@ MX_CASES = [
     ("decode_m1_heads20", 2, 2500, 2, 1, 20, 128, 300, 16),
     ("queries_causal_d128", 2, 4 * 700 + 3, 40, 4, 64, 128, 128, 8),
     ("queries_early_d128", 1, 70, 70, 4, 8, 128, 5, 0),
+    # the query-blocked kernel: several workgroups of queries, a ragged last one, key tiles past N
+    ("prefill_blocks_d128", 2, 4 * 2100 + 3, 150, 4, 64, 128, 256, 8),
+    ("prefill_blocks_heads20", 1, 4 * 900, 77, 4, 20, 128, 64, 0),
 ]
 
 
@@ -139,3 +142,19 @@ def test_index_topk_mx4_nothing_visible(csa, orc):
                   seed_base=79000)
     say(wl)
     run_mx4(csa, orc, wl, 8)
+
+
+@pytest.mark.parametrize("shape", [(3, 4 * 3001 + 2, 1, 64), (2, 4 * 2100 + 3, 150, 64), (1, 4 * 900, 77, 20)],
+                         ids=["decode", "prefill_blocks", "prefill_heads20"])
+def test_index_scores_mx4_equals_index_topk_scores(csa, shape):
+    """csa_index_scores_mx4 runs the same indexer as csa_index_topk_mx4: identical scores, bit for bit."""
+    B, T, Tq, HI = shape
+    wl = Workload("mx4_scores_only", "bf16", B=B, T=T, Tq=Tq, m=4, d=128, H=8, W=4, k=64, HI=HI, dI=128,
+                  seed_base=79500 + T)
+    x = make_inputs(wl, "cuda")
+    kc, ks = csa.csa_mx4_quantize(x["k_idx"].contiguous())
+    a = torch.empty((wl.B, wl.Tq, wl.N), dtype=torch.float32, device="cuda")
+    csa.csa_index_topk_mx4(x["q_idx"], x["w_idx"], kc, ks, wl.N, wl.m, wl.k, wl.q_pos0, scores_out=a)
+    b = csa.csa_index_scores_mx4(x["q_idx"], x["w_idx"], kc, ks, wl.N, wl.m, wl.q_pos0)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))

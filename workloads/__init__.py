@@ -103,6 +103,8 @@ CONFIGS = {
 # the same seeded inputs, the keys quantised once when the cache is prepared
 CONFIGS["c2x"] = dataclasses.replace(CONFIGS["c2"], name="csa_decode_mx4idx_B32_ctx128K", index_fmt="mx4")
 CONFIGS["c5x"] = dataclasses.replace(CONFIGS["c5"], name="csa_decode_mx4idx_B4_ctx1M_stress", index_fmt="mx4")
+# the 64K prefill chunk with FP4 index operands
+CONFIGS["c4x"] = dataclasses.replace(CONFIGS["c4"], name="csa_prefill_chunk_mx4idx_ctx64K_q4096", index_fmt="mx4")
 
 
 def _gen(wl: Workload, name: str, device) -> torch.Generator:
