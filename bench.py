@@ -9,10 +9,12 @@ csa_sparse_mqa through the C ABI, replayed from captured HIP graphs over R
 input replicas (>= 1 GiB touched in rotation, so the 256 MB Infinity Cache
 cannot serve repeats).  Inputs are resident in HBM before timing starts.
 
-Printed: ONE JSON line with tokens/s (= B*Tq / step time), the dominant
-kernel's roofline (the lightning indexer, HBM-bound: algorithmic bytes per
-launch over its HIP-event-timed average duration), the oracle timed on the
-host's cores, and the HCA 1M and CSA 1M decode workloads as secondary lines.
+Printed: ONE JSON line with tokens/s (= B*Tq / step time), the roofline of
+the call that takes longest alone (for the default decode step the lightning
+indexer, HBM-bound: algorithmic bytes per launch over its HIP-event-timed
+average duration; for a prefill chunk the MFMA-bound indexer or attention),
+the oracle timed on the host's cores, and the other workloads as secondary
+entries.
 """
 from __future__ import annotations
 
@@ -30,6 +32,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 # counter-based HBM traffic of the indexer, measured by rocprofv3 on this
 # workload and kept with the source digest of the kernel it was taken on
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_traffic_csa_decode_128K.txt")
+TRAFFIC_WORKLOAD = "csa_decode_bf16_B32_ctx128K"  # the workload those counters were taken on
 INDEXER_SOURCES = ["long_context_compressed_06_amd/csrc/indexer.hip", "long_context_compressed_06_amd/csrc/common.h",
                    "long_context_compressed_06_amd/csrc/kernels.h"]
 
@@ -70,6 +73,18 @@ def algorithmic_bytes(wl) -> dict:
         step = wl.Tq * per_query + (nv_max + win_span) * wl.d * es
     step += wl.G_new * wl.m * 4 + wl.G_new * wl.d * es  # new groups: logits, entry writes
     return {"step": step * wl.B, "indexer": indexer * wl.B}
+
+
+def attention_bytes(wl) -> int:
+    """Unique HBM bytes of one attention call (decode): per query its q, the
+    fp32 output and lse, its selection read (CSA), the rows it attends (the
+    selected or all visible entries, plus its window's raw rows)."""
+    assert wl.Tq == 1
+    es = 2 if wl.dtype == "bf16" else 4
+    nv = min(wl.N, (wl.q_pos0 + 1) // wl.m)
+    rows = (min(wl.k, nv) if wl.mode == "csa" else nv) + min(wl.W, wl.q_pos0 + 1)
+    per_query = wl.H * wl.d * es + wl.H * wl.d * 4 + wl.H * 4 + (wl.k * 4 if wl.mode == "csa" else 0)
+    return wl.B * (per_query + rows * wl.d * es)
 
 
 def indexer_source_digest() -> str:
@@ -158,6 +173,54 @@ def algorithmic_flops(wl) -> dict:
     return {"indexer": idx * wl.B, "attention": att * wl.B}
 
 
+def attention_call(csa, wl, s, x):
+    """The step's attention call alone (on the step's own selection for CSA)."""
+    if wl.mode == "csa":
+        return lambda: csa.csa_sparse_mqa(x["q"], x["entries"], s.topk_idx, x["raw"], wl.N, wl.m, wl.W, wl.q_pos0,
+                                          wl.raw_pos0, scale=wl.scale, out=s.out, lse=s.lse, workspace=s.mqa_ws)
+    return lambda: csa.hca_dense_mqa(x["q"], x["entries"], x["raw"], wl.N, wl.m, wl.W, wl.q_pos0, wl.raw_pos0,
+                                     scale=wl.scale, out=s.out, lse=s.lse, workspace=s.mqa_ws)
+
+
+def hbm_rooflines(wl, r) -> dict:
+    """HBM rates of the decode step's indexer and attention calls timed alone."""
+    out = {}
+    if "indexer_ms" in r:
+        b = algorithmic_bytes(wl)["indexer"]
+        ach = b / (r["indexer_ms"] * 1e-3) / 1e9
+        out["indexer"] = {"kernel": "k_index_mx4_dma (lightning indexer, FP4 keys)" if wl.index_fmt == "mx4"
+                          else "k_index_dma (lightning indexer, bf16 keys)", "bound": "hbm", "achieved": ach,
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": checked_frac(ach / HBM_PEAK_GBS,
+                                                                                      wl.name + " indexer"),
+                          "bytes_per_launch": b, "avg_launch_us": r["indexer_ms"] * 1e3}
+    if "attention_ms" in r:
+        b = attention_bytes(wl)
+        ach = b / (r["attention_ms"] * 1e-3) / 1e9
+        out["attention"] = {"kernel": "k_mqa_wide + k_combine16 (one attention call)", "bound": "hbm",
+                            "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": checked_frac(ach / HBM_PEAK_GBS, wl.name + " attention"),
+                            "bytes_per_launch": b, "avg_launch_us": r["attention_ms"] * 1e3}
+    return out
+
+
+def mfma_rooflines(wl, r) -> dict:
+    """MFMA rates of a prefill chunk's indexer and attention timed alone."""
+    out = {}
+    fl = algorithmic_flops(wl)
+    for kern in ("indexer", "attention"):
+        if kern + "_ms" not in r:
+            continue
+        tf = fl[kern] / (r[kern + "_ms"] * 1e-3) / 1e12
+        # (an FP4 indexer against the FP4 peak, everything else against bf16's)
+        pk = MFMA_FP4_PEAK_TFLOPS if kern == "indexer" and wl.index_fmt == "mx4" else MFMA_BF16_PEAK_TFLOPS
+        name = {"indexer": "k_index_prefill_mx4 (FP4 keys)" if wl.index_fmt == "mx4" else "k_index_prefill",
+                "attention": "k_mqa_wide + k_combine16 (one attention call)"}[kern]
+        out[kern] = {"kernel": name, "bound": "mfma", "achieved": tf, "peak": pk, "unit": "TFLOP/s",
+                     "frac": checked_frac(tf / pk, wl.name + " " + kern), "flops_per_launch": fl[kern],
+                     "avg_launch_ms": r[kern + "_ms"]}
+    return out
+
+
 def bench_workload(wl, steps, warmup, with_kernel=True, with_mfma=False):
     import torch
 
@@ -181,16 +244,28 @@ def bench_workload(wl, steps, warmup, with_kernel=True, with_mfma=False):
     multi = capture(lambda: [s(x) for s, x in zip(steps_, xs)])
     ms = time_graphs(graphs, steps, warmup, multi, R)
     res = {"ms_per_step": ms, "replicas": R}
-    if with_kernel and wl.mode == "csa" and wl.index_fmt == "elem":
-        # the lightning indexer alone, same launch configuration, 8 launches per
-        # graph over the replicas, timed with HIP events on the stream it runs on
-        sc = [torch.empty((wl.B, wl.Tq, wl.N), dtype=torch.float32, device="cuda") for _ in xs]
-        idx_call = [lambda x=x, o=o: csa.csa_index_scores(x["q_idx"], x["w_idx"], x["k_idx"], wl.N, wl.m,
-                                                          wl.q_pos0, scores=o) for x, o in zip(xs, sc)]
-        kg = [capture(f) for f in idx_call]
-        km = capture(lambda: [idx_call[i % R]() for i in range(8)])
-        res["indexer_ms"] = time_graphs(kg, steps, warmup, km, 8)
-        del sc, kg, km
+    if with_kernel and wl.Tq == 1:
+        # the lightning indexer and the attention call alone, same launch
+        # configuration, 8 launches per graph over the replicas, timed with HIP
+        # events on the stream they run on
+        if wl.mode == "csa":
+            sc = [torch.empty((wl.B, wl.Tq, wl.N), dtype=torch.float32, device="cuda") for _ in xs]
+            if wl.index_fmt == "mx4":
+                idx_call = [lambda x=x, o=o: csa.csa_index_scores_mx4(x["q_idx"], x["w_idx"], x["k_codes"],
+                                                                      x["k_scales"], wl.N, wl.m, wl.q_pos0, scores=o)
+                            for x, o in zip(xs, sc)]
+            else:
+                idx_call = [lambda x=x, o=o: csa.csa_index_scores(x["q_idx"], x["w_idx"], x["k_idx"], wl.N, wl.m,
+                                                                  wl.q_pos0, scores=o) for x, o in zip(xs, sc)]
+            kg = [capture(f) for f in idx_call]
+            km = capture(lambda: [idx_call[i % R]() for i in range(8)])
+            res["indexer_ms"] = time_graphs(kg, steps, warmup, km, 8)
+            del sc, kg, km
+        att_call = [attention_call(csa, wl, s, x) for s, x in zip(steps_, xs)]
+        kg = [capture(f) for f in att_call]
+        km = capture(lambda: [att_call[i % R]() for i in range(8)])
+        res["attention_ms"] = time_graphs(kg, steps, warmup, km, 8)
+        del kg, km
     if with_mfma and wl.mode == "csa":
         # the two MFMA-bound kernels alone (prefill chunks), each timed from graphs over the replicas
         sc = [torch.empty((wl.B, wl.Tq, wl.N), dtype=torch.float32, device="cuda") for _ in xs]
@@ -203,9 +278,7 @@ def bench_workload(wl, steps, warmup, with_kernel=True, with_mfma=False):
                                                               wl.q_pos0, scores=o) for x, o in zip(xs, sc)]
         res["indexer_ms"] = time_graphs([capture(f) for f in idx_call], max(3, steps // 4), 2)
         del sc
-        att_call = [lambda s=s, x=x: csa.csa_sparse_mqa(x["q"], x["entries"], s.topk_idx, x["raw"], wl.N, wl.m, wl.W,
-                                                        wl.q_pos0, wl.raw_pos0, scale=wl.scale, out=s.out, lse=s.lse,
-                                                        workspace=s.mqa_ws) for s, x in zip(steps_, xs)]
+        att_call = [attention_call(csa, wl, s, x) for s, x in zip(steps_, xs)]
         res["attention_ms"] = time_graphs([capture(f) for f in att_call], max(3, steps // 4), 2)
     del graphs, steps_, xs, x0
     torch.cuda.empty_cache()
@@ -529,7 +602,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl = CONFIGS[args.workload]
     log(f"[bench] {wl}")
-    r = bench_workload(wl, args.steps, args.warmup)
+    r = bench_workload(wl, args.steps, args.warmup, with_kernel=wl.Tq == 1, with_mfma=wl.Tq > 1)
     ab = algorithmic_bytes(wl)
     toks = wl.B * wl.Tq / (r["ms_per_step"] * 1e-3)
     line = {
@@ -552,17 +625,19 @@ def main():
                      "achieved_GBs": ab["step"] / (r["ms_per_step"] * 1e-3) / 1e9,
                      "frac": checked_frac(ab["step"] / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, wl.name)},
     }
-    if "indexer_ms" in r:
-        ach = ab["indexer"] / (r["indexer_ms"] * 1e-3) / 1e9
-        c1, c32 = stream_ceiling_gbs(1), stream_ceiling_gbs(32)
-        line["roofline"] = {"kernel": "k_index_dma (lightning indexer, bf16 keys)", "bound": "hbm", "achieved": ach,
-                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                            "frac": checked_frac(ach / HBM_PEAK_GBS, "indexer"), "traffic": indexer_traffic(),
-                            "bytes_per_launch": ab["indexer"], "avg_launch_us": r["indexer_ms"] * 1e3,
-                            "measured_ceiling": {"what": "csa_stream_read of 2 GiB on the same GPU (the indexer's "
-                                                         "LDS-DMA load path), bytes read per second",
-                                                 "one_front_GBs": c1, "32_fronts_GBs": c32},
-                            "frac_of_measured_ceiling": ach / c32}
+    # the roofline of the call that takes the longest alone (the dominant kernel)
+    kern = mfma_rooflines(wl, r) if wl.Tq > 1 else hbm_rooflines(wl, r)
+    if kern:
+        dom = max(kern, key=lambda k: r[k + "_ms"])
+        line["roofline"] = dict(kern[dom], traffic=None)
+        if dom == "indexer" and wl.Tq == 1 and wl.index_fmt == "elem":
+            c1, c32 = stream_ceiling_gbs(1), stream_ceiling_gbs(32)
+            line["roofline"]["traffic"] = indexer_traffic() if wl.name == TRAFFIC_WORKLOAD else None
+            line["roofline"]["measured_ceiling"] = {"what": "csa_stream_read of 2 GiB on the same GPU (the "
+                                                            "indexer's LDS-DMA load path), bytes read per second",
+                                                    "one_front_GBs": c1, "32_fronts_GBs": c32}
+            line["roofline"]["frac_of_measured_ceiling"] = line["roofline"]["achieved"] / c32
+        line["kernels"] = kern
     also = {}
     for name in [a for a in args.also.split(",") if a and a != args.workload]:
         if name in RAGGED:
@@ -608,21 +683,13 @@ def main():
         log(f"[bench] also {w2}")
         prefill = w2.Tq > 1
         r2 = bench_workload(w2, max(10, args.steps // 2) if not prefill else max(5, args.steps // 5), args.warmup,
-                            with_kernel=False, with_mfma=prefill)
+                            with_kernel=not prefill, with_mfma=prefill)
         b2 = algorithmic_bytes(w2)["step"]
         also[w2.name] = {"tokens_per_s": w2.B * w2.Tq / (r2["ms_per_step"] * 1e-3), "ms_per_step": r2["ms_per_step"],
                          "step_hbm_frac": checked_frac(b2 / (r2["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, w2.name),
                          "algorithmic_bytes": b2}
-        if "attention_ms" in r2:
-            fl = algorithmic_flops(w2)
-            for kern in ("indexer", "attention"):
-                tf = fl[kern] / (r2[kern + "_ms"] * 1e-3) / 1e12
-                # (an FP4 indexer against the FP4 peak, everything else against bf16's)
-                pk = MFMA_FP4_PEAK_TFLOPS if kern == "indexer" and w2.index_fmt == "mx4" else MFMA_BF16_PEAK_TFLOPS
-                also[w2.name][kern + "_mfma"] = {"bound": "mfma", "achieved": tf, "peak": pk,
-                                                 "unit": "TFLOP/s",
-                                                 "frac": checked_frac(tf / pk, w2.name + " " + kern),
-                                                 "flops_per_launch": fl[kern], "avg_launch_ms": r2[kern + "_ms"]}
+        for kern, v in (mfma_rooflines(w2, r2) if prefill else hbm_rooflines(w2, r2)).items():
+            also[w2.name][kern + ("_mfma" if prefill else "_hbm")] = v
         if not args.no_cpu_baseline and name in BASELINE_ALSO:
             log(f"[bench] cpu baseline (oracle) {w2.name}")
             also[w2.name]["cpu_baseline"] = cpu_baseline(w2)

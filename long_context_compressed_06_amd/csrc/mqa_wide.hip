@@ -111,46 +111,74 @@ __global__ __launch_bounds__(kWT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const float scale2 = a.scale * kLog2e;
     const int dcol0 = dh * (kD / 2);
 
-    // Q^T fragments (B operand of the logits): K-step ks covers columns
-    // dcol0 + 16 ks .. +15; this lane supplies Q[head][dcol0 + 16 ks + 8 hh .. +7]
-    bf16x8 qf[16];
-    {
-        const bf16_t *qrow = (const bf16_t *)a.q + (row * a.H + min(head, a.H - 1)) * (int64_t)kD + dcol0 + 8 * hh;
+    // The query's 64 head rows (1 KiB each) go HBM -> LDS first, into tile
+    // stages 2 and 3 (idle until tile 2 is loaded), laid out like a tile of K
+    // rows so that the Q^T fragment reads below are the conflict-free K reads;
+    // wave w moves heads 16 w .. 16 w + 15 (heads past H load head H - 1: their
+    // results are never stored).  One transfer per head row, in flight while
+    // the row table is built.
+    const uint32_t lane16 = (uint32_t)lane * 16;
+    if (ntiles > 0) {
 #pragma unroll
-        for (int ks = 0; ks < 16; ++ks) {
-            const bf16x8 v = Elem<bf16_t>::load(qrow + 16 * ks);
-            qf[ks] = head < a.H ? v : Elem<bf16_t>::zero();
+        for (int u = 0; u < 16; ++u) {
+            const int hq = wv * 16 + u;
+            const uint64_t src = (uint64_t)(uintptr_t)((const bf16_t *)a.q + (row * a.H + min(hq, a.H - 1)) * (int64_t)kD);
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(src >> 32));
+            const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)src);
+            const uint32_t l = (uint32_t)(uintptr_t)(tiles + (2 + (hq >> 5)) * kTileB + wide_slot(hq & 31) * kRS);
+            dma16_s(__builtin_amdgcn_readfirstlane(l), lane16, ((uint64_t)hi << 32) | (uint64_t)lo);
         }
     }
 
-    // the split's row addresses, once; masked rows (weight 0, marked in vmask)
-    // load the query's own first row, in bounds and finite
+    // The split's row addresses next (their index loads start the longest
+    // chain of the prologue), kRtU table entries per thread per pass with all
+    // their index loads in flight together (unconditional, from clamped
+    // positions, so that no branch waits for one); masked rows (weight 0,
+    // marked in vmask) load the query's own first row, in bounds and finite.
     const bf16_t *ent = (const bf16_t *)a.entries;
     const bf16_t *raw_b = (const bf16_t *)a.raw + b * a.raw_bs;
     const bf16_t *fallback = (const bf16_t *)a.q + row * a.H * (int64_t)kD;
     const int nr = ntiles * kTR;
     // (two tiles past the last one, all fallback rows: loads issued beyond the
     // split land in a stage that is never read again)
-    for (int i0 = 0; i0 < nr + 2 * kTR; i0 += kWT) {
-        const int i = i0 + tid;
-        const bf16_t *src = nullptr;
-        if (i < nr) {
-            const int64_t r = tile_lo * kTR + i;
-            if (r < n_slots) {
-                const int64_t jj = a.k > 0 ? (int64_t)a.idx[row * a.k + r] : r;
-                if (jj >= 0 && jj < nv) src = ent + a.em.offset(b, jj, kD);
-            } else if (r < n_rows) {
-                const int64_t p = w0 + (r - n_slots);
-                src = raw_b + (a.raw_ring ? p % a.raw_ring : p - a.raw_pos0) * kD;
-            }
+    constexpr int kRtU = 8;
+    for (int i0 = 0; i0 < nr + 2 * kTR; i0 += kWT * kRtU) {
+        int64_t jj[kRtU];
+        if (a.k > 0) {  // (uniform)
+            int32_t ld[kRtU];
+#pragma unroll
+            for (int u = 0; u < kRtU; ++u)
+                ld[u] = a.idx[row * a.k + min(tile_lo * kTR + i0 + u * kWT + tid, (int64_t)a.k - 1)];
+#pragma unroll
+            for (int u = 0; u < kRtU; ++u) jj[u] = ld[u];
         }
-        if (i < nr + 2 * kTR) rtab[i] = src ? src : fallback;
-        const uint64_t bal = __ballot(src != nullptr);  // lanes 0-31: tile i/32; lanes 32-63: the next
-        if (i < nr && (lane & 31) == 0) vmask[i >> 5] = (uint32_t)(lane ? bal >> 32 : bal);
+#pragma unroll
+        for (int u = 0; u < kRtU; ++u) {
+            const int64_t r = tile_lo * kTR + i0 + u * kWT + tid;
+            if (a.k == 0 || r >= n_slots) jj[u] = r;
+        }
+#pragma unroll
+        for (int u = 0; u < kRtU; ++u) {
+            const int i = i0 + u * kWT + tid;
+            const bf16_t *src = nullptr;
+            if (i < nr) {
+                const int64_t r = tile_lo * kTR + i;
+                if (r < n_slots) {
+                    if (jj[u] >= 0 && jj[u] < nv) src = ent + a.em.offset(b, jj[u], kD);
+                } else if (r < n_rows) {
+                    const int64_t p = w0 + (r - n_slots);
+                    src = raw_b + (a.raw_ring ? p % a.raw_ring : p - a.raw_pos0) * kD;
+                }
+            }
+            if (i < nr + 2 * kTR) rtab[i] = src ? src : fallback;
+            const uint64_t bal = __ballot(src != nullptr);  // lanes 0-31: tile i/32; lanes 32-63: the next
+            if (i < nr && (lane & 31) == 0) vmask[i >> 5] = (uint32_t)(lane ? bal >> 32 : bal);
+        }
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the Q^T loads have landed
-    __syncthreads();
 
+    lds_barrier();  // the row table and vmask are visible to every wave
+
+    bf16x8 qf[16];
     floatx16 o[8];  // O^T: block nb = columns dcol0 + 32 nb .. +31 (rows of the 32x32 result) x 32 heads
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb)
@@ -176,7 +204,6 @@ __global__ __launch_bounds__(kWT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 nsrc[u] = ((uint64_t)hi << 32) | (uint64_t)lo;
             }
         };
-        const uint32_t lane16 = (uint32_t)lane * 16;
         auto dma_row = [&](int lt, int u, uint64_t src) {
             const uint32_t l = (uint32_t)(uintptr_t)(tiles + (lt % kStages) * kTileB +
                                                       wide_slot(wv * kDmaPerWave + u) * kRS);
@@ -344,7 +371,15 @@ __global__ __launch_bounds__(kWT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         uint64_t nsrc[kDmaPerWave];  // row addresses of the next tile to load
         next_sources(2, nsrc);
         {
-            barrier_a();
+            barrier_a();  // (also: every wave's share of Q has landed, it was loaded before tile 0)
+            // Q^T fragments (B operand of the logits): K-step ks covers columns
+            // dcol0 + 16 ks .. +15; this lane supplies Q[head][dcol0 + 16 ks + 8 hh .. +7]
+            {
+                const unsigned char *qs = tiles + (2 + hg) * kTileB + k_off;
+#pragma unroll
+                for (int ks = 0; ks < 16; ++ks) qf[ks] = *(const bf16x8 *)(qs + 32 * ks);
+            }
+            lds_barrier();  // every wave has its Q^T before tile 2 is loaded over it
             pin_q();
             const floatx16 acc = block1(0, nsrc);
             publish(acc);
