@@ -111,6 +111,29 @@ struct RowMap {
 // this many entries per sequence)
 constexpr int kMaxPagesPerSeq = 1024;
 
+// Sequence b's first n page ids (n <= kMaxPagesPerSeq) into LDS pl[0, n), by
+// a workgroup of NT threads, in two parts so that other loads can be issued
+// in between: load() issues each thread's loads together, from clamped
+// (always valid) positions, store() writes them; one memory round trip.
+template <int NT>
+struct PageStage {
+    static constexpr int U = (kMaxPagesPerSeq + NT - 1) / NT;
+    int32_t v[U];
+    __device__ __forceinline__ void load(const RowMap &kl, int64_t b, int n) {
+        if (n <= 0) return;
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = kl.ptab[b * kl.pstride + min((int)threadIdx.x + u * NT, n - 1)];
+    }
+    // (the page ids are clamped into the pool here, as page_of does)
+    __device__ __forceinline__ void store(const RowMap &kl, int32_t *pl, int n) const {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = (int)threadIdx.x + u * NT;
+            if (i < n) pl[i] = (int32_t)(v[u] < 0 ? 0 : (v[u] >= kl.npages ? kl.npages - 1 : v[u]));
+        }
+    }
+};
+
 // Entries visible to a query at absolute position t: complete groups only.
 __device__ __forceinline__ int64_t n_visible(int64_t t, int m, int64_t N) {
     if (t < 0) return 0;

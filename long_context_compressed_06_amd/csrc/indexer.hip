@@ -291,25 +291,38 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_dma(int Tq, int N, int
         }
     };
 
-    // ---- stage the index query and clear the histogram
-    for (int i = threadIdx.x; i < HI * DI / 8; i += kIdxWaves * 64)
-        *(u32x4 *)(qs + i * 8) = *(const u32x4 *)(qI + row * HI * DI + i * 8);
-    if (hist)
-        for (int i = threadIdx.x; i < kTopkBins; i += kIdxWaves * 64) bh[i] = 0;
-    if constexpr (PAGED)
-        for (int i = threadIdx.x; i < (int)min((nv + (1 << kl.pshift) - 1) >> kl.pshift, (int64_t)kl.pstride);
-             i += kIdxWaves * 64)
-            pl[i] = (int32_t)kl.page_of(b, i);
+    // ---- the head weights, then the index query staged in LDS (each
+    // thread's loads issued together, from clamped positions: one memory
+    // round trip for all of them) and the histogram cleared
     float wgt[MB][4];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int hh = mb * 16 + 4 * g + e;
-            const float v = w[row * HI + min(hh, HI - 1)];
-            wgt[mb][e] = hh < HI ? v : 0.f;
+        for (int e = 0; e < 4; ++e) wgt[mb][e] = w[row * HI + min(mb * 16 + 4 * g + e, HI - 1)];
+    const int n_pages = PAGED ? (int)min((nv + (1 << kl.pshift) - 1) >> kl.pshift, (int64_t)kl.pstride) : 0;
+    PageStage<kIdxWaves * 64> pages;
+    if constexpr (PAGED) pages.load(kl, b, n_pages);
+    {
+        constexpr int kQU = (16 * MB * DI / 8 + kIdxWaves * 64 - 1) / (kIdxWaves * 64);
+        const int nq = HI * DI / 8;
+        u32x4 qv[kQU];
+#pragma unroll
+        for (int u = 0; u < kQU; ++u)
+            qv[u] = *(const u32x4 *)(qI + row * HI * DI + min((int)threadIdx.x + u * kIdxWaves * 64, nq - 1) * 8);
+#pragma unroll
+        for (int u = 0; u < kQU; ++u) {
+            const int i = (int)threadIdx.x + u * kIdxWaves * 64;
+            if (i < nq) *(u32x4 *)(qs + i * 8) = qv[u];
         }
-
+    }
+    if (hist)
+        for (int i = threadIdx.x; i < kTopkBins; i += kIdxWaves * 64) bh[i] = 0;
+    if constexpr (PAGED) pages.store(kl, pl, n_pages);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (mb * 16 + 4 * g + e >= HI) wgt[mb][e] = 0.f;
     __syncthreads();
     bf16x8 a[MB][KS];
 #pragma unroll

@@ -353,16 +353,23 @@ __global__ __launch_bounds__(kMx4Waves * 64) void k_index_mx4_dma(int Tq, int N,
 
     // paged caches: the query's page list first (the tile addresses need it)
     if constexpr (PAGED) {
-        for (int i = threadIdx.x; i < (int)min((nv + (1 << kl.pshift) - 1) >> kl.pshift, (int64_t)kl.pstride);
-             i += kMx4Waves * 64)
-            pl[i] = (int32_t)kl.page_of(b, i);
+        const int n_pages = (int)min((nv + (1 << kl.pshift) - 1) >> kl.pshift, (int64_t)kl.pstride);
+        PageStage<kMx4Waves * 64> pages;
+        pages.load(kl, b, n_pages);
+        pages.store(kl, pl, n_pages);
         __syncthreads();
     }
     // the first tiles stream in while the query is quantised (the ring is
     // disjoint from the query and histogram areas)
     for (int i = 0; i < kMx4Stages - 1 && i < n_vis; ++i) issue(i);
 
-    // ---- quantise the query once per workgroup, clear the histogram
+    // ---- the head weights (their loads in flight with the query's), the
+    // query quantised once per workgroup, the histogram cleared
+    float wgt[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wgt[mb][e] = w[row * HI + min(mb * 16 + 4 * g + e, HI - 1)];
     {
         static_assert(kMx4Waves * 64 == kMx4QBlocks, "one query block per thread");
         const int blk = threadIdx.x;
@@ -375,15 +382,11 @@ __global__ __launch_bounds__(kMx4Waves * 64) void k_index_mx4_dma(int Tq, int N,
     }
     if (hist)
         for (int i = threadIdx.x; i < kTopkBins; i += kMx4Waves * 64) bh[i] = 0;
-    float wgt[MB][4];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int hh = mb * 16 + 4 * g + e;
-            const float v = w[row * HI + min(hh, HI - 1)];
-            wgt[mb][e] = hh < HI ? v : 0.f;
-        }
+        for (int e = 0; e < 4; ++e)
+            if (mb * 16 + 4 * g + e >= HI) wgt[mb][e] = 0.f;
     __syncthreads();
     int32x8 a[MB];
     int as[MB];
