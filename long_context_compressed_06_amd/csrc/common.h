@@ -107,6 +107,24 @@ struct RowMap {
         return ptab ? paged_row(b, j) * rowlen : b * bstride + j * rowlen;
     }
 };
+// Indexer epilogues: the head sum of four 16-entry blocks at once.  Lane
+// (g, c) = (lane / 16, lane % 16) holds x[u], block u's partial score of entry
+// c over its lane group's heads; on return it holds block g's total for entry
+// c, i.e. the four lane groups end with the four blocks.  One 32-lane swap
+// pairs blocks 0/2 and 1/3 across the wave halves, one 16-lane swap finishes
+// (three swaps and three adds for four blocks; the additions are paired as
+// (g0 + g2) + (g1 + g3), the order of the one-block sum).
+__device__ __forceinline__ float sum_lane_groups4(const float (&x)[4]) {
+    // v_permlane32_swap: lanes 32-63 of the first operand <-> lanes 0-31 of the second
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[0]), __float_as_uint(x[2]), false, false);
+    const float r02 = __uint_as_float(p[0]) + __uint_as_float(p[1]);  // halves: block 0 (lanes 0-31), 2
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[1]), __float_as_uint(x[3]), false, false);
+    const float r13 = __uint_as_float(q[0]) + __uint_as_float(q[1]);  // halves: block 1, 3
+    // v_permlane16_swap: odd 16-lane rows of the first operand <-> even rows of the second
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(r02), __float_as_uint(r13), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
 // page list of one sequence staged in LDS by the indexers (pages of at most
 // this many entries per sequence)
 constexpr int kMaxPagesPerSeq = 1024;

@@ -462,6 +462,7 @@ static hipError_t launch_t(int B, int Tq, int N, int HI, int m, QPos q_pos0, con
 constexpr int kPreWaves = 8;
 constexpr int kPreMinQueries = 64;  // queries per sequence from which the query-blocked kernel is used
 constexpr int kPreRows = 128;      // entries per key tile
+static_assert(kPreRows % 64 == 0, "epilogues take four 16-entry blocks at a time");
 constexpr int kPreStages = 3;
 
 template <int DI>
@@ -553,28 +554,36 @@ __global__ __launch_bounds__(kPreWaves * 64) void k_index_prefill(int Tq, int N,
             asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
         if (t + kPreStages - 1 < vtiles) issue(t + kPreStages - 1);
         const unsigned char *tile = ring + (t % kPreStages) * S::TB;
+        // four 16-entry blocks at a time: their head sums finish together, after
+        // which every lane holds one score (block g, entry c: tile row 16 g + c of
+        // the four) for the stores and the histogram
 #pragma unroll
-        for (int nb = 0; nb < kPreRows / 16; ++nb) {
-            bf16x8 kf[KS];
+        for (int q4 = 0; q4 < kPreRows / 64; ++q4) {
+            float part[4];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                kf[ks] = *(const bf16x8 *)(tile + (nb * 16 + c) * S::RB + S::swz(nb * 16 + c, ks * 4 + g) * 16);
-            floatx4 acc[MB];
+            for (int u = 0; u < 4; ++u) {
+                const int r = (q4 * 4 + u) * 16 + c;
+                bf16x8 kf[KS];
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+                for (int ks = 0; ks < KS; ++ks) kf[ks] = *(const bf16x8 *)(tile + r * S::RB + S::swz(r, ks * 4 + g) * 16);
+                floatx4 acc[MB];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
+                for (int mb = 0; mb < MB; ++mb) acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb][ks], kf[ks], acc[mb], 0, 0, 0);
+                float sc = 0.f;
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
-                    acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb][ks], kf[ks], acc[mb], 0, 0, 0);
-            float sc = 0.f;
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sc += wgt[mb][e] * relu(acc[mb][e]);
-            sc = sum_lane_groups(sc);
-            const int64_t j = (int64_t)t * kPreRows + nb * 16 + c;
-            if (on && g == 0 && j < N) {
+                    for (int e = 0; e < 4; ++e) sc += wgt[mb][e] * relu(acc[mb][e]);
+                part[u] = sc;
+            }
+            const float sc = sum_lane_groups4(part);
+            const int64_t j = (int64_t)t * kPreRows + q4 * 64 + lane;
+            if (on && j < N) {
                 const float v = j < nv ? sc : -INFINITY;
                 srow[j] = v;
                 if (srow2) srow2[j] = v;

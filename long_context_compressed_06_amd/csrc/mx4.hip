@@ -205,10 +205,13 @@ __global__ __launch_bounds__(256) void k_index_mx4(int Tq, int N, int HI, int m,
                 kx[u] = ksb[jr * KB];
             }
         };
+        // the batch's four tiles finish their head sums together: lane group g
+        // then holds tile g's scores (entry j0 + 16 g + c = j0 + lane)
+        static_assert(UNROLL == 4, "one tile per lane group");
         auto score_batch = [&](int64_t j0, const u32x4 (&kd)[UNROLL], const int (&kx)[UNROLL]) {
+            float part[UNROLL];
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
-                const int64_t j = j0 + u * 16 + c;
                 const u32x4 z = kon ? kd[u] : u32x4{0u, 0u, 0u, 0u};
                 const int32x8 bk = {(int)z[0], (int)z[1], (int)z[2], (int)z[3], 0, 0, 0, 0};
                 const int bs = kon ? kx[u] : 127;
@@ -220,14 +223,15 @@ __global__ __launch_bounds__(256) void k_index_mx4(int Tq, int N, int HI, int m,
 #pragma unroll
                     for (int e = 0; e < 4; ++e) s += wgt[mb][e] * mx4_relu(acc[e]);
                 }
-                s = mx4_sum_lane_groups(s);
-                if (g == 0 && j < j_hi) {
-                    srow[j] = j < nv ? s : -INFINITY;
-                    if (srow2) srow2[j] = j < nv ? s : -INFINITY;
-                }
-                if (hist && g == 0 && j < j_hi && j < nv)
-                    atomicAdd(&whist[wv][order_key(s) >> (32 - kTopkBinBits)], 1u);
+                part[u] = s;
             }
+            const float s = sum_lane_groups4(part);
+            const int64_t j = j0 + lane;
+            if (j < j_hi) {
+                srow[j] = j < nv ? s : -INFINITY;
+                if (srow2) srow2[j] = j < nv ? s : -INFINITY;
+            }
+            if (hist && j < j_hi && j < nv) atomicAdd(&whist[wv][order_key(s) >> (32 - kTopkBinBits)], 1u);
         };
         // double-buffered: the next batch is in flight while this one is scored
         u32x4 d0[UNROLL], d1[UNROLL];
@@ -539,6 +543,7 @@ static hipError_t launch_mx4_di(int B, int Tq, int N, int HI, int m, QPos q_pos0
 constexpr int kPmWaves = 8;
 constexpr int kPmMinQueries = 64;  // queries per sequence from which the query-blocked kernel is used
 constexpr int kPmRows = 128;                        // entries per key tile
+static_assert(kPmRows % 64 == 0, "epilogues take four 16-entry blocks at a time");
 constexpr int kPmStages = 4;
 constexpr int kPmCodeB = kPmRows * 64;              // code bytes per tile (8 KiB: one KiB per wavefront)
 constexpr int kPmTile = kPmCodeB + kPmRows * 4;     // + the scale dwords
@@ -625,23 +630,31 @@ __global__ __launch_bounds__(kPmWaves * 64) void k_index_prefill_mx4(int Tq, int
             asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
         if (t + kPmStages - 1 < vtiles) issue(t + kPmStages - 1);
         const unsigned char *tile = ring + (t % kPmStages) * kPmTile;
+        // four 16-entry blocks at a time: their head sums finish together, after
+        // which every lane holds one score (block g, entry c: tile row 16 g + c of
+        // the four) for the stores and the histogram
 #pragma unroll
-        for (int nb = 0; nb < kPmRows / 16; ++nb) {
-            const int r = nb * 16 + c;
-            const u32x4 kd = *(const u32x4 *)(tile + r * RB + mx4_swz(r, g) * 16);
-            const int bs = tile[kPmCodeB + r * KB + g];
-            const int32x8 bk = {(int)kd[0], (int)kd[1], (int)kd[2], (int)kd[3], 0, 0, 0, 0};
-            float sc = 0.f;
+        for (int q4 = 0; q4 < kPmRows / 64; ++q4) {
+            float part[4];
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                const floatx4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    a[mb], bk, floatx4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, as[mb], 0, bs);
+            for (int u = 0; u < 4; ++u) {
+                const int r = (q4 * 4 + u) * 16 + c;
+                const u32x4 kd = *(const u32x4 *)(tile + r * RB + mx4_swz(r, g) * 16);
+                const int bs = tile[kPmCodeB + r * KB + g];
+                const int32x8 bk = {(int)kd[0], (int)kd[1], (int)kd[2], (int)kd[3], 0, 0, 0, 0};
+                float sc = 0.f;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sc += wgt[mb][e] * mx4_relu(acc[e]);
+                for (int mb = 0; mb < MB; ++mb) {
+                    const floatx4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        a[mb], bk, floatx4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, as[mb], 0, bs);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sc += wgt[mb][e] * mx4_relu(acc[e]);
+                }
+                part[u] = sc;
             }
-            sc = mx4_sum_lane_groups(sc);
-            const int64_t j = (int64_t)t * kPmRows + r;
-            if (on && g == 0 && j < N) {
+            const float sc = sum_lane_groups4(part);
+            const int64_t j = (int64_t)t * kPmRows + q4 * 64 + lane;
+            if (on && j < N) {
                 const float v = j < nv ? sc : -INFINITY;
                 srow[j] = v;
                 if (srow2) srow2[j] = v;
