@@ -132,6 +132,10 @@ SMALL = [
     ("hca_bf16_window_only", "bf16", 1, 100, 100, 128, 128, 64, 16, 0, 0, 0),
     # one query over 30016 rows of d = 512: more splits than one batch of the split-K merge
     ("hca_bf16_many_splits", "bf16", 1, 4 * 30000, 1, 4, 512, 64, 16, 0, 0, 0),
+    # the 32-head-wavefront kernel with a partial second head group (heads >= H: clamped query rows,
+    # nothing stored), split and unsplit queries
+    ("csa_bf16_d512_h48", "bf16", 2, 3001, 3, 4, 512, 48, 33, 200, 17, 128),
+    ("hca_bf16_d512_h40", "bf16", 1, 128 * 40 + 7, 2, 128, 512, 40, 16, 0, 0, 0),
 ]
 
 
