@@ -141,6 +141,11 @@ __global__ __launch_bounds__(kWT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int nr = ntiles * kTR;
     // (two tiles past the last one, all fallback rows: loads issued beyond the
     // split land in a stage that is never read again)
+    // Window rows are positions w0 .. t; in a ring of raw_ring slots position p
+    // sits in slot p mod raw_ring, taken here as (w0 mod raw_ring) + offset with
+    // one wrap-around (a window longer than the ring takes the modulo per row).
+    const int64_t ring_w0 = a.raw_ring > 0 ? w0 % a.raw_ring : 0;
+    const bool ring_step = n_win <= a.raw_ring;
     constexpr int kRtU = 8;
     for (int i0 = 0; i0 < nr + 2 * kTR; i0 += kWT * kRtU) {
         int64_t jj[kRtU];
@@ -159,6 +164,7 @@ __global__ __launch_bounds__(kWT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
 #pragma unroll
         for (int u = 0; u < kRtU; ++u) {
+            if (i0 + u * kWT >= nr + 2 * kTR) break;  // (uniform: no entries of this pass remain)
             const int i = i0 + u * kWT + tid;
             const bf16_t *src = nullptr;
             if (i < nr) {
@@ -166,8 +172,17 @@ __global__ __launch_bounds__(kWT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 if (r < n_slots) {
                     if (jj[u] >= 0 && jj[u] < nv) src = ent + a.em.offset(b, jj[u], kD);
                 } else if (r < n_rows) {
-                    const int64_t p = w0 + (r - n_slots);
-                    src = raw_b + (a.raw_ring ? p % a.raw_ring : p - a.raw_pos0) * kD;
+                    const int64_t off = r - n_slots;
+                    int64_t slot;
+                    if (a.raw_ring == 0) {
+                        slot = w0 + off - a.raw_pos0;
+                    } else if (ring_step) {
+                        slot = ring_w0 + off;
+                        if (slot >= a.raw_ring) slot -= a.raw_ring;
+                    } else {
+                        slot = (w0 + off) % a.raw_ring;
+                    }
+                    src = raw_b + slot * kD;
                 }
             }
             if (i < nr + 2 * kTR) rtab[i] = src ? src : fallback;
