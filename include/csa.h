@@ -347,6 +347,43 @@ int csa_index_scores_mx4(int dt, int B, int Tq, int N, int H_I, int d_I, int m, 
                          float *scores, void *stream);
 
 /*
+ * csa_compress_index_topk / csa_compress_index_topk_mx4 -- csa_compress
+ * followed by csa_index_topk (or csa_index_topk_mx4) on the same stream, as
+ * one CSA step issues them (overview page, section 2.2: the new groups are
+ * compressed, then the indexer selects among the cached entries).  The
+ * compression goes into the launch that also clears the selection's
+ * histograms, which saves one launch per step.  Its output is the attention's
+ * entries cache, not the index keys, so the indexer does not read it.
+ *   raw .. out_bstride  exactly csa_compress's arguments (dt, B, m and the
+ *                       rules are shared with the index call; G = 0 skips the
+ *                       compression)
+ *   Tq .. stream        exactly csa_index_topk's (csa_index_topk_mx4's)
+ *                       arguments after B and m
+ * Both results equal those of the two separate calls, bit for bit.  Besides
+ * each call's own checks, entries_out may overlap no index operand, output or
+ * the workspace, and raw / logits may not overlap the workspace (CSA_EINVAL).
+ * On an error nothing is launched.
+ */
+int csa_compress_index_topk(int dt, int B, int G, int m, int d,
+                            const void *raw, int64_t raw_bstride,
+                            const float *logits, int64_t logit_bstride,
+                            void *entries_out, int64_t out_bstride,
+                            int Tq, int N, int H_I, int d_I, int k, int64_t q_pos0,
+                            const void *q_idx, const float *w_idx,
+                            const void *k_idx, int64_t k_bstride,
+                            int32_t *topk_idx, float *scores_out,
+                            void *workspace, size_t workspace_bytes, void *stream);
+int csa_compress_index_topk_mx4(int dt, int B, int G, int m, int d,
+                                const void *raw, int64_t raw_bstride,
+                                const float *logits, int64_t logit_bstride,
+                                void *entries_out, int64_t out_bstride,
+                                int Tq, int N, int H_I, int d_I, int k, int64_t q_pos0,
+                                const void *q_idx, const float *w_idx,
+                                const uint8_t *k_codes, const uint8_t *k_scales, int64_t k_bstride,
+                                int32_t *topk_idx, float *scores_out,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * csa_sparse_mqa -- shared-KV multi-query attention over the selected
  * entries plus the raw window, one softmax (overview page, section 2.2
  * step 3: selected entries act as both key and value, all heads share them).

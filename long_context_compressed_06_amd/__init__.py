@@ -25,7 +25,8 @@ EXPORTS = ("csa_abi_version", "csa_status_string", "csa_last_error_detail", "csa
            "csa_sparse_mqa", "hca_dense_mqa", "csa_mx4_quantize", "csa_index_topk_mx4", "csa_append_rows",
            "csa_compress_channels", "csa_append_rows_multi", "csa_positions_advance", "csa_ragged_compress",
            "csa_ragged_index_topk", "csa_ragged_index_topk_mx4", "csa_ragged_sparse_mqa", "hca_ragged_dense_mqa", "csa_stream_read",
-           "csa_index_topk_noalloc", "csa_index_scores_mx4")
+           "csa_index_topk_noalloc", "csa_index_scores_mx4", "csa_compress_index_topk",
+           "csa_compress_index_topk_mx4")
 
 
 class AppendJob(ctypes.Structure):
@@ -100,6 +101,11 @@ def lib():
     L.hca_ragged_dense_mqa.restype = I
     L.csa_index_topk_noalloc.argtypes = [I, I, I, I, I, I, I, I, I64, P, P, P, I64, P, P, P]
     L.csa_index_topk_noalloc.restype = I
+    comp = [I, I, I, I, I, P, I64, P, I64, P, I64]  # csa_compress's arguments, without the stream
+    L.csa_compress_index_topk.argtypes = comp + [I, I, I, I, I, I64, P, P, P, I64, P, P, P, SZ, P]
+    L.csa_compress_index_topk.restype = I
+    L.csa_compress_index_topk_mx4.argtypes = comp + [I, I, I, I, I, I64, P, P, P, P, I64, P, P, P, SZ, P]
+    L.csa_compress_index_topk_mx4.restype = I
     L.csa_stream_read.argtypes = [P, I64, I, P, P]
     L.csa_stream_read.restype = I
     L.csa_append_rows.restype = I
@@ -143,8 +149,8 @@ def _bstride(t):
     return t.stride(0)
 
 
-def csa_compress(raw: torch.Tensor, logits: torch.Tensor, m: int, out: torch.Tensor) -> torch.Tensor:
-    """raw [B, G*m, d], logits [B, G*m] f32 -> out [B, G, d] (written in place, may be a cache view)."""
+def _compress_args(raw, logits, m, out) -> tuple:
+    """Checks csa_compress's tensors; returns its arguments from dt to out_bstride."""
     _need(raw, "raw", dims=3)
     _need(logits, "logits", torch.float32, 2)
     _need(out, "out", raw.dtype, 3)
@@ -157,8 +163,12 @@ def csa_compress(raw: torch.Tensor, logits: torch.Tensor, m: int, out: torch.Ten
             raise ValueError(f"{n} rows must be packed")
     if out.shape != (B, G, d) or logits.shape != (B, Gm) or logits.stride(1) != 1:
         raise ValueError("shape mismatch between raw, logits and out")
-    _check(lib().csa_compress(_dt(raw), B, G, m, d, _p(raw), _bstride(raw), _p(logits), _bstride(logits), _p(out),
-                              _bstride(out), _stream(raw)))
+    return (_dt(raw), B, G, m, d, _p(raw), _bstride(raw), _p(logits), _bstride(logits), _p(out), _bstride(out))
+
+
+def csa_compress(raw: torch.Tensor, logits: torch.Tensor, m: int, out: torch.Tensor) -> torch.Tensor:
+    """raw [B, G*m, d], logits [B, G*m] f32 -> out [B, G, d] (written in place, may be a cache view)."""
+    _check(lib().csa_compress(*_compress_args(raw, logits, m, out), _stream(raw)))
     return out
 
 
@@ -166,9 +176,9 @@ def index_topk_workspace_bytes(B, Tq, N, H_I, k) -> int:
     return int(lib().csa_index_topk_workspace_bytes(B, Tq, N, H_I, k))
 
 
-def csa_index_topk(q_idx, w_idx, k_idx, N: int, m: int, k: int, q_pos0: int, topk_idx=None, scores_out=None,
-                   workspace=None) -> torch.Tensor:
-    """q_idx [B,Tq,H_I,d_I], w_idx [B,Tq,H_I] f32, k_idx [B,cap,d_I] (first N rows used) -> topk_idx [B,Tq,k] int32."""
+def _index_args(q_idx, w_idx, k_idx, N, k, q_pos0, topk_idx, scores_out, workspace) -> tuple:
+    """Checks csa_index_topk's tensors (allocating the missing outputs); returns (topk_idx, its arguments from
+    Tq to workspace_bytes with m left out)."""
     _need(q_idx, "q_idx", dims=4)
     _need(w_idx, "w_idx", torch.float32, 3)
     _need(k_idx, "k_idx", q_idx.dtype, 3)
@@ -186,9 +196,31 @@ def csa_index_topk(q_idx, w_idx, k_idx, N: int, m: int, k: int, q_pos0: int, top
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q_idx.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().csa_index_topk(_dt(q_idx), B, Tq, N, HI, dI, m, k, q_pos0, _p(q_idx), _p(w_idx), _p(k_idx),
-                                _bstride(k_idx), _p(topk_idx), _p(scores_out), _p(workspace), ws_bytes,
-                                _stream(q_idx)))
+    return topk_idx, (Tq, N, HI, dI, k, q_pos0, _p(q_idx), _p(w_idx), _p(k_idx), _bstride(k_idx), _p(topk_idx),
+                      _p(scores_out), _p(workspace), ws_bytes)
+
+
+def csa_index_topk(q_idx, w_idx, k_idx, N: int, m: int, k: int, q_pos0: int, topk_idx=None, scores_out=None,
+                   workspace=None) -> torch.Tensor:
+    """q_idx [B,Tq,H_I,d_I], w_idx [B,Tq,H_I] f32, k_idx [B,cap,d_I] (first N rows used) -> topk_idx [B,Tq,k] int32."""
+    topk_idx, a = _index_args(q_idx, w_idx, k_idx, N, k, q_pos0, topk_idx, scores_out, workspace)
+    _check(lib().csa_index_topk(_dt(q_idx), q_idx.shape[0], *a[:4], m, *a[4:], _stream(q_idx)))
+    return topk_idx
+
+
+def _fused_pair(raw, q_idx):
+    if raw.dtype != q_idx.dtype or raw.shape[0] != q_idx.shape[0] or raw.device != q_idx.device:
+        raise ValueError("raw and q_idx must share the element type, the batch and the device")
+
+
+def csa_compress_index_topk(raw, logits, m: int, entries_out, q_idx, w_idx, k_idx, N: int, k: int, q_pos0: int,
+                            topk_idx=None, scores_out=None, workspace=None) -> torch.Tensor:
+    """csa_compress(raw, logits, m, entries_out) then csa_index_topk(q_idx, w_idx, k_idx, N, m, k, q_pos0, ...) in
+    one call with one launch fewer; returns topk_idx.  entries_out is the attention's cache, not k_idx."""
+    _fused_pair(raw, q_idx)
+    c = _compress_args(raw, logits, m, entries_out)
+    topk_idx, a = _index_args(q_idx, w_idx, k_idx, N, k, q_pos0, topk_idx, scores_out, workspace)
+    _check(lib().csa_compress_index_topk(*c, *a, _stream(q_idx)))
     return topk_idx
 
 
@@ -284,10 +316,9 @@ def csa_index_scores_mx4(q_idx, w_idx, k_codes, k_scales, N: int, m: int, q_pos0
     return scores
 
 
-def csa_index_topk_mx4(q_idx, w_idx, k_codes, k_scales, N: int, m: int, k: int, q_pos0: int, topk_idx=None,
-                       scores_out=None, workspace=None) -> torch.Tensor:
-    """FP4 (MXFP4) indexer + top-k.  q_idx [B,Tq,H_I,d_I] (f32/bf16, quantised inside the call), w_idx
-    [B,Tq,H_I] f32, k_codes [B,cap,d_I/2], k_scales [B,cap,d_I/32] (first N rows used) -> topk_idx [B,Tq,k]."""
+def _index_mx4_args(q_idx, w_idx, k_codes, k_scales, N, k, q_pos0, topk_idx, scores_out, workspace) -> tuple:
+    """Checks csa_index_topk_mx4's tensors (allocating the missing outputs); returns (topk_idx, its arguments
+    from Tq to workspace_bytes with m left out)."""
     _need(q_idx, "q_idx", dims=4)
     _need(w_idx, "w_idx", torch.float32, 3)
     _need(k_codes, "k_codes", torch.uint8, 3)
@@ -315,9 +346,26 @@ def csa_index_topk_mx4(q_idx, w_idx, k_codes, k_scales, N: int, m: int, k: int, 
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q_idx.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().csa_index_topk_mx4(_dt(q_idx), B, Tq, N, HI, dI, m, k, q_pos0, _p(q_idx), _p(w_idx), _p(k_codes),
-                                    _p(k_scales), cap, _p(topk_idx), _p(scores_out), _p(workspace), ws_bytes,
-                                    _stream(q_idx)))
+    return topk_idx, (Tq, N, HI, dI, k, q_pos0, _p(q_idx), _p(w_idx), _p(k_codes), _p(k_scales), cap, _p(topk_idx),
+                      _p(scores_out), _p(workspace), ws_bytes)
+
+
+def csa_index_topk_mx4(q_idx, w_idx, k_codes, k_scales, N: int, m: int, k: int, q_pos0: int, topk_idx=None,
+                       scores_out=None, workspace=None) -> torch.Tensor:
+    """FP4 (MXFP4) indexer + top-k.  q_idx [B,Tq,H_I,d_I] (f32/bf16, quantised inside the call), w_idx
+    [B,Tq,H_I] f32, k_codes [B,cap,d_I/2], k_scales [B,cap,d_I/32] (first N rows used) -> topk_idx [B,Tq,k]."""
+    topk_idx, a = _index_mx4_args(q_idx, w_idx, k_codes, k_scales, N, k, q_pos0, topk_idx, scores_out, workspace)
+    _check(lib().csa_index_topk_mx4(_dt(q_idx), q_idx.shape[0], *a[:4], m, *a[4:], _stream(q_idx)))
+    return topk_idx
+
+
+def csa_compress_index_topk_mx4(raw, logits, m: int, entries_out, q_idx, w_idx, k_codes, k_scales, N: int, k: int,
+                                q_pos0: int, topk_idx=None, scores_out=None, workspace=None) -> torch.Tensor:
+    """csa_compress then csa_index_topk_mx4 in one call with one launch fewer; returns topk_idx."""
+    _fused_pair(raw, q_idx)
+    c = _compress_args(raw, logits, m, entries_out)
+    topk_idx, a = _index_mx4_args(q_idx, w_idx, k_codes, k_scales, N, k, q_pos0, topk_idx, scores_out, workspace)
+    _check(lib().csa_compress_index_topk_mx4(*c, *a, _stream(q_idx)))
     return topk_idx
 
 

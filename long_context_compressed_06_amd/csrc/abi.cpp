@@ -126,26 +126,70 @@ const char *csa_status_string(int s) {
 
 const char *csa_last_error_detail(void) { return g_detail.c_str(); }
 
+// a compression (csa_compress's arguments), checked on its own or ahead of an index call
+struct CompressJob {
+    int dt, B, G, m, d;
+    const void *raw;
+    int64_t raw_bs;
+    const float *logits;
+    int64_t log_bs;
+    void *out;
+    int64_t out_bs;
+    // the bytes each operand spans (for the overlap checks of a fused call)
+    Span raw_span() const { return span(raw, B, raw_bs, (int64_t)G * m * d, esize(dt)); }
+    Span log_span() const { return span(logits, B, log_bs, (int64_t)G * m, 4); }
+    Span out_span() const { return span(out, B, out_bs, (int64_t)G * d, esize(dt)); }
+};
+
+// csa_compress's checks; *empty when there is nothing to compress
+static int check_compress(const CompressJob &c, bool *empty) {
+    *empty = true;
+    if (int s = check_dt(c.dt)) return s;
+    if (c.B < 0 || c.G < 0) return fail(CSA_EINVAL, "B=%d and G=%d must be >= 0", c.B, c.G);
+    if (c.m < 1 || c.m > 128) return fail(CSA_EUNSUPPORTED, "m=%d outside 1..128", c.m);
+    if (!d_supported(c.d)) return fail(CSA_EUNSUPPORTED, "d=%d not in {32,64,128,256,512}", c.d);
+    if ((int64_t)c.B * c.G == 0) return ok();
+    if (!c.raw || !c.logits || !c.out) return fail(CSA_EINVAL, "NULL tensor pointer");
+    if (c.raw_bs < (int64_t)c.G * c.m * c.d || c.log_bs < (int64_t)c.G * c.m || c.out_bs < (int64_t)c.G * c.d)
+        return fail(CSA_EINVAL, "a batch stride is smaller than one batch's extent");
+    if (!aligned(c.raw, 16) || !aligned(c.out, 16) || !aligned(c.logits, 4) || c.raw_bs % 8 || c.out_bs % 8)
+        return fail(CSA_EALIGN, "raw/out need 16-byte alignment and batch strides a multiple of 8 elements");
+    if (overlap(c.out_span(), c.raw_span()) || overlap(c.out_span(), c.log_span()))
+        return fail(CSA_EINVAL, "out overlaps raw or logits");
+    *empty = false;
+    return CSA_OK;
+}
+
+static hipError_t launch_compress_job(const CompressJob &c, hipStream_t st, uint32_t *clr = nullptr,
+                                      int64_t clr_words = 0) {
+    return csa::launch_compress(c.dt, c.B, c.G, c.m, c.d, c.raw, c.raw_bs, c.logits, c.log_bs, c.out, c.out_bs, st,
+                                clr, clr_words);
+}
+
 int csa_compress(int dt, int B, int G, int m, int d, const void *raw, int64_t raw_bstride, const float *logits,
                  int64_t logit_bstride, void *out, int64_t out_bstride, void *stream) {
-    if (int s = check_dt(dt)) return s;
-    if (B < 0 || G < 0) return fail(CSA_EINVAL, "B=%d and G=%d must be >= 0", B, G);
-    if (m < 1 || m > 128) return fail(CSA_EUNSUPPORTED, "m=%d outside 1..128", m);
-    if (!d_supported(d)) return fail(CSA_EUNSUPPORTED, "d=%d not in {32,64,128,256,512}", d);
-    if ((int64_t)B * G == 0) return ok();
-    if (!raw || !logits || !out) return fail(CSA_EINVAL, "NULL tensor pointer");
-    if (raw_bstride < (int64_t)G * m * d || logit_bstride < (int64_t)G * m || out_bstride < (int64_t)G * d)
-        return fail(CSA_EINVAL, "a batch stride is smaller than one batch's extent");
-    if (!aligned(raw, 16) || !aligned(out, 16) || !aligned(logits, 4) || raw_bstride % 8 || out_bstride % 8)
-        return fail(CSA_EALIGN, "raw/out need 16-byte alignment and batch strides a multiple of 8 elements");
-    const size_t es = esize(dt);
-    const Span so = span(out, B, out_bstride, (int64_t)G * d, es);
-    if (overlap(so, span(raw, B, raw_bstride, (int64_t)G * m * d, es)) ||
-        overlap(so, span(logits, B, logit_bstride, (int64_t)G * m, 4)))
-        return fail(CSA_EINVAL, "out overlaps raw or logits");
-    return hip_status(csa::launch_compress(dt, B, G, m, d, raw, raw_bstride, logits, logit_bstride, out,
-                                           out_bstride, (hipStream_t)stream),
-                      "compress launch");
+    const CompressJob c{dt, B, G, m, d, raw, raw_bstride, logits, logit_bstride, out, out_bstride};
+    bool empty;
+    if (int s = check_compress(c, &empty)) return s;
+    if (empty) return ok();
+    return hip_status(launch_compress_job(c, (hipStream_t)stream), "compress launch");
+}
+
+static_assert(csa::kTopkBins % 4 == 0, "the fused clear zeroes whole 16-byte runs");
+
+// a fused call's compression against the index operands, outputs and workspace
+// (its output may not overlap any of them, nor its inputs the workspace, which
+// the same launch clears)
+static int check_compress_against(const CompressJob *cj, const Span *in, int n_in, const Span &si, const Span &ss,
+                                  const Span &sw) {
+    if (!cj) return CSA_OK;
+    const Span so = cj->out_span();
+    for (int i = 0; i < n_in; ++i)
+        if (overlap(so, in[i])) return fail(CSA_EINVAL, "the compression output overlaps an index input");
+    if (overlap(so, si) || overlap(so, ss) || overlap(so, sw) || overlap(cj->raw_span(), sw) ||
+        overlap(cj->log_span(), sw))
+        return fail(CSA_EINVAL, "the compression overlaps an index output or the workspace");
+    return CSA_OK;
 }
 
 int csa_compress_channels(int dt, int B, int G, int m, int d, const void *raw, int64_t raw_bstride,
@@ -357,7 +401,7 @@ static int index_topk_impl(int dt, int B, int Tq, int N, int H_I, int d_I, int m
                            const void *q_idx, const float *w_idx, const void *k_idx, int64_t k_bstride,
                            int32_t *topk_idx, float *scores_out, void *workspace, size_t workspace_bytes,
                            void *stream, const int32_t *page_table = nullptr, int max_pages = 0, int page_rows = 0,
-                           int64_t n_pages = 0) {
+                           int64_t n_pages = 0, const CompressJob *cj = nullptr) {
     if (int s = check_dt(dt)) return s;
     if (B < 0 || Tq < 0 || N < 0) return fail(CSA_EINVAL, "B, Tq and N must be >= 0");
     if (H_I < 1 || H_I > 64) return fail(CSA_EUNSUPPORTED, "H_I=%d outside 1..64", H_I);
@@ -367,7 +411,8 @@ static int index_topk_impl(int dt, int B, int Tq, int N, int H_I, int d_I, int m
     if ((int64_t)B * Tq > 0)
         if (int s = check_qpos(q_pos0, B, Tq)) return s;
     if (N > csa::kTopkMaxEntries) return fail(CSA_EUNSUPPORTED, "N=%d above %lld entries", N, (long long)csa::kTopkMaxEntries);
-    if ((int64_t)B * Tq == 0) return ok();
+    if ((int64_t)B * Tq == 0)
+        return cj ? hip_status(launch_compress_job(*cj, (hipStream_t)stream), "compress launch") : ok();
     if (!q_idx || !w_idx || !topk_idx || (N > 0 && !k_idx)) return fail(CSA_EINVAL, "NULL tensor pointer");
     csa::RowMap kmap(k_bstride);
     int64_t k_span_b = B, k_span_stride = k_bstride, k_span_inner = (int64_t)N * d_I;
@@ -402,10 +447,13 @@ static int index_topk_impl(int dt, int B, int Tq, int N, int H_I, int d_I, int m
     for (const Span &in : inputs)
         if (overlap(sw, in)) return fail(CSA_EINVAL, "workspace overlaps an input");
     if (overlap(sw, si) || overlap(sw, ss)) return fail(CSA_EINVAL, "workspace overlaps an output");
+    if (int s = check_compress_against(cj, inputs, 3, si, ss, sw)) return s;
     hipStream_t st = (hipStream_t)stream;
     if (N > 0) {
-        // the first radix digit of the selection is counted by the indexer
-        if (int s = hip_status(csa::launch_fill_u32(scratch, (int64_t)csa::topk_clear_words(rows, N), 0u, st),
+        // the first radix digit of the selection is counted by the indexer: its
+        // histograms are cleared first, in the compression's launch when there is one
+        const int64_t cw = (int64_t)csa::topk_clear_words(rows, N);
+        if (int s = hip_status(cj ? launch_compress_job(*cj, st, scratch, cw) : csa::launch_fill_u32(scratch, cw, 0u, st),
                                "histogram clear"))
             return s;
         if (int s = hip_status(csa::launch_index_scores(dt, B, Tq, N, H_I, d_I, m, q_pos0, q_idx, w_idx, k_idx,
@@ -413,6 +461,8 @@ static int index_topk_impl(int dt, int B, int Tq, int N, int H_I, int d_I, int m
                                                          scratch, st),
                                "indexer launch"))
             return s;
+    } else if (cj) {
+        if (int s = hip_status(launch_compress_job(*cj, st), "compress launch")) return s;
     }
     return hip_status(csa::launch_topk(B, Tq, N, m, k, q_pos0, scores, scratch, topk_idx, st), "top-k launch");
 }
@@ -423,6 +473,19 @@ int csa_index_topk(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k,
     if (q_pos0 < 0) return fail(CSA_EINVAL, "q_pos0 must be >= 0");
     return index_topk_impl(dt, B, Tq, N, H_I, d_I, m, k, csa::QPos(q_pos0), q_idx, w_idx, k_idx, k_bstride, topk_idx,
                            scores_out, workspace, workspace_bytes, stream);
+}
+
+int csa_compress_index_topk(int dt, int B, int G, int m, int d, const void *raw, int64_t raw_bstride,
+                            const float *logits, int64_t logit_bstride, void *entries_out, int64_t out_bstride,
+                            int Tq, int N, int H_I, int d_I, int k, int64_t q_pos0, const void *q_idx,
+                            const float *w_idx, const void *k_idx, int64_t k_bstride, int32_t *topk_idx,
+                            float *scores_out, void *workspace, size_t workspace_bytes, void *stream) {
+    const CompressJob c{dt, B, G, m, d, raw, raw_bstride, logits, logit_bstride, entries_out, out_bstride};
+    bool empty;
+    if (int s = check_compress(c, &empty)) return s;
+    if (q_pos0 < 0) return fail(CSA_EINVAL, "q_pos0 must be >= 0");
+    return index_topk_impl(dt, B, Tq, N, H_I, d_I, m, k, csa::QPos(q_pos0), q_idx, w_idx, k_idx, k_bstride, topk_idx,
+                           scores_out, workspace, workspace_bytes, stream, nullptr, 0, 0, 0, empty ? nullptr : &c);
 }
 
 int csa_index_topk_noalloc(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k, int64_t q_pos0,
@@ -494,7 +557,7 @@ static int index_topk_mx4_impl(int dt, int B, int Tq, int N, int H_I, int d_I, i
                                const uint8_t *k_scales, int64_t k_bstride, int32_t *topk_idx, float *scores_out,
                                void *workspace, size_t workspace_bytes, void *stream,
                                const int32_t *page_table = nullptr, int max_pages = 0, int page_rows = 0,
-                               int64_t n_pages = 0) {
+                               int64_t n_pages = 0, const CompressJob *cj = nullptr) {
     if (int s = check_dt(dt)) return s;
     if (B < 0 || Tq < 0 || N < 0) return fail(CSA_EINVAL, "B, Tq and N must be >= 0");
     if (H_I < 1 || H_I > 64) return fail(CSA_EUNSUPPORTED, "H_I=%d outside 1..64", H_I);
@@ -504,7 +567,8 @@ static int index_topk_mx4_impl(int dt, int B, int Tq, int N, int H_I, int d_I, i
     if ((int64_t)B * Tq > 0)
         if (int s = check_qpos(q_pos0, B, Tq)) return s;
     if (N > csa::kTopkMaxEntries) return fail(CSA_EUNSUPPORTED, "N=%d above %lld entries", N, (long long)csa::kTopkMaxEntries);
-    if ((int64_t)B * Tq == 0) return ok();
+    if ((int64_t)B * Tq == 0)
+        return cj ? hip_status(launch_compress_job(*cj, (hipStream_t)stream), "compress launch") : ok();
     if (!q_idx || !w_idx || !topk_idx || (N > 0 && (!k_codes || !k_scales)))
         return fail(CSA_EINVAL, "NULL tensor pointer");
     csa::RowMap kmap(k_bstride);
@@ -537,11 +601,13 @@ static int index_topk_mx4_impl(int dt, int B, int Tq, int N, int H_I, int d_I, i
             return fail(CSA_EINVAL, "an output or the workspace overlaps an input");
     if (overlap(si, ss) || overlap(sw, si) || overlap(sw, ss))
         return fail(CSA_EINVAL, "outputs and workspace overlap");
+    if (int s = check_compress_against(cj, inputs, 4, si, ss, sw)) return s;
     float *scores = (float *)workspace;
     uint32_t *scratch = (uint32_t *)((char *)workspace + scores_bytes(rows, N));
     hipStream_t st = (hipStream_t)stream;
     if (N > 0) {
-        if (int s = hip_status(csa::launch_fill_u32(scratch, (int64_t)csa::topk_clear_words(rows, N), 0u, st),
+        const int64_t cw = (int64_t)csa::topk_clear_words(rows, N);
+        if (int s = hip_status(cj ? launch_compress_job(*cj, st, scratch, cw) : csa::launch_fill_u32(scratch, cw, 0u, st),
                                "histogram clear"))
             return s;
         if (int s = hip_status(csa::launch_index_mx4(dt, B, Tq, N, H_I, d_I, m, q_pos0, q_idx, w_idx, k_codes,
@@ -549,6 +615,8 @@ static int index_topk_mx4_impl(int dt, int B, int Tq, int N, int H_I, int d_I, i
                                                       scores_out, scratch, st),
                                "indexer launch"))
             return s;
+    } else if (cj) {
+        if (int s = hip_status(launch_compress_job(*cj, st), "compress launch")) return s;
     }
     return hip_status(csa::launch_topk(B, Tq, N, m, k, q_pos0, scores, scratch, topk_idx, st), "top-k launch");
 }
@@ -560,6 +628,21 @@ int csa_index_topk_mx4(int dt, int B, int Tq, int N, int H_I, int d_I, int m, in
     if (q_pos0 < 0) return fail(CSA_EINVAL, "q_pos0 must be >= 0");
     return index_topk_mx4_impl(dt, B, Tq, N, H_I, d_I, m, k, csa::QPos(q_pos0), q_idx, w_idx, k_codes, k_scales,
                                k_bstride, topk_idx, scores_out, workspace, workspace_bytes, stream);
+}
+
+int csa_compress_index_topk_mx4(int dt, int B, int G, int m, int d, const void *raw, int64_t raw_bstride,
+                                const float *logits, int64_t logit_bstride, void *entries_out, int64_t out_bstride,
+                                int Tq, int N, int H_I, int d_I, int k, int64_t q_pos0, const void *q_idx,
+                                const float *w_idx, const uint8_t *k_codes, const uint8_t *k_scales,
+                                int64_t k_bstride, int32_t *topk_idx, float *scores_out, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+    const CompressJob c{dt, B, G, m, d, raw, raw_bstride, logits, logit_bstride, entries_out, out_bstride};
+    bool empty;
+    if (int s = check_compress(c, &empty)) return s;
+    if (q_pos0 < 0) return fail(CSA_EINVAL, "q_pos0 must be >= 0");
+    return index_topk_mx4_impl(dt, B, Tq, N, H_I, d_I, m, k, csa::QPos(q_pos0), q_idx, w_idx, k_codes, k_scales,
+                               k_bstride, topk_idx, scores_out, workspace, workspace_bytes, stream, nullptr, 0, 0,
+                               0, empty ? nullptr : &c);
 }
 
 int csa_index_scores_mx4(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int64_t q_pos0, const void *q_idx,

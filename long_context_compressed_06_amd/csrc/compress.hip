@@ -79,12 +79,26 @@ __device__ __forceinline__ void compress_group(const T *__restrict__ rows, const
 // k_compress's LDS reduction adds them: the entries are bit-identical.
 constexpr int kWaveRows = 8;
 
+// Workgroups past a compression launch's own work zero words [0, n) of p (n a
+// multiple of 4, p 16-byte aligned), so a clear the next call needs rides in
+// the same launch; workgroup blk of the nblk clearing ones takes a grid stride.
+__device__ __forceinline__ void clear_words(uint32_t *__restrict__ p, int64_t n, int blk, int nblk) {
+    for (int64_t i = ((int64_t)blk * blockDim.x + threadIdx.x) * 4; i < n; i += (int64_t)nblk * blockDim.x * 4)
+        *(u32x4 *)(p + i) = u32x4{0u, 0u, 0u, 0u};
+}
+
 template <typename T>
 __global__ __launch_bounds__(64) void k_compress_wave(int G, int m, int d, int slices, const T *__restrict__ raw,
                                                       int64_t raw_bs, const float *__restrict__ logits,
-                                                      int64_t log_bs, T *__restrict__ out, int64_t out_bs) {
+                                                      int64_t log_bs, T *__restrict__ out, int64_t out_bs,
+                                                      int work_blocks, uint32_t *__restrict__ clr,
+                                                      int64_t clr_words) {
 #pragma clang fp contract(off)  // each product rounded before it is added, as in the LDS reduction
     constexpr int VEC = 16 / sizeof(T);
+    if ((int)blockIdx.x >= work_blocks) {
+        clear_words(clr, clr_words, (int)blockIdx.x - work_blocks, (int)gridDim.x - work_blocks);
+        return;
+    }
     const int lane = threadIdx.x;
     const int sl = blockIdx.x % slices;
     const int64_t bg = blockIdx.x / slices;
@@ -123,7 +137,12 @@ __global__ __launch_bounds__(64) void k_compress_wave(int G, int m, int d, int s
 template <typename T>
 __global__ __launch_bounds__(256) void k_compress(int G, int m, int d, int tpr, int slices, const T *__restrict__ raw,
                                                    int64_t raw_bs, const float *__restrict__ logits,
-                                                   int64_t log_bs, T *__restrict__ out, int64_t out_bs) {
+                                                   int64_t log_bs, T *__restrict__ out, int64_t out_bs,
+                                                   int work_blocks, uint32_t *__restrict__ clr, int64_t clr_words) {
+    if ((int)blockIdx.x >= work_blocks) {  // (uniform per workgroup: before any barrier)
+        clear_words(clr, clr_words, (int)blockIdx.x - work_blocks, (int)gridDim.x - work_blocks);
+        return;
+    }
     const int sl = blockIdx.x % slices;
     const int bg = blockIdx.x / slices;
     const int b = bg / G, g = bg % G;
@@ -233,7 +252,8 @@ __global__ __launch_bounds__(256) void k_compress_channels(int G, int m, int d, 
 
 template <typename T>
 hipError_t launch_compress_t(int B, int G, int m, int d, const void *raw, int64_t raw_bs, const float *logits,
-                             int64_t log_bs, void *out, int64_t out_bs, hipStream_t st) {
+                             int64_t log_bs, void *out, int64_t out_bs, hipStream_t st, uint32_t *clr,
+                             int64_t clr_words) {
     constexpr int VEC = 16 / sizeof(T);
     // threads per row slice: d/VEC (a whole row), halved until the workgroup's
     // row slots times kRowsPerThread cover the m rows
@@ -242,14 +262,22 @@ hipError_t launch_compress_t(int B, int G, int m, int d, const void *raw, int64_
     while (tpr > 1 && (256 / tpr) * kRowsPerThread < m) tpr /= 2;
     if ((256 / tpr) * kRowsPerThread < m) return hipErrorInvalidValue;
     const int slices = d / VEC / tpr;
+    // workgroups for the optional clear: one 16-byte store per thread per pass, at most 256 of them
+    auto clear_blocks = [&](int threads) -> int64_t {
+        const int64_t b = (clr_words / 4 + threads - 1) / threads;
+        return b < 256 ? b : 256;
+    };
     if (tpr == d / VEC && m <= 256 / tpr && m <= kWaveRows) {  // each row slot holds one row: the LDS-free form
         const int wslices = (d / VEC + 63) / 64;
-        hipLaunchKernelGGL(k_compress_wave<T>, dim3((unsigned)((int64_t)B * G * wslices)), dim3(64), 0, st, G, m, d,
-                           wslices, (const T *)raw, raw_bs, logits, log_bs, (T *)out, out_bs);
+        const int64_t work = (int64_t)B * G * wslices;
+        hipLaunchKernelGGL(k_compress_wave<T>, dim3((unsigned)(work + clear_blocks(64))), dim3(64), 0, st, G, m, d,
+                           wslices, (const T *)raw, raw_bs, logits, log_bs, (T *)out, out_bs, (int)work, clr,
+                           clr_words);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_compress<T>, dim3((unsigned)((int64_t)B * G * slices)), dim3(256), 0, st, G, m, d, tpr,
-                       slices, (const T *)raw, raw_bs, logits, log_bs, (T *)out, out_bs);
+    const int64_t work = (int64_t)B * G * slices;
+    hipLaunchKernelGGL(k_compress<T>, dim3((unsigned)(work + clear_blocks(256))), dim3(256), 0, st, G, m, d, tpr,
+                       slices, (const T *)raw, raw_bs, logits, log_bs, (T *)out, out_bs, (int)work, clr, clr_words);
     return hipGetLastError();
 }
 template <typename T>
@@ -298,9 +326,12 @@ hipError_t launch_compress_channels(int dt, int B, int G, int m, int d, const vo
     return launch_compress_channels_t<bf16_t>(B, G, m, d, raw, raw_bs, logits, log_bs, out, out_bs, st);
 }
 hipError_t launch_compress(int dt, int B, int G, int m, int d, const void *raw, int64_t raw_bs,
-                           const float *logits, int64_t log_bs, void *out, int64_t out_bs, hipStream_t st) {
-    if (dt == 0) return launch_compress_t<float>(B, G, m, d, raw, raw_bs, logits, log_bs, out, out_bs, st);
-    return launch_compress_t<bf16_t>(B, G, m, d, raw, raw_bs, logits, log_bs, out, out_bs, st);
+                           const float *logits, int64_t log_bs, void *out, int64_t out_bs, hipStream_t st,
+                           uint32_t *clr, int64_t clr_words) {
+    if ((int64_t)B * G == 0 && clr_words == 0) return hipSuccess;
+    if (dt == 0)
+        return launch_compress_t<float>(B, G, m, d, raw, raw_bs, logits, log_bs, out, out_bs, st, clr, clr_words);
+    return launch_compress_t<bf16_t>(B, G, m, d, raw, raw_bs, logits, log_bs, out, out_bs, st, clr, clr_words);
 }
 
 }  // namespace csa

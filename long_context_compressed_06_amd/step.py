@@ -1,7 +1,9 @@
 """One layer step of hybrid compressed attention, composed from the C-ABI calls.
 
 CSA (DeepSeek-V4 overview page, section 2.2):  compress the new groups ->
-lightning indexer + top-k -> sparse shared-KV MQA with the raw window.  With
+lightning indexer + top-k -> sparse shared-KV MQA with the raw window (the
+first two in one library call, the compression sharing a launch with the
+selection's histogram clear).  With
 FP4 indexer operands (section 9, item 5; index_fmt "mx4") the indexer
 quantises the index queries to MXFP4 itself and scores them against MXFP4
 keys that were quantised once, when they entered the cache
@@ -15,8 +17,8 @@ from __future__ import annotations
 
 import torch
 
-from . import csa_compress, csa_index_topk, csa_index_topk_mx4, csa_mx4_quantize, csa_sparse_mqa, hca_dense_mqa, \
-    index_topk_workspace_bytes, mqa_workspace_bytes
+from . import csa_compress, csa_compress_index_topk, csa_compress_index_topk_mx4, csa_index_topk, csa_index_topk_mx4, \
+    csa_mx4_quantize, csa_sparse_mqa, hca_dense_mqa, index_topk_workspace_bytes, mqa_workspace_bytes
 
 
 class AttentionStep:
@@ -58,16 +60,27 @@ class AttentionStep:
         if not self._ready:
             self._prepare(x)
         raw, entries = x["raw"], x["entries"]
+        # the new groups' compression rides in the index call's first launch (CSA) or runs alone (HCA)
+        comp = ()
         if self.N > self.g0:
             r0 = self.g0 * self.m - self.raw_pos0
-            csa_compress(raw[:, r0:r0 + (self.N - self.g0) * self.m], x["logits"], self.m,
-                         entries[:, self.g0:self.N])
+            comp = (raw[:, r0:r0 + (self.N - self.g0) * self.m], x["logits"], self.m, entries[:, self.g0:self.N])
         if self.mode == "csa" and self.index_fmt == "mx4":
-            csa_index_topk_mx4(x["q_idx"], x["w_idx"], x["k_codes"], x["k_scales"], self.N, self.m, self.k,
-                               self.q_pos0, topk_idx=self.topk_idx, workspace=self.idx_ws)
+            args = (x["q_idx"], x["w_idx"], x["k_codes"], x["k_scales"], self.N)
+            if comp:
+                csa_compress_index_topk_mx4(*comp, *args, self.k, self.q_pos0, topk_idx=self.topk_idx,
+                                            workspace=self.idx_ws)
+            else:
+                csa_index_topk_mx4(*args, self.m, self.k, self.q_pos0, topk_idx=self.topk_idx, workspace=self.idx_ws)
         elif self.mode == "csa":
-            csa_index_topk(x["q_idx"], x["w_idx"], x["k_idx"], self.N, self.m, self.k, self.q_pos0,
-                           topk_idx=self.topk_idx, workspace=self.idx_ws)
+            args = (x["q_idx"], x["w_idx"], x["k_idx"], self.N)
+            if comp:
+                csa_compress_index_topk(*comp, *args, self.k, self.q_pos0, topk_idx=self.topk_idx,
+                                        workspace=self.idx_ws)
+            else:
+                csa_index_topk(*args, self.m, self.k, self.q_pos0, topk_idx=self.topk_idx, workspace=self.idx_ws)
+        elif comp:
+            csa_compress(*comp)
         if self.mode == "csa":
             csa_sparse_mqa(x["q"], entries, self.topk_idx, raw, self.N, self.m, self.W, self.q_pos0, self.raw_pos0,
                            scale=self.scale, out=self.out, lse=self.lse, workspace=self.mqa_ws)

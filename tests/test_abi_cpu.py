@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
     import long_context_compressed_06_amd as csa
 
     names = header_functions()
-    assert len(names) == 24, names
+    assert len(names) == 26, names
     for n in names:
         assert hasattr(L, n), n
     assert sorted(csa.EXPORTS) == names
@@ -101,6 +101,36 @@ def test_index_topk_validation(L):
     assert sc(dt=3) == -2 and sc(HI=0) == -6 and sc(out=0) == -1 and sc(out=P + 0x200000) == -1
     need = L.csa_index_topk_workspace_bytes(2, 3, 1000, 64, 64)
     assert need >= 2 * 3 * 1000 * 4 and need % 256 == 0
+
+
+def fused(L, mx4=False, dt=1, B=1, G=1, m=4, d=512, raw=P + 0x50000000, logits=P + 0x51000000,
+          ent=P + 0x52000000, Tq=1, N=1000, HI=64, dI=128, k=64, q_pos0=3999, q=P, w=P + 0x100000,
+          kk=P + 0x200000, ks=P + 0x280000, out=P + 0x3000000, ws=P + 0x4000000, wsb=1 << 30):
+    c = (dt, B, G, m, d, raw, G * m * d, logits, G * m, ent, G * d)
+    if mx4:
+        return L.csa_compress_index_topk_mx4(*c, Tq, N, HI, dI, k, q_pos0, q, w, kk, ks, N, out, None, ws, wsb,
+                                             None)
+    return L.csa_compress_index_topk(*c, Tq, N, HI, dI, k, q_pos0, q, w, kk, N * dI, out, None, ws, wsb, None)
+
+
+@pytest.mark.parametrize("mx4", [False, True])
+def test_compress_index_topk_validation(L, mx4):
+    """The fused call keeps both calls' checks, and its compression output may touch no index operand,
+    output or the workspace (which its launch clears), nor its inputs the workspace."""
+    f = lambda **kw: fused(L, mx4, **kw)
+    assert f(dt=2) == -2
+    assert f(d=100) == -6 and f(m=0) == -6
+    assert f(ent=P + 0x50000000 + 64) == -1      # entries overlap raw
+    assert f(HI=65) == -6 and f(k=0) == -6 and f(q_pos0=-1) == -1
+    assert f(wsb=1000 * 4 - 1) == -4
+    assert f(ent=P + 16) == -1                     # entries overlap q_idx
+    assert b"index input" in L.csa_last_error_detail()
+    assert f(ent=P + 0x3000000) == -1              # ... the selection output
+    assert f(ent=P + 0x4000000 + 256) == -1        # ... the workspace
+    assert f(raw=P + 0x4000000 + 4096) == -1       # raw inside the workspace
+    assert f(logits=P + 0x4000000 + 4096) == -1
+    assert b"workspace" in L.csa_last_error_detail()
+    assert f(B=0) == 0 and f(G=0, Tq=0) == 0       # empty: nothing enqueued
 
 
 def mqa(L, fn="sparse", dt=1, B=1, Tq=1, H=64, d=512, N=1000, m=4, k=64, W=128, q_pos0=4095, scale=0.04,

@@ -315,3 +315,54 @@ def test_compress_forms_bit_identical(csa, dtype, m, d):
         torch.cuda.synchronize()
         assert torch.equal(cache[:, 0].view(torch.int16 if dtype == "bf16" else torch.int32),
                            out[:, gi].view(torch.int16 if dtype == "bf16" else torch.int32)), gi
+
+
+# ------------------------------- compression fused into the index call's first launch
+FUSED = [("elem", "bf16", 4, 512, 1, 1, 3000), ("mx4", "bf16", 4, 512, 1, 1, 3000),
+         ("elem", "bf16", 16, 128, 3, 2, 2500), ("mx4", "f32", 8, 256, 2, 4, 1900),
+         ("elem", "f32", 4, 64, 5, 1, 40), ("elem", "bf16", 4, 512, 2, 1, 0), ("mx4", "bf16", 4, 512, 1, 3, 0)]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=["-".join(map(str, c)) for c in FUSED])
+def test_compress_index_topk_fused_bit_identical(csa, case):
+    """The fused call gives what csa_compress then the index call give, bit for bit: entries, selection and
+    scores.  Both run on one workspace, the fused call after the separate one and then again, so its own
+    histogram clear is what resets the selection's counts each time."""
+    fmt, dtype, m, d, Tq, G, N = case
+    say("fused compress + index", case)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    B, HI, dI, k = 3, 16, 128, 64
+    q_pos0 = max(N * m - Tq, 0)
+    g = torch.Generator().manual_seed(9100 + 7 * m + d + N)
+    raw = (torch.randn((B, G * m, d), generator=g) * 2).to(dt).cuda()
+    logits = torch.randn((B, G * m), generator=g).cuda()
+    q_idx = torch.randn((B, Tq, HI, dI), generator=g).to(dt).cuda()
+    w_idx = torch.randn((B, Tq, HI), generator=g).cuda()
+    k_idx = torch.randn((B, max(N, 1), dI), generator=g).to(dt).cuda()
+    ws = torch.empty(max(csa.index_topk_workspace_bytes(B, Tq, N, HI, k), 256), dtype=torch.uint8, device="cuda")
+    if fmt == "mx4":
+        codes, scales = csa.csa_mx4_quantize(k_idx)
+        kargs = (codes, scales)
+        sep, fused = csa.csa_index_topk_mx4, csa.csa_compress_index_topk_mx4
+    else:
+        kargs = (k_idx,)
+        sep, fused = csa.csa_index_topk, csa.csa_compress_index_topk
+
+    def outputs():
+        return (torch.full((B, G, d), float("nan"), dtype=dt, device="cuda"),
+                torch.full((B, Tq, k), -7, dtype=torch.int32, device="cuda"),
+                torch.full((B, Tq, N), float("nan"), device="cuda"))
+
+    ea, ia, sa = outputs()
+    csa.csa_compress(raw, logits, m, ea)
+    sep(q_idx, w_idx, *kargs, N, m, k, q_pos0, topk_idx=ia, scores_out=sa, workspace=ws)
+    torch.cuda.synchronize()
+    bits = torch.int16 if dtype == "bf16" else torch.int32
+    for rep in range(2):
+        eb, ib, sb = outputs()
+        fused(raw, logits, m, eb, q_idx, w_idx, *kargs, N, k, q_pos0, topk_idx=ib, scores_out=sb, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(ea.view(bits), eb.view(bits)), rep
+        assert torch.equal(ia, ib), rep
+        assert torch.equal(sa.view(torch.int32), sb.view(torch.int32)), rep
+    assert not torch.isnan(ea.float()).any()
