@@ -231,6 +231,41 @@ int csa_ragged_index_topk_mx4(int dt, int B, int N, int H_I, int d_I, int m, int
                               const int32_t *page_table, int max_pages, int page_rows, int64_t n_pages,
                               int32_t *topk_idx, float *scores_out,
                               void *workspace, size_t workspace_bytes, void *stream);
+/*
+ * csa_ragged_compress_index_topk (+ _mx4) -- csa_ragged_compress followed by
+ * csa_ragged_index_topk (csa_ragged_index_topk_mx4) on the same stream, the
+ * compression running in the launch that clears the selection's histograms,
+ * as csa_compress_index_topk does for uniform batches.  The arguments are the
+ * two calls' own, in order (dt, B, m and pos shared; the e_ page arguments
+ * are the compression's, the others the index keys'); the results equal
+ * those of the two calls bit for bit.  Besides each call's checks,
+ * entries_out may overlap no index operand, output or the workspace, and the
+ * rings and pos may not overlap the workspace (CSA_EINVAL).
+ */
+int csa_ragged_compress_index_topk(int dt, int B, int m, int d, const int64_t *pos,
+                                   const void *raw_ring, int64_t ring_bstride,
+                                   const float *logit_ring, int64_t logit_bstride, int64_t ring,
+                                   void *entries_out, int64_t out_bstride, int64_t out_rows,
+                                   const int32_t *e_page_table, int e_max_pages, int e_page_rows,
+                                   int64_t e_n_pages,
+                                   int N, int H_I, int d_I, int k,
+                                   const void *q_idx, const float *w_idx,
+                                   const void *k_idx, int64_t k_bstride,
+                                   const int32_t *page_table, int max_pages, int page_rows, int64_t n_pages,
+                                   int32_t *topk_idx, float *scores_out,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+int csa_ragged_compress_index_topk_mx4(int dt, int B, int m, int d, const int64_t *pos,
+                                       const void *raw_ring, int64_t ring_bstride,
+                                       const float *logit_ring, int64_t logit_bstride, int64_t ring,
+                                       void *entries_out, int64_t out_bstride, int64_t out_rows,
+                                       const int32_t *e_page_table, int e_max_pages, int e_page_rows,
+                                       int64_t e_n_pages,
+                                       int N, int H_I, int d_I, int k,
+                                       const void *q_idx, const float *w_idx,
+                                       const uint8_t *k_codes, const uint8_t *k_scales, int64_t k_bstride,
+                                       const int32_t *page_table, int max_pages, int page_rows, int64_t n_pages,
+                                       int32_t *topk_idx, float *scores_out,
+                                       void *workspace, size_t workspace_bytes, void *stream);
 int csa_ragged_sparse_mqa(int dt, int B, int H, int d, int N, int m, int k, int W,
                           const int64_t *pos, float scale,
                           const void *q,

@@ -26,7 +26,7 @@ EXPORTS = ("csa_abi_version", "csa_status_string", "csa_last_error_detail", "csa
            "csa_compress_channels", "csa_append_rows_multi", "csa_positions_advance", "csa_ragged_compress",
            "csa_ragged_index_topk", "csa_ragged_index_topk_mx4", "csa_ragged_sparse_mqa", "hca_ragged_dense_mqa", "csa_stream_read",
            "csa_index_topk_noalloc", "csa_index_scores_mx4", "csa_compress_index_topk",
-           "csa_compress_index_topk_mx4")
+           "csa_compress_index_topk_mx4", "csa_ragged_compress_index_topk", "csa_ragged_compress_index_topk_mx4")
 
 
 class AppendJob(ctypes.Structure):
@@ -106,6 +106,12 @@ def lib():
     L.csa_compress_index_topk.restype = I
     L.csa_compress_index_topk_mx4.argtypes = comp + [I, I, I, I, I, I64, P, P, P, P, I64, P, P, P, SZ, P]
     L.csa_compress_index_topk_mx4.restype = I
+    rcomp = [I, I, I, I, P, P, I64, P, I64, I64, P, I64, I64, P, I, I, I64]  # csa_ragged_compress's, no stream
+    L.csa_ragged_compress_index_topk.argtypes = rcomp + [I, I, I, I, P, P, P, I64, P, I, I, I64, P, P, P, SZ, P]
+    L.csa_ragged_compress_index_topk.restype = I
+    L.csa_ragged_compress_index_topk_mx4.argtypes = rcomp + [I, I, I, I, P, P, P, P, I64, P, I, I, I64, P, P, P, SZ,
+                                                             P]
+    L.csa_ragged_compress_index_topk_mx4.restype = I
     L.csa_stream_read.argtypes = [P, I64, I, P, P]
     L.csa_stream_read.restype = I
     L.csa_append_rows.restype = I
@@ -483,10 +489,8 @@ def _ragged_pos(pos, B):
         raise ValueError("pos must be a contiguous [B] int64 tensor")
 
 
-def csa_ragged_compress(raw_ring: torch.Tensor, logit_ring: torch.Tensor, ring: int, m: int, pos: torch.Tensor,
-                        out: torch.Tensor, pages=None) -> torch.Tensor:
-    """Per sequence, the group its newest token (position pos[b]) completes, pooled out of the mirrored rings
-    raw_ring [B, 2*ring, d] / logit_ring [B, 2*ring] into out [B, cap, d] at row (pos[b]+1)/m - 1."""
+def _ragged_compress_args(raw_ring, logit_ring, ring, m, pos, out, pages) -> tuple:
+    """Checks csa_ragged_compress's tensors; returns its arguments from dt to n_pages."""
     _need(raw_ring, "raw_ring", dims=3)
     _need(logit_ring, "logit_ring", torch.float32)
     _need(out, "out", raw_ring.dtype, 3)
@@ -496,16 +500,22 @@ def csa_ragged_compress(raw_ring: torch.Tensor, logit_ring: torch.Tensor, ring: 
         raise ValueError("ring and cache rows must be packed")
     pt, mp, pr, npg = _pages(pages, B)
     rows = mp * pr if pages is not None else out.shape[1]
-    _check(lib().csa_ragged_compress(_dt(raw_ring), B, m, d, _p(pos), _p(raw_ring), _bstride(raw_ring),
-                                     _p(logit_ring), _bstride(logit_ring), ring, _p(out),
-                                     0 if pages is not None else _bstride(out), rows, pt, mp, pr, npg,
+    return (_dt(raw_ring), B, m, d, _p(pos), _p(raw_ring), _bstride(raw_ring), _p(logit_ring), _bstride(logit_ring),
+            ring, _p(out), 0 if pages is not None else _bstride(out), rows, pt, mp, pr, npg)
+
+
+def csa_ragged_compress(raw_ring: torch.Tensor, logit_ring: torch.Tensor, ring: int, m: int, pos: torch.Tensor,
+                        out: torch.Tensor, pages=None) -> torch.Tensor:
+    """Per sequence, the group its newest token (position pos[b]) completes, pooled out of the mirrored rings
+    raw_ring [B, 2*ring, d] / logit_ring [B, 2*ring] into out [B, cap, d] at row (pos[b]+1)/m - 1."""
+    _check(lib().csa_ragged_compress(*_ragged_compress_args(raw_ring, logit_ring, ring, m, pos, out, pages),
                                      _stream(raw_ring)))
     return out
 
 
-def csa_ragged_index_topk(q_idx, w_idx, k_idx, N: int, m: int, k: int, pos, topk_idx=None, scores_out=None,
-                          workspace=None, pages=None) -> torch.Tensor:
-    """One query per sequence at position pos[b]: q_idx [B,1,H_I,d_I], w_idx [B,1,H_I], k_idx [B,cap,d_I]."""
+def _ragged_index_args(q_idx, w_idx, k_idx, N, k, pos, topk_idx, scores_out, workspace, pages) -> tuple:
+    """Checks csa_ragged_index_topk's tensors (allocating the missing outputs); returns (topk_idx, its arguments
+    from N to workspace_bytes, with m and pos left out)."""
     _need(q_idx, "q_idx", dims=4)
     _need(w_idx, "w_idx", torch.float32, 3)
     _need(k_idx, "k_idx", q_idx.dtype, 3)
@@ -523,15 +533,35 @@ def csa_ragged_index_topk(q_idx, w_idx, k_idx, N: int, m: int, k: int, pos, topk
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q_idx.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().csa_ragged_index_topk(_dt(q_idx), B, N, HI, dI, m, k, _p(pos), _p(q_idx), _p(w_idx), _p(k_idx),
-                                       _bstride(k_idx), pt, mp, pr, npg, _p(topk_idx), _p(scores_out), _p(workspace),
-                                       ws_bytes, _stream(q_idx)))
+    return topk_idx, (N, HI, dI, k, _p(q_idx), _p(w_idx), _p(k_idx), _bstride(k_idx), pt, mp, pr, npg, _p(topk_idx),
+                      _p(scores_out), _p(workspace), ws_bytes)
+
+
+def csa_ragged_index_topk(q_idx, w_idx, k_idx, N: int, m: int, k: int, pos, topk_idx=None, scores_out=None,
+                          workspace=None, pages=None) -> torch.Tensor:
+    """One query per sequence at position pos[b]: q_idx [B,1,H_I,d_I], w_idx [B,1,H_I], k_idx [B,cap,d_I]."""
+    topk_idx, a = _ragged_index_args(q_idx, w_idx, k_idx, N, k, pos, topk_idx, scores_out, workspace, pages)
+    _check(lib().csa_ragged_index_topk(_dt(q_idx), q_idx.shape[0], *a[:3], m, a[3], _p(pos), *a[4:],
+                                       _stream(q_idx)))
     return topk_idx
 
 
-def csa_ragged_index_topk_mx4(q_idx, w_idx, k_codes, k_scales, N: int, m: int, k: int, pos, topk_idx=None,
-                              scores_out=None, workspace=None, pages=None) -> torch.Tensor:
-    """csa_ragged_index_topk on MXFP4 keys (codes [B,cap,d_I/2], scales [B,cap,d_I/32])."""
+def csa_ragged_compress_index_topk(raw_ring, logit_ring, ring: int, m: int, pos, entries_out, q_idx, w_idx, k_idx,
+                                   N: int, k: int, topk_idx=None, scores_out=None, workspace=None, entry_pages=None,
+                                   pages=None) -> torch.Tensor:
+    """csa_ragged_compress(raw_ring, logit_ring, ring, m, pos, entries_out, entry_pages) then
+    csa_ragged_index_topk(q_idx, w_idx, k_idx, N, m, k, pos, ..., pages) in one call with one launch fewer."""
+    _fused_pair(raw_ring, q_idx)
+    c = _ragged_compress_args(raw_ring, logit_ring, ring, m, pos, entries_out, entry_pages)
+    topk_idx, a = _ragged_index_args(q_idx, w_idx, k_idx, N, k, pos, topk_idx, scores_out, workspace, pages)
+    _check(lib().csa_ragged_compress_index_topk(*c, *a, _stream(q_idx)))
+    return topk_idx
+
+
+def _ragged_index_mx4_args(q_idx, w_idx, k_codes, k_scales, N, k, pos, topk_idx, scores_out, workspace,
+                           pages) -> tuple:
+    """Checks csa_ragged_index_topk_mx4's tensors (allocating the missing outputs); returns (topk_idx, its
+    arguments from N to workspace_bytes, with m and pos left out)."""
     _need(q_idx, "q_idx", dims=4)
     _need(w_idx, "w_idx", torch.float32, 3)
     B, Tq, HI, dI = q_idx.shape
@@ -549,9 +579,29 @@ def csa_ragged_index_topk_mx4(q_idx, w_idx, k_codes, k_scales, N: int, m: int, k
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q_idx.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().csa_ragged_index_topk_mx4(_dt(q_idx), B, N, HI, dI, m, k, _p(pos), _p(q_idx), _p(w_idx),
-                                           _p(k_codes), _p(k_scales), cap, pt, mp, pr, npg, _p(topk_idx),
-                                           _p(scores_out), _p(workspace), ws_bytes, _stream(q_idx)))
+    return topk_idx, (N, HI, dI, k, _p(q_idx), _p(w_idx), _p(k_codes), _p(k_scales), cap, pt, mp, pr, npg,
+                      _p(topk_idx), _p(scores_out), _p(workspace), ws_bytes)
+
+
+def csa_ragged_index_topk_mx4(q_idx, w_idx, k_codes, k_scales, N: int, m: int, k: int, pos, topk_idx=None,
+                              scores_out=None, workspace=None, pages=None) -> torch.Tensor:
+    """csa_ragged_index_topk on MXFP4 keys (codes [B,cap,d_I/2], scales [B,cap,d_I/32])."""
+    topk_idx, a = _ragged_index_mx4_args(q_idx, w_idx, k_codes, k_scales, N, k, pos, topk_idx, scores_out,
+                                         workspace, pages)
+    _check(lib().csa_ragged_index_topk_mx4(_dt(q_idx), q_idx.shape[0], *a[:3], m, a[3], _p(pos), *a[4:],
+                                           _stream(q_idx)))
+    return topk_idx
+
+
+def csa_ragged_compress_index_topk_mx4(raw_ring, logit_ring, ring: int, m: int, pos, entries_out, q_idx, w_idx,
+                                       k_codes, k_scales, N: int, k: int, topk_idx=None, scores_out=None,
+                                       workspace=None, entry_pages=None, pages=None) -> torch.Tensor:
+    """csa_ragged_compress then csa_ragged_index_topk_mx4 in one call with one launch fewer."""
+    _fused_pair(raw_ring, q_idx)
+    c = _ragged_compress_args(raw_ring, logit_ring, ring, m, pos, entries_out, entry_pages)
+    topk_idx, a = _ragged_index_mx4_args(q_idx, w_idx, k_codes, k_scales, N, k, pos, topk_idx, scores_out,
+                                         workspace, pages)
+    _check(lib().csa_ragged_compress_index_topk_mx4(*c, *a, _stream(q_idx)))
     return topk_idx
 
 

@@ -177,18 +177,37 @@ int csa_compress(int dt, int B, int G, int m, int d, const void *raw, int64_t ra
 
 static_assert(csa::kTopkBins % 4 == 0, "the fused clear zeroes whole 16-byte runs");
 
-// a fused call's compression against the index operands, outputs and workspace
-// (its output may not overlap any of them, nor its inputs the workspace, which
-// the same launch clears)
-static int check_compress_against(const CompressJob *cj, const Span *in, int n_in, const Span &si, const Span &ss,
-                                  const Span &sw) {
-    if (!cj) return CSA_OK;
-    const Span so = cj->out_span();
+// A checked compression that an index call runs in the launch clearing its
+// top-k histograms: the bytes it writes and reads (for the overlap checks) and
+// how to launch it with that clear.
+struct FusedCompress {
+    Span out;
+    Span in[3];
+    int n_in;
+    hipError_t (*launch)(const void *job, hipStream_t st, uint32_t *clr, int64_t clr_words);
+    const void *job;
+};
+
+static FusedCompress fused(const CompressJob &c) {
+    return FusedCompress{c.out_span(), {c.raw_span(), c.log_span(), Span{}}, 2,
+                         [](const void *j, hipStream_t st, uint32_t *clr, int64_t cw) {
+                             return launch_compress_job(*(const CompressJob *)j, st, clr, cw);
+                         },
+                         &c};
+}
+
+// the compression against the index operands, outputs and workspace (its
+// output may not overlap any of them, nor its inputs the workspace, which the
+// same launch clears)
+static int check_compress_against(const FusedCompress *fc, const Span *in, int n_in, const Span &si,
+                                  const Span &ss, const Span &sw) {
+    if (!fc) return CSA_OK;
     for (int i = 0; i < n_in; ++i)
-        if (overlap(so, in[i])) return fail(CSA_EINVAL, "the compression output overlaps an index input");
-    if (overlap(so, si) || overlap(so, ss) || overlap(so, sw) || overlap(cj->raw_span(), sw) ||
-        overlap(cj->log_span(), sw))
+        if (overlap(fc->out, in[i])) return fail(CSA_EINVAL, "the compression output overlaps an index input");
+    if (overlap(fc->out, si) || overlap(fc->out, ss) || overlap(fc->out, sw))
         return fail(CSA_EINVAL, "the compression overlaps an index output or the workspace");
+    for (int i = 0; i < fc->n_in; ++i)
+        if (overlap(fc->in[i], sw)) return fail(CSA_EINVAL, "a compression input overlaps the workspace");
     return CSA_OK;
 }
 
@@ -327,38 +346,84 @@ int csa_positions_advance(int B, int64_t *pos, int64_t delta, void *stream) {
     return hip_status(csa::launch_positions_advance(B, pos, delta, (hipStream_t)stream), "advance launch");
 }
 
+// a ragged compression (csa_ragged_compress's arguments), checked on its own or ahead of an index call
+struct RaggedCompressJob {
+    int dt, B, m, d;
+    const int64_t *pos;
+    const void *raw_ring;
+    int64_t ring_bs;
+    const float *logit_ring;
+    int64_t logit_bs, ring;
+    void *out;
+    int64_t out_bs, out_rows;
+    const int32_t *page_table;
+    int max_pages, page_rows;
+    int64_t n_pages;
+    // set by the check: the output's row map and what each operand spans
+    csa::RowMap omap{0};
+    Span so{}, sraw{}, slog{}, spos{};
+};
+
+// csa_ragged_compress's checks; *empty when nothing can be written
+static int check_ragged_compress(RaggedCompressJob &c, bool *empty) {
+    *empty = true;
+    if (int s = check_dt(c.dt)) return s;
+    if (c.B < 0 || c.out_rows < 0) return fail(CSA_EINVAL, "B and out_rows must be >= 0");
+    if (c.m < 1 || c.m > 128) return fail(CSA_EUNSUPPORTED, "m=%d outside 1..128", c.m);
+    if (!d_supported(c.d)) return fail(CSA_EUNSUPPORTED, "d=%d not in {32,64,128,256,512}", c.d);
+    if (c.ring < c.m)
+        return fail(CSA_EINVAL, "a ring of %lld positions cannot hold a group of %d", (long long)c.ring, c.m);
+    if (c.B == 0 || c.out_rows == 0) return ok();
+    if (!c.pos || !c.raw_ring || !c.logit_ring || !c.out) return fail(CSA_EINVAL, "NULL tensor pointer");
+    c.omap = csa::RowMap(c.out_bs);
+    int64_t o_span_b = c.B, o_span_stride = c.out_bs, o_span_inner = c.out_rows * c.d;
+    if (c.page_table) {
+        if (int s = check_pages(c.page_table, c.B, c.max_pages, c.page_rows, c.n_pages, c.out_rows, &c.omap))
+            return s;
+        o_span_b = 1, o_span_stride = 0, o_span_inner = c.n_pages * c.page_rows * c.d;
+    } else if (c.out_bs < c.out_rows * c.d) {
+        return fail(CSA_EINVAL, "out_bstride smaller than out_rows*d");
+    }
+    if (c.ring_bs < 2 * c.ring * c.d || c.logit_bs < 2 * c.ring)
+        return fail(CSA_EINVAL, "a batch stride is smaller than one batch's extent (rings hold 2*ring rows)");
+    if (!aligned(c.raw_ring, 16) || !aligned(c.out, 16) || !aligned(c.logit_ring, 4) || !aligned(c.pos, 8) ||
+        c.ring_bs % 8 || c.out_bs % 8)
+        return fail(CSA_EALIGN, "raw/out need 16-byte alignment and batch strides a multiple of 8 elements");
+    const size_t es = esize(c.dt);
+    c.so = span(c.out, o_span_b, o_span_stride, o_span_inner, es);
+    c.sraw = span(c.raw_ring, c.B, c.ring_bs, 2 * c.ring * c.d, es);
+    c.slog = span(c.logit_ring, c.B, c.logit_bs, 2 * c.ring, 4);
+    c.spos = span(c.pos, 1, 0, c.B, 8);
+    if (overlap(c.so, c.sraw) || overlap(c.so, c.slog) || overlap(c.so, c.spos))
+        return fail(CSA_EINVAL, "out overlaps an input");
+    *empty = false;
+    return CSA_OK;
+}
+
+static hipError_t launch_ragged_compress_job(const RaggedCompressJob &c, hipStream_t st, uint32_t *clr = nullptr,
+                                             int64_t clr_words = 0) {
+    return csa::launch_compress_ragged(c.dt, c.B, c.m, c.d, c.pos, c.raw_ring, c.ring_bs, c.logit_ring, c.logit_bs,
+                                       c.ring, c.out, c.omap, c.out_rows, st, clr, clr_words);
+}
+
+static FusedCompress fused(const RaggedCompressJob &c) {
+    return FusedCompress{c.so, {c.sraw, c.slog, c.spos}, 3,
+                         [](const void *j, hipStream_t st, uint32_t *clr, int64_t cw) {
+                             return launch_ragged_compress_job(*(const RaggedCompressJob *)j, st, clr, cw);
+                         },
+                         &c};
+}
+
 int csa_ragged_compress(int dt, int B, int m, int d, const int64_t *pos, const void *raw_ring, int64_t ring_bstride,
                         const float *logit_ring, int64_t logit_bstride, int64_t ring, void *out, int64_t out_bstride,
                         int64_t out_rows, const int32_t *page_table, int max_pages, int page_rows, int64_t n_pages,
                         void *stream) {
-    if (int s = check_dt(dt)) return s;
-    if (B < 0 || out_rows < 0) return fail(CSA_EINVAL, "B and out_rows must be >= 0");
-    if (m < 1 || m > 128) return fail(CSA_EUNSUPPORTED, "m=%d outside 1..128", m);
-    if (!d_supported(d)) return fail(CSA_EUNSUPPORTED, "d=%d not in {32,64,128,256,512}", d);
-    if (ring < m) return fail(CSA_EINVAL, "a ring of %lld positions cannot hold a group of %d", (long long)ring, m);
-    if (B == 0 || out_rows == 0) return ok();
-    if (!pos || !raw_ring || !logit_ring || !out) return fail(CSA_EINVAL, "NULL tensor pointer");
-    csa::RowMap omap(out_bstride);
-    int64_t o_span_b = B, o_span_stride = out_bstride, o_span_inner = out_rows * d;
-    if (page_table) {
-        if (int s = check_pages(page_table, B, max_pages, page_rows, n_pages, out_rows, &omap)) return s;
-        o_span_b = 1, o_span_stride = 0, o_span_inner = n_pages * page_rows * d;
-    } else if (out_bstride < out_rows * d) {
-        return fail(CSA_EINVAL, "out_bstride smaller than out_rows*d");
-    }
-    if (ring_bstride < 2 * ring * d || logit_bstride < 2 * ring)
-        return fail(CSA_EINVAL, "a batch stride is smaller than one batch's extent (rings hold 2*ring rows)");
-    if (!aligned(raw_ring, 16) || !aligned(out, 16) || !aligned(logit_ring, 4) || !aligned(pos, 8) ||
-        ring_bstride % 8 || out_bstride % 8)
-        return fail(CSA_EALIGN, "raw/out need 16-byte alignment and batch strides a multiple of 8 elements");
-    const size_t es = esize(dt);
-    const Span so = span(out, o_span_b, o_span_stride, o_span_inner, es);
-    if (overlap(so, span(raw_ring, B, ring_bstride, 2 * ring * d, es)) ||
-        overlap(so, span(logit_ring, B, logit_bstride, 2 * ring, 4)) || overlap(so, span(pos, 1, 0, B, 8)))
-        return fail(CSA_EINVAL, "out overlaps an input");
-    return hip_status(csa::launch_compress_ragged(dt, B, m, d, pos, raw_ring, ring_bstride, logit_ring, logit_bstride,
-                                                  ring, out, omap, out_rows, (hipStream_t)stream),
-                      "compress launch");
+    RaggedCompressJob c{dt, B, m, d, pos, raw_ring, ring_bstride, logit_ring, logit_bstride, ring, out, out_bstride,
+                        out_rows, page_table, max_pages, page_rows, n_pages};
+    bool empty;
+    if (int s = check_ragged_compress(c, &empty)) return s;
+    if (empty) return ok();
+    return hip_status(launch_ragged_compress_job(c, (hipStream_t)stream), "compress launch");
 }
 
 int csa_append_rows(int B, int n, int64_t row_bytes, const void *rows, int64_t rows_bstride, void *dst,
@@ -401,7 +466,7 @@ static int index_topk_impl(int dt, int B, int Tq, int N, int H_I, int d_I, int m
                            const void *q_idx, const float *w_idx, const void *k_idx, int64_t k_bstride,
                            int32_t *topk_idx, float *scores_out, void *workspace, size_t workspace_bytes,
                            void *stream, const int32_t *page_table = nullptr, int max_pages = 0, int page_rows = 0,
-                           int64_t n_pages = 0, const CompressJob *cj = nullptr) {
+                           int64_t n_pages = 0, const FusedCompress *fc = nullptr) {
     if (int s = check_dt(dt)) return s;
     if (B < 0 || Tq < 0 || N < 0) return fail(CSA_EINVAL, "B, Tq and N must be >= 0");
     if (H_I < 1 || H_I > 64) return fail(CSA_EUNSUPPORTED, "H_I=%d outside 1..64", H_I);
@@ -412,7 +477,7 @@ static int index_topk_impl(int dt, int B, int Tq, int N, int H_I, int d_I, int m
         if (int s = check_qpos(q_pos0, B, Tq)) return s;
     if (N > csa::kTopkMaxEntries) return fail(CSA_EUNSUPPORTED, "N=%d above %lld entries", N, (long long)csa::kTopkMaxEntries);
     if ((int64_t)B * Tq == 0)
-        return cj ? hip_status(launch_compress_job(*cj, (hipStream_t)stream), "compress launch") : ok();
+        return fc ? hip_status(fc->launch(fc->job, (hipStream_t)stream, nullptr, 0), "compress launch") : ok();
     if (!q_idx || !w_idx || !topk_idx || (N > 0 && !k_idx)) return fail(CSA_EINVAL, "NULL tensor pointer");
     csa::RowMap kmap(k_bstride);
     int64_t k_span_b = B, k_span_stride = k_bstride, k_span_inner = (int64_t)N * d_I;
@@ -447,13 +512,13 @@ static int index_topk_impl(int dt, int B, int Tq, int N, int H_I, int d_I, int m
     for (const Span &in : inputs)
         if (overlap(sw, in)) return fail(CSA_EINVAL, "workspace overlaps an input");
     if (overlap(sw, si) || overlap(sw, ss)) return fail(CSA_EINVAL, "workspace overlaps an output");
-    if (int s = check_compress_against(cj, inputs, 3, si, ss, sw)) return s;
+    if (int s = check_compress_against(fc, inputs, 3, si, ss, sw)) return s;
     hipStream_t st = (hipStream_t)stream;
     if (N > 0) {
         // the first radix digit of the selection is counted by the indexer: its
         // histograms are cleared first, in the compression's launch when there is one
         const int64_t cw = (int64_t)csa::topk_clear_words(rows, N);
-        if (int s = hip_status(cj ? launch_compress_job(*cj, st, scratch, cw) : csa::launch_fill_u32(scratch, cw, 0u, st),
+        if (int s = hip_status(fc ? fc->launch(fc->job, st, scratch, cw) : csa::launch_fill_u32(scratch, cw, 0u, st),
                                "histogram clear"))
             return s;
         if (int s = hip_status(csa::launch_index_scores(dt, B, Tq, N, H_I, d_I, m, q_pos0, q_idx, w_idx, k_idx,
@@ -461,8 +526,8 @@ static int index_topk_impl(int dt, int B, int Tq, int N, int H_I, int d_I, int m
                                                          scratch, st),
                                "indexer launch"))
             return s;
-    } else if (cj) {
-        if (int s = hip_status(launch_compress_job(*cj, st), "compress launch")) return s;
+    } else if (fc) {
+        if (int s = hip_status(fc->launch(fc->job, st, nullptr, 0), "compress launch")) return s;
     }
     return hip_status(csa::launch_topk(B, Tq, N, m, k, q_pos0, scores, scratch, topk_idx, st), "top-k launch");
 }
@@ -484,8 +549,9 @@ int csa_compress_index_topk(int dt, int B, int G, int m, int d, const void *raw,
     bool empty;
     if (int s = check_compress(c, &empty)) return s;
     if (q_pos0 < 0) return fail(CSA_EINVAL, "q_pos0 must be >= 0");
+    const FusedCompress fc = fused(c);
     return index_topk_impl(dt, B, Tq, N, H_I, d_I, m, k, csa::QPos(q_pos0), q_idx, w_idx, k_idx, k_bstride, topk_idx,
-                           scores_out, workspace, workspace_bytes, stream, nullptr, 0, 0, 0, empty ? nullptr : &c);
+                           scores_out, workspace, workspace_bytes, stream, nullptr, 0, 0, 0, empty ? nullptr : &fc);
 }
 
 int csa_index_topk_noalloc(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k, int64_t q_pos0,
@@ -512,6 +578,26 @@ int csa_ragged_index_topk(int dt, int B, int N, int H_I, int d_I, int m, int k, 
     return index_topk_impl(dt, B, 1, N, H_I, d_I, m, k, csa::QPos(0, pos), q_idx, w_idx, k_idx, k_bstride, topk_idx,
                            scores_out, workspace, workspace_bytes, stream, page_table, max_pages, page_rows,
                            n_pages);
+}
+
+int csa_ragged_compress_index_topk(int dt, int B, int m, int d, const int64_t *pos, const void *raw_ring,
+                                   int64_t ring_bstride, const float *logit_ring, int64_t logit_bstride,
+                                   int64_t ring, void *entries_out, int64_t out_bstride, int64_t out_rows,
+                                   const int32_t *e_page_table, int e_max_pages, int e_page_rows,
+                                   int64_t e_n_pages, int N, int H_I, int d_I, int k, const void *q_idx,
+                                   const float *w_idx, const void *k_idx, int64_t k_bstride,
+                                   const int32_t *page_table, int max_pages, int page_rows, int64_t n_pages,
+                                   int32_t *topk_idx, float *scores_out, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+    RaggedCompressJob c{dt, B, m, d, pos, raw_ring, ring_bstride, logit_ring, logit_bstride, ring, entries_out,
+                        out_bstride, out_rows, e_page_table, e_max_pages, e_page_rows, e_n_pages};
+    bool empty;
+    if (int s = check_ragged_compress(c, &empty)) return s;
+    if (B > 0 && !pos) return fail(CSA_EINVAL, "NULL pos");
+    const FusedCompress fc = fused(c);
+    return index_topk_impl(dt, B, 1, N, H_I, d_I, m, k, csa::QPos(0, pos), q_idx, w_idx, k_idx, k_bstride, topk_idx,
+                           scores_out, workspace, workspace_bytes, stream, page_table, max_pages, page_rows,
+                           n_pages, empty ? nullptr : &fc);
 }
 
 int csa_index_scores(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int64_t q_pos0, const void *q_idx,
@@ -557,7 +643,7 @@ static int index_topk_mx4_impl(int dt, int B, int Tq, int N, int H_I, int d_I, i
                                const uint8_t *k_scales, int64_t k_bstride, int32_t *topk_idx, float *scores_out,
                                void *workspace, size_t workspace_bytes, void *stream,
                                const int32_t *page_table = nullptr, int max_pages = 0, int page_rows = 0,
-                               int64_t n_pages = 0, const CompressJob *cj = nullptr) {
+                               int64_t n_pages = 0, const FusedCompress *fc = nullptr) {
     if (int s = check_dt(dt)) return s;
     if (B < 0 || Tq < 0 || N < 0) return fail(CSA_EINVAL, "B, Tq and N must be >= 0");
     if (H_I < 1 || H_I > 64) return fail(CSA_EUNSUPPORTED, "H_I=%d outside 1..64", H_I);
@@ -568,7 +654,7 @@ static int index_topk_mx4_impl(int dt, int B, int Tq, int N, int H_I, int d_I, i
         if (int s = check_qpos(q_pos0, B, Tq)) return s;
     if (N > csa::kTopkMaxEntries) return fail(CSA_EUNSUPPORTED, "N=%d above %lld entries", N, (long long)csa::kTopkMaxEntries);
     if ((int64_t)B * Tq == 0)
-        return cj ? hip_status(launch_compress_job(*cj, (hipStream_t)stream), "compress launch") : ok();
+        return fc ? hip_status(fc->launch(fc->job, (hipStream_t)stream, nullptr, 0), "compress launch") : ok();
     if (!q_idx || !w_idx || !topk_idx || (N > 0 && (!k_codes || !k_scales)))
         return fail(CSA_EINVAL, "NULL tensor pointer");
     csa::RowMap kmap(k_bstride);
@@ -601,13 +687,13 @@ static int index_topk_mx4_impl(int dt, int B, int Tq, int N, int H_I, int d_I, i
             return fail(CSA_EINVAL, "an output or the workspace overlaps an input");
     if (overlap(si, ss) || overlap(sw, si) || overlap(sw, ss))
         return fail(CSA_EINVAL, "outputs and workspace overlap");
-    if (int s = check_compress_against(cj, inputs, 4, si, ss, sw)) return s;
+    if (int s = check_compress_against(fc, inputs, 4, si, ss, sw)) return s;
     float *scores = (float *)workspace;
     uint32_t *scratch = (uint32_t *)((char *)workspace + scores_bytes(rows, N));
     hipStream_t st = (hipStream_t)stream;
     if (N > 0) {
         const int64_t cw = (int64_t)csa::topk_clear_words(rows, N);
-        if (int s = hip_status(cj ? launch_compress_job(*cj, st, scratch, cw) : csa::launch_fill_u32(scratch, cw, 0u, st),
+        if (int s = hip_status(fc ? fc->launch(fc->job, st, scratch, cw) : csa::launch_fill_u32(scratch, cw, 0u, st),
                                "histogram clear"))
             return s;
         if (int s = hip_status(csa::launch_index_mx4(dt, B, Tq, N, H_I, d_I, m, q_pos0, q_idx, w_idx, k_codes,
@@ -615,8 +701,8 @@ static int index_topk_mx4_impl(int dt, int B, int Tq, int N, int H_I, int d_I, i
                                                       scores_out, scratch, st),
                                "indexer launch"))
             return s;
-    } else if (cj) {
-        if (int s = hip_status(launch_compress_job(*cj, st), "compress launch")) return s;
+    } else if (fc) {
+        if (int s = hip_status(fc->launch(fc->job, st, nullptr, 0), "compress launch")) return s;
     }
     return hip_status(csa::launch_topk(B, Tq, N, m, k, q_pos0, scores, scratch, topk_idx, st), "top-k launch");
 }
@@ -640,9 +726,10 @@ int csa_compress_index_topk_mx4(int dt, int B, int G, int m, int d, const void *
     bool empty;
     if (int s = check_compress(c, &empty)) return s;
     if (q_pos0 < 0) return fail(CSA_EINVAL, "q_pos0 must be >= 0");
+    const FusedCompress fc = fused(c);
     return index_topk_mx4_impl(dt, B, Tq, N, H_I, d_I, m, k, csa::QPos(q_pos0), q_idx, w_idx, k_codes, k_scales,
                                k_bstride, topk_idx, scores_out, workspace, workspace_bytes, stream, nullptr, 0, 0,
-                               0, empty ? nullptr : &c);
+                               0, empty ? nullptr : &fc);
 }
 
 int csa_index_scores_mx4(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int64_t q_pos0, const void *q_idx,
@@ -680,6 +767,26 @@ int csa_ragged_index_topk_mx4(int dt, int B, int N, int H_I, int d_I, int m, int
     return index_topk_mx4_impl(dt, B, 1, N, H_I, d_I, m, k, csa::QPos(0, pos), q_idx, w_idx, k_codes, k_scales,
                                k_bstride, topk_idx, scores_out, workspace, workspace_bytes, stream, page_table,
                                max_pages, page_rows, n_pages);
+}
+
+int csa_ragged_compress_index_topk_mx4(int dt, int B, int m, int d, const int64_t *pos, const void *raw_ring,
+                                       int64_t ring_bstride, const float *logit_ring, int64_t logit_bstride,
+                                       int64_t ring, void *entries_out, int64_t out_bstride, int64_t out_rows,
+                                       const int32_t *e_page_table, int e_max_pages, int e_page_rows,
+                                       int64_t e_n_pages, int N, int H_I, int d_I, int k, const void *q_idx,
+                                       const float *w_idx, const uint8_t *k_codes, const uint8_t *k_scales,
+                                       int64_t k_bstride, const int32_t *page_table, int max_pages, int page_rows,
+                                       int64_t n_pages, int32_t *topk_idx, float *scores_out, void *workspace,
+                                       size_t workspace_bytes, void *stream) {
+    RaggedCompressJob c{dt, B, m, d, pos, raw_ring, ring_bstride, logit_ring, logit_bstride, ring, entries_out,
+                        out_bstride, out_rows, e_page_table, e_max_pages, e_page_rows, e_n_pages};
+    bool empty;
+    if (int s = check_ragged_compress(c, &empty)) return s;
+    if (B > 0 && !pos) return fail(CSA_EINVAL, "NULL pos");
+    const FusedCompress fc = fused(c);
+    return index_topk_mx4_impl(dt, B, 1, N, H_I, d_I, m, k, csa::QPos(0, pos), q_idx, w_idx, k_codes, k_scales,
+                               k_bstride, topk_idx, scores_out, workspace, workspace_bytes, stream, page_table,
+                               max_pages, page_rows, n_pages, empty ? nullptr : &fc);
 }
 
 size_t csa_mqa_workspace_bytes(int B, int Tq, int H, int d, int n_rows_max) {

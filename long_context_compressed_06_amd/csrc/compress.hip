@@ -86,6 +86,12 @@ __device__ __forceinline__ void clear_words(uint32_t *__restrict__ p, int64_t n,
     for (int64_t i = ((int64_t)blk * blockDim.x + threadIdx.x) * 4; i < n; i += (int64_t)nblk * blockDim.x * 4)
         *(u32x4 *)(p + i) = u32x4{0u, 0u, 0u, 0u};
 }
+// the clearing workgroups a launch of `threads`-thread workgroups appends: one
+// 16-byte store per thread per pass, at most 256 of them
+static int64_t clear_blocks(int64_t clr_words, int threads) {
+    const int64_t b = (clr_words / 4 + threads - 1) / threads;
+    return b < 256 ? b : 256;
+}
 
 template <typename T>
 __global__ __launch_bounds__(64) void k_compress_wave(int G, int m, int d, int slices, const T *__restrict__ raw,
@@ -161,7 +167,12 @@ __global__ __launch_bounds__(256) void k_compress_ragged(int m, int d, int tpr, 
                                                           const int64_t *__restrict__ pos, const T *__restrict__ raw,
                                                           int64_t raw_bs, const float *__restrict__ logits,
                                                           int64_t log_bs, int64_t ring, T *__restrict__ out,
-                                                          RowMap om, int64_t out_rows) {
+                                                          RowMap om, int64_t out_rows, int work_blocks,
+                                                          uint32_t *__restrict__ clr, int64_t clr_words) {
+    if ((int)blockIdx.x >= work_blocks) {  // (uniform per workgroup: before any barrier)
+        clear_words(clr, clr_words, (int)blockIdx.x - work_blocks, (int)gridDim.x - work_blocks);
+        return;
+    }
     const int sl = blockIdx.x % slices;
     const int64_t b = blockIdx.x / slices;
     const int64_t p = pos[b];
@@ -262,46 +273,43 @@ hipError_t launch_compress_t(int B, int G, int m, int d, const void *raw, int64_
     while (tpr > 1 && (256 / tpr) * kRowsPerThread < m) tpr /= 2;
     if ((256 / tpr) * kRowsPerThread < m) return hipErrorInvalidValue;
     const int slices = d / VEC / tpr;
-    // workgroups for the optional clear: one 16-byte store per thread per pass, at most 256 of them
-    auto clear_blocks = [&](int threads) -> int64_t {
-        const int64_t b = (clr_words / 4 + threads - 1) / threads;
-        return b < 256 ? b : 256;
-    };
     if (tpr == d / VEC && m <= 256 / tpr && m <= kWaveRows) {  // each row slot holds one row: the LDS-free form
         const int wslices = (d / VEC + 63) / 64;
         const int64_t work = (int64_t)B * G * wslices;
-        hipLaunchKernelGGL(k_compress_wave<T>, dim3((unsigned)(work + clear_blocks(64))), dim3(64), 0, st, G, m, d,
+        hipLaunchKernelGGL(k_compress_wave<T>, dim3((unsigned)(work + clear_blocks(clr_words, 64))), dim3(64), 0, st, G, m, d,
                            wslices, (const T *)raw, raw_bs, logits, log_bs, (T *)out, out_bs, (int)work, clr,
                            clr_words);
         return hipGetLastError();
     }
     const int64_t work = (int64_t)B * G * slices;
-    hipLaunchKernelGGL(k_compress<T>, dim3((unsigned)(work + clear_blocks(256))), dim3(256), 0, st, G, m, d, tpr,
+    hipLaunchKernelGGL(k_compress<T>, dim3((unsigned)(work + clear_blocks(clr_words, 256))), dim3(256), 0, st, G, m, d, tpr,
                        slices, (const T *)raw, raw_bs, logits, log_bs, (T *)out, out_bs, (int)work, clr, clr_words);
     return hipGetLastError();
 }
 template <typename T>
 hipError_t launch_compress_ragged_t(int B, int m, int d, const int64_t *pos, const void *raw, int64_t raw_bs,
                                     const float *logits, int64_t log_bs, int64_t ring, void *out, RowMap out_bs,
-                                    int64_t out_rows, hipStream_t st) {
+                                    int64_t out_rows, hipStream_t st, uint32_t *clr, int64_t clr_words) {
     constexpr int VEC = 16 / sizeof(T);
     int tpr = d / VEC;
     if (tpr > 256) return hipErrorInvalidValue;
     while (tpr > 1 && (256 / tpr) * kRowsPerThread < m) tpr /= 2;
     if ((256 / tpr) * kRowsPerThread < m) return hipErrorInvalidValue;
     const int slices = d / VEC / tpr;
-    hipLaunchKernelGGL(k_compress_ragged<T>, dim3((unsigned)((int64_t)B * slices)), dim3(256), 0, st, m, d, tpr,
-                       slices, pos, (const T *)raw, raw_bs, logits, log_bs, ring, (T *)out, out_bs, out_rows);
+    const int64_t work = (int64_t)B * slices;
+    hipLaunchKernelGGL(k_compress_ragged<T>, dim3((unsigned)(work + clear_blocks(clr_words, 256))), dim3(256), 0, st,
+                       m, d, tpr, slices, pos, (const T *)raw, raw_bs, logits, log_bs, ring, (T *)out, out_bs,
+                       out_rows, (int)work, clr, clr_words);
     return hipGetLastError();
 }
 hipError_t launch_compress_ragged(int dt, int B, int m, int d, const int64_t *pos, const void *raw, int64_t raw_bs,
                                   const float *logits, int64_t log_bs, int64_t ring, void *out, RowMap out_bs,
-                                  int64_t out_rows, hipStream_t st) {
+                                  int64_t out_rows, hipStream_t st, uint32_t *clr, int64_t clr_words) {
     if (dt == 0)
         return launch_compress_ragged_t<float>(B, m, d, pos, raw, raw_bs, logits, log_bs, ring, out, out_bs,
-                                               out_rows, st);
+                                               out_rows, st, clr, clr_words);
     return launch_compress_ragged_t<bf16_t>(B, m, d, pos, raw, raw_bs, logits, log_bs, ring, out, out_bs, out_rows,
-                                            st);
+                                            st, clr, clr_words);
 }
 
 template <typename T>

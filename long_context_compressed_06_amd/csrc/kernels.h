@@ -33,9 +33,9 @@ TopkPlan topk_plan(int64_t rows, int64_t N);
 size_t topk_scratch_bytes(int64_t rows, int64_t N);
 size_t topk_clear_words(int64_t rows, int64_t N);
 
-// clr / clr_words (optional): words also zeroed by the same launch (clr_words
-// a multiple of 4, clr 16-byte aligned), e.g. the top-k histograms of the
-// index call that follows
+// clr / clr_words (optional, here and in launch_compress_ragged): words also
+// zeroed by the same launch (clr_words a multiple of 4, clr 16-byte aligned),
+// e.g. the top-k histograms of the index call that follows
 hipError_t launch_compress(int dt, int B, int G, int m, int d, const void *raw, int64_t raw_bs,
                            const float *logits, int64_t log_bs, void *out, int64_t out_bs, hipStream_t st,
                            uint32_t *clr = nullptr, int64_t clr_words = 0);
@@ -43,7 +43,7 @@ hipError_t launch_compress(int dt, int B, int G, int m, int d, const void *raw, 
 // mirrored raw / logit rings of `ring` positions, into entry row (pos[b]+1)/m - 1 when below out_rows
 hipError_t launch_compress_ragged(int dt, int B, int m, int d, const int64_t *pos, const void *raw, int64_t raw_bs,
                                   const float *logits, int64_t log_bs, int64_t ring, void *out, RowMap out_map,
-                                  int64_t out_rows, hipStream_t st);
+                                  int64_t out_rows, hipStream_t st, uint32_t *clr = nullptr, int64_t clr_words = 0);
 // logits: [B][G*m][d] f32 (per channel), batch stride log_bs elements
 hipError_t launch_compress_channels(int dt, int B, int G, int m, int d, const void *raw, int64_t raw_bs,
                                     const float *logits, int64_t log_bs, void *out, int64_t out_bs,

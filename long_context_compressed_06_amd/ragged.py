@@ -15,7 +15,9 @@ A step (new token of sequence b at position t_b = pos[b]):
      completing token's key is kept, quantised first when the indexer runs
      on FP4);
   2. ragged compression: those sequences' groups pooled out of the rings;
-  3. ragged index + top-k (CSA) over each sequence's visible entries;
+  3. ragged index + top-k (CSA) over each sequence's visible entries (2 and
+     3 in one call, the compression sharing a launch with the selection's
+     histogram clear);
   4. ragged attention (selected or all visible entries, window from the ring);
   5. pos += 1.
 Ring of R = max(W, m) positions: the window of the newest token and the
@@ -34,8 +36,9 @@ from __future__ import annotations
 import torch
 
 from . import (csa_append_rows, csa_append_rows_multi, csa_mx4_quantize, csa_positions_advance,
-               csa_ragged_compress, csa_ragged_index_topk, csa_ragged_index_topk_mx4, csa_ragged_sparse_mqa,
-               hca_ragged_dense_mqa, index_topk_workspace_bytes, mqa_workspace_bytes)
+               csa_ragged_compress, csa_ragged_compress_index_topk, csa_ragged_compress_index_topk_mx4,
+               csa_ragged_index_topk, csa_ragged_index_topk_mx4, csa_ragged_sparse_mqa, hca_ragged_dense_mqa,
+               index_topk_workspace_bytes, mqa_workspace_bytes)
 
 
 class RaggedLayer:
@@ -144,15 +147,26 @@ class RaggedLayer:
             else:
                 jobs.append((k_idx_tok, self.k_idx, 0, 0, self.pos, self.m, pg))
         csa_append_rows_multi(jobs)
-        csa_ragged_compress(self.raw_ring, self.logit_ring[..., 0], self.R, self.m, self.pos, self.entries,
-                            pages=self.pages)
+        # the group the token completes (if any), pooled out of the rings: in the index call's first launch
+        # when the index operands share the rings' element type (CSA), else on its own
+        comp = (self.raw_ring, self.logit_ring[..., 0], self.R, self.m, self.pos, self.entries)
+        fuse = self.mode == "csa" and q_idx.dtype == self.raw_ring.dtype
+        if not fuse:
+            csa_ragged_compress(*comp, pages=self.pages)
         if self.mode == "csa":
+            ix = dict(topk_idx=self.topk_idx, workspace=self.idx_ws, pages=self.pages)
             if self.index_fmt == "mx4":
-                csa_ragged_index_topk_mx4(q_idx, w_idx, self.k_codes, self.k_scales, self.cap_e, self.m, self.k,
-                                          self.pos, topk_idx=self.topk_idx, workspace=self.idx_ws, pages=self.pages)
+                keys = (q_idx, w_idx, self.k_codes, self.k_scales, self.cap_e)
+                if fuse:
+                    csa_ragged_compress_index_topk_mx4(*comp, *keys, self.k, entry_pages=self.pages, **ix)
+                else:
+                    csa_ragged_index_topk_mx4(*keys, self.m, self.k, self.pos, **ix)
             else:
-                csa_ragged_index_topk(q_idx, w_idx, self.k_idx, self.cap_e, self.m, self.k, self.pos,
-                                      topk_idx=self.topk_idx, workspace=self.idx_ws, pages=self.pages)
+                keys = (q_idx, w_idx, self.k_idx, self.cap_e)
+                if fuse:
+                    csa_ragged_compress_index_topk(*comp, *keys, self.k, entry_pages=self.pages, **ix)
+                else:
+                    csa_ragged_index_topk(*keys, self.m, self.k, self.pos, **ix)
             csa_ragged_sparse_mqa(q, self.entries, self.topk_idx, self.raw_ring, self.R, self.cap_e, self.m, self.W,
                                   self.pos, scale=self.scale, out=self.out, lse=self.lse, workspace=self.mqa_ws,
                                   pages=self.pages)

@@ -65,6 +65,9 @@ class AttentionStep:
         if self.N > self.g0:
             r0 = self.g0 * self.m - self.raw_pos0
             comp = (raw[:, r0:r0 + (self.N - self.g0) * self.m], x["logits"], self.m, entries[:, self.g0:self.N])
+            if self.mode != "csa" or x["q_idx"].dtype != raw.dtype:  # (one element type per fused call)
+                csa_compress(*comp)
+                comp = ()
         if self.mode == "csa" and self.index_fmt == "mx4":
             args = (x["q_idx"], x["w_idx"], x["k_codes"], x["k_scales"], self.N)
             if comp:
@@ -79,8 +82,6 @@ class AttentionStep:
                                         workspace=self.idx_ws)
             else:
                 csa_index_topk(*args, self.m, self.k, self.q_pos0, topk_idx=self.topk_idx, workspace=self.idx_ws)
-        elif comp:
-            csa_compress(*comp)
         if self.mode == "csa":
             csa_sparse_mqa(x["q"], entries, self.topk_idx, raw, self.N, self.m, self.W, self.q_pos0, self.raw_pos0,
                            scale=self.scale, out=self.out, lse=self.lse, workspace=self.mqa_ws)

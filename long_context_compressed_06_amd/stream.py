@@ -40,7 +40,8 @@ import dataclasses
 
 import torch
 
-from . import (csa_append_rows_multi, csa_compress, csa_compress_channels, csa_index_topk, csa_index_topk_mx4,
+from . import (csa_append_rows_multi, csa_compress, csa_compress_channels, csa_compress_index_topk,
+               csa_compress_index_topk_mx4, csa_index_topk, csa_index_topk_mx4,
                csa_mx4_quantize, csa_sparse_mqa, hca_dense_mqa, index_topk_workspace_bytes, mqa_workspace_bytes)
 
 
@@ -171,11 +172,17 @@ class StreamingLayer:
             if self.pool == "channel":
                 jobs.append((k_idx_logits, self.kidx_logit_ring, p.p0, self.R))
         csa_append_rows_multi(jobs)
-        # 2. the groups completing in this chunk
+        # 2. the groups completing in this chunk (pooled by token logits in a CSA layer: inside the index
+        # call, whose first launch then also clears the selection's histograms)
+        comp = ()
         if p.g_new > 0:
             L = p.g_new * self.m
-            self._pool(self._ring_view(self.raw_ring, p.comp_lo, L), self._ring_view(self.logit_ring, p.comp_lo, L),
-                       self.entries[:, p.g0:p.g0 + p.g_new])
+            args = (self._ring_view(self.raw_ring, p.comp_lo, L), self._ring_view(self.logit_ring, p.comp_lo, L),
+                    self.entries[:, p.g0:p.g0 + p.g_new])
+            if self.mode == "csa" and self.pool != "channel" and q_idx.dtype == raw.dtype:
+                comp = (args[0], args[1][..., 0], self.m, args[2])
+            else:
+                self._pool(*args)
         N = p.g0 + p.g_new
         raw_win = self._ring_view(self.raw_ring, p.win_lo, p.win_len)
         if out is None:
@@ -200,9 +207,15 @@ class StreamingLayer:
             # 4. indexer + top-k
             if topk_idx is None:
                 topk_idx = torch.empty((B, n, self.k), dtype=torch.int32, device=raw.device)
-            if self.index_fmt == "mx4":
+            if self.index_fmt == "mx4" and comp:
+                csa_compress_index_topk_mx4(*comp, q_idx, w_idx, self.k_codes, self.k_scales, N, self.k, p.p0,
+                                            topk_idx=topk_idx, workspace=self.idx_ws)
+            elif self.index_fmt == "mx4":
                 csa_index_topk_mx4(q_idx, w_idx, self.k_codes, self.k_scales, N, self.m, self.k, p.p0,
                                    topk_idx=topk_idx, workspace=self.idx_ws)
+            elif comp:
+                csa_compress_index_topk(*comp, q_idx, w_idx, self.k_idx, N, self.k, p.p0, topk_idx=topk_idx,
+                                        workspace=self.idx_ws)
             else:
                 csa_index_topk(q_idx, w_idx, self.k_idx, N, self.m, self.k, p.p0, topk_idx=topk_idx,
                                workspace=self.idx_ws)

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
     import long_context_compressed_06_amd as csa
 
     names = header_functions()
-    assert len(names) == 26, names
+    assert len(names) == 28, names
     for n in names:
         assert hasattr(L, n), n
     assert sorted(csa.EXPORTS) == names
@@ -334,6 +334,35 @@ def test_ragged_calls_reject_bad_arguments(L):
     assert rm(ring=0) == -1
     assert rm(W=129) == -1                    # the ring cannot hold the window
     assert rm(pt=P + 0x5000000, mp=8, pr=64, npg=40) == -1   # 512 rows do not cover N = 1000
+
+
+@pytest.mark.parametrize("mx4", [False, True])
+def test_ragged_compress_index_topk_validation(L, mx4):
+    """The ragged fused call keeps both calls' checks and refuses overlaps between the compression and the
+    index operands, outputs and workspace."""
+    import long_context_compressed_06_amd as csa
+
+    ws = csa.index_topk_workspace_bytes(2, 1, 256, 64, 64)
+
+    def rf(B=2, m=4, pos=P, raw=P + 0x1000000, lg=P + 0x1100000, ent=P + 0x1200000, k=64, wsb=ws):
+        c = (1, B, m, 128, pos, raw, 2 * 16 * 128, lg, 32, 16, ent, 64 * 128, 64, None, 0, 0, 0)
+        if mx4:
+            return L.csa_ragged_compress_index_topk_mx4(*c, 256, 64, 128, k, P + 0x10000, P + 0x40000, P + 0x80000,
+                                                        P + 0xC0000, 256, None, 0, 0, 0, P + 0x200000, None,
+                                                        P + 0x300000, wsb, None)
+        return L.csa_ragged_compress_index_topk(*c, 256, 64, 128, k, P + 0x10000, P + 0x40000, P + 0x80000,
+                                                256 * 128, None, 0, 0, 0, P + 0x200000, None, P + 0x300000, wsb, None)
+
+    assert rf(m=0) == -6
+    assert rf(pos=None) == -1 and rf(pos=P + 4) == -3
+    assert rf(k=0) == -6 and rf(wsb=ws - 1) == -4
+    assert rf(ent=P + 0x10000) == -1             # entries overlap q_idx
+    assert b"index input" in L.csa_last_error_detail()
+    assert rf(ent=P + 0x200000) == -1            # ... the selection output
+    assert rf(ent=P + 0x300000) == -1            # ... the workspace
+    assert rf(raw=P + 0x300000) == -1            # the raw ring inside the workspace
+    assert b"workspace" in L.csa_last_error_detail()
+    assert rf(B=0, pos=None) == 0
 
 
 def test_stream_read_rejects_bad_arguments(L):

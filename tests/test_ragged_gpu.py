@@ -327,3 +327,45 @@ def test_ragged_paged_equals_contiguous(csa, c):
         if c.mode == "csa" and c.index_fmt == "elem":
             got = torch.cat([v for v, _, _ in paged._cache_rows(paged.k_idx, b, n)])
             assert torch.equal(got, flat.k_idx[b, :n])
+
+
+CSA_CASES = [c for c in CASES if c.mode == "csa"]
+
+
+@pytest.mark.parametrize("c", CSA_CASES, ids=[c.name for c in CSA_CASES])
+def test_ragged_fused_equals_separate_calls(csa, c, monkeypatch):
+    """The layer's fused compression + index call gives what csa_ragged_compress then the ragged index call
+    give, bit for bit: outputs, selections and every cache row, step after step (groups completing at
+    different steps in different sequences), contiguous and paged."""
+    import long_context_compressed_06_amd.ragged as rg
+
+    say(c, "fused vs separate")
+    seqs, new = draw(c)
+    fused, sep = make_layer(csa, c, seqs), make_layer(csa, c, seqs)
+
+    def sep_elem(raw_ring, logit_ring, ring, m, pos, ent, q_idx, w_idx, k_idx, N, k, topk_idx=None, workspace=None,
+                 entry_pages=None, pages=None):
+        csa.csa_ragged_compress(raw_ring, logit_ring, ring, m, pos, ent, pages=entry_pages)
+        csa.csa_ragged_index_topk(q_idx, w_idx, k_idx, N, m, k, pos, topk_idx=topk_idx, workspace=workspace,
+                                  pages=pages)
+
+    def sep_mx4(raw_ring, logit_ring, ring, m, pos, ent, q_idx, w_idx, kc, ks, N, k, topk_idx=None, workspace=None,
+                entry_pages=None, pages=None):
+        csa.csa_ragged_compress(raw_ring, logit_ring, ring, m, pos, ent, pages=entry_pages)
+        csa.csa_ragged_index_topk_mx4(q_idx, w_idx, kc, ks, N, m, k, pos, topk_idx=topk_idx, workspace=workspace,
+                                      pages=pages)
+
+    for j in range(c.steps):
+        x = step_inputs(c, new, j)
+        fused.step(**x)
+        with monkeypatch.context() as mp:
+            mp.setattr(rg, "csa_ragged_compress_index_topk", sep_elem)
+            mp.setattr(rg, "csa_ragged_compress_index_topk_mx4", sep_mx4)
+            sep.step(**x)
+        torch.cuda.synchronize()
+        assert torch.equal(fused.out, sep.out) and torch.equal(fused.lse, sep.lse), j
+        assert torch.equal(fused.topk_idx, sep.topk_idx), j
+    for b, p in enumerate(c.positions):
+        n = (p + c.steps) // c.m
+        for (u, _, _), (v, _, _) in zip(fused._cache_rows(fused.entries, b, n), sep._cache_rows(sep.entries, b, n)):
+            assert torch.equal(u, v), b
