@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void k_index_scores(int Tq, int N, int HI, int
                 if (srow2) srow2[j] = j < nv ? s : -INFINITY;
             }
             if (hist && g == 0 && j < j_hi && j < nv)
-                atomicAdd(&whist[wv][order_key(s) >> (32 - kTopkBinBits)], 1u);
+                atomicAdd(&whist[wv][topk_bin(order_key(s))], 1u);
         }
     };
     // double-buffered: the next batch is in flight while this one is scored
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_dma(int Tq, int N, int
             const float v = j < nv ? sc : -INFINITY;
             srow[j] = v;
             if (srow2) srow2[j] = v;
-            if (hist && j < nv) atomicAdd(&bh[order_key(sc) >> (32 - kTopkBinBits)], 1u);
+            if (hist && j < nv) atomicAdd(&bh[topk_bin(order_key(sc))], 1u);
         }
     }
     // tiles with no visible entry
@@ -587,7 +587,7 @@ __global__ __launch_bounds__(kPreWaves * 64) void k_index_prefill(int Tq, int N,
                 const float v = j < nv ? sc : -INFINITY;
                 srow[j] = v;
                 if (srow2) srow2[j] = v;
-                if (hist && j < nv) atomicAdd(&qh[wv * kTopkBins + (order_key(sc) >> (32 - kTopkBinBits))], 1u);
+                if (hist && j < nv) atomicAdd(&qh[wv * kTopkBins + topk_bin(order_key(sc))], 1u);
             }
         }
     }

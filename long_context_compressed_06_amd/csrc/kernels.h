@@ -8,10 +8,20 @@
 
 namespace csa {
 
-// first radix digit of the top-k select: the top 11 bits of the score key,
-// counted per query by the indexer epilogue
+// first radix digit of the top-k select, counted per query by the indexer
+// epilogue: the top 13 bits of the score key (sign, exponent, four mantissa
+// bits, so 16 bins per binade) offset into a window of kTopkBins values that
+// holds the binades 2^-63 .. 2^64 of non-negative scores; every key below the
+// window counts in bin 0, every key above it in the last bin.  An interior
+// bin is one 13-bit key prefix; the two end bins are not.
 constexpr int kTopkBinBits = 11;
 constexpr int kTopkBins = 1 << kTopkBinBits;
+constexpr int kTopkKeyShift = 19;                            // key bits below the 13-bit prefix
+constexpr uint32_t kTopkWindow0 = (1u << 12) + (64u << 4);   // the prefix at bin 0's upper edge
+__device__ __forceinline__ uint32_t topk_bin(uint32_t key) {
+    const uint32_t t = key >> kTopkKeyShift;
+    return t <= kTopkWindow0 ? 0u : min(t - kTopkWindow0, (uint32_t)(kTopkBins - 1));
+}
 // decode (few queries) top-k: scores per filter workgroup, (index, key)
 // pairs the final workgroup gathers into LDS, and the longest row accepted
 constexpr int kTopkFilterChunk = 4096;

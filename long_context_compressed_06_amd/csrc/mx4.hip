@@ -231,7 +231,7 @@ __global__ __launch_bounds__(256) void k_index_mx4(int Tq, int N, int HI, int m,
                 srow[j] = j < nv ? s : -INFINITY;
                 if (srow2) srow2[j] = j < nv ? s : -INFINITY;
             }
-            if (hist && j < j_hi && j < nv) atomicAdd(&whist[wv][order_key(s) >> (32 - kTopkBinBits)], 1u);
+            if (hist && j < j_hi && j < nv) atomicAdd(&whist[wv][topk_bin(order_key(s))], 1u);
         };
         // double-buffered: the next batch is in flight while this one is scored
         u32x4 d0[UNROLL], d1[UNROLL];
@@ -430,7 +430,7 @@ __global__ __launch_bounds__(kMx4Waves * 64) void k_index_mx4_dma(int Tq, int N,
             const float v = j < nv ? sc : -INFINITY;
             srow[j] = v;
             if (srow2) srow2[j] = v;
-            if (hist && j < nv) atomicAdd(&bh[order_key(sc) >> (32 - kTopkBinBits)], 1u);
+            if (hist && j < nv) atomicAdd(&bh[topk_bin(order_key(sc))], 1u);
         }
     }
     // tiles with no visible entry
@@ -658,7 +658,7 @@ __global__ __launch_bounds__(kPmWaves * 64) void k_index_prefill_mx4(int Tq, int
                 const float v = j < nv ? sc : -INFINITY;
                 srow[j] = v;
                 if (srow2) srow2[j] = v;
-                if (hist && j < nv) atomicAdd(&qh[wv * kTopkBins + (order_key(sc) >> (32 - kTopkBinBits))], 1u);
+                if (hist && j < nv) atomicAdd(&qh[wv * kTopkBins + topk_bin(order_key(sc))], 1u);
             }
         }
     }

@@ -5,11 +5,13 @@
 // unique even with equal scores.  Output: kept indices ascending, -1 padded.
 //
 // Method: exact radix select on order-preserving 32-bit keys.  The first
-// digit (top 11 bits) is counted by the indexer epilogue into a per-query
-// histogram, so no workgroup here rescans a row for it.  From the histogram
-// the digit D holding the k-th key follows; keys with a higher digit are kept,
-// keys with digit D are the candidates, resolved by two more digits (11 and
-// 10 bits, LDS histograms) and, for keys that are fully equal, by index.
+// digit (topk_bin: the key's top 13 bits in a window of 2048 bins, keys
+// outside the window in the two end bins) is counted by the indexer epilogue
+// into a per-query histogram, so no workgroup here rescans a row for it.
+// From the histogram the digit D holding the k-th key follows; keys with a
+// higher digit are kept, keys with digit D are the candidates, resolved by
+// more digits in LDS histograms (the key's remaining 19 bits for an interior
+// bin, all 32 for an end bin) and, for keys that are fully equal, by index.
 //
 // Many queries with rows of up to kTopkCompactMax scores (prefill chunks):
 // one workgroup per query holds its row in registers, packs the pairs of digit
@@ -60,18 +62,20 @@ struct Digit {
 // Find D with count(bin > D) < rem <= count(bin >= D) over nbins bins.
 template <int NT>
 __device__ Digit find_digit(const uint32_t *hist, int nbins, int rem, int *sh, Digit *shd) {
-    const int per = nbins / NT;
+    const int per = nbins >= NT ? nbins / NT : 1;  // bins per thread (threads past nbins hold none)
     const int tid = threadIdx.x;
+    const bool holds = tid * per < nbins;
     // (a histogram holding fewer than rem keys has no such digit: then digit 0
     // with nothing above it, so the selection stays inside the row and k)
     if (tid == 0) *shd = Digit{0u, 0, 0};
     int own = 0;
-    for (int q = 0; q < per; ++q) own += (int)hist[tid * per + q];
+    if (holds)
+        for (int q = 0; q < per; ++q) own += (int)hist[tid * per + q];
     int total;
     const int before = block_excl_scan<NT>(own, sh, &total);
     const int incl = total - before;  // keys in bins >= tid*per
     const int excl = incl - own;      // keys in bins >= (tid+1)*per
-    if (excl < rem && incl >= rem) {
+    if (holds && excl < rem && incl >= rem) {
         int above = excl;
         for (int q = per - 1; q >= 0; --q) {
             const int h = (int)hist[tid * per + q];
@@ -90,27 +94,53 @@ __device__ Digit find_digit(const uint32_t *hist, int nbins, int rem, int *sh, D
     return d;
 }
 
-// Narrow the selection among keys matching (prefix, mask) down to one full
-// key value with radix digits at bits [20:10] and [9:0].  On return, keys
-// with (key & mask) > prefix are kept, and `rem` of those equal to prefix.
+// The selection below the first digit D (the bin of the k-th key): keys of
+// a higher bin are kept outright; keys of bin D compare (key & mask) with
+// prefix, which the refinement extends digit by digit, and `rem` of those
+// equal to it are kept.  An interior bin is one 13-bit key prefix, so its
+// keys go on with bits [18:8] and [7:0]; an end bin gathers keys of many
+// prefixes and starts again from the top: bits [31:21], [20:10], [9:0].
+struct Sel {
+    uint32_t D, prefix, mask;
+    int rem;
+    __device__ static Sel start(const Digit &d, int k) {
+        Sel s;
+        const bool interior = d.digit > 0u && d.digit < (uint32_t)(kTopkBins - 1);
+        s.D = d.digit;
+        s.prefix = interior ? (d.digit + kTopkWindow0) << kTopkKeyShift : 0u;
+        s.mask = interior ? ~0u << kTopkKeyShift : 0u;
+        s.rem = k - d.above;
+        return s;
+    }
+    // 1: kept outright; 0: in bin D and equal to the prefix so far; -1: not kept
+    __device__ __forceinline__ int cmp(uint32_t key) const {
+        const uint32_t b = topk_bin(key);
+        if (b != D) return b > D ? 1 : -1;
+        const uint32_t km = key & mask;
+        return km > prefix ? 1 : (km == prefix ? 0 : -1);
+    }
+};
+
+// Narrow bin D down to one full key value (keys key_at(0 .. n-1)).
 template <int NT, class KeyAt>
-__device__ void refine(KeyAt key_at, int64_t n, uint32_t &prefix, uint32_t &mask, int &rem, uint32_t *hist, int *sh,
-                       Digit *shd) {
-    for (int pass = 1; pass < 3; ++pass) {
-        const int shift = pass == 1 ? 10 : 0;
-        const int nbins = pass == 1 ? 2048 : 1024;
-        for (int i = threadIdx.x; i < 2048; i += NT) hist[i] = 0;
+__device__ void refine(KeyAt key_at, int64_t n, Sel &s, uint32_t *hist, int *sh, Digit *shd) {
+    const bool interior = s.mask != 0u;
+    const int passes = interior ? 2 : 3;
+    for (int pass = 0; pass < passes; ++pass) {
+        const int shift = interior ? (pass == 0 ? 8 : 0) : (pass == 0 ? 21 : pass == 1 ? 10 : 0);
+        const int nbins = interior ? (pass == 0 ? 2048 : 256) : (pass < 2 ? 2048 : 1024);
+        for (int i = threadIdx.x; i < nbins; i += NT) hist[i] = 0;
         __syncthreads();
         for (int64_t j = threadIdx.x; j < n; j += NT) {
             const uint32_t key = key_at(j);
-            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & (nbins - 1)], 1u);
+            if (s.cmp(key) == 0) atomicAdd(&hist[(key >> shift) & (nbins - 1)], 1u);
         }
         __syncthreads();
-        const Digit d = find_digit<NT>(hist, nbins, rem, sh, shd);
-        rem -= d.above;
-        prefix |= d.digit << shift;
-        mask |= (uint32_t)(nbins - 1) << shift;
-        if (d.at == rem) break;  // every key equal to the prefix is kept
+        const Digit d = find_digit<NT>(hist, nbins, s.rem, sh, shd);
+        s.rem -= d.above;
+        s.prefix |= d.digit << shift;
+        s.mask |= (uint32_t)(nbins - 1) << shift;
+        if (d.at == s.rem) break;  // every key equal to the prefix is kept
     }
 }
 
@@ -125,7 +155,8 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 // one exchange of the per-wave totals gives each run its starting position,
 // and a second pass places the items with ballots.  sh: 2*NT/64 ints.
 template <int NT, class KeyAt, class Emit>
-__device__ void ordered_keep(KeyAt key_at, int64_t n, uint32_t prefix, uint32_t mask, int rem, int *sh, Emit emit) {
+__device__ void ordered_keep(KeyAt key_at, int64_t n, const Sel &s, int *sh, Emit emit) {
+    const int rem = s.rem;
     constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int64_t per = ((n + NW - 1) / NW + 63) / 64 * 64;
@@ -133,9 +164,9 @@ __device__ void ordered_keep(KeyAt key_at, int64_t n, uint32_t prefix, uint32_t 
     int gt = 0, eq = 0;
     for (int64_t c = s0; c < s1; c += 64) {
         const int64_t i = c + lane;
-        const uint32_t km = i < s1 ? key_at(i) & mask : 0u;
-        gt += __popcll(__ballot(i < s1 && km > prefix));
-        eq += __popcll(__ballot(i < s1 && km == prefix));
+        const int cv = i < s1 ? s.cmp(key_at(i)) : -1;
+        gt += __popcll(__ballot(cv == 1));
+        eq += __popcll(__ballot(cv == 0));
     }
     if (lane == 0) {
         sh[wv] = gt;
@@ -152,10 +183,10 @@ __device__ void ordered_keep(KeyAt key_at, int64_t n, uint32_t prefix, uint32_t 
     int pos = gt_b + min(eq_b, rem);
     for (int64_t c = s0; c < s1; c += 64) {
         const int64_t i = c + lane;
-        const uint32_t km = i < s1 ? key_at(i) & mask : 0u;
-        const bool e = i < s1 && km == prefix;
+        const int cv = i < s1 ? s.cmp(key_at(i)) : -1;
+        const bool e = cv == 0;
         const uint64_t em = __ballot(e);
-        const bool sel = (i < s1 && km > prefix) || (e && eq_b + lanes_below(em) < rem);
+        const bool sel = cv == 1 || (e && eq_b + lanes_below(em) < rem);
         const uint64_t sm = __ballot(sel);
         if (sel) emit(pos + lanes_below(sm), i);
         pos += __popcll(sm);
@@ -187,11 +218,10 @@ struct IdxKey {
 // the pairs of digit >= D do not fit in LDS).
 __device__ void select_row_global(const float *srow, int64_t nv, int k, Digit d, int32_t *orow, uint32_t *hist,
                                   int *sh, Digit *shd) {
-    uint32_t prefix = d.digit << (32 - kTopkBinBits), mask = ~0u << (32 - kTopkBinBits);
-    int rem = k - d.above;
+    Sel s = Sel::start(d, k);
     auto key_at = [&](int64_t j) -> uint32_t { return order_key(srow[j]); };
-    if (d.at != rem) refine<kNT>(key_at, nv, prefix, mask, rem, hist, sh, shd);
-    ordered_keep<kNT>(key_at, nv, prefix, mask, rem, sh, [&](int pos, int64_t j) {
+    if (d.at != s.rem) refine<kNT>(key_at, nv, s, hist, sh, shd);
+    ordered_keep<kNT>(key_at, nv, s, sh, [&](int pos, int64_t j) {
         if (pos >= 0 && pos < k) orow[pos] = (int32_t)j;
     });
 }
@@ -200,11 +230,10 @@ __device__ void select_row_global(const float *srow, int64_t nv, int k, Digit d,
 // the lower digits and write the kept indices, ascending.
 __device__ void select_items(const IdxKey *items, int M, int k, Digit d, int32_t *orow, uint32_t *hist, int *sh,
                              Digit *shd) {
-    uint32_t prefix = d.digit << (32 - kTopkBinBits), mask = ~0u << (32 - kTopkBinBits);
-    int rem = k - d.above;  // keys of digit D to keep
+    Sel s = Sel::start(d, k);  // keys of digit D to keep: s.rem
     auto key_at = [&](int64_t i) -> uint32_t { return items[i].key; };
-    if (d.at != rem) refine<kNT>(key_at, M, prefix, mask, rem, hist, sh, shd);
-    ordered_keep<kNT>(key_at, M, prefix, mask, rem, sh, [&](int pos, int64_t i) {
+    if (d.at != s.rem) refine<kNT>(key_at, M, s, hist, sh, shd);
+    ordered_keep<kNT>(key_at, M, s, sh, [&](int pos, int64_t i) {
         if (pos >= 0 && pos < k) orow[pos] = items[i].j;
     });
 }
@@ -245,7 +274,7 @@ __global__ __launch_bounds__(kNT) void k_topk_compact(int Tq, int N, int m, int 
     auto selected = [&](int c, int e, uint32_t &key) -> bool {
         const float4 v = sc[c];
         key = order_key(e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w);
-        return s0 + c * 256 + lane * 4 + e < s1 && (key >> (32 - kTopkBinBits)) >= d.digit;
+        return s0 + c * 256 + lane * 4 + e < s1 && topk_bin(key) >= d.digit;
     };
     int cnt = 0;
 #pragma unroll
@@ -334,7 +363,7 @@ __global__ __launch_bounds__(kFT) void k_topk_filter(int Tq, int N, int m, int k
     }
 #pragma unroll
     for (int u = 0; u < kFPT; ++u)
-        bits |= (uint32_t)(j0 + u < nv && (keys[u] >> (32 - kTopkBinBits)) >= d.digit) << u;
+        bits |= (uint32_t)(j0 + u < nv && topk_bin(keys[u]) >= d.digit) << u;
     int total;
     int pos = block_excl_scan<kFT>(__popc(bits), sh, &total);
     IdxKey *sg = seg + (row * nblk + blk) * (int64_t)kTopkFilterChunk;

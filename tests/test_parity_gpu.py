@@ -366,3 +366,38 @@ def test_compress_index_topk_fused_bit_identical(csa, case):
         assert torch.equal(ia, ib), rep
         assert torch.equal(sa.view(torch.int32), sb.view(torch.int32)), rep
     assert not torch.isnan(ea.float()).any()
+
+
+# ------------------------------------------ top-k first digit: window and end bins
+EDGE_CASES = [("elem", 4), ("elem", 256), ("mx4", 4), ("mx4", 256)]
+
+
+@pytest.mark.parametrize("fmt,tq", EDGE_CASES, ids=[f"{f}-tq{t}" for f, t in EDGE_CASES])
+def test_topk_scores_beyond_the_digit_window(csa, fmt, tq):
+    """The first radix digit resolves 16 bins per binade inside a window of non-negative scores and
+    gathers every score below it (negative, zero, tiny) or above it (huge) in its two end bins,
+    whose keys are resolved from the top bit again.  Query rows cycle through four regimes of head
+    weights: huge of both signs (the k-th score in the upper end bin), all negative and tiny (the
+    lower end bin), and ordinary (an interior bin).  Rule T against the oracle, few-query and
+    query-blocked paths, bf16 and FP4 index operands."""
+    N = 6000
+    wl = Workload("edges", "bf16", B=1, T=4 * N, Tq=tq, m=4, d=128, H=8, W=4, k=500, HI=16, dI=128,
+                  seed_base=78000 + tq, index_fmt=fmt)
+    say(wl)
+    g = torch.Generator(device="cuda").manual_seed(78011 + tq)
+    x = make_inputs(wl, "cuda")
+    w = torch.rand(x["w_idx"].shape, generator=g, device="cuda")
+    regime = torch.arange(tq, device="cuda") % 4
+    scale = torch.tensor([2.0 ** 80, -1.0, 2.0 ** -90, 1.0], device="cuda")[regime].view(1, tq, 1)
+    sign = torch.where((regime == 0).view(1, tq, 1), torch.sign(torch.rand(w.shape, generator=g, device="cuda") - 0.5),
+                       torch.ones_like(w))
+    x["w_idx"] = (w * scale * sign).contiguous()
+    if fmt == "mx4":
+        csa.AttentionStep.quantize_index_keys(x)
+    xh = host_inputs(x)
+    step = csa.AttentionStep.for_workload(wl)
+    step(x)
+    torch.cuda.synchronize()
+    ref = oracle_step(wl, xh)
+    swapped = check_topk(to_np(step.topk_idx), ref["idx"], ref["scores"], nvis_rows(wl), wl.k, "topk")
+    say(f"rows with a legal near-tie swap: {swapped} of {tq}")
