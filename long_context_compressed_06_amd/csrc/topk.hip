@@ -53,6 +53,12 @@ __device__ __forceinline__ int block_excl_scan(int v, int *sh, int *total) {
     return before + x - v;
 }
 
+// the least key of first-digit bin b: topk_bin(key) >= b exactly when
+// key >= topk_bin_floor(b)
+__device__ __forceinline__ uint32_t topk_bin_floor(uint32_t b) {
+    return b == 0u ? 0u : (b + kTopkWindow0) << kTopkKeyShift;
+}
+
 struct Digit {
     uint32_t digit;
     int above;  // keys in higher bins
@@ -271,10 +277,11 @@ __global__ __launch_bounds__(kNT) void k_topk_compact(int Tq, int N, int m, int 
 #pragma unroll
     for (int c = 0; c < F4; ++c) sc[c] = *(const float4 *)(srow + min(s0 + c * 256 + lane * 4, stride - 4));
     const Digit d = find_digit<kNT>(ghist + row * kTopkBins, kTopkBins, k, sh, &shd);
+    const uint32_t kmin = topk_bin_floor(d.digit);  // keys of digit >= D
     auto selected = [&](int c, int e, uint32_t &key) -> bool {
         const float4 v = sc[c];
         key = order_key(e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w);
-        return s0 + c * 256 + lane * 4 + e < s1 && topk_bin(key) >= d.digit;
+        return s0 + c * 256 + lane * 4 + e < s1 && key >= kmin;
     };
     int cnt = 0;
 #pragma unroll
@@ -352,6 +359,7 @@ __global__ __launch_bounds__(kFT) void k_topk_filter(int Tq, int N, int m, int k
 #pragma unroll
     for (int u = 0; u < kFPT / 4; ++u) sc[u] = *(const float4 *)(srow + min(j0 + 4 * u, stride - 4));
     const Digit d = find_digit<kFT>(ghist + row * kTopkBins, kTopkBins, k, sh, &shd);
+    const uint32_t kmin = topk_bin_floor(d.digit);  // keys of digit >= D
     uint32_t keys[kFPT];
     uint32_t bits = 0;
 #pragma unroll
@@ -363,7 +371,7 @@ __global__ __launch_bounds__(kFT) void k_topk_filter(int Tq, int N, int m, int k
     }
 #pragma unroll
     for (int u = 0; u < kFPT; ++u)
-        bits |= (uint32_t)(j0 + u < nv && topk_bin(keys[u]) >= d.digit) << u;
+        bits |= (uint32_t)(j0 + u < nv && keys[u] >= kmin) << u;
     int total;
     int pos = block_excl_scan<kFT>(__popc(bits), sh, &total);
     IdxKey *sg = seg + (row * nblk + blk) * (int64_t)kTopkFilterChunk;
