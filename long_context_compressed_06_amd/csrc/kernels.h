@@ -27,8 +27,8 @@ __device__ __forceinline__ uint32_t topk_bin(uint32_t key) {
 constexpr int kTopkFilterChunk = 4096;
 constexpr int kTopkFinalItems = 16384;
 // with at least kTopkCompactMinRows queries, rows of up to kTopkCompactMax
-// scores are selected in one pass by one workgroup per query (scores held in
-// registers); otherwise the filter + final path spreads each row over CUs
+// scores are selected in one pass by one workgroup per query (several per
+// CU); otherwise the filter + final path spreads each row over CUs
 constexpr int kTopkCompactMax = 65536;
 constexpr int kTopkCompactMinRows = 256;
 constexpr int64_t kTopkMaxEntries = (int64_t)kTopkFilterChunk * 1023;

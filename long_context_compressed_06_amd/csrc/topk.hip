@@ -14,10 +14,10 @@
 // bin, all 32 for an end bin) and, for keys that are fully equal, by index.
 //
 // Many queries with rows of up to kTopkCompactMax scores (prefill chunks):
-// one workgroup per query holds its row in registers, packs the pairs of digit
-// >= D into LDS and resolves them there.  Few queries (decode) or long rows
-// (1M context): the row is
-// cut into chunks of kTopkFilterChunk scores; a workgroup per chunk writes
+// one workgroup per query, several per CU, reads its row twice (count, then
+// pack the pairs of digit >= D into LDS) and resolves the pairs there.  Few
+// queries (decode) or long rows (1M context): the row is cut into chunks of
+// kTopkFilterChunk scores; a workgroup per chunk writes
 // the (index, key) pairs of its chunk whose digit is >= D, in index order, to
 // a segment of the workspace; then one workgroup per query gathers all
 // segments into LDS and resolves them.  Either way the kept set leaves in
@@ -222,45 +222,51 @@ struct IdxKey {
 
 // Exact select straight over a score row in global memory (used only when
 // the pairs of digit >= D do not fit in LDS).
+template <int NT>
 __device__ void select_row_global(const float *srow, int64_t nv, int k, Digit d, int32_t *orow, uint32_t *hist,
                                   int *sh, Digit *shd) {
     Sel s = Sel::start(d, k);
     auto key_at = [&](int64_t j) -> uint32_t { return order_key(srow[j]); };
-    if (d.at != s.rem) refine<kNT>(key_at, nv, s, hist, sh, shd);
-    ordered_keep<kNT>(key_at, nv, s, sh, [&](int pos, int64_t j) {
+    if (d.at != s.rem) refine<NT>(key_at, nv, s, hist, sh, shd);
+    ordered_keep<NT>(key_at, nv, s, sh, [&](int pos, int64_t j) {
         if (pos >= 0 && pos < k) orow[pos] = (int32_t)j;
     });
 }
 
 // The M pairs of digit >= D sit in LDS in index order: resolve digit D with
 // the lower digits and write the kept indices, ascending.
+template <int NT>
 __device__ void select_items(const IdxKey *items, int M, int k, Digit d, int32_t *orow, uint32_t *hist, int *sh,
                              Digit *shd) {
     Sel s = Sel::start(d, k);  // keys of digit D to keep: s.rem
     auto key_at = [&](int64_t i) -> uint32_t { return items[i].key; };
-    if (d.at != s.rem) refine<kNT>(key_at, M, s, hist, sh, shd);
-    ordered_keep<kNT>(key_at, M, s, sh, [&](int pos, int64_t i) {
+    if (d.at != s.rem) refine<NT>(key_at, M, s, hist, sh, shd);
+    ordered_keep<NT>(key_at, M, s, sh, [&](int pos, int64_t i) {
         if (pos >= 0 && pos < k) orow[pos] = items[i].j;
     });
 }
 
-// ------------------------------------- rows of up to kNT*KPL scores: one pass
-// One workgroup per query.  Wavefront w owns a contiguous run of the row and
-// loads it into registers (KPL scores per lane, as 16-byte vectors of four
-// consecutive scores) while the digit D is found from the histogram; the
-// pairs of digit >= D are then packed into LDS in index order (run offsets
-// from one exchange of per-wave counts, in-run offsets from ballots) and
-// resolved there.
-template <int KPL>
-__global__ __launch_bounds__(kNT) void k_topk_compact(int Tq, int N, int m, int k, QPos q_pos0,
-                                                      const float *__restrict__ scores,
-                                                      const uint32_t *__restrict__ ghist, int32_t *__restrict__ out) {
-    extern __shared__ IdxKey items[];  // [kTopkFinalItems]
+// ------------------------------------ streaming one pass, several rows per CU
+// One workgroup of kST threads per query, the row read twice from memory
+// instead of held in registers (the second read mostly from cache), so that
+// a workgroup needs few registers and kStreamItems pairs of LDS and several
+// rows are selected on one CU at once.  Wavefront w owns a contiguous run of
+// the row: a first read counts its pairs of digit >= D, one exchange of the
+// counts gives each run its offset, a second read packs the pairs into LDS in
+// index order (in-run offsets from ballots), and they are resolved there.
+// Rows with more pairs than that take the global select.
+constexpr int kST = 512;
+constexpr int kStreamItems = 4096;
+constexpr int kStreamBatch = 4;  // 16-byte vectors per lane in flight per batch
+
+__global__ __launch_bounds__(kST) void k_topk_stream(int Tq, int N, int m, int k, QPos q_pos0,
+                                                     const float *__restrict__ scores,
+                                                     const uint32_t *__restrict__ ghist, int32_t *__restrict__ out) {
+    __shared__ IdxKey items[kStreamItems];
     __shared__ uint32_t hist[2048];
-    __shared__ int sh[2 * kNT / 64];
+    __shared__ int sh[2 * kST / 64];
     __shared__ Digit shd;
-    constexpr int NW = kNT / 64;
-    constexpr int F4 = KPL / 4;        // 16-byte vectors per lane
+    constexpr int NW = kST / 64;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int64_t row = blockIdx.x;
     const int64_t nv = n_visible(q_pos0.at(row / Tq, row % Tq), m, N);
@@ -268,29 +274,44 @@ __global__ __launch_bounds__(kNT) void k_topk_compact(int Tq, int N, int m, int 
     if (trivial_row(nv, k, orow)) return;
     const int stride = (int)topk_score_stride(N);
     const float *srow = scores + row * stride;
-    const int per = (int)((nv + NW * 256 - 1) / (NW * 256)) * 256;  // run length, <= 64*KPL
+    const int per = (int)((nv + NW * 256 - 1) / (NW * 256)) * 256;  // run length (a multiple of 256 scores)
     const int s0 = wv * per;
     const int s1 = (int)min((int64_t)s0 + per, nv);
-    // unconditional loads (vectors past the row's end reread its last one) so
-    // that all F4 are in flight together; positions >= s1 are masked below
-    float4 sc[F4];
-#pragma unroll
-    for (int c = 0; c < F4; ++c) sc[c] = *(const float4 *)(srow + min(s0 + c * 256 + lane * 4, stride - 4));
-    const Digit d = find_digit<kNT>(ghist + row * kTopkBins, kTopkBins, k, sh, &shd);
+    const Digit d = find_digit<kST>(ghist + row * kTopkBins, kTopkBins, k, sh, &shd);
     const uint32_t kmin = topk_bin_floor(d.digit);  // keys of digit >= D
-    auto selected = [&](int c, int e, uint32_t &key) -> bool {
-        const float4 v = sc[c];
-        key = order_key(e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w);
-        return s0 + c * 256 + lane * 4 + e < s1 && key >= kmin;
+    // batches of kStreamBatch vectors of four consecutive scores per lane, all
+    // in flight together (past the row's end the last vector is reread and
+    // masked); f(c, e, selected, key) per score in index order of (c, lane, e)
+    auto for_run = [&](auto f) {
+        for (int b0 = s0; b0 < s1; b0 += kStreamBatch * 256) {
+            float4 v[kStreamBatch];
+#pragma unroll
+            for (int u = 0; u < kStreamBatch; ++u)
+                v[u] = *(const float4 *)(srow + min(b0 + u * 256 + lane * 4, stride - 4));
+#pragma unroll
+            for (int u = 0; u < kStreamBatch; ++u) {
+                const int c = b0 + u * 256;
+                if (c >= s1) break;  // (uniform)
+                f(c, v[u]);
+            }
+        }
+    };
+    auto select4 = [&](int c, const float4 &v, uint32_t (&key)[4], bool (&sel)[4]) {
+        key[0] = order_key(v.x);
+        key[1] = order_key(v.y);
+        key[2] = order_key(v.z);
+        key[3] = order_key(v.w);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sel[e] = c + lane * 4 + e < s1 && key[e] >= kmin;
     };
     int cnt = 0;
+    for_run([&](int c, const float4 &v) {
+        uint32_t key[4];
+        bool sel[4];
+        select4(c, v, key, sel);
 #pragma unroll
-    for (int c = 0; c < F4; ++c)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            uint32_t key;
-            cnt += __popcll(__ballot(selected(c, e, key)));
-        }
+        for (int e = 0; e < 4; ++e) cnt += __popcll(__ballot(sel[e]));
+    });
     if (lane == 0) sh[NW + wv] = cnt;
     __syncthreads();
     int base = 0, M = 0;
@@ -301,18 +322,17 @@ __global__ __launch_bounds__(kNT) void k_topk_compact(int Tq, int N, int m, int 
         M += v;
     }
     __syncthreads();
-    if (M > kTopkFinalItems || M != d.above + d.at) {
-        select_row_global(srow, nv, k, d, orow, hist, sh, &shd);
+    if (M > kStreamItems || M != d.above + d.at) {
+        select_row_global<kST>(srow, nv, k, d, orow, hist, sh, &shd);
         return;
     }
-#pragma unroll
-    for (int c = 0; c < F4; ++c) {
+    for_run([&](int c, const float4 &v) {
         uint32_t key[4];
         bool sel[4];
+        select4(c, v, key, sel);
         int before = 0, chunk = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            sel[e] = selected(c, e, key[e]);
             const uint64_t bm = __ballot(sel[e]);
             before += lanes_below(bm);
             chunk += __popcll(bm);
@@ -320,11 +340,11 @@ __global__ __launch_bounds__(kNT) void k_topk_compact(int Tq, int N, int m, int 
         int pos = base + before;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            if (sel[e]) items[pos++] = IdxKey{s0 + c * 256 + lane * 4 + e, key[e]};
+            if (sel[e]) items[pos++] = IdxKey{c + lane * 4 + e, key[e]};
         base += chunk;
-    }
+    });
     __syncthreads();
-    select_items(items, M, k, d, orow, hist, sh, &shd);
+    select_items<kST>(items, M, k, d, orow, hist, sh, &shd);
 }
 
 // ----------------------------------------------------- long rows: filter + final
@@ -404,7 +424,7 @@ __global__ __launch_bounds__(kNT) void k_topk_final(int Tq, int N, int m, int k,
     __syncthreads();
     if (M > kTopkFinalItems || M != d.above + d.at) {
         // more pairs than LDS holds
-        select_row_global(scores + row * topk_score_stride(N), nv, k, d, orow, hist, sh, &shd);
+        select_row_global<kNT>(scores + row * topk_score_stride(N), nv, k, d, orow, hist, sh, &shd);
         return;
     }
     // gather: batches of four pairs per thread, all loads in flight together
@@ -428,7 +448,7 @@ __global__ __launch_bounds__(kNT) void k_topk_final(int Tq, int N, int m, int k,
         }
     }
     __syncthreads();
-    select_items(items, M, k, d, orow, hist, sh, &shd);
+    select_items<kNT>(items, M, k, d, orow, hist, sh, &shd);
 }
 
 // ------------------------------------------------------------------ host side
@@ -467,29 +487,15 @@ hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int KPL>
-static hipError_t launch_compact(int64_t rows, int Tq, int N, int m, int k, QPos q_pos0, const float *scores,
-                                 const uint32_t *hist, int32_t *out, hipStream_t st) {
-    static_assert(KPL * kNT <= kTopkCompactMax, "row longer than the one-pass limit");
-    const size_t lds = (size_t)kTopkFinalItems * sizeof(IdxKey);
-    static const hipError_t attr =
-        hipFuncSetAttribute((const void *)k_topk_compact<KPL>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(k_topk_compact<KPL>, dim3((unsigned)rows), dim3(kNT), lds, st, Tq, N, m, k, q_pos0, scores,
-                       hist, out);
-    return hipGetLastError();
-}
-
 hipError_t launch_topk(int B, int Tq, int N, int m, int k, QPos q_pos0, const float *scores, void *scratch,
                        int32_t *out, hipStream_t st) {
     const int64_t rows = (int64_t)B * Tq;
     const TopkPlan p = topk_plan(rows, N);
     uint32_t *hist = (uint32_t *)scratch;
     if (!p.filter) {
-        if (N <= 8 * kNT) return launch_compact<8>(rows, Tq, N, m, k, q_pos0, scores, hist, out, st);
-        if (N <= 16 * kNT) return launch_compact<16>(rows, Tq, N, m, k, q_pos0, scores, hist, out, st);
-        if (N <= 32 * kNT) return launch_compact<32>(rows, Tq, N, m, k, q_pos0, scores, hist, out, st);
-        return launch_compact<64>(rows, Tq, N, m, k, q_pos0, scores, hist, out, st);
+        hipLaunchKernelGGL(k_topk_stream, dim3((unsigned)rows), dim3(kST), 0, st, Tq, N, m, k, q_pos0, scores, hist,
+                           out);
+        return hipGetLastError();
     }
     char *base = (char *)scratch + align256(topk_clear_words(rows, N) * 4);
     int32_t *counts = (int32_t *)base;
