@@ -232,6 +232,22 @@ int csa_ragged_index_topk_mx4(int dt, int B, int N, int H_I, int d_I, int m, int
                               int32_t *topk_idx, float *scores_out,
                               void *workspace, size_t workspace_bytes, void *stream);
 /*
+ * flags of the fused compress + index calls.
+ * CSA_HIST_ZERO: the caller vouches that the top-k histograms in the
+ *   workspace are zero, as they are in a zero-filled workspace and after any
+ *   call of these or the index calls whose most recent predecessor on the
+ *   workspace had the same B, Tq and N (every index call leaves its
+ *   histograms zero).  The call then clears nothing first: on the selection's
+ *   multi-workgroup path (few queries: decode) the compression runs in the
+ *   top-k filter launch instead, one launch fewer per step; otherwise in a
+ *   launch of its own before the indexer.  Results are unchanged.  With
+ *   nonzero histograms the selection is wrong (the kernels still touch no
+ *   memory outside the call's operands and workspace).
+ * Other bits: CSA_EINVAL.
+ */
+#define CSA_HIST_ZERO 1
+
+/*
  * csa_ragged_compress_index_topk (+ _mx4) -- csa_ragged_compress followed by
  * csa_ragged_index_topk (csa_ragged_index_topk_mx4) on the same stream, the
  * compression running in the launch that clears the selection's histograms,
@@ -240,7 +256,8 @@ int csa_ragged_index_topk_mx4(int dt, int B, int N, int H_I, int d_I, int m, int
  * are the compression's, the others the index keys'); the results equal
  * those of the two calls bit for bit.  Besides each call's checks,
  * entries_out may overlap no index operand, output or the workspace, and the
- * rings and pos may not overlap the workspace (CSA_EINVAL).
+ * rings and pos may overlap neither the workspace nor an index output
+ * (CSA_EINVAL).  flags: 0 or CSA_HIST_ZERO (above).
  */
 int csa_ragged_compress_index_topk(int dt, int B, int m, int d, const int64_t *pos,
                                    const void *raw_ring, int64_t ring_bstride,
@@ -253,7 +270,7 @@ int csa_ragged_compress_index_topk(int dt, int B, int m, int d, const int64_t *p
                                    const void *k_idx, int64_t k_bstride,
                                    const int32_t *page_table, int max_pages, int page_rows, int64_t n_pages,
                                    int32_t *topk_idx, float *scores_out,
-                                   void *workspace, size_t workspace_bytes, void *stream);
+                                   void *workspace, size_t workspace_bytes, int flags, void *stream);
 int csa_ragged_compress_index_topk_mx4(int dt, int B, int m, int d, const int64_t *pos,
                                        const void *raw_ring, int64_t ring_bstride,
                                        const float *logit_ring, int64_t logit_bstride, int64_t ring,
@@ -265,7 +282,7 @@ int csa_ragged_compress_index_topk_mx4(int dt, int B, int m, int d, const int64_
                                        const uint8_t *k_codes, const uint8_t *k_scales, int64_t k_bstride,
                                        const int32_t *page_table, int max_pages, int page_rows, int64_t n_pages,
                                        int32_t *topk_idx, float *scores_out,
-                                       void *workspace, size_t workspace_bytes, void *stream);
+                                       void *workspace, size_t workspace_bytes, int flags, void *stream);
 int csa_ragged_sparse_mqa(int dt, int B, int H, int d, int N, int m, int k, int W,
                           const int64_t *pos, float scale,
                           const void *q,
@@ -396,8 +413,9 @@ int csa_index_scores_mx4(int dt, int B, int Tq, int N, int H_I, int d_I, int m, 
  *                       arguments after B and m
  * Both results equal those of the two separate calls, bit for bit.  Besides
  * each call's own checks, entries_out may overlap no index operand, output or
- * the workspace, and raw / logits may not overlap the workspace (CSA_EINVAL).
- * On an error nothing is launched.
+ * the workspace, and raw / logits may overlap neither the workspace nor an
+ * index output (CSA_EINVAL).  flags: 0 or CSA_HIST_ZERO (defined above
+ * csa_ragged_compress_index_topk).  On an error nothing is launched.
  */
 int csa_compress_index_topk(int dt, int B, int G, int m, int d,
                             const void *raw, int64_t raw_bstride,
@@ -407,7 +425,7 @@ int csa_compress_index_topk(int dt, int B, int G, int m, int d,
                             const void *q_idx, const float *w_idx,
                             const void *k_idx, int64_t k_bstride,
                             int32_t *topk_idx, float *scores_out,
-                            void *workspace, size_t workspace_bytes, void *stream);
+                            void *workspace, size_t workspace_bytes, int flags, void *stream);
 int csa_compress_index_topk_mx4(int dt, int B, int G, int m, int d,
                                 const void *raw, int64_t raw_bstride,
                                 const float *logits, int64_t logit_bstride,
@@ -416,7 +434,7 @@ int csa_compress_index_topk_mx4(int dt, int B, int G, int m, int d,
                                 const void *q_idx, const float *w_idx,
                                 const uint8_t *k_codes, const uint8_t *k_scales, int64_t k_bstride,
                                 int32_t *topk_idx, float *scores_out,
-                                void *workspace, size_t workspace_bytes, void *stream);
+                                void *workspace, size_t workspace_bytes, int flags, void *stream);
 
 /*
  * csa_sparse_mqa -- shared-KV multi-query attention over the selected

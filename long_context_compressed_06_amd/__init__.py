@@ -102,15 +102,15 @@ def lib():
     L.csa_index_topk_noalloc.argtypes = [I, I, I, I, I, I, I, I, I64, P, P, P, I64, P, P, P]
     L.csa_index_topk_noalloc.restype = I
     comp = [I, I, I, I, I, P, I64, P, I64, P, I64]  # csa_compress's arguments, without the stream
-    L.csa_compress_index_topk.argtypes = comp + [I, I, I, I, I, I64, P, P, P, I64, P, P, P, SZ, P]
+    L.csa_compress_index_topk.argtypes = comp + [I, I, I, I, I, I64, P, P, P, I64, P, P, P, SZ, I, P]
     L.csa_compress_index_topk.restype = I
-    L.csa_compress_index_topk_mx4.argtypes = comp + [I, I, I, I, I, I64, P, P, P, P, I64, P, P, P, SZ, P]
+    L.csa_compress_index_topk_mx4.argtypes = comp + [I, I, I, I, I, I64, P, P, P, P, I64, P, P, P, SZ, I, P]
     L.csa_compress_index_topk_mx4.restype = I
     rcomp = [I, I, I, I, P, P, I64, P, I64, I64, P, I64, I64, P, I, I, I64]  # csa_ragged_compress's, no stream
-    L.csa_ragged_compress_index_topk.argtypes = rcomp + [I, I, I, I, P, P, P, I64, P, I, I, I64, P, P, P, SZ, P]
+    L.csa_ragged_compress_index_topk.argtypes = rcomp + [I, I, I, I, P, P, P, I64, P, I, I, I64, P, P, P, SZ, I, P]
     L.csa_ragged_compress_index_topk.restype = I
     L.csa_ragged_compress_index_topk_mx4.argtypes = rcomp + [I, I, I, I, P, P, P, P, I64, P, I, I, I64, P, P, P, SZ,
-                                                             P]
+                                                             I, P]
     L.csa_ragged_compress_index_topk_mx4.restype = I
     L.csa_stream_read.argtypes = [P, I64, I, P, P]
     L.csa_stream_read.restype = I
@@ -219,14 +219,28 @@ def _fused_pair(raw, q_idx):
         raise ValueError("raw and q_idx must share the element type, the batch and the device")
 
 
+
+def _flags(hist_zero, workspace):
+    if hist_zero and workspace is None:
+        raise ValueError("hist_zero needs a caller-owned workspace (a fresh one is not zero-filled)")
+    return CSA_HIST_ZERO if hist_zero else 0
+
+
+# flag of the fused calls: the workspace's top-k histograms are zero on entry (a zero-filled workspace, or one whose
+# previous call had the same shape: every index call leaves them zero); then nothing is cleared first and, for few
+# queries, the compression rides in the top-k filter launch
+CSA_HIST_ZERO = 1
+
+
 def csa_compress_index_topk(raw, logits, m: int, entries_out, q_idx, w_idx, k_idx, N: int, k: int, q_pos0: int,
-                            topk_idx=None, scores_out=None, workspace=None) -> torch.Tensor:
+                            topk_idx=None, scores_out=None, workspace=None, hist_zero=False) -> torch.Tensor:
     """csa_compress(raw, logits, m, entries_out) then csa_index_topk(q_idx, w_idx, k_idx, N, m, k, q_pos0, ...) in
-    one call with one launch fewer; returns topk_idx.  entries_out is the attention's cache, not k_idx."""
+    one call with one launch fewer; returns topk_idx.  entries_out is the attention's cache, not k_idx.
+    hist_zero: the given workspace's histograms are zero (CSA_HIST_ZERO): one launch fewer again."""
     _fused_pair(raw, q_idx)
     c = _compress_args(raw, logits, m, entries_out)
     topk_idx, a = _index_args(q_idx, w_idx, k_idx, N, k, q_pos0, topk_idx, scores_out, workspace)
-    _check(lib().csa_compress_index_topk(*c, *a, _stream(q_idx)))
+    _check(lib().csa_compress_index_topk(*c, *a, _flags(hist_zero, workspace), _stream(q_idx)))
     return topk_idx
 
 
@@ -366,12 +380,14 @@ def csa_index_topk_mx4(q_idx, w_idx, k_codes, k_scales, N: int, m: int, k: int, 
 
 
 def csa_compress_index_topk_mx4(raw, logits, m: int, entries_out, q_idx, w_idx, k_codes, k_scales, N: int, k: int,
-                                q_pos0: int, topk_idx=None, scores_out=None, workspace=None) -> torch.Tensor:
-    """csa_compress then csa_index_topk_mx4 in one call with one launch fewer; returns topk_idx."""
+                                q_pos0: int, topk_idx=None, scores_out=None, workspace=None,
+                                hist_zero=False) -> torch.Tensor:
+    """csa_compress then csa_index_topk_mx4 in one call with one launch fewer; returns topk_idx.  hist_zero: as
+    csa_compress_index_topk."""
     _fused_pair(raw, q_idx)
     c = _compress_args(raw, logits, m, entries_out)
     topk_idx, a = _index_mx4_args(q_idx, w_idx, k_codes, k_scales, N, k, q_pos0, topk_idx, scores_out, workspace)
-    _check(lib().csa_compress_index_topk_mx4(*c, *a, _stream(q_idx)))
+    _check(lib().csa_compress_index_topk_mx4(*c, *a, _flags(hist_zero, workspace), _stream(q_idx)))
     return topk_idx
 
 
@@ -548,13 +564,14 @@ def csa_ragged_index_topk(q_idx, w_idx, k_idx, N: int, m: int, k: int, pos, topk
 
 def csa_ragged_compress_index_topk(raw_ring, logit_ring, ring: int, m: int, pos, entries_out, q_idx, w_idx, k_idx,
                                    N: int, k: int, topk_idx=None, scores_out=None, workspace=None, entry_pages=None,
-                                   pages=None) -> torch.Tensor:
+                                   pages=None, hist_zero=False) -> torch.Tensor:
     """csa_ragged_compress(raw_ring, logit_ring, ring, m, pos, entries_out, entry_pages) then
-    csa_ragged_index_topk(q_idx, w_idx, k_idx, N, m, k, pos, ..., pages) in one call with one launch fewer."""
+    csa_ragged_index_topk(q_idx, w_idx, k_idx, N, m, k, pos, ..., pages) in one call with one launch fewer.
+    hist_zero: as csa_compress_index_topk."""
     _fused_pair(raw_ring, q_idx)
     c = _ragged_compress_args(raw_ring, logit_ring, ring, m, pos, entries_out, entry_pages)
     topk_idx, a = _ragged_index_args(q_idx, w_idx, k_idx, N, k, pos, topk_idx, scores_out, workspace, pages)
-    _check(lib().csa_ragged_compress_index_topk(*c, *a, _stream(q_idx)))
+    _check(lib().csa_ragged_compress_index_topk(*c, *a, _flags(hist_zero, workspace), _stream(q_idx)))
     return topk_idx
 
 
@@ -595,13 +612,15 @@ def csa_ragged_index_topk_mx4(q_idx, w_idx, k_codes, k_scales, N: int, m: int, k
 
 def csa_ragged_compress_index_topk_mx4(raw_ring, logit_ring, ring: int, m: int, pos, entries_out, q_idx, w_idx,
                                        k_codes, k_scales, N: int, k: int, topk_idx=None, scores_out=None,
-                                       workspace=None, entry_pages=None, pages=None) -> torch.Tensor:
-    """csa_ragged_compress then csa_ragged_index_topk_mx4 in one call with one launch fewer."""
+                                       workspace=None, entry_pages=None, pages=None,
+                                       hist_zero=False) -> torch.Tensor:
+    """csa_ragged_compress then csa_ragged_index_topk_mx4 in one call with one launch fewer.  hist_zero: as
+    csa_compress_index_topk."""
     _fused_pair(raw_ring, q_idx)
     c = _ragged_compress_args(raw_ring, logit_ring, ring, m, pos, entries_out, entry_pages)
     topk_idx, a = _ragged_index_mx4_args(q_idx, w_idx, k_codes, k_scales, N, k, pos, topk_idx, scores_out,
                                          workspace, pages)
-    _check(lib().csa_ragged_compress_index_topk_mx4(*c, *a, _stream(q_idx)))
+    _check(lib().csa_ragged_compress_index_topk_mx4(*c, *a, _flags(hist_zero, workspace), _stream(q_idx)))
     return topk_idx
 
 

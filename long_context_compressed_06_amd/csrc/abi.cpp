@@ -11,7 +11,7 @@
 #include <string>
 
 #include "../../include/csa.h"
-#include "kernels.h"
+#include "compress_fold.h"
 
 namespace {
 
@@ -178,14 +178,16 @@ int csa_compress(int dt, int B, int G, int m, int d, const void *raw, int64_t ra
 static_assert(csa::kTopkBins % 4 == 0, "the fused clear zeroes whole 16-byte runs");
 
 // A checked compression that an index call runs in the launch clearing its
-// top-k histograms: the bytes it writes and reads (for the overlap checks) and
-// how to launch it with that clear.
+// top-k histograms, or (histograms already zero) in its top-k filter launch:
+// the bytes it writes and reads (for the overlap checks), how to launch it
+// with that clear, and its operands for the filter launch.
 struct FusedCompress {
     Span out;
     Span in[3];
     int n_in;
     hipError_t (*launch)(const void *job, hipStream_t st, uint32_t *clr, int64_t clr_words);
     const void *job;
+    csa::FoldedCompress fold;
 };
 
 static FusedCompress fused(const CompressJob &c) {
@@ -193,12 +195,14 @@ static FusedCompress fused(const CompressJob &c) {
                          [](const void *j, hipStream_t st, uint32_t *clr, int64_t cw) {
                              return launch_compress_job(*(const CompressJob *)j, st, clr, cw);
                          },
-                         &c};
+                         &c,
+                         csa::FoldedCompress{false, c.dt, c.B, c.G, c.m, c.d, c.raw, c.raw_bs, c.logits, c.log_bs,
+                                             c.out, c.out_bs, nullptr, 0, csa::RowMap(), 0}};
 }
 
 // the compression against the index operands, outputs and workspace (its
-// output may not overlap any of them, nor its inputs the workspace, which the
-// same launch clears)
+// output may not overlap any of them, nor its inputs the workspace or the
+// index outputs: it may run before, beside or after the indexer)
 static int check_compress_against(const FusedCompress *fc, const Span *in, int n_in, const Span &si,
                                   const Span &ss, const Span &sw) {
     if (!fc) return CSA_OK;
@@ -207,9 +211,48 @@ static int check_compress_against(const FusedCompress *fc, const Span *in, int n
     if (overlap(fc->out, si) || overlap(fc->out, ss) || overlap(fc->out, sw))
         return fail(CSA_EINVAL, "the compression overlaps an index output or the workspace");
     for (int i = 0; i < fc->n_in; ++i)
-        if (overlap(fc->in[i], sw)) return fail(CSA_EINVAL, "a compression input overlaps the workspace");
+        if (overlap(fc->in[i], sw) || overlap(fc->in[i], si) || overlap(fc->in[i], ss))
+            return fail(CSA_EINVAL, "a compression input overlaps the workspace or an index output");
     return CSA_OK;
 }
+
+static int check_flags(int flags) {
+    if (flags & ~CSA_HIST_ZERO) return fail(CSA_EINVAL, "unknown flags 0x%x", (unsigned)flags);
+    return CSA_OK;
+}
+
+// The launches of an index call around its indexer launch: the top-k
+// histograms are cleared first (in the compression's launch when there is
+// one) unless the caller vouches that they are zero (CSA_HIST_ZERO: every
+// call leaves them so); then the indexer; then the top-k, whose filter launch
+// carries the compression when the histograms needed no clear and the
+// selection takes the filter path.
+extern "C++" {
+template <class IndexLaunch>
+static int run_index_call(int64_t rows, int N, const FusedCompress *fc, int flags, uint32_t *scratch,
+                          hipStream_t st, IndexLaunch index, int B, int Tq, int m, int k, csa::QPos q_pos0,
+                          const float *scores, int32_t *topk_idx) {
+    const bool zero = (flags & CSA_HIST_ZERO) != 0;
+    const bool fold = fc && zero && N > 0 && csa::topk_plan(rows, N).filter;
+    if (N > 0) {
+        if (!zero) {
+            const int64_t cw = (int64_t)csa::topk_clear_words(rows, N);
+            if (int s = hip_status(fc ? fc->launch(fc->job, st, scratch, cw) : csa::launch_fill_u32(scratch, cw, 0u, st),
+                                   "histogram clear"))
+                return s;
+        } else if (fc && !fold) {
+            if (int s = hip_status(fc->launch(fc->job, st, nullptr, 0), "compress launch")) return s;
+        }
+        if (int s = hip_status(index(), "indexer launch")) return s;
+    } else if (fc) {
+        if (int s = hip_status(fc->launch(fc->job, st, nullptr, 0), "compress launch")) return s;
+    }
+    if (fold)
+        return hip_status(csa::launch_topk_folded(B, Tq, N, m, k, q_pos0, scores, scratch, topk_idx, st, fc->fold),
+                          "top-k launch");
+    return hip_status(csa::launch_topk(B, Tq, N, m, k, q_pos0, scores, scratch, topk_idx, st), "top-k launch");
+}
+}  // extern "C++"
 
 int csa_compress_channels(int dt, int B, int G, int m, int d, const void *raw, int64_t raw_bstride,
                           const float *logits, int64_t logit_bstride, void *out, int64_t out_bstride, void *stream) {
@@ -411,7 +454,9 @@ static FusedCompress fused(const RaggedCompressJob &c) {
                          [](const void *j, hipStream_t st, uint32_t *clr, int64_t cw) {
                              return launch_ragged_compress_job(*(const RaggedCompressJob *)j, st, clr, cw);
                          },
-                         &c};
+                         &c,
+                         csa::FoldedCompress{true, c.dt, c.B, 0, c.m, c.d, c.raw_ring, c.ring_bs, c.logit_ring,
+                                             c.logit_bs, c.out, c.out_bs, c.pos, c.ring, c.omap, c.out_rows}};
 }
 
 int csa_ragged_compress(int dt, int B, int m, int d, const int64_t *pos, const void *raw_ring, int64_t ring_bstride,
@@ -466,7 +511,7 @@ static int index_topk_impl(int dt, int B, int Tq, int N, int H_I, int d_I, int m
                            const void *q_idx, const float *w_idx, const void *k_idx, int64_t k_bstride,
                            int32_t *topk_idx, float *scores_out, void *workspace, size_t workspace_bytes,
                            void *stream, const int32_t *page_table = nullptr, int max_pages = 0, int page_rows = 0,
-                           int64_t n_pages = 0, const FusedCompress *fc = nullptr) {
+                           int64_t n_pages = 0, const FusedCompress *fc = nullptr, int flags = 0) {
     if (int s = check_dt(dt)) return s;
     if (B < 0 || Tq < 0 || N < 0) return fail(CSA_EINVAL, "B, Tq and N must be >= 0");
     if (H_I < 1 || H_I > 64) return fail(CSA_EUNSUPPORTED, "H_I=%d outside 1..64", H_I);
@@ -514,22 +559,15 @@ static int index_topk_impl(int dt, int B, int Tq, int N, int H_I, int d_I, int m
     if (overlap(sw, si) || overlap(sw, ss)) return fail(CSA_EINVAL, "workspace overlaps an output");
     if (int s = check_compress_against(fc, inputs, 3, si, ss, sw)) return s;
     hipStream_t st = (hipStream_t)stream;
-    if (N > 0) {
-        // the first radix digit of the selection is counted by the indexer: its
-        // histograms are cleared first, in the compression's launch when there is one
-        const int64_t cw = (int64_t)csa::topk_clear_words(rows, N);
-        if (int s = hip_status(fc ? fc->launch(fc->job, st, scratch, cw) : csa::launch_fill_u32(scratch, cw, 0u, st),
-                               "histogram clear"))
-            return s;
-        if (int s = hip_status(csa::launch_index_scores(dt, B, Tq, N, H_I, d_I, m, q_pos0, q_idx, w_idx, k_idx,
-                                                         kmap, scores, csa::topk_score_stride(N), scores_out,
-                                                         scratch, st),
-                               "indexer launch"))
-            return s;
-    } else if (fc) {
-        if (int s = hip_status(fc->launch(fc->job, st, nullptr, 0), "compress launch")) return s;
-    }
-    return hip_status(csa::launch_topk(B, Tq, N, m, k, q_pos0, scores, scratch, topk_idx, st), "top-k launch");
+    // the first radix digit of the selection is counted by the indexer into
+    // the histograms at the start of the top-k scratch
+    return run_index_call(
+        rows, N, fc, flags, scratch, st,
+        [&] {
+            return csa::launch_index_scores(dt, B, Tq, N, H_I, d_I, m, q_pos0, q_idx, w_idx, k_idx, kmap, scores,
+                                            csa::topk_score_stride(N), scores_out, scratch, st);
+        },
+        B, Tq, m, k, q_pos0, scores, topk_idx);
 }
 
 int csa_index_topk(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k, int64_t q_pos0, const void *q_idx,
@@ -544,14 +582,16 @@ int csa_compress_index_topk(int dt, int B, int G, int m, int d, const void *raw,
                             const float *logits, int64_t logit_bstride, void *entries_out, int64_t out_bstride,
                             int Tq, int N, int H_I, int d_I, int k, int64_t q_pos0, const void *q_idx,
                             const float *w_idx, const void *k_idx, int64_t k_bstride, int32_t *topk_idx,
-                            float *scores_out, void *workspace, size_t workspace_bytes, void *stream) {
+                            float *scores_out, void *workspace, size_t workspace_bytes, int flags, void *stream) {
     const CompressJob c{dt, B, G, m, d, raw, raw_bstride, logits, logit_bstride, entries_out, out_bstride};
     bool empty;
     if (int s = check_compress(c, &empty)) return s;
+    if (int s = check_flags(flags)) return s;
     if (q_pos0 < 0) return fail(CSA_EINVAL, "q_pos0 must be >= 0");
     const FusedCompress fc = fused(c);
     return index_topk_impl(dt, B, Tq, N, H_I, d_I, m, k, csa::QPos(q_pos0), q_idx, w_idx, k_idx, k_bstride, topk_idx,
-                           scores_out, workspace, workspace_bytes, stream, nullptr, 0, 0, 0, empty ? nullptr : &fc);
+                           scores_out, workspace, workspace_bytes, stream, nullptr, 0, 0, 0, empty ? nullptr : &fc,
+                           flags);
 }
 
 int csa_index_topk_noalloc(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k, int64_t q_pos0,
@@ -588,16 +628,17 @@ int csa_ragged_compress_index_topk(int dt, int B, int m, int d, const int64_t *p
                                    const float *w_idx, const void *k_idx, int64_t k_bstride,
                                    const int32_t *page_table, int max_pages, int page_rows, int64_t n_pages,
                                    int32_t *topk_idx, float *scores_out, void *workspace, size_t workspace_bytes,
-                                   void *stream) {
+                                   int flags, void *stream) {
     RaggedCompressJob c{dt, B, m, d, pos, raw_ring, ring_bstride, logit_ring, logit_bstride, ring, entries_out,
                         out_bstride, out_rows, e_page_table, e_max_pages, e_page_rows, e_n_pages};
     bool empty;
     if (int s = check_ragged_compress(c, &empty)) return s;
+    if (int s = check_flags(flags)) return s;
     if (B > 0 && !pos) return fail(CSA_EINVAL, "NULL pos");
     const FusedCompress fc = fused(c);
     return index_topk_impl(dt, B, 1, N, H_I, d_I, m, k, csa::QPos(0, pos), q_idx, w_idx, k_idx, k_bstride, topk_idx,
                            scores_out, workspace, workspace_bytes, stream, page_table, max_pages, page_rows,
-                           n_pages, empty ? nullptr : &fc);
+                           n_pages, empty ? nullptr : &fc, flags);
 }
 
 int csa_index_scores(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int64_t q_pos0, const void *q_idx,
@@ -643,7 +684,7 @@ static int index_topk_mx4_impl(int dt, int B, int Tq, int N, int H_I, int d_I, i
                                const uint8_t *k_scales, int64_t k_bstride, int32_t *topk_idx, float *scores_out,
                                void *workspace, size_t workspace_bytes, void *stream,
                                const int32_t *page_table = nullptr, int max_pages = 0, int page_rows = 0,
-                               int64_t n_pages = 0, const FusedCompress *fc = nullptr) {
+                               int64_t n_pages = 0, const FusedCompress *fc = nullptr, int flags = 0) {
     if (int s = check_dt(dt)) return s;
     if (B < 0 || Tq < 0 || N < 0) return fail(CSA_EINVAL, "B, Tq and N must be >= 0");
     if (H_I < 1 || H_I > 64) return fail(CSA_EUNSUPPORTED, "H_I=%d outside 1..64", H_I);
@@ -691,20 +732,13 @@ static int index_topk_mx4_impl(int dt, int B, int Tq, int N, int H_I, int d_I, i
     float *scores = (float *)workspace;
     uint32_t *scratch = (uint32_t *)((char *)workspace + scores_bytes(rows, N));
     hipStream_t st = (hipStream_t)stream;
-    if (N > 0) {
-        const int64_t cw = (int64_t)csa::topk_clear_words(rows, N);
-        if (int s = hip_status(fc ? fc->launch(fc->job, st, scratch, cw) : csa::launch_fill_u32(scratch, cw, 0u, st),
-                               "histogram clear"))
-            return s;
-        if (int s = hip_status(csa::launch_index_mx4(dt, B, Tq, N, H_I, d_I, m, q_pos0, q_idx, w_idx, k_codes,
-                                                      k_scales, kmap, scores, csa::topk_score_stride(N),
-                                                      scores_out, scratch, st),
-                               "indexer launch"))
-            return s;
-    } else if (fc) {
-        if (int s = hip_status(fc->launch(fc->job, st, nullptr, 0), "compress launch")) return s;
-    }
-    return hip_status(csa::launch_topk(B, Tq, N, m, k, q_pos0, scores, scratch, topk_idx, st), "top-k launch");
+    return run_index_call(
+        rows, N, fc, flags, scratch, st,
+        [&] {
+            return csa::launch_index_mx4(dt, B, Tq, N, H_I, d_I, m, q_pos0, q_idx, w_idx, k_codes, k_scales, kmap,
+                                         scores, csa::topk_score_stride(N), scores_out, scratch, st);
+        },
+        B, Tq, m, k, q_pos0, scores, topk_idx);
 }
 
 int csa_index_topk_mx4(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int k, int64_t q_pos0,
@@ -721,15 +755,16 @@ int csa_compress_index_topk_mx4(int dt, int B, int G, int m, int d, const void *
                                 int Tq, int N, int H_I, int d_I, int k, int64_t q_pos0, const void *q_idx,
                                 const float *w_idx, const uint8_t *k_codes, const uint8_t *k_scales,
                                 int64_t k_bstride, int32_t *topk_idx, float *scores_out, void *workspace,
-                                size_t workspace_bytes, void *stream) {
+                                size_t workspace_bytes, int flags, void *stream) {
     const CompressJob c{dt, B, G, m, d, raw, raw_bstride, logits, logit_bstride, entries_out, out_bstride};
     bool empty;
     if (int s = check_compress(c, &empty)) return s;
+    if (int s = check_flags(flags)) return s;
     if (q_pos0 < 0) return fail(CSA_EINVAL, "q_pos0 must be >= 0");
     const FusedCompress fc = fused(c);
     return index_topk_mx4_impl(dt, B, Tq, N, H_I, d_I, m, k, csa::QPos(q_pos0), q_idx, w_idx, k_codes, k_scales,
                                k_bstride, topk_idx, scores_out, workspace, workspace_bytes, stream, nullptr, 0, 0,
-                               0, empty ? nullptr : &fc);
+                               0, empty ? nullptr : &fc, flags);
 }
 
 int csa_index_scores_mx4(int dt, int B, int Tq, int N, int H_I, int d_I, int m, int64_t q_pos0, const void *q_idx,
@@ -777,16 +812,17 @@ int csa_ragged_compress_index_topk_mx4(int dt, int B, int m, int d, const int64_
                                        const float *w_idx, const uint8_t *k_codes, const uint8_t *k_scales,
                                        int64_t k_bstride, const int32_t *page_table, int max_pages, int page_rows,
                                        int64_t n_pages, int32_t *topk_idx, float *scores_out, void *workspace,
-                                       size_t workspace_bytes, void *stream) {
+                                       size_t workspace_bytes, int flags, void *stream) {
     RaggedCompressJob c{dt, B, m, d, pos, raw_ring, ring_bstride, logit_ring, logit_bstride, ring, entries_out,
                         out_bstride, out_rows, e_page_table, e_max_pages, e_page_rows, e_n_pages};
     bool empty;
     if (int s = check_ragged_compress(c, &empty)) return s;
+    if (int s = check_flags(flags)) return s;
     if (B > 0 && !pos) return fail(CSA_EINVAL, "NULL pos");
     const FusedCompress fc = fused(c);
     return index_topk_mx4_impl(dt, B, 1, N, H_I, d_I, m, k, csa::QPos(0, pos), q_idx, w_idx, k_codes, k_scales,
                                k_bstride, topk_idx, scores_out, workspace, workspace_bytes, stream, page_table,
-                               max_pages, page_rows, n_pages, empty ? nullptr : &fc);
+                               max_pages, page_rows, n_pages, empty ? nullptr : &fc, flags);
 }
 
 size_t csa_mqa_workspace_bytes(int B, int Tq, int H, int d, int n_rows_max) {

@@ -10,65 +10,9 @@
 // weights in LDS; each thread then accumulates alpha_i * row in float32 and
 // the partial sums of the row slots are reduced through LDS.  The entry is
 // rounded once to the cache type.
-#include "kernels.h"
+#include "compress_fold.h"
 
 namespace csa {
-
-constexpr int kRowsPerThread = 4;
-
-// One workgroup's share of one group: rows = the group's first row at this
-// slice's first column (rows d apart), z = its m logits, o = the entry at this
-// slice's first column.
-template <typename T>
-__device__ __forceinline__ void compress_group(const T *__restrict__ rows, const float *__restrict__ z, int m, int d,
-                                               int tpr, T *__restrict__ o) {
-    constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte vector
-    __shared__ float alpha[128];
-    __shared__ float red[256 * VEC];
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int rpar = 256 / tpr;        // rows accumulated in parallel
-    const int c = tid % tpr, rs = tid / tpr;
-    const int width = tpr * VEC;       // columns of this slice
-    rows += c * VEC;
-    u32x4 v[kRowsPerThread];
-#pragma unroll
-    for (int u = 0; u < kRowsPerThread; ++u) {
-        const int i = rs + u * rpar;
-        v[u] = i < m ? *(const u32x4 *)(rows + (int64_t)i * d) : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (tid < 64) {
-        const float z0 = lane < m ? z[lane] : -INFINITY;
-        const float z1 = lane + 64 < m ? z[lane + 64] : -INFINITY;
-        const float mx = wave_max(fmaxf(z0, z1));
-        const float e0 = lane < m ? expf(z0 - mx) : 0.f;
-        const float e1 = lane + 64 < m ? expf(z1 - mx) : 0.f;
-        const float s = wave_sum(e0 + e1);
-        if (lane < m) alpha[lane] = e0 / s;
-        if (lane + 64 < m) alpha[lane + 64] = e1 / s;
-    }
-    __syncthreads();
-
-    float acc[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-#pragma unroll
-    for (int u = 0; u < kRowsPerThread; ++u) {
-        const int i = rs + u * rpar;
-        const float a = i < m ? alpha[i] : 0.f;
-        const T *ve = (const T *)&v[u];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] += a * Elem<T>::to_f32(ve[e]);
-    }
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) red[rs * width + c * VEC + e] = acc[e];
-    __syncthreads();
-    for (int x = tid; x < width; x += 256) {
-        float s = 0.f;
-        for (int r = 0; r < rpar; ++r) s += red[r * width + x];
-        o[x] = Elem<T>::from_f32(s);
-    }
-}
 
 // Small groups (m no larger than the row slots of k_compress with a whole-row
 // slice, and at most kWaveRows): one wavefront per (batch, group, slice of
@@ -149,19 +93,10 @@ __global__ __launch_bounds__(256) void k_compress(int G, int m, int d, int tpr, 
         clear_words(clr, clr_words, (int)blockIdx.x - work_blocks, (int)gridDim.x - work_blocks);
         return;
     }
-    const int sl = blockIdx.x % slices;
-    const int bg = blockIdx.x / slices;
-    const int b = bg / G, g = bg % G;
-    const int width = tpr * (16 / (int)sizeof(T));
-    compress_group(raw + b * raw_bs + (int64_t)g * m * d + sl * width, logits + b * log_bs + (int64_t)g * m, m, d,
-                   tpr, out + b * out_bs + (int64_t)g * d + sl * width);
+    CompressBlocks<T>{G, m, d, tpr, slices, raw, raw_bs, logits, log_bs, out, out_bs}.run((int)blockIdx.x);
 }
 
-// Ragged batches: sequence b's newest token is at position pos[b]; when it
-// completes a group (pos[b] + 1 a multiple of m) that group g = (pos[b]+1)/m - 1
-// is pooled out of the mirrored raw and logit rings (position p at row p mod
-// ring; the group's m rows are consecutive from row (g*m) mod ring) into entry g,
-// if g < out_rows.  Other sequences' workgroups return at once.
+// Ragged batches: the group each sequence's newest token completes (RaggedCompressBlocks).
 template <typename T>
 __global__ __launch_bounds__(256) void k_compress_ragged(int m, int d, int tpr, int slices,
                                                           const int64_t *__restrict__ pos, const T *__restrict__ raw,
@@ -173,16 +108,8 @@ __global__ __launch_bounds__(256) void k_compress_ragged(int m, int d, int tpr, 
         clear_words(clr, clr_words, (int)blockIdx.x - work_blocks, (int)gridDim.x - work_blocks);
         return;
     }
-    const int sl = blockIdx.x % slices;
-    const int64_t b = blockIdx.x / slices;
-    const int64_t p = pos[b];
-    if (p < 0 || (p + 1) % m != 0) return;
-    const int64_t g = (p + 1) / m - 1;
-    if (g >= out_rows) return;
-    const int64_t r0 = (g * m) % ring;
-    const int width = tpr * (16 / (int)sizeof(T));
-    compress_group(raw + b * raw_bs + r0 * d + sl * width, logits + b * log_bs + r0, m, d, tpr,
-                   out + om.offset(b, g, d) + sl * width);
+    RaggedCompressBlocks<T>{m, d, tpr, slices, pos, raw, raw_bs, logits, log_bs, ring, out, om, out_rows}.run(
+        (int)blockIdx.x);
 }
 
 // Per-channel pooling logits: channel x of entry g pools channel x of the

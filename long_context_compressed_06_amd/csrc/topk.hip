@@ -23,7 +23,7 @@
 // segments into LDS and resolves them.  Either way the kept set leaves in
 // ascending index order through one exchange of per-wavefront totals and
 // in-wave ballots, never a sort.
-#include "kernels.h"
+#include "compress_fold.h"
 
 namespace csa {
 
@@ -215,6 +215,13 @@ __device__ __forceinline__ bool trivial_row(int64_t nv, int k, int32_t *orow) {
     return true;
 }
 
+// Zero a query's first-digit histogram once nothing reads it any more, so
+// that every call leaves the histograms as zero as it needs them: a caller
+// that keeps one workspace for calls of one shape clears it only once.
+__device__ __forceinline__ void clear_row_hist(uint32_t *h) {
+    for (int i = threadIdx.x * 4; i < kTopkBins; i += blockDim.x * 4) *(u32x4 *)(h + i) = u32x4{0u, 0u, 0u, 0u};
+}
+
 struct IdxKey {
     int32_t j;
     uint32_t key;
@@ -261,7 +268,7 @@ constexpr int kStreamBatch = 4;  // 16-byte vectors per lane in flight per batch
 
 __global__ __launch_bounds__(kST) void k_topk_stream(int Tq, int N, int m, int k, QPos q_pos0,
                                                      const float *__restrict__ scores,
-                                                     const uint32_t *__restrict__ ghist, int32_t *__restrict__ out) {
+                                                     uint32_t *__restrict__ ghist, int32_t *__restrict__ out) {
     __shared__ IdxKey items[kStreamItems];
     __shared__ uint32_t hist[2048];
     __shared__ int sh[2 * kST / 64];
@@ -271,13 +278,18 @@ __global__ __launch_bounds__(kST) void k_topk_stream(int Tq, int N, int m, int k
     const int64_t row = blockIdx.x;
     const int64_t nv = n_visible(q_pos0.at(row / Tq, row % Tq), m, N);
     int32_t *orow = out + row * k;
-    if (trivial_row(nv, k, orow)) return;
+    uint32_t *hrow = ghist + row * kTopkBins;
+    if (trivial_row(nv, k, orow)) {
+        clear_row_hist(hrow);
+        return;
+    }
     const int stride = (int)topk_score_stride(N);
     const float *srow = scores + row * stride;
     const int per = (int)((nv + NW * 256 - 1) / (NW * 256)) * 256;  // run length (a multiple of 256 scores)
     const int s0 = wv * per;
     const int s1 = (int)min((int64_t)s0 + per, nv);
-    const Digit d = find_digit<kST>(ghist + row * kTopkBins, kTopkBins, k, sh, &shd);
+    const Digit d = find_digit<kST>(hrow, kTopkBins, k, sh, &shd);
+    clear_row_hist(hrow);
     const uint32_t kmin = topk_bin_floor(d.digit);  // keys of digit >= D
     // batches of kStreamBatch vectors of four consecutive scores per lane, all
     // in flight together (past the row's end the last vector is reread and
@@ -353,15 +365,27 @@ __global__ __launch_bounds__(kST) void k_topk_stream(int Tq, int N, int m, int k
 // least D (kept ones and candidates alike) to the chunk's segment, in index
 // order, and their number to counts.
 // k_topk_final: one workgroup per query gathers the segments into LDS (the
-// pairs arrive in index order), resolves the candidates and writes the kept
-// indices.  (A kernel boundary separates the two: on this multi-die GPU a
-// device-scope fence inside one kernel costs more.)
+// pairs arrive in index order), resolves the candidates, writes the kept
+// indices and zeroes the row's histogram.  (A kernel boundary separates the
+// two: on this multi-die GPU a device-scope fence inside one kernel costs
+// more.)  Workgroups past the filter's own (filter_blocks) run extra work of
+// the same call that neither reads nor writes what the filter touches: a
+// decode step's compression, which then needs no launch of its own.
+struct NoExtra {
+    __device__ __forceinline__ void run(int) const {}
+};
+
+template <class Extra>
 __global__ __launch_bounds__(kFT) void k_topk_filter(int Tq, int N, int m, int k, QPos q_pos0, int nblk,
                                                      const float *__restrict__ scores,
                                                      const uint32_t *__restrict__ ghist, IdxKey *__restrict__ seg,
-                                                     int32_t *__restrict__ counts) {
+                                                     int32_t *__restrict__ counts, int filter_blocks, Extra extra) {
     __shared__ int sh[kFT / 64];
     __shared__ Digit shd;
+    if ((int)blockIdx.x >= filter_blocks) {  // (uniform per workgroup: before any barrier)
+        extra.run((int)blockIdx.x - filter_blocks);
+        return;
+    }
     const int64_t row = blockIdx.x / nblk;
     const int blk = blockIdx.x % nblk;
     const int64_t nv = n_visible(q_pos0.at(row / Tq, row % Tq), m, N);
@@ -403,7 +427,7 @@ __global__ __launch_bounds__(kFT) void k_topk_filter(int Tq, int N, int m, int k
 
 __global__ __launch_bounds__(kNT) void k_topk_final(int Tq, int N, int m, int k, QPos q_pos0, int nblk,
                                                     const float *__restrict__ scores,
-                                                    const uint32_t *__restrict__ ghist,
+                                                    uint32_t *__restrict__ ghist,
                                                     const IdxKey *__restrict__ seg,
                                                     const int32_t *__restrict__ counts, int32_t *__restrict__ out) {
     extern __shared__ IdxKey items[];  // [kTopkFinalItems]
@@ -414,10 +438,15 @@ __global__ __launch_bounds__(kNT) void k_topk_final(int Tq, int N, int m, int k,
     const int64_t row = blockIdx.x;
     const int64_t nv = n_visible(q_pos0.at(row / Tq, row % Tq), m, N);
     int32_t *orow = out + row * k;
-    if (trivial_row(nv, k, orow)) return;
+    uint32_t *hrow = ghist + row * kTopkBins;
+    if (trivial_row(nv, k, orow)) {
+        clear_row_hist(hrow);
+        return;
+    }
     // the segment sizes are fetched alongside the histogram
     const int cnt = (int)threadIdx.x < nblk ? counts[row * nblk + threadIdx.x] : 0;
-    const Digit d = find_digit<kNT>(ghist + row * kTopkBins, kTopkBins, k, sh, &shd);
+    const Digit d = find_digit<kNT>(hrow, kTopkBins, k, sh, &shd);
+    clear_row_hist(hrow);
     int M;
     const int x = block_excl_scan<kNT>(cnt, sh, &M);
     if ((int)threadIdx.x <= nblk) pre[threadIdx.x] = (int)threadIdx.x < nblk ? x : M;
@@ -487,12 +516,15 @@ hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_topk(int B, int Tq, int N, int m, int k, QPos q_pos0, const float *scores, void *scratch,
-                       int32_t *out, hipStream_t st) {
+// extra_blocks workgroups of `extra` follow the filter's (filter path only)
+template <class Extra>
+static hipError_t launch_topk_x(int B, int Tq, int N, int m, int k, QPos q_pos0, const float *scores, void *scratch,
+                                int32_t *out, hipStream_t st, const Extra &extra, int64_t extra_blocks) {
     const int64_t rows = (int64_t)B * Tq;
     const TopkPlan p = topk_plan(rows, N);
     uint32_t *hist = (uint32_t *)scratch;
     if (!p.filter) {
+        if (extra_blocks) return hipErrorInvalidValue;
         hipLaunchKernelGGL(k_topk_stream, dim3((unsigned)rows), dim3(kST), 0, st, Tq, N, m, k, q_pos0, scores, hist,
                            out);
         return hipGetLastError();
@@ -501,10 +533,13 @@ hipError_t launch_topk(int B, int Tq, int N, int m, int k, QPos q_pos0, const fl
     int32_t *counts = (int32_t *)base;
     IdxKey *seg = (IdxKey *)(base + align256((size_t)rows * p.nblk * 4));
     if (N > 0) {
-        hipLaunchKernelGGL(k_topk_filter, dim3((unsigned)(rows * p.nblk)), dim3(kFT), 0, st, Tq, N, m, k, q_pos0,
-                           (int)p.nblk, scores, hist, seg, counts);
+        const int64_t fb = rows * p.nblk;
+        hipLaunchKernelGGL(k_topk_filter<Extra>, dim3((unsigned)(fb + extra_blocks)), dim3(kFT), 0, st, Tq, N, m, k,
+                           q_pos0, (int)p.nblk, scores, hist, seg, counts, (int)fb, extra);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+    } else if (extra_blocks) {
+        return hipErrorInvalidValue;
     }
     const size_t lds = (size_t)kTopkFinalItems * sizeof(IdxKey);
     static const hipError_t attr =
@@ -513,6 +548,32 @@ hipError_t launch_topk(int B, int Tq, int N, int m, int k, QPos q_pos0, const fl
     hipLaunchKernelGGL(k_topk_final, dim3((unsigned)rows), dim3(kNT), lds, st, Tq, N, m, k, q_pos0, (int)p.nblk,
                        scores, hist, seg, counts, out);
     return hipGetLastError();
+}
+
+hipError_t launch_topk(int B, int Tq, int N, int m, int k, QPos q_pos0, const float *scores, void *scratch,
+                       int32_t *out, hipStream_t st) {
+    return launch_topk_x(B, Tq, N, m, k, q_pos0, scores, scratch, out, st, NoExtra{}, 0);
+}
+
+template <typename T>
+static hipError_t launch_topk_folded_t(int B, int Tq, int N, int m, int k, QPos q_pos0, const float *scores,
+                                       void *scratch, int32_t *out, hipStream_t st, const FoldedCompress &c) {
+    int tpr, slices;
+    if (!compress_partition(c.d, c.m, 16 / (int)sizeof(T), &tpr, &slices)) return hipErrorInvalidValue;
+    if (c.ragged) {
+        const RaggedCompressBlocks<T> x{c.m, c.d, tpr, slices, c.pos, (const T *)c.raw, c.raw_bs, c.logits,
+                                        c.log_bs, c.ring, (T *)c.out, c.omap, c.out_rows};
+        return launch_topk_x(B, Tq, N, m, k, q_pos0, scores, scratch, out, st, x, (int64_t)c.B * slices);
+    }
+    const CompressBlocks<T> x{c.G, c.m, c.d, tpr, slices, (const T *)c.raw, c.raw_bs, c.logits, c.log_bs,
+                              (T *)c.out, c.out_bs};
+    return launch_topk_x(B, Tq, N, m, k, q_pos0, scores, scratch, out, st, x, (int64_t)c.B * c.G * slices);
+}
+
+hipError_t launch_topk_folded(int B, int Tq, int N, int m, int k, QPos q_pos0, const float *scores, void *scratch,
+                              int32_t *out, hipStream_t st, const FoldedCompress &fc) {
+    if (fc.dt == 0) return launch_topk_folded_t<float>(B, Tq, N, m, k, q_pos0, scores, scratch, out, st, fc);
+    return launch_topk_folded_t<bf16_t>(B, Tq, N, m, k, q_pos0, scores, scratch, out, st, fc);
 }
 
 }  // namespace csa

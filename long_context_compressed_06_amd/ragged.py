@@ -80,7 +80,8 @@ class RaggedLayer:
             else:
                 self.k_idx = torch.zeros(lead + (dI,), dtype=dtype, device=device)
             nb = index_topk_workspace_bytes(B, 1, self.cap_e, HI, k)
-            self.idx_ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=device)
+            # zero-filled once; the index calls (one shape) leave its top-k histograms zero
+            self.idx_ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device=device)
             self.topk_idx = torch.empty((B, 1, k), dtype=torch.int32, device=device)
         rows_max = (k if mode == "csa" else self.cap_e) + W
         nb = mqa_workspace_bytes(B, 1, H, d, rows_max)
@@ -147,7 +148,7 @@ class RaggedLayer:
             else:
                 jobs.append((k_idx_tok, self.k_idx, 0, 0, self.pos, self.m, pg))
         csa_append_rows_multi(jobs)
-        # the group the token completes (if any), pooled out of the rings: in the index call's first launch
+        # the group the token completes (if any), pooled out of the rings: in one of the index call's launches
         # when the index operands share the rings' element type (CSA), else on its own
         comp = (self.raw_ring, self.logit_ring[..., 0], self.R, self.m, self.pos, self.entries)
         fuse = self.mode == "csa" and q_idx.dtype == self.raw_ring.dtype
@@ -158,13 +159,14 @@ class RaggedLayer:
             if self.index_fmt == "mx4":
                 keys = (q_idx, w_idx, self.k_codes, self.k_scales, self.cap_e)
                 if fuse:
-                    csa_ragged_compress_index_topk_mx4(*comp, *keys, self.k, entry_pages=self.pages, **ix)
+                    csa_ragged_compress_index_topk_mx4(*comp, *keys, self.k, entry_pages=self.pages, hist_zero=True,
+                                                       **ix)
                 else:
                     csa_ragged_index_topk_mx4(*keys, self.m, self.k, self.pos, **ix)
             else:
                 keys = (q_idx, w_idx, self.k_idx, self.cap_e)
                 if fuse:
-                    csa_ragged_compress_index_topk(*comp, *keys, self.k, entry_pages=self.pages, **ix)
+                    csa_ragged_compress_index_topk(*comp, *keys, self.k, entry_pages=self.pages, hist_zero=True, **ix)
                 else:
                     csa_ragged_index_topk(*keys, self.m, self.k, self.pos, **ix)
             csa_ragged_sparse_mqa(q, self.entries, self.topk_idx, self.raw_ring, self.R, self.cap_e, self.m, self.W,

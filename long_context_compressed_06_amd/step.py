@@ -52,7 +52,9 @@ class AttentionStep:
             self.topk_idx = torch.empty((B, Tq, self.k), dtype=torch.int32, device=dev)
 
             nb = index_topk_workspace_bytes(B, Tq, self.N, HI, self.k)
-            self.idx_ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+            # zero-filled once: every index call of this one shape leaves its top-k histograms zero, so the fused
+            # calls need not clear them (and carry the compression in the top-k filter launch)
+            self.idx_ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device=dev)
         self._ready = True
 
     def __call__(self, x: dict) -> torch.Tensor:
@@ -60,7 +62,7 @@ class AttentionStep:
         if not self._ready:
             self._prepare(x)
         raw, entries = x["raw"], x["entries"]
-        # the new groups' compression rides in the index call's first launch (CSA) or runs alone (HCA)
+        # the new groups' compression rides in one of the index call's launches (CSA) or runs alone (HCA)
         comp = ()
         if self.N > self.g0:
             r0 = self.g0 * self.m - self.raw_pos0
@@ -72,14 +74,14 @@ class AttentionStep:
             args = (x["q_idx"], x["w_idx"], x["k_codes"], x["k_scales"], self.N)
             if comp:
                 csa_compress_index_topk_mx4(*comp, *args, self.k, self.q_pos0, topk_idx=self.topk_idx,
-                                            workspace=self.idx_ws)
+                                            workspace=self.idx_ws, hist_zero=True)
             else:
                 csa_index_topk_mx4(*args, self.m, self.k, self.q_pos0, topk_idx=self.topk_idx, workspace=self.idx_ws)
         elif self.mode == "csa":
             args = (x["q_idx"], x["w_idx"], x["k_idx"], self.N)
             if comp:
                 csa_compress_index_topk(*comp, *args, self.k, self.q_pos0, topk_idx=self.topk_idx,
-                                        workspace=self.idx_ws)
+                                        workspace=self.idx_ws, hist_zero=True)
             else:
                 csa_index_topk(*args, self.m, self.k, self.q_pos0, topk_idx=self.topk_idx, workspace=self.idx_ws)
         if self.mode == "csa":

@@ -105,18 +105,20 @@ def test_index_topk_validation(L):
 
 def fused(L, mx4=False, dt=1, B=1, G=1, m=4, d=512, raw=P + 0x50000000, logits=P + 0x51000000,
           ent=P + 0x52000000, Tq=1, N=1000, HI=64, dI=128, k=64, q_pos0=3999, q=P, w=P + 0x100000,
-          kk=P + 0x200000, ks=P + 0x280000, out=P + 0x3000000, ws=P + 0x4000000, wsb=1 << 30):
+          kk=P + 0x200000, ks=P + 0x280000, out=P + 0x3000000, ws=P + 0x4000000, wsb=1 << 30, flags=0):
     c = (dt, B, G, m, d, raw, G * m * d, logits, G * m, ent, G * d)
     if mx4:
         return L.csa_compress_index_topk_mx4(*c, Tq, N, HI, dI, k, q_pos0, q, w, kk, ks, N, out, None, ws, wsb,
-                                             None)
-    return L.csa_compress_index_topk(*c, Tq, N, HI, dI, k, q_pos0, q, w, kk, N * dI, out, None, ws, wsb, None)
+                                             flags, None)
+    return L.csa_compress_index_topk(*c, Tq, N, HI, dI, k, q_pos0, q, w, kk, N * dI, out, None, ws, wsb, flags,
+                                     None)
 
 
 @pytest.mark.parametrize("mx4", [False, True])
 def test_compress_index_topk_validation(L, mx4):
     """The fused call keeps both calls' checks, and its compression output may touch no index operand,
-    output or the workspace (which its launch clears), nor its inputs the workspace."""
+    output or the workspace, nor its inputs the workspace or an index output (the compression may run before
+    or after the indexer); flags other than CSA_HIST_ZERO are refused."""
     f = lambda **kw: fused(L, mx4, **kw)
     assert f(dt=2) == -2
     assert f(d=100) == -6 and f(m=0) == -6
@@ -130,7 +132,12 @@ def test_compress_index_topk_validation(L, mx4):
     assert f(raw=P + 0x4000000 + 4096) == -1       # raw inside the workspace
     assert f(logits=P + 0x4000000 + 4096) == -1
     assert b"workspace" in L.csa_last_error_detail()
+    assert f(raw=P + 0x3000000) == -1              # raw on the selection output
+    assert b"index output" in L.csa_last_error_detail()
+    assert f(flags=2) == -1 and f(flags=-1) == -1
+    assert b"flags" in L.csa_last_error_detail()
     assert f(B=0) == 0 and f(G=0, Tq=0) == 0       # empty: nothing enqueued
+    assert f(B=0, flags=1) == 0
 
 
 def mqa(L, fn="sparse", dt=1, B=1, Tq=1, H=64, d=512, N=1000, m=4, k=64, W=128, q_pos0=4095, scale=0.04,
@@ -344,14 +351,15 @@ def test_ragged_compress_index_topk_validation(L, mx4):
 
     ws = csa.index_topk_workspace_bytes(2, 1, 256, 64, 64)
 
-    def rf(B=2, m=4, pos=P, raw=P + 0x1000000, lg=P + 0x1100000, ent=P + 0x1200000, k=64, wsb=ws):
+    def rf(B=2, m=4, pos=P, raw=P + 0x1000000, lg=P + 0x1100000, ent=P + 0x1200000, k=64, wsb=ws, flags=0):
         c = (1, B, m, 128, pos, raw, 2 * 16 * 128, lg, 32, 16, ent, 64 * 128, 64, None, 0, 0, 0)
         if mx4:
             return L.csa_ragged_compress_index_topk_mx4(*c, 256, 64, 128, k, P + 0x10000, P + 0x40000, P + 0x80000,
                                                         P + 0xC0000, 256, None, 0, 0, 0, P + 0x200000, None,
-                                                        P + 0x300000, wsb, None)
+                                                        P + 0x300000, wsb, flags, None)
         return L.csa_ragged_compress_index_topk(*c, 256, 64, 128, k, P + 0x10000, P + 0x40000, P + 0x80000,
-                                                256 * 128, None, 0, 0, 0, P + 0x200000, None, P + 0x300000, wsb, None)
+                                                256 * 128, None, 0, 0, 0, P + 0x200000, None, P + 0x300000, wsb,
+                                                flags, None)
 
     assert rf(m=0) == -6
     assert rf(pos=None) == -1 and rf(pos=P + 4) == -3
@@ -362,7 +370,10 @@ def test_ragged_compress_index_topk_validation(L, mx4):
     assert rf(ent=P + 0x300000) == -1            # ... the workspace
     assert rf(raw=P + 0x300000) == -1            # the raw ring inside the workspace
     assert b"workspace" in L.csa_last_error_detail()
-    assert rf(B=0, pos=None) == 0
+    assert rf(pos=P + 0x200000) == -1            # pos on the selection output
+    assert b"index output" in L.csa_last_error_detail()
+    assert rf(flags=4) == -1
+    assert rf(B=0, pos=None) == 0 and rf(B=0, pos=None, flags=1) == 0
 
 
 def test_stream_read_rejects_bad_arguments(L):

@@ -317,17 +317,21 @@ def test_compress_forms_bit_identical(csa, dtype, m, d):
                            out[:, gi].view(torch.int16 if dtype == "bf16" else torch.int32)), gi
 
 
-# ------------------------------- compression fused into the index call's first launch
+# ------------------------------- compression fused into one of the index call's launches
 FUSED = [("elem", "bf16", 4, 512, 1, 1, 3000), ("mx4", "bf16", 4, 512, 1, 1, 3000),
          ("elem", "bf16", 16, 128, 3, 2, 2500), ("mx4", "f32", 8, 256, 2, 4, 1900),
-         ("elem", "f32", 4, 64, 5, 1, 40), ("elem", "bf16", 4, 512, 2, 1, 0), ("mx4", "bf16", 4, 512, 1, 3, 0)]
+         ("elem", "f32", 4, 64, 5, 1, 40), ("elem", "bf16", 4, 512, 2, 1, 0), ("mx4", "bf16", 4, 512, 1, 3, 0),
+         ("elem", "bf16", 4, 128, 100, 2, 3000), ("mx4", "bf16", 4, 512, 90, 1, 2000)]
 
 
 @pytest.mark.parametrize("case", FUSED, ids=["-".join(map(str, c)) for c in FUSED])
 def test_compress_index_topk_fused_bit_identical(csa, case):
     """The fused call gives what csa_compress then the index call give, bit for bit: entries, selection and
     scores.  Both run on one workspace, the fused call after the separate one and then again, so its own
-    histogram clear is what resets the selection's counts each time."""
+    histogram clear is what resets the selection's counts each time.  Then with hist_zero (no clear: the
+    compression in the top-k filter launch for few queries, alone before the indexer for many, the last two
+    cases), three times in a row on that workspace and on a zero-filled one: each call must leave the
+    histograms zero for the next."""
     fmt, dtype, m, d, Tq, G, N = case
     say("fused compress + index", case)
     dt = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -366,6 +370,16 @@ def test_compress_index_topk_fused_bit_identical(csa, case):
         assert torch.equal(ia, ib), rep
         assert torch.equal(sa.view(torch.int32), sb.view(torch.int32)), rep
     assert not torch.isnan(ea.float()).any()
+    ws0 = torch.zeros_like(ws)
+    for w in (ws, ws0):
+        for rep in range(3):
+            eb, ib, sb = outputs()
+            fused(raw, logits, m, eb, q_idx, w_idx, *kargs, N, k, q_pos0, topk_idx=ib, scores_out=sb, workspace=w,
+                  hist_zero=True)
+            torch.cuda.synchronize()
+            assert torch.equal(ea.view(bits), eb.view(bits)), ("hist_zero", rep)
+            assert torch.equal(ia, ib), ("hist_zero", rep)
+            assert torch.equal(sa.view(torch.int32), sb.view(torch.int32)), ("hist_zero", rep)
 
 
 # ------------------------------------------ top-k first digit: window and end bins

@@ -336,7 +336,9 @@ CSA_CASES = [c for c in CASES if c.mode == "csa"]
 def test_ragged_fused_equals_separate_calls(csa, c, monkeypatch):
     """The layer's fused compression + index call gives what csa_ragged_compress then the ragged index call
     give, bit for bit: outputs, selections and every cache row, step after step (groups completing at
-    different steps in different sequences), contiguous and paged."""
+    different steps in different sequences), contiguous and paged.  The fused layer passes hist_zero (its
+    workspace starts zero and every call leaves the histograms zero), so its compression runs in the top-k
+    filter launch."""
     import long_context_compressed_06_amd.ragged as rg
 
     say(c, "fused vs separate")
@@ -344,13 +346,13 @@ def test_ragged_fused_equals_separate_calls(csa, c, monkeypatch):
     fused, sep = make_layer(csa, c, seqs), make_layer(csa, c, seqs)
 
     def sep_elem(raw_ring, logit_ring, ring, m, pos, ent, q_idx, w_idx, k_idx, N, k, topk_idx=None, workspace=None,
-                 entry_pages=None, pages=None):
+                 entry_pages=None, pages=None, hist_zero=False):
         csa.csa_ragged_compress(raw_ring, logit_ring, ring, m, pos, ent, pages=entry_pages)
         csa.csa_ragged_index_topk(q_idx, w_idx, k_idx, N, m, k, pos, topk_idx=topk_idx, workspace=workspace,
                                   pages=pages)
 
     def sep_mx4(raw_ring, logit_ring, ring, m, pos, ent, q_idx, w_idx, kc, ks, N, k, topk_idx=None, workspace=None,
-                entry_pages=None, pages=None):
+                entry_pages=None, pages=None, hist_zero=False):
         csa.csa_ragged_compress(raw_ring, logit_ring, ring, m, pos, ent, pages=entry_pages)
         csa.csa_ragged_index_topk_mx4(q_idx, w_idx, kc, ks, N, m, k, pos, topk_idx=topk_idx, workspace=workspace,
                                       pages=pages)
