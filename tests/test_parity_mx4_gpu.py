@@ -108,7 +108,10 @@ def run_mx4(csa, orc, wl: Workload, cap_extra: int, scale_offset: int = 0):
     fin = np.isfinite(ref)
     assert np.array_equal(np.isfinite(got), fin), "finiteness of scores differs"
     if ref.size:
-        err = np.abs(np.where(fin, got - ref, 0.0)).max(axis=2)
+        # masked entries are -inf on both sides: take differences only where finite
+        diff = np.zeros_like(ref)
+        diff[fin] = got[fin] - ref[fin]
+        err = np.abs(diff).max(axis=2)
         scale = np.abs(np.where(fin, ref, 0.0)).max(axis=2)
         worst = (err / np.maximum(scale, 1e-30)).max()
         assert np.all(err <= F32_REL * np.maximum(scale, 1e-30)), f"scores: worst {worst:.3e}"
